@@ -1,0 +1,70 @@
+"""Forward and backward of the QLoRA linear in float64.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Shapes (LoRA convention of "LoRA, QLoRA, QA-LoRA explained", section 1, and
+"bitsandbytes deep dive", section 12.2): x [M, K=Din], W_hat as the [K, N=Dout]
+view of the stored [N, K] dequantized weight, A [K, r], B [r, N], s = alpha/r.
+
+Forward (deep dive 12.4; explained, section 2: W_eff = dequant(W4) + (alpha/r) A B):
+    y = x W_hat + s (x A) B
+Backward: the base weight is frozen (requires_grad = False, deep dive 12.4), so
+there is no dW; by the chain rule through the same graph
+    u  = s dy B^T                (gradient reaching the LoRA bottleneck)
+    dx = dy W_hat^T + u A^T
+    dA = x^T u      = s x^T (dy B^T)
+    dB = t^T dy     with t = s x A
+No bias, no dropout (no workload asks for them).  Every product is a float64
+numpy matmul of the exact bf16 input values.
+"""
+import numpy as np
+
+
+def lora_scale(alpha, r):
+    """s = alpha / r (deep dive 12.2: s follows lora_alpha / r)."""
+    return float(alpha) / float(r)
+
+
+def lora_branch(x, A, B, s):
+    """s (x A) B -- the low-rank side path."""
+    return s * ((np.asarray(x, np.float64) @ np.asarray(A, np.float64)) @ np.asarray(B, np.float64))
+
+
+def linear_fwd(x, W_hat_nk, A, B, alpha, r):
+    """y = x W_hat + s (x A) B; W_hat_nk is the stored [N, K] dequantized weight (float64).
+
+    Returns (y [M, N], t = s x A [M, r]).
+    """
+    x = np.asarray(x, np.float64)
+    s = lora_scale(alpha, r)
+    t = s * (x @ np.asarray(A, np.float64))
+    y = x @ np.asarray(W_hat_nk, np.float64).T + t @ np.asarray(B, np.float64)
+    return y, t
+
+
+def linear_bwd(x, W_hat_nk, A, B, alpha, r, dy):
+    """Gradients of <dy, y> w.r.t. x, A and B (no dW: the base is frozen).
+
+    Returns (dx [M, K], dA [K, r], dB [r, N]).
+    """
+    x = np.asarray(x, np.float64)
+    dy = np.asarray(dy, np.float64)
+    A = np.asarray(A, np.float64)
+    B = np.asarray(B, np.float64)
+    s = lora_scale(alpha, r)
+    u = s * (dy @ B.T)
+    dx = dy @ np.asarray(W_hat_nk, np.float64) + u @ A.T
+    dA = x.T @ u
+    dB = (s * (x @ A)).T @ dy
+    return dx, dA, dB
+
+
+def rel_err(got, ref):
+    """Normwise relative error ||got - ref||_F / ||ref||_F (0 when both are zero)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.linalg.norm(ref)
+    num = np.linalg.norm(got - ref)
+    if den == 0.0:
+        return 0.0 if num == 0.0 else float("inf")
+    return float(num / den)

@@ -1,0 +1,120 @@
+"""Pins of the CPU oracle's forward / backward against the pages and the mathematics.
+
+* the worked rank-1 example and the pooled-branch example printed on
+  "LoRA, QLoRA, QA-LoRA explained" (tests/golden/lora_worked_examples.json);
+* B = 0 reduces the layer to a plain product with the dequantized weight;
+* the merged-weight identity y = x (W_hat + s A B) from the same page;
+* adjoint identities (y is linear in each of x, A, B separately) and central
+  finite differences, on non-square shapes so that a transposed operand or a
+  dropped term cannot pass.
+"""
+import json
+import os
+
+import numpy as np
+
+from oracle import bf16, lora, nf4
+from bit_nf4_quantized_15_amd import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _g():
+    with open(os.path.join(GOLDEN, "lora_worked_examples.json")) as f:
+        return json.load(f)
+
+
+def test_worked_rank1_delta_w():
+    ex = _g()["rank1_delta_w"]
+    A = np.array(ex["A"])
+    B = np.array(ex["B"])
+    dW = np.array(ex["delta_w"])
+    for i in range(4):
+        e = np.zeros((1, 4)); e[0, i] = 1.0
+        assert np.allclose(lora.lora_branch(e, A, B, 1.0), dW[i:i + 1], atol=1e-15)
+    x = np.array([[1.0, 2.0, 3.0, 4.0]])
+    assert np.allclose(lora.lora_branch(x, A, B, 1.0), x @ dW, atol=1e-14)
+    # through the full layer with a zero base weight and s = alpha/r = 1
+    y, t = lora.linear_fwd(x, np.zeros((2, 4)), A, B, alpha=1.0, r=1)
+    assert np.allclose(y, x @ dW, atol=1e-14) and np.allclose(t, x @ A)
+
+
+def test_pooled_branch_example():
+    ex = _g()["qa_lora_pooled_branch"]
+    x = np.array(ex["x"])
+    gsz = ex["group_size"]
+    pooled = x.reshape(-1, gsz).mean(axis=1)
+    assert np.allclose(pooled, ex["pooled"])
+    A = np.array(ex["A"]); B = np.array(ex["B"])
+    assert np.isclose((pooled[None, :] @ A)[0, 0], ex["xA"])
+    assert np.allclose(lora.lora_branch(pooled[None, :], A, B, 1.0)[0], ex["branch"], atol=1e-15)
+
+
+def _small(seed, M=3, N=48, K=128, r=4):
+    rng = np.random.default_rng(seed)
+    W = workloads.custom(seed, (N, K), 0.02)
+    p, q8, A2 = nf4.quantize(W)
+    Wh = bf16.to_f64(nf4.dequantize(p, q8, A2, N, K))
+    x = rng.standard_normal((M, K))
+    A = rng.standard_normal((K, r)) / np.sqrt(r)
+    B = rng.standard_normal((r, N)) * 0.01
+    dy = rng.standard_normal((M, N))
+    return Wh, x, A, B, dy
+
+
+def test_lora_off_is_plain_product():
+    Wh, x, A, B, _ = _small(1)
+    y, _ = lora.linear_fwd(x, Wh, A, np.zeros_like(B), alpha=16, r=4)
+    ref = np.einsum("mk,nk->mn", x, Wh)
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_merged_weight_identity():
+    Wh, x, A, B, _ = _small(2)
+    s = lora.lora_scale(16, 4)
+    W_eff = Wh.T + s * (A @ B)                 # [K, N]
+    y, _ = lora.linear_fwd(x, Wh, A, B, alpha=16, r=4)
+    assert np.allclose(y, x @ W_eff, rtol=1e-12, atol=1e-14)
+
+
+def test_backward_adjoint_identities():
+    Wh, x, A, B, dy = _small(3)
+    alpha, r = 8.0, 4
+    dx, dA, dB = lora.linear_bwd(x, Wh, A, B, alpha, r, dy)
+    y, _ = lora.linear_fwd(x, Wh, A, B, alpha, r)
+    # <dy, y(x)> = <dx, x>            (y linear in x)
+    assert np.isclose(np.sum(dy * y), np.sum(dx * x), rtol=1e-12)
+    # <dy, y(A) - y(0)> = <dA, A>     (y affine in A)
+    y0, _ = lora.linear_fwd(x, Wh, np.zeros_like(A), B, alpha, r)
+    assert np.isclose(np.sum(dy * (y - y0)), np.sum(dA * A), rtol=1e-12)
+    y0b, _ = lora.linear_fwd(x, Wh, A, np.zeros_like(B), alpha, r)
+    assert np.isclose(np.sum(dy * (y - y0b)), np.sum(dB * B), rtol=1e-12)
+    assert dx.shape == x.shape and dA.shape == A.shape and dB.shape == B.shape
+
+
+def test_backward_central_differences():
+    Wh, x, A, B, dy = _small(4, M=2, N=16, K=64, r=2)
+    alpha, r = 3.0, 2
+    dx, dA, dB = lora.linear_bwd(x, Wh, A, B, alpha, r, dy)
+
+    def f(x_, A_, B_):
+        return np.sum(dy * lora.linear_fwd(x_, Wh, A_, B_, alpha, r)[0])
+
+    h = 1e-3
+    rng = np.random.default_rng(0)
+    for _ in range(12):
+        i, j = rng.integers(0, x.shape[0]), rng.integers(0, x.shape[1])
+        e = np.zeros_like(x); e[i, j] = h
+        assert np.isclose((f(x + e, A, B) - f(x - e, A, B)) / (2 * h), dx[i, j], rtol=1e-7, atol=1e-9)
+        i, j = rng.integers(0, A.shape[0]), rng.integers(0, A.shape[1])
+        e = np.zeros_like(A); e[i, j] = h
+        assert np.isclose((f(x, A + e, B) - f(x, A - e, B)) / (2 * h), dA[i, j], rtol=1e-7, atol=1e-9)
+        i, j = rng.integers(0, B.shape[0]), rng.integers(0, B.shape[1])
+        e = np.zeros_like(B); e[i, j] = h
+        assert np.isclose((f(x, A, B + e) - f(x, A, B - e)) / (2 * h), dB[i, j], rtol=1e-7, atol=1e-9)
+
+
+def test_rel_err():
+    assert lora.rel_err(np.ones(4), np.ones(4)) == 0.0
+    assert np.isclose(lora.rel_err(np.array([3.0, 4.0]) * 1.01, np.array([3.0, 4.0])), 0.01)
+    assert lora.rel_err(np.zeros(3), np.zeros(3)) == 0.0
