@@ -1,0 +1,65 @@
+// Internal helpers shared by the HIP kernels of libqlora (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qlora.h"
+
+namespace qlora {
+
+constexpr int kBlock = 64;                 // weights per first-level block
+constexpr int kSuper = 256;                // blocks per second-level (fp32) scale
+constexpr int kSuperElems = kBlock * kSuper;
+constexpr int kZeroCode = 7;
+
+// The 16 NF4 levels as IEEE binary32 bit patterns, ascending: Phi^-1 of
+// 8 (positive half) and 7 (negative half) equal-probability points between
+// 1/2 and delta = 1 - (1/32 + 1/30)/2, plus an exact 0, divided by
+// Phi^-1(delta) and rounded to nearest float ("bitsandbytes deep dive",
+// section 6.2: quantiles of N(0,1), normalised to [-1,1], asymmetric, exact 0).
+constexpr uint32_t kNf4Bits[16] = {
+    0xbf800000u, 0xbf3239b1u, 0xbf066b2eu, 0xbeca329eu, 0xbe91a24bu, 0xbe3d353du,
+    0xbdba7869u, 0x00000000u, 0x3da2fb01u, 0x3e24cadfu, 0x3e7c04dau, 0x3ead0336u,
+    0x3ee1a4b5u, 0x3f1007a9u, 0x3f3913b0u, 0x3f800000u};
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float nf4_level(int j) { return __uint_as_float(kNf4Bits[j]); }
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// Two floats -> packed bf16x2 (lo in bits 15..0), round to nearest even
+// (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2_t f = {lo, hi};
+    bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, b);
+}
+
+// Round a float down (toward -inf) onto the bf16 grid; returned as a float.
+__device__ __forceinline__ float f32_rd_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    uint32_t t = u & 0xFFFF0000u;                       // truncation toward zero
+    if ((u & 0x80000000u) && (u & 0x0000FFFFu)) t += 0x00010000u;  // negative: one step down
+    return __uint_as_float(t);
+}
+
+// Report a launch error as a status.
+inline qlora_status launch_status() {
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP;
+}
+
+// Launchers (one per translation unit).
+qlora_status launch_quantize(const uint16_t* W, int64_t nblocks, uint8_t* codes, uint8_t* q8, float* a2,
+                             hipStream_t s);
+qlora_status launch_dequantize(const uint8_t* codes, const uint8_t* q8, const float* a2, int64_t nblocks,
+                               uint16_t* out, hipStream_t s);
+
+}  // namespace qlora

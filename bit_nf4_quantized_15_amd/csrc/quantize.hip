@@ -1,0 +1,201 @@
+// NF4 blockwise quantization with double-quantized scales, and the matching
+// dequantization ("bitsandbytes deep dive", sections 5.1-5.2, 6.2, 7.2).
+//
+// nf4_quantize_kernel: one workgroup (256 lanes) per group of 256 blocks
+// (16384 weights, 32 KB of bf16).  Every weight is read from HBM once:
+//   1. each lane loads 8 bf16 (16 B) per pass, 8 passes; a wave's load covers
+//      1 KB of consecutive weights (8 blocks x 8 lanes x 16 B);
+//   2. block absmax: integer max of |bits| over the lane's 8 values, then a
+//      3-step shuffle over the block's 8 lanes;
+//   3. lane t computes block t's 15 decision thresholds
+//      T_j = RD_bf16(a * m_j), m_j = (c_j + c_{j+1}) / 2, exactly (the product
+//      is exact in fp64, then rounded down to the bf16 grid), the group scale
+//      a2 = max a, and the 8-bit scale code;
+//   4. for a bf16 weight w and any real X, w > X  <=>  w > RD_bf16(X), so the
+//      code = #{j : w/a > m_j} (nearest level, ties to the lower index) is a
+//      4-step branchless binary search over T_j in fp32 compares;
+//   5. nibbles are packed (element 2i high) and stored as one dword per lane.
+#include "common.h"
+
+namespace qlora {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kPasses = kSuper / 32;  // 32 blocks per pass (4 waves x 8 blocks)
+
+__device__ __forceinline__ uint32_t absmax_bits8(u32x4_t v) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t x = v[i] & 0x7FFF7FFFu;
+        m = max(m, max(x & 0xFFFFu, x >> 16));
+    }
+    return m;
+}
+
+// count of thresholds strictly below w (T ascending, 15 entries)
+__device__ __forceinline__ uint32_t nf4_code(float w, const float* T) {
+    const bool b3 = w > T[7];
+    const float t2 = b3 ? T[11] : T[3];
+    const bool b2 = w > t2;
+    const float t1 = b3 ? (b2 ? T[13] : T[9]) : (b2 ? T[5] : T[1]);
+    const bool b1 = w > t1;
+    const float t0 = b3 ? (b2 ? (b1 ? T[14] : T[12]) : (b1 ? T[10] : T[8]))
+                        : (b2 ? (b1 ? T[6] : T[4]) : (b1 ? T[2] : T[0]));
+    const bool b0 = w > t0;
+    return (b3 ? 8u : 0u) | (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
+}
+
+__global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint16_t* __restrict__ W,
+                                                                int64_t nblocks,
+                                                                uint8_t* __restrict__ codes,
+                                                                uint8_t* __restrict__ q8,
+                                                                float* __restrict__ a2) {
+    __shared__ float s_amax[kSuper];
+    __shared__ float s_thr[kSuper * 16];
+    __shared__ float s_wmax[kThreads / 64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t b0 = (int64_t)blockIdx.x * kSuper;
+    const int nb_here = (int)min((int64_t)kSuper, nblocks - b0);
+    const int sub = lane & 7;
+
+    // 1. all loads in flight at once
+    u32x4_t v[kPasses];
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+        const int bl = p * 32 + wave * 8 + (lane >> 3);
+        if (bl < nb_here) {
+            const u32x4_t* src = reinterpret_cast<const u32x4_t*>(W + (b0 + bl) * kBlock + sub * 8);
+            v[p] = __builtin_nontemporal_load(src);
+        } else {
+            v[p] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+    }
+
+    // 2. block absmax
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+        uint32_t m = absmax_bits8(v[p]);
+        m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+        m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+        m = max(m, (uint32_t)__shfl_xor((int)m, 4));
+        const int bl = p * 32 + wave * 8 + (lane >> 3);
+        if (sub == 0) s_amax[bl] = bf16_bits_to_f32(m);   // 0 for blocks past the end
+    }
+    __syncthreads();
+
+    // 3. thresholds of block `tid`, group scale, scale code
+    const float a = s_amax[tid];
+    {
+        float T[15];
+        if (a > 0.0f) {
+            const double ad = (double)a;
+#pragma unroll
+            for (int j = 0; j < 15; ++j) {
+                const double m = 0.5 * ((double)nf4_level(j) + (double)nf4_level(j + 1));  // exact
+                T[j] = f32_rd_bf16(__double2float_rd(ad * m));                          // exact product
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 15; ++j) T[j] = (j < kZeroCode) ? -1.0f : 1.0f;  // every w = 0 -> code 7
+        }
+        f32x4_t* dst = reinterpret_cast<f32x4_t*>(&s_thr[tid * 16]);
+        dst[0] = f32x4_t{T[0], T[1], T[2], T[3]};
+        dst[1] = f32x4_t{T[4], T[5], T[6], T[7]};
+        dst[2] = f32x4_t{T[8], T[9], T[10], T[11]};
+        dst[3] = f32x4_t{T[12], T[13], T[14], 0.0f};
+    }
+    float gm = a;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) gm = fmaxf(gm, __shfl_xor(gm, o));
+    if (lane == 0) s_wmax[wave] = gm;
+    __syncthreads();
+    const float A2 = fmaxf(fmaxf(s_wmax[0], s_wmax[1]), fmaxf(s_wmax[2], s_wmax[3]));
+    if (tid < nb_here) {
+        // q8 = #{k in 1..255 : 510 a > (2k-1) A2}; all products exact in fp64
+        const double x = 510.0 * (double)a;
+        const double y = (double)A2;
+        int k = 0;
+#pragma unroll
+        for (int step = 128; step >= 1; step >>= 1) {
+            const int c = k + step;
+            if (c <= 255 && (double)(2 * c - 1) * y < x) k = c;
+        }
+        q8[b0 + tid] = (uint8_t)k;
+    }
+    if (tid == 0) a2[blockIdx.x] = A2;
+
+    // 4-5. codes against the true absmax, packed and stored
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+        const int bl = p * 32 + wave * 8 + (lane >> 3);
+        if (bl < nb_here) {
+            float T[16];
+            const f32x4_t* src = reinterpret_cast<const f32x4_t*>(&s_thr[bl * 16]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x4_t t = src[i];
+                T[4 * i + 0] = t[0]; T[4 * i + 1] = t[1]; T[4 * i + 2] = t[2]; T[4 * i + 3] = t[3];
+            }
+            uint32_t packed = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t bits = (i & 1) ? (v[p][i >> 1] >> 16) : (v[p][i >> 1] & 0xFFFFu);
+                const uint32_t q = nf4_code(bf16_bits_to_f32(bits), T);
+                packed |= q << (4 * (i ^ 1));
+            }
+            *reinterpret_cast<uint32_t*>(codes + (b0 + bl) * (kBlock / 2) + sub * 4) = packed;
+        }
+    }
+}
+
+// nf4_dequantize_kernel: 256 lanes x 8 weights = 32 blocks per workgroup.
+//   a_hat = fl32(fl32(a2/255) * q8), w_hat = RNE_bf16(fl32(a_hat * c_code)).
+__global__ __launch_bounds__(kThreads) void nf4_dequantize_kernel(const uint8_t* __restrict__ codes,
+                                                                  const uint8_t* __restrict__ q8,
+                                                                  const float* __restrict__ a2,
+                                                                  int64_t nblocks,
+                                                                  uint16_t* __restrict__ out) {
+    __shared__ float s_c[16];
+    const int tid = threadIdx.x;
+    if (tid < 16) s_c[tid] = nf4_level(tid);
+    __syncthreads();
+    const int64_t b = (int64_t)blockIdx.x * 32 + (tid >> 3);
+    const int sub = tid & 7;
+    if (b >= nblocks) return;
+    const float step = __fdiv_rn(a2[b / kSuper], 255.0f);
+    const float ahat = __fmul_rn(step, (float)q8[b]);
+    const uint32_t pk = *reinterpret_cast<const uint32_t*>(codes + b * (kBlock / 2) + sub * 4);
+    u32x4_t o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t byte = (pk >> (8 * j)) & 0xFFu;
+        const float w0 = __fmul_rn(ahat, s_c[byte >> 4]);
+        const float w1 = __fmul_rn(ahat, s_c[byte & 0xFu]);
+        o[j] = pack_bf16x2(w0, w1);
+    }
+    *reinterpret_cast<u32x4_t*>(out + b * kBlock + sub * 8) = o;
+}
+
+}  // namespace
+
+qlora_status launch_quantize(const uint16_t* W, int64_t nblocks, uint8_t* codes, uint8_t* q8, float* a2,
+                             hipStream_t s) {
+    const int64_t groups = (nblocks + kSuper - 1) / kSuper;
+    hipLaunchKernelGGL(nf4_quantize_kernel, dim3((unsigned)groups), dim3(kThreads), 0, s, W, nblocks, codes,
+                       q8, a2);
+    return launch_status();
+}
+
+qlora_status launch_dequantize(const uint8_t* codes, const uint8_t* q8, const float* a2, int64_t nblocks,
+                               uint16_t* out, hipStream_t s) {
+    const int64_t grid = (nblocks + 31) / 32;
+    hipLaunchKernelGGL(nf4_dequantize_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, codes, q8, a2,
+                       nblocks, out);
+    return launch_status();
+}
+
+}  // namespace qlora

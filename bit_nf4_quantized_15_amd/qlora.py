@@ -1,0 +1,198 @@
+"""Thin ctypes binding over libqlora.so (include/qlora.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream; every step of the computation runs in the library's HIP kernels.
+Importing this module loads the library and raises ImportError when it has not
+been built (python -m bit_nf4_quantized_15_amd.build); there is no fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqlora.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "qlora.h")
+
+BLOCK = 64
+SUPER = 256
+
+c_i64 = ctypes.c_int64
+c_vp = ctypes.c_void_p
+c_sz = ctypes.c_size_t
+
+
+class NF4State(ctypes.Structure):
+    """Mirror of struct qlora_nf4."""
+    _fields_ = [("codes", c_vp), ("q8", c_vp), ("a2", c_vp), ("n", c_i64), ("k", c_i64)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m bit_nf4_quantized_15_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(NF4State)
+    sig = {
+        "qlora_version": (ctypes.c_int, []),
+        "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "qlora_nf4_sizes": (ctypes.c_int, [c_i64, c_i64, ctypes.POINTER(c_sz), ctypes.POINTER(c_sz),
+                                           ctypes.POINTER(c_sz)]),
+        "qlora_quantize": (ctypes.c_int, [c_vp, c_i64, c_i64, P, c_vp]),
+        "qlora_dequantize": (ctypes.c_int, [P, c_vp, c_vp]),
+        "qlora_fwd_workspace": (c_sz, [c_i64, c_i64, c_i64, ctypes.c_int]),
+        "qlora_linear_fwd": (ctypes.c_int, [P, c_vp, c_i64, c_vp, c_vp, ctypes.c_int, ctypes.c_float,
+                                            c_vp, c_vp, c_vp, c_sz, c_vp]),
+        "qlora_bwd_workspace": (c_sz, [c_i64, c_i64, c_i64, ctypes.c_int]),
+        "qlora_linear_bwd": (ctypes.c_int, [P, c_vp, c_i64, c_vp, c_vp, ctypes.c_int, ctypes.c_float,
+                                            c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name, None)
+        if fn is None:
+            continue
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class QLoraError(RuntimeError):
+    def __init__(self, status, where):
+        msg = lib.qlora_status_string(status).decode()
+        super().__init__(f"{where}: status {status} ({msg})")
+        self.status = status
+
+
+def _check(status, where):
+    if status != 0:
+        raise QLoraError(status, where)
+
+
+def _stream():
+    return c_vp(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else c_vp(t.data_ptr())
+
+
+def _dev(t, dtype, name, shape=None):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name}: must be a contiguous device tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def sizes(N, K):
+    """(codes bytes, q8 bytes, a2 bytes) of an [N, K] quantized weight."""
+    cb, qb, ab = c_sz(), c_sz(), c_sz()
+    _check(lib.qlora_nf4_sizes(N, K, ctypes.byref(cb), ctypes.byref(qb), ctypes.byref(ab)), "qlora_nf4_sizes")
+    return cb.value, qb.value, ab.value
+
+
+class NF4Weight:
+    """Device-resident quantized weight: codes / q8 (uint8) and a2 (float32) tensors."""
+
+    def __init__(self, codes, q8, a2, N, K):
+        self.codes, self.q8, self.a2, self.N, self.K = codes, q8, a2, int(N), int(K)
+
+    @classmethod
+    def empty(cls, N, K, device="cuda"):
+        cb, qb, ab = sizes(N, K)
+        return cls(torch.empty(cb, dtype=torch.uint8, device=device),
+                   torch.empty(qb, dtype=torch.uint8, device=device),
+                   torch.empty(ab // 4, dtype=torch.float32, device=device), N, K)
+
+    def state(self):
+        return NF4State(self.codes.data_ptr(), self.q8.data_ptr(), self.a2.data_ptr(), self.N, self.K)
+
+
+def quantize(W, out=None):
+    """NF4 + double-quant of a bf16 [N, K] device weight (qlora_quantize)."""
+    N, K = W.shape
+    _dev(W, torch.bfloat16, "W")
+    w = NF4Weight.empty(N, K, W.device) if out is None else out
+    st = w.state()
+    _check(lib.qlora_quantize(_ptr(W), N, K, ctypes.byref(st), _stream()), "qlora_quantize")
+    return w
+
+
+def dequantize(w, out=None):
+    """bf16 [N, K] reconstruction (qlora_dequantize); tests and export only."""
+    o = torch.empty((w.N, w.K), dtype=torch.bfloat16, device=w.codes.device) if out is None else out
+    _dev(o, torch.bfloat16, "out", (w.N, w.K))
+    st = w.state()
+    _check(lib.qlora_dequantize(ctypes.byref(st), _ptr(o), _stream()), "qlora_dequantize")
+    return o
+
+
+def fwd_workspace(M, N, K, r):
+    return int(lib.qlora_fwd_workspace(M, N, K, r))
+
+
+def bwd_workspace(M, N, K, r):
+    return int(lib.qlora_bwd_workspace(M, N, K, r))
+
+
+def _ws(nbytes, device, ws):
+    if nbytes == 0:
+        return None, 0
+    if ws is not None and ws.numel() >= nbytes:
+        return ws, ws.numel()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def linear_fwd(w, x, A, B, alpha, y=None, t=None, want_t=True, ws=None):
+    """y = x W_hat + (alpha/r)(x A) B (qlora_linear_fwd).  Returns (y, t or None)."""
+    M, K = x.shape
+    r = A.shape[1]
+    _dev(x, torch.bfloat16, "x", (M, w.K))
+    _dev(A, torch.bfloat16, "A", (w.K, r))
+    _dev(B, torch.bfloat16, "B", (r, w.N))
+    dev = x.device
+    y = torch.empty((M, w.N), dtype=torch.bfloat16, device=dev) if y is None else _dev(y, torch.bfloat16, "y", (M, w.N))
+    if want_t and t is None:
+        t = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
+    if t is not None:
+        _dev(t, torch.bfloat16, "t", (M, r))
+    wsb, wsn = _ws(fwd_workspace(M, w.N, w.K, r), dev, ws)
+    st = w.state()
+    _check(lib.qlora_linear_fwd(ctypes.byref(st), _ptr(x), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(y),
+                                _ptr(t), _ptr(wsb), wsn, _stream()), "qlora_linear_fwd")
+    return y, t
+
+
+def linear_bwd(w, x, A, B, alpha, dy, t=None, need_dx=True, dx=None, dA=None, dB=None, ws=None):
+    """(dx, dA, dB) of the layer for upstream dy (qlora_linear_bwd); dx is None when not needed."""
+    M, K = x.shape
+    r = A.shape[1]
+    _dev(x, torch.bfloat16, "x", (M, w.K))
+    _dev(A, torch.bfloat16, "A", (w.K, r))
+    _dev(B, torch.bfloat16, "B", (r, w.N))
+    _dev(dy, torch.bfloat16, "dy", (M, w.N))
+    if t is not None:
+        _dev(t, torch.bfloat16, "t", (M, r))
+    dev = x.device
+    if need_dx and dx is None:
+        dx = torch.empty((M, w.K), dtype=torch.bfloat16, device=dev)
+    dA = torch.empty((w.K, r), dtype=torch.float32, device=dev) if dA is None else _dev(dA, torch.float32, "dA", (w.K, r))
+    dB = torch.empty((r, w.N), dtype=torch.float32, device=dev) if dB is None else _dev(dB, torch.float32, "dB", (r, w.N))
+    wsb, wsn = _ws(bwd_workspace(M, w.N, w.K, r), dev, ws)
+    st = w.state()
+    _check(lib.qlora_linear_bwd(ctypes.byref(st), _ptr(x), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(t),
+                                _ptr(dy), _ptr(dx) if need_dx else None, _ptr(dA), _ptr(dB), _ptr(wsb), wsn,
+                                _stream()), "qlora_linear_bwd")
+    return (dx if need_dx else None), dA, dB
+
+
+def declared_symbols():
+    """Function names declared in include/qlora.h (for the export check)."""
+    import re
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))

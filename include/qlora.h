@@ -1,0 +1,131 @@
+/*
+ * qlora.h -- C ABI of the NF4 frozen-base linear layer with a LoRA branch,
+ * hand-written HIP kernels for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes (web pages on QLoRA / NF4 / bitsandbytes):
+ *  - "bitsandbytes deep dive" (aicoding.csdn.net), section 5.2: blockwise
+ *    absmax 4-bit encoding, a = max|w| per block of 64, q = argmin_j |w/a - c_j|,
+ *    w_hat = a * c_q, two 4-bit codes per byte;
+ *  - same page, section 6.2: the 16 NF4 levels c_j (normal quantiles,
+ *    normalised to [-1, 1], asymmetric, exact 0);
+ *  - same page, section 7.2: double quantization -- the block absmax values
+ *    are stored as 8-bit codes, with one fp32 scale per 256 blocks;
+ *  - same page, sections 8.6 / 12.4, and "LoRA, QLoRA, QA-LoRA explained"
+ *    (ludovicoyin.github.io), section 2: y = x dequant(W4) + (alpha/r) x A B
+ *    with the dequantization fused into the matrix product, frozen base.
+ *
+ * Conventions shared by every entry point
+ *  - Weight storage is the nn.Linear layout [N = Dout, K = Din], row-major,
+ *    flattened row-major into blocks of 64 consecutive elements (K % 64 == 0,
+ *    so no block straddles a row).  Block b covers flat elements
+ *    [64 b, 64 b + 64); scale group S covers blocks [256 S, 256 S + 256), the
+ *    last group may be short and groups may straddle rows.
+ *  - Packed codes: element 2i in bits 7..4 and element 2i+1 in bits 3..0 of
+ *    byte i.
+ *  - bf16 tensors are passed as uint16_t bit patterns; every matrix is dense
+ *    row-major with no padding; all tensor pointers are DEVICE pointers,
+ *    16-byte aligned, owned by the caller.  The library allocates nothing and
+ *    keeps no mutable global state.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every compute call
+ *    only validates and enqueues: a return of QLORA_OK means the kernels were
+ *    launched, not that they finished.  Inputs must be finite.
+ *  - Errors: invalid arguments are reported before anything is launched and
+ *    leave every output untouched.  No C++ exception crosses the ABI.
+ *  - Reentrant; calls on different streams may run concurrently as long as
+ *    they do not share output or workspace buffers.
+ */
+#ifndef QLORA_H
+#define QLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qlora_status {
+    QLORA_OK = 0,
+    QLORA_ERR_INVALID_ARG = -1,       /* null pointer, negative size, r or alpha out of range */
+    QLORA_ERR_UNSUPPORTED_SHAPE = -2, /* K % 64 != 0, sizes beyond the supported range */
+    QLORA_ERR_MISALIGNED = -3,        /* a tensor pointer is not 16-byte aligned */
+    QLORA_ERR_WORKSPACE = -4,         /* workspace missing or smaller than required */
+    QLORA_ERR_HIP = -5                /* a HIP launch error was reported */
+} qlora_status;
+
+/* Quantized weight: three flat device arrays plus the logical shape.  This is
+ * the "quantization state" the deep dive (section 5.2) says is kept next to
+ * the codes: codes, first-level 8-bit scale codes, second-level fp32 scales. */
+typedef struct qlora_nf4 {
+    uint8_t* codes; /* [N*K/2]            packed 4-bit NF4 codes                     */
+    uint8_t* q8;    /* [N*K/64]           8-bit code of each block's absmax          */
+    float* a2;      /* [ceil(N*K/16384)]  fp32 absmax of each group of 256 absmaxes  */
+    int64_t n;      /* N = Dout (rows of the stored weight)                          */
+    int64_t k;      /* K = Din, a multiple of 64                                     */
+} qlora_nf4;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int qlora_version(void);
+
+/* Static English text for a status code (never NULL). */
+const char* qlora_status_string(int status);
+
+/* Byte sizes of the three arrays of an [N, K] quantized weight:
+ *   codes N*K/2, q8 N*K/64, a2 4*ceil(N*K/16384)
+ * (deep dive 7.2: 4 + 8/64 + 32/(64*256) bits per weight).  Any output
+ * pointer may be NULL.  Errors: N < 1 or K < 1 -> INVALID_ARG, K % 64 -> UNSUPPORTED_SHAPE. */
+qlora_status qlora_nf4_sizes(int64_t N, int64_t K, size_t* codes_bytes, size_t* q8_bytes,
+                             size_t* a2_bytes);
+
+/* Quantize a bf16 weight W [N, K] into `out` (deep dive 5.2 and 7.2).
+ *   a_b  = max |w| over block b
+ *   code = argmin_j |w/a_b - c_j| in exact arithmetic, ties to the lower j;
+ *          a_b = 0 gives the zero code 7
+ *   a2_S = max of a_b over group S
+ *   q8_b = argmin_k |a_b/a2_S - k/255| over k = 0..255, ties to the lower k
+ * out->codes/q8/a2 must hold qlora_nf4_sizes() bytes; out->n/k must equal N/K.
+ * Codes are computed against the true a_b, not its 8-bit reconstruction. */
+qlora_status qlora_quantize(const uint16_t* W, int64_t N, int64_t K, const qlora_nf4* out,
+                            void* stream);
+
+/* Dequantize to bf16 out [N, K] (deep dive 5.2: w_hat = a * c_q):
+ *   a_hat = fl32( fl32(a2_S / 255) * q8_b ),  out = RNE_bf16( fl32(a_hat * c_code) ).
+ * For tests and export only: the linear layer never materialises W. */
+qlora_status qlora_dequantize(const qlora_nf4* w, uint16_t* out, void* stream);
+
+/* Workspace bytes qlora_linear_fwd needs for these sizes (0 if none). */
+size_t qlora_fwd_workspace(int64_t M, int64_t N, int64_t K, int r);
+
+/* Fused forward of the frozen NF4 linear with its LoRA branch
+ * (deep dive 12.4; explained, section 2):
+ *   t = s * (x A)            [M, r]  bf16, s = alpha / r
+ *   y = x W_hat + t B        [M, N]  bf16, W_hat = [K, N] view of dequant(w)
+ * x [M, K] bf16, A [K, r] bf16, B [r, N] bf16.  The products accumulate in
+ * fp32; W_hat is dequantized inside the kernels (registers / LDS tiles) and is
+ * never written to memory.  t_out (nullable) receives t for the backward.
+ * 1 <= r <= 128, M >= 0 (M = 0 is a no-op), alpha finite.  ws may be NULL when
+ * qlora_fwd_workspace() returns 0. */
+qlora_status qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uint16_t* A,
+                              const uint16_t* B, int r, float alpha, uint16_t* y, uint16_t* t_out,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes qlora_linear_bwd needs for these sizes. */
+size_t qlora_bwd_workspace(int64_t M, int64_t N, int64_t K, int r);
+
+/* Backward of the same layer for an upstream gradient dy [M, N] bf16.  The
+ * base weight is frozen (deep dive 12.4): there is no dW.  By the chain rule:
+ *   u  = s * (dy B^T)           [M, r]   (internal, workspace)
+ *   dx = dy W_hat^T + u A^T     [M, K]   bf16 (skipped when dx == NULL)
+ *   dA = x^T u                  [K, r]   fp32, overwritten
+ *   dB = t^T dy                 [r, N]   fp32, overwritten
+ * t is the forward's t_out (nullable: then it is recomputed from x and A). */
+qlora_status qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uint16_t* A,
+                              const uint16_t* B, int r, float alpha, const uint16_t* t,
+                              const uint16_t* dy, uint16_t* dx, float* dA, float* dB, void* ws,
+                              size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_H */

@@ -1,0 +1,118 @@
+"""Parity of qlora_quantize / qlora_dequantize (HIP) with the CPU oracle.
+
+Bar: packed codes, q8, a2 and the dequantized bf16 weight bit-exact.
+Small cases run the full oracle; the full-size weights of every workload are
+checked completely when the oracle finishes in seconds and on sampled scale
+groups otherwise (the oracle quantizes those groups on its own).
+"""
+import numpy as np
+import pytest
+
+from oracle import bf16, nf4
+from bit_nf4_quantized_15_amd import workloads
+
+from gpu_util import dev_bf16, host_bits, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q():
+    from bit_nf4_quantized_15_amd import qlora
+    return qlora
+
+
+def _gpu_quant(q, W):
+    w = q.quantize(dev_bf16(W))
+    wh = q.dequantize(w)
+    import torch
+    torch.cuda.synchronize()
+    return (w.codes.cpu().numpy(), w.q8.cpu().numpy(), w.a2.cpu().numpy(), host_bits(wh))
+
+
+def _check_full(q, W, tag):
+    N, K = W.shape
+    say(f"[quantize] {tag} N={N} K={K}")
+    codes, q8, a2, wh = _gpu_quant(q, W)
+    rc, rq, ra = nf4.quantize(W)
+    assert np.array_equal(codes, rc), f"{tag}: codes differ at {np.flatnonzero(codes != rc)[:8]}"
+    assert np.array_equal(q8, rq), f"{tag}: q8 differ at {np.flatnonzero(q8 != rq)[:8]}"
+    assert np.array_equal(a2.view(np.uint32), ra.view(np.uint32)), f"{tag}: a2 differ"
+    rwh = nf4.dequantize(rc, rq, ra, N, K)
+    assert np.array_equal(wh, rwh), f"{tag}: dequant differs at {np.flatnonzero(wh != rwh)[:8]}"
+
+
+def test_c1_linear_256(q):
+    _check_full(q, workloads.weight(1), "c1")
+
+
+def test_c2_q_proj_with_outliers(q):
+    _check_full(q, workloads.weight(2), "c2")
+
+
+@pytest.mark.parametrize("N,K", [(1, 64), (3, 192), (5, 640), (257, 64), (64, 11008), (7, 16384 + 64)])
+def test_ragged_shapes(q, N, K):
+    """Block counts that are not a multiple of 256 (short last group, groups straddling rows)."""
+    _check_full(q, workloads.custom(100 + N + K, (N, K), 0.02), f"ragged {N}x{K}")
+
+
+def test_edge_blocks(q):
+    """All-zero block and group, +-0, absmax with both signs, values on levels, subnormal
+    and huge scales, planted q8 ties (a2 = 510, a odd), a block whose q8 is 0."""
+    rng = np.random.default_rng(1234)
+    K = 64 * 8
+    # row 0: assorted blocks
+    r0 = rng.standard_normal(K).astype(np.float32) * 0.02
+    r0[0:64] = 0.0                                          # all-zero block
+    r0[64:128] = -0.0
+    r0[64 + 3] = 0.0
+    r0[128 + 5], r0[128 + 9] = 0.5, -0.5                   # absmax with both signs
+    lv = np.array([float(v) for v in nf4.nf4_table()], np.float32)
+    r0[192:208] = lv * 4.0                                  # exactly on the levels, a = 4
+    r0[256:320] = (rng.standard_normal(64) * 1e-39).astype(np.float32)   # subnormal weights
+    r0[320:384] = (rng.standard_normal(64) * 1e36).astype(np.float32)
+    r0[384:448] = 1e-30                                     # q8 = 0 against the 1e36 group max
+    # row 1: q8 ties: one block with a = 510, blocks with odd a <= 255
+    r1 = np.zeros(K, np.float32)
+    r1[0] = 510.0
+    for j, a in enumerate([1.0, 3.0, 5.0, 101.0, 255.0, 127.0, 63.0]):
+        r1[64 * (j + 1)] = a
+        r1[64 * (j + 1) + 1] = -a / 3
+    # group layout (K = 512: 8 blocks per row, 32 rows per group of 256 blocks):
+    # group 0 = row 0 + filler, group 1 = the q8-tie row + zeros (max 510),
+    # group 2 = all zero, then a short last group of filler
+    filler = bf16.to_f32(workloads.custom(55, (36, K), 0.02))
+    W = np.concatenate([r0[None, :], filler[:31], r1[None, :], np.zeros((31, K), np.float32),
+                        np.zeros((32, K), np.float32), filler[31:]], axis=0)
+    W = bf16.from_f32_rne(W)
+    _check_full(q, W, "edge blocks")
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_full_size_workloads(q, cfg):
+    for li, (name, N, K) in enumerate(workloads.CONFIGS[cfg]["layers"]):
+        if cfg == 4 and li not in (0, 4, 6):                 # q, gate, down cover every shape
+            continue
+        _check_full(q, workloads.weight(cfg, li), f"c{cfg} {name}")
+
+
+@pytest.mark.slow
+def test_c5_sampled_groups(q):
+    """70B-like MLP weights (235M weights each): every group's a2, then sampled groups bit-exact."""
+    import torch
+    rng = np.random.default_rng(7)
+    for li, (name, N, K) in enumerate(workloads.CONFIGS[5]["layers"]):
+        say(f"[quantize] c5 {name} N={N} K={K} (sampled)")
+        W = workloads.weight(5, li)
+        w = q.quantize(dev_bf16(W))
+        torch.cuda.synchronize()
+        codes = w.codes.cpu().numpy(); q8 = w.q8.cpu().numpy(); a2 = w.a2.cpu().numpy()
+        flat = W.reshape(-1)
+        ngroups = a2.size
+        for g in rng.choice(ngroups, 24, replace=False):
+            seg = flat[g * 16384:(g + 1) * 16384].reshape(1, -1)
+            rc, rq, ra = nf4.quantize(seg)
+            assert np.array_equal(codes[g * 8192:(g + 1) * 8192], rc), f"{name} group {g}"
+            assert np.array_equal(q8[g * 256:(g + 1) * 256], rq)
+            assert a2[g] == ra[0]
+        del w
