@@ -1,8 +1,11 @@
 // C ABI of libqlora: argument validation and dispatch (declared in include/qlora.h).
+#include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdint>
 
 #include "common.h"
+#include "lora_plan.h"
 
 using namespace qlora;
 
@@ -18,6 +21,44 @@ inline qlora_status check_state(const qlora_nf4* w) {
     if (!aligned16(w->codes) || !aligned16(w->q8) || !aligned16(w->a2)) return QLORA_ERR_MISALIGNED;
     return QLORA_OK;
 }
+
+inline bool bad_dims(int64_t M, int64_t N, int64_t K, int r) {
+    return M < 0 || N < 1 || K < 1 || r < 1 || r > 128 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX;
+}
+
+// Workspace carve-up.  Every piece starts on a 256-byte boundary.
+struct FwdWs {
+    size_t at, part, tbuf, total;
+};
+inline FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int r) {
+    (void)N;
+    FwdWs w{};
+    const SplitPlan sp = plan_nt(M, K);
+    w.at = 0;
+    w.part = w.at + align256((size_t)r * K * 2);
+    w.tbuf = w.part + align256((size_t)sp.splits * M * r * 4);
+    w.total = w.tbuf + align256((size_t)M * r * 2);
+    return w;
+}
+
+struct BwdWs {
+    size_t u, part, at, tbuf, pa, pb, total;
+};
+inline BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int r) {
+    BwdWs w{};
+    const SplitPlan su = plan_nt(M, N), st = plan_nt(M, K);
+    const SplitPlan sa = plan_tn(M, K, r), sb = plan_tn(M, r, N);
+    w.u = 0;
+    w.part = w.u + align256((size_t)M * r * 2);
+    w.at = w.part + align256((size_t)std::max(su.splits, st.splits) * M * r * 4);
+    w.tbuf = w.at + align256((size_t)r * K * 2);
+    w.pa = w.tbuf + align256((size_t)M * r * 2);
+    w.pb = w.pa + align256((size_t)sa.splits * K * r * 4);
+    w.total = w.pb + align256((size_t)sb.splits * r * N * 4);
+    return w;
+}
+
+inline uint8_t* at(void* ws, size_t off) { return static_cast<uint8_t*>(ws) + off; }
 
 }  // namespace
 
@@ -62,6 +103,82 @@ qlora_status qlora_dequantize(const qlora_nf4* w, uint16_t* out, void* stream) {
     if (!out) return QLORA_ERR_INVALID_ARG;
     if (!aligned16(out)) return QLORA_ERR_MISALIGNED;
     return launch_dequantize(w->codes, w->q8, w->a2, w->n * w->k / kBlock, out, (hipStream_t)stream);
+}
+
+size_t qlora_fwd_workspace(int64_t M, int64_t N, int64_t K, int r) {
+    if (bad_dims(M, N, K, r) || M == 0 || K % kBlock) return 0;
+    return fwd_ws(M, N, K, r).total;
+}
+
+size_t qlora_bwd_workspace(int64_t M, int64_t N, int64_t K, int r) {
+    if (bad_dims(M, N, K, r) || M == 0 || K % kBlock) return 0;
+    return bwd_ws(M, N, K, r).total;
+}
+
+qlora_status qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
+                              int r, float alpha, uint16_t* y, uint16_t* t_out, void* ws, size_t ws_bytes,
+                              void* stream) {
+    qlora_status st = check_state(w);
+    if (st != QLORA_OK) return st;
+    const int64_t N = w->n, K = w->k;
+    if (bad_dims(M, N, K, r) || !std::isfinite(alpha)) return QLORA_ERR_INVALID_ARG;
+    if (M == 0) return QLORA_OK;
+    if (!x || !A || !B || !y) return QLORA_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(y) || (t_out && !aligned16(t_out)))
+        return QLORA_ERR_MISALIGNED;
+    const FwdWs L = fwd_ws(M, N, K, r);
+    if (!ws || ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
+    if (!aligned16(ws)) return QLORA_ERR_MISALIGNED;
+    hipStream_t s = (hipStream_t)stream;
+    const float scale = alpha / (float)r;
+    uint16_t* At = reinterpret_cast<uint16_t*>(at(ws, L.at));
+    float* part = reinterpret_cast<float*>(at(ws, L.part));
+    uint16_t* t = t_out ? t_out : reinterpret_cast<uint16_t*>(at(ws, L.tbuf));
+    if ((st = launch_transpose(A, At, (int)K, r, s)) != QLORA_OK) return st;
+    if ((st = launch_nt(x, At, part, t, scale, (int)M, (int)K, r, s)) != QLORA_OK) return st;
+    return launch_gemm_fwd(x, w->codes, w->q8, w->a2, t, B, y, (int)M, (int)N, (int)K, r, s);
+}
+
+qlora_status qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
+                              int r, float alpha, const uint16_t* t, const uint16_t* dy, uint16_t* dx, float* dA,
+                              float* dB, void* ws, size_t ws_bytes, void* stream) {
+    qlora_status st = check_state(w);
+    if (st != QLORA_OK) return st;
+    const int64_t N = w->n, K = w->k;
+    if (bad_dims(M, N, K, r) || !std::isfinite(alpha)) return QLORA_ERR_INVALID_ARG;
+    if (!dA || !dB) return QLORA_ERR_INVALID_ARG;
+    if (!aligned16(dA) || !aligned16(dB)) return QLORA_ERR_MISALIGNED;
+    hipStream_t s = (hipStream_t)stream;
+    if (M == 0) {  // empty sums
+        if ((st = launch_fill(dA, K * r, 0.0f, s)) != QLORA_OK) return st;
+        return launch_fill(dB, (int64_t)r * N, 0.0f, s);
+    }
+    if (!x || !A || !B || !dy) return QLORA_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(dy) || (t && !aligned16(t)) ||
+        (dx && !aligned16(dx)))
+        return QLORA_ERR_MISALIGNED;
+    const BwdWs L = bwd_ws(M, N, K, r);
+    if (!ws || ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
+    if (!aligned16(ws)) return QLORA_ERR_MISALIGNED;
+    const float scale = alpha / (float)r;
+    uint16_t* u = reinterpret_cast<uint16_t*>(at(ws, L.u));
+    float* part = reinterpret_cast<float*>(at(ws, L.part));
+    // u = s dy B^T  (B [r, N] is already the row-major transpose the kernel wants)
+    if ((st = launch_nt(dy, B, part, u, scale, (int)M, (int)N, r, s)) != QLORA_OK) return st;
+    if (!t) {  // recompute t = s x A
+        uint16_t* At = reinterpret_cast<uint16_t*>(at(ws, L.at));
+        uint16_t* tb = reinterpret_cast<uint16_t*>(at(ws, L.tbuf));
+        if ((st = launch_transpose(A, At, (int)K, r, s)) != QLORA_OK) return st;
+        if ((st = launch_nt(x, At, part, tb, scale, (int)M, (int)K, r, s)) != QLORA_OK) return st;
+        t = tb;
+    }
+    if (dx) {
+        if ((st = launch_gemm_bwd_dx(dy, w->codes, w->q8, w->a2, u, A, dx, (int)M, (int)N, (int)K, r, s)) != QLORA_OK)
+            return st;
+    }
+    if ((st = launch_tn(x, u, reinterpret_cast<float*>(at(ws, L.pa)), dA, (int)M, (int)K, r, s)) != QLORA_OK)
+        return st;
+    return launch_tn(t, dy, reinterpret_cast<float*>(at(ws, L.pb)), dB, (int)M, r, (int)N, s);
 }
 
 }  // extern "C"

@@ -61,5 +61,17 @@ qlora_status launch_quantize(const uint16_t* W, int64_t nblocks, uint8_t* codes,
                              hipStream_t s);
 qlora_status launch_dequantize(const uint8_t* codes, const uint8_t* q8, const float* a2, int64_t nblocks,
                                uint16_t* out, hipStream_t s);
+qlora_status launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* q8, const float* a2,
+                             const uint16_t* t, const uint16_t* B, uint16_t* y, int M, int N, int K, int r,
+                             hipStream_t s);
+qlora_status launch_gemm_bwd_dx(const uint16_t* dy, const uint8_t* codes, const uint8_t* q8, const float* a2,
+                                const uint16_t* u, const uint16_t* A, uint16_t* dx, int M, int N, int K, int r,
+                                hipStream_t s);
+qlora_status launch_transpose(const uint16_t* A, uint16_t* At, int K, int r, hipStream_t s);
+qlora_status launch_nt(const uint16_t* X, const uint16_t* Yt, float* part, uint16_t* out, float scale, int M, int C,
+                       int r, hipStream_t s);
+qlora_status launch_tn(const uint16_t* P, const uint16_t* Q, float* part, float* out, int M, int Pd, int Qd,
+                       hipStream_t s);
+qlora_status launch_fill(float* out, int64_t count, float v, hipStream_t s);
 
 }  // namespace qlora

@@ -1,0 +1,407 @@
+// Fused NF4-dequant GEMMs on MFMA (v_mfma_f32_32x32x16_bf16), gfx950.
+//
+// Forward  y[m,n]  = sum_k x[m,k] w_hat[n,k] + sum_j t[m,j] B[j,n]
+// Backward dx[m,k] = sum_n dy[m,n] w_hat[n,k] + sum_j u[m,j] A[k,j]
+// ("bitsandbytes deep dive" 8.6 and 12.4: 4-bit storage, 16-bit compute, the
+// full-precision weight is restored tile by tile and never held in memory;
+// the LoRA up-projection is the same product continued over r extra
+// reduction steps with operands [t | B] resp. [u | A^T]).
+//
+// Both kernels: 256 lanes (4 waves), output tile 256 x 256, reduction step 64
+// (one NF4 block).  The activation tile (256 rows x 64) goes HBM -> registers
+// -> LDS (double buffered, XOR-swizzled); every wave reads all 256 rows of it.
+//  * forward: wave w owns output columns [64w, 64w+64).  Each lane loads the
+//    16 bytes of packed codes it needs straight into registers, builds the
+//    block's 16-entry bf16 table and expands its codes with v_perm_b32 into
+//    MFMA B operands: the dequantized weight never touches LDS or HBM.
+//  * backward: the reduction runs over n, across rows of the stored codes, so
+//    the weight tile is dequantized cooperatively (lane = one row x one block)
+//    and scattered transposed into a second LDS tile that the MFMA reads like
+//    the activation tile.
+// Accumulation is fp32; outputs are rounded to bf16 (nearest even).
+#include "common.h"
+#include "dequant_tile.h"
+
+namespace qlora {
+namespace {
+
+constexpr int kT = 256;             // lanes per workgroup
+constexpr int kTM = 256;            // output rows per tile
+constexpr int kTN = 256;            // output columns per tile
+constexpr int kTK = 64;             // reduction step
+constexpr int kTileBytes = kTM * kTK * 2;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ f32x16_t mfma32(bf16x8 a, bf16x8 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Map a linear workgroup id to a tile id so that the workgroups placed on one
+// XCD (ids are dealt round-robin over the 8 XCDs) get a contiguous run of
+// tiles, i.e. share activation rows and weight columns in that XCD's L2.
+__device__ __forceinline__ int xcd_tile(int bid, int total) {
+    const int xcd = bid & 7, idx = bid >> 3;
+    const int per = total >> 3, rem = total & 7;
+    return xcd * per + min(xcd, rem) + idx;
+}
+
+// ---- activation tile loader: rows [row0, row0+256) x cols [col0, col0+64) of a
+// row-major bf16 matrix with leading dimension ld; rows >= nrows and columns >=
+// ncols read as 0.  Lane tid covers row tid/8 + 32p, chunk tid%8 (p = 0..7).
+// VEC: ld % 8 == 0 and the base is 16-byte aligned, so whole chunks can be read.
+template <bool VEC>
+__device__ __forceinline__ void load_tile(u32x4_t (&r)[8], const uint16_t* __restrict__ src, int64_t ld,
+                                          int row0, int nrows, int col0, int ncols, int tid) {
+    const int lr = tid >> 3, lc = tid & 7;
+    const int col = col0 + lc * 8;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int row = row0 + lr + 32 * p;
+        if (VEC) {
+            if (row < nrows && col < ncols) {
+                r[p] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)row * ld + col);
+            } else {
+                r[p] = u32x4_t{0u, 0u, 0u, 0u};
+            }
+        } else {
+            uint32_t w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c0 = col + 2 * i;
+                uint32_t lo = 0, hi = 0;
+                if (row < nrows && c0 < ncols) lo = src[(int64_t)row * ld + c0];
+                if (row < nrows && c0 + 1 < ncols) hi = src[(int64_t)row * ld + c0 + 1];
+                w[i] = lo | (hi << 16);
+            }
+            r[p] = u32x4_t{w[0], w[1], w[2], w[3]};
+        }
+    }
+}
+
+__device__ __forceinline__ void store_tile(uint8_t* lds, const u32x4_t (&r)[8], int tid) {
+    const int lr = tid >> 3, lc = tid & 7;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) *reinterpret_cast<u32x4_t*>(lds + tile_off(lr + 32 * p, lc)) = r[p];
+}
+
+__device__ __forceinline__ bf16x8 lds_operand(const uint8_t* lds, int row, int chunk) {
+    return *reinterpret_cast<const bf16x8*>(lds + tile_off(row, chunk));
+}
+
+// 8 bf16 from a strided column: src[(j0 + i) * ld + col], i = 0..7, zero when
+// j0 + i >= jmax or col is out of range.
+__device__ __forceinline__ bf16x8 gather8(const uint16_t* __restrict__ src, int64_t ld, int j0, int jmax, int col,
+                                         bool col_ok) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ja = j0 + 2 * i, jb = ja + 1;
+        const uint32_t lo = (col_ok && ja < jmax) ? src[(int64_t)ja * ld + col] : 0u;
+        const uint32_t hi = (col_ok && jb < jmax) ? src[(int64_t)jb * ld + col] : 0u;
+        w[i] = lo | (hi << 16);
+    }
+    return as_bf16x8(u32x4_t{w[0], w[1], w[2], w[3]});
+}
+
+// 8 contiguous bf16 src[row * ld + j0 .. +7], zero past jmax or an invalid row.
+__device__ __forceinline__ bf16x8 row8(const uint16_t* __restrict__ src, int64_t ld, int row, bool row_ok, int j0,
+                                      int jmax) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ja = j0 + 2 * i, jb = ja + 1;
+        const uint32_t lo = (row_ok && ja < jmax) ? src[(int64_t)row * ld + ja] : 0u;
+        const uint32_t hi = (row_ok && jb < jmax) ? src[(int64_t)row * ld + jb] : 0u;
+        w[i] = lo | (hi << 16);
+    }
+    return as_bf16x8(u32x4_t{w[0], w[1], w[2], w[3]});
+}
+
+// Store an fp32 accumulator tile (this wave: 8 x 32-row tiles times 2 x 32-col
+// tiles) as bf16.  Lane l of a 32x32 tile holds column l%32 and rows
+// 8*(v/4) + 4*(l/32) + v%4 for v = 0..15.
+__device__ __forceinline__ void store_acc(uint16_t* __restrict__ out, int64_t ld, const f32x16_t (&acc)[8][2],
+                                          int m0, int M, const int (&col)[2], const bool (&col_ok)[2], int h) {
+    const int l32 = threadIdx.x & 31;
+    (void)l32;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            if (!col_ok[t]) continue;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int m = m0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+                if (m < M) out[(int64_t)m * ld + col[t]] = (uint16_t)(pack_bf16x2(acc[i][t][v], 0.0f) & 0xFFFFu);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ forward
+template <bool XVEC>
+__global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ q8,
+    const float* __restrict__ a2, const uint16_t* __restrict__ t, const uint16_t* __restrict__ Bl,
+    uint16_t* __restrict__ y, int M, int N, int K, int r, int tiles_m, int tiles_n) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kTileBytes];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h = lane >> 5, l32 = lane & 31;
+    const int tile = xcd_tile(blockIdx.x, tiles_m * tiles_n);
+    const int mt = tile / tiles_n, nt = tile - mt * tiles_n;
+    const int m0 = mt * kTM, n0 = nt * kTN;
+    const int KB = K / kTK;
+
+    int col[2];
+    bool col_ok[2];
+    const uint8_t* crow[2];
+    int64_t blk0[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        col[u] = n0 + wave * 64 + u * 32 + l32;
+        col_ok[u] = col[u] < N;
+        const int cr = col_ok[u] ? col[u] : N - 1;  // stay in bounds; results discarded
+        crow[u] = codes + (int64_t)cr * (K / 2) + h * 16;
+        blk0[u] = (int64_t)cr * KB;
+    }
+
+    f32x16_t acc[8][2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][u][v] = 0.0f;
+
+    u32x4_t xr[8];
+    load_tile<XVEC>(xr, x, K, m0, M, 0, K, tid);
+    store_tile(lds, xr, tid);
+    u32x4_t cr[2];
+    float ah[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        cr[u] = *reinterpret_cast<const u32x4_t*>(crow[u]);
+        ah[u] = block_ahat(q8, a2, blk0[u]);
+    }
+    __syncthreads();
+
+    for (int ks = 0; ks < KB; ++ks) {
+        const int buf = ks & 1;
+        const bool more = ks + 1 < KB;
+        u32x4_t cn[2];
+        float ahn[2];
+        if (more) {
+            load_tile<XVEC>(xr, x, K, m0, M, (ks + 1) * kTK, K, tid);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                cn[u] = *reinterpret_cast<const u32x4_t*>(crow[u] + (int64_t)(ks + 1) * (kTK / 2));
+                ahn[u] = block_ahat(q8, a2, blk0[u] + ks + 1);
+            }
+        }
+        bf16x8 bop[2][4];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const Nf4Tab T = make_tab(ah[u]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) bop[u][c] = as_bf16x8(deq8(T, cr[u][c]));
+        }
+        const uint8_t* base = lds + buf * kTileBytes;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const bf16x8 a = lds_operand(base, 32 * i + l32, 4 * h + c);
+                acc[i][0] = mfma32(a, bop[0][c], acc[i][0]);
+                acc[i][1] = mfma32(a, bop[1][c], acc[i][1]);
+            }
+        }
+        if (more) {
+            store_tile(lds + (buf ^ 1) * kTileBytes, xr, tid);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                cr[u] = cn[u];
+                ah[u] = ahn[u];
+            }
+        }
+        __syncthreads();
+    }
+
+    // LoRA up-projection: r more reduction steps with A-operand t [M, r] and
+    // B-operand B [r, N] (t already carries the alpha/r scale).
+    for (int j0 = 0; j0 < r; j0 += kTK) {
+        load_tile<false>(xr, t, r, m0, M, j0, r, tid);
+        store_tile(lds, xr, tid);
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            bf16x8 bl[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) bl[u] = gather8(Bl, N, j0 + 32 * h + 8 * c, r, col[u], col_ok[u]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const bf16x8 a = lds_operand(lds, 32 * i + l32, 4 * h + c);
+                acc[i][0] = mfma32(a, bl[0], acc[i][0]);
+                acc[i][1] = mfma32(a, bl[1], acc[i][1]);
+            }
+        }
+        __syncthreads();
+    }
+
+    store_acc(y, N, acc, m0, M, col, col_ok, h);
+}
+
+// ------------------------------------------------------------------ backward dx
+template <bool DYVEC>
+__global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
+    const uint16_t* __restrict__ dy, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ q8,
+    const float* __restrict__ a2, const uint16_t* __restrict__ u_, const uint16_t* __restrict__ Al,
+    uint16_t* __restrict__ dx, int M, int N, int K, int r, int tiles_m, int tiles_k) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[2 * kTileBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_b[kTileBytes];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h = lane >> 5, l32 = lane & 31;
+    const int tile = xcd_tile(blockIdx.x, tiles_m * tiles_k);
+    const int mt = tile / tiles_k, kt = tile - mt * tiles_k;
+    const int m0 = mt * kTM, k0 = kt * kTN;
+    const int KB = K / kTK;
+    const int NS = (N + kTK - 1) / kTK;
+
+    // dequant role: row n0 + (tid >> 2) of the current step, block k0/64 + (tid & 3)
+    const int dq_row = tid >> 2, dq_blk = tid & 3;
+    const int dq_kcol = k0 + dq_blk * kTK;         // first output column of the block
+    const bool dq_kok = dq_kcol < K;
+
+    // MFMA role: output columns k0 + 64 w + 32 u + l32
+    int col[2];
+    bool col_ok[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        col[u] = k0 + wave * 64 + u * 32 + l32;
+        col_ok[u] = col[u] < K;
+    }
+
+    f32x16_t acc[8][2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][u][v] = 0.0f;
+
+    u32x4_t ar[8];
+    load_tile<DYVEC>(ar, dy, N, m0, M, 0, N, tid);
+    store_tile(lds_a, ar, tid);
+
+    for (int ns = 0; ns < NS; ++ns) {
+        const int buf = ns & 1;
+        const bool more = ns + 1 < NS;
+        // this step's weight tile: rows n = 64 ns + dq_row, one block per lane
+        {
+            const int n = ns * kTK + dq_row;
+            u32x4_t c0 = u32x4_t{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
+            u32x4_t c1 = c0;
+            float ah = 0.0f;
+            if (n < N && dq_kok) {
+                const uint8_t* p = codes + (int64_t)n * (K / 2) + dq_kcol / 2;
+                c0 = *reinterpret_cast<const u32x4_t*>(p);
+                c1 = *reinterpret_cast<const u32x4_t*>(p + 16);
+                ah = block_ahat(q8, a2, (int64_t)n * KB + dq_kcol / kTK);
+            }
+            if (more) load_tile<DYVEC>(ar, dy, N, m0, M, (ns + 1) * kTK, N, tid);
+            const Nf4Tab T = make_tab(ah);  // a_hat = 0 (masked rows) gives all-zero weights
+            const int chunk = dq_row >> 3;
+            const uint32_t sub = (uint32_t)(dq_row & 7) * 2u;
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                const uint32_t cw = d < 4 ? c0[d] : c1[d - 4];
+                const u32x4_t eo = deq8_evens_odds(T, cw);  // [w0|w2] [w4|w6] [w1|w3] [w5|w7]
+                const int kr = dq_blk * kTK + 8 * d;          // tile row of weight 0 of this dword
+                uint8_t* b = lds_b + sub;
+                *reinterpret_cast<uint16_t*>(b + tile_off(kr + 0, chunk)) = (uint16_t)(eo[0] & 0xFFFFu);
+                *reinterpret_cast<uint16_t*>(b + tile_off(kr + 2, chunk)) = (uint16_t)(eo[0] >> 16);
+                *reinterpret_cast<uint16_t*>(b + tile_off(kr + 4, chunk)) = (uint16_t)(eo[1] & 0xFFFFu);
+                *reinterpret_cast<uint16_t*>(b + tile_off(kr + 6, chunk)) = (uint16_t)(eo[1] >> 16);
+                *reinterpret_cast<uint16_t*>(b + tile_off(kr + 1, chunk)) = (uint16_t)(eo[2] & 0xFFFFu);
+                *reinterpret_cast<uint16_t*>(b + tile_off(kr + 3, chunk)) = (uint16_t)(eo[2] >> 16);
+                *reinterpret_cast<uint16_t*>(b + tile_off(kr + 5, chunk)) = (uint16_t)(eo[3] & 0xFFFFu);
+                *reinterpret_cast<uint16_t*>(b + tile_off(kr + 7, chunk)) = (uint16_t)(eo[3] >> 16);
+            }
+        }
+        __syncthreads();  // activation tile `buf` and the weight tile are complete
+        const uint8_t* base = lds_a + buf * kTileBytes;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            bf16x8 b[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) b[u] = lds_operand(lds_b, wave * 64 + u * 32 + l32, 4 * h + c);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const bf16x8 a = lds_operand(base, 32 * i + l32, 4 * h + c);
+                acc[i][0] = mfma32(a, b[0], acc[i][0]);
+                acc[i][1] = mfma32(a, b[1], acc[i][1]);
+            }
+        }
+        if (more) store_tile(lds_a + (buf ^ 1) * kTileBytes, ar, tid);
+        __syncthreads();  // everyone is done with lds_b and lds_a[buf]
+    }
+
+    // LoRA: r more reduction steps with A-operand u [M, r] and B-operand A^T,
+    // i.e. A [K, r] read along its rows.
+    for (int j0 = 0; j0 < r; j0 += kTK) {
+        load_tile<false>(ar, u_, r, m0, M, j0, r, tid);
+        store_tile(lds_a, ar, tid);
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            bf16x8 b[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) b[u] = row8(Al, r, col[u], col_ok[u], j0 + 32 * h + 8 * c, r);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const bf16x8 a = lds_operand(lds_a, 32 * i + l32, 4 * h + c);
+                acc[i][0] = mfma32(a, b[0], acc[i][0]);
+                acc[i][1] = mfma32(a, b[1], acc[i][1]);
+            }
+        }
+        __syncthreads();
+    }
+
+    store_acc(dx, K, acc, m0, M, col, col_ok, h);
+}
+
+}  // namespace
+
+qlora_status launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* q8, const float* a2,
+                             const uint16_t* t, const uint16_t* B, uint16_t* y, int M, int N, int K, int r,
+                             hipStream_t s) {
+    const int tm = (M + kTM - 1) / kTM, tn = (N + kTN - 1) / kTN;
+    const bool vec = (reinterpret_cast<uintptr_t>(x) & 15u) == 0;  // K % 64 == 0 always
+    if (vec)
+        hipLaunchKernelGGL(nf4_gemm_fwd_kernel<true>, dim3(tm * tn), dim3(kT), 0, s, x, codes, q8, a2, t, B, y, M,
+                           N, K, r, tm, tn);
+    else
+        hipLaunchKernelGGL(nf4_gemm_fwd_kernel<false>, dim3(tm * tn), dim3(kT), 0, s, x, codes, q8, a2, t, B, y,
+                           M, N, K, r, tm, tn);
+    return launch_status();
+}
+
+qlora_status launch_gemm_bwd_dx(const uint16_t* dy, const uint8_t* codes, const uint8_t* q8, const float* a2,
+                                const uint16_t* u, const uint16_t* A, uint16_t* dx, int M, int N, int K, int r,
+                                hipStream_t s) {
+    const int tm = (M + kTM - 1) / kTM, tk = (K + kTN - 1) / kTN;
+    const bool vec = (N % 8 == 0) && ((reinterpret_cast<uintptr_t>(dy) & 15u) == 0);
+    if (vec)
+        hipLaunchKernelGGL(nf4_gemm_bwd_dx_kernel<true>, dim3(tm * tk), dim3(kT), 0, s, dy, codes, q8, a2, u, A,
+                           dx, M, N, K, r, tm, tk);
+    else
+        hipLaunchKernelGGL(nf4_gemm_bwd_dx_kernel<false>, dim3(tm * tk), dim3(kT), 0, s, dy, codes, q8, a2, u, A,
+                           dx, M, N, K, r, tm, tk);
+    return launch_status();
+}
+
+}  // namespace qlora

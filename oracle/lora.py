@@ -59,6 +59,19 @@ def linear_bwd(x, W_hat_nk, A, B, alpha, r, dy):
     return dx, dA, dB
 
 
+def lora_grads(x, A, B, alpha, r, dy):
+    """dA, dB alone (the dx-free part of linear_bwd), for sampled full-size checks.
+
+    Same formulas: u = s dy B^T, dA = x^T u, dB = (s x A)^T dy.
+    """
+    x = np.asarray(x, np.float64)
+    dy = np.asarray(dy, np.float64)
+    A = np.asarray(A, np.float64)
+    B = np.asarray(B, np.float64)
+    s = lora_scale(alpha, r)
+    return x.T @ (s * (dy @ B.T)), (s * (x @ A)).T @ dy
+
+
 def rel_err(got, ref):
     """Normwise relative error ||got - ref||_F / ||ref||_F (0 when both are zero)."""
     got = np.asarray(got, np.float64)

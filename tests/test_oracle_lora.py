@@ -114,6 +114,13 @@ def test_backward_central_differences():
         assert np.isclose((f(x, A, B + e) - f(x, A, B - e)) / (2 * h), dB[i, j], rtol=1e-7, atol=1e-9)
 
 
+def test_lora_grads_match_linear_bwd():
+    Wh, x, A, B, dy = _small(5)
+    _, dA, dB = lora.linear_bwd(x, Wh, A, B, 16.0, 4, dy)
+    gA, gB = lora.lora_grads(x, A, B, 16.0, 4, dy)
+    assert np.allclose(gA, dA, rtol=1e-13, atol=1e-15) and np.allclose(gB, dB, rtol=1e-13, atol=1e-15)
+
+
 def test_rel_err():
     assert lora.rel_err(np.ones(4), np.ones(4)) == 0.0
     assert np.isclose(lora.rel_err(np.array([3.0, 4.0]) * 1.01, np.array([3.0, 4.0])), 0.01)
