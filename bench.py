@@ -1,0 +1,309 @@
+#!/usr/bin/env python3
+"""Throughput of the NF4 frozen-base linear + LoRA hot path on one MI355X.
+
+One step = the whole hot path over one batch of the 7B-like decoder block
+(q/k/v/o 4096x4096, gate/up 4096->11008, down 11008->4096, LoRA r=64,
+alpha=16, M = 4096 tokens): NF4 + double-quant quantization of all seven
+weights, the fused forward of all seven layers (LoRA down-projection, fused
+dequant GEMM with the LoRA up-projection), and the backward of all seven
+(u, dx, dA, dB).  Inputs are seeded synthetic tensors already resident in HBM.
+
+value = algorithmic fwd+bwd FLOP of the seven linears / step time, where a
+layer counts 2MKN (forward base) + 2MKN (dx) + 2Mr(K+N) (forward LoRA) +
+4Mr(K+N) (backward LoRA); quantization time is inside the step but adds no
+FLOP.  Extra fields: the dominant kernel against the bf16 MFMA roofline, the
+decode GEMV (4096x4096, M=1 and 16) against HBM bandwidth, quantize /
+dequantize bandwidth, a dense bf16 torch.matmul for context, and the CPU
+oracle timed on a bounded sample.
+
+usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
+       python bench.py --mode pmc     (a few untimed steps + a calibration copy, for rocprofv3 --pmc)
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA
+METRIC = "fused NF4-dequant+LoRA linear TFLOP/s (M=4096) and decode GEMV HBM GB/s, 1 MI355X"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extras", action="store_true", help="skip decode / quantize / dense context lines")
+    p.add_argument("--mode", choices=["bench", "pmc"], default="bench")
+    return p.parse_args()
+
+
+def layer_flops(M, N, K, r):
+    return dict(fwd_gemm=2 * M * K * N + 2 * M * r * N, fwd=2 * M * K * N + 2 * M * r * (K + N),
+                bwd=2 * M * K * N + 4 * M * r * (K + N))
+
+
+def gemv_bytes(M, N, K, r):
+    """Algorithmic HBM bytes of one decode forward: codes, q8, a2, x, y, A, B."""
+    return N * K // 2 + N * K // 64 + 4 * (-(-N * K // 16384)) + 2 * M * K + 2 * M * N + 2 * K * r + 2 * r * N
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no collectives; see the sharding note in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from bit_nf4_quantized_15_amd import qlora, workloads
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    def to_dev(u16):
+        return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---------------------------------------------------------------- workload (c4)
+    cfg_id = 4
+    cfg = workloads.CONFIGS[cfg_id]
+    M, r, alpha = cfg["M"], cfg["r"], cfg["alpha"]
+    L = []
+    for li, (name, N, K) in enumerate(cfg["layers"]):
+        d = dict(name=name, N=N, K=K)
+        d["W"] = to_dev(workloads.weight(cfg_id, li))
+        d["x"] = to_dev(workloads.activations(cfg_id, li))
+        d["A"] = to_dev(workloads.lora_A(cfg_id, li))
+        d["B"] = to_dev(workloads.lora_B(cfg_id, li))
+        d["dy"] = to_dev(workloads.grad_output(cfg_id, li))
+        d["w"] = qlora.NF4Weight.empty(N, K, dev)
+        d["t"] = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
+        d["y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        d["dx"] = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        d["dA"] = torch.empty((K, r), dtype=torch.float32, device=dev)
+        d["dB"] = torch.empty((r, N), dtype=torch.float32, device=dev)
+        d["flops"] = layer_flops(M, N, K, r)
+        L.append(d)
+    ws_bytes = max(max(qlora.bwd_workspace(M, d["N"], d["K"], r), qlora.fwd_workspace(M, d["N"], d["K"], r),
+                       int(qlora.lib.qlora_lora_down_workspace(M, d["K"], r))) for d in L)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    total_flops = sum(d["flops"]["fwd"] + d["flops"]["bwd"] for d in L)
+    n_weights = sum(d["N"] * d["K"] for d in L)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    timing = dict(fwd_gemm=[], bwd=[])
+
+    def step(record):
+        for d in L:
+            qlora.quantize(d["W"], out=d["w"])
+        for d in L:
+            qlora.lora_down(d["x"], d["A"], alpha, t=d["t"], ws=ws)
+            if record:
+                a = ev(); a.record()
+            qlora.fused_gemm_fwd(d["w"], d["x"], d["t"], d["B"], y=d["y"])
+            if record:
+                b = ev(); b.record()
+                timing["fwd_gemm"].append((a, b, d["flops"]["fwd_gemm"]))
+        for d in L:
+            if record:
+                a = ev(); a.record()
+            qlora.linear_bwd(d["w"], d["x"], d["A"], d["B"], alpha, d["dy"], t=d["t"], dx=d["dx"], dA=d["dA"],
+                             dB=d["dB"], ws=ws)
+            if record:
+                b = ev(); b.record()
+                timing["bwd"].append((a, b, d["flops"]["bwd"]))
+
+    if args.mode == "pmc":
+        for _ in range(2):
+            step(False)
+        nbytes = 512 << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)                                 # calibration: reads and writes exactly 512 MiB
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "pmc", "calibration_copy_bytes": nbytes}))
+        return
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t_start, t_stop = ev(), ev()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for _ in range(args.steps):
+        step(True)
+    t_stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_stop) / args.steps
+    value = total_flops / (ms_step * 1e-3) / 1e12
+
+    def agg(lst):
+        tot_ms = sum(a.elapsed_time(b) for a, b, _ in lst)
+        tot_f = sum(f for _, _, f in lst)
+        return tot_f / (tot_ms * 1e-3) / 1e12, tot_ms / len(lst)
+
+    fwd_tfs, fwd_avg_ms = agg(timing["fwd_gemm"])
+    bwd_tfs, bwd_avg_ms = agg(timing["bwd"])
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded normal weights/activations, no checkpoint)",
+        "config": {"workload": cfg["workload"] + " (NF4 quantize + fwd + bwd of all 7 linears)",
+                   "M": M, "r": r, "alpha": alpha, "layers": [[d["name"], d["N"], d["K"]] for d in L],
+                   "blocksize": 64, "double_quant": "8-bit codes, fp32 per 256 blocks"},
+        "roofline": {"kernel": "nf4_gemm_fwd_kernel (fused dequant GEMM + LoRA up-projection)", "bound": "mfma",
+                     "achieved": round(fwd_tfs, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": round(fwd_tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
+                     "avg_launch_ms": round(fwd_avg_ms, 4),
+                     "per_launch_flop": "2*M*K*N + 2*M*r*N over the 7 layer shapes, M=4096, r=64"},
+        "breakdown": {"bwd_call_tflops": round(bwd_tfs, 2), "bwd_call_avg_ms": round(bwd_avg_ms, 4),
+                      "wall_s_timed": round(wall, 3), "weights_per_step": n_weights,
+                      "flop_per_step": total_flops},
+    }
+
+    if not args.no_extras:
+        out["extras"] = extras(torch, qlora, workloads, dev, to_dev, L, M, r)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(workloads, cfg_id, total_flops, n_weights)
+    print(json.dumps(out))
+
+
+def extras(torch, qlora, workloads, dev, to_dev, L, M, r):
+    """Decode GEMV bandwidth, quantize/dequantize bandwidth, dense bf16 context."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    res = {}
+    # quantize / dequantize of the block's weights (bytes: bf16 in + codes/q8/a2 out)
+    q_bytes = sum(d["N"] * d["K"] * 2 + sum(qlora.sizes(d["N"], d["K"])) for d in L)
+    for _ in range(2):
+        for d in L:
+            qlora.quantize(d["W"], out=d["w"])
+    a, b = ev(), ev()
+    a.record()
+    reps = 5
+    for _ in range(reps):
+        for d in L:
+            qlora.quantize(d["W"], out=d["w"])
+    b.record()
+    torch.cuda.synchronize()
+    q_ms = a.elapsed_time(b) / reps
+    res["quantize"] = {"GB/s": round(q_bytes / (q_ms * 1e-3) / 1e9, 1), "ms": round(q_ms, 4),
+                       "frac_of_hbm_peak": round(q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "weights": sum(d["N"] * d["K"] for d in L)}
+    d0 = L[0]
+    out = torch.empty((d0["N"], d0["K"]), dtype=torch.bfloat16, device=dev)
+    qlora.dequantize(d0["w"], out=out)
+    a, b = ev(), ev()
+    a.record()
+    for _ in range(reps):
+        qlora.dequantize(d0["w"], out=out)
+    b.record()
+    torch.cuda.synchronize()
+    dq_ms = a.elapsed_time(b) / reps
+    dq_bytes = d0["N"] * d0["K"] * 2 + sum(qlora.sizes(d0["N"], d0["K"]))
+    res["dequantize_q_proj"] = {"GB/s": round(dq_bytes / (dq_ms * 1e-3) / 1e9, 1), "ms": round(dq_ms, 4)}
+    del out
+
+    # decode GEMV: 4096x4096 q_proj, r=16, M in {1, 16}; 64 distinct weight copies
+    # (> 2x the 256 MB Infinity Cache) rotated so that HBM, not cache, is measured
+    c2 = workloads.CONFIGS[2]
+    _, N2, K2 = c2["layers"][0]
+    W2 = to_dev(workloads.weight(2))
+    copies = [qlora.quantize(W2) for _ in range(64)]
+    A2 = to_dev(workloads.lora_A(2)); B2 = to_dev(workloads.lora_B(2))
+    dec = {}
+    for Md in (1, 16):
+        xd = to_dev(workloads.activations(2, M=Md))
+        td = torch.empty((Md, c2["r"]), dtype=torch.bfloat16, device=dev)
+        yd = torch.empty((Md, N2), dtype=torch.bfloat16, device=dev)
+        wsd = torch.empty(max(qlora.fwd_workspace(Md, N2, K2, c2["r"]), 256), dtype=torch.uint8, device=dev)
+        for w in copies[:4]:
+            qlora.linear_fwd(w, xd, A2, B2, c2["alpha"], y=yd, t=td, ws=wsd)
+        torch.cuda.synchronize()
+        pairs, gpairs = [], []
+        for rep in range(3):
+            for w in copies:
+                a, g0, b = ev(), ev(), ev()
+                a.record()
+                qlora.lora_down(xd, A2, c2["alpha"], t=td, ws=wsd)
+                g0.record()
+                qlora.fused_gemm_fwd(w, xd, td, B2, y=yd)
+                b.record()
+                pairs.append((a, b)); gpairs.append((g0, b))
+        torch.cuda.synchronize()
+        call_ms = np.median([p.elapsed_time(q) for p, q in pairs])
+        gemv_ms = np.median([p.elapsed_time(q) for p, q in gpairs])
+        nb = gemv_bytes(Md, N2, K2, c2["r"])
+        dec[f"M={Md}"] = {"bytes": nb, "fwd_call_us": round(call_ms * 1e3, 2), "gemv_kernel_us": round(gemv_ms * 1e3, 2),
+                          "GB/s_fwd_call": round(nb / (call_ms * 1e-3) / 1e9, 1),
+                          "GB/s_gemv_kernel": round((nb - 2 * K2 * c2["r"]) / (gemv_ms * 1e-3) / 1e9, 1),
+                          "frac_of_hbm_peak_fwd_call": round(nb / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    res["decode_gemv_q_proj_4096x4096_r16"] = dec
+    del copies
+
+    # context: dense bf16 torch.matmul (hipBLASLt) on the same shapes, forward base product only
+    tot_f, tot_ms = 0, 0.0
+    for d in L:
+        Wd = d["W"]
+        torch.matmul(d["x"], Wd.t())
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(3):
+            torch.matmul(d["x"], Wd.t())
+        b.record()
+        torch.cuda.synchronize()
+        tot_ms += a.elapsed_time(b) / 3
+        tot_f += 2 * M * d["N"] * d["K"]
+    res["context_dense_bf16_matmul_fwd_tflops"] = round(tot_f / (tot_ms * 1e-3) / 1e12, 1)
+    return res
+
+
+def cpu_baseline(workloads, cfg_id, total_flops, n_weights):
+    """The oracle as it stands, on the host cores, on a bounded sample of the same step:
+    quantize two of the seven weights (q_proj, gate_proj) and run fp64 forward+backward
+    on 256 of the 4096 token rows for those two layers; the full-step time is
+    extrapolated from the measured quantize rate (weights/s) and fp64 GEMM rate (FLOP/s)."""
+    from oracle import bf16, lora, nf4
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = os.cpu_count() or 1
+    cfg = workloads.CONFIGS[cfg_id]
+    M, r, alpha = cfg["M"], cfg["r"], cfg["alpha"]
+    rows = 256
+    q_w, q_s, f_f, f_s = 0, 0.0, 0, 0.0
+    for li in (0, 4):
+        name, N, K = cfg["layers"][li]
+        W = workloads.weight(cfg_id, li)
+        t0 = time.perf_counter()
+        p, q8, a2 = nf4.quantize(W)
+        q_s += time.perf_counter() - t0
+        q_w += N * K
+        x = workloads.activations(cfg_id, li)[:rows]
+        dy = workloads.grad_output(cfg_id, li)[:rows]
+        A = workloads.lora_A(cfg_id, li); B = workloads.lora_B(cfg_id, li)
+        t0 = time.perf_counter()
+        Wh = bf16.to_f64(nf4.dequantize(p, q8, a2, N, K))
+        xf, Af, Bf, dyf = (bf16.to_f64(v) for v in (x, A, B, dy))
+        lora.linear_fwd(xf, Wh, Af, Bf, alpha, r)
+        lora.linear_bwd(xf, Wh, Af, Bf, alpha, r, dyf)
+        f_s += time.perf_counter() - t0
+        f_f += 4 * rows * K * N + 6 * rows * r * (K + N)
+    est_s = n_weights / (q_w / q_s) + total_flops / (f_f / f_s)
+    return {"value": round(total_flops / est_s / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": (f"numpy fp64 oracle: quantize q_proj+gate_proj ({q_w} weights, {q_s:.1f} s, 1 thread) and "
+                       f"fwd+bwd on {rows}/{M} token rows of those layers ({f_f / 1e9:.1f} GFLOP, {f_s:.1f} s, "
+                       f"BLAS threads {blas_threads}); full step extrapolated to {est_s:.1f} s"),
+            "sample_seconds": round(q_s + f_s, 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -42,17 +42,20 @@ inline FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int r) {
 }
 
 struct BwdWs {
-    size_t u, part, at, tbuf, pa, pb, total;
+    size_t u, ut, part, at, tbuf, tt, pa, pb, total;
 };
 inline BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int r) {
     BwdWs w{};
     const SplitPlan su = plan_nt(M, N), st = plan_nt(M, K);
-    const SplitPlan sa = plan_tn(M, K, r), sb = plan_tn(M, r, N);
+    const SplitPlan sa = plan_tn(M, K), sb = plan_tn(M, N);
+    const size_t mr2 = align256((size_t)M * r * 2);
     w.u = 0;
-    w.part = w.u + align256((size_t)M * r * 2);
+    w.ut = w.u + mr2;
+    w.part = w.ut + mr2;
     w.at = w.part + align256((size_t)std::max(su.splits, st.splits) * M * r * 4);
     w.tbuf = w.at + align256((size_t)r * K * 2);
-    w.pa = w.tbuf + align256((size_t)M * r * 2);
+    w.tt = w.tbuf + mr2;
+    w.pa = w.tt + mr2;
     w.pb = w.pa + align256((size_t)sa.splits * K * r * 4);
     w.total = w.pb + align256((size_t)sb.splits * r * N * 4);
     return w;
@@ -115,6 +118,42 @@ size_t qlora_bwd_workspace(int64_t M, int64_t N, int64_t K, int r) {
     return bwd_ws(M, N, K, r).total;
 }
 
+size_t qlora_lora_down_workspace(int64_t M, int64_t K, int r) {
+    if (bad_dims(M, 1, K, r) || M == 0 || K % kBlock) return 0;
+    const SplitPlan sp = plan_nt(M, K);
+    return align256((size_t)r * K * 2) + align256((size_t)sp.splits * M * r * 4);
+}
+
+qlora_status qlora_lora_down(const uint16_t* x, int64_t M, int64_t K, const uint16_t* A, int r, float alpha,
+                             uint16_t* t_out, void* ws, size_t ws_bytes, void* stream) {
+    if (bad_dims(M, 1, K, r) || !std::isfinite(alpha)) return QLORA_ERR_INVALID_ARG;
+    if (K % kBlock) return QLORA_ERR_UNSUPPORTED_SHAPE;
+    if (M == 0) return QLORA_OK;
+    if (!x || !A || !t_out) return QLORA_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(A) || !aligned16(t_out)) return QLORA_ERR_MISALIGNED;
+    const size_t need = qlora_lora_down_workspace(M, K, r);
+    if (!ws || ws_bytes < need) return QLORA_ERR_WORKSPACE;
+    if (!aligned16(ws)) return QLORA_ERR_MISALIGNED;
+    hipStream_t s = (hipStream_t)stream;
+    uint16_t* At = reinterpret_cast<uint16_t*>(ws);
+    float* part = reinterpret_cast<float*>(at(ws, align256((size_t)r * K * 2)));
+    qlora_status st = launch_transpose(A, At, (int)K, r, s);
+    if (st != QLORA_OK) return st;
+    return launch_nt(x, At, part, t_out, nullptr, alpha / (float)r, (int)M, (int)K, r, s);
+}
+
+qlora_status qlora_fused_gemm_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uint16_t* t,
+                                  const uint16_t* B, int r, uint16_t* y, void* stream) {
+    qlora_status st = check_state(w);
+    if (st != QLORA_OK) return st;
+    const int64_t N = w->n, K = w->k;
+    if (bad_dims(M, N, K, r)) return QLORA_ERR_INVALID_ARG;
+    if (M == 0) return QLORA_OK;
+    if (!x || !t || !B || !y) return QLORA_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(t) || !aligned16(B) || !aligned16(y)) return QLORA_ERR_MISALIGNED;
+    return launch_gemm_fwd(x, w->codes, w->q8, w->a2, t, B, y, (int)M, (int)N, (int)K, r, (hipStream_t)stream);
+}
+
 qlora_status qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
                               int r, float alpha, uint16_t* y, uint16_t* t_out, void* ws, size_t ws_bytes,
                               void* stream) {
@@ -135,7 +174,7 @@ qlora_status qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, 
     float* part = reinterpret_cast<float*>(at(ws, L.part));
     uint16_t* t = t_out ? t_out : reinterpret_cast<uint16_t*>(at(ws, L.tbuf));
     if ((st = launch_transpose(A, At, (int)K, r, s)) != QLORA_OK) return st;
-    if ((st = launch_nt(x, At, part, t, scale, (int)M, (int)K, r, s)) != QLORA_OK) return st;
+    if ((st = launch_nt(x, At, part, t, nullptr, scale, (int)M, (int)K, r, s)) != QLORA_OK) return st;
     return launch_gemm_fwd(x, w->codes, w->q8, w->a2, t, B, y, (int)M, (int)N, (int)K, r, s);
 }
 
@@ -162,23 +201,28 @@ qlora_status qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, int64_t M, 
     if (!aligned16(ws)) return QLORA_ERR_MISALIGNED;
     const float scale = alpha / (float)r;
     uint16_t* u = reinterpret_cast<uint16_t*>(at(ws, L.u));
+    uint16_t* uT = reinterpret_cast<uint16_t*>(at(ws, L.ut));
+    uint16_t* tT = reinterpret_cast<uint16_t*>(at(ws, L.tt));
     float* part = reinterpret_cast<float*>(at(ws, L.part));
     // u = s dy B^T  (B [r, N] is already the row-major transpose the kernel wants)
-    if ((st = launch_nt(dy, B, part, u, scale, (int)M, (int)N, r, s)) != QLORA_OK) return st;
-    if (!t) {  // recompute t = s x A
+    if ((st = launch_nt(dy, B, part, u, uT, scale, (int)M, (int)N, r, s)) != QLORA_OK) return st;
+    if (!t) {  // recompute t = s x A (and its transpose)
         uint16_t* At = reinterpret_cast<uint16_t*>(at(ws, L.at));
         uint16_t* tb = reinterpret_cast<uint16_t*>(at(ws, L.tbuf));
         if ((st = launch_transpose(A, At, (int)K, r, s)) != QLORA_OK) return st;
-        if ((st = launch_nt(x, At, part, tb, scale, (int)M, (int)K, r, s)) != QLORA_OK) return st;
+        if ((st = launch_nt(x, At, part, tb, tT, scale, (int)M, (int)K, r, s)) != QLORA_OK) return st;
         t = tb;
+    } else if ((st = launch_transpose(t, tT, (int)M, r, s)) != QLORA_OK) {
+        return st;
     }
     if (dx) {
         if ((st = launch_gemm_bwd_dx(dy, w->codes, w->q8, w->a2, u, A, dx, (int)M, (int)N, (int)K, r, s)) != QLORA_OK)
             return st;
     }
-    if ((st = launch_tn(x, u, reinterpret_cast<float*>(at(ws, L.pa)), dA, (int)M, (int)K, r, s)) != QLORA_OK)
+    // dA [K, r] = x^T u ; dB [r, N] = t^T dy, stored transposed from the [N, r] reduction
+    if ((st = launch_tn(x, uT, reinterpret_cast<float*>(at(ws, L.pa)), dA, (int)M, (int)K, r, r, 1, s)) != QLORA_OK)
         return st;
-    return launch_tn(t, dy, reinterpret_cast<float*>(at(ws, L.pb)), dB, (int)M, r, (int)N, s);
+    return launch_tn(dy, tT, reinterpret_cast<float*>(at(ws, L.pb)), dB, (int)M, (int)N, r, 1, N, s);
 }
 
 }  // extern "C"

@@ -81,6 +81,23 @@ __device__ __forceinline__ void load_tile(u32x4_t (&r)[8], const uint16_t* __res
     }
 }
 
+// Branch-free variant for full-width column steps (col0 + 64 <= ld): rows past
+// nrows re-read the last row; the outputs they feed are never stored.
+template <bool VEC>
+__device__ __forceinline__ void load_tile_clamped(u32x4_t (&r)[8], const uint16_t* __restrict__ src, int64_t ld,
+                                                  int row0, int nrows, int col0, int tid) {
+    if (!VEC) {
+        load_tile<false>(r, src, ld, row0, nrows, col0, (int)ld, tid);
+        return;
+    }
+    const int lr = tid >> 3, lc = tid & 7;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int row = min(row0 + lr + 32 * p, nrows - 1);
+        r[p] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)row * ld + col0 + lc * 8);
+    }
+}
+
 __device__ __forceinline__ void store_tile(uint8_t* lds, const u32x4_t (&r)[8], int tid) {
     const int lr = tid >> 3, lc = tid & 7;
 #pragma unroll
@@ -142,116 +159,174 @@ __device__ __forceinline__ void store_acc(uint16_t* __restrict__ out, int64_t ld
 }
 
 // ------------------------------------------------------------------ forward
+// Waves in a 2 x 2 arrangement, each owning a 128 x 128 quarter of the output
+// tile (4 x 4 MFMA tiles).  Both operand tiles live in LDS, double buffered:
+//   A = x rows (HBM -> registers -> LDS),
+//   B = the dequantized weight rows: lane `tid` owns weight row n0 + tid and
+//       expands that row's 64-code block of the next step (one table per lane
+//       and step) while the MFMAs of the current step run.
+// The loop body is a single basic block (clamped indices instead of
+// branches) so the scheduler can interleave the dequant VALU work, the LDS
+// traffic and the MFMAs; sched_group_barrier pins that interleave.
 template <bool XVEC>
 __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ q8,
     const float* __restrict__ a2, const uint16_t* __restrict__ t, const uint16_t* __restrict__ Bl,
     uint16_t* __restrict__ y, int M, int N, int K, int r, int tiles_m, int tiles_n) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kTileBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kTileBytes];
+    uint8_t* const ldsA0 = lds;
+    uint8_t* const ldsB0 = lds + 2 * kTileBytes;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, l32 = lane & 31;
+    const int wm = wave >> 1, wn = wave & 1;
     const int tile = xcd_tile(blockIdx.x, tiles_m * tiles_n);
     const int mt = tile / tiles_n, nt = tile - mt * tiles_n;
     const int m0 = mt * kTM, n0 = nt * kTN;
     const int KB = K / kTK;
 
-    int col[2];
-    bool col_ok[2];
-    const uint8_t* crow[2];
-    int64_t blk0[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        col[u] = n0 + wave * 64 + u * 32 + l32;
-        col_ok[u] = col[u] < N;
-        const int cr = col_ok[u] ? col[u] : N - 1;  // stay in bounds; results discarded
-        crow[u] = codes + (int64_t)cr * (K / 2) + h * 16;
-        blk0[u] = (int64_t)cr * KB;
-    }
+    // dequant role: weight row n0 + tid (rows past N read row N-1; never stored)
+    const int drow = min(n0 + tid, N - 1);
+    const uint8_t* crow = codes + (int64_t)drow * (K / 2);
+    const int64_t dblk = (int64_t)drow * KB;
 
-    f32x16_t acc[8][2];
+    f32x16_t acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][u][v] = 0.0f;
 
-    u32x4_t xr[8];
-    load_tile<XVEC>(xr, x, K, m0, M, 0, K, tid);
-    store_tile(lds, xr, tid);
-    u32x4_t cr[2];
-    float ah[2];
+    // raw inputs of one step's dequant: 32 code bytes, the block's 8-bit scale
+    // code and its group's fp32 scale (converted only when used, one step
+    // later, so that no wait on this step's loads is needed)
+    auto load_codes = [&](int ks, u32x4_t& c0, u32x4_t& c1, uint32_t& q, float& g) {
+        const uint8_t* p = crow + (int64_t)ks * (kTK / 2);
+        c0 = *reinterpret_cast<const u32x4_t*>(p);
+        c1 = *reinterpret_cast<const u32x4_t*>(p + 16);
+        const int64_t blk = dblk + ks;
+        q = q8[blk];
+        g = a2[blk >> 8];
+    };
+    auto dequant_store = [&](uint8_t* ldsB, const u32x4_t& c0, const u32x4_t& c1, uint32_t q, float g) {
+        const Nf4Tab T = make_tab(scale_step(g) * (float)q);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        cr[u] = *reinterpret_cast<const u32x4_t*>(crow[u]);
-        ah[u] = block_ahat(q8, a2, blk0[u]);
-    }
+        for (int d = 0; d < 8; ++d) {
+            const uint32_t cw = d < 4 ? c0[d] : c1[d - 4];
+            *reinterpret_cast<u32x4_t*>(ldsB + tile_off(tid, d)) = deq8(T, cw);
+        }
+    };
+
+    // prologue: A(0), B(0) in LDS; codes of step 1 in registers
+    u32x4_t xr[8];
+    load_tile_clamped<XVEC>(xr, x, K, m0, M, 0, tid);
+    u32x4_t c0, c1;
+    uint32_t cq;
+    float cg;
+    load_codes(0, c0, c1, cq, cg);
+    store_tile(ldsA0, xr, tid);
+    dequant_store(ldsB0, c0, c1, cq, cg);
+    load_codes(min(1, KB - 1), c0, c1, cq, cg);
     __syncthreads();
 
     for (int ks = 0; ks < KB; ++ks) {
         const int buf = ks & 1;
-        const bool more = ks + 1 < KB;
-        u32x4_t cn[2];
-        float ahn[2];
-        if (more) {
-            load_tile<XVEC>(xr, x, K, m0, M, (ks + 1) * kTK, K, tid);
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                cn[u] = *reinterpret_cast<const u32x4_t*>(crow[u] + (int64_t)(ks + 1) * (kTK / 2));
-                ahn[u] = block_ahat(q8, a2, blk0[u] + ks + 1);
-            }
-        }
-        bf16x8 bop[2][4];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const Nf4Tab T = make_tab(ah[u]);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) bop[u][c] = as_bf16x8(deq8(T, cr[u][c]));
-        }
-        const uint8_t* base = lds + buf * kTileBytes;
+        const uint8_t* A = ldsA0 + buf * kTileBytes;
+        const uint8_t* B = ldsB0 + buf * kTileBytes;
+        uint8_t* An = ldsA0 + (buf ^ 1) * kTileBytes;
+        uint8_t* Bn = ldsB0 + (buf ^ 1) * kTileBytes;
+        // next step's operands: x tile (ks+1) and codes (ks+2) from HBM
+        load_tile_clamped<XVEC>(xr, x, K, m0, M, min(ks + 1, KB - 1) * kTK, tid);
+        u32x4_t n0c, n1c;
+        uint32_t nq;
+        float ng;
+        load_codes(min(ks + 2, KB - 1), n0c, n1c, nq, ng);
+        // step ks+1's codes are expanded between this step's MFMAs (register
+        // work only); all LDS writes follow this step's LDS reads.
+        const Nf4Tab T = make_tab(scale_step(cg) * (float)cq);
+        u32x4_t deq[8];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
+            bf16x8 a[4], b[4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const bf16x8 a = lds_operand(base, 32 * i + l32, 4 * h + c);
-                acc[i][0] = mfma32(a, bop[0][c], acc[i][0]);
-                acc[i][1] = mfma32(a, bop[1][c], acc[i][1]);
+            for (int i = 0; i < 4; ++i) a[i] = lds_operand(A, 128 * wm + 32 * i + l32, 4 * h + c);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) b[u] = lds_operand(B, 128 * wn + 32 * u + l32, 4 * h + c);
+            deq[2 * c] = deq8(T, c < 2 ? c0[2 * c] : c1[2 * c - 4]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc[i][u] = mfma32(a[i], b[u], acc[i][u]);
+            deq[2 * c + 1] = deq8(T, c < 2 ? c0[2 * c + 1] : c1[2 * c - 3]);
+#pragma unroll
+            for (int i = 2; i < 4; ++i)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc[i][u] = mfma32(a[i], b[u], acc[i][u]);
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // the 8 operand reads
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // 4 VALU
             }
         }
-        if (more) {
-            store_tile(lds + (buf ^ 1) * kTileBytes, xr, tid);
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                cr[u] = cn[u];
-                ah[u] = ahn[u];
-            }
-        }
+        for (int d = 0; d < 8; ++d) *reinterpret_cast<u32x4_t*>(Bn + tile_off(tid, d)) = deq[d];
+        store_tile(An, xr, tid);
+        c0 = n0c;
+        c1 = n1c;
+        cq = nq;
+        cg = ng;
         __syncthreads();
     }
 
-    // LoRA up-projection: r more reduction steps with A-operand t [M, r] and
-    // B-operand B [r, N] (t already carries the alpha/r scale).
+    // LoRA up-projection: r more reduction steps, A = t [M, r], B = B^T staged
+    // in LDS (lane tid copies column n0 + tid of B).
+    const int bn = n0 + tid;
     for (int j0 = 0; j0 < r; j0 += kTK) {
         load_tile<false>(xr, t, r, m0, M, j0, r, tid);
-        store_tile(lds, xr, tid);
+        store_tile(ldsA0, xr, tid);
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ja = j0 + 8 * d + 2 * e, jb = ja + 1;
+                const uint32_t lo = (bn < N && ja < r) ? Bl[(int64_t)ja * N + bn] : 0u;
+                const uint32_t hi = (bn < N && jb < r) ? Bl[(int64_t)jb * N + bn] : 0u;
+                w[e] = lo | (hi << 16);
+            }
+            *reinterpret_cast<u32x4_t*>(ldsB0 + tile_off(tid, d)) = u32x4_t{w[0], w[1], w[2], w[3]};
+        }
         __syncthreads();
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            bf16x8 bl[2];
+            bf16x8 a[4], b[4];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) bl[u] = gather8(Bl, N, j0 + 32 * h + 8 * c, r, col[u], col_ok[u]);
+            for (int i = 0; i < 4; ++i) a[i] = lds_operand(ldsA0, 128 * wm + 32 * i + l32, 4 * h + c);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const bf16x8 a = lds_operand(lds, 32 * i + l32, 4 * h + c);
-                acc[i][0] = mfma32(a, bl[0], acc[i][0]);
-                acc[i][1] = mfma32(a, bl[1], acc[i][1]);
-            }
+            for (int u = 0; u < 4; ++u) b[u] = lds_operand(ldsB0, 128 * wn + 32 * u + l32, 4 * h + c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc[i][u] = mfma32(a[i], b[u], acc[i][u]);
         }
         __syncthreads();
     }
 
-    store_acc(y, N, acc, m0, M, col, col_ok, h);
+    // epilogue
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int col = n0 + 128 * wn + 32 * u + l32;
+        if (col >= N) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int m = m0 + 128 * wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+                if (m < M) y[(int64_t)m * N + col] = (uint16_t)(pack_bf16x2(acc[i][u][v], 0.0f) & 0xFFFFu);
+            }
+    }
 }
 
 // ------------------------------------------------------------------ backward dx

@@ -42,22 +42,7 @@ __device__ __forceinline__ bf16x8 load8_row(const uint16_t* __restrict__ src, in
     return __builtin_bit_cast(bf16x8, u32x4_t{w[0], w[1], w[2], w[3]});
 }
 
-// 8 bf16 down a column: src[(r0 + i)*ld + col], i = 0..7.
-__device__ __forceinline__ bf16x8 load8_col(const uint16_t* __restrict__ src, int64_t ld, int r0, int nrows, int col,
-                                           int ncols) {
-    uint32_t w[4];
-    const bool cok = col < ncols;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int a = r0 + 2 * i, b = a + 1;
-        const uint32_t lo = (cok && a < nrows) ? src[(int64_t)a * ld + col] : 0u;
-        const uint32_t hi = (cok && b < nrows) ? src[(int64_t)b * ld + col] : 0u;
-        w[i] = lo | (hi << 16);
-    }
-    return __builtin_bit_cast(bf16x8, u32x4_t{w[0], w[1], w[2], w[3]});
-}
-
-// At[j, k] = A[k, j]
+// At[j, k] = A[k, j] for A [K, r] (any row-major matrix transpose)
 __global__ void transpose_kernel(const uint16_t* __restrict__ A, uint16_t* __restrict__ At, int K, int r) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (int64_t)K * r) return;
@@ -66,12 +51,16 @@ __global__ void transpose_kernel(const uint16_t* __restrict__ A, uint16_t* __res
 }
 
 // part[split, m, j] = sum over c in the split's range of X[m, c] * Yt[j, c]
-// One wave per (32-row tile, split); TQ 32-column tiles of j.
+// Workgroup = 4 waves = 4 tiles of 32 rows of M; TQ 32-wide tiles of j.  The
+// reduction runs in steps of 64: lane half h takes c + 32h .. c + 32h + 31 as
+// four 16-byte loads (the two halves of an MFMA's k slots may map to any
+// reduction indices, as long as both operands agree), and the next step's
+// loads are issued before this step's MFMAs.
 template <int TQ, bool VEC>
-__global__ __launch_bounds__(64) void nt_partial_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Yt,
-                                                        float* __restrict__ part, int M, int C, int r, int chunk) {
-    const int lane = threadIdx.x, h = lane >> 5, l32 = lane & 31;
-    const int m0 = blockIdx.x * 32;
+__global__ __launch_bounds__(256) void nt_partial_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Yt,
+                                                         float* __restrict__ part, int M, int C, int r, int chunk) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, l32 = lane & 31;
+    const int m0 = blockIdx.x * 128 + wave * 32;
     const int split = blockIdx.y;
     const int c_begin = split * chunk;
     const int c_end = min(C, c_begin + chunk);
@@ -80,14 +69,30 @@ __global__ __launch_bounds__(64) void nt_partial_kernel(const uint16_t* __restri
     for (int q = 0; q < TQ; ++q)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[q][v] = 0.0f;
-    for (int c = c_begin; c < c_end; c += 16) {
-        const int cc = c + 8 * h;
-        const bf16x8 a = load8_row<VEC>(X, C, m0 + l32, M, cc, c_end);
+    bf16x8 xa[4], yb[TQ][4];
+    auto load = [&](int c) {
 #pragma unroll
-        for (int q = 0; q < TQ; ++q) {
-            const bf16x8 b = load8_row<VEC>(Yt, C, 32 * q + l32, r, cc, c_end);
-            acc[q] = mfma32(a, b, acc[q]);
+        for (int i = 0; i < 4; ++i) {
+            const int cc = c + 32 * h + 8 * i;
+            xa[i] = load8_row<VEC>(X, C, m0 + l32, M, cc, c_end);
+#pragma unroll
+            for (int q = 0; q < TQ; ++q) yb[q][i] = load8_row<VEC>(Yt, C, 32 * q + l32, r, cc, c_end);
         }
+    };
+    if (c_begin < c_end) load(c_begin);
+    for (int c = c_begin; c < c_end; c += 64) {
+        bf16x8 ca[4], cb[TQ][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ca[i] = xa[i];
+#pragma unroll
+            for (int q = 0; q < TQ; ++q) cb[q][i] = yb[q][i];
+        }
+        if (c + 64 < c_end) load(c + 64);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < TQ; ++q) acc[q] = mfma32(ca[i], cb[q][i], acc[q]);
     }
     float* out = part + (int64_t)split * M * r;
 #pragma unroll
@@ -102,67 +107,110 @@ __global__ __launch_bounds__(64) void nt_partial_kernel(const uint16_t* __restri
     }
 }
 
-// out[m, j] = bf16( s * sum_split part[split, m, j] )
-__global__ void finalize_bf16_kernel(const float* __restrict__ part, int splits, int64_t count, float s,
-                                     uint16_t* __restrict__ out) {
+// out[m, j] = bf16( s * sum_split part[split, m, j] ); optionally also outT[j, m].
+__global__ void finalize_bf16_kernel(const float* __restrict__ part, int splits, int M, int r, float s,
+                                     uint16_t* __restrict__ out, uint16_t* __restrict__ outT) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t count = (int64_t)M * r;
     if (i >= count) return;
     float acc = 0.0f;
     for (int p = 0; p < splits; ++p) acc += part[(int64_t)p * count + i];
-    out[i] = (uint16_t)(pack_bf16x2(s * acc, 0.0f) & 0xFFFFu);
+    const uint16_t v = (uint16_t)(pack_bf16x2(s * acc, 0.0f) & 0xFFFFu);
+    out[i] = v;
+    if (outT) {
+        const int m = (int)(i / r), j = (int)(i - (int64_t)m * r);
+        outT[(int64_t)j * M + m] = v;
+    }
 }
 
-// part[split, p, q] = sum over m in the split's range of P[m, p] * Q[m, q]
-// One wave per (32*TP x 32*TQ output tile, split).
-template <int TP, int TQ>
-__global__ __launch_bounds__(64) void tn_partial_kernel(const uint16_t* __restrict__ P, const uint16_t* __restrict__ Q,
-                                                        float* __restrict__ part, int M, int Pd, int Qd, int chunk) {
-    const int lane = threadIdx.x, h = lane >> 5, l32 = lane & 31;
-    const int p0 = blockIdx.x * 32 * TP, q0 = blockIdx.y * 32 * TQ;
-    const int split = blockIdx.z;
+// part[split, d, j] = sum over m in the split's range of X[m, d] * S[m, j],
+// with S given transposed (ST [r, M]).  Workgroup = 4 waves over 128 columns
+// d of X (32 each); the [64 m x 128 d] tile of X is staged in LDS (double
+// buffered, next tile prefetched into registers) and read back down its
+// columns for the MFMA A operand (8 consecutive m per lane); the B operand is
+// 8 consecutive m of a row of ST (one 16-byte load).
+constexpr int kTnRows = 64, kTnCols = 128, kTnLd = kTnCols + 8;  // +8: conflict-free column reads
+
+template <int TQ, bool VEC>
+__global__ __launch_bounds__(256) void tn_partial_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ ST,
+                                                         float* __restrict__ part, int M, int D, int r, int chunk) {
+    __shared__ __attribute__((aligned(16))) uint16_t tile[2][kTnRows * kTnLd];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    const int d0 = blockIdx.x * kTnCols;
+    const int split = blockIdx.y;
     const int m_begin = split * chunk;
     const int m_end = min(M, m_begin + chunk);
-    f32x16_t acc[TP][TQ];
+    // loader: row tid/4 of the tile, columns 32*(tid%4) .. +31
+    const int lr = tid >> 2, lc = (tid & 3) * 32;
+    f32x16_t acc[TQ];
 #pragma unroll
-    for (int a = 0; a < TP; ++a)
+    for (int q = 0; q < TQ; ++q)
 #pragma unroll
-        for (int b = 0; b < TQ; ++b)
+        for (int v = 0; v < 16; ++v) acc[q][v] = 0.0f;
+    bf16x8 xr[4];
+    auto load_x = [&](int m) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
-    for (int m = m_begin; m < m_end; m += 16) {
-        const int mm = m + 8 * h;
-        bf16x8 pa[TP], qb[TQ];
+        for (int i = 0; i < 4; ++i) xr[i] = load8_row<VEC>(X, D, m + lr, m_end, d0 + lc + 8 * i, D);
+    };
+    auto store_x = [&](int buf) {
 #pragma unroll
-        for (int a = 0; a < TP; ++a) pa[a] = load8_col(P, Pd, mm, m_end, p0 + 32 * a + l32, Pd);
-#pragma unroll
-        for (int b = 0; b < TQ; ++b) qb[b] = load8_col(Q, Qd, mm, m_end, q0 + 32 * b + l32, Qd);
-#pragma unroll
-        for (int a = 0; a < TP; ++a)
-#pragma unroll
-            for (int b = 0; b < TQ; ++b) acc[a][b] = mfma32(pa[a], qb[b], acc[a][b]);
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<bf16x8*>(&tile[buf][lr * kTnLd + lc + 8 * i]) = xr[i];
+    };
+    if (m_begin < m_end) {
+        load_x(m_begin);
+        store_x(0);
     }
-    float* out = part + (int64_t)split * Pd * Qd;
+    __syncthreads();
+    const int dcol = 32 * wave + l32;   // this lane's column of the tile (A operand row)
+    int buf = 0;
+    for (int m = m_begin; m < m_end; m += kTnRows) {
+        const bool more = m + kTnRows < m_end;
+        if (more) load_x(m + kTnRows);
 #pragma unroll
-    for (int a = 0; a < TP; ++a)
+        for (int mc = 0; mc < kTnRows / 16; ++mc) {
+            const int mr = mc * 16 + 8 * h;   // tile row of this lane's first k slot
+            uint32_t w[4];
 #pragma unroll
-        for (int b = 0; b < TQ; ++b) {
-            const int q = q0 + 32 * b + l32;
-            if (q >= Qd) continue;
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t lo = tile[buf][(mr + 2 * i) * kTnLd + dcol];
+                const uint32_t hi = tile[buf][(mr + 2 * i + 1) * kTnLd + dcol];
+                w[i] = lo | (hi << 16);
+            }
+            const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4_t{w[0], w[1], w[2], w[3]});
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int p = p0 + 32 * a + 8 * (v >> 2) + 4 * h + (v & 3);
-                if (p < Pd) out[(int64_t)p * Qd + q] = acc[a][b][v];
+            for (int q = 0; q < TQ; ++q) {
+                const bf16x8 b = load8_row<VEC>(ST, M, 32 * q + l32, r, m + mr, m_end);
+                acc[q] = mfma32(a, b, acc[q]);
             }
         }
+        if (more) store_x(buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
+    }
+    float* out = part + (int64_t)split * D * r;
+#pragma unroll
+    for (int q = 0; q < TQ; ++q) {
+        const int j = 32 * q + l32;
+        if (j >= r) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int d = d0 + 32 * wave + 8 * (v >> 2) + 4 * h + (v & 3);
+            if (d < D) out[(int64_t)d * r + j] = acc[q][v];
+        }
+    }
 }
 
-// out[i] = sum_split part[split, i]   (fp32)
-__global__ void reduce_f32_kernel(const float* __restrict__ part, int splits, int64_t count, float* __restrict__ out) {
+// out[d * ld_d + j * ld_j] = sum_split part[split, d, j]   (fp32)
+__global__ void reduce_f32_kernel(const float* __restrict__ part, int splits, int D, int r, int64_t ld_d,
+                                  int64_t ld_j, float* __restrict__ out) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t count = (int64_t)D * r;
     if (i >= count) return;
     float acc = 0.0f;
     for (int p = 0; p < splits; ++p) acc += part[(int64_t)p * count + i];
-    out[i] = acc;
+    const int64_t d = i / r, j = i - d * r;
+    out[d * ld_d + j * ld_j] = acc;
 }
 
 __global__ void fill_f32_kernel(float* __restrict__ out, int64_t count, float v) {
@@ -179,16 +227,16 @@ qlora_status launch_transpose(const uint16_t* A, uint16_t* At, int K, int r, hip
     return launch_status();
 }
 
-qlora_status launch_nt(const uint16_t* X, const uint16_t* Yt, float* part, uint16_t* out, float scale, int M, int C,
-                       int r, hipStream_t s) {
+qlora_status launch_nt(const uint16_t* X, const uint16_t* Yt, float* part, uint16_t* out, uint16_t* outT,
+                       float scale, int M, int C, int r, hipStream_t s) {
     const SplitPlan sp = plan_nt(M, C);
-    const dim3 grid((unsigned)((M + 31) / 32), (unsigned)sp.splits);
+    const dim3 grid((unsigned)((M + 127) / 128), (unsigned)sp.splits);
     const bool vec = (C % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15u) == 0) &&
                      ((reinterpret_cast<uintptr_t>(Yt) & 15u) == 0);
     const int tq = (r + 31) / 32;
-#define QL_NT(TQ)                                                                                              \
-    if (vec) hipLaunchKernelGGL((nt_partial_kernel<TQ, true>), grid, dim3(64), 0, s, X, Yt, part, M, C, r, sp.chunk); \
-    else hipLaunchKernelGGL((nt_partial_kernel<TQ, false>), grid, dim3(64), 0, s, X, Yt, part, M, C, r, sp.chunk);
+#define QL_NT(TQ)                                                                                               \
+    if (vec) hipLaunchKernelGGL((nt_partial_kernel<TQ, true>), grid, dim3(256), 0, s, X, Yt, part, M, C, r, sp.chunk); \
+    else hipLaunchKernelGGL((nt_partial_kernel<TQ, false>), grid, dim3(256), 0, s, X, Yt, part, M, C, r, sp.chunk);
     switch (tq) {
         case 1: QL_NT(1) break;
         case 2: QL_NT(2) break;
@@ -197,40 +245,31 @@ qlora_status launch_nt(const uint16_t* X, const uint16_t* Yt, float* part, uint1
     }
 #undef QL_NT
     const int64_t count = (int64_t)M * r;
-    hipLaunchKernelGGL(finalize_bf16_kernel, dim3(blocks_for(count, 256)), dim3(256), 0, s, part, sp.splits, count,
-                       scale, out);
+    hipLaunchKernelGGL(finalize_bf16_kernel, dim3(blocks_for(count, 256)), dim3(256), 0, s, part, sp.splits, M, r,
+                       scale, out, outT);
     return launch_status();
 }
 
-qlora_status launch_tn(const uint16_t* P, const uint16_t* Q, float* part, float* out, int M, int Pd, int Qd,
-                       hipStream_t s) {
-    // the small dimension (r <= 128) is covered whole by one wave
-    const SplitPlan sp = plan_tn(M, Pd, Qd);
-    const int64_t count = (int64_t)Pd * Qd;
-    if (Qd <= 128 && Qd <= Pd) {
-        const int tq = (Qd + 31) / 32;
-        const dim3 grid((unsigned)((Pd + 31) / 32), 1u, (unsigned)sp.splits);
-#define QL_TN(TQ) hipLaunchKernelGGL((tn_partial_kernel<1, TQ>), grid, dim3(64), 0, s, P, Q, part, M, Pd, Qd, sp.chunk);
-        switch (tq) {
-            case 1: QL_TN(1) break;
-            case 2: QL_TN(2) break;
-            case 3: QL_TN(3) break;
-            default: QL_TN(4) break;
-        }
-#undef QL_TN
-    } else {
-        const int tp = (Pd + 31) / 32;
-        const dim3 grid(1u, (unsigned)((Qd + 31) / 32), (unsigned)sp.splits);
-#define QL_TN(TP) hipLaunchKernelGGL((tn_partial_kernel<TP, 1>), grid, dim3(64), 0, s, P, Q, part, M, Pd, Qd, sp.chunk);
-        switch (tp) {
-            case 1: QL_TN(1) break;
-            case 2: QL_TN(2) break;
-            case 3: QL_TN(3) break;
-            default: QL_TN(4) break;
-        }
-#undef QL_TN
+qlora_status launch_tn(const uint16_t* X, const uint16_t* ST, float* part, float* out, int M, int D, int r,
+                       int64_t ld_d, int64_t ld_j, hipStream_t s) {
+    const SplitPlan sp = plan_tn(M, D);
+    const dim3 grid((unsigned)((D + kTnCols - 1) / kTnCols), (unsigned)sp.splits);
+    const bool vec = (D % 8 == 0) && (M % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15u) == 0) &&
+                     ((reinterpret_cast<uintptr_t>(ST) & 15u) == 0);
+    const int tq = (r + 31) / 32;
+#define QL_TN(TQ)                                                                                                \
+    if (vec) hipLaunchKernelGGL((tn_partial_kernel<TQ, true>), grid, dim3(256), 0, s, X, ST, part, M, D, r, sp.chunk); \
+    else hipLaunchKernelGGL((tn_partial_kernel<TQ, false>), grid, dim3(256), 0, s, X, ST, part, M, D, r, sp.chunk);
+    switch (tq) {
+        case 1: QL_TN(1) break;
+        case 2: QL_TN(2) break;
+        case 3: QL_TN(3) break;
+        default: QL_TN(4) break;
     }
-    hipLaunchKernelGGL(reduce_f32_kernel, dim3(blocks_for(count, 256)), dim3(256), 0, s, part, sp.splits, count, out);
+#undef QL_TN
+    const int64_t count = (int64_t)D * r;
+    hipLaunchKernelGGL(reduce_f32_kernel, dim3(blocks_for(count, 256)), dim3(256), 0, s, part, sp.splits, D, r, ld_d,
+                       ld_j, out);
     return launch_status();
 }
 

@@ -12,10 +12,10 @@ struct SplitPlan {
     int chunk;   // reduction length per split (multiple of 16)
 };
 
-constexpr int kWaveTarget = 1024;  // waves to keep 256 CUs busy on an HBM-bound pass
+constexpr int kGroupTarget = 512;  // workgroups (2 per CU) for an HBM-bound pass
 
 inline SplitPlan make_plan(int64_t tiles, int64_t len, int min_len) {
-    int64_t want = std::max<int64_t>(1, kWaveTarget / std::max<int64_t>(1, tiles));
+    int64_t want = std::max<int64_t>(1, kGroupTarget / std::max<int64_t>(1, tiles));
     int64_t maxs = std::max<int64_t>(1, len / min_len);
     int64_t s = std::min(want, maxs);
     int64_t chunk = ((len + s - 1) / s + 15) / 16 * 16;
@@ -25,13 +25,11 @@ inline SplitPlan make_plan(int64_t tiles, int64_t len, int min_len) {
     return SplitPlan{(int)s, (int)chunk};
 }
 
-// out[M, r] = X[M, C] * Yt[r, C]^T : one wave per 32 rows of M and split of C
-inline SplitPlan plan_nt(int64_t M, int64_t C) { return make_plan((M + 31) / 32, C, 256); }
+// out[M, r] = X[M, C] * Yt[r, C]^T : one workgroup per 128 rows of M and split of C
+inline SplitPlan plan_nt(int64_t M, int64_t C) { return make_plan((M + 127) / 128, C, 256); }
 
-// out[Pd, Qd] = P[M, Pd]^T * Q[M, Qd] : one wave per 32 of the larger dim, splits over M
-inline SplitPlan plan_tn(int64_t M, int64_t Pd, int64_t Qd) {
-    return make_plan((std::max(Pd, Qd) + 31) / 32, M, 256);
-}
+// out[D, r] = X[M, D]^T * S[M, r] : one workgroup per 128 columns of X and split of M
+inline SplitPlan plan_tn(int64_t M, int64_t D) { return make_plan((D + 127) / 128, M, 128); }
 
 inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 

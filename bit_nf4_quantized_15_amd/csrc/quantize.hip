@@ -33,16 +33,22 @@ __device__ __forceinline__ uint32_t absmax_bits8(u32x4_t v) {
     return m;
 }
 
-// count of thresholds strictly below w (T ascending, 15 entries)
-__device__ __forceinline__ uint32_t nf4_code(float w, const float* T) {
-    const bool b3 = w > T[7];
-    const float t2 = b3 ? T[11] : T[3];
-    const bool b2 = w > t2;
-    const float t1 = b3 ? (b2 ? T[13] : T[9]) : (b2 ? T[5] : T[1]);
-    const bool b1 = w > t1;
-    const float t0 = b3 ? (b2 ? (b1 ? T[14] : T[12]) : (b1 ? T[10] : T[8]))
-                        : (b2 ? (b1 ? T[6] : T[4]) : (b1 ? T[2] : T[0]));
-    const bool b0 = w > t0;
+// count of thresholds strictly below w; the 15 ascending thresholds come as
+// four vectors (T0..T3, T4..T7, T8..T11, T12..T14 + unused).  Every select is
+// on register values, so nothing is indexed dynamically.
+__device__ __forceinline__ uint32_t nf4_code(float w, f32x4_t t0, f32x4_t t1, f32x4_t t2, f32x4_t t3) {
+    const bool b3 = w > t1[3];                                   // T7
+    const float s2 = b3 ? t2[3] : t0[3];                         // T11 : T3
+    const bool b2 = w > s2;
+    const float s1a = b3 ? t3[1] : t1[1];                        // T13 : T5
+    const float s1b = b3 ? t2[1] : t0[1];                        // T9  : T1
+    const bool b1 = w > (b2 ? s1a : s1b);
+    const float e3 = b3 ? t3[2] : t1[2];                         // T14 : T6
+    const float e2 = b3 ? t3[0] : t1[0];                         // T12 : T4
+    const float e1 = b3 ? t2[2] : t0[2];                         // T10 : T2
+    const float e0 = b3 ? t2[0] : t0[0];                         // T8  : T0
+    const float s0 = b2 ? (b1 ? e3 : e2) : (b1 ? e1 : e0);
+    const bool b0 = w > s0;
     return (b3 ? 8u : 0u) | (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
 }
 
@@ -133,18 +139,13 @@ __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint16_t* 
     for (int p = 0; p < kPasses; ++p) {
         const int bl = p * 32 + wave * 8 + (lane >> 3);
         if (bl < nb_here) {
-            float T[16];
             const f32x4_t* src = reinterpret_cast<const f32x4_t*>(&s_thr[bl * 16]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const f32x4_t t = src[i];
-                T[4 * i + 0] = t[0]; T[4 * i + 1] = t[1]; T[4 * i + 2] = t[2]; T[4 * i + 3] = t[3];
-            }
+            const f32x4_t t0 = src[0], t1 = src[1], t2 = src[2], t3 = src[3];
             uint32_t packed = 0;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const uint32_t bits = (i & 1) ? (v[p][i >> 1] >> 16) : (v[p][i >> 1] & 0xFFFFu);
-                const uint32_t q = nf4_code(bf16_bits_to_f32(bits), T);
+                const uint32_t q = nf4_code(bf16_bits_to_f32(bits), t0, t1, t2, t3);
                 packed |= q << (4 * (i ^ 1));
             }
             *reinterpret_cast<uint32_t*>(codes + (b0 + bl) * (kBlock / 2) + sub * 4) = packed;

@@ -42,6 +42,10 @@ def _load():
         "qlora_fwd_workspace": (c_sz, [c_i64, c_i64, c_i64, ctypes.c_int]),
         "qlora_linear_fwd": (ctypes.c_int, [P, c_vp, c_i64, c_vp, c_vp, ctypes.c_int, ctypes.c_float,
                                             c_vp, c_vp, c_vp, c_sz, c_vp]),
+        "qlora_lora_down_workspace": (c_sz, [c_i64, c_i64, ctypes.c_int]),
+        "qlora_lora_down": (ctypes.c_int, [c_vp, c_i64, c_i64, c_vp, ctypes.c_int, ctypes.c_float, c_vp, c_vp,
+                                           c_sz, c_vp]),
+        "qlora_fused_gemm_fwd": (ctypes.c_int, [P, c_vp, c_i64, c_vp, c_vp, ctypes.c_int, c_vp, c_vp]),
         "qlora_bwd_workspace": (c_sz, [c_i64, c_i64, c_i64, ctypes.c_int]),
         "qlora_linear_bwd": (ctypes.c_int, [P, c_vp, c_i64, c_vp, c_vp, ctypes.c_int, ctypes.c_float,
                                             c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
@@ -165,6 +169,33 @@ def linear_fwd(w, x, A, B, alpha, y=None, t=None, want_t=True, ws=None):
     _check(lib.qlora_linear_fwd(ctypes.byref(st), _ptr(x), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(y),
                                 _ptr(t), _ptr(wsb), wsn, _stream()), "qlora_linear_fwd")
     return y, t
+
+
+def lora_down(x, A, alpha, t=None, ws=None):
+    """t = (alpha/r) x A as bf16 [M, r] (qlora_lora_down)."""
+    M, K = x.shape
+    r = A.shape[1]
+    _dev(x, torch.bfloat16, "x")
+    _dev(A, torch.bfloat16, "A", (K, r))
+    t = torch.empty((M, r), dtype=torch.bfloat16, device=x.device) if t is None else _dev(t, torch.bfloat16, "t", (M, r))
+    wsb, wsn = _ws(int(lib.qlora_lora_down_workspace(M, K, r)), x.device, ws)
+    _check(lib.qlora_lora_down(_ptr(x), M, K, _ptr(A), r, float(alpha), _ptr(t), _ptr(wsb), wsn, _stream()),
+           "qlora_lora_down")
+    return t
+
+
+def fused_gemm_fwd(w, x, t, B, y=None):
+    """y = x W_hat + t B (qlora_fused_gemm_fwd): one kernel launch."""
+    M = x.shape[0]
+    r = t.shape[1]
+    _dev(x, torch.bfloat16, "x", (M, w.K))
+    _dev(t, torch.bfloat16, "t", (M, r))
+    _dev(B, torch.bfloat16, "B", (r, w.N))
+    y = torch.empty((M, w.N), dtype=torch.bfloat16, device=x.device) if y is None else _dev(y, torch.bfloat16, "y", (M, w.N))
+    st = w.state()
+    _check(lib.qlora_fused_gemm_fwd(ctypes.byref(st), _ptr(x), M, _ptr(t), _ptr(B), r, _ptr(y), _stream()),
+           "qlora_fused_gemm_fwd")
+    return y
 
 
 def linear_bwd(w, x, A, B, alpha, dy, t=None, need_dx=True, dx=None, dA=None, dB=None, ws=None):

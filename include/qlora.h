@@ -109,6 +109,24 @@ qlora_status qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, 
                               const uint16_t* B, int r, float alpha, uint16_t* y, uint16_t* t_out,
                               void* ws, size_t ws_bytes, void* stream);
 
+/* The two stages of qlora_linear_fwd, for callers that keep t across calls
+ * or time the stages separately.  qlora_linear_fwd is exactly
+ * qlora_lora_down followed by qlora_fused_gemm_fwd. */
+
+/* Workspace bytes qlora_lora_down needs (0 for M == 0). */
+size_t qlora_lora_down_workspace(int64_t M, int64_t K, int r);
+
+/* t = s * (x A) as bf16 [M, r], s = alpha / r (the LoRA down-projection,
+ * deep dive 12.2).  x [M, K] bf16 (K % 64 == 0), A [K, r] bf16, 1 <= r <= 128. */
+qlora_status qlora_lora_down(const uint16_t* x, int64_t M, int64_t K, const uint16_t* A, int r, float alpha,
+                             uint16_t* t_out, void* ws, size_t ws_bytes, void* stream);
+
+/* y = x W_hat + t B as bf16 [M, N]: the fused dequant GEMM with the LoRA
+ * up-projection folded in as r extra reduction steps.  t [M, r] bf16 (already
+ * scaled), B [r, N] bf16.  No workspace.  One kernel launch. */
+qlora_status qlora_fused_gemm_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uint16_t* t,
+                                  const uint16_t* B, int r, uint16_t* y, void* stream);
+
 /* Workspace bytes qlora_linear_bwd needs for these sizes. */
 size_t qlora_bwd_workspace(int64_t M, int64_t N, int64_t K, int r);
 
