@@ -98,6 +98,54 @@ __device__ __forceinline__ void load_tile_clamped(u32x4_t (&r)[8], const uint16_
     }
 }
 
+// Forward-kernel tile layout: the XOR swizzle uses only row % 32, so the
+// operand reads of rows R + 32 i (i = 0..3) differ by the immediate offset
+// 4096 i; 8 or 16 consecutive rows still cover distinct banks.
+__device__ __forceinline__ uint32_t ftile_off(int row, int chunk) {
+    return (uint32_t)row * 128u + ((uint32_t)(chunk ^ ((row ^ (row >> 3)) & 3 ^ (row & 4))) << 4);
+}
+
+__device__ __forceinline__ void store_ftile(uint8_t* lds, const u32x4_t (&r)[8], int tid) {
+    const int lr = tid >> 3, lc = tid & 7;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) *reinterpret_cast<u32x4_t*>(lds + ftile_off(lr + 32 * p, lc)) = r[p];
+}
+
+// ---- direct HBM -> LDS tile loads (buffer_load_dwordx4 ... lds).  Lane l of
+// an instruction writes 16 bytes at the instruction's LDS base + 16 l, so a
+// wave fills 8 consecutive tile rows (1 KB); the swizzle is applied on the
+// global side by choosing which 16-byte chunk each lane fetches.  Offsets past
+// the buffer's byte range read as zero (rows past M).
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+__device__ void raw_buffer_load_lds(i32x4_t rsrc, __attribute__((address_space(3))) uint32_t* lds_ptr, int size,
+                                    int voffset, int soffset, int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4_t r;
+    r[0] = (int32_t)(uint32_t)(a & 0xffffffffu);
+    r[1] = (int32_t)(uint32_t)(a >> 32);   // stride 0
+    r[2] = (int32_t)bytes;                 // num_records in bytes
+    r[3] = 0x00020000;                     // gfx9 buffer format word
+    return r;
+}
+
+// One 256 x 64 bf16 tile of a row-major matrix (row stride ld elements) whose
+// row 0 is the buffer base: columns [col0, col0 + 64) into `tile` (ftile
+// layout).  voff0 = this lane's byte offset of tile row 8*wave + lane/8, its
+// logical chunk, column 0.
+__device__ __forceinline__ void load_tile_direct(i32x4_t rs, uint8_t* tile, uint32_t voff0, int wave, int col0,
+                                                 int64_t ld) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        auto* dst = reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(
+            reinterpret_cast<uintptr_t>(tile + (32 * j + 8 * wave) * 128));
+        raw_buffer_load_lds(rs, dst, 16, (int)voff0, (int)(32 * j * ld * 2 + col0 * 2), 0, 0);
+    }
+}
+
+__device__ __forceinline__ void wait_direct_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ void store_tile(uint8_t* lds, const u32x4_t (&r)[8], int tid) {
     const int lr = tid >> 3, lc = tid & 7;
 #pragma unroll
@@ -159,174 +207,156 @@ __device__ __forceinline__ void store_acc(uint16_t* __restrict__ out, int64_t ld
 }
 
 // ------------------------------------------------------------------ forward
-// Waves in a 2 x 2 arrangement, each owning a 128 x 128 quarter of the output
-// tile (4 x 4 MFMA tiles).  Both operand tiles live in LDS, double buffered:
-//   A = x rows (HBM -> registers -> LDS),
-//   B = the dequantized weight rows: lane `tid` owns weight row n0 + tid and
-//       expands that row's 64-code block of the next step (one table per lane
-//       and step) while the MFMAs of the current step run.
-// The loop body is a single basic block (clamped indices instead of
-// branches) so the scheduler can interleave the dequant VALU work, the LDS
-// traffic and the MFMAs; sched_group_barrier pins that interleave.
-template <bool XVEC>
+// Wave w owns output columns [64w, 64w + 64) of the 256 x 256 tile, all 256
+// rows (8 x 2 MFMA tiles).  The x tile goes HBM -> registers -> LDS (double
+// buffered); every wave reads all of it (8 operand reads per 16 MFMAs).  The
+// weight never touches LDS: lane (h, l32) holds, for its two columns, the 16
+// code bytes of k = 32h .. 32h + 31 of the current block, builds each
+// column's 16-entry bf16 table once per step and expands 8 codes at a time
+// into the MFMA B operand just before use, interleaved with the MFMAs of the
+// previous chunk.  Codes and scale bytes arrive two steps ahead; the scale is
+// converted only when its table is built.
 __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ q8,
     const float* __restrict__ a2, const uint16_t* __restrict__ t, const uint16_t* __restrict__ Bl,
     uint16_t* __restrict__ y, int M, int N, int K, int r, int tiles_m, int tiles_n) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kTileBytes];
-    uint8_t* const ldsA0 = lds;
-    uint8_t* const ldsB0 = lds + 2 * kTileBytes;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kTileBytes];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, l32 = lane & 31;
-    const int wm = wave >> 1, wn = wave & 1;
     const int tile = xcd_tile(blockIdx.x, tiles_m * tiles_n);
     const int mt = tile / tiles_n, nt = tile - mt * tiles_n;
     const int m0 = mt * kTM, n0 = nt * kTN;
     const int KB = K / kTK;
 
-    // dequant role: weight row n0 + tid (rows past N read row N-1; never stored)
-    const int drow = min(n0 + tid, N - 1);
-    const uint8_t* crow = codes + (int64_t)drow * (K / 2);
-    const int64_t dblk = (int64_t)drow * KB;
+    int col[2];
+    const uint8_t* crow[2];
+    int64_t blk0[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        col[u] = n0 + wave * 64 + u * 32 + l32;
+        const int cr = min(col[u], N - 1);  // columns past N compute garbage that is never stored
+        crow[u] = codes + (int64_t)cr * (K / 2) + h * 16;
+        blk0[u] = (int64_t)cr * KB;
+    }
+    // A operand offsets: rows 32 i + l32, chunk 4h + c; row tiles are immediate offsets
+    uint32_t offA[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) offA[c] = ftile_off(l32, 4 * h + c);
 
-    f32x16_t acc[4][4];
+    f32x16_t acc[8][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][u][v] = 0.0f;
 
-    // raw inputs of one step's dequant: 32 code bytes, the block's 8-bit scale
-    // code and its group's fp32 scale (converted only when used, one step
-    // later, so that no wait on this step's loads is needed)
-    auto load_codes = [&](int ks, u32x4_t& c0, u32x4_t& c1, uint32_t& q, float& g) {
-        const uint8_t* p = crow + (int64_t)ks * (kTK / 2);
-        c0 = *reinterpret_cast<const u32x4_t*>(p);
-        c1 = *reinterpret_cast<const u32x4_t*>(p + 16);
-        const int64_t blk = dblk + ks;
-        q = q8[blk];
-        g = a2[blk >> 8];
+    struct Step {
+        u32x4_t c[2];
+        uint32_t q[2];
+        float g[2];
     };
-    auto dequant_store = [&](uint8_t* ldsB, const u32x4_t& c0, const u32x4_t& c1, uint32_t q, float g) {
-        const Nf4Tab T = make_tab(scale_step(g) * (float)q);
+    auto load_step = [&](int ks, Step& S) {
 #pragma unroll
-        for (int d = 0; d < 8; ++d) {
-            const uint32_t cw = d < 4 ? c0[d] : c1[d - 4];
-            *reinterpret_cast<u32x4_t*>(ldsB + tile_off(tid, d)) = deq8(T, cw);
+        for (int u = 0; u < 2; ++u) {
+            S.c[u] = *reinterpret_cast<const u32x4_t*>(crow[u] + (int64_t)ks * (kTK / 2));
+            const int64_t blk = blk0[u] + ks;
+            S.q[u] = q8[blk];
+            S.g[u] = a2[blk >> 8];
         }
     };
 
-    // prologue: A(0), B(0) in LDS; codes of step 1 in registers
-    u32x4_t xr[8];
-    load_tile_clamped<XVEC>(xr, x, K, m0, M, 0, tid);
-    u32x4_t c0, c1;
-    uint32_t cq;
-    float cg;
-    load_codes(0, c0, c1, cq, cg);
-    store_tile(ldsA0, xr, tid);
-    dequant_store(ldsB0, c0, c1, cq, cg);
-    load_codes(min(1, KB - 1), c0, c1, cq, cg);
+    // x panel rows [m0, M) as a buffer; lane's tile row 8*wave + lane/8, chunk
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const i32x4_t xrs = buffer_rsrc(x + (int64_t)m0 * K, (uint32_t)((int64_t)(M - m0) * K * 2));
+    const int xrow = 8 * wv + (lane >> 3);
+    const int xchunk = (lane & 7) ^ (((xrow ^ (xrow >> 3)) & 3) ^ (xrow & 4));
+    const uint32_t xvoff = (uint32_t)(((int64_t)xrow * K + 8 * xchunk) * 2);
+
+    load_tile_direct(xrs, lds, xvoff, wv, 0, K);
+    Step cur, nxt;
+    load_step(0, cur);
+    load_step(min(1, KB - 1), nxt);
+    Nf4Tab T[2];
+    bf16x8 b[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        T[u] = make_tab(scale_step(cur.g[u]) * (float)cur.q[u]);
+        b[0][u] = as_bf16x8(deq8(T[u], cur.c[u][0]));
+    }
+    wait_direct_loads();
     __syncthreads();
 
+    // Software pipeline per step ks: operand reads of chunk c+1 and the
+    // expansion of chunk c+1's codes overlap the MFMAs of chunk c; the tables
+    // of step ks+1 are built while chunk 0's reads are in flight and its
+    // chunk-0 operands are expanded during chunk 3.
     for (int ks = 0; ks < KB; ++ks) {
-        const int buf = ks & 1;
-        const uint8_t* A = ldsA0 + buf * kTileBytes;
-        const uint8_t* B = ldsB0 + buf * kTileBytes;
-        uint8_t* An = ldsA0 + (buf ^ 1) * kTileBytes;
-        uint8_t* Bn = ldsB0 + (buf ^ 1) * kTileBytes;
-        // next step's operands: x tile (ks+1) and codes (ks+2) from HBM
-        load_tile_clamped<XVEC>(xr, x, K, m0, M, min(ks + 1, KB - 1) * kTK, tid);
-        u32x4_t n0c, n1c;
-        uint32_t nq;
-        float ng;
-        load_codes(min(ks + 2, KB - 1), n0c, n1c, nq, ng);
-        // step ks+1's codes are expanded between this step's MFMAs (register
-        // work only); all LDS writes follow this step's LDS reads.
-        const Nf4Tab T = make_tab(scale_step(cg) * (float)cq);
-        u32x4_t deq[8];
+        const uint8_t* A = lds + (ks & 1) * kTileBytes;
+        uint8_t* An = lds + ((ks + 1) & 1) * kTileBytes;
+        bf16x8 a[2][8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[0][i] = *reinterpret_cast<const bf16x8*>(A + offA[0] + 4096u * i);
+        load_tile_direct(xrs, An, xvoff, wv, min(ks + 1, KB - 1) * kTK, K);
+        Step nn;
+        load_step(min(ks + 2, KB - 1), nn);
+        Nf4Tab Tn[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) Tn[u] = make_tab(scale_step(nxt.g[u]) * (float)nxt.q[u]);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            bf16x8 a[4], b[4];
+            const int p = c & 1;
+            if (c < 3) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = lds_operand(A, 128 * wm + 32 * i + l32, 4 * h + c);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) b[u] = lds_operand(B, 128 * wn + 32 * u + l32, 4 * h + c);
-            deq[2 * c] = deq8(T, c < 2 ? c0[2 * c] : c1[2 * c - 4]);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int u = 0; u < 4; ++u) acc[i][u] = mfma32(a[i], b[u], acc[i][u]);
-            deq[2 * c + 1] = deq8(T, c < 2 ? c0[2 * c + 1] : c1[2 * c - 3]);
-#pragma unroll
-            for (int i = 2; i < 4; ++i)
-#pragma unroll
-                for (int u = 0; u < 4; ++u) acc[i][u] = mfma32(a[i], b[u], acc[i][u]);
-            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // the 8 operand reads
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // 4 VALU
+                for (int i = 0; i < 8; ++i) a[p ^ 1][i] = *reinterpret_cast<const bf16x8*>(A + offA[c + 1] + 4096u * i);
             }
-        }
 #pragma unroll
-        for (int d = 0; d < 8; ++d) *reinterpret_cast<u32x4_t*>(Bn + tile_off(tid, d)) = deq[d];
-        store_tile(An, xr, tid);
-        c0 = n0c;
-        c1 = n1c;
-        cq = nq;
-        cg = ng;
+            for (int i = 0; i < 4; ++i) {
+                acc[i][0] = mfma32(a[p][i], b[p][0], acc[i][0]);
+                acc[i][1] = mfma32(a[p][i], b[p][1], acc[i][1]);
+            }
+            b[p ^ 1][0] = as_bf16x8(c < 3 ? deq8(T[0], cur.c[0][c + 1]) : deq8(Tn[0], nxt.c[0][0]));
+#pragma unroll
+            for (int i = 4; i < 8; ++i) {
+                acc[i][0] = mfma32(a[p][i], b[p][0], acc[i][0]);
+                acc[i][1] = mfma32(a[p][i], b[p][1], acc[i][1]);
+            }
+            b[p ^ 1][1] = as_bf16x8(c < 3 ? deq8(T[1], cur.c[1][c + 1]) : deq8(Tn[1], nxt.c[1][0]));
+        }
+        // chunk 3 used b[1]; the expansion of step ks+1's chunk 0 is in b[0]
+#pragma unroll
+        for (int u = 0; u < 2; ++u) T[u] = Tn[u];
+        cur = nxt;
+        nxt = nn;
+        wait_direct_loads();
         __syncthreads();
     }
 
-    // LoRA up-projection: r more reduction steps, A = t [M, r], B = B^T staged
-    // in LDS (lane tid copies column n0 + tid of B).
-    const int bn = n0 + tid;
+    u32x4_t xr[8];
+    // LoRA up-projection: r more reduction steps with A-operand t [M, r] and
+    // B-operand B [r, N] (t already carries the alpha/r scale).
+    const bool col_ok0 = col[0] < N, col_ok1 = col[1] < N;
     for (int j0 = 0; j0 < r; j0 += kTK) {
         load_tile<false>(xr, t, r, m0, M, j0, r, tid);
-        store_tile(ldsA0, xr, tid);
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-            uint32_t w[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int ja = j0 + 8 * d + 2 * e, jb = ja + 1;
-                const uint32_t lo = (bn < N && ja < r) ? Bl[(int64_t)ja * N + bn] : 0u;
-                const uint32_t hi = (bn < N && jb < r) ? Bl[(int64_t)jb * N + bn] : 0u;
-                w[e] = lo | (hi << 16);
-            }
-            *reinterpret_cast<u32x4_t*>(ldsB0 + tile_off(tid, d)) = u32x4_t{w[0], w[1], w[2], w[3]};
-        }
+        store_ftile(lds, xr, tid);
         __syncthreads();
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            bf16x8 a[4], b[4];
+            const bf16x8 bl0 = gather8(Bl, N, j0 + 32 * h + 8 * c, r, col[0], col_ok0);
+            const bf16x8 bl1 = gather8(Bl, N, j0 + 32 * h + 8 * c, r, col[1], col_ok1);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = lds_operand(ldsA0, 128 * wm + 32 * i + l32, 4 * h + c);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) b[u] = lds_operand(ldsB0, 128 * wn + 32 * u + l32, 4 * h + c);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int u = 0; u < 4; ++u) acc[i][u] = mfma32(a[i], b[u], acc[i][u]);
+            for (int i = 0; i < 8; ++i) {
+                const bf16x8 av = *reinterpret_cast<const bf16x8*>(lds + offA[c] + 4096u * i);
+                acc[i][0] = mfma32(av, bl0, acc[i][0]);
+                acc[i][1] = mfma32(av, bl1, acc[i][1]);
+            }
         }
         __syncthreads();
     }
 
-    // epilogue
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int col = n0 + 128 * wn + 32 * u + l32;
-        if (col >= N) continue;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int m = m0 + 128 * wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-                if (m < M) y[(int64_t)m * N + col] = (uint16_t)(pack_bf16x2(acc[i][u][v], 0.0f) & 0xFFFFu);
-            }
-    }
+    const bool col_ok[2] = {col_ok0, col_ok1};
+    store_acc(y, N, acc, m0, M, col, col_ok, h);
 }
 
 // ------------------------------------------------------------------ backward dx
@@ -455,13 +485,11 @@ qlora_status launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const uint
                              const uint16_t* t, const uint16_t* B, uint16_t* y, int M, int N, int K, int r,
                              hipStream_t s) {
     const int tm = (M + kTM - 1) / kTM, tn = (N + kTN - 1) / kTN;
-    const bool vec = (reinterpret_cast<uintptr_t>(x) & 15u) == 0;  // K % 64 == 0 always
-    if (vec)
-        hipLaunchKernelGGL(nf4_gemm_fwd_kernel<true>, dim3(tm * tn), dim3(kT), 0, s, x, codes, q8, a2, t, B, y, M,
-                           N, K, r, tm, tn);
-    else
-        hipLaunchKernelGGL(nf4_gemm_fwd_kernel<false>, dim3(tm * tn), dim3(kT), 0, s, x, codes, q8, a2, t, B, y,
-                           M, N, K, r, tm, tn);
+    // x is 16-byte aligned (checked by the caller) and K % 64 == 0, so every
+    // 16-byte chunk of a row is aligned; a 256-row panel must fit a 32-bit offset
+    if ((int64_t)kTM * K * 2 >= (int64_t(1) << 32)) return QLORA_ERR_UNSUPPORTED_SHAPE;
+    hipLaunchKernelGGL(nf4_gemm_fwd_kernel, dim3(tm * tn), dim3(kT), 0, s, x, codes, q8, a2, t, B, y, M, N, K, r,
+                       tm, tn);
     return launch_status();
 }
 
