@@ -360,123 +360,219 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
 }
 
 // ------------------------------------------------------------------ backward dx
+// dx[m, k] = sum_n dy[m, n] w_hat[n, k]: the reduction runs across rows of the
+// stored codes.  Each step covers 64 rows n: lane (n = tid % 64, block = tid / 64)
+// expands one 64-code block of row n with its own table into 8 x 16-byte
+// stores of a natural [n][k] weight tile in LDS; the MFMA B operand (8
+// consecutive n of one column k) is then read with ds_read_b64_tr_b16, which
+// hands lane j of a 16-lane group element j of the 4-element row pieces
+// addressed by 4 lanes (rows R..R+3 -> 4 consecutive n of column j).  The dy
+// tile arrives by direct HBM -> LDS loads.  Waves are 2 x 2 (128 x 128 each);
+// the next step's codes arrive two steps ahead and are expanded while this
+// step's MFMAs run.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// weight tile layout: 64 rows of 256 bf16 (512 B), 16-byte chunks XOR-swizzled
+// by a 4-bit function of the row (conflict-free 16-byte row stores and
+// transposed 8-byte reads)
+__device__ __forceinline__ uint32_t wtile_off(int row, int col) {
+    const int f = ((row & 3) << 2) | ((row >> 2) & 3);
+    return (uint32_t)row * 512u + ((uint32_t)((col >> 3) ^ f) << 4) + ((uint32_t)(col & 7) << 1);
+}
+
 template <bool DYVEC>
 __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
     const uint16_t* __restrict__ dy, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ q8,
     const float* __restrict__ a2, const uint16_t* __restrict__ u_, const uint16_t* __restrict__ Al,
     uint16_t* __restrict__ dx, int M, int N, int K, int r, int tiles_m, int tiles_k) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds_a[2 * kTileBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_b[kTileBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kTileBytes];
+    uint8_t* const ldsA0 = lds;                      // dy tiles (ftile layout), 2 buffers
+    uint8_t* const ldsB0 = lds + 2 * kTileBytes;     // weight tiles (wtile layout), 2 buffers
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, l32 = lane & 31;
+    const int wm = wave >> 1, wk = wave & 1;
     const int tile = xcd_tile(blockIdx.x, tiles_m * tiles_k);
     const int mt = tile / tiles_k, kt = tile - mt * tiles_k;
     const int m0 = mt * kTM, k0 = kt * kTN;
     const int KB = K / kTK;
     const int NS = (N + kTK - 1) / kTK;
 
-    // dequant role: row n0 + (tid >> 2) of the current step, block k0/64 + (tid & 3)
-    const int dq_row = tid >> 2, dq_blk = tid & 3;
-    const int dq_kcol = k0 + dq_blk * kTK;         // first output column of the block
-    const bool dq_kok = dq_kcol < K;
-
-    // MFMA role: output columns k0 + 64 w + 32 u + l32
-    int col[2];
-    bool col_ok[2];
+    // dequant role
+    const int dn = tid & 63, dkb = tid >> 6;
+    const int dkcol = k0 + dkb * kTK;                 // first column of this lane's block
+    const bool dk_ok = dkcol < K;
+    struct Step {
+        u32x4_t c0, c1;
+        uint32_t q;
+        float g;
+    };
+    // rows past N / blocks past K read a valid block and get scale code 0,
+    // i.e. all-zero weights (branch-free, so the loop stays one basic block)
+    const int dkc = dk_ok ? dkcol : K - kTK;
+    auto load_step = [&](int ns, Step& S) {
+        const int n = ns * kTK + dn;
+        const int nc = min(n, N - 1);
+        const uint8_t* p = codes + (int64_t)nc * (K / 2) + dkc / 2;
+        S.c0 = *reinterpret_cast<const u32x4_t*>(p);
+        S.c1 = *reinterpret_cast<const u32x4_t*>(p + 16);
+        const int64_t blk = (int64_t)nc * KB + dkc / kTK;
+        uint32_t q = q8[blk];
+        asm volatile("" : "+v"(q));   // unconditional load, then select (no branch)
+        S.q = (n < N && dk_ok) ? q : 0u;
+        S.g = a2[blk >> 8];
+    };
+    auto expand = [&](const Step& S, u32x4_t (&out)[8]) {
+        const Nf4Tab T = make_tab(scale_step(S.g) * (float)S.q);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        col[u] = k0 + wave * 64 + u * 32 + l32;
-        col_ok[u] = col[u] < K;
+        for (int d = 0; d < 8; ++d) out[d] = deq8(T, d < 4 ? S.c0[d] : S.c1[d - 4]);
+    };
+    auto store_w = [&](uint8_t* Bt, const u32x4_t (&w)[8]) {
+#pragma unroll
+        for (int d = 0; d < 8; ++d) *reinterpret_cast<u32x4_t*>(Bt + wtile_off(dn, dkb * kTK + 8 * d)) = w[d];
+    };
+
+    // MFMA operand addresses
+    uint32_t offA[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) offA[c] = ftile_off(l32, 2 * c + h);   // + 4096*(4wm + i)
+    // transposed reads: group lane j = l32 % 16 -> row 8h + 4*s2 + j/4 (+16c), column
+    // 128wk + 32u + 16*(l32/16) + 4*(j%4)
+    uint32_t offB[4][2];
+    {
+        const int j = l32 & 15, g = l32 >> 4;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+                offB[u][s2] = wtile_off(8 * h + 4 * s2 + (j >> 2), 128 * wk + 32 * u + 16 * g + 4 * (j & 3));
     }
+    auto read_ops = [&](const uint8_t* A, const uint8_t* Bt, int c, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            a[i] = *reinterpret_cast<const bf16x8*>(A + offA[c] + 4096u * (4 * wm + i));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                reinterpret_cast<__attribute__((address_space(3))) s16x4_t*>(
+                    reinterpret_cast<uintptr_t>(Bt + offB[u][0] + 8192u * c)));
+            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                reinterpret_cast<__attribute__((address_space(3))) s16x4_t*>(
+                    reinterpret_cast<uintptr_t>(Bt + offB[u][1] + 8192u * c)));
+            b[u] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    };
 
-    f32x16_t acc[8][2];
+    f32x16_t acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][u][v] = 0.0f;
 
+    // dy panel rows [m0, M): direct loads when rows are 16-byte aligned
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const i32x4_t drs = buffer_rsrc(dy + (int64_t)m0 * N, (uint32_t)((int64_t)(M - m0) * N * 2));
+    const int xrow = 8 * wv + (lane >> 3);
+    const int xchunk = (lane & 7) ^ (((xrow ^ (xrow >> 3)) & 3) ^ (xrow & 4));
+    const uint32_t dvoff = (uint32_t)(((int64_t)xrow * N + 8 * xchunk) * 2);
     u32x4_t ar[8];
-    load_tile<DYVEC>(ar, dy, N, m0, M, 0, N, tid);
-    store_tile(lds_a, ar, tid);
+    auto load_dy = [&](uint8_t* A, int ns) {
+        if (DYVEC) {
+            load_tile_direct(drs, A, dvoff, wv, ns * kTK, N);
+        } else {
+            load_tile<false>(ar, dy, N, m0, M, ns * kTK, N, tid);
+            store_ftile(A, ar, tid);
+        }
+    };
+
+    // prologue
+    Step cur, nxt;
+    load_dy(ldsA0, 0);
+    load_step(0, cur);
+    load_step(min(1, NS - 1), nxt);
+    {
+        u32x4_t w[8];
+        expand(cur, w);
+        store_w(ldsB0, w);
+    }
+    wait_direct_loads();
+    __syncthreads();
 
     for (int ns = 0; ns < NS; ++ns) {
         const int buf = ns & 1;
-        const bool more = ns + 1 < NS;
-        // this step's weight tile: rows n = 64 ns + dq_row, one block per lane
-        {
-            const int n = ns * kTK + dq_row;
-            u32x4_t c0 = u32x4_t{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
-            u32x4_t c1 = c0;
-            float ah = 0.0f;
-            if (n < N && dq_kok) {
-                const uint8_t* p = codes + (int64_t)n * (K / 2) + dq_kcol / 2;
-                c0 = *reinterpret_cast<const u32x4_t*>(p);
-                c1 = *reinterpret_cast<const u32x4_t*>(p + 16);
-                ah = block_ahat(q8, a2, (int64_t)n * KB + dq_kcol / kTK);
-            }
-            if (more) load_tile<DYVEC>(ar, dy, N, m0, M, (ns + 1) * kTK, N, tid);
-            const Nf4Tab T = make_tab(ah);  // a_hat = 0 (masked rows) gives all-zero weights
-            const int chunk = dq_row >> 3;
-            const uint32_t sub = (uint32_t)(dq_row & 7) * 2u;
-#pragma unroll
-            for (int d = 0; d < 8; ++d) {
-                const uint32_t cw = d < 4 ? c0[d] : c1[d - 4];
-                const u32x4_t eo = deq8_evens_odds(T, cw);  // [w0|w2] [w4|w6] [w1|w3] [w5|w7]
-                const int kr = dq_blk * kTK + 8 * d;          // tile row of weight 0 of this dword
-                uint8_t* b = lds_b + sub;
-                *reinterpret_cast<uint16_t*>(b + tile_off(kr + 0, chunk)) = (uint16_t)(eo[0] & 0xFFFFu);
-                *reinterpret_cast<uint16_t*>(b + tile_off(kr + 2, chunk)) = (uint16_t)(eo[0] >> 16);
-                *reinterpret_cast<uint16_t*>(b + tile_off(kr + 4, chunk)) = (uint16_t)(eo[1] & 0xFFFFu);
-                *reinterpret_cast<uint16_t*>(b + tile_off(kr + 6, chunk)) = (uint16_t)(eo[1] >> 16);
-                *reinterpret_cast<uint16_t*>(b + tile_off(kr + 1, chunk)) = (uint16_t)(eo[2] & 0xFFFFu);
-                *reinterpret_cast<uint16_t*>(b + tile_off(kr + 3, chunk)) = (uint16_t)(eo[2] >> 16);
-                *reinterpret_cast<uint16_t*>(b + tile_off(kr + 5, chunk)) = (uint16_t)(eo[3] & 0xFFFFu);
-                *reinterpret_cast<uint16_t*>(b + tile_off(kr + 7, chunk)) = (uint16_t)(eo[3] >> 16);
-            }
-        }
-        __syncthreads();  // activation tile `buf` and the weight tile are complete
-        const uint8_t* base = lds_a + buf * kTileBytes;
+        const uint8_t* A = ldsA0 + buf * kTileBytes;
+        const uint8_t* Bt = ldsB0 + buf * kTileBytes;
+        uint8_t* An = ldsA0 + (buf ^ 1) * kTileBytes;
+        uint8_t* Bn = ldsB0 + (buf ^ 1) * kTileBytes;
+        bf16x8 a[2][4], b[2][4];
+        read_ops(A, Bt, 0, a[0], b[0]);
+        load_dy(An, min(ns + 1, NS - 1));
+        Step nn;
+        load_step(min(ns + 2, NS - 1), nn);
+        u32x4_t w[8];
+        const Nf4Tab T = make_tab(scale_step(nxt.g) * (float)nxt.q);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            bf16x8 b[2];
+            const int p = c & 1;
+            if (c < 3) read_ops(A, Bt, c + 1, a[p ^ 1], b[p ^ 1]);
+            w[2 * c] = deq8(T, c < 2 ? nxt.c0[2 * c] : nxt.c1[2 * c - 4]);
 #pragma unroll
-            for (int u = 0; u < 2; ++u) b[u] = lds_operand(lds_b, wave * 64 + u * 32 + l32, 4 * h + c);
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const bf16x8 a = lds_operand(base, 32 * i + l32, 4 * h + c);
-                acc[i][0] = mfma32(a, b[0], acc[i][0]);
-                acc[i][1] = mfma32(a, b[1], acc[i][1]);
-            }
+                for (int u = 0; u < 4; ++u) acc[i][u] = mfma32(a[p][i], b[p][u], acc[i][u]);
+            w[2 * c + 1] = deq8(T, c < 2 ? nxt.c0[2 * c + 1] : nxt.c1[2 * c - 3]);
+#pragma unroll
+            for (int i = 2; i < 4; ++i)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc[i][u] = mfma32(a[p][i], b[p][u], acc[i][u]);
         }
-        if (more) store_tile(lds_a + (buf ^ 1) * kTileBytes, ar, tid);
-        __syncthreads();  // everyone is done with lds_b and lds_a[buf]
+        store_w(Bn, w);
+        cur = nxt;
+        nxt = nn;
+        wait_direct_loads();
+        __syncthreads();
     }
 
-    // LoRA: r more reduction steps with A-operand u [M, r] and B-operand A^T,
-    // i.e. A [K, r] read along its rows.
+    // LoRA: r more reduction steps with A-operand u [M, r] (LDS) and B-operand
+    // A^T, i.e. rows of A [K, r] read directly.
     for (int j0 = 0; j0 < r; j0 += kTK) {
         load_tile<false>(ar, u_, r, m0, M, j0, r, tid);
-        store_tile(lds_a, ar, tid);
+        store_ftile(ldsA0, ar, tid);
         __syncthreads();
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            bf16x8 b[2];
+            bf16x8 a[4], b[4];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) b[u] = row8(Al, r, col[u], col_ok[u], j0 + 32 * h + 8 * c, r);
+            for (int i = 0; i < 4; ++i)
+                a[i] = *reinterpret_cast<const bf16x8*>(ldsA0 + offA[c] + 4096u * (4 * wm + i));
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const bf16x8 a = lds_operand(lds_a, 32 * i + l32, 4 * h + c);
-                acc[i][0] = mfma32(a, b[0], acc[i][0]);
-                acc[i][1] = mfma32(a, b[1], acc[i][1]);
+            for (int u = 0; u < 4; ++u) {
+                const int col = k0 + 128 * wk + 32 * u + l32;
+                b[u] = row8(Al, r, col, col < K, j0 + 16 * c + 8 * h, r);
             }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc[i][u] = mfma32(a[i], b[u], acc[i][u]);
         }
         __syncthreads();
     }
 
-    store_acc(dx, K, acc, m0, M, col, col_ok, h);
+    // epilogue: lane holds column l32 of each 32 x 32 tile, rows 8*(v/4) + 4h + v%4
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int col = k0 + 128 * wk + 32 * u + l32;
+        if (col >= K) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int m = m0 + 128 * wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+                if (m < M) dx[(int64_t)m * K + col] = (uint16_t)(pack_bf16x2(acc[i][u][v], 0.0f) & 0xFFFFu);
+            }
+    }
 }
 
 }  // namespace
@@ -497,7 +593,8 @@ qlora_status launch_gemm_bwd_dx(const uint16_t* dy, const uint8_t* codes, const 
                                 const uint16_t* u, const uint16_t* A, uint16_t* dx, int M, int N, int K, int r,
                                 hipStream_t s) {
     const int tm = (M + kTM - 1) / kTM, tk = (K + kTN - 1) / kTN;
-    const bool vec = (N % 8 == 0) && ((reinterpret_cast<uintptr_t>(dy) & 15u) == 0);
+    const bool vec = (N % 8 == 0) && ((reinterpret_cast<uintptr_t>(dy) & 15u) == 0) &&
+                     ((int64_t)kTM * N * 2 < (int64_t(1) << 32));
     if (vec)
         hipLaunchKernelGGL(nf4_gemm_bwd_dx_kernel<true>, dim3(tm * tk), dim3(kT), 0, s, dy, codes, q8, a2, u, A,
                            dx, M, N, K, r, tm, tk);
