@@ -39,6 +39,18 @@ __device__ __forceinline__ f32x16_t mfma32(bf16x8 a, bf16x8 b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Scheduling pattern for one chunk of a main loop: the next chunk's operand
+// reads first, then 16 MFMAs each followed by up to 4 VALU instructions, so
+// that no VALU run outlasts the 32-cycle MFMA in flight (one wave per SIMD).
+#define QLORA_INTERLEAVE(NREADS)                                        \
+    do {                                                                \
+        if ((NREADS) > 0) __builtin_amdgcn_sched_group_barrier(0x100, (NREADS), 0); \
+        _Pragma("unroll") for (int j_ = 0; j_ < 16; ++j_) {             \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          \
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);          \
+        }                                                               \
+    } while (0)
+
 // Map a linear workgroup id to a tile id so that the workgroups placed on one
 // XCD (ids are dealt round-robin over the 8 XCDs) get a contiguous run of
 // tiles, i.e. share activation rows and weight columns in that XCD's L2.
@@ -527,6 +539,7 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
             for (int i = 2; i < 4; ++i)
 #pragma unroll
                 for (int u = 0; u < 4; ++u) acc[i][u] = mfma32(a[p][i], b[p][u], acc[i][u]);
+            if (c < 3) QLORA_INTERLEAVE(12); else QLORA_INTERLEAVE(0);
         }
         store_w(Bn, w);
         cur = nxt;
