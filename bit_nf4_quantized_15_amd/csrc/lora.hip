@@ -17,6 +17,7 @@ namespace qlora {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x16_t mfma32(bf16x8 a, bf16x8 b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -52,14 +53,18 @@ __global__ void transpose_kernel(const uint16_t* __restrict__ A, uint16_t* __res
 
 // part[split, m, j] = sum over c in the split's range of X[m, c] * Yt[j, c]
 // Workgroup = 4 waves = 4 tiles of 32 rows of M; TQ 32-wide tiles of j.  The
-// reduction runs in steps of 64: lane half h takes c + 32h .. c + 32h + 31 as
-// four 16-byte loads (the two halves of an MFMA's k slots may map to any
-// reduction indices, as long as both operands agree), and the next step's
-// loads are issued before this step's MFMAs.
+// reduction runs in steps of 64: lane half h takes c + 32h .. c + 32h + 31 of
+// its X row as four 16-byte loads (the two halves of an MFMA's k slots may
+// map to any reduction indices, as long as both operands agree).  The Yt
+// chunk of a step (32*TQ rows x 64) is shared by the 4 waves, so it is staged
+// once per workgroup in LDS (double buffered); X is prefetched one step ahead.
 template <int TQ, bool VEC>
 __global__ __launch_bounds__(256) void nt_partial_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Yt,
                                                          float* __restrict__ part, int M, int C, int r, int chunk) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, l32 = lane & 31;
+    constexpr int kRows = 32 * TQ;                     // staged Yt rows
+    constexpr int kLd = 64 + 8;                        // padded row (bf16), 144 B
+    __shared__ __attribute__((aligned(16))) uint16_t ys[2][kRows * kLd];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
     const int m0 = blockIdx.x * 128 + wave * 32;
     const int split = blockIdx.y;
     const int c_begin = split * chunk;
@@ -69,30 +74,43 @@ __global__ __launch_bounds__(256) void nt_partial_kernel(const uint16_t* __restr
     for (int q = 0; q < TQ; ++q)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[q][v] = 0.0f;
-    bf16x8 xa[4], yb[TQ][4];
-    auto load = [&](int c) {
+    bf16x8 xa[4];
+    auto load_x = [&](int c) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int cc = c + 32 * h + 8 * i;
-            xa[i] = load8_row<VEC>(X, C, m0 + l32, M, cc, c_end);
+        for (int i = 0; i < 4; ++i) xa[i] = load8_row<VEC>(X, C, m0 + l32, M, c + 32 * h + 8 * i, c_end);
+    };
+    // Yt staging: kRows x 8 chunks of 16 B over 256 lanes
+    auto stage_y = [&](int c, int buf) {
 #pragma unroll
-            for (int q = 0; q < TQ; ++q) yb[q][i] = load8_row<VEC>(Yt, C, 32 * q + l32, r, cc, c_end);
+        for (int e = tid; e < kRows * 8; e += 256) {
+            const int row = e >> 3, ch = e & 7;
+            *reinterpret_cast<bf16x8*>(&ys[buf][row * kLd + 8 * ch]) = load8_row<VEC>(Yt, C, row, r, c + 8 * ch, c_end);
         }
     };
-    if (c_begin < c_end) load(c_begin);
+    if (c_begin < c_end) {
+        load_x(c_begin);
+        stage_y(c_begin, 0);
+    }
+    __syncthreads();
+    int buf = 0;
     for (int c = c_begin; c < c_end; c += 64) {
-        bf16x8 ca[4], cb[TQ][4];
+        bf16x8 ca[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            ca[i] = xa[i];
-#pragma unroll
-            for (int q = 0; q < TQ; ++q) cb[q][i] = yb[q][i];
+        for (int i = 0; i < 4; ++i) ca[i] = xa[i];
+        const bool more = c + 64 < c_end;
+        if (more) {
+            load_x(c + 64);
+            stage_y(c + 64, buf ^ 1);
         }
-        if (c + 64 < c_end) load(c + 64);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int q = 0; q < TQ; ++q) acc[q] = mfma32(ca[i], cb[q][i], acc[q]);
+            for (int q = 0; q < TQ; ++q) {
+                const bf16x8 yb = *reinterpret_cast<const bf16x8*>(&ys[buf][(32 * q + l32) * kLd + 32 * h + 8 * i]);
+                acc[q] = mfma32(ca[i], yb, acc[q]);
+            }
+        __syncthreads();
+        buf ^= 1;
     }
     float* out = part + (int64_t)split * M * r;
 #pragma unroll
@@ -129,7 +147,7 @@ __global__ void finalize_bf16_kernel(const float* __restrict__ part, int splits,
 // buffered, next tile prefetched into registers) and read back down its
 // columns for the MFMA A operand (8 consecutive m per lane); the B operand is
 // 8 consecutive m of a row of ST (one 16-byte load).
-constexpr int kTnRows = 64, kTnCols = 128, kTnLd = kTnCols + 8;  // +8: conflict-free column reads
+constexpr int kTnRows = 64, kTnCols = 128, kTnLd = kTnCols + 32;  // 320-byte rows: conflict-free transposed reads
 
 template <int TQ, bool VEC>
 __global__ __launch_bounds__(256) void tn_partial_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ ST,
@@ -162,7 +180,11 @@ __global__ __launch_bounds__(256) void tn_partial_kernel(const uint16_t* __restr
         store_x(0);
     }
     __syncthreads();
-    const int dcol = 32 * wave + l32;   // this lane's column of the tile (A operand row)
+    // A operand = X^T: 8 consecutive m of column d = 32*wave + l32, read with two
+    // ds_read_b64_tr_b16 (16-lane group lane j gets element j of the 4-element
+    // row pieces addressed by lanes j%4 + 4e -> rows R + e, columns C0 + 4*(j%4))
+    const int tj = l32 & 15, tg = l32 >> 4;
+    const int trow = tj >> 2, tcol = 32 * wave + 16 * tg + 4 * (tj & 3);
     int buf = 0;
     for (int m = m_begin; m < m_end; m += kTnRows) {
         const bool more = m + kTnRows < m_end;
@@ -170,14 +192,13 @@ __global__ __launch_bounds__(256) void tn_partial_kernel(const uint16_t* __restr
 #pragma unroll
         for (int mc = 0; mc < kTnRows / 16; ++mc) {
             const int mr = mc * 16 + 8 * h;   // tile row of this lane's first k slot
-            uint32_t w[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t lo = tile[buf][(mr + 2 * i) * kTnLd + dcol];
-                const uint32_t hi = tile[buf][(mr + 2 * i + 1) * kTnLd + dcol];
-                w[i] = lo | (hi << 16);
-            }
-            const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4_t{w[0], w[1], w[2], w[3]});
+            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                reinterpret_cast<__attribute__((address_space(3))) s16x4_t*>(
+                    reinterpret_cast<uintptr_t>(&tile[buf][(mr + trow) * kTnLd + tcol])));
+            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                reinterpret_cast<__attribute__((address_space(3))) s16x4_t*>(
+                    reinterpret_cast<uintptr_t>(&tile[buf][(mr + 4 + trow) * kTnLd + tcol])));
+            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
             for (int q = 0; q < TQ; ++q) {
                 const bf16x8 b = load8_row<VEC>(ST, M, 32 * q + l32, r, m + mr, m_end);
