@@ -64,6 +64,12 @@ qlora_status launch_dequantize(const uint8_t* codes, const uint8_t* q8, const fl
 qlora_status launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* q8, const float* a2,
                              const uint16_t* t, const uint16_t* B, uint16_t* y, int M, int N, int K, int r,
                              hipStream_t s);
+// Decode-size forward (1 <= M <= kGemvMaxM): same result as launch_gemm_fwd.
+constexpr int kGemvMaxM = 16;
+bool gemv_supported(int M, int N, int K, int r);
+qlora_status launch_gemv_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* q8, const float* a2,
+                             const uint16_t* t, const uint16_t* B, uint16_t* y, int M, int N, int K, int r,
+                             hipStream_t s);
 qlora_status launch_gemm_bwd_dx(const uint16_t* dy, const uint8_t* codes, const uint8_t* q8, const float* a2,
                                 const uint16_t* u, const uint16_t* A, uint16_t* dx, int M, int N, int K, int r,
                                 hipStream_t s);

@@ -593,6 +593,7 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
 qlora_status launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* q8, const float* a2,
                              const uint16_t* t, const uint16_t* B, uint16_t* y, int M, int N, int K, int r,
                              hipStream_t s) {
+    if (gemv_supported(M, N, K, r)) return launch_gemv_fwd(x, codes, q8, a2, t, B, y, M, N, K, r, s);
     const int tm = (M + kTM - 1) / kTM, tn = (N + kTN - 1) / kTN;
     // x is 16-byte aligned (checked by the caller) and K % 64 == 0, so every
     // 16-byte chunk of a row is aligned; a 256-row panel must fit a 32-bit offset

@@ -1,0 +1,69 @@
+"""Parity of the decode-size forward (M <= 16 rows of x) with the fp64 oracle.
+
+qlora_fused_gemm_fwd and qlora_linear_fwd take a separate GEMV kernel for
+M <= 16; these shapes walk its structure: rows past N in the last
+workgroup, K whose block count is not a multiple of the 4 waves, rows with
+fewer blocks than waves, several x staging phases (M * K * 2 above 64 KB),
+several code chunks per wave (odd and even counts), and every scale-FMA
+variant (M = 1, 2, >= 3).  Bar: normwise relative error of y <= 5e-3.
+"""
+import numpy as np
+import pytest
+
+from oracle import bf16, lora, nf4
+from bit_nf4_quantized_15_amd import workloads
+
+from gpu_util import dev_bf16, host_f64, say
+
+pytestmark = pytest.mark.gpu
+TOL = 5e-3
+
+
+@pytest.fixture(scope="module")
+def q():
+    from bit_nf4_quantized_15_amd import qlora
+    return qlora
+
+
+@pytest.mark.parametrize("M,N,K,r", [
+    (1, 512, 11008, 16),    # 172 blocks per row: 3 chunks per wave (odd)
+    (1, 300, 64 * 129, 8),  # 129 blocks: 33 per wave for one wave, 32 for the rest
+    (2, 4096, 4096, 64),    # q_proj shape, M = 2 variant
+    (3, 17, 64, 1),         # one block per row: three waves idle; r = 1
+    (5, 33, 4160, 128),     # 65 blocks; r = 128; rows past N
+    (16, 100, 11008, 8),    # six x phases, the last one short
+    (16, 16, 28672, 16),    # fourteen x phases
+    (16, 4096, 4096, 16),   # two x phases at the decode shape
+])
+def test_gemv_forward(q, M, N, K, r):
+    import torch
+    seed = 7 * M + N + 3 * K + r
+    W = workloads.custom(seed, (N, K), 0.02)
+    x = workloads.custom(seed + 1, (M, K), 1.0)
+    A = workloads.custom(seed + 2, (K, r), float(1 / np.sqrt(r)))
+    B = workloads.custom(seed + 3, (r, N), 0.01)
+    alpha = 2.0 * r
+    say(f"[gemv] M={M} N={N} K={K} r={r}")
+    w = q.quantize(dev_bf16(W))
+    y, t = q.linear_fwd(w, dev_bf16(x), dev_bf16(A), dev_bf16(B), alpha)
+    torch.cuda.synchronize()
+    p, q8, a2 = nf4.quantize(W)
+    Wh = bf16.to_f64(nf4.dequantize(p, q8, a2, N, K))
+    y_ref, t_ref = lora.linear_fwd(bf16.to_f64(x), Wh, bf16.to_f64(A), bf16.to_f64(B), alpha, r)
+    ey, et = lora.rel_err(host_f64(y), y_ref), lora.rel_err(host_f64(t), t_ref)
+    say(f"    rel err y {ey:.3e}  t {et:.3e}")
+    assert ey <= TOL and et <= TOL
+
+
+def test_gemv_fused_entry_matches_linear(q):
+    """qlora_fused_gemm_fwd(x, t, B) == qlora_linear_fwd's y for the same t (one kernel, same bits)."""
+    import torch
+    M, N, K, r = 4, 1000, 2048, 32
+    W = workloads.custom(91, (N, K), 0.02)
+    x, A, B = (dev_bf16(workloads.custom(92 + i, s, v)) for i, (s, v) in
+               enumerate((((M, K), 1.0), ((K, r), 0.2), ((r, N), 0.01))))
+    w = q.quantize(dev_bf16(W))
+    y1, t = q.linear_fwd(w, x, A, B, 64.0)
+    y2 = q.fused_gemm_fwd(w, x, t, B)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
