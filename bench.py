@@ -18,7 +18,11 @@ oracle timed on a bounded sample.
 
 usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
        python bench.py --mode pmc     (a few untimed steps + a calibration copy, for rocprofv3 --pmc)
+       python bench.py --pmc-summary FETCH_CSV WRITE_CSV
+                                      (HBM bytes per launch of the forward GEMM from the two
+                                       counter runs, scaled by the calibration copy)
 """
+import hashlib
 import argparse
 import json
 import os
@@ -40,7 +44,83 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="skip decode / quantize / dense context lines")
     p.add_argument("--mode", choices=["bench", "pmc"], default="bench")
+    p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     return p.parse_args()
+
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+FWD_KERNEL = "nf4_gemm_fwd_kernel"
+GEMM_SRC = os.path.join(HERE, "bit_nf4_quantized_15_amd", "csrc", "gemm.hip")
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "nf4_gemm_fwd_kernel__7B_block_7_layers_M4096_r64__hbm_traffic.txt")
+CALIB_BYTES = 512 << 20
+
+
+def gemm_source_sha():
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def fwd_algorithmic_bytes(layers, M, r):
+    """Per-launch HBM bytes the forward GEMM must move, averaged over the layer shapes:
+    x, codes, q8, a2, t, B in and y out."""
+    tot = 0
+    for _, N, K in layers:
+        tot += 2 * M * K + N * K // 2 + N * K // 64 + 4 * (-(-N * K // 16384)) + 2 * M * r + 2 * r * N + 2 * M * N
+    return tot / len(layers)
+
+
+def measured_traffic():
+    """HBM bytes per forward-GEMM launch from the committed counter runs, or None when
+    they are missing or were taken on a different version of the kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(": ", 1) for line in f.read().splitlines() if ": " in line and not line.startswith("#"))
+        if kv.get("source_sha256", "").strip() != gemm_source_sha():
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def pmc_summary(fetch_csv, write_csv):
+    """Per-launch FETCH_SIZE / WRITE_SIZE of the forward GEMM, each scaled by the factor
+    that makes the same counter read the calibration copy's known bytes."""
+    import csv
+    import collections
+
+    def per_kernel(path, counter):
+        vals = collections.defaultdict(dict)
+        for row in csv.DictReader(open(path)):
+            if row["Counter_Name"] == counter:
+                vals[row["Dispatch_Id"]][row["Kernel_Name"]] = vals[row["Dispatch_Id"]].get(row["Kernel_Name"], 0.0) + \
+                    float(row["Counter_Value"])
+        fwd = [v for d in vals.values() for k, v in d.items() if FWD_KERNEL in k]
+        cal = [v for d in vals.values() for k, v in d.items() if "elementwise" in k]
+        if not fwd or not cal:
+            raise SystemExit(f"{path}: no {FWD_KERNEL} or calibration dispatch for {counter}")
+        return sum(fwd) / len(fwd), len(fwd), max(cal)
+
+    f_kib, n_f, f_cal = per_kernel(fetch_csv, "FETCH_SIZE")
+    w_kib, n_w, w_cal = per_kernel(write_csv, "WRITE_SIZE")
+    f_scale, w_scale = CALIB_BYTES / (f_cal * 1024), CALIB_BYTES / (w_cal * 1024)
+    fetch_b, write_b = f_kib * 1024 * f_scale, w_kib * 1024 * w_scale
+    from bit_nf4_quantized_15_amd import workloads
+    cfg = workloads.CONFIGS[4]
+    algo = fwd_algorithmic_bytes(cfg["layers"], cfg["M"], cfg["r"])
+    print(f"source_sha256: {gemm_source_sha()}")
+    print(f"fwd_dispatches: {n_f} (FETCH run), {n_w} (WRITE run)")
+    print(f"fetch_kib_per_launch_raw: {f_kib:.1f}")
+    print(f"write_kib_per_launch_raw: {w_kib:.1f}")
+    print(f"calibration_copy_bytes: {CALIB_BYTES} read + {CALIB_BYTES} written")
+    print(f"calibration_fetch_kib: {f_cal:.1f}")
+    print(f"calibration_write_kib: {w_cal:.1f}")
+    print(f"fetch_scale: {f_scale:.4f}")
+    print(f"write_scale: {w_scale:.4f}")
+    print(f"hbm_fetch_bytes_per_launch: {fetch_b:.0f}")
+    print(f"hbm_write_bytes_per_launch: {write_b:.0f}")
+    print(f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}")
+    print(f"algorithmic_bytes_per_launch: {algo:.0f}")
+    print(f"traffic_over_algorithmic: {(fetch_b + write_b) / algo:.3f}")
 
 
 def layer_flops(M, N, K, r):
@@ -79,6 +159,9 @@ def gemv_bytes(M, N, K, r):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path has no collectives; see the sharding note in DESIGN.md)", file=sys.stderr)
@@ -145,12 +228,11 @@ def main():
     if args.mode == "pmc":
         for _ in range(2):
             step(False)
-        nbytes = 512 << 20
-        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
-        dst.copy_(src)                                 # calibration: reads and writes exactly 512 MiB
+        torch.mul(src, 2.0, out=dst)                   # calibration: reads and writes exactly 512 MiB
         torch.cuda.synchronize()
-        print(json.dumps({"mode": "pmc", "calibration_copy_bytes": nbytes}))
+        print(json.dumps({"mode": "pmc", "calibration_copy_bytes": CALIB_BYTES}))
         return
 
     for _ in range(args.warmup):
@@ -184,7 +266,9 @@ def main():
                    "blocksize": 64, "double_quant": "8-bit codes, fp32 per 256 blocks"},
         "roofline": {"kernel": "nf4_gemm_fwd_kernel (fused dequant GEMM + LoRA up-projection)", "bound": "mfma",
                      "achieved": round(fwd_tfs, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                     "frac": round(fwd_tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
+                     "frac": round(fwd_tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": measured_traffic(),
+                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "algorithmic_bytes_per_launch": round(fwd_algorithmic_bytes(cfg["layers"], M, r)),
                      "avg_launch_ms": round(fwd_avg_ms, 4),
                      "per_launch_flop": "2*M*K*N + 2*M*r*N over the 7 layer shapes, M=4096, r=64"},
         "breakdown": {"bwd_call_tflops": round(bwd_tfs, 2), "bwd_call_avg_ms": round(bwd_avg_ms, 4),

@@ -127,7 +127,8 @@ __device__ __forceinline__ void store_ftile(uint8_t* lds, const u32x4_t (&r)[8],
 // an instruction writes 16 bytes at the instruction's LDS base + 16 l, so a
 // wave fills 8 consecutive tile rows (1 KB); the swizzle is applied on the
 // global side by choosing which 16-byte chunk each lane fetches.  Offsets past
-// the buffer's byte range read as zero (rows past M).
+// the buffer's byte range read as zero (rows past M): the range check applies
+// to the lane's voffset, so every row offset is kept there.
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 __device__ void raw_buffer_load_lds(i32x4_t rsrc, __attribute__((address_space(3))) uint32_t* lds_ptr, int size,
                                     int voffset, int soffset, int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
@@ -152,7 +153,9 @@ __device__ __forceinline__ void load_tile_direct(i32x4_t rs, uint8_t* tile, uint
     for (int j = 0; j < 8; ++j) {
         auto* dst = reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(
             reinterpret_cast<uintptr_t>(tile + (32 * j + 8 * wave) * 128));
-        raw_buffer_load_lds(rs, dst, 16, (int)voff0, (int)(32 * j * ld * 2 + col0 * 2), 0, 0);
+        // the row offset goes in voffset: the buffer range check covers voffset
+        // (not soffset), so rows past the end of the buffer read as zero
+        raw_buffer_load_lds(rs, dst, 16, (int)(voff0 + (uint32_t)(32 * j * ld * 2)), (int)(col0 * 2), 0, 0);
     }
 }
 
