@@ -8,16 +8,19 @@
 // reduction steps with operands [t | B] resp. [u | A^T]).
 //
 // Both kernels: 256 lanes (4 waves), output tile 256 x 256, reduction step 64
-// (one NF4 block).  The activation tile (256 rows x 64) goes HBM -> registers
-// -> LDS (double buffered, XOR-swizzled); every wave reads all 256 rows of it.
-//  * forward: wave w owns output columns [64w, 64w+64).  Each lane loads the
-//    16 bytes of packed codes it needs straight into registers, builds the
-//    block's 16-entry bf16 table and expands its codes with v_perm_b32 into
-//    MFMA B operands: the dequantized weight never touches LDS or HBM.
+// (one NF4 block).  The activation tile (256 rows x 64 of x, resp. of dy) is
+// copied HBM -> LDS with direct buffer loads (16 B per lane, XOR-swizzled on
+// the global side), double buffered.
+//  * forward: wave w owns output columns [64w, 64w+64) over all 256 rows.
+//    Each lane loads the packed codes, 8-bit scale and group scale it needs
+//    two steps ahead, builds the block's 16-entry bf16 table one step ahead,
+//    and expands its codes with v_perm_b32 straight into MFMA B operands: the
+//    dequantized weight never touches LDS or HBM.
 //  * backward: the reduction runs over n, across rows of the stored codes, so
 //    the weight tile is dequantized cooperatively (lane = one row x one block)
-//    and scattered transposed into a second LDS tile that the MFMA reads like
-//    the activation tile.
+//    into LDS in its natural [n][k] layout and read transposed by the MFMA
+//    operand loads (ds_read_b64_tr_b16); waves form a 2 x 2 grid of 128 x 128
+//    sub-tiles, and the dequantization VALU work is interleaved with the MFMAs.
 // Accumulation is fp32; outputs are rounded to bf16 (nearest even).
 #include "common.h"
 #include "dequant_tile.h"

@@ -24,9 +24,9 @@
 //  * a block's two MFMAs start from zero and a_hat multiplies that fp32
 //    partial sum into the running total:
 //      y = sum_b a_hat_b * sum_{k in b} bf16(c_q) x_k.
-//    Relative to RNE_bf16(a_hat c_q) (the dequantized weight), the weight
-//    used differs by at most 2^-9 relative: both are within half a bf16 ulp
-//    of a_hat c_q;
+//    The weight used, a_hat bf16(c_q), and the dequantized weight
+//    RNE_bf16(a_hat c_q) are each within half a bf16 ulp (at most 2^-8
+//    relative) of a_hat c_q, so they differ by at most 2^-7 relative;
 //  * x is staged in LDS per phase, t and the 16 columns of B once; the LoRA
 //    term t B runs on the same MFMA accumulators (r <= 128 as up to four
 //    32-wide k chunks, one per wave), and the 4 waves' partial sums are added
