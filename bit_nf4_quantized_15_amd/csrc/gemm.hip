@@ -164,6 +164,16 @@ __device__ __forceinline__ void load_tile_direct(i32x4_t rs, uint8_t* tile, uint
 
 __device__ __forceinline__ void wait_direct_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// In the backward's main loop a step issues the next tile's direct loads and
+// then, pinned after them by a scheduling barrier, exactly N ordinary loads of
+// codes and scales for two steps ahead.  Loads complete in order, so at most N loads
+// in flight means the tile has landed while those N stay outstanding.
+constexpr int kAllButVmem = 0x078F;  // sched_barrier mask: every class but VMEM may cross
+template <int N>
+__device__ __forceinline__ void wait_direct_loads_behind() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 __device__ __forceinline__ void store_tile(uint8_t* lds, const u32x4_t (&r)[8], int tid) {
     const int lr = tid >> 3, lc = tid & 7;
 #pragma unroll
@@ -347,6 +357,8 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
         for (int u = 0; u < 2; ++u) T[u] = Tn[u];
         cur = nxt;
         nxt = nn;
+        // the codes of step ks + 2 (issued mid-step, mostly L2 hits) are waited
+        // for here as well; measured faster than leaving them in flight
         wait_direct_loads();
         __syncthreads();
     }
@@ -424,6 +436,7 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
         u32x4_t c0, c1;
         uint32_t q;
         float g;
+        bool ok;  // false past row N or column K: the block's weights are zero
     };
     // rows past N / blocks past K read a valid block and get scale code 0,
     // i.e. all-zero weights (branch-free, so the loop stays one basic block)
@@ -435,13 +448,19 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
         S.c0 = *reinterpret_cast<const u32x4_t*>(p);
         S.c1 = *reinterpret_cast<const u32x4_t*>(p + 16);
         const int64_t blk = (int64_t)nc * KB + dkc / kTK;
-        uint32_t q = q8[blk];
-        asm volatile("" : "+v"(q));   // unconditional load, then select (no branch)
-        S.q = (n < N && dk_ok) ? q : 0u;
+        S.q = q8[blk];
+        S.ok = n < N && dk_ok;
         S.g = a2[blk >> 8];
     };
+    // scale of a loaded step; the load above stays unconditional because the
+    // validity select happens here, where the value is needed anyway
+    auto ahat_of = [&](const Step& S) {
+        uint32_t q = S.q;
+        asm volatile("" : "+v"(q));
+        return scale_step(S.g) * (float)(S.ok ? q : 0u);
+    };
     auto expand = [&](const Step& S, u32x4_t (&out)[8]) {
-        const Nf4Tab T = make_tab(scale_step(S.g) * (float)S.q);
+        const Nf4Tab T = make_tab(ahat_of(S));
 #pragma unroll
         for (int d = 0; d < 8; ++d) out[d] = deq8(T, d < 4 ? S.c0[d] : S.c1[d - 4]);
     };
@@ -527,10 +546,11 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
         bf16x8 a[2][4], b[2][4];
         read_ops(A, Bt, 0, a[0], b[0]);
         load_dy(An, min(ns + 1, NS - 1));
+        __builtin_amdgcn_sched_barrier(kAllButVmem);  // keep the loads in this order
         Step nn;
-        load_step(min(ns + 2, NS - 1), nn);
+        load_step(min(ns + 2, NS - 1), nn);  // 4 loads: codes (2), q8, a2
         u32x4_t w[8];
-        const Nf4Tab T = make_tab(scale_step(nxt.g) * (float)nxt.q);
+        const Nf4Tab T = make_tab(ahat_of(nxt));
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int p = c & 1;
@@ -550,7 +570,7 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
         store_w(Bn, w);
         cur = nxt;
         nxt = nn;
-        wait_direct_loads();
+        if (DYVEC) wait_direct_loads_behind<4>();
         __syncthreads();
     }
 
