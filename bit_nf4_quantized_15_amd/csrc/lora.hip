@@ -52,65 +52,85 @@ __global__ void transpose_kernel(const uint16_t* __restrict__ A, uint16_t* __res
 }
 
 // part[split, m, j] = sum over c in the split's range of X[m, c] * Yt[j, c]
-// Workgroup = 4 waves = 4 tiles of 32 rows of M; TQ 32-wide tiles of j.  The
-// reduction runs in steps of 64: lane half h takes c + 32h .. c + 32h + 31 of
-// its X row as four 16-byte loads (the two halves of an MFMA's k slots may
-// map to any reduction indices, as long as both operands agree).  The Yt
-// chunk of a step (32*TQ rows x 64) is shared by the 4 waves, so it is staged
-// once per workgroup in LDS (double buffered); X is prefetched one step ahead.
+// Workgroup = 4 waves = 4 tiles of 32 rows of M; TQ 32-wide tiles of j; a
+// split covers `chunk` (a multiple of 64, at most kNtMaxChunk) columns of C.
+// The split's Yt slice (32*TQ rows x chunk) is staged in LDS once, with rows
+// padded so that 16 consecutive rows start 4 banks apart; after that single
+// barrier every wave streams its X rows through a 4-stage register ring (16
+// loads of 16 B per lane in flight) with no further synchronisation.  Lane
+// half h takes columns c + 32h .. c + 32h + 31 of each 64-column step (the two
+// halves of an MFMA's k slots may map to any reduction indices, as long as
+// both operands agree).
+constexpr int kNtMaxChunk = 512;  // columns of C per split (64 chunks of 8 per Yt row)
+constexpr int kNtRing = 4;
+
 template <int TQ, bool VEC>
 __global__ __launch_bounds__(256) void nt_partial_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Yt,
                                                          float* __restrict__ part, int M, int C, int r, int chunk) {
     constexpr int kRows = 32 * TQ;                     // staged Yt rows
-    constexpr int kLd = 64 + 8;                        // padded row (bf16), 144 B
-    __shared__ __attribute__((aligned(16))) uint16_t ys[2][kRows * kLd];
+    constexpr int kLd = kNtMaxChunk + 8;               // padded row (bf16)
+    __shared__ __attribute__((aligned(16))) uint16_t ys[kRows * kLd];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
     const int m0 = blockIdx.x * 128 + wave * 32;
     const int split = blockIdx.y;
     const int c_begin = split * chunk;
     const int c_end = min(C, c_begin + chunk);
+    const int steps = (c_end - c_begin + 63) >> 6;
+
+    // X ring first (the long-latency HBM stream), then the Yt slice (L2)
+    bf16x8 xa[kNtRing][4];
+    auto load_x = [&](int st, bf16x8 (&dst)[4]) {
+        const int c = c_begin + 64 * st;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = load8_row<VEC>(X, C, m0 + l32, M, c + 32 * h + 8 * i, c_end);
+    };
+#pragma unroll
+    for (int st = 0; st < kNtRing; ++st)
+        if (st < steps) load_x(st, xa[st]);
+    // Yt slice: kRows x 64 chunks of 16 B; thread tid takes chunks tid + 256 e,
+    // in batches of 16 whose loads are all issued before their stores
+    constexpr int kPer = kRows * (kNtMaxChunk / 8) / 256;
+    constexpr int kBatch = kPer < 16 ? kPer : 16;
+#pragma unroll
+    for (int e0 = 0; e0 < kPer; e0 += kBatch) {
+        bf16x8 yv[kBatch];
+#pragma unroll
+        for (int e = 0; e < kBatch; ++e) {
+            const int idx = tid + 256 * (e0 + e), row = idx >> 6, ch = idx & 63;
+            if (8 * ch < 64 * steps) yv[e] = load8_row<VEC>(Yt, C, row, r, c_begin + 8 * ch, c_end);
+        }
+#pragma unroll
+        for (int e = 0; e < kBatch; ++e) {
+            const int idx = tid + 256 * (e0 + e), row = idx >> 6, ch = idx & 63;
+            if (8 * ch < 64 * steps) *reinterpret_cast<bf16x8*>(&ys[row * kLd + 8 * ch]) = yv[e];
+        }
+    }
+    __syncthreads();
+
     f32x16_t acc[TQ];
 #pragma unroll
     for (int q = 0; q < TQ; ++q)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[q][v] = 0.0f;
-    bf16x8 xa[4];
-    auto load_x = [&](int c) {
+    for (int s0 = 0; s0 < steps; s0 += kNtRing) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xa[i] = load8_row<VEC>(X, C, m0 + l32, M, c + 32 * h + 8 * i, c_end);
-    };
-    // Yt staging: kRows x 8 chunks of 16 B over 256 lanes
-    auto stage_y = [&](int c, int buf) {
+        for (int u = 0; u < kNtRing; ++u) {
+            const int st = s0 + u;
+            if (st < steps) {
+                bf16x8 ca[4];
 #pragma unroll
-        for (int e = tid; e < kRows * 8; e += 256) {
-            const int row = e >> 3, ch = e & 7;
-            *reinterpret_cast<bf16x8*>(&ys[buf][row * kLd + 8 * ch]) = load8_row<VEC>(Yt, C, row, r, c + 8 * ch, c_end);
-        }
-    };
-    if (c_begin < c_end) {
-        load_x(c_begin);
-        stage_y(c_begin, 0);
-    }
-    __syncthreads();
-    int buf = 0;
-    for (int c = c_begin; c < c_end; c += 64) {
-        bf16x8 ca[4];
+                for (int i = 0; i < 4; ++i) ca[i] = xa[u][i];
+                if (st + kNtRing < steps) load_x(st + kNtRing, xa[u]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ca[i] = xa[i];
-        const bool more = c + 64 < c_end;
-        if (more) {
-            load_x(c + 64);
-            stage_y(c + 64, buf ^ 1);
-        }
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int q = 0; q < TQ; ++q) {
-                const bf16x8 yb = *reinterpret_cast<const bf16x8*>(&ys[buf][(32 * q + l32) * kLd + 32 * h + 8 * i]);
-                acc[q] = mfma32(ca[i], yb, acc[q]);
+                    for (int q = 0; q < TQ; ++q) {
+                        const bf16x8 yb =
+                            *reinterpret_cast<const bf16x8*>(&ys[(32 * q + l32) * kLd + 64 * st + 32 * h + 8 * i]);
+                        acc[q] = mfma32(ca[i], yb, acc[q]);
+                    }
             }
-        __syncthreads();
-        buf ^= 1;
+        }
     }
     float* out = part + (int64_t)split * M * r;
 #pragma unroll
