@@ -47,7 +47,7 @@ struct BwdWs {
 inline BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int r) {
     BwdWs w{};
     const SplitPlan su = plan_nt(M, N), st = plan_nt(M, K);
-    const SplitPlan sa = plan_tn(M, K), sb = plan_tn(M, N);
+    const SplitPlan sa = plan_tn(M, K, r), sb = plan_tn(M, N, r);
     const size_t mr2 = align256((size_t)M * r * 2);
     w.u = 0;
     w.ut = w.u + mr2;

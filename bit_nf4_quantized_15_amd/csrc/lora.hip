@@ -163,71 +163,105 @@ __global__ void finalize_bf16_kernel(const float* __restrict__ part, int splits,
 
 // part[split, d, j] = sum over m in the split's range of X[m, d] * S[m, j],
 // with S given transposed (ST [r, M]).  Workgroup = 4 waves over 128 columns
-// d of X (32 each); the [64 m x 128 d] tile of X is staged in LDS (double
-// buffered, next tile prefetched into registers) and read back down its
-// columns for the MFMA A operand (8 consecutive m per lane); the B operand is
-// 8 consecutive m of a row of ST (one 16-byte load).
+// d of X (32 each); a split covers `chunk` (a multiple of 64, at most
+// tn_max_chunk(r)) rows m.  The split's ST slice (32*TQ rows x chunk) is staged in
+// LDS once, padded so that 16 consecutive rows start 4 banks apart; it is the
+// MFMA B operand (8 consecutive m of one row j).  The X rows stream through a
+// 4-stage register ring into a double-buffered [64 m x 128 d] LDS tile, read
+// back down its columns for the A operand (8 consecutive m per lane).
 constexpr int kTnRows = 64, kTnCols = 128, kTnLd = kTnCols + 32;  // 320-byte rows: conflict-free transposed reads
+constexpr int kTnRing = 4;
 
 template <int TQ, bool VEC>
 __global__ __launch_bounds__(256) void tn_partial_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ ST,
                                                          float* __restrict__ part, int M, int D, int r, int chunk) {
+    constexpr int kTnMaxChunk = TQ <= 3 ? 512 : 256;  // = tn_max_chunk(r) for r in (32 (TQ-1), 32 TQ]
+    constexpr int kSLd = kTnMaxChunk + 8;
     __shared__ __attribute__((aligned(16))) uint16_t tile[2][kTnRows * kTnLd];
+    __shared__ __attribute__((aligned(16))) uint16_t ss[32 * TQ * kSLd];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
     const int d0 = blockIdx.x * kTnCols;
     const int split = blockIdx.y;
     const int m_begin = split * chunk;
     const int m_end = min(M, m_begin + chunk);
-    // loader: row tid/4 of the tile, columns 32*(tid%4) .. +31
+    const int steps = (m_end - m_begin + kTnRows - 1) / kTnRows;
+    // loader: row tid/4 of a 64-row step, columns 32*(tid%4) .. +31
     const int lr = tid >> 2, lc = (tid & 3) * 32;
+    bf16x8 xr[kTnRing][4];
+    auto load_x = [&](int st, bf16x8 (&dst)[4]) {
+        const int m = m_begin + kTnRows * st;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = load8_row<VEC>(X, D, m + lr, m_end, d0 + lc + 8 * i, D);
+    };
+    auto store_x = [&](const bf16x8 (&src)[4], int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<bf16x8*>(&tile[buf][lr * kTnLd + lc + 8 * i]) = src[i];
+    };
+#pragma unroll
+    for (int st = 0; st < kTnRing; ++st)
+        if (st < steps) load_x(st, xr[st]);
+    // ST slice: 32*TQ rows x 64 chunks of 16 B, loads of a batch before its stores
+    {
+        constexpr int kPer = 32 * TQ * (kTnMaxChunk / 8) / 256;
+        constexpr int kBatch = kPer < 16 ? kPer : 16;
+#pragma unroll
+        for (int e0 = 0; e0 < kPer; e0 += kBatch) {
+            bf16x8 sv[kBatch];
+#pragma unroll
+            for (int e = 0; e < kBatch; ++e) {
+                const int idx = tid + 256 * (e0 + e), row = idx / (kTnMaxChunk / 8), ch = idx % (kTnMaxChunk / 8);
+                if (8 * ch < kTnRows * steps) sv[e] = load8_row<VEC>(ST, M, row, r, m_begin + 8 * ch, m_end);
+            }
+#pragma unroll
+            for (int e = 0; e < kBatch; ++e) {
+                const int idx = tid + 256 * (e0 + e), row = idx / (kTnMaxChunk / 8), ch = idx % (kTnMaxChunk / 8);
+                if (8 * ch < kTnRows * steps) *reinterpret_cast<bf16x8*>(&ss[row * kSLd + 8 * ch]) = sv[e];
+            }
+        }
+    }
+    if (steps > 0) store_x(xr[0], 0);
+    __syncthreads();
+
     f32x16_t acc[TQ];
 #pragma unroll
     for (int q = 0; q < TQ; ++q)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[q][v] = 0.0f;
-    bf16x8 xr[4];
-    auto load_x = [&](int m) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xr[i] = load8_row<VEC>(X, D, m + lr, m_end, d0 + lc + 8 * i, D);
-    };
-    auto store_x = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<bf16x8*>(&tile[buf][lr * kTnLd + lc + 8 * i]) = xr[i];
-    };
-    if (m_begin < m_end) {
-        load_x(m_begin);
-        store_x(0);
-    }
-    __syncthreads();
     // A operand = X^T: 8 consecutive m of column d = 32*wave + l32, read with two
     // ds_read_b64_tr_b16 (16-lane group lane j gets element j of the 4-element
     // row pieces addressed by lanes j%4 + 4e -> rows R + e, columns C0 + 4*(j%4))
     const int tj = l32 & 15, tg = l32 >> 4;
     const int trow = tj >> 2, tcol = 32 * wave + 16 * tg + 4 * (tj & 3);
-    int buf = 0;
-    for (int m = m_begin; m < m_end; m += kTnRows) {
-        const bool more = m + kTnRows < m_end;
-        if (more) load_x(m + kTnRows);
+    for (int s0 = 0; s0 < steps; s0 += kTnRing) {
 #pragma unroll
-        for (int mc = 0; mc < kTnRows / 16; ++mc) {
-            const int mr = mc * 16 + 8 * h;   // tile row of this lane's first k slot
-            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                reinterpret_cast<__attribute__((address_space(3))) s16x4_t*>(
-                    reinterpret_cast<uintptr_t>(&tile[buf][(mr + trow) * kTnLd + tcol])));
-            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                reinterpret_cast<__attribute__((address_space(3))) s16x4_t*>(
-                    reinterpret_cast<uintptr_t>(&tile[buf][(mr + 4 + trow) * kTnLd + tcol])));
-            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        for (int u = 0; u < kTnRing; ++u) {
+            const int st = s0 + u;
+            if (st < steps) {
+                const int buf = st & 1;
+                // next step's rows into the other buffer (read two steps ago), and
+                // this ring slot's next load (its data went to LDS a step ago)
+                if (st + 1 < steps) store_x(xr[(u + 1) % kTnRing], buf ^ 1);
+                if (st + kTnRing < steps) load_x(st + kTnRing, xr[u]);
 #pragma unroll
-            for (int q = 0; q < TQ; ++q) {
-                const bf16x8 b = load8_row<VEC>(ST, M, 32 * q + l32, r, m + mr, m_end);
-                acc[q] = mfma32(a, b, acc[q]);
+                for (int mc = 0; mc < kTnRows / 16; ++mc) {
+                    const int mr = mc * 16 + 8 * h;   // tile row of this lane's first k slot
+                    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        reinterpret_cast<__attribute__((address_space(3))) s16x4_t*>(
+                            reinterpret_cast<uintptr_t>(&tile[buf][(mr + trow) * kTnLd + tcol])));
+                    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        reinterpret_cast<__attribute__((address_space(3))) s16x4_t*>(
+                            reinterpret_cast<uintptr_t>(&tile[buf][(mr + 4 + trow) * kTnLd + tcol])));
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                    for (int q = 0; q < TQ; ++q) {
+                        const bf16x8 b = *reinterpret_cast<const bf16x8*>(
+                            &ss[(32 * q + l32) * kSLd + kTnRows * st + mr]);
+                        acc[q] = mfma32(a, b, acc[q]);
+                    }
+                }
+                __syncthreads();
             }
         }
-        if (more) store_x(buf ^ 1);
-        __syncthreads();
-        buf ^= 1;
     }
     float* out = part + (int64_t)split * D * r;
 #pragma unroll
@@ -293,7 +327,7 @@ qlora_status launch_nt(const uint16_t* X, const uint16_t* Yt, float* part, uint1
 
 qlora_status launch_tn(const uint16_t* X, const uint16_t* ST, float* part, float* out, int M, int D, int r,
                        int64_t ld_d, int64_t ld_j, hipStream_t s) {
-    const SplitPlan sp = plan_tn(M, D);
+    const SplitPlan sp = plan_tn(M, D, r);
     const dim3 grid((unsigned)((D + kTnCols - 1) / kTnCols), (unsigned)sp.splits);
     const bool vec = (D % 8 == 0) && (M % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15u) == 0) &&
                      ((reinterpret_cast<uintptr_t>(ST) & 15u) == 0);
