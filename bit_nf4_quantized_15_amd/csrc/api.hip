@@ -28,21 +28,20 @@ inline bool bad_dims(int64_t M, int64_t N, int64_t K, int r) {
 
 // Workspace carve-up.  Every piece starts on a 256-byte boundary.
 struct FwdWs {
-    size_t at, part, tbuf, total;
+    size_t part, tbuf, total;  // partial sums of t; t when the caller keeps none
 };
 inline FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int r) {
     (void)N;
     FwdWs w{};
     const SplitPlan sp = plan_nt(M, K);
-    w.at = 0;
-    w.part = w.at + align256((size_t)r * K * 2);
+    w.part = 0;
     w.tbuf = w.part + align256((size_t)sp.splits * M * r * 4);
     w.total = w.tbuf + align256((size_t)M * r * 2);
     return w;
 }
 
 struct BwdWs {
-    size_t u, ut, part, at, tbuf, tt, pa, pb, total;
+    size_t u, part, tbuf, pa, pb, total;  // u; partials of u (and of t); t; partials of dA, dB
 };
 inline BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int r) {
     BwdWs w{};
@@ -50,12 +49,9 @@ inline BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int r) {
     const SplitPlan sa = plan_tn(M, K, r), sb = plan_tn(M, N, r);
     const size_t mr2 = align256((size_t)M * r * 2);
     w.u = 0;
-    w.ut = w.u + mr2;
-    w.part = w.ut + mr2;
-    w.at = w.part + align256((size_t)std::max(su.splits, st.splits) * M * r * 4);
-    w.tbuf = w.at + align256((size_t)r * K * 2);
-    w.tt = w.tbuf + mr2;
-    w.pa = w.tt + mr2;
+    w.part = w.u + mr2;
+    w.tbuf = w.part + align256((size_t)std::max(su.splits, st.splits) * M * r * 4);
+    w.pa = w.tbuf + mr2;
     w.pb = w.pa + align256((size_t)sa.splits * K * r * 4);
     w.total = w.pb + align256((size_t)sb.splits * r * N * 4);
     return w;
@@ -121,7 +117,7 @@ size_t qlora_bwd_workspace(int64_t M, int64_t N, int64_t K, int r) {
 size_t qlora_lora_down_workspace(int64_t M, int64_t K, int r) {
     if (bad_dims(M, 1, K, r) || M == 0 || K % kBlock) return 0;
     const SplitPlan sp = plan_nt(M, K);
-    return align256((size_t)r * K * 2) + align256((size_t)sp.splits * M * r * 4);
+    return align256((size_t)sp.splits * M * r * 4);
 }
 
 qlora_status qlora_lora_down(const uint16_t* x, int64_t M, int64_t K, const uint16_t* A, int r, float alpha,
@@ -135,11 +131,8 @@ qlora_status qlora_lora_down(const uint16_t* x, int64_t M, int64_t K, const uint
     if (!ws || ws_bytes < need) return QLORA_ERR_WORKSPACE;
     if (!aligned16(ws)) return QLORA_ERR_MISALIGNED;
     hipStream_t s = (hipStream_t)stream;
-    uint16_t* At = reinterpret_cast<uint16_t*>(ws);
-    float* part = reinterpret_cast<float*>(at(ws, align256((size_t)r * K * 2)));
-    qlora_status st = launch_transpose(A, At, (int)K, r, s);
-    if (st != QLORA_OK) return st;
-    return launch_nt(x, At, part, t_out, nullptr, alpha / (float)r, (int)M, (int)K, r, s);
+    float* part = reinterpret_cast<float*>(ws);
+    return launch_nt(x, A, true, part, t_out, alpha / (float)r, (int)M, (int)K, r, s);
 }
 
 qlora_status qlora_fused_gemm_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uint16_t* t,
@@ -170,11 +163,9 @@ qlora_status qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, 
     if (!aligned16(ws)) return QLORA_ERR_MISALIGNED;
     hipStream_t s = (hipStream_t)stream;
     const float scale = alpha / (float)r;
-    uint16_t* At = reinterpret_cast<uint16_t*>(at(ws, L.at));
     float* part = reinterpret_cast<float*>(at(ws, L.part));
     uint16_t* t = t_out ? t_out : reinterpret_cast<uint16_t*>(at(ws, L.tbuf));
-    if ((st = launch_transpose(A, At, (int)K, r, s)) != QLORA_OK) return st;
-    if ((st = launch_nt(x, At, part, t, nullptr, scale, (int)M, (int)K, r, s)) != QLORA_OK) return st;
+    if ((st = launch_nt(x, A, true, part, t, scale, (int)M, (int)K, r, s)) != QLORA_OK) return st;
     return launch_gemm_fwd(x, w->codes, w->q8, w->a2, t, B, y, (int)M, (int)N, (int)K, r, s);
 }
 
@@ -201,28 +192,22 @@ qlora_status qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, int64_t M, 
     if (!aligned16(ws)) return QLORA_ERR_MISALIGNED;
     const float scale = alpha / (float)r;
     uint16_t* u = reinterpret_cast<uint16_t*>(at(ws, L.u));
-    uint16_t* uT = reinterpret_cast<uint16_t*>(at(ws, L.ut));
-    uint16_t* tT = reinterpret_cast<uint16_t*>(at(ws, L.tt));
     float* part = reinterpret_cast<float*>(at(ws, L.part));
-    // u = s dy B^T  (B [r, N] is already the row-major transpose the kernel wants)
-    if ((st = launch_nt(dy, B, part, u, uT, scale, (int)M, (int)N, r, s)) != QLORA_OK) return st;
-    if (!t) {  // recompute t = s x A (and its transpose)
-        uint16_t* At = reinterpret_cast<uint16_t*>(at(ws, L.at));
+    // u = s dy B^T  (B [r, N] is the row-major transpose of B^T)
+    if ((st = launch_nt(dy, B, false, part, u, scale, (int)M, (int)N, r, s)) != QLORA_OK) return st;
+    if (!t) {  // recompute t = s x A
         uint16_t* tb = reinterpret_cast<uint16_t*>(at(ws, L.tbuf));
-        if ((st = launch_transpose(A, At, (int)K, r, s)) != QLORA_OK) return st;
-        if ((st = launch_nt(x, At, part, tb, tT, scale, (int)M, (int)K, r, s)) != QLORA_OK) return st;
+        if ((st = launch_nt(x, A, true, part, tb, scale, (int)M, (int)K, r, s)) != QLORA_OK) return st;
         t = tb;
-    } else if ((st = launch_transpose(t, tT, (int)M, r, s)) != QLORA_OK) {
-        return st;
     }
     if (dx) {
         if ((st = launch_gemm_bwd_dx(dy, w->codes, w->q8, w->a2, u, A, dx, (int)M, (int)N, (int)K, r, s)) != QLORA_OK)
             return st;
     }
     // dA [K, r] = x^T u ; dB [r, N] = t^T dy, stored transposed from the [N, r] reduction
-    if ((st = launch_tn(x, uT, reinterpret_cast<float*>(at(ws, L.pa)), dA, (int)M, (int)K, r, r, 1, s)) != QLORA_OK)
+    if ((st = launch_tn(x, u, reinterpret_cast<float*>(at(ws, L.pa)), dA, (int)M, (int)K, r, r, 1, s)) != QLORA_OK)
         return st;
-    return launch_tn(dy, tT, reinterpret_cast<float*>(at(ws, L.pb)), dB, (int)M, (int)N, r, 1, N, s);
+    return launch_tn(dy, t, reinterpret_cast<float*>(at(ws, L.pb)), dB, (int)M, (int)N, r, 1, N, s);
 }
 
 }  // extern "C"

@@ -73,12 +73,11 @@ qlora_status launch_gemv_fwd(const uint16_t* x, const uint8_t* codes, const uint
 qlora_status launch_gemm_bwd_dx(const uint16_t* dy, const uint8_t* codes, const uint8_t* q8, const float* a2,
                                 const uint16_t* u, const uint16_t* A, uint16_t* dx, int M, int N, int K, int r,
                                 hipStream_t s);
-qlora_status launch_transpose(const uint16_t* A, uint16_t* At, int K, int r, hipStream_t s);
-// out [M, r] (and outT [r, M] when not null) = bf16(scale * X [M, C] Yt [r, C]^T)
-qlora_status launch_nt(const uint16_t* X, const uint16_t* Yt, float* part, uint16_t* out, uint16_t* outT,
-                       float scale, int M, int C, int r, hipStream_t s);
-// out[d * ld_d + j * ld_j] = sum_m X [M, D][m, d] * S[m, j], S given as ST [r, M]
-qlora_status launch_tn(const uint16_t* X, const uint16_t* ST, float* part, float* out, int M, int D, int r,
+// out [M, r] = bf16(scale * X [M, C] Y), Y given as Yt [r, C] or, with y_natural, as [C, r]
+qlora_status launch_nt(const uint16_t* X, const uint16_t* Y, bool y_natural, float* part, uint16_t* out, float scale,
+                       int M, int C, int r, hipStream_t s);
+// out[d * ld_d + j * ld_j] = sum_m X [M, D][m, d] * S [M, r][m, j]
+qlora_status launch_tn(const uint16_t* X, const uint16_t* S, float* part, float* out, int M, int D, int r,
                        int64_t ld_d, int64_t ld_j, hipStream_t s);
 qlora_status launch_fill(float* out, int64_t count, float v, hipStream_t s);
 

@@ -7,6 +7,8 @@
 //   u  = s dy B^T     [M, r]
 //   dA = x^T u        [K, r]
 //   dB = t^T dy       [r, N]
+// The small operands (A, B, t, u) are read in their own layouts: a slice of
+// each is staged in LDS and transposed, where needed, by the LDS reads.
 // All four stream one large operand (x or dy) once and are HBM bound.  The
 // reductions are split over the long dimension for parallelism; partial sums
 // go to a workspace and are added in a fixed order (deterministic results).
@@ -43,41 +45,87 @@ __device__ __forceinline__ bf16x8 load8_row(const uint16_t* __restrict__ src, in
     return __builtin_bit_cast(bf16x8, u32x4_t{w[0], w[1], w[2], w[3]});
 }
 
-// At[j, k] = A[k, j] for A [K, r] (any row-major matrix transpose)
-__global__ void transpose_kernel(const uint16_t* __restrict__ A, uint16_t* __restrict__ At, int K, int r) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (int64_t)K * r) return;
-    const int j = (int)(i / K), k = (int)(i - (int64_t)j * K);
-    At[i] = A[(int64_t)k * r + j];
+// Slices of a small row-major [R, r] operand (A [K, r], t or u [M, r]) live in
+// LDS with rows of 32*TQ + 16 bf16: for every TQ the 16-lane groups of the
+// transposed reads below then touch 16 distinct pairs of banks.
+template <int TQ>
+constexpr int slice_ld() { return 32 * TQ + 16; }
+
+// Rows [row0, row0 + rows_used) of src (row stride r; rows at or past row_end and
+// columns at or past r read as zero) into dst[row * slice_ld + col], all loads of
+// a batch issued before its stores.
+template <int TQ, bool VEC, int MAXROWS>
+__device__ __forceinline__ void stage_slice(uint16_t* __restrict__ dst, const uint16_t* __restrict__ src, int r,
+                                            int row0, int row_end, int rows_used, int tid) {
+    constexpr int kCh = 4 * TQ;  // 16-byte chunks per slice row
+    constexpr int kLd = slice_ld<TQ>();
+    constexpr int kPer = MAXROWS * kCh / 256;
+    constexpr int kBatch = kPer < 16 ? kPer : 16;
+#pragma unroll
+    for (int e0 = 0; e0 < kPer; e0 += kBatch) {
+        bf16x8 v[kBatch];
+#pragma unroll
+        for (int e = 0; e < kBatch; ++e) {
+            const int idx = tid + 256 * (e0 + e), row = idx / kCh, ch = idx % kCh;
+            if (row < rows_used) v[e] = load8_row<VEC>(src, r, row0 + row, row_end, 8 * ch, r);
+        }
+#pragma unroll
+        for (int e = 0; e < kBatch; ++e) {
+            const int idx = tid + 256 * (e0 + e), row = idx / kCh, ch = idx % kCh;
+            if (row < rows_used) *reinterpret_cast<bf16x8*>(dst + row * kLd + 8 * ch) = v[e];
+        }
+    }
 }
 
-// part[split, m, j] = sum over c in the split's range of X[m, c] * Yt[j, c]
+// MFMA operand of 8 consecutive slice rows row .. row+7 of column col16 + l32 % 16
+// (col16 = the 16-column group of this half-wave), from two ds_read_b64_tr_b16:
+// lane j of a 16-lane group receives element j of the 4-element row pieces
+// addressed by lanes j%4 + 4e, which point at rows row + e, columns col16 + 4*(j%4).
+__device__ __forceinline__ bf16x8 slice_col8(const uint16_t* __restrict__ slice, int ld, int row, int col16,
+                                             int tj) {
+    const uint16_t* p = slice + (row + (tj >> 2)) * ld + col16 + 4 * (tj & 3);
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<__attribute__((address_space(3))) s16x4_t*>(reinterpret_cast<uintptr_t>(p)));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<__attribute__((address_space(3))) s16x4_t*>(reinterpret_cast<uintptr_t>(p + 4 * ld)));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// part[split, m, j] = sum over c in the split's range of X[m, c] * Y[c, j]
+// Y comes either as its rows' transpose Yt [r, C] (YNAT false: u = dy B^T with
+// B [r, N]) or in its natural layout [C, r] (YNAT true: t = x A with A [K, r]).
 // Workgroup = 4 waves = 4 tiles of 32 rows of M; TQ 32-wide tiles of j; a
 // split covers `chunk` (a multiple of 64, at most kNtMaxChunk) columns of C.
-// The split's Yt slice (32*TQ rows x chunk) is staged in LDS once, with rows
-// padded so that 16 consecutive rows start 4 banks apart; after that single
-// barrier every wave streams its X rows through a 4-stage register ring (16
-// loads of 16 B per lane in flight) with no further synchronisation.  Lane
-// half h takes columns c + 32h .. c + 32h + 31 of each 64-column step (the two
-// halves of an MFMA's k slots may map to any reduction indices, as long as
-// both operands agree).
-constexpr int kNtMaxChunk = 512;  // columns of C per split (64 chunks of 8 per Yt row)
+// The split's slice of Y is staged in LDS once (Yt rows padded so that 16
+// consecutive rows start 4 banks apart; natural rows as slice_ld, read with
+// transposed loads); after that single barrier every wave streams its X rows
+// through a 4-stage register ring (16 loads of 16 B per lane in flight) with
+// no further synchronisation.  Lane half h takes columns c + 32h .. c + 32h +
+// 31 of each 64-column step (the two halves of an MFMA's k slots may map to any
+// reduction indices, as long as both operands agree).
+constexpr int kNtMaxChunk = 512;  // columns of C per split
 constexpr int kNtRing = 4;
 
-template <int TQ, bool VEC>
-__global__ __launch_bounds__(256) void nt_partial_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Yt,
+template <int TQ, bool YNAT>
+constexpr int nt_slice_elems() {
+    return YNAT ? kNtMaxChunk * slice_ld<TQ>() : 32 * TQ * (kNtMaxChunk + 8);
+}
+
+template <int TQ, bool VEC, bool YNAT>
+__global__ __launch_bounds__(256) void nt_partial_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Y,
                                                          float* __restrict__ part, int M, int C, int r, int chunk) {
-    constexpr int kRows = 32 * TQ;                     // staged Yt rows
-    constexpr int kLd = kNtMaxChunk + 8;               // padded row (bf16)
-    __shared__ __attribute__((aligned(16))) uint16_t ys[kRows * kLd];
+    constexpr int kLdT = kNtMaxChunk + 8;  // Yt row (bf16)
+    constexpr int kLdN = slice_ld<TQ>();   // natural row (bf16)
+    __shared__ __attribute__((aligned(16))) uint16_t ys[nt_slice_elems<TQ, YNAT>()];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    const int tj = l32 & 15, tg = l32 >> 4;
     const int m0 = blockIdx.x * 128 + wave * 32;
     const int split = blockIdx.y;
     const int c_begin = split * chunk;
     const int c_end = min(C, c_begin + chunk);
     const int steps = (c_end - c_begin + 63) >> 6;
 
-    // X ring first (the long-latency HBM stream), then the Yt slice (L2)
+    // X ring first (the long-latency HBM stream), then the Y slice (L2)
     bf16x8 xa[kNtRing][4];
     auto load_x = [&](int st, bf16x8 (&dst)[4]) {
         const int c = c_begin + 64 * st;
@@ -87,22 +135,25 @@ __global__ __launch_bounds__(256) void nt_partial_kernel(const uint16_t* __restr
 #pragma unroll
     for (int st = 0; st < kNtRing; ++st)
         if (st < steps) load_x(st, xa[st]);
-    // Yt slice: kRows x 64 chunks of 16 B; thread tid takes chunks tid + 256 e,
-    // in batches of 16 whose loads are all issued before their stores
-    constexpr int kPer = kRows * (kNtMaxChunk / 8) / 256;
-    constexpr int kBatch = kPer < 16 ? kPer : 16;
+    if (YNAT) {
+        stage_slice<TQ, VEC, kNtMaxChunk>(ys, Y, r, c_begin, c_end, 64 * steps, tid);
+    } else {
+        // Yt slice: 32*TQ rows x 64 chunks of 16 B
+        constexpr int kPer = 32 * TQ * (kNtMaxChunk / 8) / 256;
+        constexpr int kBatch = kPer < 16 ? kPer : 16;
 #pragma unroll
-    for (int e0 = 0; e0 < kPer; e0 += kBatch) {
-        bf16x8 yv[kBatch];
+        for (int e0 = 0; e0 < kPer; e0 += kBatch) {
+            bf16x8 yv[kBatch];
 #pragma unroll
-        for (int e = 0; e < kBatch; ++e) {
-            const int idx = tid + 256 * (e0 + e), row = idx >> 6, ch = idx & 63;
-            if (8 * ch < 64 * steps) yv[e] = load8_row<VEC>(Yt, C, row, r, c_begin + 8 * ch, c_end);
-        }
+            for (int e = 0; e < kBatch; ++e) {
+                const int idx = tid + 256 * (e0 + e), row = idx >> 6, ch = idx & 63;
+                if (8 * ch < 64 * steps) yv[e] = load8_row<VEC>(Y, C, row, r, c_begin + 8 * ch, c_end);
+            }
 #pragma unroll
-        for (int e = 0; e < kBatch; ++e) {
-            const int idx = tid + 256 * (e0 + e), row = idx >> 6, ch = idx & 63;
-            if (8 * ch < 64 * steps) *reinterpret_cast<bf16x8*>(&ys[row * kLd + 8 * ch]) = yv[e];
+            for (int e = 0; e < kBatch; ++e) {
+                const int idx = tid + 256 * (e0 + e), row = idx >> 6, ch = idx & 63;
+                if (8 * ch < 64 * steps) *reinterpret_cast<bf16x8*>(&ys[row * kLdT + 8 * ch]) = yv[e];
+            }
         }
     }
     __syncthreads();
@@ -125,8 +176,9 @@ __global__ __launch_bounds__(256) void nt_partial_kernel(const uint16_t* __restr
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int q = 0; q < TQ; ++q) {
-                        const bf16x8 yb =
-                            *reinterpret_cast<const bf16x8*>(&ys[(32 * q + l32) * kLd + 64 * st + 32 * h + 8 * i]);
+                        const int c = 64 * st + 32 * h + 8 * i;  // slice column of the lane's k slots
+                        const bf16x8 yb = YNAT ? slice_col8(ys, kLdN, c, 32 * q + 16 * tg, tj)
+                                               : *reinterpret_cast<const bf16x8*>(&ys[(32 * q + l32) * kLdT + c]);
                         acc[q] = mfma32(ca[i], yb, acc[q]);
                     }
             }
@@ -145,41 +197,37 @@ __global__ __launch_bounds__(256) void nt_partial_kernel(const uint16_t* __restr
     }
 }
 
-// out[m, j] = bf16( s * sum_split part[split, m, j] ); optionally also outT[j, m].
+// out[m, j] = bf16( s * sum_split part[split, m, j] )
 __global__ void finalize_bf16_kernel(const float* __restrict__ part, int splits, int M, int r, float s,
-                                     uint16_t* __restrict__ out, uint16_t* __restrict__ outT) {
+                                     uint16_t* __restrict__ out) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t count = (int64_t)M * r;
     if (i >= count) return;
     float acc = 0.0f;
     for (int p = 0; p < splits; ++p) acc += part[(int64_t)p * count + i];
-    const uint16_t v = (uint16_t)(pack_bf16x2(s * acc, 0.0f) & 0xFFFFu);
-    out[i] = v;
-    if (outT) {
-        const int m = (int)(i / r), j = (int)(i - (int64_t)m * r);
-        outT[(int64_t)j * M + m] = v;
-    }
+    out[i] = (uint16_t)(pack_bf16x2(s * acc, 0.0f) & 0xFFFFu);
 }
 
-// part[split, d, j] = sum over m in the split's range of X[m, d] * S[m, j],
-// with S given transposed (ST [r, M]).  Workgroup = 4 waves over 128 columns
-// d of X (32 each); a split covers `chunk` (a multiple of 64, at most
-// tn_max_chunk(r)) rows m.  The split's ST slice (32*TQ rows x chunk) is staged in
-// LDS once, padded so that 16 consecutive rows start 4 banks apart; it is the
-// MFMA B operand (8 consecutive m of one row j).  The X rows stream through a
-// 4-stage register ring into a double-buffered [64 m x 128 d] LDS tile, read
-// back down its columns for the A operand (8 consecutive m per lane).
+// part[split, d, j] = sum over m in the split's range of X[m, d] * S[m, j]
+// (S [M, r] row-major: u or t).  Workgroup = 4 waves over 128 columns d of X
+// (32 each); a split covers `chunk` (a multiple of 64, at most tn_max_chunk(r))
+// rows m.  The split's slice of S is staged in LDS once and read with
+// transposed loads as the MFMA B operand (8 consecutive m of one column j).
+// The X rows stream through a 4-stage register ring into a double-buffered
+// [64 m x 128 d] LDS tile, read back down its columns for the A operand (8
+// consecutive m per lane), also with transposed loads.
 constexpr int kTnRows = 64, kTnCols = 128, kTnLd = kTnCols + 32;  // 320-byte rows: conflict-free transposed reads
 constexpr int kTnRing = 4;
 
 template <int TQ, bool VEC>
-__global__ __launch_bounds__(256) void tn_partial_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ ST,
+__global__ __launch_bounds__(256) void tn_partial_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ S,
                                                          float* __restrict__ part, int M, int D, int r, int chunk) {
     constexpr int kTnMaxChunk = TQ <= 3 ? 512 : 256;  // = tn_max_chunk(r) for r in (32 (TQ-1), 32 TQ]
-    constexpr int kSLd = kTnMaxChunk + 8;
+    constexpr int kSLd = slice_ld<TQ>();
     __shared__ __attribute__((aligned(16))) uint16_t tile[2][kTnRows * kTnLd];
-    __shared__ __attribute__((aligned(16))) uint16_t ss[32 * TQ * kSLd];
+    __shared__ __attribute__((aligned(16))) uint16_t ss[kTnMaxChunk * kSLd];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    const int tj = l32 & 15, tg = l32 >> 4;
     const int d0 = blockIdx.x * kTnCols;
     const int split = blockIdx.y;
     const int m_begin = split * chunk;
@@ -200,25 +248,7 @@ __global__ __launch_bounds__(256) void tn_partial_kernel(const uint16_t* __restr
 #pragma unroll
     for (int st = 0; st < kTnRing; ++st)
         if (st < steps) load_x(st, xr[st]);
-    // ST slice: 32*TQ rows x 64 chunks of 16 B, loads of a batch before its stores
-    {
-        constexpr int kPer = 32 * TQ * (kTnMaxChunk / 8) / 256;
-        constexpr int kBatch = kPer < 16 ? kPer : 16;
-#pragma unroll
-        for (int e0 = 0; e0 < kPer; e0 += kBatch) {
-            bf16x8 sv[kBatch];
-#pragma unroll
-            for (int e = 0; e < kBatch; ++e) {
-                const int idx = tid + 256 * (e0 + e), row = idx / (kTnMaxChunk / 8), ch = idx % (kTnMaxChunk / 8);
-                if (8 * ch < kTnRows * steps) sv[e] = load8_row<VEC>(ST, M, row, r, m_begin + 8 * ch, m_end);
-            }
-#pragma unroll
-            for (int e = 0; e < kBatch; ++e) {
-                const int idx = tid + 256 * (e0 + e), row = idx / (kTnMaxChunk / 8), ch = idx % (kTnMaxChunk / 8);
-                if (8 * ch < kTnRows * steps) *reinterpret_cast<bf16x8*>(&ss[row * kSLd + 8 * ch]) = sv[e];
-            }
-        }
-    }
+    stage_slice<TQ, VEC, kTnMaxChunk>(ss, S, r, m_begin, m_end, kTnRows * steps, tid);
     if (steps > 0) store_x(xr[0], 0);
     __syncthreads();
 
@@ -227,11 +257,7 @@ __global__ __launch_bounds__(256) void tn_partial_kernel(const uint16_t* __restr
     for (int q = 0; q < TQ; ++q)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[q][v] = 0.0f;
-    // A operand = X^T: 8 consecutive m of column d = 32*wave + l32, read with two
-    // ds_read_b64_tr_b16 (16-lane group lane j gets element j of the 4-element
-    // row pieces addressed by lanes j%4 + 4e -> rows R + e, columns C0 + 4*(j%4))
-    const int tj = l32 & 15, tg = l32 >> 4;
-    const int trow = tj >> 2, tcol = 32 * wave + 16 * tg + 4 * (tj & 3);
+    // A operand = X^T: 8 consecutive m of column d = 32*wave + l32 of the tile
     for (int s0 = 0; s0 < steps; s0 += kTnRing) {
 #pragma unroll
         for (int u = 0; u < kTnRing; ++u) {
@@ -245,17 +271,10 @@ __global__ __launch_bounds__(256) void tn_partial_kernel(const uint16_t* __restr
 #pragma unroll
                 for (int mc = 0; mc < kTnRows / 16; ++mc) {
                     const int mr = mc * 16 + 8 * h;   // tile row of this lane's first k slot
-                    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        reinterpret_cast<__attribute__((address_space(3))) s16x4_t*>(
-                            reinterpret_cast<uintptr_t>(&tile[buf][(mr + trow) * kTnLd + tcol])));
-                    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        reinterpret_cast<__attribute__((address_space(3))) s16x4_t*>(
-                            reinterpret_cast<uintptr_t>(&tile[buf][(mr + 4 + trow) * kTnLd + tcol])));
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    const bf16x8 a = slice_col8(tile[buf], kTnLd, mr, 32 * wave + 16 * tg, tj);
 #pragma unroll
                     for (int q = 0; q < TQ; ++q) {
-                        const bf16x8 b = *reinterpret_cast<const bf16x8*>(
-                            &ss[(32 * q + l32) * kSLd + kTnRows * st + mr]);
+                        const bf16x8 b = slice_col8(ss, kSLd, kTnRows * st + mr, 32 * q + 16 * tg, tj);
                         acc[q] = mfma32(a, b, acc[q]);
                     }
                 }
@@ -297,44 +316,42 @@ inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1)
 
 }  // namespace
 
-qlora_status launch_transpose(const uint16_t* A, uint16_t* At, int K, int r, hipStream_t s) {
-    hipLaunchKernelGGL(transpose_kernel, dim3(blocks_for((int64_t)K * r, 256)), dim3(256), 0, s, A, At, K, r);
-    return launch_status();
-}
-
-qlora_status launch_nt(const uint16_t* X, const uint16_t* Yt, float* part, uint16_t* out, uint16_t* outT,
+qlora_status launch_nt(const uint16_t* X, const uint16_t* Y, bool y_natural, float* part, uint16_t* out,
                        float scale, int M, int C, int r, hipStream_t s) {
     const SplitPlan sp = plan_nt(M, C);
     const dim3 grid((unsigned)((M + 127) / 128), (unsigned)sp.splits);
-    const bool vec = (C % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15u) == 0) &&
-                     ((reinterpret_cast<uintptr_t>(Yt) & 15u) == 0);
+    const bool vec = (C % 8 == 0) && (!y_natural || r % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15u) == 0) &&
+                     ((reinterpret_cast<uintptr_t>(Y) & 15u) == 0);
     const int tq = (r + 31) / 32;
-#define QL_NT(TQ)                                                                                               \
-    if (vec) hipLaunchKernelGGL((nt_partial_kernel<TQ, true>), grid, dim3(256), 0, s, X, Yt, part, M, C, r, sp.chunk); \
-    else hipLaunchKernelGGL((nt_partial_kernel<TQ, false>), grid, dim3(256), 0, s, X, Yt, part, M, C, r, sp.chunk);
+#define QL_NT(TQ, NAT)                                                                                            \
+    if (vec) hipLaunchKernelGGL((nt_partial_kernel<TQ, true, NAT>), grid, dim3(256), 0, s, X, Y, part, M, C, r, sp.chunk); \
+    else hipLaunchKernelGGL((nt_partial_kernel<TQ, false, NAT>), grid, dim3(256), 0, s, X, Y, part, M, C, r, sp.chunk);
+#define QL_NT2(TQ) \
+    if (y_natural) { QL_NT(TQ, true) } else { QL_NT(TQ, false) }
     switch (tq) {
-        case 1: QL_NT(1) break;
-        case 2: QL_NT(2) break;
-        case 3: QL_NT(3) break;
-        default: QL_NT(4) break;
+        case 1: QL_NT2(1) break;
+        case 2: QL_NT2(2) break;
+        case 3: QL_NT2(3) break;
+        default: QL_NT2(4) break;
     }
+#undef QL_NT2
 #undef QL_NT
     const int64_t count = (int64_t)M * r;
     hipLaunchKernelGGL(finalize_bf16_kernel, dim3(blocks_for(count, 256)), dim3(256), 0, s, part, sp.splits, M, r,
-                       scale, out, outT);
+                       scale, out);
     return launch_status();
 }
 
-qlora_status launch_tn(const uint16_t* X, const uint16_t* ST, float* part, float* out, int M, int D, int r,
+qlora_status launch_tn(const uint16_t* X, const uint16_t* S, float* part, float* out, int M, int D, int r,
                        int64_t ld_d, int64_t ld_j, hipStream_t s) {
     const SplitPlan sp = plan_tn(M, D, r);
     const dim3 grid((unsigned)((D + kTnCols - 1) / kTnCols), (unsigned)sp.splits);
-    const bool vec = (D % 8 == 0) && (M % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15u) == 0) &&
-                     ((reinterpret_cast<uintptr_t>(ST) & 15u) == 0);
+    const bool vec = (D % 8 == 0) && (r % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15u) == 0) &&
+                     ((reinterpret_cast<uintptr_t>(S) & 15u) == 0);
     const int tq = (r + 31) / 32;
 #define QL_TN(TQ)                                                                                                \
-    if (vec) hipLaunchKernelGGL((tn_partial_kernel<TQ, true>), grid, dim3(256), 0, s, X, ST, part, M, D, r, sp.chunk); \
-    else hipLaunchKernelGGL((tn_partial_kernel<TQ, false>), grid, dim3(256), 0, s, X, ST, part, M, D, r, sp.chunk);
+    if (vec) hipLaunchKernelGGL((tn_partial_kernel<TQ, true>), grid, dim3(256), 0, s, X, S, part, M, D, r, sp.chunk); \
+    else hipLaunchKernelGGL((tn_partial_kernel<TQ, false>), grid, dim3(256), 0, s, X, S, part, M, D, r, sp.chunk);
     switch (tq) {
         case 1: QL_TN(1) break;
         case 2: QL_TN(2) break;
