@@ -236,19 +236,31 @@ __device__ __forceinline__ void store_acc(uint16_t* __restrict__ out, int64_t ld
 
 // ------------------------------------------------------------------ forward
 // Wave w owns output columns [64w, 64w + 64) of the 256 x 256 tile, all 256
-// rows (8 x 2 MFMA tiles).  The x tile goes HBM -> registers -> LDS (double
-// buffered); every wave reads all of it (8 operand reads per 16 MFMAs).  The
-// weight never touches LDS: lane (h, l32) holds, for its two columns, the 16
-// code bytes of k = 32h .. 32h + 31 of the current block, builds each
-// column's 16-entry bf16 table once per step and expands 8 codes at a time
-// into the MFMA B operand just before use, interleaved with the MFMAs of the
-// previous chunk.  Codes and scale bytes arrive two steps ahead; the scale is
-// converted only when its table is built.
+// rows (8 x 2 MFMA tiles).  The x tile (256 x 64) arrives by direct loads one
+// step ahead; every wave reads all of it (8 operand reads per 16 MFMAs).
+// Codes arrive four blocks (a super-step) at a time: the tile's 256 rows of
+// codes x 128 B are copied HBM -> LDS by direct loads, 8 full rows per 1 KB
+// instruction, a super-step ahead (16-byte chunks XOR-swizzled by row), and
+// thread t computes the block scales a_hat of tile row t for those blocks
+// into a small LDS table.  The dequantized weight never touches LDS: lane
+// (h, l32) reads, for its two columns, the 16 code bytes of k = 32h .. 32h +
+// 31 of the block and the block's a_hat, builds each column's 16-entry bf16
+// table and expands 8 codes at a time into the MFMA B operand just before use,
+// interleaved with the MFMAs of the previous chunk.
+constexpr int kSuper4 = 4;                                 // blocks per super-step
+constexpr int kCodeTileBytes = kTN * kSuper4 * kBlock / 2;  // 256 rows x 128 B
+
+template <bool Q8DW>
 __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ q8,
     const float* __restrict__ a2, const uint16_t* __restrict__ t, const uint16_t* __restrict__ Bl,
     uint16_t* __restrict__ y, int M, int N, int K, int r, int tiles_m, int tiles_n) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kTileBytes];
+    // separate objects, so that reads of one buffer never wait for loads into the other
+    __shared__ __attribute__((aligned(16))) uint8_t cds0[kCodeTileBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t cds1[kCodeTileBytes];
+    __shared__ __attribute__((aligned(16))) float ahs0[kTN * kSuper4];
+    __shared__ __attribute__((aligned(16))) float ahs1[kTN * kSuper4];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, l32 = lane & 31;
@@ -256,16 +268,14 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
     const int mt = tile / tiles_n, nt = tile - mt * tiles_n;
     const int m0 = mt * kTM, n0 = nt * kTN;
     const int KB = K / kTK;
+    const int NS = (KB + kSuper4 - 1) / kSuper4;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
 
-    int col[2];
-    const uint8_t* crow[2];
-    int64_t blk0[2];
+    int col[2], crl[2];  // global column; row of the code tile (column within the tile)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        col[u] = n0 + wave * 64 + u * 32 + l32;
-        const int cr = min(col[u], N - 1);  // columns past N compute garbage that is never stored
-        crow[u] = codes + (int64_t)cr * (K / 2) + h * 16;
-        blk0[u] = (int64_t)cr * KB;
+        crl[u] = wave * 64 + u * 32 + l32;
+        col[u] = n0 + crl[u];
     }
     // A operand offsets: rows 32 i + l32, chunk 4h + c; row tiles are immediate offsets
     uint32_t offA[4];
@@ -280,58 +290,122 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][u][v] = 0.0f;
 
-    struct Step {
-        u32x4_t c[2];
-        uint32_t q[2];
-        float g[2];
-    };
-    auto load_step = [&](int ks, Step& S) {
+    // ---- code tiles.  Instruction i of wave w fills code-tile rows 8 (8w + i) .. +7:
+    // lane l takes row 8 (8w + i) + l / 8 and LDS chunk l % 8, which holds that
+    // row's 16-byte chunk (l % 8) ^ (row % 8) (block 2 chunks, half of 32 B).
+    // Rows past N repeat row N - 1 (never stored); the whole offset is in voffset,
+    // so blocks past the end of the last row read as zero.
+    const uint32_t half_k = (uint32_t)K >> 1;
+    const i32x4_t crs = buffer_rsrc(codes, (uint32_t)((uint64_t)N * half_k));
+    uint32_t cvoff[8];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            S.c[u] = *reinterpret_cast<const u32x4_t*>(crow[u] + (int64_t)ks * (kTK / 2));
-            const int64_t blk = blk0[u] + ks;
-            S.q[u] = q8[blk];
-            S.g[u] = a2[blk >> 8];
+    for (int i = 0; i < 8; ++i) {
+        const int row = 8 * (8 * wv + i) + (lane >> 3);
+        const int q = (lane & 7) ^ (row & 7);
+        cvoff[i] = (uint32_t)min(n0 + row, N - 1) * half_k + 32u * (uint32_t)(q >> 1) + 16u * (uint32_t)(q & 1);
+    }
+    auto load_codes = [&](uint8_t* dst, int S) __attribute__((always_inline)) {
+        const uint32_t boff = 32u * (uint32_t)(kSuper4 * S);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            auto* d = reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(
+                reinterpret_cast<uintptr_t>(dst + 1024 * (8 * wv + i)));
+            raw_buffer_load_lds(crs, d, 16, (int)(cvoff[i] + boff), 0, 0, 0);
         }
+    };
+    // ---- block scales: thread tid, tile row tid, the 4 blocks of a super-step
+    const int srow = min(n0 + tid, N - 1);
+    const int64_t sblk = (int64_t)srow * KB;
+    struct Sc {
+        uint32_t q;   // 8-bit scale codes of the 4 blocks, block j in byte j
+        float g0, g1; // second-level scales of the first and last block's groups
+    };
+    auto load_scales = [&](int S, Sc& sc) __attribute__((always_inline)) {
+        const int b0 = kSuper4 * S;
+        if (Q8DW) {  // blocks per row % 4 == 0: the 4 codes are one aligned dword
+            sc.q = *reinterpret_cast<const uint32_t*>(q8 + sblk + b0);
+        } else {
+            uint32_t qv = 0;
+#pragma unroll
+            for (int j = 0; j < kSuper4; ++j) qv |= (uint32_t)q8[sblk + min(b0 + j, KB - 1)] << (8 * j);
+            sc.q = qv;
+        }
+        sc.g0 = a2[(sblk + b0) >> 8];
+        sc.g1 = a2[(sblk + min(b0 + kSuper4 - 1, KB - 1)) >> 8];
+    };
+    auto make_scales = [&](const Sc& sc, float* dst, int S) __attribute__((always_inline)) {
+        const int b0 = kSuper4 * S;
+        const float s0 = scale_step(sc.g0), s1 = scale_step(sc.g1);
+        const int64_t g0 = (sblk + b0) >> 8;
+        f32x4_t ah;
+#pragma unroll
+        for (int j = 0; j < kSuper4; ++j) {
+            const int b = b0 + j;
+            const float st = ((sblk + b) >> 8) == g0 ? s0 : s1;
+            ah[j] = b < KB ? st * (float)((sc.q >> (8 * j)) & 0xFFu) : 0.0f;
+        }
+        *reinterpret_cast<f32x4_t*>(dst + kSuper4 * tid) = ah;
+    };
+    // this lane's 16 code bytes and a_hat of column u at block j of a super-step
+    auto read_codes = [&](const uint8_t* cd, int j, int u) __attribute__((always_inline)) {
+        return *reinterpret_cast<const u32x4_t*>(cd + crl[u] * 128 + 16 * ((2 * j + h) ^ (crl[u] & 7)));
     };
 
     // x panel rows [m0, M) as a buffer; lane's tile row 8*wave + lane/8, chunk
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
     const i32x4_t xrs = buffer_rsrc(x + (int64_t)m0 * K, (uint32_t)((int64_t)(M - m0) * K * 2));
     const int xrow = 8 * wv + (lane >> 3);
     const int xchunk = (lane & 7) ^ (((xrow ^ (xrow >> 3)) & 3) ^ (xrow & 4));
     const uint32_t xvoff = (uint32_t)(((int64_t)xrow * K + 8 * xchunk) * 2);
 
+    // prologue: x tile 0, super-step 0's codes and scales
     load_tile_direct(xrs, lds, xvoff, wv, 0, K);
-    Step cur, nxt;
-    load_step(0, cur);
-    load_step(min(1, KB - 1), nxt);
+    load_codes(cds0, 0);
+    Sc sc;
+    load_scales(0, sc);
+    make_scales(sc, ahs0, 0);
+    wait_direct_loads();
+    __syncthreads();
     Nf4Tab T[2];
+    u32x4_t cc[2];
     bf16x8 b[2][2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        T[u] = make_tab(scale_step(cur.g[u]) * (float)cur.q[u]);
-        b[0][u] = as_bf16x8(deq8(T[u], cur.c[u][0]));
+        cc[u] = read_codes(cds0, 0, u);
+        T[u] = make_tab(ahs0[kSuper4 * crl[u]]);
+        b[0][u] = as_bf16x8(deq8(T[u], cc[u][0]));
     }
-    wait_direct_loads();
-    __syncthreads();
 
-    // Software pipeline per step ks: operand reads of chunk c+1 and the
-    // expansion of chunk c+1's codes overlap the MFMAs of chunk c; the tables
-    // of step ks+1 are built while chunk 0's reads are in flight and its
-    // chunk-0 operands are expanded during chunk 3.
-    for (int ks = 0; ks < KB; ++ks) {
+    // One step ks = 4 S + j.  Operand reads of chunk c+1 and the expansion of
+    // chunk c+1's codes overlap the MFMAs of chunk c; the tables of step ks+1 are
+    // built while chunk 0's reads are in flight and its chunk-0 operands are
+    // expanded during chunk 3.  At j = 0 the next super-step's codes and scales
+    // are requested, at j = 2 its scales are written, and at j = 3 step ks+1's
+    // operands come from the other buffers.
+    auto do_step = [&](int S, int j, uint8_t* cdC, float* ahC, uint8_t* cdO, float* ahO) __attribute__((always_inline)) {
+        const int ks = kSuper4 * S + j;
         const uint8_t* A = lds + (ks & 1) * kTileBytes;
         uint8_t* An = lds + ((ks + 1) & 1) * kTileBytes;
         bf16x8 a[2][8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) a[0][i] = *reinterpret_cast<const bf16x8*>(A + offA[0] + 4096u * i);
         load_tile_direct(xrs, An, xvoff, wv, min(ks + 1, KB - 1) * kTK, K);
-        Step nn;
-        load_step(min(ks + 2, KB - 1), nn);
+        const bool pre = j == 0 && S + 1 < NS;
+        if (pre) {
+            __builtin_amdgcn_sched_barrier(kAllButVmem);  // keep the x tile's loads first
+            load_codes(cdO, S + 1);
+            load_scales(S + 1, sc);
+        }
+        // step ks+1's codes and tables
+        const uint8_t* cdN = j < kSuper4 - 1 ? cdC : cdO;
+        const float* ahN = j < kSuper4 - 1 ? ahC : ahO;
+        const int jn = (j + 1) & (kSuper4 - 1);
+        u32x4_t cn[2];
         Nf4Tab Tn[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) Tn[u] = make_tab(scale_step(nxt.g[u]) * (float)nxt.q[u]);
+        for (int u = 0; u < 2; ++u) {
+            cn[u] = read_codes(cdN, jn, u);
+            Tn[u] = make_tab(ahN[kSuper4 * crl[u] + jn]);
+        }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int p = c & 1;
@@ -344,23 +418,33 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
                 acc[i][0] = mfma32(a[p][i], b[p][0], acc[i][0]);
                 acc[i][1] = mfma32(a[p][i], b[p][1], acc[i][1]);
             }
-            b[p ^ 1][0] = as_bf16x8(c < 3 ? deq8(T[0], cur.c[0][c + 1]) : deq8(Tn[0], nxt.c[0][0]));
+            b[p ^ 1][0] = as_bf16x8(c < 3 ? deq8(T[0], cc[0][c + 1]) : deq8(Tn[0], cn[0][0]));
 #pragma unroll
             for (int i = 4; i < 8; ++i) {
                 acc[i][0] = mfma32(a[p][i], b[p][0], acc[i][0]);
                 acc[i][1] = mfma32(a[p][i], b[p][1], acc[i][1]);
             }
-            b[p ^ 1][1] = as_bf16x8(c < 3 ? deq8(T[1], cur.c[1][c + 1]) : deq8(Tn[1], nxt.c[1][0]));
+            b[p ^ 1][1] = as_bf16x8(c < 3 ? deq8(T[1], cc[1][c + 1]) : deq8(Tn[1], cn[1][0]));
         }
         // chunk 3 used b[1]; the expansion of step ks+1's chunk 0 is in b[0]
 #pragma unroll
-        for (int u = 0; u < 2; ++u) T[u] = Tn[u];
-        cur = nxt;
-        nxt = nn;
-        // the codes of step ks + 2 (issued mid-step, mostly L2 hits) are waited
-        // for here as well; measured faster than leaving them in flight
-        wait_direct_loads();
+        for (int u = 0; u < 2; ++u) {
+            T[u] = Tn[u];
+            cc[u] = cn[u];
+        }
+        if (j == 2 && S + 1 < NS) make_scales(sc, ahO, S + 1);
+        if (pre) wait_direct_loads_behind<Q8DW ? 11 : 14>();  // only this step's x tile must have landed
+        else wait_direct_loads();
         __syncthreads();
+    };
+    auto do_super = [&](int S, uint8_t* cdC, float* ahC, uint8_t* cdO, float* ahO) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < kSuper4; ++j)
+            if (kSuper4 * S + j < KB) do_step(S, j, cdC, ahC, cdO, ahO);
+    };
+    for (int S = 0; S < NS; S += 2) {
+        do_super(S, cds0, ahs0, cds1, ahs1);
+        if (S + 1 < NS) do_super(S + 1, cds1, ahs1, cds0, ahs0);
     }
 
     u32x4_t xr[8];
@@ -624,8 +708,14 @@ qlora_status launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const uint
     // x is 16-byte aligned (checked by the caller) and K % 64 == 0, so every
     // 16-byte chunk of a row is aligned; a 256-row panel must fit a 32-bit offset
     if ((int64_t)kTM * K * 2 >= (int64_t(1) << 32)) return QLORA_ERR_UNSUPPORTED_SHAPE;
-    hipLaunchKernelGGL(nf4_gemm_fwd_kernel, dim3(tm * tn), dim3(kT), 0, s, x, codes, q8, a2, t, B, y, M, N, K, r,
-                       tm, tn);
+    // code-tile offsets (including blocks past a row's end) must fit a 32-bit voffset
+    if ((uint64_t)N * (uint64_t)K / 2 + 4096 >= (uint64_t(1) << 32)) return QLORA_ERR_UNSUPPORTED_SHAPE;
+    if ((K / kTK) % kSuper4 == 0)
+        hipLaunchKernelGGL(nf4_gemm_fwd_kernel<true>, dim3(tm * tn), dim3(kT), 0, s, x, codes, q8, a2, t, B, y, M, N,
+                           K, r, tm, tn);
+    else
+        hipLaunchKernelGGL(nf4_gemm_fwd_kernel<false>, dim3(tm * tn), dim3(kT), 0, s, x, codes, q8, a2, t, B, y, M,
+                           N, K, r, tm, tn);
     return launch_status();
 }
 
