@@ -35,6 +35,7 @@ constexpr int kTK = 64;             // reduction step
 constexpr int kTileBytes = kTM * kTK * 2;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -449,28 +450,99 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
 
     u32x4_t xr[8];
     // LoRA up-projection: r more reduction steps with A-operand t [M, r] and
-    // B-operand B [r, N] (t already carries the alpha/r scale).
+    // B-operand B [r, N] (t already carries the alpha/r scale).  B's rows
+    // [j0, j0 + 64) x the tile's 256 columns are staged in LDS in natural
+    // layout (rows 0-31 in cds0, 32-63 in cds1, 544-byte rows) and read down
+    // their columns with ds_read_b64_tr_b16.
     const bool col_ok0 = col[0] < N, col_ok1 = col[1] < N;
+    const bool tvec = (r % 8) == 0;   // t rows are whole 16-byte chunks
+    const bool nvec = (N % 8) == 0;   // rows of B and y are whole 16-byte chunks
+    constexpr int kBLd = 544;         // bytes per staged B row
+    const int tj = l32 & 15, tg = l32 >> 4;
     for (int j0 = 0; j0 < r; j0 += kTK) {
-        load_tile<false>(xr, t, r, m0, M, j0, r, tid);
+        if (tvec) load_tile<true>(xr, t, r, m0, M, j0, r, tid);
+        else load_tile<false>(xr, t, r, m0, M, j0, r, tid);
+        {
+            u32x4_t bv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int idx = tid + kT * e, row = idx >> 5, n = n0 + 8 * (idx & 31), j = j0 + row;
+                if (nvec) {
+                    bv[e] = (j < r && n < N) ? *reinterpret_cast<const u32x4_t*>(Bl + (int64_t)j * N + n)
+                                             : u32x4_t{0u, 0u, 0u, 0u};
+                } else {
+                    uint32_t w[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t lo = (j < r && n + 2 * i < N) ? Bl[(int64_t)j * N + n + 2 * i] : 0u;
+                        const uint32_t hi = (j < r && n + 2 * i + 1 < N) ? Bl[(int64_t)j * N + n + 2 * i + 1] : 0u;
+                        w[i] = lo | (hi << 16);
+                    }
+                    bv[e] = u32x4_t{w[0], w[1], w[2], w[3]};
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int idx = tid + kT * e, row = idx >> 5;
+                *reinterpret_cast<u32x4_t*>((row < 32 ? cds0 : cds1) + (row & 31) * kBLd + 16 * (idx & 31)) = bv[e];
+            }
+        }
         store_ftile(lds, xr, tid);
         __syncthreads();
+        const uint8_t* bhalf = h ? cds1 : cds0;   // B rows 32h .. 32h + 31 of this step
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const bf16x8 bl0 = gather8(Bl, N, j0 + 32 * h + 8 * c, r, col[0], col_ok0);
-            const bf16x8 bl1 = gather8(Bl, N, j0 + 32 * h + 8 * c, r, col[1], col_ok1);
+            bf16x8 bl[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const uint8_t* p = bhalf + (8 * c + (tj >> 2)) * kBLd + 2 * (wave * 64 + 32 * u + 16 * tg + 4 * (tj & 3));
+                const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    reinterpret_cast<__attribute__((address_space(3))) s16x4_t*>(reinterpret_cast<uintptr_t>(p)));
+                const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    reinterpret_cast<__attribute__((address_space(3))) s16x4_t*>(reinterpret_cast<uintptr_t>(p + 4 * kBLd)));
+                bl[u] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const bf16x8 av = *reinterpret_cast<const bf16x8*>(lds + offA[c] + 4096u * i);
-                acc[i][0] = mfma32(av, bl0, acc[i][0]);
-                acc[i][1] = mfma32(av, bl1, acc[i][1]);
+                acc[i][0] = mfma32(av, bl[0], acc[i][0]);
+                acc[i][1] = mfma32(av, bl[1], acc[i][1]);
             }
         }
         __syncthreads();
     }
 
-    const bool col_ok[2] = {col_ok0, col_ok1};
-    store_acc(y, N, acc, m0, M, col, col_ok, h);
+    // y tile as bf16 through LDS, 128 rows at a time: lanes write their values
+    // into a [128][256] staging area, then each thread stores 16-byte row chunks
+    if (!nvec) {
+        const bool col_ok[2] = {col_ok0, col_ok1};
+        store_acc(y, N, acc, m0, M, col, col_ok, h);
+        return;
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int i = 4 * half + ii;
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int row = 32 * ii + 8 * (v >> 2) + 4 * h + (v & 3);
+                    *reinterpret_cast<uint16_t*>(lds + row * 512 + 2 * crl[u]) =
+                        (uint16_t)(pack_bf16x2(acc[i][u][v], 0.0f) & 0xFFFFu);
+                }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int idx = tid + kT * e, row = idx >> 5, ch = idx & 31;
+            const int m = m0 + 128 * half + row, n = n0 + 8 * ch;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + row * 512 + 16 * ch);
+            if (m < M && n < N) *reinterpret_cast<u32x4_t*>(y + (int64_t)m * N + n) = v;
+        }
+        __syncthreads();
+    }
 }
 
 // ------------------------------------------------------------------ backward dx
@@ -484,7 +556,6 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
 // tile arrives by direct HBM -> LDS loads.  Waves are 2 x 2 (128 x 128 each);
 // the next step's codes arrive two steps ahead and are expanded while this
 // step's MFMAs run.
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 // weight tile layout: 64 rows of 256 bf16 (512 B), 16-byte chunks XOR-swizzled
 // by a 4-bit function of the row (conflict-free 16-byte row stores and
@@ -659,9 +730,11 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
     }
 
     // LoRA: r more reduction steps with A-operand u [M, r] (LDS) and B-operand
-    // A^T, i.e. rows of A [K, r] read directly.
+    // A^T, i.e. rows of A [K, r] read directly (one 16-byte load when r % 8 == 0).
+    const bool rvec = (r % 8) == 0;
     for (int j0 = 0; j0 < r; j0 += kTK) {
-        load_tile<false>(ar, u_, r, m0, M, j0, r, tid);
+        if (rvec) load_tile<true>(ar, u_, r, m0, M, j0, r, tid);
+        else load_tile<false>(ar, u_, r, m0, M, j0, r, tid);
         store_ftile(ldsA0, ar, tid);
         __syncthreads();
 #pragma unroll
@@ -673,7 +746,13 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int col = k0 + 128 * wk + 32 * u + l32;
-                b[u] = row8(Al, r, col, col < K, j0 + 16 * c + 8 * h, r);
+                const int j = j0 + 16 * c + 8 * h;
+                if (rvec) {
+                    b[u] = (col < K && j < r) ? *reinterpret_cast<const bf16x8*>(Al + (int64_t)col * r + j)
+                                              : as_bf16x8(u32x4_t{0u, 0u, 0u, 0u});
+                } else {
+                    b[u] = row8(Al, r, col, col < K, j, r);
+                }
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -683,18 +762,26 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
         __syncthreads();
     }
 
-    // epilogue: lane holds column l32 of each 32 x 32 tile, rows 8*(v/4) + 4h + v%4
+    // dx tile as bf16 through LDS (256 x 256 x 2 B: all four tile buffers):
+    // lane (column l32 of each 32 x 32 tile, rows 8*(v/4) + 4h + v%4) writes its
+    // values, then each thread stores 16-byte row chunks
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int col = k0 + 128 * wk + 32 * u + l32;
-        if (col >= K) continue;
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int m = m0 + 128 * wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-                if (m < M) dx[(int64_t)m * K + col] = (uint16_t)(pack_bf16x2(acc[i][u][v], 0.0f) & 0xFFFFu);
+                const int row = 128 * wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+                *reinterpret_cast<uint16_t*>(lds + row * 512 + 2 * (128 * wk + 32 * u + l32)) =
+                    (uint16_t)(pack_bf16x2(acc[i][u][v], 0.0f) & 0xFFFFu);
             }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+        const int idx = tid + kT * e, row = idx >> 5, ch = idx & 31;
+        const int m = m0 + row, k = k0 + 8 * ch;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + row * 512 + 16 * ch);
+        if (m < M && k < K) *reinterpret_cast<u32x4_t*>(dx + (int64_t)m * K + k) = v;
     }
 }
 
