@@ -45,34 +45,52 @@ __device__ __forceinline__ bf16x8 load8_row(const uint16_t* __restrict__ src, in
     return __builtin_bit_cast(bf16x8, u32x4_t{w[0], w[1], w[2], w[3]});
 }
 
+// Branch-free vector loads: each workgroup addresses the rows it reads through
+// a buffer resource based at its first row (so offsets stay far below 2 GiB),
+// and an offset is replaced by one past any buffer when the chunk lies outside
+// the valid range, so the hardware returns zeros.  Straight-line loads keep
+// the compiler's wait counts exact (a load under a branch makes it wait for
+// everything in flight).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t buf_rsrc(const void* p, uint64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)(uint32_t)bytes, 0x00020000);
+}
+__device__ __forceinline__ bf16x8 bload8(rsrc_t rs, bool ok, uint32_t elem) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? 2u * elem : 0x80000000u, 0, 0));
+}
+
 // Slices of a small row-major [R, r] operand (A [K, r], t or u [M, r]) live in
 // LDS with rows of 32*TQ + 16 bf16: for every TQ the 16-lane groups of the
 // transposed reads below then touch 16 distinct pairs of banks.
 template <int TQ>
 constexpr int slice_ld() { return 32 * TQ + 16; }
 
-// Rows [row0, row0 + rows_used) of src (row stride r; rows at or past row_end and
+// Rows [row0, row0 + MAXROWS) of src (row stride r; rows at or past row_end and
 // columns at or past r read as zero) into dst[row * slice_ld + col], all loads of
-// a batch issued before its stores.
+// a batch issued before its stores.  Every row is written, so steps padded past
+// the end of a split multiply zeros.
 template <int TQ, bool VEC, int MAXROWS>
 __device__ __forceinline__ void stage_slice(uint16_t* __restrict__ dst, const uint16_t* __restrict__ src, int r,
-                                            int row0, int row_end, int rows_used, int tid) {
+                                            int row0, int row_end, int tid) {
     constexpr int kCh = 4 * TQ;  // 16-byte chunks per slice row
     constexpr int kLd = slice_ld<TQ>();
     constexpr int kPer = MAXROWS * kCh / 256;
     constexpr int kBatch = kPer < 16 ? kPer : 16;
+    const rsrc_t rs = buf_rsrc(src + (int64_t)row0 * r, (uint64_t)(row_end - row0) * r * 2);
 #pragma unroll
     for (int e0 = 0; e0 < kPer; e0 += kBatch) {
         bf16x8 v[kBatch];
 #pragma unroll
         for (int e = 0; e < kBatch; ++e) {
             const int idx = tid + 256 * (e0 + e), row = idx / kCh, ch = idx % kCh;
-            if (row < rows_used) v[e] = load8_row<VEC>(src, r, row0 + row, row_end, 8 * ch, r);
+            const bool ok = row0 + row < row_end;
+            v[e] = VEC ? bload8(rs, ok && 8 * ch < r, (uint32_t)(row * r + 8 * ch))
+                       : load8_row<false>(src, r, row0 + row, row_end, 8 * ch, r);
         }
 #pragma unroll
         for (int e = 0; e < kBatch; ++e) {
             const int idx = tid + 256 * (e0 + e), row = idx / kCh, ch = idx % kCh;
-            if (row < rows_used) *reinterpret_cast<bf16x8*>(dst + row * kLd + 8 * ch) = v[e];
+            *reinterpret_cast<bf16x8*>(dst + row * kLd + 8 * ch) = v[e];
         }
     }
 }
@@ -105,13 +123,14 @@ __device__ __forceinline__ bf16x8 slice_col8(const uint16_t* __restrict__ slice,
 // reduction indices, as long as both operands agree).
 constexpr int kNtMaxChunk = 512;  // columns of C per split
 constexpr int kNtRing = 4;
+static_assert(2 * kNtRing * 64 == kNtMaxChunk, "two ring passes cover a split");
 
 template <int TQ, bool YNAT>
 constexpr int nt_slice_elems() {
     return YNAT ? kNtMaxChunk * slice_ld<TQ>() : 32 * TQ * (kNtMaxChunk + 8);
 }
 
-template <int TQ, bool VEC, bool YNAT>
+template <int TQ, bool VEC, bool YNAT, int NST>
 __global__ __launch_bounds__(256) void nt_partial_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Y,
                                                          float* __restrict__ part, int M, int C, int r, int chunk) {
     constexpr int kLdT = kNtMaxChunk + 8;  // Yt row (bf16)
@@ -123,36 +142,47 @@ __global__ __launch_bounds__(256) void nt_partial_kernel(const uint16_t* __restr
     const int split = blockIdx.y;
     const int c_begin = split * chunk;
     const int c_end = min(C, c_begin + chunk);
-    const int steps = (c_end - c_begin + 63) >> 6;
 
-    // X ring first (the long-latency HBM stream), then the Y slice (L2)
+    // X ring first (the long-latency HBM stream), then the Y slice (L2).  Steps
+    // past the split's end load zeros, so no load is conditional and the waits
+    // for the ring are exact counts.
+    const int bm0 = blockIdx.x * 128;
+    const rsrc_t xrs = buf_rsrc(X + (int64_t)bm0 * C, (uint64_t)min(128, M - bm0) * C * 2);
+    const int xrow = m0 + l32;
     bf16x8 xa[kNtRing][4];
     auto load_x = [&](int st, bf16x8 (&dst)[4]) {
-        const int c = c_begin + 64 * st;
+        const int c = c_begin + 64 * st + 32 * h;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = load8_row<VEC>(X, C, m0 + l32, M, c + 32 * h + 8 * i, c_end);
+        for (int i = 0; i < 4; ++i) {
+            if (VEC)
+                dst[i] = bload8(xrs, xrow < M && c + 8 * i < c_end, (uint32_t)((xrow - bm0) * C + c + 8 * i));
+            else
+                dst[i] = load8_row<false>(X, C, xrow, M, c + 8 * i, c_end);
+        }
     };
 #pragma unroll
-    for (int st = 0; st < kNtRing; ++st)
-        if (st < steps) load_x(st, xa[st]);
+    for (int st = 0; st < kNtRing; ++st) load_x(st, xa[st]);
     if (YNAT) {
-        stage_slice<TQ, VEC, kNtMaxChunk>(ys, Y, r, c_begin, c_end, 64 * steps, tid);
+        stage_slice<TQ, VEC, kNtMaxChunk>(ys, Y, r, c_begin, c_end, tid);
     } else {
-        // Yt slice: 32*TQ rows x 64 chunks of 16 B
+        // Yt slice: 32*TQ rows x 64 chunks of 16 B (zeros past r or c_end)
         constexpr int kPer = 32 * TQ * (kNtMaxChunk / 8) / 256;
         constexpr int kBatch = kPer < 16 ? kPer : 16;
+        const rsrc_t yrs = buf_rsrc(Y + c_begin, ((uint64_t)r * C - c_begin) * 2);
 #pragma unroll
         for (int e0 = 0; e0 < kPer; e0 += kBatch) {
             bf16x8 yv[kBatch];
 #pragma unroll
             for (int e = 0; e < kBatch; ++e) {
                 const int idx = tid + 256 * (e0 + e), row = idx >> 6, ch = idx & 63;
-                if (8 * ch < 64 * steps) yv[e] = load8_row<VEC>(Y, C, row, r, c_begin + 8 * ch, c_end);
+                const int c = c_begin + 8 * ch;
+                yv[e] = VEC ? bload8(yrs, row < r && c < c_end, (uint32_t)(row * C + 8 * ch))
+                            : load8_row<false>(Y, C, row, r, c, c_end);
             }
 #pragma unroll
             for (int e = 0; e < kBatch; ++e) {
                 const int idx = tid + 256 * (e0 + e), row = idx >> 6, ch = idx & 63;
-                if (8 * ch < 64 * steps) *reinterpret_cast<bf16x8*>(&ys[row * kLdT + 8 * ch]) = yv[e];
+                *reinterpret_cast<bf16x8*>(&ys[row * kLdT + 8 * ch]) = yv[e];
             }
         }
     }
@@ -163,26 +193,28 @@ __global__ __launch_bounds__(256) void nt_partial_kernel(const uint16_t* __restr
     for (int q = 0; q < TQ; ++q)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[q][v] = 0.0f;
-    for (int s0 = 0; s0 < steps; s0 += kNtRing) {
+    // NST (4 or 8, at least the split's step count) steps, all unrolled: a
+    // rolled loop copies the ring registers at its back edge, which waits for
+    // the loads in flight, and an early exit lets the compiler sink the refills
+    // behind it.
 #pragma unroll
-        for (int u = 0; u < kNtRing; ++u) {
-            const int st = s0 + u;
-            if (st < steps) {
-                bf16x8 ca[4];
+    for (int st = 0; st < NST; ++st) {
+        const int u = st % kNtRing;
+        bf16x8 ca[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) ca[i] = xa[u][i];
-                if (st + kNtRing < steps) load_x(st + kNtRing, xa[u]);
+        for (int i = 0; i < 4; ++i) ca[i] = xa[u][i];
+        if (st + kNtRing < NST) load_x(st + kNtRing, xa[u]);
+        // keep the refill ahead of this step's MFMAs
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int q = 0; q < TQ; ++q) {
-                        const int c = 64 * st + 32 * h + 8 * i;  // slice column of the lane's k slots
-                        const bf16x8 yb = YNAT ? slice_col8(ys, kLdN, c, 32 * q + 16 * tg, tj)
-                                               : *reinterpret_cast<const bf16x8*>(&ys[(32 * q + l32) * kLdT + c]);
-                        acc[q] = mfma32(ca[i], yb, acc[q]);
-                    }
+            for (int q = 0; q < TQ; ++q) {
+                const int c = 64 * st + 32 * h + 8 * i;  // slice column of the lane's k slots
+                const bf16x8 yb = YNAT ? slice_col8(ys, kLdN, c, 32 * q + 16 * tg, tj)
+                                       : *reinterpret_cast<const bf16x8*>(&ys[(32 * q + l32) * kLdT + c]);
+                acc[q] = mfma32(ca[i], yb, acc[q]);
             }
-        }
     }
     float* out = part + (int64_t)split * M * r;
 #pragma unroll
@@ -233,23 +265,31 @@ __global__ __launch_bounds__(256) void tn_partial_kernel(const uint16_t* __restr
     const int m_begin = split * chunk;
     const int m_end = min(M, m_begin + chunk);
     const int steps = (m_end - m_begin + kTnRows - 1) / kTnRows;
-    // loader: row tid/4 of a 64-row step, columns 32*(tid%4) .. +31
+    // loader: row tid/4 of a 64-row step, columns 32*(tid%4) .. +31.  As in the
+    // down-projection, the step loop runs a multiple of the ring depth (at most
+    // kTnMaxChunk / 64 steps) and padded steps load zeros: no conditional loads.
     const int lr = tid >> 2, lc = (tid & 3) * 32;
+    const rsrc_t xrs = buf_rsrc(X + (int64_t)m_begin * D, (uint64_t)(m_end - m_begin) * D * 2);
     bf16x8 xr[kTnRing][4];
     auto load_x = [&](int st, bf16x8 (&dst)[4]) {
-        const int m = m_begin + kTnRows * st;
+        const int m = m_begin + kTnRows * st + lr;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = load8_row<VEC>(X, D, m + lr, m_end, d0 + lc + 8 * i, D);
+        for (int i = 0; i < 4; ++i) {
+            const int d = d0 + lc + 8 * i;
+            if (VEC)
+                dst[i] = bload8(xrs, m < m_end && d < D, (uint32_t)((m - m_begin) * D + d));
+            else
+                dst[i] = load8_row<false>(X, D, m, m_end, d, D);
+        }
     };
     auto store_x = [&](const bf16x8 (&src)[4], int buf) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) *reinterpret_cast<bf16x8*>(&tile[buf][lr * kTnLd + lc + 8 * i]) = src[i];
     };
 #pragma unroll
-    for (int st = 0; st < kTnRing; ++st)
-        if (st < steps) load_x(st, xr[st]);
-    stage_slice<TQ, VEC, kTnMaxChunk>(ss, S, r, m_begin, m_end, kTnRows * steps, tid);
-    if (steps > 0) store_x(xr[0], 0);
+    for (int st = 0; st < kTnRing; ++st) load_x(st, xr[st]);
+    stage_slice<TQ, VEC, kTnMaxChunk>(ss, S, r, m_begin, m_end, tid);
+    store_x(xr[0], 0);
     __syncthreads();
 
     f32x16_t acc[TQ];
@@ -262,24 +302,22 @@ __global__ __launch_bounds__(256) void tn_partial_kernel(const uint16_t* __restr
 #pragma unroll
         for (int u = 0; u < kTnRing; ++u) {
             const int st = s0 + u;
-            if (st < steps) {
-                const int buf = st & 1;
-                // next step's rows into the other buffer (read two steps ago), and
-                // this ring slot's next load (its data went to LDS a step ago)
-                if (st + 1 < steps) store_x(xr[(u + 1) % kTnRing], buf ^ 1);
-                if (st + kTnRing < steps) load_x(st + kTnRing, xr[u]);
+            const int buf = u & 1;
+            // next step's rows into the other buffer (read two steps ago), and
+            // this ring slot's next load (its data went to LDS a step ago)
+            store_x(xr[(u + 1) % kTnRing], buf ^ 1);
+            load_x(st + kTnRing, xr[u]);
 #pragma unroll
-                for (int mc = 0; mc < kTnRows / 16; ++mc) {
-                    const int mr = mc * 16 + 8 * h;   // tile row of this lane's first k slot
-                    const bf16x8 a = slice_col8(tile[buf], kTnLd, mr, 32 * wave + 16 * tg, tj);
+            for (int mc = 0; mc < kTnRows / 16; ++mc) {
+                const int mr = mc * 16 + 8 * h;   // tile row of this lane's first k slot
+                const bf16x8 a = slice_col8(tile[buf], kTnLd, mr, 32 * wave + 16 * tg, tj);
 #pragma unroll
-                    for (int q = 0; q < TQ; ++q) {
-                        const bf16x8 b = slice_col8(ss, kSLd, kTnRows * st + mr, 32 * q + 16 * tg, tj);
-                        acc[q] = mfma32(a, b, acc[q]);
-                    }
+                for (int q = 0; q < TQ; ++q) {
+                    const bf16x8 b = slice_col8(ss, kSLd, kTnRows * st + mr, 32 * q + 16 * tg, tj);
+                    acc[q] = mfma32(a, b, acc[q]);
                 }
-                __syncthreads();
             }
+            __syncthreads();
         }
     }
     float* out = part + (int64_t)split * D * r;
@@ -320,14 +358,23 @@ qlora_status launch_nt(const uint16_t* X, const uint16_t* Y, bool y_natural, flo
                        float scale, int M, int C, int r, hipStream_t s) {
     const SplitPlan sp = plan_nt(M, C);
     const dim3 grid((unsigned)((M + 127) / 128), (unsigned)sp.splits);
+    // vector path: 16-byte aligned rows, and one workgroup's rows (128 of X, r of
+    // Yt) under 1 GiB of buffer offsets
     const bool vec = (C % 8 == 0) && (!y_natural || r % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15u) == 0) &&
-                     ((reinterpret_cast<uintptr_t>(Y) & 15u) == 0);
+                     ((reinterpret_cast<uintptr_t>(Y) & 15u) == 0) && (int64_t)C * 128 * 2 < (int64_t(1) << 30);
     const int tq = (r + 31) / 32;
-#define QL_NT(TQ, NAT)                                                                                            \
-    if (vec) hipLaunchKernelGGL((nt_partial_kernel<TQ, true, NAT>), grid, dim3(256), 0, s, X, Y, part, M, C, r, sp.chunk); \
-    else hipLaunchKernelGGL((nt_partial_kernel<TQ, false, NAT>), grid, dim3(256), 0, s, X, Y, part, M, C, r, sp.chunk);
-#define QL_NT2(TQ) \
-    if (y_natural) { QL_NT(TQ, true) } else { QL_NT(TQ, false) }
+    const bool short_split = sp.chunk <= 64 * kNtRing;
+#define QL_NT(TQ, V, NAT)                                                                                            \
+    if (short_split) hipLaunchKernelGGL((nt_partial_kernel<TQ, V, NAT, kNtRing>), grid, dim3(256), 0, s, X, Y, part, M, \
+                                        C, r, sp.chunk);                                                             \
+    else hipLaunchKernelGGL((nt_partial_kernel<TQ, V, NAT, 2 * kNtRing>), grid, dim3(256), 0, s, X, Y, part, M, C, r,  \
+                            sp.chunk);
+#define QL_NT2(TQ)                                    \
+    if (y_natural) {                                  \
+        if (vec) { QL_NT(TQ, true, true) } else { QL_NT(TQ, false, true) } \
+    } else {                                          \
+        if (vec) { QL_NT(TQ, true, false) } else { QL_NT(TQ, false, false) } \
+    }
     switch (tq) {
         case 1: QL_NT2(1) break;
         case 2: QL_NT2(2) break;
@@ -346,8 +393,9 @@ qlora_status launch_tn(const uint16_t* X, const uint16_t* S, float* part, float*
                        int64_t ld_d, int64_t ld_j, hipStream_t s) {
     const SplitPlan sp = plan_tn(M, D, r);
     const dim3 grid((unsigned)((D + kTnCols - 1) / kTnCols), (unsigned)sp.splits);
+    // vector path: 16-byte aligned rows, and one split's rows of X under 1 GiB
     const bool vec = (D % 8 == 0) && (r % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15u) == 0) &&
-                     ((reinterpret_cast<uintptr_t>(S) & 15u) == 0);
+                     ((reinterpret_cast<uintptr_t>(S) & 15u) == 0) && (int64_t)D * 512 * 2 < (int64_t(1) << 30);
     const int tq = (r + 31) / 32;
 #define QL_TN(TQ)                                                                                                \
     if (vec) hipLaunchKernelGGL((tn_partial_kernel<TQ, true>), grid, dim3(256), 0, s, X, S, part, M, D, r, sp.chunk); \
