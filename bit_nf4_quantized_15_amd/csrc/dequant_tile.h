@@ -4,9 +4,10 @@
 // a_hat = fl32(fl32(a2/255) * q8), so its 16 possible bf16 values
 // RNE_bf16(fl32(a_hat * c_j)) form a per-block table.  The table is kept as
 // two 16-byte byte tables (low bytes, high bytes of the 16 bf16 entries) in 8
-// VGPRs; v_perm_b32 looks up 4 codes at once in an 8-entry half, and a bitfield
-// select picks the half.  Every dequantized value is exactly the bf16 that
-// qlora_dequantize produces ("bitsandbytes deep dive" 5.2: w_hat = a * c_q).
+// VGPRs; v_perm_b32 looks up 4 codes at once in each 8-entry half, and an AND
+// keeps the half that holds the code.  Every dequantized value is exactly the
+// bf16 that qlora_dequantize produces ("bitsandbytes deep dive" 5.2:
+// w_hat = a * c_q).
 #pragma once
 
 #include "common.h"
@@ -48,43 +49,44 @@ __device__ __forceinline__ Nf4Tab make_tab(float ahat) {
     return T;
 }
 
-// s holds 4 codes (0..15), one per byte; returns the low and high bytes of
-// their table entries, byte i for code i.
-__device__ __forceinline__ void lut4(const Nf4Tab& T, uint32_t s, uint32_t& lo, uint32_t& hi) {
-    const uint32_t sel = s & 0x07070707u;
-    // 0xFF in the bytes whose code is >= 8 (v_perm selector 12 -> 0x00, 13 -> 0xFF)
-    const uint32_t m = perm_b32(0u, 0u, ((s >> 3) & 0x01010101u) | 0x0C0C0C0Cu);
-    const uint32_t l0 = perm_b32(T.lo[1], T.lo[0], sel);
-    const uint32_t l1 = perm_b32(T.lo[3], T.lo[2], sel);
-    const uint32_t h0 = perm_b32(T.hi[1], T.hi[0], sel);
-    const uint32_t h1 = perm_b32(T.hi[3], T.hi[2], sel);
-    lo = (m & l1) | (~m & l0);
-    hi = (m & h1) | (~m & h0);
+// s1 holds 4 codes, one per byte, as lookup selectors: code c < 8 as c and
+// code c >= 8 as 16 + (c - 8).  Returns the low and high bytes of their table
+// entries, byte i for code i.  v_perm_b32 yields 0xFF for a selector byte >= 13,
+// so looking up s1 in entries 0..7 and s1 ^ 0x10 in entries 8..15 leaves the hit
+// in one half and 0xFF in the other, and AND merges them.
+__device__ __forceinline__ void lut4(const Nf4Tab& T, uint32_t s1, uint32_t& lo, uint32_t& hi) {
+    const uint32_t s2 = s1 ^ 0x10101010u;
+    lo = perm_b32(T.lo[1], T.lo[0], s1) & perm_b32(T.lo[3], T.lo[2], s2);
+    hi = perm_b32(T.hi[1], T.hi[0], s1) & perm_b32(T.hi[3], T.hi[2], s2);
 }
 
 // One dword of packed codes (8 consecutive weights, weight 2i in the high
 // nibble of byte i) -> the 8 bf16 weights as 4 dwords (weight 2j in the low
 // half of dword j), i.e. an MFMA bf16x8 operand in k order.
 __device__ __forceinline__ u32x4_t deq8(const Nf4Tab& T, uint32_t d) {
-    uint32_t le, he, lo, ho;
-    lut4(T, (d >> 4) & 0x0F0F0F0Fu, le, he);  // weights 0, 2, 4, 6
-    lut4(T, d & 0x0F0F0F0Fu, lo, ho);         // weights 1, 3, 5, 7
-    const uint32_t p0 = perm_b32(he, le, 0x05010400u);  // [w0 | w2]
-    const uint32_t p1 = perm_b32(he, le, 0x07030602u);  // [w4 | w6]
-    const uint32_t q0 = perm_b32(ho, lo, 0x05010400u);  // [w1 | w3]
-    const uint32_t q1 = perm_b32(ho, lo, 0x07030602u);  // [w5 | w7]
-    return u32x4_t{perm_b32(q0, p0, 0x05040100u), perm_b32(q0, p0, 0x07060302u),
-                   perm_b32(q1, p1, 0x05040100u), perm_b32(q1, p1, 0x07060302u)};
+    // selectors of the odd (low nibble) and even (high nibble) weights
+    const uint32_t so = (d & 0x07070707u) | ((d << 1) & 0x10101010u);
+    const uint32_t se = ((d >> 4) & 0x07070707u) | ((d >> 3) & 0x10101010u);
+    uint32_t la, ha, lb, hb;
+    lut4(T, perm_b32(so, se, 0x05010400u), la, ha);  // weights 0..3
+    lut4(T, perm_b32(so, se, 0x07030602u), lb, hb);  // weights 4..7
+    return u32x4_t{perm_b32(ha, la, 0x05010400u), perm_b32(ha, la, 0x07030602u),
+                   perm_b32(hb, lb, 0x05010400u), perm_b32(hb, lb, 0x07030602u)};
 }
 
-// Same lookup, but returns the weights as [w0|w2], [w4|w6], [w1|w3], [w5|w7]
-// (for kernels that scatter single bf16 values).
-__device__ __forceinline__ u32x4_t deq8_evens_odds(const Nf4Tab& T, uint32_t d) {
-    uint32_t le, he, lo, ho;
-    lut4(T, (d >> 4) & 0x0F0F0F0Fu, le, he);
-    lut4(T, d & 0x0F0F0F0Fu, lo, ho);
-    return u32x4_t{perm_b32(he, le, 0x05010400u), perm_b32(he, le, 0x07030602u),
-                   perm_b32(ho, lo, 0x05010400u), perm_b32(ho, lo, 0x07030602u)};
+// The fused forward's lane halves dequantize the same two columns: lanes 0-31
+// build the table of the first and lanes 32-63 that of the second, and
+// v_permlane32_swap hands each half the other's, so every lane ends with both.
+__device__ __forceinline__ void share_tabs(const Nf4Tab& mine, Nf4Tab& t0, Nf4Tab& t1) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const auto l = __builtin_amdgcn_permlane32_swap(mine.lo[q], mine.lo[q], false, false);
+        const auto h = __builtin_amdgcn_permlane32_swap(mine.hi[q], mine.hi[q], false, false);
+        t0.lo[q] = l[0];
+        t1.lo[q] = l[1];
+        t0.hi[q] = h[0];
+        t1.hi[q] = h[1];
+    }
 }
 
 // Byte offset of 16-byte chunk `chunk` (0..7) of row `row` in an LDS tile of

@@ -369,10 +369,10 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
     Nf4Tab T[2];
     u32x4_t cc[2];
     bf16x8 b[2][2];
+    share_tabs(make_tab(ahs0[kSuper4 * crl[h]]), T[0], T[1]);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         cc[u] = read_codes(cds0, 0, u);
-        T[u] = make_tab(ahs0[kSuper4 * crl[u]]);
         b[0][u] = as_bf16x8(deq8(T[u], cc[u][0]));
     }
 
@@ -403,10 +403,8 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
         u32x4_t cn[2];
         Nf4Tab Tn[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            cn[u] = read_codes(cdN, jn, u);
-            Tn[u] = make_tab(ahN[kSuper4 * crl[u] + jn]);
-        }
+        for (int u = 0; u < 2; ++u) cn[u] = read_codes(cdN, jn, u);
+        share_tabs(make_tab(ahN[kSuper4 * crl[h] + jn]), Tn[0], Tn[1]);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int p = c & 1;
