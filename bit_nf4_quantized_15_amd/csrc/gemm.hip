@@ -386,44 +386,66 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
         const int ks = kSuper4 * S + j;
         const uint8_t* A = lds + (ks & 1) * kTileBytes;
         uint8_t* An = lds + ((ks + 1) & 1) * kTileBytes;
-        bf16x8 a[2][8];
+        // A operands by half chunk: row tiles 4 half .. 4 half + 3 of chunk c
+        bf16x8 a[2][4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a[0][i] = *reinterpret_cast<const bf16x8*>(A + offA[0] + 4096u * i);
+        for (int i = 0; i < 4; ++i) a[0][i] = *reinterpret_cast<const bf16x8*>(A + offA[0] + 4096u * i);
         load_tile_direct(xrs, An, xvoff, wv, min(ks + 1, KB - 1) * kTK, K);
-        const bool pre = j == 0 && S + 1 < NS;
-        if (pre) {
+        // the next super-step's codes and scales (the last super-step reloads its
+        // own into the idle buffers, which nothing reads afterwards)
+        const int Sp = min(S + 1, NS - 1);
+        if (j == 0) {
             __builtin_amdgcn_sched_barrier(kAllButVmem);  // keep the x tile's loads first
-            load_codes(cdO, S + 1);
-            load_scales(S + 1, sc);
+            load_codes(cdO, Sp);
+            load_scales(Sp, sc);
         }
         // step ks+1's codes and tables
         const uint8_t* cdN = j < kSuper4 - 1 ? cdC : cdO;
         const float* ahN = j < kSuper4 - 1 ? ahC : ahO;
         const int jn = (j + 1) & (kSuper4 - 1);
         u32x4_t cn[2];
-        Nf4Tab Tn[2];
+        Nf4Tab Tn[2], mine;
+        uint32_t e[8];
 #pragma unroll
         for (int u = 0; u < 2; ++u) cn[u] = read_codes(cdN, jn, u);
-        share_tabs(make_tab(ahN[kSuper4 * crl[h] + jn]), Tn[0], Tn[1]);
+        const float ahn = ahN[kSuper4 * crl[h] + jn];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int p = c & 1;
-            if (c < 3) {
+        for (int hc = 0; hc < 8; ++hc) {
+            const int c = hc >> 1, half = hc & 1, p = c & 1;
+            if (hc < 7) {
+                const int c1 = (hc + 1) >> 1, h1 = (hc + 1) & 1;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) a[p ^ 1][i] = *reinterpret_cast<const bf16x8*>(A + offA[c + 1] + 4096u * i);
+                for (int i = 0; i < 4; ++i)
+                    a[half ^ 1][i] = *reinterpret_cast<const bf16x8*>(A + offA[c1] + 4096u * (4 * h1 + i));
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                acc[i][0] = mfma32(a[p][i], b[p][0], acc[i][0]);
-                acc[i][1] = mfma32(a[p][i], b[p][1], acc[i][1]);
+                acc[4 * half + i][0] = mfma32(a[half][i], b[p][0], acc[4 * half + i][0]);
+                acc[4 * half + i][1] = mfma32(a[half][i], b[p][1], acc[4 * half + i][1]);
             }
-            b[p ^ 1][0] = as_bf16x8(c < 3 ? deq8(T[0], cc[0][c + 1]) : deq8(Tn[0], cn[0][0]));
+            if (half == 0) b[p ^ 1][0] = as_bf16x8(c < 3 ? deq8(T[0], cc[0][c + 1]) : deq8(Tn[0], cn[0][0]));
+            else b[p ^ 1][1] = as_bf16x8(c < 3 ? deq8(T[1], cc[1][c + 1]) : deq8(Tn[1], cn[1][0]));
+            // step ks+1's tables, spread over half chunks 2..4 (first used in 6)
+            if (hc == 2 || hc == 3) {
 #pragma unroll
-            for (int i = 4; i < 8; ++i) {
-                acc[i][0] = mfma32(a[p][i], b[p][0], acc[i][0]);
-                acc[i][1] = mfma32(a[p][i], b[p][1], acc[i][1]);
+                for (int q = 4 * (hc - 2); q < 4 * (hc - 2) + 4; ++q)
+                    e[q] = pack_bf16x2(ahn * nf4_level(2 * q), ahn * nf4_level(2 * q + 1));
+#pragma unroll
+                for (int q = 2 * (hc - 2); q < 2 * (hc - 2) + 2; ++q) {
+                    mine.lo[q] = perm_b32(e[2 * q + 1], e[2 * q], 0x06040200u);
+                    mine.hi[q] = perm_b32(e[2 * q + 1], e[2 * q], 0x07050301u);
+                }
             }
-            b[p ^ 1][1] = as_bf16x8(c < 3 ? deq8(T[1], cc[1][c + 1]) : deq8(Tn[1], cn[1][0]));
+            if (hc == 4) share_tabs(mine, Tn[0], Tn[1]);
+            // 4 operand reads ahead, then each MFMA followed by up to 6 VALU;
+            // nothing crosses into the next half chunk
+            if (hc < 7) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int m_ = 0; m_ < 8; ++m_) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
         // chunk 3 used b[1]; the expansion of step ks+1's chunk 0 is in b[0]
 #pragma unroll
@@ -431,15 +453,15 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
             T[u] = Tn[u];
             cc[u] = cn[u];
         }
-        if (j == 2 && S + 1 < NS) make_scales(sc, ahO, S + 1);
-        if (pre) wait_direct_loads_behind<Q8DW ? 11 : 14>();  // only this step's x tile must have landed
+        if (j == 2) make_scales(sc, ahO, Sp);
+        if (j == 0) wait_direct_loads_behind<Q8DW ? 11 : 14>();  // only this step's x tile must have landed
         else wait_direct_loads();
         __syncthreads();
     };
     auto do_super = [&](int S, uint8_t* cdC, float* ahC, uint8_t* cdO, float* ahO) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < kSuper4; ++j)
-            if (kSuper4 * S + j < KB) do_step(S, j, cdC, ahC, cdO, ahO);
+            if (Q8DW || kSuper4 * S + j < KB) do_step(S, j, cdC, ahC, cdO, ahO);
     };
     for (int S = 0; S < NS; S += 2) {
         do_super(S, cds0, ahs0, cds1, ahs1);
