@@ -229,15 +229,37 @@ __global__ __launch_bounds__(256) void nt_partial_kernel(const uint16_t* __restr
     }
 }
 
-// out[m, j] = bf16( s * sum_split part[split, m, j] )
-__global__ void finalize_bf16_kernel(const float* __restrict__ part, int splits, int M, int r, float s,
-                                     uint16_t* __restrict__ out) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t count = (int64_t)M * r;
-    if (i >= count) return;
+// Sum over splits of part[split * count + i] for the 64 outputs i of this
+// workgroup: thread (o, g) adds splits g, g + 4, ... with 4 independent loads
+// in flight, and the 4 groups' sums meet in LDS.  (A decode-size down-
+// projection has up to 64 splits of a handful of outputs: a serial loop per
+// output would wait for one load at a time.)
+__device__ __forceinline__ float sum_splits(const float* __restrict__ part, int splits, int64_t count, int64_t i,
+                                            bool ok) {
+    __shared__ float red[4][64];
+    const int o = threadIdx.x & 63, g = threadIdx.x >> 6;
     float acc = 0.0f;
-    for (int p = 0; p < splits; ++p) acc += part[(int64_t)p * count + i];
-    out[i] = (uint16_t)(pack_bf16x2(s * acc, 0.0f) & 0xFFFFu);
+    if (ok) {
+        int p = g;
+        for (; p + 12 < splits; p += 16) {
+            const float v0 = part[(int64_t)p * count + i], v1 = part[(int64_t)(p + 4) * count + i];
+            const float v2 = part[(int64_t)(p + 8) * count + i], v3 = part[(int64_t)(p + 12) * count + i];
+            acc += (v0 + v1) + (v2 + v3);
+        }
+        for (; p < splits; p += 4) acc += part[(int64_t)p * count + i];
+    }
+    red[g][o] = acc;
+    __syncthreads();
+    return (red[0][o] + red[1][o]) + (red[2][o] + red[3][o]);
+}
+
+// out[m, j] = bf16( s * sum_split part[split, m, j] ); 256 threads per 64 outputs
+__global__ __launch_bounds__(256) void finalize_bf16_kernel(const float* __restrict__ part, int splits, int M, int r,
+                                                            float s, uint16_t* __restrict__ out) {
+    const int64_t count = (int64_t)M * r;
+    const int64_t i = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
+    const float v = sum_splits(part, splits, count, i, i < count);
+    if (threadIdx.x < 64 && i < count) out[i] = (uint16_t)(pack_bf16x2(s * v, 0.0f) & 0xFFFFu);
 }
 
 // part[split, d, j] = sum over m in the split's range of X[m, d] * S[m, j]
@@ -333,16 +355,16 @@ __global__ __launch_bounds__(256) void tn_partial_kernel(const uint16_t* __restr
     }
 }
 
-// out[d * ld_d + j * ld_j] = sum_split part[split, d, j]   (fp32)
-__global__ void reduce_f32_kernel(const float* __restrict__ part, int splits, int D, int r, int64_t ld_d,
-                                  int64_t ld_j, float* __restrict__ out) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// out[d * ld_d + j * ld_j] = sum_split part[split, d, j]   (fp32); 256 threads per 64 outputs
+__global__ __launch_bounds__(256) void reduce_f32_kernel(const float* __restrict__ part, int splits, int D, int r,
+                                                         int64_t ld_d, int64_t ld_j, float* __restrict__ out) {
     const int64_t count = (int64_t)D * r;
-    if (i >= count) return;
-    float acc = 0.0f;
-    for (int p = 0; p < splits; ++p) acc += part[(int64_t)p * count + i];
-    const int64_t d = i / r, j = i - d * r;
-    out[d * ld_d + j * ld_j] = acc;
+    const int64_t i = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
+    const float v = sum_splits(part, splits, count, i, i < count);
+    if (threadIdx.x < 64 && i < count) {
+        const int64_t d = i / r, j = i - d * r;
+        out[d * ld_d + j * ld_j] = v;
+    }
 }
 
 __global__ void fill_f32_kernel(float* __restrict__ out, int64_t count, float v) {
@@ -384,7 +406,7 @@ qlora_status launch_nt(const uint16_t* X, const uint16_t* Y, bool y_natural, flo
 #undef QL_NT2
 #undef QL_NT
     const int64_t count = (int64_t)M * r;
-    hipLaunchKernelGGL(finalize_bf16_kernel, dim3(blocks_for(count, 256)), dim3(256), 0, s, part, sp.splits, M, r,
+    hipLaunchKernelGGL(finalize_bf16_kernel, dim3(blocks_for(count, 64)), dim3(256), 0, s, part, sp.splits, M, r,
                        scale, out);
     return launch_status();
 }
@@ -408,7 +430,7 @@ qlora_status launch_tn(const uint16_t* X, const uint16_t* S, float* part, float*
     }
 #undef QL_TN
     const int64_t count = (int64_t)D * r;
-    hipLaunchKernelGGL(reduce_f32_kernel, dim3(blocks_for(count, 256)), dim3(256), 0, s, part, sp.splits, D, r, ld_d,
+    hipLaunchKernelGGL(reduce_f32_kernel, dim3(blocks_for(count, 64)), dim3(256), 0, s, part, sp.splits, D, r, ld_d,
                        ld_j, out);
     return launch_status();
 }
