@@ -175,6 +175,13 @@ __device__ __forceinline__ void wait_direct_loads_behind() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Workgroup barrier that lets the last N LDS reads of the wave stay in flight
+// (every earlier LDS access, reads and writes, has completed when it passes).
+template <int N>
+__device__ __forceinline__ void barrier_reads_in_flight() {
+    asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 __device__ __forceinline__ void store_tile(uint8_t* lds, const u32x4_t (&r)[8], int tid) {
     const int lr = tid >> 3, lc = tid & 7;
 #pragma unroll
@@ -248,20 +255,30 @@ __device__ __forceinline__ void store_acc(uint16_t* __restrict__ out, int64_t ld
 // 31 of the block and the block's a_hat, builds each column's 16-entry bf16
 // table and expands 8 codes at a time into the MFMA B operand just before use,
 // interleaved with the MFMAs of the previous chunk.
-constexpr int kSuper4 = 4;                                 // blocks per super-step
-constexpr int kCodeTileBytes = kTN * kSuper4 * kBlock / 2;  // 256 rows x 128 B
+constexpr int kSup = 2;                                     // blocks per super-step
+constexpr int kCodeTileBytes = kTN * kSup * kBlock / 2;     // 256 rows x 64 B
 
 template <bool Q8DW>
 __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ q8,
     const float* __restrict__ a2, const uint16_t* __restrict__ t, const uint16_t* __restrict__ Bl,
     uint16_t* __restrict__ y, int M, int N, int K, int r, int tiles_m, int tiles_n) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kTileBytes];
-    // separate objects, so that reads of one buffer never wait for loads into the other
+    // Separate objects, so that the compiler's tracking of direct loads never
+    // makes a read of one buffer wait for the loads into another.  x tiles:
+    // a 3-deep ring (tile ks in xt[ks % 3]); code tiles and scale tables: one
+    // per super-step, 3 deep (super-step S in cds[S % 3], ahs[S % 3]).
+    __shared__ __attribute__((aligned(16))) uint8_t xt0[kTileBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t xt1[kTileBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t xt2[kTileBytes];
     __shared__ __attribute__((aligned(16))) uint8_t cds0[kCodeTileBytes];
     __shared__ __attribute__((aligned(16))) uint8_t cds1[kCodeTileBytes];
-    __shared__ __attribute__((aligned(16))) float ahs0[kTN * kSuper4];
-    __shared__ __attribute__((aligned(16))) float ahs1[kTN * kSuper4];
+    __shared__ __attribute__((aligned(16))) uint8_t cds2[kCodeTileBytes];
+    __shared__ __attribute__((aligned(16))) float ahs0[kTN * kSup];
+    __shared__ __attribute__((aligned(16))) float ahs1[kTN * kSup];
+    __shared__ __attribute__((aligned(16))) float ahs2[kTN * kSup];
+    uint8_t* const xts[3] = {xt0, xt1, xt2};
+    uint8_t* const cdss[3] = {cds0, cds1, cds2};
+    float* const ahss[3] = {ahs0, ahs1, ahs2};
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, l32 = lane & 31;
@@ -269,7 +286,7 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
     const int mt = tile / tiles_n, nt = tile - mt * tiles_n;
     const int m0 = mt * kTM, n0 = nt * kTN;
     const int KB = K / kTK;
-    const int NS = (KB + kSuper4 - 1) / kSuper4;
+    const int NS = (KB + kSup - 1) / kSup;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
 
     int col[2], crl[2];  // global column; row of the code tile (column within the tile)
@@ -291,65 +308,58 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][u][v] = 0.0f;
 
-    // ---- code tiles.  Instruction i of wave w fills code-tile rows 8 (8w + i) .. +7:
-    // lane l takes row 8 (8w + i) + l / 8 and LDS chunk l % 8, which holds that
-    // row's 16-byte chunk (l % 8) ^ (row % 8) (block 2 chunks, half of 32 B).
-    // Rows past N repeat row N - 1 (never stored); the whole offset is in voffset,
-    // so blocks past the end of the last row read as zero.
+    // ---- code tiles: 256 rows x 64 B (2 blocks).  Instruction i of wave w fills
+    // rows 16 (4w + i) .. +15: lane l takes row 16 (4w + i) + l / 4 and LDS chunk
+    // l % 4, which holds that row's 16-byte chunk (l % 4) ^ ((row / 2) % 4)
+    // (block chunk / 2, half chunk % 2).  Rows past N repeat row N - 1 (never
+    // stored); the whole offset is in voffset, so blocks past the end of the
+    // last row read as zero.
     const uint32_t half_k = (uint32_t)K >> 1;
     const i32x4_t crs = buffer_rsrc(codes, (uint32_t)((uint64_t)N * half_k));
-    uint32_t cvoff[8];
+    uint32_t cvoff[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = 8 * (8 * wv + i) + (lane >> 3);
-        const int q = (lane & 7) ^ (row & 7);
+    for (int i = 0; i < 4; ++i) {
+        const int row = 16 * (4 * wv + i) + (lane >> 2);
+        const int q = (lane & 3) ^ ((row >> 1) & 3);
         cvoff[i] = (uint32_t)min(n0 + row, N - 1) * half_k + 32u * (uint32_t)(q >> 1) + 16u * (uint32_t)(q & 1);
     }
     auto load_codes = [&](uint8_t* dst, int S) __attribute__((always_inline)) {
-        const uint32_t boff = 32u * (uint32_t)(kSuper4 * S);
+        const uint32_t boff = 32u * (uint32_t)(kSup * S);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
             auto* d = reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(
-                reinterpret_cast<uintptr_t>(dst + 1024 * (8 * wv + i)));
+                reinterpret_cast<uintptr_t>(dst + 1024 * (4 * wv + i)));
             raw_buffer_load_lds(crs, d, 16, (int)(cvoff[i] + boff), 0, 0, 0);
         }
     };
-    // ---- block scales: thread tid, tile row tid, the 4 blocks of a super-step
+    // ---- block scales: thread tid, tile row tid, the 2 blocks of a super-step
+    // (an even first block, so both lie in one group of 256 blocks)
     const int srow = min(n0 + tid, N - 1);
     const int64_t sblk = (int64_t)srow * KB;
     struct Sc {
-        uint32_t q;   // 8-bit scale codes of the 4 blocks, block j in byte j
-        float g0, g1; // second-level scales of the first and last block's groups
+        uint32_t q;  // 8-bit scale codes of the 2 blocks, block j in byte j
+        float g;     // second-level scale of their group
     };
     auto load_scales = [&](int S, Sc& sc) __attribute__((always_inline)) {
-        const int b0 = kSuper4 * S;
-        if (Q8DW) {  // blocks per row % 4 == 0: the 4 codes are one aligned dword
-            sc.q = *reinterpret_cast<const uint32_t*>(q8 + sblk + b0);
+        const int b0 = kSup * S;
+        if (Q8DW) {  // blocks per row even: the 2 codes are one aligned 16-bit word
+            sc.q = *reinterpret_cast<const uint16_t*>(q8 + sblk + b0);
         } else {
-            uint32_t qv = 0;
-#pragma unroll
-            for (int j = 0; j < kSuper4; ++j) qv |= (uint32_t)q8[sblk + min(b0 + j, KB - 1)] << (8 * j);
-            sc.q = qv;
+            sc.q = (uint32_t)q8[sblk + b0] | ((uint32_t)q8[sblk + min(b0 + 1, KB - 1)] << 8);
         }
-        sc.g0 = a2[(sblk + b0) >> 8];
-        sc.g1 = a2[(sblk + min(b0 + kSuper4 - 1, KB - 1)) >> 8];
+        sc.g = a2[(sblk + b0) >> 8];
     };
     auto make_scales = [&](const Sc& sc, float* dst, int S) __attribute__((always_inline)) {
-        const int b0 = kSuper4 * S;
-        const float s0 = scale_step(sc.g0), s1 = scale_step(sc.g1);
-        const int64_t g0 = (sblk + b0) >> 8;
-        f32x4_t ah;
-#pragma unroll
-        for (int j = 0; j < kSuper4; ++j) {
-            const int b = b0 + j;
-            const float st = ((sblk + b) >> 8) == g0 ? s0 : s1;
-            ah[j] = b < KB ? st * (float)((sc.q >> (8 * j)) & 0xFFu) : 0.0f;
-        }
-        *reinterpret_cast<f32x4_t*>(dst + kSuper4 * tid) = ah;
+        const int b0 = kSup * S;
+        const float st = scale_step(sc.g);
+        f32x2_t ah;
+        ah[0] = st * (float)(sc.q & 0xFFu);
+        ah[1] = b0 + 1 < KB ? st * (float)((sc.q >> 8) & 0xFFu) : 0.0f;
+        *reinterpret_cast<f32x2_t*>(dst + kSup * tid) = ah;
     };
-    // this lane's 16 code bytes and a_hat of column u at block j of a super-step
+    // this lane's 16 code bytes of column u at block j of a super-step
     auto read_codes = [&](const uint8_t* cd, int j, int u) __attribute__((always_inline)) {
-        return *reinterpret_cast<const u32x4_t*>(cd + crl[u] * 128 + 16 * ((2 * j + h) ^ (crl[u] & 7)));
+        return *reinterpret_cast<const u32x4_t*>(cd + crl[u] * 64 + 16 * ((2 * j + h) ^ ((crl[u] >> 1) & 3)));
     };
 
     // x panel rows [m0, M) as a buffer; lane's tile row 8*wave + lane/8, chunk
@@ -358,57 +368,67 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
     const int xchunk = (lane & 7) ^ (((xrow ^ (xrow >> 3)) & 3) ^ (xrow & 4));
     const uint32_t xvoff = (uint32_t)(((int64_t)xrow * K + 8 * xchunk) * 2);
 
-    // prologue: x tile 0, super-step 0's codes and scales
-    load_tile_direct(xrs, lds, xvoff, wv, 0, K);
+    // prologue: x tiles 0 and 1, super-steps 0 and 1's codes and scales, the
+    // scales of super-step 2 in registers
+    load_tile_direct(xrs, xt0, xvoff, wv, 0, K);
+    load_tile_direct(xrs, xt1, xvoff, wv, min(1, KB - 1) * kTK, K);
     load_codes(cds0, 0);
+    load_codes(cds1, min(1, NS - 1));
     Sc sc;
     load_scales(0, sc);
     make_scales(sc, ahs0, 0);
+    load_scales(min(1, NS - 1), sc);
+    make_scales(sc, ahs1, min(1, NS - 1));
+    load_scales(min(2, NS - 1), sc);
     wait_direct_loads();
     __syncthreads();
     Nf4Tab T[2];
     u32x4_t cc[2];
     bf16x8 b[2][2];
-    share_tabs(make_tab(ahs0[kSuper4 * crl[h]]), T[0], T[1]);
+    bf16x8 a[2][4];  // A operands by half chunk: row tiles 4 half .. 4 half + 3 of chunk c
+    share_tabs(make_tab(ahs0[kSup * crl[h]]), T[0], T[1]);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         cc[u] = read_codes(cds0, 0, u);
         b[0][u] = as_bf16x8(deq8(T[u], cc[u][0]));
     }
-
-    // One step ks = 4 S + j.  Operand reads of chunk c+1 and the expansion of
-    // chunk c+1's codes overlap the MFMAs of chunk c; the tables of step ks+1 are
-    // built while chunk 0's reads are in flight and its chunk-0 operands are
-    // expanded during chunk 3.  At j = 0 the next super-step's codes and scales
-    // are requested, at j = 2 its scales are written, and at j = 3 step ks+1's
-    // operands come from the other buffers.
-    auto do_step = [&](int S, int j, uint8_t* cdC, float* ahC, uint8_t* cdO, float* ahO) __attribute__((always_inline)) {
-        const int ks = kSuper4 * S + j;
-        const uint8_t* A = lds + (ks & 1) * kTileBytes;
-        uint8_t* An = lds + ((ks + 1) & 1) * kTileBytes;
-        // A operands by half chunk: row tiles 4 half .. 4 half + 3 of chunk c
-        bf16x8 a[2][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[0][i] = *reinterpret_cast<const bf16x8*>(A + offA[0] + 4096u * i);
-        load_tile_direct(xrs, An, xvoff, wv, min(ks + 1, KB - 1) * kTK, K);
-        // the next super-step's codes and scales (the last super-step reloads its
-        // own into the idle buffers, which nothing reads afterwards)
-        const int Sp = min(S + 1, NS - 1);
+    for (int i = 0; i < 4; ++i) a[0][i] = *reinterpret_cast<const bf16x8*>(xt0 + offA[0] + 4096u * i);
+
+    // One step ks = 2 S + j on x tile ks (xt[ks % 3]), in 8 half chunks: each
+    // issues the next half chunk's 4 operand reads (the last one: the next
+    // step's first, from tile ks + 1, which the previous barrier published),
+    // then 8 MFMAs with the expansion of the next chunk's codes interleaved.
+    // At its start the step requests x tile ks + 2 (into the buffer of tile
+    // ks - 1, which every wave finished a barrier ago) and, at j = 0, super-step
+    // S + 2's codes and the scales of S + 3; at its end tile ks + 2 must have
+    // landed, and the barrier publishes it while the next step's first operand
+    // reads are in flight.  At j = 0 the table of super-step S + 2 is written
+    // from the scales loaded a super-step earlier.
+    auto do_step = [&](int S, int j, int s) __attribute__((always_inline)) {
+        const int ks = kSup * S + j;
+        const int xr = (2 * s + j) % 3;  // ks % 3, as S = s (mod 3)
+        const uint8_t* A = xts[xr];
+        const uint8_t* A1 = xts[(xr + 1) % 3];
+        uint8_t* A2 = xts[(xr + 2) % 3];
+        load_tile_direct(xrs, A2, xvoff, wv, min(ks + 2, KB - 1) * kTK, K);
         if (j == 0) {
-            __builtin_amdgcn_sched_barrier(kAllButVmem);  // keep the x tile's loads first
-            load_codes(cdO, Sp);
-            load_scales(Sp, sc);
+            __builtin_amdgcn_sched_barrier(kAllButVmem);  // the x tile's loads first
+            load_codes(cdss[(s + 2) % 3], min(S + 2, NS - 1));
+            make_scales(sc, ahss[(s + 2) % 3], min(S + 2, NS - 1));
+            load_scales(min(S + 3, NS - 1), sc);
         }
+        __builtin_amdgcn_sched_barrier(kAllButVmem);  // keep this step's loads in this order
         // step ks+1's codes and tables
-        const uint8_t* cdN = j < kSuper4 - 1 ? cdC : cdO;
-        const float* ahN = j < kSuper4 - 1 ? ahC : ahO;
-        const int jn = (j + 1) & (kSuper4 - 1);
+        const uint8_t* cdN = j == 0 ? cdss[s] : cdss[(s + 1) % 3];
+        const float* ahN = j == 0 ? ahss[s] : ahss[(s + 1) % 3];
+        const int jn = j ^ 1;
         u32x4_t cn[2];
         Nf4Tab Tn[2], mine;
         uint32_t e[8];
 #pragma unroll
         for (int u = 0; u < 2; ++u) cn[u] = read_codes(cdN, jn, u);
-        const float ahn = ahN[kSuper4 * crl[h] + jn];
+        const float ahn = ahN[kSup * crl[h] + jn];
 #pragma unroll
         for (int hc = 0; hc < 8; ++hc) {
             const int c = hc >> 1, half = hc & 1, p = c & 1;
@@ -417,6 +437,9 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     a[half ^ 1][i] = *reinterpret_cast<const bf16x8*>(A + offA[c1] + 4096u * (4 * h1 + i));
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a[0][i] = *reinterpret_cast<const bf16x8*>(A1 + offA[0] + 4096u * i);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -439,7 +462,7 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
             if (hc == 4) share_tabs(mine, Tn[0], Tn[1]);
             // 4 operand reads ahead, then each MFMA followed by up to 6 VALU;
             // nothing crosses into the next half chunk
-            if (hc < 7) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
             for (int m_ = 0; m_ < 8; ++m_) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -453,27 +476,30 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
             T[u] = Tn[u];
             cc[u] = cn[u];
         }
-        if (j == 2) make_scales(sc, ahO, Sp);
-        if (j == 0) wait_direct_loads_behind<Q8DW ? 11 : 14>();  // only this step's x tile must have landed
+        // tile ks+2 must have landed (the codes and scales requested after it may
+        // stay in flight); the 4 operand reads of the next step stay in flight
+        // across the barrier, every earlier LDS access has completed.
+        if (j == 0) wait_direct_loads_behind<4 + (Q8DW ? 2 : 3)>();
         else wait_direct_loads();
-        __syncthreads();
+        barrier_reads_in_flight<4>();
     };
-    auto do_super = [&](int S, uint8_t* cdC, float* ahC, uint8_t* cdO, float* ahO) __attribute__((always_inline)) {
+    auto do_super = [&](int S, int s) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < kSuper4; ++j)
-            if (Q8DW || kSuper4 * S + j < KB) do_step(S, j, cdC, ahC, cdO, ahO);
+        for (int j = 0; j < kSup; ++j)
+            if (Q8DW || kSup * S + j < KB) do_step(S, j, s);
     };
-    for (int S = 0; S < NS; S += 2) {
-        do_super(S, cds0, ahs0, cds1, ahs1);
-        if (S + 1 < NS) do_super(S + 1, cds1, ahs1, cds0, ahs0);
+    for (int S = 0; S < NS; S += 3) {
+        do_super(S, 0);
+        if (S + 1 < NS) do_super(S + 1, 1);
+        if (S + 2 < NS) do_super(S + 2, 2);
     }
 
     u32x4_t xr[8];
     // LoRA up-projection: r more reduction steps with A-operand t [M, r] and
-    // B-operand B [r, N] (t already carries the alpha/r scale).  B's rows
-    // [j0, j0 + 64) x the tile's 256 columns are staged in LDS in natural
-    // layout (rows 0-31 in cds0, 32-63 in cds1, 544-byte rows) and read down
-    // their columns with ds_read_b64_tr_b16.
+    // B-operand B [r, N] (t already carries the alpha/r scale).  The t tile goes
+    // to xt0; B's rows [j0, j0 + 64) x the tile's 256 columns are staged in LDS
+    // in natural layout (rows 0-31 in xt1, 32-63 in xt2, 544-byte rows) and read
+    // down their columns with ds_read_b64_tr_b16.
     const bool col_ok0 = col[0] < N, col_ok1 = col[1] < N;
     const bool tvec = (r % 8) == 0;   // t rows are whole 16-byte chunks
     const bool nvec = (N % 8) == 0;   // rows of B and y are whole 16-byte chunks
@@ -504,12 +530,12 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int idx = tid + kT * e, row = idx >> 5;
-                *reinterpret_cast<u32x4_t*>((row < 32 ? cds0 : cds1) + (row & 31) * kBLd + 16 * (idx & 31)) = bv[e];
+                *reinterpret_cast<u32x4_t*>((row < 32 ? xt1 : xt2) + (row & 31) * kBLd + 16 * (idx & 31)) = bv[e];
             }
         }
-        store_ftile(lds, xr, tid);
+        store_ftile(xt0, xr, tid);
         __syncthreads();
-        const uint8_t* bhalf = h ? cds1 : cds0;   // B rows 32h .. 32h + 31 of this step
+        const uint8_t* bhalf = h ? xt2 : xt1;   // B rows 32h .. 32h + 31 of this step
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             bf16x8 bl[2];
@@ -524,7 +550,7 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const bf16x8 av = *reinterpret_cast<const bf16x8*>(lds + offA[c] + 4096u * i);
+                const bf16x8 av = *reinterpret_cast<const bf16x8*>(xt0 + offA[c] + 4096u * i);
                 acc[i][0] = mfma32(av, bl[0], acc[i][0]);
                 acc[i][1] = mfma32(av, bl[1], acc[i][1]);
             }
@@ -533,7 +559,8 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
     }
 
     // y tile as bf16 through LDS, 128 rows at a time: lanes write their values
-    // into a [128][256] staging area, then each thread stores 16-byte row chunks
+    // into a [128][256] staging area (rows 0-63 in xt0, 64-127 in xt1), then
+    // each thread stores 16-byte row chunks
     if (!nvec) {
         const bool col_ok[2] = {col_ok0, col_ok1};
         store_acc(y, N, acc, m0, M, col, col_ok, h);
@@ -549,7 +576,7 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int row = 32 * ii + 8 * (v >> 2) + 4 * h + (v & 3);
-                    *reinterpret_cast<uint16_t*>(lds + row * 512 + 2 * crl[u]) =
+                    *reinterpret_cast<uint16_t*>((row < 64 ? xt0 : xt1) + (row & 63) * 512 + 2 * crl[u]) =
                         (uint16_t)(pack_bf16x2(acc[i][u][v], 0.0f) & 0xFFFFu);
                 }
         }
@@ -558,7 +585,7 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
         for (int e = 0; e < 16; ++e) {
             const int idx = tid + kT * e, row = idx >> 5, ch = idx & 31;
             const int m = m0 + 128 * half + row, n = n0 + 8 * ch;
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + row * 512 + 16 * ch);
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>((row < 64 ? xt0 : xt1) + (row & 63) * 512 + 16 * ch);
             if (m < M && n < N) *reinterpret_cast<u32x4_t*>(y + (int64_t)m * N + n) = v;
         }
         __syncthreads();
@@ -817,7 +844,7 @@ qlora_status launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const uint
     if ((int64_t)kTM * K * 2 >= (int64_t(1) << 32)) return QLORA_ERR_UNSUPPORTED_SHAPE;
     // code-tile offsets (including blocks past a row's end) must fit a 32-bit voffset
     if ((uint64_t)N * (uint64_t)K / 2 + 4096 >= (uint64_t(1) << 32)) return QLORA_ERR_UNSUPPORTED_SHAPE;
-    if ((K / kTK) % kSuper4 == 0)
+    if ((K / kTK) % kSup == 0)
         hipLaunchKernelGGL(nf4_gemm_fwd_kernel<true>, dim3(tm * tn), dim3(kT), 0, s, x, codes, q8, a2, t, B, y, M, N,
                            K, r, tm, tn);
     else
