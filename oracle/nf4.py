@@ -246,6 +246,61 @@ def quantize(W_u16, table=None):
     return pack_nibbles(codes), q8, A2
 
 
+# ----------------------------------------------------------------------------
+# Double quantization off: one fp32 absmax per block
+# ----------------------------------------------------------------------------
+def quantize_nodq(W_u16, table=None):
+    """Quantize a bf16 weight [N, K] without double quantization -> (packed codes, absmax).
+
+    "bitsandbytes deep dive" 7.1 and 9.5: with double quantization off every
+    block keeps its absmax as an fp32 constant (32 bits per 64 weights).  The
+    codes are the same nearest-level codes as with it on (both are taken
+    against the true block absmax).  Returns packed uint8 [N*K/2] and absmax
+    float32 [N*K/64] (exact: the absmax of bf16 values is a bf16 value).
+    """
+    wb16 = blocks(np.asarray(W_u16, dtype=np.uint16))
+    nb = wb16.shape[0]
+    a = np.empty(nb, dtype=np.float32)
+    codes = np.empty((nb, BLOCK), dtype=np.uint8)
+    step = 1 << 14
+    for s in range(0, nb, step):
+        wb = bf16.to_f64(wb16[s:s + step])
+        ab = block_absmax(wb)
+        a[s:s + step] = ab
+        codes[s:s + step] = nf4_codes(wb, ab, table)
+    return pack_nibbles(codes), a
+
+
+def dequantize_nodq(packed, absmax, N, K, table=None):
+    """w_hat = RNE_bf16( fl32(a_b * c_q) ) with the stored fp32 block absmax, shape [N, K].
+
+    Section 5.2 (w_hat = a * c_q) with a kept exactly (section 7.1: no second
+    quantization), rounded once to the bf16 compute dtype (section 8.3).
+    """
+    return dequant_blocks(packed, np.asarray(absmax, np.float32), table).reshape(N, K)
+
+
+def dequantize_rows_nodq(packed, absmax, K, rows, table=None):
+    """w_hat of the selected rows of an [N, K] weight quantized without double quantization."""
+    rows = np.asarray(rows, dtype=np.int64)
+    bpr = K // BLOCK
+    bidx = (rows[:, None] * bpr + np.arange(bpr)[None, :]).reshape(-1)
+    pk = np.asarray(packed).reshape(-1, BLOCK // 2)[bidx].reshape(-1)
+    return dequant_blocks(pk, np.asarray(absmax, np.float32)[bidx], table).reshape(rows.size, K)
+
+
+def storage_bytes_nodq(N, K):
+    """Bytes of (packed codes, fp32 block absmax) for an [N, K] weight."""
+    n = N * K
+    return n // 2, 4 * (n // BLOCK)
+
+
+def bits_per_param_nodq(N, K):
+    """Average stored bits per weight without double quantization: 4 + 32/64 = 4.5."""
+    cb, ab = storage_bytes_nodq(N, K)
+    return 8.0 * (cb + ab) / (N * K)
+
+
 def storage_bytes(N, K):
     """Bytes of (packed codes, q8, A2) for an [N, K] weight."""
     n = N * K

@@ -276,3 +276,68 @@ def test_storage_numbers_printed_on_pages():
     lp = g["lora_param_count"]
     assert lp["r"] * (lp["d"] + lp["k"]) == lp["lora"]
     assert lp["d"] * lp["k"] == lp["full"] and lp["full"] // lp["lora"] == lp["ratio"]
+
+
+# --------------------------------------------------------------------------- double quantization off
+def test_nodq_storage_matches_page():
+    """Deep dive 7.1: without double quantization each block keeps a 32-bit scale, 32/64 = 0.5 bit per
+    weight on top of the 4-bit codes (4.5 bits/param)."""
+    g = _golden("storage_pages.json")
+    for cfg in workloads.CONFIGS.values():
+        for _, N, K in cfg["layers"]:
+            assert nf4.bits_per_param_nodq(N, K) == 4 + g["scale_bits_without_dq"]["value"]
+            assert nf4.storage_bytes_nodq(N, K) == (N * K // 2, 4 * (N * K // 64))
+
+
+def test_nodq_codes_and_absmax_match_bruteforce():
+    """Codes: the same rational nearest-level search as with double quantization on; absmax: the exact
+    block maximum of |w| (a bf16 value, stored exactly as fp32)."""
+    rng = np.random.default_rng(17)
+    wb = _rand_blocks(rng, 64)
+    W = bf16.from_f32_rne(wb.astype(np.float32)).reshape(4, -1)
+    packed, absmax = nf4.quantize_nodq(W)
+    codes = nf4.unpack_nibbles(packed).reshape(-1, 64)
+    c = nf4.nf4_table()
+    for b in range(wb.shape[0]):
+        assert list(codes[b]) == brute.nf4_codes_block(wb[b], c), f"block {b}"
+    assert np.array_equal(absmax, np.abs(wb).max(axis=1).astype(np.float32))
+    # the same codes as the double-quantized path (both encode against the true absmax)
+    p2, _, _ = nf4.quantize(W)
+    assert np.array_equal(packed, p2)
+
+
+def test_nodq_dequant_against_fraction_and_exact_extremes():
+    """w_hat = RNE_bf16(fl32(a * c_q)) element by element (Fraction products), and the element that
+    sets the absmax comes back exactly (its code is 0 or 15, levels -1 and +1)."""
+    torch = pytest.importorskip("torch")
+    W = workloads.custom(78, (32, 256), 0.02)
+    packed, absmax = nf4.quantize_nodq(W)
+    Wh = nf4.dequantize_nodq(packed, absmax, 32, 256)
+    codes = nf4.unpack_nibbles(packed).reshape(-1, 64)
+    c = nf4.nf4_table()
+    prod = np.empty(codes.shape, np.float32)
+    for b in range(codes.shape[0]):
+        for i in range(codes.shape[1]):
+            prod[b, i] = float(brute.round_f32(Fraction(float(absmax[b])) * Fraction(float(c[codes[b, i]]))))
+    ref = torch.from_numpy(prod).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(Wh.reshape(-1, 64), ref)
+    w = bf16.to_f64(W).reshape(-1, 64)
+    wh = bf16.to_f64(Wh).reshape(-1, 64)
+    top = np.argmax(np.abs(w), axis=1)
+    rows = np.arange(w.shape[0])
+    assert np.array_equal(wh[rows, top], w[rows, top])
+    rows_sel = np.array([0, 7, 31])
+    assert np.array_equal(nf4.dequantize_rows_nodq(packed, absmax, 256, rows_sel), Wh[rows_sel])
+
+
+def test_nodq_error_bound():
+    """|w - w_hat| <= a * (largest half gap of the table) + bf16 rounding of w_hat: no scale error term,
+    since the scale is stored exactly."""
+    W = workloads.weight(2)[:128]                          # includes 10x outliers
+    packed, absmax = nf4.quantize_nodq(W)
+    Wh = nf4.dequantize_nodq(packed, absmax, 128, 4096)
+    w = bf16.to_f64(W).reshape(-1, 64)
+    wh = bf16.to_f64(Wh).reshape(-1, 64)
+    half_gap = np.max(np.diff(nf4.nf4_table().astype(np.float64))) / 2
+    bound = absmax.astype(np.float64)[:, None] * half_gap + np.abs(wh) * 2.0 ** -8
+    assert np.all(np.abs(w - wh) <= bound + 1e-30)
