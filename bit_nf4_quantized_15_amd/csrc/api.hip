@@ -13,12 +13,14 @@ namespace {
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// q8 == NULL selects the state without double quantization (a2 = one fp32
+// absmax per block); codes and a2 are required either way.
 inline qlora_status check_state(const qlora_nf4* w) {
-    if (!w || !w->codes || !w->q8 || !w->a2) return QLORA_ERR_INVALID_ARG;
+    if (!w || !w->codes || !w->a2) return QLORA_ERR_INVALID_ARG;
     if (w->n < 1 || w->k < 1) return QLORA_ERR_INVALID_ARG;
     if (w->k % kBlock) return QLORA_ERR_UNSUPPORTED_SHAPE;
     if (w->n > (int64_t(1) << 31) || w->k > (int64_t(1) << 31)) return QLORA_ERR_UNSUPPORTED_SHAPE;
-    if (!aligned16(w->codes) || !aligned16(w->q8) || !aligned16(w->a2)) return QLORA_ERR_MISALIGNED;
+    if (!aligned16(w->codes) || (w->q8 && !aligned16(w->q8)) || !aligned16(w->a2)) return QLORA_ERR_MISALIGNED;
     return QLORA_OK;
 }
 
@@ -84,6 +86,15 @@ qlora_status qlora_nf4_sizes(int64_t N, int64_t K, size_t* codes_bytes, size_t* 
     if (codes_bytes) *codes_bytes = (size_t)(n / 2);
     if (q8_bytes) *q8_bytes = (size_t)(n / kBlock);
     if (a2_bytes) *a2_bytes = (size_t)(4 * ((n + kSuperElems - 1) / kSuperElems));
+    return QLORA_OK;
+}
+
+qlora_status qlora_nf4_sizes_nodq(int64_t N, int64_t K, size_t* codes_bytes, size_t* absmax_bytes) {
+    if (N < 1 || K < 1) return QLORA_ERR_INVALID_ARG;
+    if (K % kBlock) return QLORA_ERR_UNSUPPORTED_SHAPE;
+    const int64_t n = N * K;
+    if (codes_bytes) *codes_bytes = (size_t)(n / 2);
+    if (absmax_bytes) *absmax_bytes = (size_t)(4 * (n / kBlock));
     return QLORA_OK;
 }
 

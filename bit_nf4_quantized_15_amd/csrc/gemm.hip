@@ -258,7 +258,7 @@ __device__ __forceinline__ void store_acc(uint16_t* __restrict__ out, int64_t ld
 constexpr int kSup = 2;                                     // blocks per super-step
 constexpr int kCodeTileBytes = kTN * kSup * kBlock / 2;     // 256 rows x 64 B
 
-template <bool Q8DW>
+template <bool Q8DW, bool DQ>
 __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ q8,
     const float* __restrict__ a2, const uint16_t* __restrict__ t, const uint16_t* __restrict__ Bl,
@@ -333,15 +333,29 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
         }
     };
     // ---- block scales: thread tid, tile row tid, the 2 blocks of a super-step
-    // (an even first block, so both lie in one group of 256 blocks)
+    // (an even first block, so both lie in one group of 256 blocks).  Without
+    // double quantization a2 holds the blocks' fp32 absmax itself.
     const int srow = min(n0 + tid, N - 1);
     const int64_t sblk = (int64_t)srow * KB;
     struct Sc {
-        uint32_t q;  // 8-bit scale codes of the 2 blocks, block j in byte j
-        float g;     // second-level scale of their group
+        uint32_t q;  // 8-bit scale codes of the 2 blocks, block j in byte j (DQ off: block 0's scale bits)
+        float g;     // second-level scale of their group (DQ off: block 1's scale)
     };
+    // loads per load_scales call, all issued after the step's x tile
+    constexpr int kScaleLoads = DQ ? (Q8DW ? 2 : 3) : (Q8DW ? 1 : 2);
     auto load_scales = [&](int S, Sc& sc) __attribute__((always_inline)) {
         const int b0 = kSup * S;
+        if (!DQ) {
+            if (Q8DW) {  // blocks per row even: the 2 scales are one aligned 8-byte pair
+                const f32x2_t v = *reinterpret_cast<const f32x2_t*>(a2 + sblk + b0);
+                sc.q = __builtin_bit_cast(uint32_t, v[0]);
+                sc.g = v[1];
+            } else {
+                sc.q = __builtin_bit_cast(uint32_t, a2[sblk + b0]);
+                sc.g = a2[sblk + min(b0 + 1, KB - 1)];
+            }
+            return;
+        }
         if (Q8DW) {  // blocks per row even: the 2 codes are one aligned 16-bit word
             sc.q = *reinterpret_cast<const uint16_t*>(q8 + sblk + b0);
         } else {
@@ -351,10 +365,15 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
     };
     auto make_scales = [&](const Sc& sc, float* dst, int S) __attribute__((always_inline)) {
         const int b0 = kSup * S;
-        const float st = scale_step(sc.g);
         f32x2_t ah;
-        ah[0] = st * (float)(sc.q & 0xFFu);
-        ah[1] = b0 + 1 < KB ? st * (float)((sc.q >> 8) & 0xFFu) : 0.0f;
+        if (DQ) {
+            const float st = scale_step(sc.g);
+            ah[0] = st * (float)(sc.q & 0xFFu);
+            ah[1] = b0 + 1 < KB ? st * (float)((sc.q >> 8) & 0xFFu) : 0.0f;
+        } else {
+            ah[0] = __builtin_bit_cast(float, sc.q);
+            ah[1] = b0 + 1 < KB ? sc.g : 0.0f;
+        }
         *reinterpret_cast<f32x2_t*>(dst + kSup * tid) = ah;
     };
     // this lane's 16 code bytes of column u at block j of a super-step
@@ -479,7 +498,7 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
         // tile ks+2 must have landed (the codes and scales requested after it may
         // stay in flight); the 4 operand reads of the next step stay in flight
         // across the barrier, every earlier LDS access has completed.
-        if (j == 0) wait_direct_loads_behind<4 + (Q8DW ? 2 : 3)>();
+        if (j == 0) wait_direct_loads_behind<4 + kScaleLoads>();
         else wait_direct_loads();
         barrier_reads_in_flight<4>();
     };
@@ -612,7 +631,7 @@ __device__ __forceinline__ uint32_t wtile_off(int row, int col) {
     return (uint32_t)row * 512u + ((uint32_t)((col >> 3) ^ f) << 4) + ((uint32_t)(col & 7) << 1);
 }
 
-template <bool DYVEC>
+template <bool DYVEC, bool DQ>
 __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
     const uint16_t* __restrict__ dy, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ q8,
     const float* __restrict__ a2, const uint16_t* __restrict__ u_, const uint16_t* __restrict__ Al,
@@ -650,13 +669,25 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
         S.c0 = *reinterpret_cast<const u32x4_t*>(p);
         S.c1 = *reinterpret_cast<const u32x4_t*>(p + 16);
         const int64_t blk = (int64_t)nc * KB + dkc / kTK;
-        S.q = q8[blk];
         S.ok = n < N && dk_ok;
-        S.g = a2[blk >> 8];
+        if (DQ) {
+            S.q = q8[blk];
+            S.g = a2[blk >> 8];
+        } else {
+            S.q = 0u;
+            S.g = a2[blk];  // no double quantization: the block's fp32 absmax
+        }
     };
+    // loads per load_step: codes (2) and the scale data
+    constexpr int kStepLoads = DQ ? 4 : 3;
     // scale of a loaded step; the load above stays unconditional because the
     // validity select happens here, where the value is needed anyway
     auto ahat_of = [&](const Step& S) {
+        if (!DQ) {
+            float g = S.g;
+            asm volatile("" : "+v"(g));
+            return S.ok ? g : 0.0f;
+        }
         uint32_t q = S.q;
         asm volatile("" : "+v"(q));
         return scale_step(S.g) * (float)(S.ok ? q : 0u);
@@ -750,7 +781,7 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
         load_dy(An, min(ns + 1, NS - 1));
         __builtin_amdgcn_sched_barrier(kAllButVmem);  // keep the loads in this order
         Step nn;
-        load_step(min(ns + 2, NS - 1), nn);  // 4 loads: codes (2), q8, a2
+        load_step(min(ns + 2, NS - 1), nn);  // kStepLoads loads: codes (2), scale data
         u32x4_t w[8];
         const Nf4Tab T = make_tab(ahat_of(nxt));
 #pragma unroll
@@ -772,7 +803,7 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
         store_w(Bn, w);
         cur = nxt;
         nxt = nn;
-        if (DYVEC) wait_direct_loads_behind<4>();
+        if (DYVEC) wait_direct_loads_behind<kStepLoads>();
         __syncthreads();
     }
 
@@ -844,12 +875,17 @@ qlora_status launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const uint
     if ((int64_t)kTM * K * 2 >= (int64_t(1) << 32)) return QLORA_ERR_UNSUPPORTED_SHAPE;
     // code-tile offsets (including blocks past a row's end) must fit a 32-bit voffset
     if ((uint64_t)N * (uint64_t)K / 2 + 4096 >= (uint64_t(1) << 32)) return QLORA_ERR_UNSUPPORTED_SHAPE;
-    if ((K / kTK) % kSup == 0)
-        hipLaunchKernelGGL(nf4_gemm_fwd_kernel<true>, dim3(tm * tn), dim3(kT), 0, s, x, codes, q8, a2, t, B, y, M, N,
-                           K, r, tm, tn);
-    else
-        hipLaunchKernelGGL(nf4_gemm_fwd_kernel<false>, dim3(tm * tn), dim3(kT), 0, s, x, codes, q8, a2, t, B, y, M,
-                           N, K, r, tm, tn);
+    // q8 == NULL: no double quantization, a2 holds one fp32 absmax per block
+#define QL_FWD(Q8DW, DQ)                                                                                        \
+    hipLaunchKernelGGL((nf4_gemm_fwd_kernel<Q8DW, DQ>), dim3(tm * tn), dim3(kT), 0, s, x, codes, q8, a2, t, B, y, M, \
+                       N, K, r, tm, tn)
+    const bool even = (K / kTK) % kSup == 0;
+    if (q8) {
+        if (even) QL_FWD(true, true); else QL_FWD(false, true);
+    } else {
+        if (even) QL_FWD(true, false); else QL_FWD(false, false);
+    }
+#undef QL_FWD
     return launch_status();
 }
 
@@ -859,12 +895,16 @@ qlora_status launch_gemm_bwd_dx(const uint16_t* dy, const uint8_t* codes, const 
     const int tm = (M + kTM - 1) / kTM, tk = (K + kTN - 1) / kTN;
     const bool vec = (N % 8 == 0) && ((reinterpret_cast<uintptr_t>(dy) & 15u) == 0) &&
                      ((int64_t)kTM * N * 2 < (int64_t(1) << 32));
-    if (vec)
-        hipLaunchKernelGGL(nf4_gemm_bwd_dx_kernel<true>, dim3(tm * tk), dim3(kT), 0, s, dy, codes, q8, a2, u, A,
-                           dx, M, N, K, r, tm, tk);
-    else
-        hipLaunchKernelGGL(nf4_gemm_bwd_dx_kernel<false>, dim3(tm * tk), dim3(kT), 0, s, dy, codes, q8, a2, u, A,
-                           dx, M, N, K, r, tm, tk);
+    // q8 == NULL: no double quantization, a2 holds one fp32 absmax per block
+#define QL_BWD(V, DQ)                                                                                          \
+    hipLaunchKernelGGL((nf4_gemm_bwd_dx_kernel<V, DQ>), dim3(tm * tk), dim3(kT), 0, s, dy, codes, q8, a2, u, A, dx, \
+                       M, N, K, r, tm, tk)
+    if (q8) {
+        if (vec) QL_BWD(true, true); else QL_BWD(false, true);
+    } else {
+        if (vec) QL_BWD(true, false); else QL_BWD(false, false);
+    }
+#undef QL_BWD
     return launch_status();
 }
 

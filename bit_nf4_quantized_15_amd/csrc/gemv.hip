@@ -97,7 +97,7 @@ struct GvPlan {
     int tsh;     // log2 of the threads that stage one x row
 };
 
-template <int NV, int NG>
+template <int NV, int NG, bool DQ>
 __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const uint16_t* __restrict__ x,
                                                               const uint8_t* __restrict__ codes,
                                                               const uint8_t* __restrict__ q8,
@@ -165,10 +165,11 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const uint16_t* __
     // ---- per phase and wave: 8-bit scales and group scales into registers, then
     // the codes straight into LDS.  Lane l computes the scales of row l % 16
     // and blocks l / 16 + 4 u of the wave's range.
+    // (without double quantization: the blocks' fp32 absmax, read from a2)
     const int arow = min(n0 + (lane & 15), N - 1);
     const rsrc_t qrs = make_rsrc(q8, (uint32_t)((uint64_t)N * Kb));
     const int ngroups = (int)(((int64_t)N * Kb + kSuper - 1) / kSuper);
-    const rsrc_t ars = make_rsrc(a2, (uint32_t)ngroups * 4u);
+    const rsrc_t ars = make_rsrc(a2, DQ ? (uint32_t)ngroups * 4u : (uint32_t)((uint64_t)N * Kb * 4));
     const i32x4_t crs = raw_rsrc(codes, (uint32_t)((uint64_t)N * (uint32_t)(K >> 1)));
     // DMA lane mapping: instruction (group j, half hh) writes rows 8 hh + l / 8,
     // LDS chunk l % 8, which holds global chunk (l % 8) ^ ((row / 2) % 8)
@@ -191,12 +192,15 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const uint16_t* __
 #pragma unroll
         for (int u = 0; u < NG; ++u) {
             const int b = min(bw0 + (lane >> 4) + 4 * u, Kb - 1);
-            qv[u] = __builtin_amdgcn_raw_buffer_load_b8(qrs, rkb + (uint32_t)b, 0, 0);
+            qv[u] = DQ ? __builtin_amdgcn_raw_buffer_load_b8(qrs, rkb + (uint32_t)b, 0, 0)
+                       : __builtin_amdgcn_raw_buffer_load_b32(ars, 4u * (rkb + (uint32_t)b), 0, 0);
         }
-        g_lo = (int)((rkb + (uint32_t)min(bw0, Kb - 1)) >> 8);
-        a_lo = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ars, 4u * (uint32_t)g_lo, 0, 0));
-        a_hi = __builtin_bit_cast(float,
-                                  __builtin_amdgcn_raw_buffer_load_b32(ars, 4u * (uint32_t)min(g_lo + 1, ngroups - 1), 0, 0));
+        if (DQ) {
+            g_lo = (int)((rkb + (uint32_t)min(bw0, Kb - 1)) >> 8);
+            a_lo = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ars, 4u * (uint32_t)g_lo, 0, 0));
+            a_hi = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(ars, 4u * (uint32_t)min(g_lo + 1, ngroups - 1), 0, 0));
+        }
 #pragma unroll
         for (int j = 0; j < NG; ++j) {
 #pragma unroll
@@ -218,7 +222,8 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const uint16_t* __
             const int jb = (lane >> 4) + 4 * u;
             const int b = bw0 + jb;
             const float step = (int)((rkb + (uint32_t)b) >> 8) == g_lo ? s_lo : s_hi;
-            aw[(lane & 15) * (PBw + 4) + jb] = b < Kb ? step * (float)qv[u] : 0.0f;
+            const float ah = DQ ? step * (float)qv[u] : __builtin_bit_cast(float, qv[u]);
+            aw[(lane & 15) * (PBw + 4) + jb] = b < Kb ? ah : 0.0f;
         }
     };
 
@@ -363,10 +368,16 @@ qlora_status launch_gemv_fwd(const uint16_t* x, const uint8_t* codes, const uint
     P.xs = pb * 128 + 16;
     const dim3 grid((unsigned)((N + kGvRows - 1) / kGvRows));
     const int nv = M == 1 ? 1 : M == 2 ? 2 : 4;
+    // q8 == NULL: no double quantization, a2 holds one fp32 absmax per block
 #define QLORA_GEMV(NV_, NG_)                                                                                   \
-    if (nv == NV_ && ng == NG_)                                                                                \
-        hipLaunchKernelGGL((nf4_gemv_kernel<NV_, NG_>), grid, dim3(kGvThreads), 0, s, x, codes, q8, a2, t, B, y, M, N, \
-                           K, r, P);
+    if (nv == NV_ && ng == NG_) {                                                                              \
+        if (q8)                                                                                                \
+            hipLaunchKernelGGL((nf4_gemv_kernel<NV_, NG_, true>), grid, dim3(kGvThreads), 0, s, x, codes, q8, a2, t, B, \
+                               y, M, N, K, r, P);                                                              \
+        else                                                                                                   \
+            hipLaunchKernelGGL((nf4_gemv_kernel<NV_, NG_, false>), grid, dim3(kGvThreads), 0, s, x, codes, q8, a2, t,  \
+                               B, y, M, N, K, r, P);                                                           \
+    }
     QLORA_GEMV(1, 1) QLORA_GEMV(1, 2) QLORA_GEMV(1, 4)
     QLORA_GEMV(2, 1) QLORA_GEMV(2, 2) QLORA_GEMV(2, 4)
     QLORA_GEMV(4, 1) QLORA_GEMV(4, 2) QLORA_GEMV(4, 4)

@@ -15,6 +15,8 @@
 //      code = #{j : w/a > m_j} (nearest level, ties to the lower index) is a
 //      4-step branchless binary search over T_j in fp32 compares;
 //   5. nibbles are packed (element 2i high) and stored as one dword per lane.
+// Without double quantization (sections 7.1, 9.5) step 3 stores each block's
+// absmax as its fp32 scale instead of the 8-bit code and the group scale.
 #include "common.h"
 
 namespace qlora {
@@ -52,6 +54,7 @@ __device__ __forceinline__ uint32_t nf4_code(float w, f32x4_t t0, f32x4_t t1, f3
     return (b3 ? 8u : 0u) | (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
 }
 
+template <bool DQ>
 __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint16_t* __restrict__ W,
                                                                 int64_t nblocks,
                                                                 uint8_t* __restrict__ codes,
@@ -114,13 +117,16 @@ __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint16_t* 
         dst[2] = f32x4_t{T[8], T[9], T[10], T[11]};
         dst[3] = f32x4_t{T[12], T[13], T[14], 0.0f};
     }
+    if (!DQ) {
+        if (tid < nb_here) a2[b0 + tid] = a;  // the exact block absmax is the fp32 scale
+    }
     float gm = a;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) gm = fmaxf(gm, __shfl_xor(gm, o));
-    if (lane == 0) s_wmax[wave] = gm;
+    if (DQ && lane == 0) s_wmax[wave] = gm;
     __syncthreads();
     const float A2 = fmaxf(fmaxf(s_wmax[0], s_wmax[1]), fmaxf(s_wmax[2], s_wmax[3]));
-    if (tid < nb_here) {
+    if (DQ && tid < nb_here) {
         // q8 = #{k in 1..255 : 510 a > (2k-1) A2}; all products exact in fp64
         const double x = 510.0 * (double)a;
         const double y = (double)A2;
@@ -132,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint16_t* 
         }
         q8[b0 + tid] = (uint8_t)k;
     }
-    if (tid == 0) a2[blockIdx.x] = A2;
+    if (DQ && tid == 0) a2[blockIdx.x] = A2;
 
     // 4-5. codes against the true absmax, packed and stored
 #pragma unroll
@@ -154,7 +160,9 @@ __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint16_t* 
 }
 
 // nf4_dequantize_kernel: 256 lanes x 8 weights = 32 blocks per workgroup.
-//   a_hat = fl32(fl32(a2/255) * q8), w_hat = RNE_bf16(fl32(a_hat * c_code)).
+//   a_hat = fl32(fl32(a2/255) * q8) (without double quantization: the stored
+//   fp32 absmax a2[b]), w_hat = RNE_bf16(fl32(a_hat * c_code)).
+template <bool DQ>
 __global__ __launch_bounds__(kThreads) void nf4_dequantize_kernel(const uint8_t* __restrict__ codes,
                                                                   const uint8_t* __restrict__ q8,
                                                                   const float* __restrict__ a2,
@@ -167,8 +175,7 @@ __global__ __launch_bounds__(kThreads) void nf4_dequantize_kernel(const uint8_t*
     const int64_t b = (int64_t)blockIdx.x * 32 + (tid >> 3);
     const int sub = tid & 7;
     if (b >= nblocks) return;
-    const float step = __fdiv_rn(a2[b / kSuper], 255.0f);
-    const float ahat = __fmul_rn(step, (float)q8[b]);
+    const float ahat = DQ ? __fmul_rn(__fdiv_rn(a2[b / kSuper], 255.0f), (float)q8[b]) : a2[b];
     const uint32_t pk = *reinterpret_cast<const uint32_t*>(codes + b * (kBlock / 2) + sub * 4);
     u32x4_t o;
 #pragma unroll
@@ -186,16 +193,24 @@ __global__ __launch_bounds__(kThreads) void nf4_dequantize_kernel(const uint8_t*
 qlora_status launch_quantize(const uint16_t* W, int64_t nblocks, uint8_t* codes, uint8_t* q8, float* a2,
                              hipStream_t s) {
     const int64_t groups = (nblocks + kSuper - 1) / kSuper;
-    hipLaunchKernelGGL(nf4_quantize_kernel, dim3((unsigned)groups), dim3(kThreads), 0, s, W, nblocks, codes,
-                       q8, a2);
+    if (q8)
+        hipLaunchKernelGGL(nf4_quantize_kernel<true>, dim3((unsigned)groups), dim3(kThreads), 0, s, W, nblocks,
+                           codes, q8, a2);
+    else
+        hipLaunchKernelGGL(nf4_quantize_kernel<false>, dim3((unsigned)groups), dim3(kThreads), 0, s, W, nblocks,
+                           codes, q8, a2);
     return launch_status();
 }
 
 qlora_status launch_dequantize(const uint8_t* codes, const uint8_t* q8, const float* a2, int64_t nblocks,
                                uint16_t* out, hipStream_t s) {
     const int64_t grid = (nblocks + 31) / 32;
-    hipLaunchKernelGGL(nf4_dequantize_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, codes, q8, a2,
-                       nblocks, out);
+    if (q8)
+        hipLaunchKernelGGL(nf4_dequantize_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s, codes, q8, a2,
+                           nblocks, out);
+    else
+        hipLaunchKernelGGL(nf4_dequantize_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s, codes, q8, a2,
+                           nblocks, out);
     return launch_status();
 }
 

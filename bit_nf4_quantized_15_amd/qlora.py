@@ -37,6 +37,7 @@ def _load():
         "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "qlora_nf4_sizes": (ctypes.c_int, [c_i64, c_i64, ctypes.POINTER(c_sz), ctypes.POINTER(c_sz),
                                            ctypes.POINTER(c_sz)]),
+        "qlora_nf4_sizes_nodq": (ctypes.c_int, [c_i64, c_i64, ctypes.POINTER(c_sz), ctypes.POINTER(c_sz)]),
         "qlora_quantize": (ctypes.c_int, [c_vp, c_i64, c_i64, P, c_vp]),
         "qlora_dequantize": (ctypes.c_int, [P, c_vp, c_vp]),
         "qlora_fwd_workspace": (c_sz, [c_i64, c_i64, c_i64, ctypes.c_int]),
@@ -99,28 +100,46 @@ def sizes(N, K):
     return cb.value, qb.value, ab.value
 
 
+def sizes_nodq(N, K):
+    """(codes bytes, fp32 block-absmax bytes) of an [N, K] weight quantized without double quantization."""
+    cb, ab = c_sz(), c_sz()
+    _check(lib.qlora_nf4_sizes_nodq(N, K, ctypes.byref(cb), ctypes.byref(ab)), "qlora_nf4_sizes_nodq")
+    return cb.value, ab.value
+
+
 class NF4Weight:
-    """Device-resident quantized weight: codes / q8 (uint8) and a2 (float32) tensors."""
+    """Device-resident quantized weight: codes (uint8), q8 (uint8) and a2 (float32) tensors; without
+    double quantization q8 is None and a2 holds one fp32 absmax per 64-block."""
 
     def __init__(self, codes, q8, a2, N, K):
         self.codes, self.q8, self.a2, self.N, self.K = codes, q8, a2, int(N), int(K)
 
+    @property
+    def double_quant(self):
+        return self.q8 is not None
+
     @classmethod
-    def empty(cls, N, K, device="cuda"):
+    def empty(cls, N, K, device="cuda", double_quant=True):
+        if not double_quant:
+            cb, ab = sizes_nodq(N, K)
+            return cls(torch.empty(cb, dtype=torch.uint8, device=device), None,
+                       torch.empty(ab // 4, dtype=torch.float32, device=device), N, K)
         cb, qb, ab = sizes(N, K)
         return cls(torch.empty(cb, dtype=torch.uint8, device=device),
                    torch.empty(qb, dtype=torch.uint8, device=device),
                    torch.empty(ab // 4, dtype=torch.float32, device=device), N, K)
 
     def state(self):
-        return NF4State(self.codes.data_ptr(), self.q8.data_ptr(), self.a2.data_ptr(), self.N, self.K)
+        q8 = None if self.q8 is None else self.q8.data_ptr()
+        return NF4State(self.codes.data_ptr(), q8, self.a2.data_ptr(), self.N, self.K)
 
 
-def quantize(W, out=None):
-    """NF4 + double-quant of a bf16 [N, K] device weight (qlora_quantize)."""
+def quantize(W, out=None, double_quant=True):
+    """NF4 of a bf16 [N, K] device weight (qlora_quantize), with or without double quantization of the
+    block scales (ignored when `out` is given: its layout decides)."""
     N, K = W.shape
     _dev(W, torch.bfloat16, "W")
-    w = NF4Weight.empty(N, K, W.device) if out is None else out
+    w = NF4Weight.empty(N, K, W.device, double_quant) if out is None else out
     st = w.state()
     _check(lib.qlora_quantize(_ptr(W), N, K, ctypes.byref(st), _stream()), "qlora_quantize")
     return w

@@ -53,13 +53,18 @@ typedef enum qlora_status {
     QLORA_ERR_HIP = -5                /* a HIP launch error was reported */
 } qlora_status;
 
-/* Quantized weight: three flat device arrays plus the logical shape.  This is
- * the "quantization state" the deep dive (section 5.2) says is kept next to
- * the codes: codes, first-level 8-bit scale codes, second-level fp32 scales. */
+/* Quantized weight: flat device arrays plus the logical shape.  This is the
+ * "quantization state" the deep dive (section 5.2) says is kept next to the
+ * codes.  With double quantization (section 7.2; q8 != NULL): codes, the
+ * first-level 8-bit scale codes and the second-level fp32 scales.  Without it
+ * (sections 7.1 and 9.5; q8 == NULL): codes and one fp32 absmax per 64-block
+ * in a2, 4.5 bits per weight.  Every entry point taking a qlora_nf4 accepts
+ * both; a2 is never NULL. */
 typedef struct qlora_nf4 {
     uint8_t* codes; /* [N*K/2]            packed 4-bit NF4 codes                     */
-    uint8_t* q8;    /* [N*K/64]           8-bit code of each block's absmax          */
-    float* a2;      /* [ceil(N*K/16384)]  fp32 absmax of each group of 256 absmaxes  */
+    uint8_t* q8;    /* [N*K/64]           8-bit code of each block's absmax, or NULL */
+    float* a2;      /* [ceil(N*K/16384)]  fp32 absmax of each group of 256 absmaxes; */
+                    /* [N*K/64] fp32 absmax of each block when q8 == NULL            */
     int64_t n;      /* N = Dout (rows of the stored weight)                          */
     int64_t k;      /* K = Din, a multiple of 64                                     */
 } qlora_nf4;
@@ -77,6 +82,11 @@ const char* qlora_status_string(int status);
 qlora_status qlora_nf4_sizes(int64_t N, int64_t K, size_t* codes_bytes, size_t* q8_bytes,
                              size_t* a2_bytes);
 
+/* Byte sizes of the two arrays of an [N, K] weight quantized without double
+ * quantization (deep dive 7.1: 4 + 32/64 bits per weight): codes N*K/2, fp32
+ * block absmax 4*N*K/64.  Errors as qlora_nf4_sizes. */
+qlora_status qlora_nf4_sizes_nodq(int64_t N, int64_t K, size_t* codes_bytes, size_t* absmax_bytes);
+
 /* Quantize a bf16 weight W [N, K] into `out` (deep dive 5.2 and 7.2).
  *   a_b  = max |w| over block b
  *   code = argmin_j |w/a_b - c_j| in exact arithmetic, ties to the lower j;
@@ -84,12 +94,15 @@ qlora_status qlora_nf4_sizes(int64_t N, int64_t K, size_t* codes_bytes, size_t* 
  *   a2_S = max of a_b over group S
  *   q8_b = argmin_k |a_b/a2_S - k/255| over k = 0..255, ties to the lower k
  * out->codes/q8/a2 must hold qlora_nf4_sizes() bytes; out->n/k must equal N/K.
- * Codes are computed against the true a_b, not its 8-bit reconstruction. */
+ * Codes are computed against the true a_b, not its 8-bit reconstruction.
+ * out->q8 == NULL quantizes without double quantization: a2[b] = a_b (fp32),
+ * sized by qlora_nf4_sizes_nodq(); the codes are the same. */
 qlora_status qlora_quantize(const uint16_t* W, int64_t N, int64_t K, const qlora_nf4* out,
                             void* stream);
 
 /* Dequantize to bf16 out [N, K] (deep dive 5.2: w_hat = a * c_q):
- *   a_hat = fl32( fl32(a2_S / 255) * q8_b ),  out = RNE_bf16( fl32(a_hat * c_code) ).
+ *   a_hat = fl32( fl32(a2_S / 255) * q8_b ) (out->q8 == NULL: a_hat = a2_b),
+ *   out = RNE_bf16( fl32(a_hat * c_code) ).
  * For tests and export only: the linear layer never materialises W. */
 qlora_status qlora_dequantize(const qlora_nf4* w, uint16_t* out, void* stream);
 

@@ -44,6 +44,16 @@ def test_sizes(q):
     assert q.lib.qlora_nf4_sizes(4, 64, None, None, None) == OK
 
 
+def test_sizes_nodq(q):
+    """Without double quantization: codes N*K/2 and one fp32 absmax per 64-block (deep dive 7.1)."""
+    assert q.sizes_nodq(4096, 4096) == (4096 * 4096 // 2, 4 * 4096 * 4096 // 64)
+    assert q.sizes_nodq(3, 192) == (288, 36)
+    cb = ctypes.c_size_t()
+    assert q.lib.qlora_nf4_sizes_nodq(4, 100, ctypes.byref(cb), None) == SHAPE
+    assert q.lib.qlora_nf4_sizes_nodq(0, 64, None, None) == INVALID
+    assert q.lib.qlora_nf4_sizes_nodq(4, 64, None, None) == OK
+
+
 def test_workspace_queries(q):
     for M, N, K, r in ((1, 4096, 4096, 16), (2048, 11008, 4096, 64), (16, 256, 256, 8)):
         f, b = q.fwd_workspace(M, N, K, r), q.bwd_workspace(M, N, K, r)
@@ -73,6 +83,10 @@ def test_quantize_argument_errors(q):
     assert f(FAKE, 32, 64, ctypes.byref(st), None) == INVALID                 # shape mismatch
     assert f(FAKE + 2, 64, 64, ctypes.byref(st), None) == MISALIGNED
     assert f(FAKE, 64, 64, ctypes.byref(_state(q, q8=FAKE + 8)), None) == MISALIGNED
+    # q8 == NULL selects the state without double quantization; codes and a2 stay required
+    assert f(FAKE, 64, 64, ctypes.byref(_state(q, q8=None, a2=0)), None) == INVALID
+    assert f(FAKE, 64, 64, ctypes.byref(_state(q, q8=None, a2=FAKE + 4)), None) == MISALIGNED
+    assert f(FAKE, 64, 100, ctypes.byref(_state(q, q8=None, k=100)), None) == SHAPE
     assert q.lib.qlora_dequantize(ctypes.byref(st), None, None) == INVALID
     assert q.lib.qlora_dequantize(ctypes.byref(st), FAKE + 4, None) == MISALIGNED
 
