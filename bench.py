@@ -158,9 +158,11 @@ def graph_ms(calls, reps=5):
     return a.elapsed_time(b) / (reps * len(calls))
 
 
-def gemv_bytes(M, N, K, r):
-    """Algorithmic HBM bytes of one decode forward: codes, q8, a2, x, y, A, B."""
-    return N * K // 2 + N * K // 64 + 4 * (-(-N * K // 16384)) + 2 * M * K + 2 * M * N + 2 * K * r + 2 * r * N
+def gemv_bytes(M, N, K, r, double_quant=True):
+    """Algorithmic HBM bytes of one decode forward: codes, scales (q8 + a2, or the fp32 block absmax
+    without double quantization), x, y, A, B."""
+    scales = N * K // 64 + 4 * (-(-N * K // 16384)) if double_quant else 4 * (N * K // 64)
+    return N * K // 2 + scales + 2 * M * K + 2 * M * N + 2 * K * r + 2 * r * N
 
 
 def main():
@@ -367,6 +369,8 @@ def extras(torch, qlora, workloads, dev, to_dev, L, M, r):
     res["decode_gemv_q_proj_4096x4096_r16"] = dec
     del copies
 
+    res["double_quant_off"] = extras_nodq(torch, qlora, workloads, dev, to_dev, L, M, r, ev)
+
     # context: dense bf16 torch.matmul (hipBLASLt) on the same shapes, forward base product only
     tot_f, tot_ms = 0, 0.0
     for d in L:
@@ -381,6 +385,73 @@ def extras(torch, qlora, workloads, dev, to_dev, L, M, r):
         tot_ms += a.elapsed_time(b) / 3
         tot_f += 2 * M * d["N"] * d["K"]
     res["context_dense_bf16_matmul_fwd_tflops"] = round(tot_f / (tot_ms * 1e-3) / 1e12, 1)
+    return res
+
+
+def extras_nodq(torch, qlora, workloads, dev, to_dev, L, M, r, ev):
+    """The same workloads with double quantization off (fp32 absmax per block, deep dive 7.1 and 9.5):
+    the whole quantize + fwd + bwd step of the 7 linears, the forward GEMM alone, quantize bandwidth and
+    the decode GEMV (64 rotated weight copies)."""
+    res = {}
+    alpha = workloads.CONFIGS[4]["alpha"]
+    Wn = [qlora.NF4Weight.empty(d["N"], d["K"], dev, double_quant=False) for d in L]
+    ws = torch.empty(max(qlora.bwd_workspace(M, d["N"], d["K"], r) for d in L), dtype=torch.uint8, device=dev)
+    total_flops = sum(d["flops"]["fwd"] + d["flops"]["bwd"] for d in L)
+    fwd_flops = sum(d["flops"]["fwd_gemm"] for d in L)
+
+    def quant():
+        for d, w in zip(L, Wn):
+            qlora.quantize(d["W"], out=w)
+
+    def fwd():
+        for d, w in zip(L, Wn):
+            qlora.fused_gemm_fwd(w, d["x"], d["t"], d["B"], y=d["y"])
+
+    def step():
+        quant()
+        for d, w in zip(L, Wn):
+            qlora.lora_down(d["x"], d["A"], alpha, t=d["t"], ws=ws)
+            qlora.fused_gemm_fwd(w, d["x"], d["t"], d["B"], y=d["y"])
+        for d, w in zip(L, Wn):
+            qlora.linear_bwd(w, d["x"], d["A"], d["B"], alpha, d["dy"], t=d["t"], dx=d["dx"], dA=d["dA"],
+                             dB=d["dB"], ws=ws)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    step_ms = timed(step, 5)
+    fwd_ms = timed(fwd, 5)
+    q_ms = timed(quant, 5)
+    q_bytes = sum(d["N"] * d["K"] * 2 + sum(qlora.sizes_nodq(d["N"], d["K"])) for d in L)
+    res["step"] = {"ms": round(step_ms, 4), "TFLOP/s": round(total_flops / (step_ms * 1e-3) / 1e12, 2)}
+    res["fwd_gemm"] = {"avg_launch_ms": round(fwd_ms / len(L), 4),
+                       "TFLOP/s": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2)}
+    res["quantize"] = {"GB/s": round(q_bytes / (q_ms * 1e-3) / 1e9, 1), "ms": round(q_ms, 4),
+                       "bytes_per_weight": 2 + 0.5 + 4 / 64}
+    del Wn, ws
+    c2 = workloads.CONFIGS[2]
+    _, N2, K2 = c2["layers"][0]
+    W2 = to_dev(workloads.weight(2))
+    copies = [qlora.quantize(W2, double_quant=False) for _ in range(64)]
+    B2 = to_dev(workloads.lora_B(2))
+    xd = to_dev(workloads.activations(2, M=1))
+    td = torch.zeros((1, c2["r"]), dtype=torch.bfloat16, device=dev)
+    yd = torch.empty((1, N2), dtype=torch.bfloat16, device=dev)
+    for w in copies[:4]:
+        qlora.fused_gemm_fwd(w, xd, td, B2, y=yd)
+    torch.cuda.synchronize()
+    gemv_ms = graph_ms([lambda w=w: qlora.fused_gemm_fwd(w, xd, td, B2, y=yd) for w in copies])
+    nb = gemv_bytes(1, N2, K2, c2["r"], double_quant=False) - 2 * K2 * c2["r"]
+    res["decode_gemv_q_proj_M=1"] = {"gemv_kernel_us": round(gemv_ms * 1e3, 2), "bytes_gemv_kernel": nb,
+                                     "GB/s_gemv_kernel": round(nb / (gemv_ms * 1e-3) / 1e9, 1)}
     return res
 
 
