@@ -16,7 +16,8 @@ Sources (web pages on QLoRA / NF4 / bitsandbytes):
   normalised to [-1, 1], asymmetric, with an exact zero.
 * same page, section 7.2: double quantization -- 8-bit first-level scales, one
   fp32 second-level scale per 256 first-level scales;
-  8/64 + 32/(64*256) = 0.127 bit per parameter.
+  8/64 + 32/(64*256) = 0.127 bit per parameter (section 7.1, 9.5: without it,
+  one fp32 scale per block, 0.5 bit per parameter).
 * same page, section 12.2 / 12.4 and "LoRA, QLoRA, QA-LoRA explained"
   (ludovicoyin.github.io), section 2: y = x dequant(W4) + (alpha/r) x A B,
   A: [Din, r], B: [r, Dout]; the base is frozen (no dW).
@@ -26,4 +27,5 @@ Modules:
   nf4    -- codebook, blocking, codes, packing, double quantization, dequant
   brute  -- exact rational (fractions.Fraction) brute-force versions
   lora   -- fp64 forward / backward of the QLoRA linear
+  merge  -- the LoRA merge W_eff = W_hat + (alpha/r) (A B)^T for deployment
 """
