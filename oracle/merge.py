@@ -2,10 +2,11 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-"LoRA, QLoRA, QA-LoRA explained", section 1: the adapter can be folded back
-into the weight, W' = W + (alpha/r) A B, so inference pays no extra latency;
-"bitsandbytes deep dive", section 12 (deployment): a 4-bit base is merged in
-higher precision and may then be re-quantized, which adds error of its own.
+"LoRA, QLoRA, QA-LoRA explained", section 2: the effective weight is
+W_eff = dequant(W4) + (alpha/r) A B; the model-compression interview card:
+folding the adapter back into the weight removes its inference latency;
+"bitsandbytes deep dive", section 12.10: a 4-bit base is merged in higher
+precision and may then be re-quantized, which adds error of its own.
 Here the stored weight is [N = Dout, K = Din], A is [K, r], B is [r, N], so
     W_eff[n, k] = W_hat[n, k] + s * sum_j A[k, j] B[j, n],   s = alpha / r.
 Reading (the pages do not fix the precision): the rank-r sum is accumulated

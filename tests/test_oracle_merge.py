@@ -1,7 +1,8 @@
 """Pins of the merge oracle (oracle.merge) against the pages and the mathematics.
 
-* the worked rank-1 example of "LoRA, QLoRA, QA-LoRA explained" (section 1):
-  with a zero base weight and s = 1 the merged weight is Delta W = A B;
+* the worked rank-1 example of "LoRA, QLoRA, QA-LoRA explained" (section 1,
+  a minimal example): with a zero base weight and s = 1 the merged weight is
+  Delta W = A B (the effective weight of section 2);
 * an exact rational re-derivation (fractions.Fraction) of every rounding step
   on a small case, so the vectorized form cannot transpose an operand, drop the
   scale or round at a different point;
