@@ -33,6 +33,7 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA
+FP32_VECTOR_PEAK_TFS = 157.3   # MI355X fp32 vector (non-matrix) peak
 METRIC = "fused NF4-dequant+LoRA linear TFLOP/s (M=4096) and decode GEMV HBM GB/s, 1 MI355X"
 
 
@@ -370,6 +371,26 @@ def extras(torch, qlora, workloads, dev, to_dev, L, M, r):
     del copies
 
     res["double_quant_off"] = extras_nodq(torch, qlora, workloads, dev, to_dev, L, M, r, ev)
+
+    # LoRA merge for deployment (qlora_merge) of the 7 layers: N*K*r fp32 FMAs (VALU-bound) and
+    # codes + scales + A + B in, the bf16 merged weight out
+    mo = [torch.empty((d["N"], d["K"]), dtype=torch.bfloat16, device=dev) for d in L]
+    for d, o in zip(L, mo):
+        qlora.merge(d["w"], d["A"], d["B"], workloads.CONFIGS[4]["alpha"], out=o)
+    a, b = ev(), ev()
+    a.record()
+    for _ in range(reps):
+        for d, o in zip(L, mo):
+            qlora.merge(d["w"], d["A"], d["B"], workloads.CONFIGS[4]["alpha"], out=o)
+    b.record()
+    torch.cuda.synchronize()
+    m_ms = a.elapsed_time(b) / reps
+    m_bytes = sum(sum(qlora.sizes(d["N"], d["K"])) + 2 * r * (d["N"] + d["K"]) + 2 * d["N"] * d["K"] for d in L)
+    m_fma = sum(d["N"] * d["K"] * r for d in L)
+    res["merge"] = {"ms": round(m_ms, 4), "GB/s": round(m_bytes / (m_ms * 1e-3) / 1e9, 1),
+                    "tera_fma_per_s": round(m_fma / (m_ms * 1e-3) / 1e12, 2),
+                    "frac_of_fp32_vector_fma_peak": round(m_fma / (m_ms * 1e-3) / (FP32_VECTOR_PEAK_TFS * 1e12 / 2), 4)}
+    del mo
 
     # context: dense bf16 torch.matmul (hipBLASLt) on the same shapes, forward base product only
     tot_f, tot_ms = 0, 0.0

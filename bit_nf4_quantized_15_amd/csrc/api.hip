@@ -115,6 +115,16 @@ qlora_status qlora_dequantize(const qlora_nf4* w, uint16_t* out, void* stream) {
     return launch_dequantize(w->codes, w->q8, w->a2, w->n * w->k / kBlock, out, (hipStream_t)stream);
 }
 
+qlora_status qlora_merge(const qlora_nf4* w, const uint16_t* A, const uint16_t* B, int r, float alpha,
+                         uint16_t* out, void* stream) {
+    qlora_status st = check_state(w);
+    if (st != QLORA_OK) return st;
+    if (!A || !B || !out || r < 1 || r > 128 || !std::isfinite(alpha)) return QLORA_ERR_INVALID_ARG;
+    if (!aligned16(A) || !aligned16(B) || !aligned16(out)) return QLORA_ERR_MISALIGNED;
+    const float s = alpha / (float)r;
+    return launch_merge(w->codes, w->q8, w->a2, A, B, r, s, out, (int)w->n, (int)w->k, (hipStream_t)stream);
+}
+
 size_t qlora_fwd_workspace(int64_t M, int64_t N, int64_t K, int r) {
     if (bad_dims(M, N, K, r) || M == 0 || K % kBlock) return 0;
     return fwd_ws(M, N, K, r).total;

@@ -40,6 +40,7 @@ def _load():
         "qlora_nf4_sizes_nodq": (ctypes.c_int, [c_i64, c_i64, ctypes.POINTER(c_sz), ctypes.POINTER(c_sz)]),
         "qlora_quantize": (ctypes.c_int, [c_vp, c_i64, c_i64, P, c_vp]),
         "qlora_dequantize": (ctypes.c_int, [P, c_vp, c_vp]),
+        "qlora_merge": (ctypes.c_int, [P, c_vp, c_vp, ctypes.c_int, ctypes.c_float, c_vp, c_vp]),
         "qlora_fwd_workspace": (c_sz, [c_i64, c_i64, c_i64, ctypes.c_int]),
         "qlora_linear_fwd": (ctypes.c_int, [P, c_vp, c_i64, c_vp, c_vp, ctypes.c_int, ctypes.c_float,
                                             c_vp, c_vp, c_vp, c_sz, c_vp]),
@@ -151,6 +152,19 @@ def dequantize(w, out=None):
     _dev(o, torch.bfloat16, "out", (w.N, w.K))
     st = w.state()
     _check(lib.qlora_dequantize(ctypes.byref(st), _ptr(o), _stream()), "qlora_dequantize")
+    return o
+
+
+def merge(w, A, B, alpha, out=None):
+    """LoRA merge for deployment (qlora_merge): bf16 [N, K] = w_hat + (alpha/r) (A B)^T.
+    Re-quantize with quantize(out)."""
+    K, r = A.shape
+    _dev(A, torch.bfloat16, "A", (w.K, r))
+    _dev(B, torch.bfloat16, "B", (r, w.N))
+    o = torch.empty((w.N, w.K), dtype=torch.bfloat16, device=A.device) if out is None else out
+    _dev(o, torch.bfloat16, "out", (w.N, w.K))
+    st = w.state()
+    _check(lib.qlora_merge(ctypes.byref(st), _ptr(A), _ptr(B), r, float(alpha), _ptr(o), _stream()), "qlora_merge")
     return o
 
 

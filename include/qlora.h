@@ -106,6 +106,18 @@ qlora_status qlora_quantize(const uint16_t* W, int64_t N, int64_t K, const qlora
  * For tests and export only: the linear layer never materialises W. */
 qlora_status qlora_dequantize(const qlora_nf4* w, uint16_t* out, void* stream);
 
+/* LoRA merge for deployment ("LoRA, QLoRA, QA-LoRA explained", section 2:
+ * W_eff = dequant(W4) + (alpha/r) A B; "bitsandbytes deep dive", section 12.10:
+ * merge in higher precision, re-quantize afterwards if a 4-bit model is wanted,
+ * which adds error of its own).  In the stored layout, bf16 out [N, K]:
+ *   out[n, k] = RNE_bf16( fl32( w_hat[n, k] + fl32( fl32(alpha/r) * acc[n, k] ) ) ),
+ *   acc[n, k] = fp32 sum over j = 0 .. r-1, in that order, of A[k, j] * B[j, n],
+ * w_hat as qlora_dequantize.  w: either scale layout; A [K, r] and B [r, N] bf16.
+ * Re-quantize with qlora_quantize(out, ...).  Errors: null pointer, r outside
+ * 1..128 or non-finite alpha -> INVALID_ARG; unaligned pointer -> MISALIGNED. */
+qlora_status qlora_merge(const qlora_nf4* w, const uint16_t* A, const uint16_t* B, int r, float alpha,
+                         uint16_t* out, void* stream);
+
 /* Workspace bytes qlora_linear_fwd needs for these sizes (0 if none). */
 size_t qlora_fwd_workspace(int64_t M, int64_t N, int64_t K, int r);
 

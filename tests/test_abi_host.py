@@ -91,6 +91,19 @@ def test_quantize_argument_errors(q):
     assert q.lib.qlora_dequantize(ctypes.byref(st), FAKE + 4, None) == MISALIGNED
 
 
+def test_merge_argument_errors(q):
+    st = ctypes.byref(_state(q, n=64, k=128))
+    f = q.lib.qlora_merge
+    # (w, A, B, r, alpha, out, stream)
+    assert f(st, FAKE, FAKE, 0, 16.0, FAKE, None) == INVALID
+    assert f(st, FAKE, FAKE, 129, 16.0, FAKE, None) == INVALID
+    assert f(st, FAKE, FAKE, 8, float("inf"), FAKE, None) == INVALID
+    assert f(st, None, FAKE, 8, 16.0, FAKE, None) == INVALID
+    assert f(st, FAKE, FAKE, 8, 16.0, None, None) == INVALID
+    assert f(st, FAKE, FAKE + 2, 8, 16.0, FAKE, None) == MISALIGNED
+    assert f(ctypes.byref(_state(q, n=64, k=100)), FAKE, FAKE, 8, 16.0, FAKE, None) == SHAPE
+
+
 def test_linear_argument_errors(q):
     st = ctypes.byref(_state(q, n=64, k=128))
     fwd = q.lib.qlora_linear_fwd
