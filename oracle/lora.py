@@ -16,6 +16,10 @@ there is no dW; by the chain rule through the same graph
     dB = t^T dy     with t = s x A
 No bias, no dropout (no workload asks for them).  Every product is a float64
 numpy matmul of the exact bf16 input values.
+
+The QA-LoRA pooled branch (same page, sections 3-5) replaces x A by pool(x) A,
+pool averaging each group of g consecutive input columns, A [K/g, r]:
+    y = x W_hat + s pool(x) A B
 """
 import numpy as np
 
@@ -81,3 +85,43 @@ def rel_err(got, ref):
     if den == 0.0:
         return 0.0 if num == 0.0 else float("inf")
     return float(num / den)
+
+
+# ----------------------------------------------------------------------------
+# QA-LoRA pooled branch ("LoRA, QLoRA, QA-LoRA explained", sections 3-5)
+# ----------------------------------------------------------------------------
+def pool(x, g):
+    """pool(x): the mean of each group of g consecutive input columns, [M, K] -> [M, K/g] (section 3)."""
+    x = np.asarray(x, np.float64)
+    M, K = x.shape
+    assert K % g == 0
+    return x.reshape(M, K // g, g).mean(axis=2)
+
+
+def pooled_fwd(x, W_hat_nk, A, B, alpha, r, g):
+    """y = x W_hat + s pool(x) A B with A [K/g, r] (section 3: y = x W + pool(x) A B; s = alpha/r as in
+    the plain branch).  Returns (y [M, N], t = s pool(x) A [M, r])."""
+    x = np.asarray(x, np.float64)
+    s = lora_scale(alpha, r)
+    t = s * (pool(x, g) @ np.asarray(A, np.float64))
+    y = x @ np.asarray(W_hat_nk, np.float64).T + t @ np.asarray(B, np.float64)
+    return y, t
+
+
+def pooled_bwd(x, W_hat_nk, A, B, alpha, r, g, dy):
+    """Gradients of <dy, y> for the pooled branch (chain rule through pool, which is linear):
+        u  = s dy B^T
+        dx = dy W_hat^T + unpool(u A^T) / g    (each group's g columns get the group's value / g)
+        dA = pool(x)^T u,   dB = t^T dy
+    Returns (dx [M, K], dA [K/g, r], dB [r, N])."""
+    x = np.asarray(x, np.float64)
+    dy = np.asarray(dy, np.float64)
+    A = np.asarray(A, np.float64)
+    B = np.asarray(B, np.float64)
+    s = lora_scale(alpha, r)
+    u = s * (dy @ B.T)
+    dx = dy @ np.asarray(W_hat_nk, np.float64) + np.repeat(u @ A.T, g, axis=1) / g
+    px = pool(x, g)
+    dA = px.T @ u
+    dB = (s * (px @ A)).T @ dy
+    return dx, dA, dB

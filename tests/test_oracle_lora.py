@@ -6,7 +6,9 @@
 * the merged-weight identity y = x (W_hat + s A B) from the same page;
 * adjoint identities (y is linear in each of x, A, B separately) and central
   finite differences, on non-square shapes so that a transposed operand or a
-  dropped term cannot pass.
+  dropped term cannot pass;
+* the QA-LoRA pooled branch: the page's printed forward and per-column group
+  updates, g = 1 reducing to plain LoRA, central differences of its backward.
 """
 import json
 import os
@@ -125,3 +127,53 @@ def test_rel_err():
     assert lora.rel_err(np.ones(4), np.ones(4)) == 0.0
     assert np.isclose(lora.rel_err(np.array([3.0, 4.0]) * 1.01, np.array([3.0, 4.0])), 0.01)
     assert lora.rel_err(np.zeros(3), np.zeros(3)) == 0.0
+
+
+# --------------------------------------------------------------------------- QA-LoRA pooled branch
+def test_pooled_fwd_printed_example():
+    """Section 4's numbers through the pooled layer (zero base weight, s = 1): y = [0.475, -0.95];
+    section 5's per-column updates: group 1's columns get [0.1, -0.2], group 2's [0.025, -0.05]."""
+    ex = _g()["qa_lora_pooled_branch"]
+    x = np.array([ex["x"]])
+    A = np.array(ex["A"]); B = np.array(ex["B"])
+    g = ex["group_size"]
+    y, t = lora.pooled_fwd(x, np.zeros((2, 4)), A, B, alpha=1.0, r=1, g=g)
+    assert np.allclose(y[0], ex["branch"], atol=1e-15) and np.isclose(t[0, 0], ex["xA"])
+    # x e_k for a unit input column k gives column k's weight update
+    upd = np.stack([lora.pooled_fwd(np.eye(4)[k:k + 1], np.zeros((2, 4)), A, B, 1.0, 1, g)[0][0] for k in range(4)])
+    assert np.allclose(upd, [[0.1, -0.2], [0.1, -0.2], [0.025, -0.05], [0.025, -0.05]], atol=1e-15)
+
+
+def test_pooled_group_one_is_plain_lora():
+    Wh, x, A, B, dy = _small(7, K=128)
+    y1, t1 = lora.pooled_fwd(x, Wh, A, B, 16, 4, g=1)
+    y2, t2 = lora.linear_fwd(x, Wh, A, B, 16, 4)
+    assert np.allclose(y1, y2, rtol=1e-13, atol=1e-15) and np.allclose(t1, t2, rtol=1e-13, atol=1e-15)
+    for a, b in zip(lora.pooled_bwd(x, Wh, A, B, 16, 4, 1, dy), lora.linear_bwd(x, Wh, A, B, 16, 4, dy)):
+        assert np.allclose(a, b, rtol=1e-12, atol=1e-14)
+
+
+def test_pooled_backward_adjoint_and_differences():
+    """<dy, y> is linear in x, A and B separately; the pooled gradients are checked against central
+    differences on a non-square shape with g = 4 (a dropped 1/g or an unpooled dA would fail)."""
+    rng = np.random.default_rng(21)
+    M, N, K, r, g, alpha = 3, 20, 32, 3, 4, 6.0
+    Wh = rng.standard_normal((N, K)) * 0.02
+    x = rng.standard_normal((M, K)); A = rng.standard_normal((K // g, r)); B = rng.standard_normal((r, N)) * 0.1
+    dy = rng.standard_normal((M, N))
+    dx, dA, dB = lora.pooled_bwd(x, Wh, A, B, alpha, r, g, dy)
+    f = lambda x_, A_, B_: float(np.sum(dy * lora.pooled_fwd(x_, Wh, A_, B_, alpha, r, g)[0]))
+    h = 1e-6
+    for arr, grad, which in ((x, dx, 0), (A, dA, 1), (B, dB, 2)):
+        for idx in [(0, 0), (arr.shape[0] - 1, arr.shape[1] - 1), (1 % arr.shape[0], 2 % arr.shape[1])]:
+            p = arr.copy(); p[idx] += h
+            m = arr.copy(); m[idx] -= h
+            args_p = [x, A, B]; args_p[which] = p
+            args_m = [x, A, B]; args_m[which] = m
+            num = (f(*args_p) - f(*args_m)) / (2 * h)
+            assert abs(num - grad[idx]) <= 1e-6 * max(1.0, abs(num)), (which, idx)
+    # linear in x: the forward on x1 + x2 is the sum of the forwards
+    x2 = rng.standard_normal((M, K))
+    ya = lora.pooled_fwd(x + x2, Wh, A, B, alpha, r, g)[0]
+    yb = lora.pooled_fwd(x, Wh, A, B, alpha, r, g)[0] + lora.pooled_fwd(x2, Wh, A, B, alpha, r, g)[0]
+    assert np.allclose(ya, yb, rtol=1e-12, atol=1e-13)
