@@ -332,17 +332,20 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
             raw_buffer_load_lds(crs, d, 16, (int)(cvoff[i] + boff), 0, 0, 0);
         }
     };
-    // ---- block scales: thread tid, tile row tid, the 2 blocks of a super-step
-    // (an even first block, so both lie in one group of 256 blocks).  Without
-    // double quantization a2 holds the blocks' fp32 absmax itself.
+    // ---- block scales: thread tid, tile row tid, the 2 blocks of a super-step.
+    // With an even block count per row both blocks have an even-odd flat index
+    // pair, so they lie in one group of 256 blocks; with an odd count the pair
+    // can straddle a group boundary and each block takes its own group's scale.
+    // Without double quantization a2 holds the blocks' fp32 absmax itself.
     const int srow = min(n0 + tid, N - 1);
     const int64_t sblk = (int64_t)srow * KB;
     struct Sc {
         uint32_t q;  // 8-bit scale codes of the 2 blocks, block j in byte j (DQ off: block 0's scale bits)
-        float g;     // second-level scale of their group (DQ off: block 1's scale)
+        float g;     // second-level scale of block 0's group (DQ off: block 1's scale)
+        float g1;    // second-level scale of block 1's group (odd block counts only)
     };
     // loads per load_scales call, all issued after the step's x tile
-    constexpr int kScaleLoads = DQ ? (Q8DW ? 2 : 3) : (Q8DW ? 1 : 2);
+    constexpr int kScaleLoads = DQ ? (Q8DW ? 2 : 4) : (Q8DW ? 1 : 2);
     auto load_scales = [&](int S, Sc& sc) __attribute__((always_inline)) {
         const int b0 = kSup * S;
         if (!DQ) {
@@ -358,18 +361,21 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
         }
         if (Q8DW) {  // blocks per row even: the 2 codes are one aligned 16-bit word
             sc.q = *reinterpret_cast<const uint16_t*>(q8 + sblk + b0);
+            sc.g = a2[(sblk + b0) >> 8];
+            sc.g1 = sc.g;
         } else {
-            sc.q = (uint32_t)q8[sblk + b0] | ((uint32_t)q8[sblk + min(b0 + 1, KB - 1)] << 8);
+            const int64_t b1 = sblk + min(b0 + 1, KB - 1);
+            sc.q = (uint32_t)q8[sblk + b0] | ((uint32_t)q8[b1] << 8);
+            sc.g = a2[(sblk + b0) >> 8];
+            sc.g1 = a2[b1 >> 8];
         }
-        sc.g = a2[(sblk + b0) >> 8];
     };
     auto make_scales = [&](const Sc& sc, float* dst, int S) __attribute__((always_inline)) {
         const int b0 = kSup * S;
         f32x2_t ah;
         if (DQ) {
-            const float st = scale_step(sc.g);
-            ah[0] = st * (float)(sc.q & 0xFFu);
-            ah[1] = b0 + 1 < KB ? st * (float)((sc.q >> 8) & 0xFFu) : 0.0f;
+            ah[0] = scale_step(sc.g) * (float)(sc.q & 0xFFu);
+            ah[1] = b0 + 1 < KB ? scale_step(sc.g1) * (float)((sc.q >> 8) & 0xFFu) : 0.0f;
         } else {
             ah[0] = __builtin_bit_cast(float, sc.q);
             ah[1] = b0 + 1 < KB ? sc.g : 0.0f;

@@ -74,6 +74,27 @@ def test_ragged_shapes(q, M, N, K, r):
     _check_full(q, W, x, A, B, dy, 2.0 * r, f"ragged {M}x{N}x{K} r{r}")
 
 
+@pytest.mark.parametrize("M,N,K,r", [(64, 72, 64 * 43, 16), (9, 260, 320, 8)])
+def test_groups_straddling_a_block_pair(q, M, N, K, r):
+    """Odd blocks per row: a pair of adjacent blocks of one row can fall into two
+    groups of 256 first-level scales (deep dive 7.2), each with its own
+    second-level scale.  Weights in every other group are 100x larger, so a block
+    dequantized with its neighbour group's scale is off by 100x."""
+    seed = 7 * M + N + K
+    W = workloads.custom(seed, (N, K), 0.02)
+    KB = K // 64
+    flat = np.arange(N)[:, None] * KB + np.arange(KB)[None, :]          # flat block index
+    big = np.repeat((flat >> 8) & 1, 64, axis=1).astype(bool)
+    Wf = bf16.to_f64(W)
+    Wf[big] *= 100.0
+    W = bf16.from_f32_rne(Wf.astype(np.float32))
+    x = workloads.custom(seed + 1, (M, K), 1.0)
+    A = workloads.custom(seed + 2, (K, r), float(1 / np.sqrt(r)))
+    B = workloads.custom(seed + 3, (r, N), 0.01)
+    dy = workloads.custom(seed + 4, (M, N), 1.0)
+    _check_full(q, W, x, A, B, dy, 2.0 * r, f"straddle {M}x{N}x{K} r{r}")
+
+
 def test_recomputed_t_and_no_dx(q):
     M, N, K, r = 40, 192, 256, 16
     W = workloads.custom(1, (N, K), 0.02); x = workloads.custom(2, (M, K), 1.0)
