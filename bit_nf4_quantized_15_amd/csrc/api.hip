@@ -231,4 +231,55 @@ qlora_status qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, int64_t M, 
     return launch_tn(dy, t, reinterpret_cast<float*>(at(ws, L.pb)), dB, (int)M, (int)N, r, 1, N, s);
 }
 
+// ---- QA-LoRA pooled branch: A [K/g, r]; the plain path runs on A~ = expand(A) / g
+static bool bad_group(int64_t K, int g) { return g < 1 || (g & (g - 1)) != 0 || K % g != 0; }
+
+size_t qlora_pooled_fwd_workspace(int64_t M, int64_t N, int64_t K, int r, int g) {
+    if (bad_dims(M, N, K, r) || M == 0 || K % kBlock || bad_group(K, g)) return 0;
+    return align256((size_t)K * r * 2) + fwd_ws(M, N, K, r).total;
+}
+
+size_t qlora_pooled_bwd_workspace(int64_t M, int64_t N, int64_t K, int r, int g) {
+    if (bad_dims(M, N, K, r) || K % kBlock || bad_group(K, g)) return 0;
+    return align256((size_t)K * r * 2) + align256((size_t)K * r * 4) + bwd_ws(std::max<int64_t>(M, 1), N, K, r).total;
+}
+
+qlora_status qlora_pooled_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
+                              int r, int g, float alpha, uint16_t* y, uint16_t* t_out, void* ws, size_t ws_bytes,
+                              void* stream) {
+    qlora_status st = check_state(w);
+    if (st != QLORA_OK) return st;
+    if (bad_dims(M, w->n, w->k, r) || bad_group(w->k, g) || !std::isfinite(alpha)) return QLORA_ERR_INVALID_ARG;
+    if (M == 0) return QLORA_OK;
+    if (!A) return QLORA_ERR_INVALID_ARG;
+    if (!aligned16(A)) return QLORA_ERR_MISALIGNED;
+    const size_t head = align256((size_t)w->k * r * 2);
+    if (!ws || ws_bytes < head) return QLORA_ERR_WORKSPACE;
+    if (!aligned16(ws)) return QLORA_ERR_MISALIGNED;
+    uint16_t* Ax = reinterpret_cast<uint16_t*>(ws);
+    if ((st = launch_expand_pooled(A, (int)w->k, r, g, Ax, (hipStream_t)stream)) != QLORA_OK) return st;
+    return qlora_linear_fwd(w, x, M, Ax, B, r, alpha, y, t_out, at(ws, head), ws_bytes - head, stream);
+}
+
+qlora_status qlora_pooled_bwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
+                              int r, int g, float alpha, const uint16_t* t, const uint16_t* dy, uint16_t* dx, float* dA,
+                              float* dB, void* ws, size_t ws_bytes, void* stream) {
+    qlora_status st = check_state(w);
+    if (st != QLORA_OK) return st;
+    if (bad_dims(M, w->n, w->k, r) || bad_group(w->k, g) || !std::isfinite(alpha)) return QLORA_ERR_INVALID_ARG;
+    if (!A || !dA) return QLORA_ERR_INVALID_ARG;
+    if (!aligned16(A) || !aligned16(dA)) return QLORA_ERR_MISALIGNED;
+    const size_t ha = align256((size_t)w->k * r * 2), hd = align256((size_t)w->k * r * 4);
+    if (!ws || ws_bytes < ha + hd) return QLORA_ERR_WORKSPACE;
+    if (!aligned16(ws)) return QLORA_ERR_MISALIGNED;
+    hipStream_t s = (hipStream_t)stream;
+    uint16_t* Ax = reinterpret_cast<uint16_t*>(ws);
+    float* dAx = reinterpret_cast<float*>(at(ws, ha));
+    if ((st = launch_expand_pooled(A, (int)w->k, r, g, Ax, s)) != QLORA_OK) return st;
+    if ((st = qlora_linear_bwd(w, x, M, Ax, B, r, alpha, t, dy, dx, dAx, dB, at(ws, ha + hd), ws_bytes - ha - hd,
+                               stream)) != QLORA_OK)
+        return st;
+    return launch_pool_rows(dAx, (int)w->k, r, g, dA, s);
+}
+
 }  // extern "C"

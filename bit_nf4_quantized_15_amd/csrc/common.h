@@ -82,5 +82,7 @@ qlora_status launch_nt(const uint16_t* X, const uint16_t* Y, bool y_natural, flo
 qlora_status launch_tn(const uint16_t* X, const uint16_t* S, float* part, float* out, int M, int D, int r,
                        int64_t ld_d, int64_t ld_j, hipStream_t s);
 qlora_status launch_fill(float* out, int64_t count, float v, hipStream_t s);
+qlora_status launch_expand_pooled(const uint16_t* A, int K, int r, int g, uint16_t* out, hipStream_t s);
+qlora_status launch_pool_rows(const float* in, int K, int r, int g, float* out, hipStream_t s);
 
 }  // namespace qlora

@@ -367,6 +367,30 @@ __global__ __launch_bounds__(256) void reduce_f32_kernel(const float* __restrict
     }
 }
 
+// QA-LoRA pooled branch ("LoRA, QLoRA, QA-LoRA explained", sections 3-5):
+// pool(x) A = x A~ with A~[k, j] = A[k / g, j] / g, exact in bf16 for g a power
+// of two (a shift of the exponent) unless it underflows, so the plain kernels run on A~; the
+// gradient of A sums each group of g rows of the gradient of A~:
+// dA[i, j] = (1/g) sum_{q < g} dA~[g i + q, j], q ascending, in fp32.
+__global__ void expand_pooled_kernel(const uint16_t* __restrict__ A, int64_t count, int r, int g_log2,
+                                     uint16_t* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= count) return;
+    const int64_t k = i / r, j = i - k * r;
+    const float v = bf16_bits_to_f32(A[(k >> g_log2) * r + j]) * __uint_as_float((uint32_t)(127 - g_log2) << 23);
+    out[i] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+}
+
+__global__ void pool_rows_kernel(const float* __restrict__ in, int64_t count, int r, int g, int g_log2,
+                                 float* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // output element [K/g, r]
+    if (i >= count) return;
+    const int64_t p = i / r, j = i - p * r;
+    float acc = 0.0f;
+    for (int q = 0; q < g; ++q) acc += in[(p * g + q) * r + j];
+    out[i] = acc * __uint_as_float((uint32_t)(127 - g_log2) << 23);
+}
+
 __global__ void fill_f32_kernel(float* __restrict__ out, int64_t count, float v) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < count) out[i] = v;
@@ -432,6 +456,20 @@ qlora_status launch_tn(const uint16_t* X, const uint16_t* S, float* part, float*
     const int64_t count = (int64_t)D * r;
     hipLaunchKernelGGL(reduce_f32_kernel, dim3(blocks_for(count, 64)), dim3(256), 0, s, part, sp.splits, D, r, ld_d,
                        ld_j, out);
+    return launch_status();
+}
+
+qlora_status launch_expand_pooled(const uint16_t* A, int K, int r, int g, uint16_t* out, hipStream_t s) {
+    const int64_t count = (int64_t)K * r;
+    const int g_log2 = __builtin_ctz((unsigned)g);
+    hipLaunchKernelGGL(expand_pooled_kernel, dim3(blocks_for(count, 256)), dim3(256), 0, s, A, count, r, g_log2, out);
+    return launch_status();
+}
+
+qlora_status launch_pool_rows(const float* in, int K, int r, int g, float* out, hipStream_t s) {
+    const int64_t count = (int64_t)(K / g) * r;
+    const int g_log2 = __builtin_ctz((unsigned)g);
+    hipLaunchKernelGGL(pool_rows_kernel, dim3(blocks_for(count, 256)), dim3(256), 0, s, in, count, r, g, g_log2, out);
     return launch_status();
 }
 

@@ -48,6 +48,12 @@ def _load():
         "qlora_lora_down": (ctypes.c_int, [c_vp, c_i64, c_i64, c_vp, ctypes.c_int, ctypes.c_float, c_vp, c_vp,
                                            c_sz, c_vp]),
         "qlora_fused_gemm_fwd": (ctypes.c_int, [P, c_vp, c_i64, c_vp, c_vp, ctypes.c_int, c_vp, c_vp]),
+        "qlora_pooled_fwd_workspace": (c_sz, [c_i64, c_i64, c_i64, ctypes.c_int, ctypes.c_int]),
+        "qlora_pooled_fwd": (ctypes.c_int, [P, c_vp, c_i64, c_vp, c_vp, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                            c_vp, c_vp, c_vp, c_sz, c_vp]),
+        "qlora_pooled_bwd_workspace": (c_sz, [c_i64, c_i64, c_i64, ctypes.c_int, ctypes.c_int]),
+        "qlora_pooled_bwd": (ctypes.c_int, [P, c_vp, c_i64, c_vp, c_vp, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                            c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
         "qlora_bwd_workspace": (c_sz, [c_i64, c_i64, c_i64, ctypes.c_int]),
         "qlora_linear_bwd": (ctypes.c_int, [P, c_vp, c_i64, c_vp, c_vp, ctypes.c_int, ctypes.c_float,
                                             c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
@@ -252,6 +258,42 @@ def linear_bwd(w, x, A, B, alpha, dy, t=None, need_dx=True, dx=None, dA=None, dB
                                 _ptr(dy), _ptr(dx) if need_dx else None, _ptr(dA), _ptr(dB), _ptr(wsb), wsn,
                                 _stream()), "qlora_linear_bwd")
     return (dx if need_dx else None), dA, dB
+
+
+def pooled_fwd(w, x, A, B, alpha, g, y=None, t=None, ws=None):
+    """QA-LoRA pooled forward (qlora_pooled_fwd): y = x W_hat + s pool(x) A B, A [K/g, r]. Returns (y, t)."""
+    M, K = x.shape
+    _, r = A.shape
+    _dev(x, torch.bfloat16, "x", (M, w.K))
+    _dev(A, torch.bfloat16, "A", (w.K // g, r))
+    _dev(B, torch.bfloat16, "B", (r, w.N))
+    y = torch.empty((M, w.N), dtype=torch.bfloat16, device=x.device) if y is None else _dev(y, torch.bfloat16, "y", (M, w.N))
+    t = torch.empty((M, r), dtype=torch.bfloat16, device=x.device) if t is None else _dev(t, torch.bfloat16, "t", (M, r))
+    wsb, wsn = _ws(int(lib.qlora_pooled_fwd_workspace(M, w.N, w.K, r, g)), x.device, ws)
+    st = w.state()
+    _check(lib.qlora_pooled_fwd(ctypes.byref(st), _ptr(x), M, _ptr(A), _ptr(B), r, g, float(alpha), _ptr(y), _ptr(t),
+                                _ptr(wsb), wsn, _stream()), "qlora_pooled_fwd")
+    return y, t
+
+
+def pooled_bwd(w, x, A, B, alpha, g, dy, t=None, need_dx=True, ws=None):
+    """QA-LoRA pooled backward (qlora_pooled_bwd). Returns (dx or None, dA [K/g, r] fp32, dB [r, N] fp32)."""
+    M, K = x.shape
+    _, r = A.shape
+    _dev(x, torch.bfloat16, "x", (M, w.K))
+    _dev(A, torch.bfloat16, "A", (w.K // g, r))
+    _dev(B, torch.bfloat16, "B", (r, w.N))
+    _dev(dy, torch.bfloat16, "dy", (M, w.N))
+    if t is not None:
+        _dev(t, torch.bfloat16, "t", (M, r))
+    dx = torch.empty((M, w.K), dtype=torch.bfloat16, device=x.device) if need_dx else None
+    dA = torch.empty((w.K // g, r), dtype=torch.float32, device=x.device)
+    dB = torch.empty((r, w.N), dtype=torch.float32, device=x.device)
+    wsb, wsn = _ws(int(lib.qlora_pooled_bwd_workspace(M, w.N, w.K, r, g)), x.device, ws)
+    st = w.state()
+    _check(lib.qlora_pooled_bwd(ctypes.byref(st), _ptr(x), M, _ptr(A), _ptr(B), r, g, float(alpha), _ptr(t), _ptr(dy),
+                                _ptr(dx), _ptr(dA), _ptr(dB), _ptr(wsb), wsn, _stream()), "qlora_pooled_bwd")
+    return dx, dA, dB
 
 
 def declared_symbols():

@@ -167,6 +167,28 @@ qlora_status qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, int64_t M, 
                               const uint16_t* dy, uint16_t* dx, float* dA, float* dB, void* ws,
                               size_t ws_bytes, void* stream);
 
+/* QA-LoRA pooled branch ("LoRA, QLoRA, QA-LoRA explained", sections 3-5): the
+ * LoRA input is pool(x), the mean of each group of g consecutive input
+ * columns, and A is [K/g, r]:
+ *   y = x W_hat + s pool(x) A B,   t = s pool(x) A,   s = alpha / r.
+ * Backward: u = s dy B^T, dx = dy W_hat^T + (u A^T repeated over each group) / g,
+ * dA = pool(x)^T u [K/g, r] (fp32), dB = t^T dy.  g must be a power of two
+ * dividing K (g = 1 is the plain layer).  Implementation: pool(x) A = x A~ with
+ * A~[k, j] = A[k/g, j] / g, exact in bf16 unless it underflows, so the plain
+ * kernels run on A~ (kept in the workspace); dA sums each group of g rows of
+ * the gradient of A~, in fp32 in row order.  Arguments and errors as qlora_linear_fwd / _bwd, plus
+ * a g that is not a power of two dividing K -> INVALID_ARG.  The workspace
+ * queries return 0 for invalid sizes. */
+size_t qlora_pooled_fwd_workspace(int64_t M, int64_t N, int64_t K, int r, int g);
+qlora_status qlora_pooled_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uint16_t* A,
+                              const uint16_t* B, int r, int g, float alpha, uint16_t* y,
+                              uint16_t* t_out, void* ws, size_t ws_bytes, void* stream);
+size_t qlora_pooled_bwd_workspace(int64_t M, int64_t N, int64_t K, int r, int g);
+qlora_status qlora_pooled_bwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uint16_t* A,
+                              const uint16_t* B, int r, int g, float alpha, const uint16_t* t,
+                              const uint16_t* dy, uint16_t* dx, float* dA, float* dB, void* ws,
+                              size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -104,6 +104,21 @@ def test_merge_argument_errors(q):
     assert f(ctypes.byref(_state(q, n=64, k=100)), FAKE, FAKE, 8, 16.0, FAKE, None) == SHAPE
 
 
+def test_pooled_argument_errors(q):
+    st = ctypes.byref(_state(q, n=64, k=128))
+    assert q.lib.qlora_pooled_fwd_workspace(8, 64, 128, 8, 3) == 0          # g not a power of two
+    assert q.lib.qlora_pooled_fwd_workspace(8, 64, 128, 8, 256) == 0        # g does not divide K
+    need = q.lib.qlora_pooled_fwd_workspace(8, 64, 128, 8, 32)
+    assert need >= 128 * 8 * 2 + q.fwd_workspace(8, 64, 128, 8)
+    f = q.lib.qlora_pooled_fwd
+    # (w, x, M, A, B, r, g, alpha, y, t_out, ws, ws_bytes, stream)
+    assert f(st, FAKE, 8, FAKE, FAKE, 8, 3, 16.0, FAKE, None, FAKE, need, None) == INVALID
+    assert f(st, FAKE, 8, None, FAKE, 8, 32, 16.0, FAKE, None, FAKE, need, None) == INVALID
+    assert f(st, FAKE, 8, FAKE + 2, FAKE, 8, 32, 16.0, FAKE, None, FAKE, need, None) == MISALIGNED
+    assert f(st, FAKE, 8, FAKE, FAKE, 8, 32, 16.0, FAKE, None, FAKE, 100, None) == WORKSPACE
+    assert q.lib.qlora_pooled_bwd_workspace(8, 64, 128, 8, 6) == 0
+
+
 def test_linear_argument_errors(q):
     st = ctypes.byref(_state(q, n=64, k=128))
     fwd = q.lib.qlora_linear_fwd
