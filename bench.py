@@ -371,6 +371,7 @@ def extras(torch, qlora, workloads, dev, to_dev, L, M, r):
     del copies
 
     res["double_quant_off"] = extras_nodq(torch, qlora, workloads, dev, to_dev, L, M, r, ev)
+    res["qa_lora_pooled_g64"] = extras_pooled(torch, qlora, workloads, dev, to_dev, L, M, r, ev, 64)
 
     # LoRA merge for deployment (qlora_merge) of the 7 layers: N*K*r fp32 FMAs (VALU-bound) and
     # codes + scales + A + B in, the bf16 merged weight out
@@ -474,6 +475,40 @@ def extras_nodq(torch, qlora, workloads, dev, to_dev, L, M, r, ev):
     res["decode_gemv_q_proj_M=1"] = {"gemv_kernel_us": round(gemv_ms * 1e3, 2), "bytes_gemv_kernel": nb,
                                      "GB/s_gemv_kernel": round(nb / (gemv_ms * 1e-3) / 1e9, 1)}
     return res
+
+
+def extras_pooled(torch, qlora, workloads, dev, to_dev, L, M, r, ev, g):
+    """The whole quantize + fwd + bwd step of the 7 linears with the QA-LoRA pooled branch
+    ("LoRA, QLoRA, QA-LoRA explained", sections 3-5): A is [K/g, r] and the LoRA input is the mean
+    of each group of g columns of x.  Reported beside the plain step it replaces."""
+    alpha = workloads.CONFIGS[4]["alpha"]
+    Ap = [to_dev(workloads.custom(900 + i, (d["K"] // g, r), float(1 / np.sqrt(r)))) for i, d in enumerate(L)]
+    ws = torch.empty(max(max(qlora.lib.qlora_pooled_fwd_workspace(M, d["N"], d["K"], r, g),
+                              qlora.lib.qlora_pooled_bwd_workspace(M, d["N"], d["K"], r, g)) for d in L),
+                     dtype=torch.uint8, device=dev)
+    dAp = [torch.empty((d["K"] // g, r), dtype=torch.float32, device=dev) for d in L]
+
+    def step():
+        for d in L:
+            qlora.quantize(d["W"], out=d["w"])
+        for d, A in zip(L, Ap):
+            qlora.pooled_fwd(d["w"], d["x"], A, d["B"], alpha, g, y=d["y"], t=d["t"], ws=ws)
+        for d, A, dA in zip(L, Ap, dAp):
+            qlora.pooled_bwd(d["w"], d["x"], A, d["B"], alpha, g, d["dy"], t=d["t"], dx=d["dx"], dA=dA, dB=d["dB"],
+                             ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    a, b = ev(), ev()
+    a.record()
+    reps = 5
+    for _ in range(reps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    total_flops = sum(d["flops"]["fwd"] + d["flops"]["bwd"] for d in L)
+    return {"g": g, "step_ms": round(ms, 4), "TFLOP/s_plain_step_flops": round(total_flops / (ms * 1e-3) / 1e12, 2)}
 
 
 def cpu_baseline(workloads, cfg_id, total_flops, n_weights):

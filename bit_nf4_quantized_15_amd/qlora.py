@@ -276,7 +276,7 @@ def pooled_fwd(w, x, A, B, alpha, g, y=None, t=None, ws=None):
     return y, t
 
 
-def pooled_bwd(w, x, A, B, alpha, g, dy, t=None, need_dx=True, ws=None):
+def pooled_bwd(w, x, A, B, alpha, g, dy, t=None, need_dx=True, dx=None, dA=None, dB=None, ws=None):
     """QA-LoRA pooled backward (qlora_pooled_bwd). Returns (dx or None, dA [K/g, r] fp32, dB [r, N] fp32)."""
     M, K = x.shape
     _, r = A.shape
@@ -286,9 +286,15 @@ def pooled_bwd(w, x, A, B, alpha, g, dy, t=None, need_dx=True, ws=None):
     _dev(dy, torch.bfloat16, "dy", (M, w.N))
     if t is not None:
         _dev(t, torch.bfloat16, "t", (M, r))
-    dx = torch.empty((M, w.K), dtype=torch.bfloat16, device=x.device) if need_dx else None
-    dA = torch.empty((w.K // g, r), dtype=torch.float32, device=x.device)
-    dB = torch.empty((r, w.N), dtype=torch.float32, device=x.device)
+    if need_dx:
+        dx = torch.empty((M, w.K), dtype=torch.bfloat16, device=x.device) if dx is None else \
+            _dev(dx, torch.bfloat16, "dx", (M, w.K))
+    else:
+        dx = None
+    dA = torch.empty((w.K // g, r), dtype=torch.float32, device=x.device) if dA is None else \
+        _dev(dA, torch.float32, "dA", (w.K // g, r))
+    dB = torch.empty((r, w.N), dtype=torch.float32, device=x.device) if dB is None else \
+        _dev(dB, torch.float32, "dB", (r, w.N))
     wsb, wsn = _ws(int(lib.qlora_pooled_bwd_workspace(M, w.N, w.K, r, g)), x.device, ws)
     st = w.state()
     _check(lib.qlora_pooled_bwd(ctypes.byref(st), _ptr(x), M, _ptr(A), _ptr(B), r, g, float(alpha), _ptr(t), _ptr(dy),
