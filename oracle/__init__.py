@@ -28,4 +28,5 @@ Modules:
   brute  -- exact rational (fractions.Fraction) brute-force versions
   lora   -- fp64 forward / backward of the QLoRA linear
   merge  -- the LoRA merge W_eff = W_hat + (alpha/r) (A B)^T for deployment
+  fp4    -- the fp4 quant type: E2M1 4-bit float levels / 6 in the same scheme
 """

@@ -28,6 +28,25 @@ def nf4_codes_block(block, table, zero_code=7):
     return [argmin_lower(cs, w / a) for w in ws]
 
 
+def fp4_codes_block(block, table):
+    """FP4 codes of one block by the literal definition: the code whose level is nearest to u = w/a.
+
+    table: the 16 float32 levels in code order.  Among equally near codes the
+    lower level wins, and between the two zeros (+0, code 0 and -0, code 8)
+    code 0; an all-zero block is all code 0.
+    """
+    ws = [Fraction(float(w)) for w in block]
+    cs = [Fraction(float(c)) for c in table]
+    a = max(abs(w) for w in ws)
+    if a == 0:
+        return [0] * len(ws)
+    out = []
+    for w in ws:
+        u = w / a
+        out.append(min(range(16), key=lambda c: (abs(u - cs[c]), cs[c], c)))
+    return out
+
+
 def scale_code(a, A2):
     """q8 = argmin_k |a/A2 - k/255| over k = 0..255, ties to the lower k; A2 = 0 gives 0."""
     a, A2 = Fraction(float(a)), Fraction(float(A2))
