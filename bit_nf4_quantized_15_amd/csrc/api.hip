@@ -20,9 +20,12 @@ inline qlora_status check_state(const qlora_nf4* w) {
     if (w->n < 1 || w->k < 1) return QLORA_ERR_INVALID_ARG;
     if (w->k % kBlock) return QLORA_ERR_UNSUPPORTED_SHAPE;
     if (w->n > (int64_t(1) << 31) || w->k > (int64_t(1) << 31)) return QLORA_ERR_UNSUPPORTED_SHAPE;
+    if (w->quant_type != QLORA_QUANT_NF4 && w->quant_type != QLORA_QUANT_FP4) return QLORA_ERR_INVALID_ARG;
     if (!aligned16(w->codes) || (w->q8 && !aligned16(w->q8)) || !aligned16(w->a2)) return QLORA_ERR_MISALIGNED;
     return QLORA_OK;
 }
+
+inline int cb_of(const qlora_nf4* w) { return w->quant_type == QLORA_QUANT_FP4 ? kCbFp4 : kCbNf4; }
 
 inline bool bad_dims(int64_t M, int64_t N, int64_t K, int r) {
     return M < 0 || N < 1 || K < 1 || r < 1 || r > 128 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX;
@@ -65,7 +68,7 @@ inline uint8_t* at(void* ws, size_t off) { return static_cast<uint8_t*>(ws) + of
 
 extern "C" {
 
-int qlora_version(void) { return 100; }
+int qlora_version(void) { return 200; }
 
 const char* qlora_status_string(int status) {
     switch (status) {
@@ -104,7 +107,7 @@ qlora_status qlora_quantize(const uint16_t* W, int64_t N, int64_t K, const qlora
     if (st != QLORA_OK) return st;
     if (out->n != N || out->k != K) return QLORA_ERR_INVALID_ARG;
     if (!aligned16(W)) return QLORA_ERR_MISALIGNED;
-    return launch_quantize(W, N * K / kBlock, out->codes, out->q8, out->a2, (hipStream_t)stream);
+    return launch_quantize(W, N * K / kBlock, out->codes, out->q8, out->a2, cb_of(out), (hipStream_t)stream);
 }
 
 qlora_status qlora_dequantize(const qlora_nf4* w, uint16_t* out, void* stream) {
@@ -112,7 +115,7 @@ qlora_status qlora_dequantize(const qlora_nf4* w, uint16_t* out, void* stream) {
     if (st != QLORA_OK) return st;
     if (!out) return QLORA_ERR_INVALID_ARG;
     if (!aligned16(out)) return QLORA_ERR_MISALIGNED;
-    return launch_dequantize(w->codes, w->q8, w->a2, w->n * w->k / kBlock, out, (hipStream_t)stream);
+    return launch_dequantize(w->codes, w->q8, w->a2, cb_of(w), w->n * w->k / kBlock, out, (hipStream_t)stream);
 }
 
 qlora_status qlora_merge(const qlora_nf4* w, const uint16_t* A, const uint16_t* B, int r, float alpha,
@@ -122,7 +125,7 @@ qlora_status qlora_merge(const qlora_nf4* w, const uint16_t* A, const uint16_t* 
     if (!A || !B || !out || r < 1 || r > 128 || !std::isfinite(alpha)) return QLORA_ERR_INVALID_ARG;
     if (!aligned16(A) || !aligned16(B) || !aligned16(out)) return QLORA_ERR_MISALIGNED;
     const float s = alpha / (float)r;
-    return launch_merge(w->codes, w->q8, w->a2, A, B, r, s, out, (int)w->n, (int)w->k, (hipStream_t)stream);
+    return launch_merge(w->codes, w->q8, w->a2, cb_of(w), A, B, r, s, out, (int)w->n, (int)w->k, (hipStream_t)stream);
 }
 
 size_t qlora_fwd_workspace(int64_t M, int64_t N, int64_t K, int r) {
@@ -165,7 +168,8 @@ qlora_status qlora_fused_gemm_fwd(const qlora_nf4* w, const uint16_t* x, int64_t
     if (M == 0) return QLORA_OK;
     if (!x || !t || !B || !y) return QLORA_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(t) || !aligned16(B) || !aligned16(y)) return QLORA_ERR_MISALIGNED;
-    return launch_gemm_fwd(x, w->codes, w->q8, w->a2, t, B, y, (int)M, (int)N, (int)K, r, (hipStream_t)stream);
+    return launch_gemm_fwd(x, w->codes, w->q8, w->a2, cb_of(w), t, B, y, (int)M, (int)N, (int)K, r,
+                           (hipStream_t)stream);
 }
 
 qlora_status qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
@@ -187,7 +191,7 @@ qlora_status qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, 
     float* part = reinterpret_cast<float*>(at(ws, L.part));
     uint16_t* t = t_out ? t_out : reinterpret_cast<uint16_t*>(at(ws, L.tbuf));
     if ((st = launch_nt(x, A, true, part, t, scale, (int)M, (int)K, r, s)) != QLORA_OK) return st;
-    return launch_gemm_fwd(x, w->codes, w->q8, w->a2, t, B, y, (int)M, (int)N, (int)K, r, s);
+    return launch_gemm_fwd(x, w->codes, w->q8, w->a2, cb_of(w), t, B, y, (int)M, (int)N, (int)K, r, s);
 }
 
 qlora_status qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
@@ -222,7 +226,7 @@ qlora_status qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, int64_t M, 
         t = tb;
     }
     if (dx) {
-        if ((st = launch_gemm_bwd_dx(dy, w->codes, w->q8, w->a2, u, A, dx, (int)M, (int)N, (int)K, r, s)) != QLORA_OK)
+        if ((st = launch_gemm_bwd_dx(dy, w->codes, w->q8, w->a2, cb_of(w), u, A, dx, (int)M, (int)N, (int)K, r, s)) != QLORA_OK)
             return st;
     }
     // dA [K, r] = x^T u ; dB [r, N] = t^T dy, stored transposed from the [N, r] reduction

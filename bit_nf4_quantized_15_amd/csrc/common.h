@@ -30,7 +30,35 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float nf4_level(int j) { return __uint_as_float(kNf4Bits[j]); }
+// The 16 FP4 levels in code order: the 4-bit float E2M1 (bit 3 sign, bits
+// 2..1 exponent with bias 1, bit 0 mantissa; magnitudes 0, 0.5, 1, 1.5, 2, 3,
+// 4, 6) divided by 6 and rounded to nearest float; code 8 is -0 ("bitsandbytes
+// deep dive", sections 6.5 and 8.1: fp4 is a floating-point-style codebook).
+constexpr uint32_t kFp4Bits[16] = {
+    0x00000000u, 0x3daaaaabu, 0x3e2aaaabu, 0x3e800000u, 0x3eaaaaabu, 0x3f000000u,
+    0x3f2aaaabu, 0x3f800000u, 0x80000000u, 0xbdaaaaabu, 0xbe2aaaabu, 0xbe800000u,
+    0xbeaaaaabu, 0xbf000000u, 0xbf2aaaabu, 0xbf800000u};
+
+// Codebook selector of the kernels (the quant_type of qlora_nf4).
+constexpr int kCbNf4 = 0;
+constexpr int kCbFp4 = 1;
+
+// Level of code j in codebook CB.
+template <int CB>
+__device__ __forceinline__ float level(int j) {
+    return __uint_as_float(CB == kCbFp4 ? kFp4Bits[j] : kNf4Bits[j]);
+}
+
+// The distinct levels in ascending order, as codes: index i -> code.  NF4 is
+// ascending already (16 levels); FP4 has 15 distinct levels (one zero, +0):
+// codes 15, 14, .., 9 (negative, magnitude descending), then 0, 1, .., 7.
+template <int CB>
+__device__ __forceinline__ uint32_t code_of_sorted(uint32_t i) {
+    if (CB == kCbFp4) return i >= 7u ? i - 7u : 15u - i;
+    return i;
+}
+template <int CB>
+constexpr int kDistinctLevels = CB == kCbFp4 ? 15 : 16;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
@@ -57,23 +85,24 @@ inline qlora_status launch_status() {
 }
 
 // Launchers (one per translation unit).
-qlora_status launch_quantize(const uint16_t* W, int64_t nblocks, uint8_t* codes, uint8_t* q8, float* a2,
+// `cb` selects the codebook (kCbNf4, kCbFp4) of the codes the kernels read or write.
+qlora_status launch_quantize(const uint16_t* W, int64_t nblocks, uint8_t* codes, uint8_t* q8, float* a2, int cb,
                              hipStream_t s);
-qlora_status launch_dequantize(const uint8_t* codes, const uint8_t* q8, const float* a2, int64_t nblocks,
+qlora_status launch_dequantize(const uint8_t* codes, const uint8_t* q8, const float* a2, int cb, int64_t nblocks,
                                uint16_t* out, hipStream_t s);
-qlora_status launch_merge(const uint8_t* codes, const uint8_t* q8, const float* a2, const uint16_t* A,
+qlora_status launch_merge(const uint8_t* codes, const uint8_t* q8, const float* a2, int cb, const uint16_t* A,
                           const uint16_t* B, int r, float s, uint16_t* out, int N, int K, hipStream_t st);
-qlora_status launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* q8, const float* a2,
+qlora_status launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* q8, const float* a2, int cb,
                              const uint16_t* t, const uint16_t* B, uint16_t* y, int M, int N, int K, int r,
                              hipStream_t s);
 // Decode-size forward (1 <= M <= kGemvMaxM): same result as launch_gemm_fwd.
 constexpr int kGemvMaxM = 16;
 bool gemv_supported(int M, int N, int K, int r);
-qlora_status launch_gemv_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* q8, const float* a2,
+qlora_status launch_gemv_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* q8, const float* a2, int cb,
                              const uint16_t* t, const uint16_t* B, uint16_t* y, int M, int N, int K, int r,
                              hipStream_t s);
 qlora_status launch_gemm_bwd_dx(const uint16_t* dy, const uint8_t* codes, const uint8_t* q8, const float* a2,
-                                const uint16_t* u, const uint16_t* A, uint16_t* dx, int M, int N, int K, int r,
+                                int cb, const uint16_t* u, const uint16_t* A, uint16_t* dx, int M, int N, int K, int r,
                                 hipStream_t s);
 // out [M, r] = bf16(scale * X [M, C] Y), Y given as Yt [r, C] or, with y_natural, as [C, r]
 qlora_status launch_nt(const uint16_t* X, const uint16_t* Y, bool y_natural, float* part, uint16_t* out, float scale,

@@ -258,7 +258,7 @@ __device__ __forceinline__ void store_acc(uint16_t* __restrict__ out, int64_t ld
 constexpr int kSup = 2;                                     // blocks per super-step
 constexpr int kCodeTileBytes = kTN * kSup * kBlock / 2;     // 256 rows x 64 B
 
-template <bool Q8DW, bool DQ>
+template <bool Q8DW, bool DQ, int CB>
 __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ q8,
     const float* __restrict__ a2, const uint16_t* __restrict__ t, const uint16_t* __restrict__ Bl,
@@ -411,7 +411,7 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
     u32x4_t cc[2];
     bf16x8 b[2][2];
     bf16x8 a[2][4];  // A operands by half chunk: row tiles 4 half .. 4 half + 3 of chunk c
-    share_tabs(make_tab(ahs0[kSup * crl[h]]), T[0], T[1]);
+    share_tabs(make_tab<CB>(ahs0[kSup * crl[h]]), T[0], T[1]);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         cc[u] = read_codes(cds0, 0, u);
@@ -477,7 +477,7 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
             if (hc == 2 || hc == 3) {
 #pragma unroll
                 for (int q = 4 * (hc - 2); q < 4 * (hc - 2) + 4; ++q)
-                    e[q] = pack_bf16x2(ahn * nf4_level(2 * q), ahn * nf4_level(2 * q + 1));
+                    e[q] = pack_bf16x2(ahn * level<CB>(2 * q), ahn * level<CB>(2 * q + 1));
 #pragma unroll
                 for (int q = 2 * (hc - 2); q < 2 * (hc - 2) + 2; ++q) {
                     mine.lo[q] = perm_b32(e[2 * q + 1], e[2 * q], 0x06040200u);
@@ -637,7 +637,7 @@ __device__ __forceinline__ uint32_t wtile_off(int row, int col) {
     return (uint32_t)row * 512u + ((uint32_t)((col >> 3) ^ f) << 4) + ((uint32_t)(col & 7) << 1);
 }
 
-template <bool DYVEC, bool DQ>
+template <bool DYVEC, bool DQ, int CB>
 __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
     const uint16_t* __restrict__ dy, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ q8,
     const float* __restrict__ a2, const uint16_t* __restrict__ u_, const uint16_t* __restrict__ Al,
@@ -699,7 +699,7 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
         return scale_step(S.g) * (float)(S.ok ? q : 0u);
     };
     auto expand = [&](const Step& S, u32x4_t (&out)[8]) {
-        const Nf4Tab T = make_tab(ahat_of(S));
+        const Nf4Tab T = make_tab<CB>(ahat_of(S));
 #pragma unroll
         for (int d = 0; d < 8; ++d) out[d] = deq8(T, d < 4 ? S.c0[d] : S.c1[d - 4]);
     };
@@ -789,7 +789,7 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
         Step nn;
         load_step(min(ns + 2, NS - 1), nn);  // kStepLoads loads: codes (2), scale data
         u32x4_t w[8];
-        const Nf4Tab T = make_tab(ahat_of(nxt));
+        const Nf4Tab T = make_tab<CB>(ahat_of(nxt));
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int p = c & 1;
@@ -871,10 +871,10 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
 
 }  // namespace
 
-qlora_status launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* q8, const float* a2,
+qlora_status launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* q8, const float* a2, int cb,
                              const uint16_t* t, const uint16_t* B, uint16_t* y, int M, int N, int K, int r,
                              hipStream_t s) {
-    if (gemv_supported(M, N, K, r)) return launch_gemv_fwd(x, codes, q8, a2, t, B, y, M, N, K, r, s);
+    if (gemv_supported(M, N, K, r)) return launch_gemv_fwd(x, codes, q8, a2, cb, t, B, y, M, N, K, r, s);
     const int tm = (M + kTM - 1) / kTM, tn = (N + kTN - 1) / kTN;
     // x is 16-byte aligned (checked by the caller) and K % 64 == 0, so every
     // 16-byte chunk of a row is aligned; a 256-row panel must fit a 32-bit offset
@@ -882,9 +882,14 @@ qlora_status launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const uint
     // code-tile offsets (including blocks past a row's end) must fit a 32-bit voffset
     if ((uint64_t)N * (uint64_t)K / 2 + 4096 >= (uint64_t(1) << 32)) return QLORA_ERR_UNSUPPORTED_SHAPE;
     // q8 == NULL: no double quantization, a2 holds one fp32 absmax per block
-#define QL_FWD(Q8DW, DQ)                                                                                        \
-    hipLaunchKernelGGL((nf4_gemm_fwd_kernel<Q8DW, DQ>), dim3(tm * tn), dim3(kT), 0, s, x, codes, q8, a2, t, B, y, M, \
-                       N, K, r, tm, tn)
+#define QL_FWD1(Q8DW, DQ, CB)                                                                                  \
+    hipLaunchKernelGGL((nf4_gemm_fwd_kernel<Q8DW, DQ, CB>), dim3(tm * tn), dim3(kT), 0, s, x, codes, q8, a2, t, B, y, \
+                       M, N, K, r, tm, tn)
+#define QL_FWD(Q8DW, DQ)                           \
+    do {                                           \
+        if (cb == kCbFp4) QL_FWD1(Q8DW, DQ, kCbFp4); \
+        else QL_FWD1(Q8DW, DQ, kCbNf4);            \
+    } while (0)
     const bool even = (K / kTK) % kSup == 0;
     if (q8) {
         if (even) QL_FWD(true, true); else QL_FWD(false, true);
@@ -892,25 +897,32 @@ qlora_status launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const uint
         if (even) QL_FWD(true, false); else QL_FWD(false, false);
     }
 #undef QL_FWD
+#undef QL_FWD1
     return launch_status();
 }
 
 qlora_status launch_gemm_bwd_dx(const uint16_t* dy, const uint8_t* codes, const uint8_t* q8, const float* a2,
-                                const uint16_t* u, const uint16_t* A, uint16_t* dx, int M, int N, int K, int r,
+                                int cb, const uint16_t* u, const uint16_t* A, uint16_t* dx, int M, int N, int K, int r,
                                 hipStream_t s) {
     const int tm = (M + kTM - 1) / kTM, tk = (K + kTN - 1) / kTN;
     const bool vec = (N % 8 == 0) && ((reinterpret_cast<uintptr_t>(dy) & 15u) == 0) &&
                      ((int64_t)kTM * N * 2 < (int64_t(1) << 32));
     // q8 == NULL: no double quantization, a2 holds one fp32 absmax per block
-#define QL_BWD(V, DQ)                                                                                          \
-    hipLaunchKernelGGL((nf4_gemm_bwd_dx_kernel<V, DQ>), dim3(tm * tk), dim3(kT), 0, s, dy, codes, q8, a2, u, A, dx, \
+#define QL_BWD1(V, DQ, CB)                                                                                      \
+    hipLaunchKernelGGL((nf4_gemm_bwd_dx_kernel<V, DQ, CB>), dim3(tm * tk), dim3(kT), 0, s, dy, codes, q8, a2, u, A, dx, \
                        M, N, K, r, tm, tk)
+#define QL_BWD(V, DQ)                           \
+    do {                                        \
+        if (cb == kCbFp4) QL_BWD1(V, DQ, kCbFp4); \
+        else QL_BWD1(V, DQ, kCbNf4);            \
+    } while (0)
     if (q8) {
         if (vec) QL_BWD(true, true); else QL_BWD(false, true);
     } else {
         if (vec) QL_BWD(true, false); else QL_BWD(false, false);
     }
 #undef QL_BWD
+#undef QL_BWD1
     return launch_status();
 }
 

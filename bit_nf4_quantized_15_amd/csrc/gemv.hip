@@ -97,7 +97,7 @@ struct GvPlan {
     int tsh;     // log2 of the threads that stage one x row
 };
 
-template <int NV, int NG, bool DQ>
+template <int NV, int NG, bool DQ, int CB>
 __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const uint16_t* __restrict__ x,
                                                               const uint8_t* __restrict__ codes,
                                                               const uint8_t* __restrict__ q8,
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const uint16_t* __
     const int tid = threadIdx.x;
     // codebook level of this thread's table entries, loaded before anything
     // that waits on HBM so that building the table never waits behind it
-    const float lo_level = nf4_level(tid >> 4);
+    const float lo_level = level<CB>(tid >> 4);
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ln = lane & 15;  // B column (weight row) / A row (x row) of the lane
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const uint16_t* __
     {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            const uint32_t v = pack_bf16x2(nf4_level(j), lo_level);
+            const uint32_t v = pack_bf16x2(level<CB>(j), lo_level);
             *reinterpret_cast<u32x4_t*>(lut + 16 * (tid + 256 * j)) = u32x4_t{v, v, v, v};
         }
     }
@@ -345,7 +345,7 @@ bool gemv_supported(int M, int N, int K, int r) {
     return M >= 1 && M <= kGemvMaxM && r <= 128 && (uint64_t)N * (uint64_t)K / 2 < (uint64_t(1) << 31);
 }
 
-qlora_status launch_gemv_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* q8, const float* a2,
+qlora_status launch_gemv_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* q8, const float* a2, int cb,
                              const uint16_t* t, const uint16_t* B, uint16_t* y, int M, int N, int K, int r,
                              hipStream_t s) {
     if (!gemv_supported(M, N, K, r)) return QLORA_ERR_UNSUPPORTED_SHAPE;
@@ -369,19 +369,24 @@ qlora_status launch_gemv_fwd(const uint16_t* x, const uint8_t* codes, const uint
     const dim3 grid((unsigned)((N + kGvRows - 1) / kGvRows));
     const int nv = M == 1 ? 1 : M == 2 ? 2 : 4;
     // q8 == NULL: no double quantization, a2 holds one fp32 absmax per block
-#define QLORA_GEMV(NV_, NG_)                                                                                   \
-    if (nv == NV_ && ng == NG_) {                                                                              \
-        if (q8)                                                                                                \
-            hipLaunchKernelGGL((nf4_gemv_kernel<NV_, NG_, true>), grid, dim3(kGvThreads), 0, s, x, codes, q8, a2, t, B, \
-                               y, M, N, K, r, P);                                                              \
-        else                                                                                                   \
-            hipLaunchKernelGGL((nf4_gemv_kernel<NV_, NG_, false>), grid, dim3(kGvThreads), 0, s, x, codes, q8, a2, t,  \
-                               B, y, M, N, K, r, P);                                                           \
+#define QLORA_GEMV1(NV_, NG_, DQ_, CB_)                                                                         \
+    hipLaunchKernelGGL((nf4_gemv_kernel<NV_, NG_, DQ_, CB_>), grid, dim3(kGvThreads), 0, s, x, codes, q8, a2, t, B, y, \
+                       M, N, K, r, P)
+#define QLORA_GEMV(NV_, NG_)                                           \
+    if (nv == NV_ && ng == NG_) {                                      \
+        if (q8) {                                                      \
+            if (cb == kCbFp4) QLORA_GEMV1(NV_, NG_, true, kCbFp4);     \
+            else QLORA_GEMV1(NV_, NG_, true, kCbNf4);                  \
+        } else {                                                       \
+            if (cb == kCbFp4) QLORA_GEMV1(NV_, NG_, false, kCbFp4);    \
+            else QLORA_GEMV1(NV_, NG_, false, kCbNf4);                 \
+        }                                                              \
     }
     QLORA_GEMV(1, 1) QLORA_GEMV(1, 2) QLORA_GEMV(1, 4)
     QLORA_GEMV(2, 1) QLORA_GEMV(2, 2) QLORA_GEMV(2, 4)
     QLORA_GEMV(4, 1) QLORA_GEMV(4, 2) QLORA_GEMV(4, 4)
 #undef QLORA_GEMV
+#undef QLORA_GEMV1
     return launch_status();
 }
 

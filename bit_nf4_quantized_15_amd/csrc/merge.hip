@@ -23,7 +23,7 @@ namespace {
 constexpr int kMT = 64;       // tile rows (n) and columns (k): one NF4 block of columns
 constexpr int kMaxR = 128;
 
-template <bool DQ>
+template <bool DQ, int CB>
 __global__ __launch_bounds__(256) void nf4_merge_kernel(const uint8_t* __restrict__ codes,
                                                         const uint8_t* __restrict__ q8, const float* __restrict__ a2,
                                                         const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void nf4_merge_kernel(const uint8_t* __restric
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const uint32_t code = h == 0 ? byte >> 4 : byte & 0xFu;
-                const uint32_t wh = pack_bf16x2(__fmul_rn(ahat, nf4_level((int)code)), 0.0f) & 0xFFFFu;
+                const uint32_t wh = pack_bf16x2(__fmul_rn(ahat, level<CB>((int)code)), 0.0f) & 0xFFFFu;
                 const float corr = __fmul_rn(s, acc[i][2 * e2 + h]);
                 v[h] = __fadd_rn(bf16_bits_to_f32(wh), corr);
             }
@@ -86,14 +86,18 @@ __global__ __launch_bounds__(256) void nf4_merge_kernel(const uint8_t* __restric
 
 }  // namespace
 
-qlora_status launch_merge(const uint8_t* codes, const uint8_t* q8, const float* a2, const uint16_t* A,
+qlora_status launch_merge(const uint8_t* codes, const uint8_t* q8, const float* a2, int cb, const uint16_t* A,
                           const uint16_t* B, int r, float s, uint16_t* out, int N, int K, hipStream_t st) {
     if (r < 1 || r > kMaxR) return QLORA_ERR_INVALID_ARG;
     const dim3 grid((unsigned)(K / kMT), (unsigned)((N + kMT - 1) / kMT));
-    if (q8)
-        hipLaunchKernelGGL(nf4_merge_kernel<true>, grid, dim3(256), 0, st, codes, q8, a2, A, B, r, s, out, N, K);
-    else
-        hipLaunchKernelGGL(nf4_merge_kernel<false>, grid, dim3(256), 0, st, codes, q8, a2, A, B, r, s, out, N, K);
+#define QL_MERGE(DQ_, CB_) \
+    hipLaunchKernelGGL((nf4_merge_kernel<DQ_, CB_>), grid, dim3(256), 0, st, codes, q8, a2, A, B, r, s, out, N, K)
+    if (q8) {
+        if (cb == kCbFp4) QL_MERGE(true, kCbFp4); else QL_MERGE(true, kCbNf4);
+    } else {
+        if (cb == kCbFp4) QL_MERGE(false, kCbFp4); else QL_MERGE(false, kCbNf4);
+    }
+#undef QL_MERGE
     return launch_status();
 }
 

@@ -54,7 +54,7 @@ __device__ __forceinline__ uint32_t nf4_code(float w, f32x4_t t0, f32x4_t t1, f3
     return (b3 ? 8u : 0u) | (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
 }
 
-template <bool DQ>
+template <bool DQ, int CB>
 __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint16_t* __restrict__ W,
                                                                 int64_t nblocks,
                                                                 uint8_t* __restrict__ codes,
@@ -104,8 +104,13 @@ __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint16_t* 
             const double ad = (double)a;
 #pragma unroll
             for (int j = 0; j < 15; ++j) {
-                const double m = 0.5 * ((double)nf4_level(j) + (double)nf4_level(j + 1));  // exact
-                T[j] = f32_rd_bf16(__double2float_rd(ad * m));                          // exact product
+                if (j + 1 < kDistinctLevels<CB>) {
+                    const double m = 0.5 * ((double)level<CB>(code_of_sorted<CB>(j)) +
+                                            (double)level<CB>(code_of_sorted<CB>(j + 1)));  // exact
+                    T[j] = f32_rd_bf16(__double2float_rd(ad * m));                        // exact product
+                } else {
+                    T[j] = __builtin_huge_valf();  // no level above the last distinct one
+                }
             }
         } else {
 #pragma unroll
@@ -151,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint16_t* 
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const uint32_t bits = (i & 1) ? (v[p][i >> 1] >> 16) : (v[p][i >> 1] & 0xFFFFu);
-                const uint32_t q = nf4_code(bf16_bits_to_f32(bits), t0, t1, t2, t3);
+                const uint32_t q = code_of_sorted<CB>(nf4_code(bf16_bits_to_f32(bits), t0, t1, t2, t3));
                 packed |= q << (4 * (i ^ 1));
             }
             *reinterpret_cast<uint32_t*>(codes + (b0 + bl) * (kBlock / 2) + sub * 4) = packed;
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint16_t* 
 // nf4_dequantize_kernel: 256 lanes x 8 weights = 32 blocks per workgroup.
 //   a_hat = fl32(fl32(a2/255) * q8) (without double quantization: the stored
 //   fp32 absmax a2[b]), w_hat = RNE_bf16(fl32(a_hat * c_code)).
-template <bool DQ>
+template <bool DQ, int CB>
 __global__ __launch_bounds__(kThreads) void nf4_dequantize_kernel(const uint8_t* __restrict__ codes,
                                                                   const uint8_t* __restrict__ q8,
                                                                   const float* __restrict__ a2,
@@ -170,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void nf4_dequantize_kernel(const uint8_t*
                                                                   uint16_t* __restrict__ out) {
     __shared__ float s_c[16];
     const int tid = threadIdx.x;
-    if (tid < 16) s_c[tid] = nf4_level(tid);
+    if (tid < 16) s_c[tid] = level<CB>(tid);
     __syncthreads();
     const int64_t b = (int64_t)blockIdx.x * 32 + (tid >> 3);
     const int sub = tid & 7;
@@ -190,27 +195,33 @@ __global__ __launch_bounds__(kThreads) void nf4_dequantize_kernel(const uint8_t*
 
 }  // namespace
 
-qlora_status launch_quantize(const uint16_t* W, int64_t nblocks, uint8_t* codes, uint8_t* q8, float* a2,
+qlora_status launch_quantize(const uint16_t* W, int64_t nblocks, uint8_t* codes, uint8_t* q8, float* a2, int cb,
                              hipStream_t s) {
     const int64_t groups = (nblocks + kSuper - 1) / kSuper;
-    if (q8)
-        hipLaunchKernelGGL(nf4_quantize_kernel<true>, dim3((unsigned)groups), dim3(kThreads), 0, s, W, nblocks,
-                           codes, q8, a2);
-    else
-        hipLaunchKernelGGL(nf4_quantize_kernel<false>, dim3((unsigned)groups), dim3(kThreads), 0, s, W, nblocks,
-                           codes, q8, a2);
+#define QL_QUANT(DQ_, CB_)                                                                                     \
+    hipLaunchKernelGGL((nf4_quantize_kernel<DQ_, CB_>), dim3((unsigned)groups), dim3(kThreads), 0, s, W, nblocks, \
+                       codes, q8, a2)
+    if (q8) {
+        if (cb == kCbFp4) QL_QUANT(true, kCbFp4); else QL_QUANT(true, kCbNf4);
+    } else {
+        if (cb == kCbFp4) QL_QUANT(false, kCbFp4); else QL_QUANT(false, kCbNf4);
+    }
+#undef QL_QUANT
     return launch_status();
 }
 
-qlora_status launch_dequantize(const uint8_t* codes, const uint8_t* q8, const float* a2, int64_t nblocks,
+qlora_status launch_dequantize(const uint8_t* codes, const uint8_t* q8, const float* a2, int cb, int64_t nblocks,
                                uint16_t* out, hipStream_t s) {
     const int64_t grid = (nblocks + 31) / 32;
-    if (q8)
-        hipLaunchKernelGGL(nf4_dequantize_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s, codes, q8, a2,
-                           nblocks, out);
-    else
-        hipLaunchKernelGGL(nf4_dequantize_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s, codes, q8, a2,
-                           nblocks, out);
+#define QL_DEQ(DQ_, CB_)                                                                                         \
+    hipLaunchKernelGGL((nf4_dequantize_kernel<DQ_, CB_>), dim3((unsigned)grid), dim3(kThreads), 0, s, codes, q8, a2, \
+                       nblocks, out)
+    if (q8) {
+        if (cb == kCbFp4) QL_DEQ(true, kCbFp4); else QL_DEQ(true, kCbNf4);
+    } else {
+        if (cb == kCbFp4) QL_DEQ(false, kCbFp4); else QL_DEQ(false, kCbNf4);
+    }
+#undef QL_DEQ
     return launch_status();
 }
 

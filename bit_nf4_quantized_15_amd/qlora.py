@@ -24,7 +24,10 @@ c_sz = ctypes.c_size_t
 
 class NF4State(ctypes.Structure):
     """Mirror of struct qlora_nf4."""
-    _fields_ = [("codes", c_vp), ("q8", c_vp), ("a2", c_vp), ("n", c_i64), ("k", c_i64)]
+    _fields_ = [("codes", c_vp), ("q8", c_vp), ("a2", c_vp), ("n", c_i64), ("k", c_i64), ("quant_type", ctypes.c_int32)]
+
+
+QUANT_TYPES = {"nf4": 0, "fp4": 1}   # qlora_quant_type: the 4-bit codebook
 
 
 def _load():
@@ -116,37 +119,42 @@ def sizes_nodq(N, K):
 
 class NF4Weight:
     """Device-resident quantized weight: codes (uint8), q8 (uint8) and a2 (float32) tensors; without
-    double quantization q8 is None and a2 holds one fp32 absmax per 64-block."""
+    double quantization q8 is None and a2 holds one fp32 absmax per 64-block.  quant_type names the
+    4-bit codebook: "nf4" or "fp4"."""
 
-    def __init__(self, codes, q8, a2, N, K):
+    def __init__(self, codes, q8, a2, N, K, quant_type="nf4"):
+        if quant_type not in QUANT_TYPES:
+            raise ValueError(f"quant_type must be one of {sorted(QUANT_TYPES)}, got {quant_type!r}")
         self.codes, self.q8, self.a2, self.N, self.K = codes, q8, a2, int(N), int(K)
+        self.quant_type = quant_type
 
     @property
     def double_quant(self):
         return self.q8 is not None
 
     @classmethod
-    def empty(cls, N, K, device="cuda", double_quant=True):
+    def empty(cls, N, K, device="cuda", double_quant=True, quant_type="nf4"):
         if not double_quant:
             cb, ab = sizes_nodq(N, K)
             return cls(torch.empty(cb, dtype=torch.uint8, device=device), None,
-                       torch.empty(ab // 4, dtype=torch.float32, device=device), N, K)
+                       torch.empty(ab // 4, dtype=torch.float32, device=device), N, K, quant_type)
         cb, qb, ab = sizes(N, K)
         return cls(torch.empty(cb, dtype=torch.uint8, device=device),
                    torch.empty(qb, dtype=torch.uint8, device=device),
-                   torch.empty(ab // 4, dtype=torch.float32, device=device), N, K)
+                   torch.empty(ab // 4, dtype=torch.float32, device=device), N, K, quant_type)
 
     def state(self):
         q8 = None if self.q8 is None else self.q8.data_ptr()
-        return NF4State(self.codes.data_ptr(), q8, self.a2.data_ptr(), self.N, self.K)
+        return NF4State(self.codes.data_ptr(), q8, self.a2.data_ptr(), self.N, self.K, QUANT_TYPES[self.quant_type])
 
 
-def quantize(W, out=None, double_quant=True):
-    """NF4 of a bf16 [N, K] device weight (qlora_quantize), with or without double quantization of the
-    block scales (ignored when `out` is given: its layout decides)."""
+def quantize(W, out=None, double_quant=True, quant_type="nf4"):
+    """4-bit blockwise quantization of a bf16 [N, K] device weight (qlora_quantize) with the NF4 or the FP4
+    codebook, with or without double quantization of the block scales (both ignored when `out` is given:
+    its layout and quant_type decide)."""
     N, K = W.shape
     _dev(W, torch.bfloat16, "W")
-    w = NF4Weight.empty(N, K, W.device, double_quant) if out is None else out
+    w = NF4Weight.empty(N, K, W.device, double_quant, quant_type) if out is None else out
     st = w.state()
     _check(lib.qlora_quantize(_ptr(W), N, K, ctypes.byref(st), _stream()), "qlora_quantize")
     return w

@@ -60,13 +60,29 @@ typedef enum qlora_status {
  * (sections 7.1 and 9.5; q8 == NULL): codes and one fp32 absmax per 64-block
  * in a2, 4.5 bits per weight.  Every entry point taking a qlora_nf4 accepts
  * both; a2 is never NULL. */
+/* The 4-bit codebook: what value each code 0..15 stands for (deep dive 8.1,
+ * the quant type).
+ *  - NF4: the 16 normal-quantile levels of section 6.2, ascending with the code.
+ *  - FP4: a floating-point-style codebook (section 6.5), whose values the page
+ *    does not give.  Taken as the 4-bit float E2M1 of the OCP MX formats
+ *    (bit 3 sign, bits 2..1 exponent with bias 1, bit 0 mantissa, subnormals at
+ *    exponent 0), divided by its largest magnitude 6:
+ *      c = +-{0, 1/12, 1/6, 1/4, 1/3, 1/2, 2/3, 1}, each rounded to fp32,
+ *    and the code is the E2M1 bit pattern.
+ * Both encode to the nearest level of w/a, ties to the lower level.  For FP4 a
+ * zero weight (either sign) encodes as +0 (code 0); code 8 (-0) decodes to -0
+ * but is never produced.  Everything else is the same for both. */
+typedef enum qlora_quant_type { QLORA_QUANT_NF4 = 0, QLORA_QUANT_FP4 = 1 } qlora_quant_type;
+
 typedef struct qlora_nf4 {
-    uint8_t* codes; /* [N*K/2]            packed 4-bit NF4 codes                     */
-    uint8_t* q8;    /* [N*K/64]           8-bit code of each block's absmax, or NULL */
-    float* a2;      /* [ceil(N*K/16384)]  fp32 absmax of each group of 256 absmaxes; */
-                    /* [N*K/64] fp32 absmax of each block when q8 == NULL            */
-    int64_t n;      /* N = Dout (rows of the stored weight)                          */
-    int64_t k;      /* K = Din, a multiple of 64                                     */
+    uint8_t* codes;     /* [N*K/2]            packed 4-bit codes                         */
+    uint8_t* q8;        /* [N*K/64]           8-bit code of each block's absmax, or NULL */
+    float* a2;          /* [ceil(N*K/16384)]  fp32 absmax of each group of 256 absmaxes; */
+                        /* [N*K/64] fp32 absmax of each block when q8 == NULL            */
+    int64_t n;          /* N = Dout (rows of the stored weight)                          */
+    int64_t k;          /* K = Din, a multiple of 64                                     */
+    int32_t quant_type; /* a qlora_quant_type; 0 (zero-initialised) is NF4. Any other   */
+                        /* value -> QLORA_ERR_INVALID_ARG                                */
 } qlora_nf4;
 
 /* Library version (major*10000 + minor*100 + patch). */

@@ -87,6 +87,11 @@ def test_quantize_argument_errors(q):
     assert f(FAKE, 64, 64, ctypes.byref(_state(q, q8=None, a2=0)), None) == INVALID
     assert f(FAKE, 64, 64, ctypes.byref(_state(q, q8=None, a2=FAKE + 4)), None) == MISALIGNED
     assert f(FAKE, 64, 100, ctypes.byref(_state(q, q8=None, k=100)), None) == SHAPE
+    # quant_type: 0 (NF4) and 1 (FP4) only
+    bad_qt = _state(q)
+    bad_qt.quant_type = 2
+    assert f(FAKE, 64, 64, ctypes.byref(bad_qt), None) == INVALID
+    assert q.lib.qlora_dequantize(ctypes.byref(bad_qt), FAKE, None) == INVALID
     assert q.lib.qlora_dequantize(ctypes.byref(st), None, None) == INVALID
     assert q.lib.qlora_dequantize(ctypes.byref(st), FAKE + 4, None) == MISALIGNED
 
