@@ -370,7 +370,8 @@ def extras(torch, qlora, workloads, dev, to_dev, L, M, r):
     res["decode_gemv_q_proj_4096x4096_r16"] = dec
     del copies
 
-    res["double_quant_off"] = extras_nodq(torch, qlora, workloads, dev, to_dev, L, M, r, ev)
+    res["double_quant_off"] = extras_variant(torch, qlora, workloads, dev, to_dev, L, M, r, ev, double_quant=False)
+    res["fp4"] = extras_variant(torch, qlora, workloads, dev, to_dev, L, M, r, ev, quant_type="fp4")
     res["qa_lora_pooled_g64"] = extras_pooled(torch, qlora, workloads, dev, to_dev, L, M, r, ev, 64)
 
     # LoRA merge for deployment (qlora_merge) of the 7 layers: N*K*r fp32 FMAs (VALU-bound) and
@@ -410,13 +411,14 @@ def extras(torch, qlora, workloads, dev, to_dev, L, M, r):
     return res
 
 
-def extras_nodq(torch, qlora, workloads, dev, to_dev, L, M, r, ev):
-    """The same workloads with double quantization off (fp32 absmax per block, deep dive 7.1 and 9.5):
-    the whole quantize + fwd + bwd step of the 7 linears, the forward GEMM alone, quantize bandwidth and
-    the decode GEMV (64 rotated weight copies)."""
+def extras_variant(torch, qlora, workloads, dev, to_dev, L, M, r, ev, double_quant=True, quant_type="nf4"):
+    """The same workloads with another scale layout or codebook: double quantization off (fp32 absmax per
+    block, deep dive 7.1 and 9.5) or the fp4 codebook (deep dive 6.5, 8.1).  The whole quantize + fwd +
+    bwd step of the 7 linears, the forward GEMM alone, quantize bandwidth and the decode GEMV (64 rotated
+    weight copies)."""
     res = {}
     alpha = workloads.CONFIGS[4]["alpha"]
-    Wn = [qlora.NF4Weight.empty(d["N"], d["K"], dev, double_quant=False) for d in L]
+    Wn = [qlora.NF4Weight.empty(d["N"], d["K"], dev, double_quant=double_quant, quant_type=quant_type) for d in L]
     ws = torch.empty(max(qlora.bwd_workspace(M, d["N"], d["K"], r) for d in L), dtype=torch.uint8, device=dev)
     total_flops = sum(d["flops"]["fwd"] + d["flops"]["bwd"] for d in L)
     fwd_flops = sum(d["flops"]["fwd_gemm"] for d in L)
@@ -452,17 +454,18 @@ def extras_nodq(torch, qlora, workloads, dev, to_dev, L, M, r, ev):
     step_ms = timed(step, 5)
     fwd_ms = timed(fwd, 5)
     q_ms = timed(quant, 5)
-    q_bytes = sum(d["N"] * d["K"] * 2 + sum(qlora.sizes_nodq(d["N"], d["K"])) for d in L)
+    size_of = qlora.sizes if double_quant else qlora.sizes_nodq
+    q_bytes = sum(d["N"] * d["K"] * 2 + sum(size_of(d["N"], d["K"])) for d in L)
     res["step"] = {"ms": round(step_ms, 4), "TFLOP/s": round(total_flops / (step_ms * 1e-3) / 1e12, 2)}
     res["fwd_gemm"] = {"avg_launch_ms": round(fwd_ms / len(L), 4),
                        "TFLOP/s": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2)}
     res["quantize"] = {"GB/s": round(q_bytes / (q_ms * 1e-3) / 1e9, 1), "ms": round(q_ms, 4),
-                       "bytes_per_weight": 2 + 0.5 + 4 / 64}
+                       "bytes_per_weight": round(q_bytes / sum(d["N"] * d["K"] for d in L), 4)}
     del Wn, ws
     c2 = workloads.CONFIGS[2]
     _, N2, K2 = c2["layers"][0]
     W2 = to_dev(workloads.weight(2))
-    copies = [qlora.quantize(W2, double_quant=False) for _ in range(64)]
+    copies = [qlora.quantize(W2, double_quant=double_quant, quant_type=quant_type) for _ in range(64)]
     B2 = to_dev(workloads.lora_B(2))
     xd = to_dev(workloads.activations(2, M=1))
     td = torch.zeros((1, c2["r"]), dtype=torch.bfloat16, device=dev)
@@ -471,7 +474,7 @@ def extras_nodq(torch, qlora, workloads, dev, to_dev, L, M, r, ev):
         qlora.fused_gemm_fwd(w, xd, td, B2, y=yd)
     torch.cuda.synchronize()
     gemv_ms = graph_ms([lambda w=w: qlora.fused_gemm_fwd(w, xd, td, B2, y=yd) for w in copies])
-    nb = gemv_bytes(1, N2, K2, c2["r"], double_quant=False) - 2 * K2 * c2["r"]
+    nb = gemv_bytes(1, N2, K2, c2["r"], double_quant=double_quant) - 2 * K2 * c2["r"]
     res["decode_gemv_q_proj_M=1"] = {"gemv_kernel_us": round(gemv_ms * 1e3, 2), "bytes_gemv_kernel": nb,
                                      "GB/s_gemv_kernel": round(nb / (gemv_ms * 1e-3) / 1e9, 1)}
     return res
