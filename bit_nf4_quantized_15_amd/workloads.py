@@ -88,6 +88,16 @@ def normal_bf16(seed, shape, std):
     return bf16_bits(v).reshape(shape)
 
 
+def normal_f16(seed, shape, std):
+    """fp16 (uint16 bits) tensor of N(0, std^2) values: the same draws as normal_bf16, rounded to
+    binary16 (nearest, ties to even) instead."""
+    n = int(np.prod(shape))
+    v = normal_f32(seed, n)
+    if std != 1.0:
+        v *= np.float32(std)
+    return v.astype(np.float16).view(np.uint16).reshape(shape)
+
+
 def seed_of(cfg_id, layer, tensor_id):
     return CONFIGS[cfg_id]["base"] + 10 * layer + tensor_id
 

@@ -24,6 +24,7 @@ Sources (web pages on QLoRA / NF4 / bitsandbytes):
 
 Modules:
   bf16   -- bf16 decode and round-to-nearest-even encode (own implementation)
+  f16    -- fp16 decode and encode (numpy's IEEE binary16), the other 16-bit compute dtype
   nf4    -- codebook, blocking, codes, packing, double quantization, dequant
   brute  -- exact rational (fractions.Fraction) brute-force versions
   lora   -- fp64 forward / backward of the QLoRA linear

@@ -29,7 +29,7 @@ from fractions import Fraction
 
 import numpy as np
 
-from . import bf16, nf4
+from . import nf4
 
 E2M1_BIAS = 1
 E2M1_MAX = 6.0          # largest magnitude: exponent 3, mantissa 1 -> 2^(3-1) * 1.5
@@ -106,7 +106,7 @@ def fp4_codes(wb, a):
     return q
 
 
-def quantize(W_u16):
+def quantize(W_u16, dtype="bf16"):
     """FP4 blockwise quantization with double-quantized scales -> (packed codes, q8, A2).
 
     The scales depend on the block absmax only, so q8 and A2 equal those of
@@ -119,7 +119,7 @@ def quantize(W_u16):
     codes = np.empty((nb, nf4.BLOCK), dtype=np.uint8)
     step = 1 << 14
     for s in range(0, nb, step):
-        wb = bf16.to_f64(wb16[s:s + step])
+        wb = nf4.codec(dtype).to_f64(wb16[s:s + step])
         a[s:s + step] = nf4.block_absmax(wb)
         codes[s:s + step] = fp4_codes(wb, a[s:s + step])
     A2 = nf4.superblock_absmax(a)
@@ -130,7 +130,7 @@ def quantize(W_u16):
     return nf4.pack_nibbles(codes), q8, A2
 
 
-def quantize_nodq(W_u16):
+def quantize_nodq(W_u16, dtype="bf16"):
     """FP4 codes with one fp32 absmax per block (double quantization off) -> (packed codes, absmax)."""
     wb16 = nf4.blocks(np.asarray(W_u16, dtype=np.uint16))
     nb = wb16.shape[0]
@@ -138,23 +138,23 @@ def quantize_nodq(W_u16):
     codes = np.empty((nb, nf4.BLOCK), dtype=np.uint8)
     step = 1 << 14
     for s in range(0, nb, step):
-        wb = bf16.to_f64(wb16[s:s + step])
+        wb = nf4.codec(dtype).to_f64(wb16[s:s + step])
         ab = nf4.block_absmax(wb)
         a[s:s + step] = ab
         codes[s:s + step] = fp4_codes(wb, ab)
     return nf4.pack_nibbles(codes), a
 
 
-def dequantize(packed, q8, A2, N, K):
-    """w_hat = RNE_bf16(fl32(a_hat * c_q)) with the FP4 table, shape [N, K], bf16 bits."""
-    return nf4.dequantize(packed, q8, A2, N, K, table=fp4_table())
+def dequantize(packed, q8, A2, N, K, dtype="bf16"):
+    """w_hat = RNE_16(fl32(a_hat * c_q)) with the FP4 table, shape [N, K], 16-bit bits of `dtype`."""
+    return nf4.dequantize(packed, q8, A2, N, K, table=fp4_table(), dtype=dtype)
 
 
-def dequantize_nodq(packed, absmax, N, K):
+def dequantize_nodq(packed, absmax, N, K, dtype="bf16"):
     """w_hat with the stored fp32 block absmax and the FP4 table."""
-    return nf4.dequantize_nodq(packed, absmax, N, K, table=fp4_table())
+    return nf4.dequantize_nodq(packed, absmax, N, K, table=fp4_table(), dtype=dtype)
 
 
-def dequantize_rows(packed, q8, A2, K, rows):
+def dequantize_rows(packed, q8, A2, K, rows, dtype="bf16"):
     """w_hat of selected rows (double-quantized scales) with the FP4 table."""
-    return nf4.dequantize_rows(packed, q8, A2, K, rows, table=fp4_table())
+    return nf4.dequantize_rows(packed, q8, A2, K, rows, table=fp4_table(), dtype=dtype)

@@ -18,7 +18,7 @@ from statistics import NormalDist
 
 import numpy as np
 
-from . import bf16
+from . import bf16, f16
 
 BLOCK = 64          # first-level block (section 5.1: default block size 64)
 SUPER = 256         # first-level scales per fp32 second-level scale (section 7.2)
@@ -29,6 +29,11 @@ ZERO_CODE = 7       # index of the exact-zero codebook entry
 # ----------------------------------------------------------------------------
 # a1: the NF4 codebook
 # ----------------------------------------------------------------------------
+def codec(dtype):
+    """The 16-bit float format of a tensor: "bf16" (the default compute dtype) or "f16" (deep dive 8.3)."""
+    return {"bf16": bf16, "f16": f16}[dtype]
+
+
 def nf4_delta():
     """Truncation probability of the outermost quantile (reading R1).
 
@@ -183,34 +188,35 @@ def scale_dequant(q8, A2):
 # ----------------------------------------------------------------------------
 # a5: dequantization
 # ----------------------------------------------------------------------------
-def dequantize(packed, q8, A2, N, K, table=None):
-    """w_hat = RNE_bf16( fl32(a_hat_b * c_q) ) as uint16 bits, shape [N, K].
+def dequantize(packed, q8, A2, N, K, table=None, dtype="bf16"):
+    """w_hat = RNE_16( fl32(a_hat_b * c_q) ) as uint16 bits, shape [N, K].
 
     Section 5.2: w_hat = a * c_q, with the scale itself recovered from its 8-bit
     code (section 7).  The product is taken in float32 and rounded once to the
-    bf16 compute dtype (section 8.3); IEEE signed zeros are kept.
+    compute dtype (section 8.3: bf16, or fp16 with dtype="f16"); IEEE signed
+    zeros are kept.
     """
     ahat = scale_dequant(q8, A2)
-    return dequant_blocks(packed, ahat, table).reshape(N, K)
+    return dequant_blocks(packed, ahat, table, dtype).reshape(N, K)
 
 
-def dequant_blocks(packed, ahat, table=None):
-    """w_hat for whole blocks: packed [nb*32] bytes, ahat [nb] float32 -> [nb, 64] bf16 bits."""
+def dequant_blocks(packed, ahat, table=None, dtype="bf16"):
+    """w_hat for whole blocks: packed [nb*32] bytes, ahat [nb] float32 -> [nb, 64] 16-bit bits."""
     c = nf4_table() if table is None else np.asarray(table, np.float32)
     codes = unpack_nibbles(packed).reshape(-1, BLOCK)
     ahat = np.asarray(ahat, dtype=np.float32)
     w32 = (ahat[:, None] * c[codes]).astype(np.float32)
-    return bf16.from_f32_rne(w32)
+    return codec(dtype).from_f32_rne(w32)
 
 
-def dequantize_rows(packed, q8, A2, K, rows, table=None):
+def dequantize_rows(packed, q8, A2, K, rows, table=None, dtype="bf16"):
     """w_hat of the selected rows of an [N, K] weight only (for sampled checks)."""
     rows = np.asarray(rows, dtype=np.int64)
     bpr = K // BLOCK
     bidx = (rows[:, None] * bpr + np.arange(bpr)[None, :]).reshape(-1)
     ahat = _ahat_of_blocks(q8, A2, bidx)
     pk = np.asarray(packed).reshape(-1, BLOCK // 2)[bidx].reshape(-1)
-    return dequant_blocks(pk, ahat, table).reshape(rows.size, K)
+    return dequant_blocks(pk, ahat, table, dtype).reshape(rows.size, K)
 
 
 def _ahat_of_blocks(q8, A2, bidx):
@@ -222,8 +228,8 @@ def _ahat_of_blocks(q8, A2, bidx):
 # ----------------------------------------------------------------------------
 # a2..a4 composed: quantize a bf16 weight
 # ----------------------------------------------------------------------------
-def quantize(W_u16, table=None):
-    """Quantize a bf16 weight [N, K] (uint16 bits) -> (packed codes, q8, A2).
+def quantize(W_u16, table=None, dtype="bf16"):
+    """Quantize a bf16 (or, with dtype="f16", fp16) weight [N, K] (uint16 bits) -> (packed codes, q8, A2).
 
     The codes are taken against the true block absmax a (the page encodes the
     weights first and only then re-quantizes the constants, section 7).
@@ -235,7 +241,7 @@ def quantize(W_u16, table=None):
     codes = np.empty((nb, BLOCK), dtype=np.uint8)
     step = 1 << 14                     # blocks per pass: bounds the temporaries only
     for s in range(0, nb, step):
-        wb = bf16.to_f64(wb16[s:s + step])
+        wb = codec(dtype).to_f64(wb16[s:s + step])
         a[s:s + step] = block_absmax(wb)
         codes[s:s + step] = nf4_codes(wb, a[s:s + step], table)
     A2 = superblock_absmax(a)
@@ -249,8 +255,8 @@ def quantize(W_u16, table=None):
 # ----------------------------------------------------------------------------
 # Double quantization off: one fp32 absmax per block
 # ----------------------------------------------------------------------------
-def quantize_nodq(W_u16, table=None):
-    """Quantize a bf16 weight [N, K] without double quantization -> (packed codes, absmax).
+def quantize_nodq(W_u16, table=None, dtype="bf16"):
+    """Quantize a bf16 (or fp16) weight [N, K] without double quantization -> (packed codes, absmax).
 
     "bitsandbytes deep dive" 7.1 and 9.5: with double quantization off every
     block keeps its absmax as an fp32 constant (32 bits per 64 weights).  The
@@ -264,29 +270,29 @@ def quantize_nodq(W_u16, table=None):
     codes = np.empty((nb, BLOCK), dtype=np.uint8)
     step = 1 << 14
     for s in range(0, nb, step):
-        wb = bf16.to_f64(wb16[s:s + step])
+        wb = codec(dtype).to_f64(wb16[s:s + step])
         ab = block_absmax(wb)
         a[s:s + step] = ab
         codes[s:s + step] = nf4_codes(wb, ab, table)
     return pack_nibbles(codes), a
 
 
-def dequantize_nodq(packed, absmax, N, K, table=None):
+def dequantize_nodq(packed, absmax, N, K, table=None, dtype="bf16"):
     """w_hat = RNE_bf16( fl32(a_b * c_q) ) with the stored fp32 block absmax, shape [N, K].
 
     Section 5.2 (w_hat = a * c_q) with a kept exactly (section 7.1: no second
     quantization), rounded once to the bf16 compute dtype (section 8.3).
     """
-    return dequant_blocks(packed, np.asarray(absmax, np.float32), table).reshape(N, K)
+    return dequant_blocks(packed, np.asarray(absmax, np.float32), table, dtype).reshape(N, K)
 
 
-def dequantize_rows_nodq(packed, absmax, K, rows, table=None):
+def dequantize_rows_nodq(packed, absmax, K, rows, table=None, dtype="bf16"):
     """w_hat of the selected rows of an [N, K] weight quantized without double quantization."""
     rows = np.asarray(rows, dtype=np.int64)
     bpr = K // BLOCK
     bidx = (rows[:, None] * bpr + np.arange(bpr)[None, :]).reshape(-1)
     pk = np.asarray(packed).reshape(-1, BLOCK // 2)[bidx].reshape(-1)
-    return dequant_blocks(pk, np.asarray(absmax, np.float32)[bidx], table).reshape(rows.size, K)
+    return dequant_blocks(pk, np.asarray(absmax, np.float32)[bidx], table, dtype).reshape(rows.size, K)
 
 
 def storage_bytes_nodq(N, K):
