@@ -21,11 +21,14 @@ inline qlora_status check_state(const qlora_nf4* w) {
     if (w->k % kBlock) return QLORA_ERR_UNSUPPORTED_SHAPE;
     if (w->n > (int64_t(1) << 31) || w->k > (int64_t(1) << 31)) return QLORA_ERR_UNSUPPORTED_SHAPE;
     if (w->quant_type != QLORA_QUANT_NF4 && w->quant_type != QLORA_QUANT_FP4) return QLORA_ERR_INVALID_ARG;
+    if (w->dtype != QLORA_DTYPE_BF16 && w->dtype != QLORA_DTYPE_F16) return QLORA_ERR_INVALID_ARG;
     if (!aligned16(w->codes) || (w->q8 && !aligned16(w->q8)) || !aligned16(w->a2)) return QLORA_ERR_MISALIGNED;
     return QLORA_OK;
 }
 
 inline int cb_of(const qlora_nf4* w) { return w->quant_type == QLORA_QUANT_FP4 ? kCbFp4 : kCbNf4; }
+inline int dt_of(int dtype) { return dtype == QLORA_DTYPE_F16 ? kDtF16 : kDtBf16; }
+inline int dt_of(const qlora_nf4* w) { return dt_of(w->dtype); }
 
 inline bool bad_dims(int64_t M, int64_t N, int64_t K, int r) {
     return M < 0 || N < 1 || K < 1 || r < 1 || r > 128 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX;
@@ -107,7 +110,8 @@ qlora_status qlora_quantize(const uint16_t* W, int64_t N, int64_t K, const qlora
     if (st != QLORA_OK) return st;
     if (out->n != N || out->k != K) return QLORA_ERR_INVALID_ARG;
     if (!aligned16(W)) return QLORA_ERR_MISALIGNED;
-    return launch_quantize(W, N * K / kBlock, out->codes, out->q8, out->a2, cb_of(out), (hipStream_t)stream);
+    return launch_quantize(W, N * K / kBlock, out->codes, out->q8, out->a2, cb_of(out), dt_of(out),
+                           (hipStream_t)stream);
 }
 
 qlora_status qlora_dequantize(const qlora_nf4* w, uint16_t* out, void* stream) {
@@ -115,7 +119,8 @@ qlora_status qlora_dequantize(const qlora_nf4* w, uint16_t* out, void* stream) {
     if (st != QLORA_OK) return st;
     if (!out) return QLORA_ERR_INVALID_ARG;
     if (!aligned16(out)) return QLORA_ERR_MISALIGNED;
-    return launch_dequantize(w->codes, w->q8, w->a2, cb_of(w), w->n * w->k / kBlock, out, (hipStream_t)stream);
+    return launch_dequantize(w->codes, w->q8, w->a2, cb_of(w), dt_of(w), w->n * w->k / kBlock, out,
+                             (hipStream_t)stream);
 }
 
 qlora_status qlora_merge(const qlora_nf4* w, const uint16_t* A, const uint16_t* B, int r, float alpha,
@@ -125,7 +130,8 @@ qlora_status qlora_merge(const qlora_nf4* w, const uint16_t* A, const uint16_t* 
     if (!A || !B || !out || r < 1 || r > 128 || !std::isfinite(alpha)) return QLORA_ERR_INVALID_ARG;
     if (!aligned16(A) || !aligned16(B) || !aligned16(out)) return QLORA_ERR_MISALIGNED;
     const float s = alpha / (float)r;
-    return launch_merge(w->codes, w->q8, w->a2, cb_of(w), A, B, r, s, out, (int)w->n, (int)w->k, (hipStream_t)stream);
+    return launch_merge(w->codes, w->q8, w->a2, cb_of(w), dt_of(w), A, B, r, s, out, (int)w->n, (int)w->k,
+                        (hipStream_t)stream);
 }
 
 size_t qlora_fwd_workspace(int64_t M, int64_t N, int64_t K, int r) {
@@ -145,8 +151,9 @@ size_t qlora_lora_down_workspace(int64_t M, int64_t K, int r) {
 }
 
 qlora_status qlora_lora_down(const uint16_t* x, int64_t M, int64_t K, const uint16_t* A, int r, float alpha,
-                             uint16_t* t_out, void* ws, size_t ws_bytes, void* stream) {
+                             int dtype, uint16_t* t_out, void* ws, size_t ws_bytes, void* stream) {
     if (bad_dims(M, 1, K, r) || !std::isfinite(alpha)) return QLORA_ERR_INVALID_ARG;
+    if (dtype != QLORA_DTYPE_BF16 && dtype != QLORA_DTYPE_F16) return QLORA_ERR_INVALID_ARG;
     if (K % kBlock) return QLORA_ERR_UNSUPPORTED_SHAPE;
     if (M == 0) return QLORA_OK;
     if (!x || !A || !t_out) return QLORA_ERR_INVALID_ARG;
@@ -156,7 +163,7 @@ qlora_status qlora_lora_down(const uint16_t* x, int64_t M, int64_t K, const uint
     if (!aligned16(ws)) return QLORA_ERR_MISALIGNED;
     hipStream_t s = (hipStream_t)stream;
     float* part = reinterpret_cast<float*>(ws);
-    return launch_nt(x, A, true, part, t_out, alpha / (float)r, (int)M, (int)K, r, s);
+    return launch_nt(x, A, true, part, t_out, alpha / (float)r, (int)M, (int)K, r, dt_of(dtype), s);
 }
 
 qlora_status qlora_fused_gemm_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uint16_t* t,
@@ -168,7 +175,7 @@ qlora_status qlora_fused_gemm_fwd(const qlora_nf4* w, const uint16_t* x, int64_t
     if (M == 0) return QLORA_OK;
     if (!x || !t || !B || !y) return QLORA_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(t) || !aligned16(B) || !aligned16(y)) return QLORA_ERR_MISALIGNED;
-    return launch_gemm_fwd(x, w->codes, w->q8, w->a2, cb_of(w), t, B, y, (int)M, (int)N, (int)K, r,
+    return launch_gemm_fwd(x, w->codes, w->q8, w->a2, cb_of(w), dt_of(w), t, B, y, (int)M, (int)N, (int)K, r,
                            (hipStream_t)stream);
 }
 
@@ -190,8 +197,8 @@ qlora_status qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, 
     const float scale = alpha / (float)r;
     float* part = reinterpret_cast<float*>(at(ws, L.part));
     uint16_t* t = t_out ? t_out : reinterpret_cast<uint16_t*>(at(ws, L.tbuf));
-    if ((st = launch_nt(x, A, true, part, t, scale, (int)M, (int)K, r, s)) != QLORA_OK) return st;
-    return launch_gemm_fwd(x, w->codes, w->q8, w->a2, cb_of(w), t, B, y, (int)M, (int)N, (int)K, r, s);
+    if ((st = launch_nt(x, A, true, part, t, scale, (int)M, (int)K, r, dt_of(w), s)) != QLORA_OK) return st;
+    return launch_gemm_fwd(x, w->codes, w->q8, w->a2, cb_of(w), dt_of(w), t, B, y, (int)M, (int)N, (int)K, r, s);
 }
 
 qlora_status qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
@@ -219,20 +226,22 @@ qlora_status qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, int64_t M, 
     uint16_t* u = reinterpret_cast<uint16_t*>(at(ws, L.u));
     float* part = reinterpret_cast<float*>(at(ws, L.part));
     // u = s dy B^T  (B [r, N] is the row-major transpose of B^T)
-    if ((st = launch_nt(dy, B, false, part, u, scale, (int)M, (int)N, r, s)) != QLORA_OK) return st;
+    if ((st = launch_nt(dy, B, false, part, u, scale, (int)M, (int)N, r, dt_of(w), s)) != QLORA_OK) return st;
     if (!t) {  // recompute t = s x A
         uint16_t* tb = reinterpret_cast<uint16_t*>(at(ws, L.tbuf));
-        if ((st = launch_nt(x, A, true, part, tb, scale, (int)M, (int)K, r, s)) != QLORA_OK) return st;
+        if ((st = launch_nt(x, A, true, part, tb, scale, (int)M, (int)K, r, dt_of(w), s)) != QLORA_OK) return st;
         t = tb;
     }
     if (dx) {
-        if ((st = launch_gemm_bwd_dx(dy, w->codes, w->q8, w->a2, cb_of(w), u, A, dx, (int)M, (int)N, (int)K, r, s)) != QLORA_OK)
+        if ((st = launch_gemm_bwd_dx(dy, w->codes, w->q8, w->a2, cb_of(w), dt_of(w), u, A, dx, (int)M, (int)N, (int)K,
+                                     r, s)) != QLORA_OK)
             return st;
     }
     // dA [K, r] = x^T u ; dB [r, N] = t^T dy, stored transposed from the [N, r] reduction
-    if ((st = launch_tn(x, u, reinterpret_cast<float*>(at(ws, L.pa)), dA, (int)M, (int)K, r, r, 1, s)) != QLORA_OK)
+    if ((st = launch_tn(x, u, reinterpret_cast<float*>(at(ws, L.pa)), dA, (int)M, (int)K, r, r, 1, dt_of(w), s)) !=
+        QLORA_OK)
         return st;
-    return launch_tn(dy, t, reinterpret_cast<float*>(at(ws, L.pb)), dB, (int)M, (int)N, r, 1, N, s);
+    return launch_tn(dy, t, reinterpret_cast<float*>(at(ws, L.pb)), dB, (int)M, (int)N, r, 1, N, dt_of(w), s);
 }
 
 // ---- QA-LoRA pooled branch: A [K/g, r]; the plain path runs on A~ = expand(A) / g
@@ -261,7 +270,7 @@ qlora_status qlora_pooled_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, 
     if (!ws || ws_bytes < head) return QLORA_ERR_WORKSPACE;
     if (!aligned16(ws)) return QLORA_ERR_MISALIGNED;
     uint16_t* Ax = reinterpret_cast<uint16_t*>(ws);
-    if ((st = launch_expand_pooled(A, (int)w->k, r, g, Ax, (hipStream_t)stream)) != QLORA_OK) return st;
+    if ((st = launch_expand_pooled(A, (int)w->k, r, g, dt_of(w), Ax, (hipStream_t)stream)) != QLORA_OK) return st;
     return qlora_linear_fwd(w, x, M, Ax, B, r, alpha, y, t_out, at(ws, head), ws_bytes - head, stream);
 }
 
@@ -279,7 +288,7 @@ qlora_status qlora_pooled_bwd(const qlora_nf4* w, const uint16_t* x, int64_t M, 
     hipStream_t s = (hipStream_t)stream;
     uint16_t* Ax = reinterpret_cast<uint16_t*>(ws);
     float* dAx = reinterpret_cast<float*>(at(ws, ha));
-    if ((st = launch_expand_pooled(A, (int)w->k, r, g, Ax, s)) != QLORA_OK) return st;
+    if ((st = launch_expand_pooled(A, (int)w->k, r, g, dt_of(w), Ax, s)) != QLORA_OK) return st;
     if ((st = qlora_linear_bwd(w, x, M, Ax, B, r, alpha, t, dy, dx, dAx, dB, at(ws, ha + hd), ws_bytes - ha - hd,
                                stream)) != QLORA_OK)
         return st;

@@ -1,6 +1,8 @@
 // Internal helpers shared by the HIP kernels of libqlora (gfx950 only).
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -70,6 +72,52 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, b);
 }
 
+// The 16-bit compute dtype of a layer's tensors (the dtype field of qlora_nf4;
+// "bitsandbytes deep dive" 8.3): bf16 (default) or IEEE fp16.
+constexpr int kDtBf16 = 0;
+constexpr int kDtF16 = 1;
+
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+// Exact value of a 16-bit pattern of dtype DT.
+template <int DT>
+__device__ __forceinline__ float h16_to_f32(uint32_t b16) {
+    if (DT == kDtF16) return (float)__builtin_bit_cast(_Float16, (uint16_t)b16);
+    return bf16_bits_to_f32(b16);
+}
+
+// Two floats -> packed pair of dtype DT (lo in bits 15..0), round to nearest even.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    if (DT == kDtF16) {
+        f32x2_t f = {lo, hi};
+        f16x2_t h = __builtin_convertvector(f, f16x2_t);
+        return __builtin_bit_cast(uint32_t, h);
+    }
+    return pack_bf16x2(lo, hi);
+}
+
+// Host-side dispatch from the runtime codebook and dtype to template
+// arguments: calls f(IntC<CB>{}, IntC<DT>{}).
+template <int V>
+using IntC = std::integral_constant<int, V>;
+template <typename F>
+inline void with_cb_dt(int cb, int dt, F&& f) {
+    if (cb == kCbFp4) {
+        if (dt == kDtF16) f(IntC<kCbFp4>{}, IntC<kDtF16>{});
+        else f(IntC<kCbFp4>{}, IntC<kDtBf16>{});
+    } else {
+        if (dt == kDtF16) f(IntC<kCbNf4>{}, IntC<kDtF16>{});
+        else f(IntC<kCbNf4>{}, IntC<kDtBf16>{});
+    }
+}
+template <typename F>
+inline void with_dt(int dt, F&& f) {
+    if (dt == kDtF16) f(IntC<kDtF16>{});
+    else f(IntC<kDtBf16>{});
+}
+
 // Round a float down (toward -inf) onto the bf16 grid; returned as a float.
 __device__ __forceinline__ float f32_rd_bf16(float f) {
     uint32_t u = __float_as_uint(f);
@@ -85,33 +133,34 @@ inline qlora_status launch_status() {
 }
 
 // Launchers (one per translation unit).
-// `cb` selects the codebook (kCbNf4, kCbFp4) of the codes the kernels read or write.
+// `cb` selects the codebook (kCbNf4, kCbFp4) of the codes the kernels read or
+// write, `dt` the compute dtype (kDtBf16, kDtF16) of every 16-bit tensor.
 qlora_status launch_quantize(const uint16_t* W, int64_t nblocks, uint8_t* codes, uint8_t* q8, float* a2, int cb,
-                             hipStream_t s);
-qlora_status launch_dequantize(const uint8_t* codes, const uint8_t* q8, const float* a2, int cb, int64_t nblocks,
-                               uint16_t* out, hipStream_t s);
-qlora_status launch_merge(const uint8_t* codes, const uint8_t* q8, const float* a2, int cb, const uint16_t* A,
+                             int dt, hipStream_t s);
+qlora_status launch_dequantize(const uint8_t* codes, const uint8_t* q8, const float* a2, int cb, int dt,
+                               int64_t nblocks, uint16_t* out, hipStream_t s);
+qlora_status launch_merge(const uint8_t* codes, const uint8_t* q8, const float* a2, int cb, int dt, const uint16_t* A,
                           const uint16_t* B, int r, float s, uint16_t* out, int N, int K, hipStream_t st);
 qlora_status launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* q8, const float* a2, int cb,
-                             const uint16_t* t, const uint16_t* B, uint16_t* y, int M, int N, int K, int r,
+                             int dt, const uint16_t* t, const uint16_t* B, uint16_t* y, int M, int N, int K, int r,
                              hipStream_t s);
 // Decode-size forward (1 <= M <= kGemvMaxM): same result as launch_gemm_fwd.
 constexpr int kGemvMaxM = 16;
 bool gemv_supported(int M, int N, int K, int r);
 qlora_status launch_gemv_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* q8, const float* a2, int cb,
-                             const uint16_t* t, const uint16_t* B, uint16_t* y, int M, int N, int K, int r,
+                             int dt, const uint16_t* t, const uint16_t* B, uint16_t* y, int M, int N, int K, int r,
                              hipStream_t s);
 qlora_status launch_gemm_bwd_dx(const uint16_t* dy, const uint8_t* codes, const uint8_t* q8, const float* a2,
-                                int cb, const uint16_t* u, const uint16_t* A, uint16_t* dx, int M, int N, int K, int r,
+                                int cb, int dt, const uint16_t* u, const uint16_t* A, uint16_t* dx, int M, int N, int K, int r,
                                 hipStream_t s);
 // out [M, r] = bf16(scale * X [M, C] Y), Y given as Yt [r, C] or, with y_natural, as [C, r]
 qlora_status launch_nt(const uint16_t* X, const uint16_t* Y, bool y_natural, float* part, uint16_t* out, float scale,
-                       int M, int C, int r, hipStream_t s);
+                       int M, int C, int r, int dt, hipStream_t s);
 // out[d * ld_d + j * ld_j] = sum_m X [M, D][m, d] * S [M, r][m, j]
 qlora_status launch_tn(const uint16_t* X, const uint16_t* S, float* part, float* out, int M, int D, int r,
-                       int64_t ld_d, int64_t ld_j, hipStream_t s);
+                       int64_t ld_d, int64_t ld_j, int dt, hipStream_t s);
 qlora_status launch_fill(float* out, int64_t count, float v, hipStream_t s);
-qlora_status launch_expand_pooled(const uint16_t* A, int K, int r, int g, uint16_t* out, hipStream_t s);
+qlora_status launch_expand_pooled(const uint16_t* A, int K, int r, int g, int dt, uint16_t* out, hipStream_t s);
 qlora_status launch_pool_rows(const float* in, int K, int r, int g, float* out, hipStream_t s);
 
 }  // namespace qlora

@@ -1,13 +1,13 @@
 // In-register 4-bit dequantization for the fused GEMM kernels.
 //
 // A weight block (64 codes of one row) has one reconstructed scale
-// a_hat = fl32(fl32(a2/255) * q8), so its 16 possible bf16 values
-// RNE_bf16(fl32(a_hat * c_j)) form a per-block table (c: the NF4 or the FP4
-// codebook).  The table is kept as
-// two 16-byte byte tables (low bytes, high bytes of the 16 bf16 entries) in 8
+// a_hat = fl32(fl32(a2/255) * q8), so its 16 possible 16-bit values
+// RNE_16(fl32(a_hat * c_j)) form a per-block table (c: the NF4 or the FP4
+// codebook; 16-bit: the bf16 or fp16 compute dtype).  The table is kept as
+// two 16-byte byte tables (low bytes, high bytes of the 16 entries) in 8
 // VGPRs; v_perm_b32 looks up 4 codes at once in each 8-entry half, and an AND
 // keeps the half that holds the code.  Every dequantized value is exactly the
-// bf16 that qlora_dequantize produces ("bitsandbytes deep dive" 5.2:
+// value that qlora_dequantize produces ("bitsandbytes deep dive" 5.2:
 // w_hat = a * c_q).
 #pragma once
 
@@ -37,11 +37,11 @@ struct Nf4Tab {
     uint32_t hi[4];  // byte i of hi[q] = high byte of entry 4q + i
 };
 
-template <int CB>
+template <int CB, int DT>
 __device__ __forceinline__ Nf4Tab make_tab(float ahat) {
     uint32_t e[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] = pack_bf16x2(ahat * level<CB>(2 * j), ahat * level<CB>(2 * j + 1));
+    for (int j = 0; j < 8; ++j) e[j] = pack2<DT>(ahat * level<CB>(2 * j), ahat * level<CB>(2 * j + 1));
     Nf4Tab T;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {

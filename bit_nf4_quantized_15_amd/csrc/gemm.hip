@@ -39,7 +39,12 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8, v); }
 
+// 32x32x16 MFMA on operands of the compute dtype DT (bf16 or fp16 bit patterns).
+template <int DT>
 __device__ __forceinline__ f32x16_t mfma32(bf16x8 a, bf16x8 b, f32x16_t c) {
+    if (DT == kDtF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
+                                                      c, 0, 0, 0);
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
@@ -224,6 +229,7 @@ __device__ __forceinline__ bf16x8 row8(const uint16_t* __restrict__ src, int64_t
 // Store an fp32 accumulator tile (this wave: 8 x 32-row tiles times 2 x 32-col
 // tiles) as bf16.  Lane l of a 32x32 tile holds column l%32 and rows
 // 8*(v/4) + 4*(l/32) + v%4 for v = 0..15.
+template <int DT>
 __device__ __forceinline__ void store_acc(uint16_t* __restrict__ out, int64_t ld, const f32x16_t (&acc)[8][2],
                                           int m0, int M, const int (&col)[2], const bool (&col_ok)[2], int h) {
     const int l32 = threadIdx.x & 31;
@@ -236,7 +242,7 @@ __device__ __forceinline__ void store_acc(uint16_t* __restrict__ out, int64_t ld
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int m = m0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-                if (m < M) out[(int64_t)m * ld + col[t]] = (uint16_t)(pack_bf16x2(acc[i][t][v], 0.0f) & 0xFFFFu);
+                if (m < M) out[(int64_t)m * ld + col[t]] = (uint16_t)(pack2<DT>(acc[i][t][v], 0.0f) & 0xFFFFu);
             }
         }
     }
@@ -258,7 +264,7 @@ __device__ __forceinline__ void store_acc(uint16_t* __restrict__ out, int64_t ld
 constexpr int kSup = 2;                                     // blocks per super-step
 constexpr int kCodeTileBytes = kTN * kSup * kBlock / 2;     // 256 rows x 64 B
 
-template <bool Q8DW, bool DQ, int CB>
+template <bool Q8DW, bool DQ, int CB, int DT>
 __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ q8,
     const float* __restrict__ a2, const uint16_t* __restrict__ t, const uint16_t* __restrict__ Bl,
@@ -411,7 +417,7 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
     u32x4_t cc[2];
     bf16x8 b[2][2];
     bf16x8 a[2][4];  // A operands by half chunk: row tiles 4 half .. 4 half + 3 of chunk c
-    share_tabs(make_tab<CB>(ahs0[kSup * crl[h]]), T[0], T[1]);
+    share_tabs(make_tab<CB, DT>(ahs0[kSup * crl[h]]), T[0], T[1]);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         cc[u] = read_codes(cds0, 0, u);
@@ -468,8 +474,8 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                acc[4 * half + i][0] = mfma32(a[half][i], b[p][0], acc[4 * half + i][0]);
-                acc[4 * half + i][1] = mfma32(a[half][i], b[p][1], acc[4 * half + i][1]);
+                acc[4 * half + i][0] = mfma32<DT>(a[half][i], b[p][0], acc[4 * half + i][0]);
+                acc[4 * half + i][1] = mfma32<DT>(a[half][i], b[p][1], acc[4 * half + i][1]);
             }
             if (half == 0) b[p ^ 1][0] = as_bf16x8(c < 3 ? deq8(T[0], cc[0][c + 1]) : deq8(Tn[0], cn[0][0]));
             else b[p ^ 1][1] = as_bf16x8(c < 3 ? deq8(T[1], cc[1][c + 1]) : deq8(Tn[1], cn[1][0]));
@@ -477,7 +483,7 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
             if (hc == 2 || hc == 3) {
 #pragma unroll
                 for (int q = 4 * (hc - 2); q < 4 * (hc - 2) + 4; ++q)
-                    e[q] = pack_bf16x2(ahn * level<CB>(2 * q), ahn * level<CB>(2 * q + 1));
+                    e[q] = pack2<DT>(ahn * level<CB>(2 * q), ahn * level<CB>(2 * q + 1));
 #pragma unroll
                 for (int q = 2 * (hc - 2); q < 2 * (hc - 2) + 2; ++q) {
                     mine.lo[q] = perm_b32(e[2 * q + 1], e[2 * q], 0x06040200u);
@@ -576,8 +582,8 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const bf16x8 av = *reinterpret_cast<const bf16x8*>(xt0 + offA[c] + 4096u * i);
-                acc[i][0] = mfma32(av, bl[0], acc[i][0]);
-                acc[i][1] = mfma32(av, bl[1], acc[i][1]);
+                acc[i][0] = mfma32<DT>(av, bl[0], acc[i][0]);
+                acc[i][1] = mfma32<DT>(av, bl[1], acc[i][1]);
             }
         }
         __syncthreads();
@@ -588,7 +594,7 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
     // each thread stores 16-byte row chunks
     if (!nvec) {
         const bool col_ok[2] = {col_ok0, col_ok1};
-        store_acc(y, N, acc, m0, M, col, col_ok, h);
+        store_acc<DT>(y, N, acc, m0, M, col, col_ok, h);
         return;
     }
 #pragma unroll
@@ -602,7 +608,7 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
                 for (int v = 0; v < 16; ++v) {
                     const int row = 32 * ii + 8 * (v >> 2) + 4 * h + (v & 3);
                     *reinterpret_cast<uint16_t*>((row < 64 ? xt0 : xt1) + (row & 63) * 512 + 2 * crl[u]) =
-                        (uint16_t)(pack_bf16x2(acc[i][u][v], 0.0f) & 0xFFFFu);
+                        (uint16_t)(pack2<DT>(acc[i][u][v], 0.0f) & 0xFFFFu);
                 }
         }
         __syncthreads();
@@ -637,7 +643,7 @@ __device__ __forceinline__ uint32_t wtile_off(int row, int col) {
     return (uint32_t)row * 512u + ((uint32_t)((col >> 3) ^ f) << 4) + ((uint32_t)(col & 7) << 1);
 }
 
-template <bool DYVEC, bool DQ, int CB>
+template <bool DYVEC, bool DQ, int CB, int DT>
 __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
     const uint16_t* __restrict__ dy, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ q8,
     const float* __restrict__ a2, const uint16_t* __restrict__ u_, const uint16_t* __restrict__ Al,
@@ -699,7 +705,7 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
         return scale_step(S.g) * (float)(S.ok ? q : 0u);
     };
     auto expand = [&](const Step& S, u32x4_t (&out)[8]) {
-        const Nf4Tab T = make_tab<CB>(ahat_of(S));
+        const Nf4Tab T = make_tab<CB, DT>(ahat_of(S));
 #pragma unroll
         for (int d = 0; d < 8; ++d) out[d] = deq8(T, d < 4 ? S.c0[d] : S.c1[d - 4]);
     };
@@ -789,7 +795,7 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
         Step nn;
         load_step(min(ns + 2, NS - 1), nn);  // kStepLoads loads: codes (2), scale data
         u32x4_t w[8];
-        const Nf4Tab T = make_tab<CB>(ahat_of(nxt));
+        const Nf4Tab T = make_tab<CB, DT>(ahat_of(nxt));
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int p = c & 1;
@@ -798,12 +804,12 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int u = 0; u < 4; ++u) acc[i][u] = mfma32(a[p][i], b[p][u], acc[i][u]);
+                for (int u = 0; u < 4; ++u) acc[i][u] = mfma32<DT>(a[p][i], b[p][u], acc[i][u]);
             w[2 * c + 1] = deq8(T, c < 2 ? nxt.c0[2 * c + 1] : nxt.c1[2 * c - 3]);
 #pragma unroll
             for (int i = 2; i < 4; ++i)
 #pragma unroll
-                for (int u = 0; u < 4; ++u) acc[i][u] = mfma32(a[p][i], b[p][u], acc[i][u]);
+                for (int u = 0; u < 4; ++u) acc[i][u] = mfma32<DT>(a[p][i], b[p][u], acc[i][u]);
             if (c < 3) QLORA_INTERLEAVE(12); else QLORA_INTERLEAVE(0);
         }
         store_w(Bn, w);
@@ -841,7 +847,7 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int u = 0; u < 4; ++u) acc[i][u] = mfma32(a[i], b[u], acc[i][u]);
+                for (int u = 0; u < 4; ++u) acc[i][u] = mfma32<DT>(a[i], b[u], acc[i][u]);
         }
         __syncthreads();
     }
@@ -857,7 +863,7 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
             for (int v = 0; v < 16; ++v) {
                 const int row = 128 * wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
                 *reinterpret_cast<uint16_t*>(lds + row * 512 + 2 * (128 * wk + 32 * u + l32)) =
-                    (uint16_t)(pack_bf16x2(acc[i][u][v], 0.0f) & 0xFFFFu);
+                    (uint16_t)(pack2<DT>(acc[i][u][v], 0.0f) & 0xFFFFu);
             }
     __syncthreads();
 #pragma unroll
@@ -872,9 +878,9 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
 }  // namespace
 
 qlora_status launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* q8, const float* a2, int cb,
-                             const uint16_t* t, const uint16_t* B, uint16_t* y, int M, int N, int K, int r,
+                             int dt, const uint16_t* t, const uint16_t* B, uint16_t* y, int M, int N, int K, int r,
                              hipStream_t s) {
-    if (gemv_supported(M, N, K, r)) return launch_gemv_fwd(x, codes, q8, a2, cb, t, B, y, M, N, K, r, s);
+    if (gemv_supported(M, N, K, r)) return launch_gemv_fwd(x, codes, q8, a2, cb, dt, t, B, y, M, N, K, r, s);
     const int tm = (M + kTM - 1) / kTM, tn = (N + kTN - 1) / kTN;
     // x is 16-byte aligned (checked by the caller) and K % 64 == 0, so every
     // 16-byte chunk of a row is aligned; a 256-row panel must fit a 32-bit offset
@@ -882,47 +888,41 @@ qlora_status launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const uint
     // code-tile offsets (including blocks past a row's end) must fit a 32-bit voffset
     if ((uint64_t)N * (uint64_t)K / 2 + 4096 >= (uint64_t(1) << 32)) return QLORA_ERR_UNSUPPORTED_SHAPE;
     // q8 == NULL: no double quantization, a2 holds one fp32 absmax per block
-#define QL_FWD1(Q8DW, DQ, CB)                                                                                  \
-    hipLaunchKernelGGL((nf4_gemm_fwd_kernel<Q8DW, DQ, CB>), dim3(tm * tn), dim3(kT), 0, s, x, codes, q8, a2, t, B, y, \
-                       M, N, K, r, tm, tn)
-#define QL_FWD(Q8DW, DQ)                           \
-    do {                                           \
-        if (cb == kCbFp4) QL_FWD1(Q8DW, DQ, kCbFp4); \
-        else QL_FWD1(Q8DW, DQ, kCbNf4);            \
-    } while (0)
     const bool even = (K / kTK) % kSup == 0;
-    if (q8) {
-        if (even) QL_FWD(true, true); else QL_FWD(false, true);
-    } else {
-        if (even) QL_FWD(true, false); else QL_FWD(false, false);
-    }
+    with_cb_dt(cb, dt, [&](auto cbc, auto dtc) {
+        constexpr int CB = decltype(cbc)::value, DT = decltype(dtc)::value;
+#define QL_FWD(Q8DW, DQ)                                                                                       \
+    hipLaunchKernelGGL((nf4_gemm_fwd_kernel<Q8DW, DQ, CB, DT>), dim3(tm * tn), dim3(kT), 0, s, x, codes, q8, a2, t, \
+                       B, y, M, N, K, r, tm, tn)
+        if (q8) {
+            if (even) QL_FWD(true, true); else QL_FWD(false, true);
+        } else {
+            if (even) QL_FWD(true, false); else QL_FWD(false, false);
+        }
 #undef QL_FWD
-#undef QL_FWD1
+    });
     return launch_status();
 }
 
 qlora_status launch_gemm_bwd_dx(const uint16_t* dy, const uint8_t* codes, const uint8_t* q8, const float* a2,
-                                int cb, const uint16_t* u, const uint16_t* A, uint16_t* dx, int M, int N, int K, int r,
-                                hipStream_t s) {
+                                int cb, int dt, const uint16_t* u, const uint16_t* A, uint16_t* dx, int M, int N, int K,
+                                int r, hipStream_t s) {
     const int tm = (M + kTM - 1) / kTM, tk = (K + kTN - 1) / kTN;
     const bool vec = (N % 8 == 0) && ((reinterpret_cast<uintptr_t>(dy) & 15u) == 0) &&
                      ((int64_t)kTM * N * 2 < (int64_t(1) << 32));
     // q8 == NULL: no double quantization, a2 holds one fp32 absmax per block
-#define QL_BWD1(V, DQ, CB)                                                                                      \
-    hipLaunchKernelGGL((nf4_gemm_bwd_dx_kernel<V, DQ, CB>), dim3(tm * tk), dim3(kT), 0, s, dy, codes, q8, a2, u, A, dx, \
-                       M, N, K, r, tm, tk)
-#define QL_BWD(V, DQ)                           \
-    do {                                        \
-        if (cb == kCbFp4) QL_BWD1(V, DQ, kCbFp4); \
-        else QL_BWD1(V, DQ, kCbNf4);            \
-    } while (0)
-    if (q8) {
-        if (vec) QL_BWD(true, true); else QL_BWD(false, true);
-    } else {
-        if (vec) QL_BWD(true, false); else QL_BWD(false, false);
-    }
+    with_cb_dt(cb, dt, [&](auto cbc, auto dtc) {
+        constexpr int CB = decltype(cbc)::value, DT = decltype(dtc)::value;
+#define QL_BWD(V, DQ)                                                                                           \
+    hipLaunchKernelGGL((nf4_gemm_bwd_dx_kernel<V, DQ, CB, DT>), dim3(tm * tk), dim3(kT), 0, s, dy, codes, q8, a2, u, \
+                       A, dx, M, N, K, r, tm, tk)
+        if (q8) {
+            if (vec) QL_BWD(true, true); else QL_BWD(false, true);
+        } else {
+            if (vec) QL_BWD(true, false); else QL_BWD(false, false);
+        }
 #undef QL_BWD
-#undef QL_BWD1
+    });
     return launch_status();
 }
 

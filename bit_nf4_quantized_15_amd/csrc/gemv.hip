@@ -97,7 +97,16 @@ struct GvPlan {
     int tsh;     // log2 of the threads that stage one x row
 };
 
-template <int NV, int NG, bool DQ, int CB>
+// 16x16x32 MFMA on operands of the compute dtype DT (bf16 or fp16 bit patterns).
+template <int DT>
+__device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+    if (DT == kDtF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
+                                                      c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int NV, int NG, bool DQ, int CB, int DT>
 __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const uint16_t* __restrict__ x,
                                                               const uint8_t* __restrict__ codes,
                                                               const uint8_t* __restrict__ q8,
@@ -251,7 +260,7 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const uint16_t* __
     {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            const uint32_t v = pack_bf16x2(level<CB>(j), lo_level);
+            const uint32_t v = pack2<DT>(level<CB>(j), lo_level);
             *reinterpret_cast<u32x4_t*>(lut + 16 * (tid + 256 * j)) = u32x4_t{v, v, v, v};
         }
     }
@@ -299,9 +308,8 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const uint16_t* __
                     w0[jj] = *reinterpret_cast<const uint32_t*>(lut + __builtin_amdgcn_perm(c.x, lane4, sel));
                     w1[jj] = *reinterpret_cast<const uint32_t*>(lut + __builtin_amdgcn_perm(c.y, lane4, sel));
                 }
-                f32x4_t part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(bf16x8_t, w0),
-                                                                       f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-                part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8_t, w1), part, 0, 0, 0);
+                f32x4_t part = mfma16<DT>(a0, __builtin_bit_cast(bf16x8_t, w0), f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
+                part = mfma16<DT>(a1, __builtin_bit_cast(bf16x8_t, w1), part);
                 // blocks past the row end have a_hat = 0; their x and codes are
                 // staged values or zeros (finite), so they add exactly nothing
 #pragma unroll
@@ -316,7 +324,7 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const uint16_t* __
             bf16x8_t, *reinterpret_cast<const u32x4_t*>(tl + 2 * (xrow * 128 + 32 * w + 8 * lg)));
         const bf16x8_t tb = __builtin_bit_cast(
             bf16x8_t, *reinterpret_cast<const u32x4_t*>(bl + ln * 128 + 32 * w + 8 * lg));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ta, tb, acc, 0, 0, 0);
+        acc = mfma16<DT>(ta, tb, acc);
     }
 
     // sum of the 4 waves' partial tiles and the bf16 store
@@ -333,7 +341,7 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const uint16_t* __
         float s = red[(0 * 16 + m) * 16 + n] + red[(1 * 16 + m) * 16 + n];
         s += red[(2 * 16 + m) * 16 + n] + red[(3 * 16 + m) * 16 + n];
         if (n0 + n < N) {
-            const uint32_t o = pack_bf16x2(s, 0.0f);
+            const uint32_t o = pack2<DT>(s, 0.0f);
             y[(int64_t)m * N + n0 + n] = (uint16_t)(o & 0xFFFFu);
         }
     }
@@ -346,7 +354,7 @@ bool gemv_supported(int M, int N, int K, int r) {
 }
 
 qlora_status launch_gemv_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* q8, const float* a2, int cb,
-                             const uint16_t* t, const uint16_t* B, uint16_t* y, int M, int N, int K, int r,
+                             int dt, const uint16_t* t, const uint16_t* B, uint16_t* y, int M, int N, int K, int r,
                              hipStream_t s) {
     if (!gemv_supported(M, N, K, r)) return QLORA_ERR_UNSUPPORTED_SHAPE;
     GvPlan P;
@@ -369,24 +377,22 @@ qlora_status launch_gemv_fwd(const uint16_t* x, const uint8_t* codes, const uint
     const dim3 grid((unsigned)((N + kGvRows - 1) / kGvRows));
     const int nv = M == 1 ? 1 : M == 2 ? 2 : 4;
     // q8 == NULL: no double quantization, a2 holds one fp32 absmax per block
-#define QLORA_GEMV1(NV_, NG_, DQ_, CB_)                                                                         \
-    hipLaunchKernelGGL((nf4_gemv_kernel<NV_, NG_, DQ_, CB_>), grid, dim3(kGvThreads), 0, s, x, codes, q8, a2, t, B, y, \
-                       M, N, K, r, P)
-#define QLORA_GEMV(NV_, NG_)                                           \
-    if (nv == NV_ && ng == NG_) {                                      \
-        if (q8) {                                                      \
-            if (cb == kCbFp4) QLORA_GEMV1(NV_, NG_, true, kCbFp4);     \
-            else QLORA_GEMV1(NV_, NG_, true, kCbNf4);                  \
-        } else {                                                       \
-            if (cb == kCbFp4) QLORA_GEMV1(NV_, NG_, false, kCbFp4);    \
-            else QLORA_GEMV1(NV_, NG_, false, kCbNf4);                 \
-        }                                                              \
+    with_cb_dt(cb, dt, [&](auto cbc, auto dtc) {
+        constexpr int CB = decltype(cbc)::value, DT = decltype(dtc)::value;
+#define QLORA_GEMV1(NV_, NG_, DQ_)                                                                                 \
+    hipLaunchKernelGGL((nf4_gemv_kernel<NV_, NG_, DQ_, CB, DT>), grid, dim3(kGvThreads), 0, s, x, codes, q8, a2, t, B, \
+                       y, M, N, K, r, P)
+#define QLORA_GEMV(NV_, NG_)                                 \
+    if (nv == NV_ && ng == NG_) {                            \
+        if (q8) QLORA_GEMV1(NV_, NG_, true);                 \
+        else QLORA_GEMV1(NV_, NG_, false);                   \
     }
-    QLORA_GEMV(1, 1) QLORA_GEMV(1, 2) QLORA_GEMV(1, 4)
-    QLORA_GEMV(2, 1) QLORA_GEMV(2, 2) QLORA_GEMV(2, 4)
-    QLORA_GEMV(4, 1) QLORA_GEMV(4, 2) QLORA_GEMV(4, 4)
+        QLORA_GEMV(1, 1) QLORA_GEMV(1, 2) QLORA_GEMV(1, 4)
+        QLORA_GEMV(2, 1) QLORA_GEMV(2, 2) QLORA_GEMV(2, 4)
+        QLORA_GEMV(4, 1) QLORA_GEMV(4, 2) QLORA_GEMV(4, 4)
 #undef QLORA_GEMV
 #undef QLORA_GEMV1
+    });
     return launch_status();
 }
 

@@ -21,7 +21,12 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
+// 32x32x16 MFMA on operands of the compute dtype DT (bf16 or fp16 bit patterns).
+template <int DT>
 __device__ __forceinline__ f32x16_t mfma32(bf16x8 a, bf16x8 b, f32x16_t c) {
+    if (DT == kDtF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
+                                                      c, 0, 0, 0);
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
@@ -130,7 +135,7 @@ constexpr int nt_slice_elems() {
     return YNAT ? kNtMaxChunk * slice_ld<TQ>() : 32 * TQ * (kNtMaxChunk + 8);
 }
 
-template <int TQ, bool VEC, bool YNAT, int NST>
+template <int TQ, bool VEC, bool YNAT, int NST, int DT>
 __global__ __launch_bounds__(256) void nt_partial_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Y,
                                                          float* __restrict__ part, int M, int C, int r, int chunk) {
     constexpr int kLdT = kNtMaxChunk + 8;  // Yt row (bf16)
@@ -213,7 +218,7 @@ __global__ __launch_bounds__(256) void nt_partial_kernel(const uint16_t* __restr
                 const int c = 64 * st + 32 * h + 8 * i;  // slice column of the lane's k slots
                 const bf16x8 yb = YNAT ? slice_col8(ys, kLdN, c, 32 * q + 16 * tg, tj)
                                        : *reinterpret_cast<const bf16x8*>(&ys[(32 * q + l32) * kLdT + c]);
-                acc[q] = mfma32(ca[i], yb, acc[q]);
+                acc[q] = mfma32<DT>(ca[i], yb, acc[q]);
             }
     }
     float* out = part + (int64_t)split * M * r;
@@ -253,13 +258,15 @@ __device__ __forceinline__ float sum_splits(const float* __restrict__ part, int 
     return (red[0][o] + red[1][o]) + (red[2][o] + red[3][o]);
 }
 
-// out[m, j] = bf16( s * sum_split part[split, m, j] ); 256 threads per 64 outputs
-__global__ __launch_bounds__(256) void finalize_bf16_kernel(const float* __restrict__ part, int splits, int M, int r,
+// out[m, j] = RNE_16( s * sum_split part[split, m, j] ) in the compute dtype DT;
+// 256 threads per 64 outputs
+template <int DT>
+__global__ __launch_bounds__(256) void finalize_16_kernel(const float* __restrict__ part, int splits, int M, int r,
                                                             float s, uint16_t* __restrict__ out) {
     const int64_t count = (int64_t)M * r;
     const int64_t i = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
     const float v = sum_splits(part, splits, count, i, i < count);
-    if (threadIdx.x < 64 && i < count) out[i] = (uint16_t)(pack_bf16x2(s * v, 0.0f) & 0xFFFFu);
+    if (threadIdx.x < 64 && i < count) out[i] = (uint16_t)(pack2<DT>(s * v, 0.0f) & 0xFFFFu);
 }
 
 // part[split, d, j] = sum over m in the split's range of X[m, d] * S[m, j]
@@ -273,7 +280,7 @@ __global__ __launch_bounds__(256) void finalize_bf16_kernel(const float* __restr
 constexpr int kTnRows = 64, kTnCols = 128, kTnLd = kTnCols + 32;  // 320-byte rows: conflict-free transposed reads
 constexpr int kTnRing = 4;
 
-template <int TQ, bool VEC>
+template <int TQ, bool VEC, int DT>
 __global__ __launch_bounds__(256) void tn_partial_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ S,
                                                          float* __restrict__ part, int M, int D, int r, int chunk) {
     constexpr int kTnMaxChunk = TQ <= 3 ? 512 : 256;  // = tn_max_chunk(r) for r in (32 (TQ-1), 32 TQ]
@@ -336,7 +343,7 @@ __global__ __launch_bounds__(256) void tn_partial_kernel(const uint16_t* __restr
 #pragma unroll
                 for (int q = 0; q < TQ; ++q) {
                     const bf16x8 b = slice_col8(ss, kSLd, kTnRows * st + mr, 32 * q + 16 * tg, tj);
-                    acc[q] = mfma32(a, b, acc[q]);
+                    acc[q] = mfma32<DT>(a, b, acc[q]);
                 }
             }
             __syncthreads();
@@ -372,13 +379,14 @@ __global__ __launch_bounds__(256) void reduce_f32_kernel(const float* __restrict
 // of two (a shift of the exponent) unless it underflows, so the plain kernels run on A~; the
 // gradient of A sums each group of g rows of the gradient of A~:
 // dA[i, j] = (1/g) sum_{q < g} dA~[g i + q, j], q ascending, in fp32.
+template <int DT>
 __global__ void expand_pooled_kernel(const uint16_t* __restrict__ A, int64_t count, int r, int g_log2,
                                      uint16_t* __restrict__ out) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= count) return;
     const int64_t k = i / r, j = i - k * r;
-    const float v = bf16_bits_to_f32(A[(k >> g_log2) * r + j]) * __uint_as_float((uint32_t)(127 - g_log2) << 23);
-    out[i] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+    const float v = h16_to_f32<DT>(A[(k >> g_log2) * r + j]) * __uint_as_float((uint32_t)(127 - g_log2) << 23);
+    out[i] = (uint16_t)(pack2<DT>(v, 0.0f) & 0xFFFFu);
 }
 
 __global__ void pool_rows_kernel(const float* __restrict__ in, int64_t count, int r, int g, int g_log2,
@@ -401,7 +409,7 @@ inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1)
 }  // namespace
 
 qlora_status launch_nt(const uint16_t* X, const uint16_t* Y, bool y_natural, float* part, uint16_t* out,
-                       float scale, int M, int C, int r, hipStream_t s) {
+                       float scale, int M, int C, int r, int dt, hipStream_t s) {
     const SplitPlan sp = plan_nt(M, C);
     const dim3 grid((unsigned)((M + 127) / 128), (unsigned)sp.splits);
     // vector path: 16-byte aligned rows, and one workgroup's rows (128 of X, r of
@@ -410,48 +418,54 @@ qlora_status launch_nt(const uint16_t* X, const uint16_t* Y, bool y_natural, flo
                      ((reinterpret_cast<uintptr_t>(Y) & 15u) == 0) && (int64_t)C * 128 * 2 < (int64_t(1) << 30);
     const int tq = (r + 31) / 32;
     const bool short_split = sp.chunk <= 64 * kNtRing;
-#define QL_NT(TQ, V, NAT)                                                                                            \
-    if (short_split) hipLaunchKernelGGL((nt_partial_kernel<TQ, V, NAT, kNtRing>), grid, dim3(256), 0, s, X, Y, part, M, \
-                                        C, r, sp.chunk);                                                             \
-    else hipLaunchKernelGGL((nt_partial_kernel<TQ, V, NAT, 2 * kNtRing>), grid, dim3(256), 0, s, X, Y, part, M, C, r,  \
-                            sp.chunk);
+#define QL_NT(TQ, V, NAT)                                                                                          \
+    if (short_split) hipLaunchKernelGGL((nt_partial_kernel<TQ, V, NAT, kNtRing, DT>), grid, dim3(256), 0, s, X, Y, part, \
+                                        M, C, r, sp.chunk);                                                        \
+    else hipLaunchKernelGGL((nt_partial_kernel<TQ, V, NAT, 2 * kNtRing, DT>), grid, dim3(256), 0, s, X, Y, part, M, C, \
+                            r, sp.chunk);
 #define QL_NT2(TQ)                                    \
     if (y_natural) {                                  \
         if (vec) { QL_NT(TQ, true, true) } else { QL_NT(TQ, false, true) } \
     } else {                                          \
         if (vec) { QL_NT(TQ, true, false) } else { QL_NT(TQ, false, false) } \
     }
-    switch (tq) {
-        case 1: QL_NT2(1) break;
-        case 2: QL_NT2(2) break;
-        case 3: QL_NT2(3) break;
-        default: QL_NT2(4) break;
-    }
+    const int64_t count = (int64_t)M * r;
+    with_dt(dt, [&](auto dtc) {
+        constexpr int DT = decltype(dtc)::value;
+        switch (tq) {
+            case 1: QL_NT2(1) break;
+            case 2: QL_NT2(2) break;
+            case 3: QL_NT2(3) break;
+            default: QL_NT2(4) break;
+        }
+        hipLaunchKernelGGL(finalize_16_kernel<DT>, dim3(blocks_for(count, 64)), dim3(256), 0, s, part, sp.splits, M, r,
+                           scale, out);
+    });
 #undef QL_NT2
 #undef QL_NT
-    const int64_t count = (int64_t)M * r;
-    hipLaunchKernelGGL(finalize_bf16_kernel, dim3(blocks_for(count, 64)), dim3(256), 0, s, part, sp.splits, M, r,
-                       scale, out);
     return launch_status();
 }
 
 qlora_status launch_tn(const uint16_t* X, const uint16_t* S, float* part, float* out, int M, int D, int r,
-                       int64_t ld_d, int64_t ld_j, hipStream_t s) {
+                       int64_t ld_d, int64_t ld_j, int dt, hipStream_t s) {
     const SplitPlan sp = plan_tn(M, D, r);
     const dim3 grid((unsigned)((D + kTnCols - 1) / kTnCols), (unsigned)sp.splits);
     // vector path: 16-byte aligned rows, and one split's rows of X under 1 GiB
     const bool vec = (D % 8 == 0) && (r % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15u) == 0) &&
                      ((reinterpret_cast<uintptr_t>(S) & 15u) == 0) && (int64_t)D * 512 * 2 < (int64_t(1) << 30);
     const int tq = (r + 31) / 32;
-#define QL_TN(TQ)                                                                                                \
-    if (vec) hipLaunchKernelGGL((tn_partial_kernel<TQ, true>), grid, dim3(256), 0, s, X, S, part, M, D, r, sp.chunk); \
-    else hipLaunchKernelGGL((tn_partial_kernel<TQ, false>), grid, dim3(256), 0, s, X, S, part, M, D, r, sp.chunk);
-    switch (tq) {
-        case 1: QL_TN(1) break;
-        case 2: QL_TN(2) break;
-        case 3: QL_TN(3) break;
-        default: QL_TN(4) break;
-    }
+#define QL_TN(TQ)                                                                                                   \
+    if (vec) hipLaunchKernelGGL((tn_partial_kernel<TQ, true, DT>), grid, dim3(256), 0, s, X, S, part, M, D, r, sp.chunk); \
+    else hipLaunchKernelGGL((tn_partial_kernel<TQ, false, DT>), grid, dim3(256), 0, s, X, S, part, M, D, r, sp.chunk);
+    with_dt(dt, [&](auto dtc) {
+        constexpr int DT = decltype(dtc)::value;
+        switch (tq) {
+            case 1: QL_TN(1) break;
+            case 2: QL_TN(2) break;
+            case 3: QL_TN(3) break;
+            default: QL_TN(4) break;
+        }
+    });
 #undef QL_TN
     const int64_t count = (int64_t)D * r;
     hipLaunchKernelGGL(reduce_f32_kernel, dim3(blocks_for(count, 64)), dim3(256), 0, s, part, sp.splits, D, r, ld_d,
@@ -459,10 +473,14 @@ qlora_status launch_tn(const uint16_t* X, const uint16_t* S, float* part, float*
     return launch_status();
 }
 
-qlora_status launch_expand_pooled(const uint16_t* A, int K, int r, int g, uint16_t* out, hipStream_t s) {
+qlora_status launch_expand_pooled(const uint16_t* A, int K, int r, int g, int dt, uint16_t* out, hipStream_t s) {
     const int64_t count = (int64_t)K * r;
     const int g_log2 = __builtin_ctz((unsigned)g);
-    hipLaunchKernelGGL(expand_pooled_kernel, dim3(blocks_for(count, 256)), dim3(256), 0, s, A, count, r, g_log2, out);
+    with_dt(dt, [&](auto dtc) {
+        constexpr int DT = decltype(dtc)::value;
+        hipLaunchKernelGGL(expand_pooled_kernel<DT>, dim3(blocks_for(count, 256)), dim3(256), 0, s, A, count, r, g_log2,
+                           out);
+    });
     return launch_status();
 }
 

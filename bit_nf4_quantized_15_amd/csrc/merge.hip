@@ -23,7 +23,7 @@ namespace {
 constexpr int kMT = 64;       // tile rows (n) and columns (k): one NF4 block of columns
 constexpr int kMaxR = 128;
 
-template <bool DQ, int CB>
+template <bool DQ, int CB, int DT>
 __global__ __launch_bounds__(256) void nf4_merge_kernel(const uint8_t* __restrict__ codes,
                                                         const uint8_t* __restrict__ q8, const float* __restrict__ a2,
                                                         const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
@@ -34,11 +34,11 @@ __global__ __launch_bounds__(256) void nf4_merge_kernel(const uint8_t* __restric
     const int n0 = blockIdx.y * kMT, kb = blockIdx.x, k0 = kb * kMT;
     for (int i = tid; i < r * kMT; i += 256) {
         const int kk = i / r, j = i - kk * r;  // consecutive lanes read consecutive elements of A's rows
-        As[j][kk] = bf16_bits_to_f32(A[(int64_t)(k0 + kk) * r + j]);
+        As[j][kk] = h16_to_f32<DT>(A[(int64_t)(k0 + kk) * r + j]);
     }
     for (int i = tid; i < r * kMT; i += 256) {
         const int j = i / kMT, nn = i - j * kMT;
-        Bs[j][nn] = n0 + nn < N ? bf16_bits_to_f32(B[(int64_t)j * N + n0 + nn]) : 0.0f;
+        Bs[j][nn] = n0 + nn < N ? h16_to_f32<DT>(B[(int64_t)j * N + n0 + nn]) : 0.0f;
     }
     __syncthreads();
 
@@ -74,11 +74,11 @@ __global__ __launch_bounds__(256) void nf4_merge_kernel(const uint8_t* __restric
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const uint32_t code = h == 0 ? byte >> 4 : byte & 0xFu;
-                const uint32_t wh = pack_bf16x2(__fmul_rn(ahat, level<CB>((int)code)), 0.0f) & 0xFFFFu;
+                const uint32_t wh = pack2<DT>(__fmul_rn(ahat, level<CB>((int)code)), 0.0f) & 0xFFFFu;
                 const float corr = __fmul_rn(s, acc[i][2 * e2 + h]);
-                v[h] = __fadd_rn(bf16_bits_to_f32(wh), corr);
+                v[h] = __fadd_rn(h16_to_f32<DT>(wh), corr);
             }
-            o[e2] = pack_bf16x2(v[0], v[1]);
+            o[e2] = pack2<DT>(v[0], v[1]);
         }
         *reinterpret_cast<uint2*>(out + (int64_t)n * K + k0 + 4 * tk) = uint2{o[0], o[1]};
     }
@@ -86,18 +86,19 @@ __global__ __launch_bounds__(256) void nf4_merge_kernel(const uint8_t* __restric
 
 }  // namespace
 
-qlora_status launch_merge(const uint8_t* codes, const uint8_t* q8, const float* a2, int cb, const uint16_t* A,
+qlora_status launch_merge(const uint8_t* codes, const uint8_t* q8, const float* a2, int cb, int dt, const uint16_t* A,
                           const uint16_t* B, int r, float s, uint16_t* out, int N, int K, hipStream_t st) {
     if (r < 1 || r > kMaxR) return QLORA_ERR_INVALID_ARG;
     const dim3 grid((unsigned)(K / kMT), (unsigned)((N + kMT - 1) / kMT));
-#define QL_MERGE(DQ_, CB_) \
-    hipLaunchKernelGGL((nf4_merge_kernel<DQ_, CB_>), grid, dim3(256), 0, st, codes, q8, a2, A, B, r, s, out, N, K)
-    if (q8) {
-        if (cb == kCbFp4) QL_MERGE(true, kCbFp4); else QL_MERGE(true, kCbNf4);
-    } else {
-        if (cb == kCbFp4) QL_MERGE(false, kCbFp4); else QL_MERGE(false, kCbNf4);
-    }
-#undef QL_MERGE
+    with_cb_dt(cb, dt, [&](auto cbc, auto dtc) {
+        constexpr int CB = decltype(cbc)::value, DT = decltype(dtc)::value;
+        if (q8)
+            hipLaunchKernelGGL((nf4_merge_kernel<true, CB, DT>), grid, dim3(256), 0, st, codes, q8, a2, A, B, r, s, out,
+                               N, K);
+        else
+            hipLaunchKernelGGL((nf4_merge_kernel<false, CB, DT>), grid, dim3(256), 0, st, codes, q8, a2, A, B, r, s,
+                               out, N, K);
+    });
     return launch_status();
 }
 

@@ -54,7 +54,7 @@ __device__ __forceinline__ uint32_t nf4_code(float w, f32x4_t t0, f32x4_t t1, f3
     return (b3 ? 8u : 0u) | (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
 }
 
-template <bool DQ, int CB>
+template <bool DQ, int CB, int DT>
 __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint16_t* __restrict__ W,
                                                                 int64_t nblocks,
                                                                 uint8_t* __restrict__ codes,
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint16_t* 
         m = max(m, (uint32_t)__shfl_xor((int)m, 2));
         m = max(m, (uint32_t)__shfl_xor((int)m, 4));
         const int bl = p * 32 + wave * 8 + (lane >> 3);
-        if (sub == 0) s_amax[bl] = bf16_bits_to_f32(m);   // 0 for blocks past the end
+        if (sub == 0) s_amax[bl] = h16_to_f32<DT>(m);   // 0 for blocks past the end
     }
     __syncthreads();
 
@@ -107,7 +107,10 @@ __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint16_t* 
                 if (j + 1 < kDistinctLevels<CB>) {
                     const double m = 0.5 * ((double)level<CB>(code_of_sorted<CB>(j)) +
                                             (double)level<CB>(code_of_sorted<CB>(j + 1)));  // exact
-                    T[j] = f32_rd_bf16(__double2float_rd(ad * m));                        // exact product
+                    // the product is exact; any float weight w has w > X <=> w > RD_f32(X),
+                    // and a bf16 weight also w > X <=> w > RD_bf16(X)
+                    const float x = __double2float_rd(ad * m);
+                    T[j] = DT == kDtBf16 ? f32_rd_bf16(x) : x;
                 } else {
                     T[j] = __builtin_huge_valf();  // no level above the last distinct one
                 }
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint16_t* 
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const uint32_t bits = (i & 1) ? (v[p][i >> 1] >> 16) : (v[p][i >> 1] & 0xFFFFu);
-                const uint32_t q = code_of_sorted<CB>(nf4_code(bf16_bits_to_f32(bits), t0, t1, t2, t3));
+                const uint32_t q = code_of_sorted<CB>(nf4_code(h16_to_f32<DT>(bits), t0, t1, t2, t3));
                 packed |= q << (4 * (i ^ 1));
             }
             *reinterpret_cast<uint32_t*>(codes + (b0 + bl) * (kBlock / 2) + sub * 4) = packed;
@@ -167,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint16_t* 
 // nf4_dequantize_kernel: 256 lanes x 8 weights = 32 blocks per workgroup.
 //   a_hat = fl32(fl32(a2/255) * q8) (without double quantization: the stored
 //   fp32 absmax a2[b]), w_hat = RNE_bf16(fl32(a_hat * c_code)).
-template <bool DQ, int CB>
+template <bool DQ, int CB, int DT>
 __global__ __launch_bounds__(kThreads) void nf4_dequantize_kernel(const uint8_t* __restrict__ codes,
                                                                   const uint8_t* __restrict__ q8,
                                                                   const float* __restrict__ a2,
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void nf4_dequantize_kernel(const uint8_t*
         const uint32_t byte = (pk >> (8 * j)) & 0xFFu;
         const float w0 = __fmul_rn(ahat, s_c[byte >> 4]);
         const float w1 = __fmul_rn(ahat, s_c[byte & 0xFu]);
-        o[j] = pack_bf16x2(w0, w1);
+        o[j] = pack2<DT>(w0, w1);
     }
     *reinterpret_cast<u32x4_t*>(out + b * kBlock + sub * 8) = o;
 }
@@ -196,32 +199,32 @@ __global__ __launch_bounds__(kThreads) void nf4_dequantize_kernel(const uint8_t*
 }  // namespace
 
 qlora_status launch_quantize(const uint16_t* W, int64_t nblocks, uint8_t* codes, uint8_t* q8, float* a2, int cb,
-                             hipStream_t s) {
+                             int dt, hipStream_t s) {
     const int64_t groups = (nblocks + kSuper - 1) / kSuper;
-#define QL_QUANT(DQ_, CB_)                                                                                     \
-    hipLaunchKernelGGL((nf4_quantize_kernel<DQ_, CB_>), dim3((unsigned)groups), dim3(kThreads), 0, s, W, nblocks, \
-                       codes, q8, a2)
-    if (q8) {
-        if (cb == kCbFp4) QL_QUANT(true, kCbFp4); else QL_QUANT(true, kCbNf4);
-    } else {
-        if (cb == kCbFp4) QL_QUANT(false, kCbFp4); else QL_QUANT(false, kCbNf4);
-    }
-#undef QL_QUANT
+    with_cb_dt(cb, dt, [&](auto cbc, auto dtc) {
+        constexpr int CB = decltype(cbc)::value, DT = decltype(dtc)::value;
+        if (q8)
+            hipLaunchKernelGGL((nf4_quantize_kernel<true, CB, DT>), dim3((unsigned)groups), dim3(kThreads), 0, s, W,
+                               nblocks, codes, q8, a2);
+        else
+            hipLaunchKernelGGL((nf4_quantize_kernel<false, CB, DT>), dim3((unsigned)groups), dim3(kThreads), 0, s, W,
+                               nblocks, codes, q8, a2);
+    });
     return launch_status();
 }
 
-qlora_status launch_dequantize(const uint8_t* codes, const uint8_t* q8, const float* a2, int cb, int64_t nblocks,
-                               uint16_t* out, hipStream_t s) {
+qlora_status launch_dequantize(const uint8_t* codes, const uint8_t* q8, const float* a2, int cb, int dt,
+                               int64_t nblocks, uint16_t* out, hipStream_t s) {
     const int64_t grid = (nblocks + 31) / 32;
-#define QL_DEQ(DQ_, CB_)                                                                                         \
-    hipLaunchKernelGGL((nf4_dequantize_kernel<DQ_, CB_>), dim3((unsigned)grid), dim3(kThreads), 0, s, codes, q8, a2, \
-                       nblocks, out)
-    if (q8) {
-        if (cb == kCbFp4) QL_DEQ(true, kCbFp4); else QL_DEQ(true, kCbNf4);
-    } else {
-        if (cb == kCbFp4) QL_DEQ(false, kCbFp4); else QL_DEQ(false, kCbNf4);
-    }
-#undef QL_DEQ
+    with_cb_dt(cb, dt, [&](auto cbc, auto dtc) {
+        constexpr int CB = decltype(cbc)::value, DT = decltype(dtc)::value;
+        if (q8)
+            hipLaunchKernelGGL((nf4_dequantize_kernel<true, CB, DT>), dim3((unsigned)grid), dim3(kThreads), 0, s, codes,
+                               q8, a2, nblocks, out);
+        else
+            hipLaunchKernelGGL((nf4_dequantize_kernel<false, CB, DT>), dim3((unsigned)grid), dim3(kThreads), 0, s,
+                               codes, q8, a2, nblocks, out);
+    });
     return launch_status();
 }
 

@@ -24,10 +24,18 @@ c_sz = ctypes.c_size_t
 
 class NF4State(ctypes.Structure):
     """Mirror of struct qlora_nf4."""
-    _fields_ = [("codes", c_vp), ("q8", c_vp), ("a2", c_vp), ("n", c_i64), ("k", c_i64), ("quant_type", ctypes.c_int32)]
+    _fields_ = [("codes", c_vp), ("q8", c_vp), ("a2", c_vp), ("n", c_i64), ("k", c_i64), ("quant_type", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
 
 
-QUANT_TYPES = {"nf4": 0, "fp4": 1}   # qlora_quant_type: the 4-bit codebook
+QUANT_TYPES = {"nf4": 0, "fp4": 1}                        # qlora_quant_type: the 4-bit codebook
+DTYPES = {torch.bfloat16: 0, torch.float16: 1}            # qlora_dtype: the 16-bit compute dtype
+
+
+def _dtype_code(dtype):
+    if dtype not in DTYPES:
+        raise TypeError(f"compute dtype must be torch.bfloat16 or torch.float16, got {dtype}")
+    return DTYPES[dtype]
 
 
 def _load():
@@ -48,8 +56,8 @@ def _load():
         "qlora_linear_fwd": (ctypes.c_int, [P, c_vp, c_i64, c_vp, c_vp, ctypes.c_int, ctypes.c_float,
                                             c_vp, c_vp, c_vp, c_sz, c_vp]),
         "qlora_lora_down_workspace": (c_sz, [c_i64, c_i64, ctypes.c_int]),
-        "qlora_lora_down": (ctypes.c_int, [c_vp, c_i64, c_i64, c_vp, ctypes.c_int, ctypes.c_float, c_vp, c_vp,
-                                           c_sz, c_vp]),
+        "qlora_lora_down": (ctypes.c_int, [c_vp, c_i64, c_i64, c_vp, ctypes.c_int, ctypes.c_float, ctypes.c_int,
+                                           c_vp, c_vp, c_sz, c_vp]),
         "qlora_fused_gemm_fwd": (ctypes.c_int, [P, c_vp, c_i64, c_vp, c_vp, ctypes.c_int, c_vp, c_vp]),
         "qlora_pooled_fwd_workspace": (c_sz, [c_i64, c_i64, c_i64, ctypes.c_int, ctypes.c_int]),
         "qlora_pooled_fwd": (ctypes.c_int, [P, c_vp, c_i64, c_vp, c_vp, ctypes.c_int, ctypes.c_int, ctypes.c_float,
@@ -120,41 +128,47 @@ def sizes_nodq(N, K):
 class NF4Weight:
     """Device-resident quantized weight: codes (uint8), q8 (uint8) and a2 (float32) tensors; without
     double quantization q8 is None and a2 holds one fp32 absmax per 64-block.  quant_type names the
-    4-bit codebook: "nf4" or "fp4"."""
+    4-bit codebook ("nf4" or "fp4"); dtype is the compute dtype of every 16-bit tensor used with it
+    (torch.bfloat16 or torch.float16)."""
 
-    def __init__(self, codes, q8, a2, N, K, quant_type="nf4"):
+    def __init__(self, codes, q8, a2, N, K, quant_type="nf4", dtype=torch.bfloat16):
         if quant_type not in QUANT_TYPES:
             raise ValueError(f"quant_type must be one of {sorted(QUANT_TYPES)}, got {quant_type!r}")
+        _dtype_code(dtype)
         self.codes, self.q8, self.a2, self.N, self.K = codes, q8, a2, int(N), int(K)
-        self.quant_type = quant_type
+        self.quant_type, self.dtype = quant_type, dtype
 
     @property
     def double_quant(self):
         return self.q8 is not None
 
     @classmethod
-    def empty(cls, N, K, device="cuda", double_quant=True, quant_type="nf4"):
+    def empty(cls, N, K, device="cuda", double_quant=True, quant_type="nf4", dtype=torch.bfloat16):
         if not double_quant:
             cb, ab = sizes_nodq(N, K)
             return cls(torch.empty(cb, dtype=torch.uint8, device=device), None,
-                       torch.empty(ab // 4, dtype=torch.float32, device=device), N, K, quant_type)
+                       torch.empty(ab // 4, dtype=torch.float32, device=device), N, K, quant_type, dtype)
         cb, qb, ab = sizes(N, K)
         return cls(torch.empty(cb, dtype=torch.uint8, device=device),
                    torch.empty(qb, dtype=torch.uint8, device=device),
-                   torch.empty(ab // 4, dtype=torch.float32, device=device), N, K, quant_type)
+                   torch.empty(ab // 4, dtype=torch.float32, device=device), N, K, quant_type, dtype)
 
     def state(self):
         q8 = None if self.q8 is None else self.q8.data_ptr()
-        return NF4State(self.codes.data_ptr(), q8, self.a2.data_ptr(), self.N, self.K, QUANT_TYPES[self.quant_type])
+        return NF4State(self.codes.data_ptr(), q8, self.a2.data_ptr(), self.N, self.K, QUANT_TYPES[self.quant_type],
+                        _dtype_code(self.dtype))
 
 
 def quantize(W, out=None, double_quant=True, quant_type="nf4"):
-    """4-bit blockwise quantization of a bf16 [N, K] device weight (qlora_quantize) with the NF4 or the FP4
-    codebook, with or without double quantization of the block scales (both ignored when `out` is given:
-    its layout and quant_type decide)."""
+    """4-bit blockwise quantization of a bf16 or fp16 [N, K] device weight (qlora_quantize) with the NF4 or
+    the FP4 codebook, with or without double quantization of the block scales (both ignored when `out` is
+    given: its layout and quant_type decide).  W's dtype becomes the weight's compute dtype."""
     N, K = W.shape
-    _dev(W, torch.bfloat16, "W")
-    w = NF4Weight.empty(N, K, W.device, double_quant, quant_type) if out is None else out
+    _dtype_code(W.dtype)
+    _dev(W, W.dtype, "W")
+    w = NF4Weight.empty(N, K, W.device, double_quant, quant_type, W.dtype) if out is None else out
+    if w.dtype != W.dtype:
+        raise TypeError(f"out has compute dtype {w.dtype}, W is {W.dtype}")
     st = w.state()
     _check(lib.qlora_quantize(_ptr(W), N, K, ctypes.byref(st), _stream()), "qlora_quantize")
     return w
@@ -162,8 +176,8 @@ def quantize(W, out=None, double_quant=True, quant_type="nf4"):
 
 def dequantize(w, out=None):
     """bf16 [N, K] reconstruction (qlora_dequantize); tests and export only."""
-    o = torch.empty((w.N, w.K), dtype=torch.bfloat16, device=w.codes.device) if out is None else out
-    _dev(o, torch.bfloat16, "out", (w.N, w.K))
+    o = torch.empty((w.N, w.K), dtype=w.dtype, device=w.codes.device) if out is None else out
+    _dev(o, w.dtype, "out", (w.N, w.K))
     st = w.state()
     _check(lib.qlora_dequantize(ctypes.byref(st), _ptr(o), _stream()), "qlora_dequantize")
     return o
@@ -173,10 +187,10 @@ def merge(w, A, B, alpha, out=None):
     """LoRA merge for deployment (qlora_merge): bf16 [N, K] = w_hat + (alpha/r) (A B)^T.
     Re-quantize with quantize(out)."""
     K, r = A.shape
-    _dev(A, torch.bfloat16, "A", (w.K, r))
-    _dev(B, torch.bfloat16, "B", (r, w.N))
-    o = torch.empty((w.N, w.K), dtype=torch.bfloat16, device=A.device) if out is None else out
-    _dev(o, torch.bfloat16, "out", (w.N, w.K))
+    _dev(A, w.dtype, "A", (w.K, r))
+    _dev(B, w.dtype, "B", (r, w.N))
+    o = torch.empty((w.N, w.K), dtype=w.dtype, device=A.device) if out is None else out
+    _dev(o, w.dtype, "out", (w.N, w.K))
     st = w.state()
     _check(lib.qlora_merge(ctypes.byref(st), _ptr(A), _ptr(B), r, float(alpha), _ptr(o), _stream()), "qlora_merge")
     return o
@@ -202,15 +216,15 @@ def linear_fwd(w, x, A, B, alpha, y=None, t=None, want_t=True, ws=None):
     """y = x W_hat + (alpha/r)(x A) B (qlora_linear_fwd).  Returns (y, t or None)."""
     M, K = x.shape
     r = A.shape[1]
-    _dev(x, torch.bfloat16, "x", (M, w.K))
-    _dev(A, torch.bfloat16, "A", (w.K, r))
-    _dev(B, torch.bfloat16, "B", (r, w.N))
+    _dev(x, w.dtype, "x", (M, w.K))
+    _dev(A, w.dtype, "A", (w.K, r))
+    _dev(B, w.dtype, "B", (r, w.N))
     dev = x.device
-    y = torch.empty((M, w.N), dtype=torch.bfloat16, device=dev) if y is None else _dev(y, torch.bfloat16, "y", (M, w.N))
+    y = torch.empty((M, w.N), dtype=w.dtype, device=dev) if y is None else _dev(y, w.dtype, "y", (M, w.N))
     if want_t and t is None:
-        t = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
+        t = torch.empty((M, r), dtype=w.dtype, device=dev)
     if t is not None:
-        _dev(t, torch.bfloat16, "t", (M, r))
+        _dev(t, w.dtype, "t", (M, r))
     wsb, wsn = _ws(fwd_workspace(M, w.N, w.K, r), dev, ws)
     st = w.state()
     _check(lib.qlora_linear_fwd(ctypes.byref(st), _ptr(x), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(y),
@@ -219,14 +233,16 @@ def linear_fwd(w, x, A, B, alpha, y=None, t=None, want_t=True, ws=None):
 
 
 def lora_down(x, A, alpha, t=None, ws=None):
-    """t = (alpha/r) x A as bf16 [M, r] (qlora_lora_down)."""
+    """t = (alpha/r) x A [M, r] in x's dtype, bf16 or fp16 (qlora_lora_down)."""
     M, K = x.shape
     r = A.shape[1]
-    _dev(x, torch.bfloat16, "x")
-    _dev(A, torch.bfloat16, "A", (K, r))
-    t = torch.empty((M, r), dtype=torch.bfloat16, device=x.device) if t is None else _dev(t, torch.bfloat16, "t", (M, r))
+    dt = x.dtype
+    code = _dtype_code(dt)
+    _dev(x, dt, "x")
+    _dev(A, dt, "A", (K, r))
+    t = torch.empty((M, r), dtype=dt, device=x.device) if t is None else _dev(t, dt, "t", (M, r))
     wsb, wsn = _ws(int(lib.qlora_lora_down_workspace(M, K, r)), x.device, ws)
-    _check(lib.qlora_lora_down(_ptr(x), M, K, _ptr(A), r, float(alpha), _ptr(t), _ptr(wsb), wsn, _stream()),
+    _check(lib.qlora_lora_down(_ptr(x), M, K, _ptr(A), r, float(alpha), code, _ptr(t), _ptr(wsb), wsn, _stream()),
            "qlora_lora_down")
     return t
 
@@ -235,10 +251,10 @@ def fused_gemm_fwd(w, x, t, B, y=None):
     """y = x W_hat + t B (qlora_fused_gemm_fwd): one kernel launch."""
     M = x.shape[0]
     r = t.shape[1]
-    _dev(x, torch.bfloat16, "x", (M, w.K))
-    _dev(t, torch.bfloat16, "t", (M, r))
-    _dev(B, torch.bfloat16, "B", (r, w.N))
-    y = torch.empty((M, w.N), dtype=torch.bfloat16, device=x.device) if y is None else _dev(y, torch.bfloat16, "y", (M, w.N))
+    _dev(x, w.dtype, "x", (M, w.K))
+    _dev(t, w.dtype, "t", (M, r))
+    _dev(B, w.dtype, "B", (r, w.N))
+    y = torch.empty((M, w.N), dtype=w.dtype, device=x.device) if y is None else _dev(y, w.dtype, "y", (M, w.N))
     st = w.state()
     _check(lib.qlora_fused_gemm_fwd(ctypes.byref(st), _ptr(x), M, _ptr(t), _ptr(B), r, _ptr(y), _stream()),
            "qlora_fused_gemm_fwd")
@@ -249,15 +265,15 @@ def linear_bwd(w, x, A, B, alpha, dy, t=None, need_dx=True, dx=None, dA=None, dB
     """(dx, dA, dB) of the layer for upstream dy (qlora_linear_bwd); dx is None when not needed."""
     M, K = x.shape
     r = A.shape[1]
-    _dev(x, torch.bfloat16, "x", (M, w.K))
-    _dev(A, torch.bfloat16, "A", (w.K, r))
-    _dev(B, torch.bfloat16, "B", (r, w.N))
-    _dev(dy, torch.bfloat16, "dy", (M, w.N))
+    _dev(x, w.dtype, "x", (M, w.K))
+    _dev(A, w.dtype, "A", (w.K, r))
+    _dev(B, w.dtype, "B", (r, w.N))
+    _dev(dy, w.dtype, "dy", (M, w.N))
     if t is not None:
-        _dev(t, torch.bfloat16, "t", (M, r))
+        _dev(t, w.dtype, "t", (M, r))
     dev = x.device
-    if need_dx and dx is None:
-        dx = torch.empty((M, w.K), dtype=torch.bfloat16, device=dev)
+    if need_dx:
+        dx = torch.empty((M, w.K), dtype=w.dtype, device=dev) if dx is None else _dev(dx, w.dtype, "dx", (M, w.K))
     dA = torch.empty((w.K, r), dtype=torch.float32, device=dev) if dA is None else _dev(dA, torch.float32, "dA", (w.K, r))
     dB = torch.empty((r, w.N), dtype=torch.float32, device=dev) if dB is None else _dev(dB, torch.float32, "dB", (r, w.N))
     wsb, wsn = _ws(bwd_workspace(M, w.N, w.K, r), dev, ws)
@@ -272,11 +288,11 @@ def pooled_fwd(w, x, A, B, alpha, g, y=None, t=None, ws=None):
     """QA-LoRA pooled forward (qlora_pooled_fwd): y = x W_hat + s pool(x) A B, A [K/g, r]. Returns (y, t)."""
     M, K = x.shape
     _, r = A.shape
-    _dev(x, torch.bfloat16, "x", (M, w.K))
-    _dev(A, torch.bfloat16, "A", (w.K // g, r))
-    _dev(B, torch.bfloat16, "B", (r, w.N))
-    y = torch.empty((M, w.N), dtype=torch.bfloat16, device=x.device) if y is None else _dev(y, torch.bfloat16, "y", (M, w.N))
-    t = torch.empty((M, r), dtype=torch.bfloat16, device=x.device) if t is None else _dev(t, torch.bfloat16, "t", (M, r))
+    _dev(x, w.dtype, "x", (M, w.K))
+    _dev(A, w.dtype, "A", (w.K // g, r))
+    _dev(B, w.dtype, "B", (r, w.N))
+    y = torch.empty((M, w.N), dtype=w.dtype, device=x.device) if y is None else _dev(y, w.dtype, "y", (M, w.N))
+    t = torch.empty((M, r), dtype=w.dtype, device=x.device) if t is None else _dev(t, w.dtype, "t", (M, r))
     wsb, wsn = _ws(int(lib.qlora_pooled_fwd_workspace(M, w.N, w.K, r, g)), x.device, ws)
     st = w.state()
     _check(lib.qlora_pooled_fwd(ctypes.byref(st), _ptr(x), M, _ptr(A), _ptr(B), r, g, float(alpha), _ptr(y), _ptr(t),
@@ -288,15 +304,15 @@ def pooled_bwd(w, x, A, B, alpha, g, dy, t=None, need_dx=True, dx=None, dA=None,
     """QA-LoRA pooled backward (qlora_pooled_bwd). Returns (dx or None, dA [K/g, r] fp32, dB [r, N] fp32)."""
     M, K = x.shape
     _, r = A.shape
-    _dev(x, torch.bfloat16, "x", (M, w.K))
-    _dev(A, torch.bfloat16, "A", (w.K // g, r))
-    _dev(B, torch.bfloat16, "B", (r, w.N))
-    _dev(dy, torch.bfloat16, "dy", (M, w.N))
+    _dev(x, w.dtype, "x", (M, w.K))
+    _dev(A, w.dtype, "A", (w.K // g, r))
+    _dev(B, w.dtype, "B", (r, w.N))
+    _dev(dy, w.dtype, "dy", (M, w.N))
     if t is not None:
-        _dev(t, torch.bfloat16, "t", (M, r))
+        _dev(t, w.dtype, "t", (M, r))
     if need_dx:
-        dx = torch.empty((M, w.K), dtype=torch.bfloat16, device=x.device) if dx is None else \
-            _dev(dx, torch.bfloat16, "dx", (M, w.K))
+        dx = torch.empty((M, w.K), dtype=w.dtype, device=x.device) if dx is None else \
+            _dev(dx, w.dtype, "dx", (M, w.K))
     else:
         dx = None
     dA = torch.empty((w.K // g, r), dtype=torch.float32, device=x.device) if dA is None else \

@@ -74,6 +74,17 @@ typedef enum qlora_status {
  * but is never produced.  Everything else is the same for both. */
 typedef enum qlora_quant_type { QLORA_QUANT_NF4 = 0, QLORA_QUANT_FP4 = 1 } qlora_quant_type;
 
+/* The compute dtype (deep dive 8.3: fp32, bf16 or fp16; bf16 recommended): the
+ * 16-bit float format of every 16-bit tensor exchanged with a layer -- the
+ * weight given to qlora_quantize, the output of qlora_dequantize and
+ * qlora_merge, and x, A, B, y, t, dy, dx of the layer calls.  bf16 (the
+ * default, zero-initialised) or IEEE binary16.  Dequantized weights are
+ * RNE_16(fl32(a_hat * c_q)) in that format and the products run on the MFMA
+ * instruction of that type with fp32 accumulation; dA and dB stay fp32.
+ * Where the text below says bf16, read "the compute dtype".  fp32 compute is
+ * not provided (the matrix cores' fp32 rate is 1/16 of the 16-bit rate). */
+typedef enum qlora_dtype { QLORA_DTYPE_BF16 = 0, QLORA_DTYPE_F16 = 1 } qlora_dtype;
+
 typedef struct qlora_nf4 {
     uint8_t* codes;     /* [N*K/2]            packed 4-bit codes                         */
     uint8_t* q8;        /* [N*K/64]           8-bit code of each block's absmax, or NULL */
@@ -83,6 +94,8 @@ typedef struct qlora_nf4 {
     int64_t k;          /* K = Din, a multiple of 64                                     */
     int32_t quant_type; /* a qlora_quant_type; 0 (zero-initialised) is NF4. Any other   */
                         /* value -> QLORA_ERR_INVALID_ARG                                */
+    int32_t dtype;      /* a qlora_dtype; 0 (zero-initialised) is bf16. Any other value  */
+                        /* -> QLORA_ERR_INVALID_ARG                                      */
 } qlora_nf4;
 
 /* Library version (major*10000 + minor*100 + patch). */
@@ -158,9 +171,11 @@ qlora_status qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, 
 size_t qlora_lora_down_workspace(int64_t M, int64_t K, int r);
 
 /* t = s * (x A) as bf16 [M, r], s = alpha / r (the LoRA down-projection,
- * deep dive 12.2).  x [M, K] bf16 (K % 64 == 0), A [K, r] bf16, 1 <= r <= 128. */
+ * deep dive 12.2).  x [M, K] bf16 (K % 64 == 0), A [K, r] bf16, 1 <= r <= 128.
+ * dtype: a qlora_dtype, the format of x, A and t (this call takes no weight
+ * state to carry it); any other value -> QLORA_ERR_INVALID_ARG. */
 qlora_status qlora_lora_down(const uint16_t* x, int64_t M, int64_t K, const uint16_t* A, int r, float alpha,
-                             uint16_t* t_out, void* ws, size_t ws_bytes, void* stream);
+                             int dtype, uint16_t* t_out, void* ws, size_t ws_bytes, void* stream);
 
 /* y = x W_hat + t B as bf16 [M, N]: the fused dequant GEMM with the LoRA
  * up-projection folded in as r extra reduction steps.  t [M, r] bf16 (already

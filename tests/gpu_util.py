@@ -23,3 +23,9 @@ def host_f64(t):
 
 def say(msg):
     print(msg, flush=True)
+
+
+def dev_f16(u16):
+    """uint16 fp16 bits (numpy) -> contiguous torch.float16 tensor on cuda:0."""
+    a = np.ascontiguousarray(u16, dtype=np.uint16)
+    return torch.from_numpy(a.view(np.int16)).view(torch.float16).to("cuda:0")

@@ -92,6 +92,11 @@ def test_quantize_argument_errors(q):
     bad_qt.quant_type = 2
     assert f(FAKE, 64, 64, ctypes.byref(bad_qt), None) == INVALID
     assert q.lib.qlora_dequantize(ctypes.byref(bad_qt), FAKE, None) == INVALID
+    # dtype: 0 (bf16) and 1 (fp16) only
+    bad_dt = _state(q)
+    bad_dt.dtype = 2
+    assert f(FAKE, 64, 64, ctypes.byref(bad_dt), None) == INVALID
+    assert q.lib.qlora_dequantize(ctypes.byref(bad_dt), FAKE, None) == INVALID
     assert q.lib.qlora_dequantize(ctypes.byref(st), None, None) == INVALID
     assert q.lib.qlora_dequantize(ctypes.byref(st), FAKE + 4, None) == MISALIGNED
 
@@ -122,6 +127,18 @@ def test_pooled_argument_errors(q):
     assert f(st, FAKE, 8, FAKE + 2, FAKE, 8, 32, 16.0, FAKE, None, FAKE, need, None) == MISALIGNED
     assert f(st, FAKE, 8, FAKE, FAKE, 8, 32, 16.0, FAKE, None, FAKE, 100, None) == WORKSPACE
     assert q.lib.qlora_pooled_bwd_workspace(8, 64, 128, 8, 6) == 0
+
+
+def test_lora_down_argument_errors(q):
+    f = q.lib.qlora_lora_down
+    need = q.lib.qlora_lora_down_workspace(8, 128, 8)
+    # (x, M, K, A, r, alpha, dtype, t_out, ws, ws_bytes, stream)
+    assert f(FAKE, 8, 128, FAKE, 8, 16.0, 2, FAKE, FAKE, need, None) == INVALID     # dtype not bf16 / fp16
+    assert f(FAKE, 8, 128, FAKE, 8, 16.0, -1, FAKE, FAKE, need, None) == INVALID
+    assert f(FAKE, 8, 100, FAKE, 8, 16.0, 1, FAKE, FAKE, need, None) == SHAPE
+    assert f(FAKE + 2, 8, 128, FAKE, 8, 16.0, 1, FAKE, FAKE, need, None) == MISALIGNED
+    assert f(FAKE, 8, 128, FAKE, 8, 16.0, 0, FAKE, FAKE, need - 1, None) == WORKSPACE
+    assert f(None, 0, 128, None, 8, 16.0, 1, None, None, 0, None) == OK               # M = 0: no-op
 
 
 def test_linear_argument_errors(q):
