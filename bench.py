@@ -372,6 +372,7 @@ def extras(torch, qlora, workloads, dev, to_dev, L, M, r):
 
     res["double_quant_off"] = extras_variant(torch, qlora, workloads, dev, to_dev, L, M, r, ev, double_quant=False)
     res["fp4"] = extras_variant(torch, qlora, workloads, dev, to_dev, L, M, r, ev, quant_type="fp4")
+    res["fp16_compute"] = extras_variant(torch, qlora, workloads, dev, to_dev, L, M, r, ev, dtype=torch.float16)
     res["qa_lora_pooled_g64"] = extras_pooled(torch, qlora, workloads, dev, to_dev, L, M, r, ev, 64)
 
     # LoRA merge for deployment (qlora_merge) of the 7 layers: N*K*r fp32 FMAs (VALU-bound) and
@@ -411,14 +412,21 @@ def extras(torch, qlora, workloads, dev, to_dev, L, M, r):
     return res
 
 
-def extras_variant(torch, qlora, workloads, dev, to_dev, L, M, r, ev, double_quant=True, quant_type="nf4"):
-    """The same workloads with another scale layout or codebook: double quantization off (fp32 absmax per
-    block, deep dive 7.1 and 9.5) or the fp4 codebook (deep dive 6.5, 8.1).  The whole quantize + fwd +
-    bwd step of the 7 linears, the forward GEMM alone, quantize bandwidth and the decode GEMV (64 rotated
-    weight copies)."""
+def extras_variant(torch, qlora, workloads, dev, to_dev, L, M, r, ev, double_quant=True, quant_type="nf4",
+                   dtype=None):
+    """The same workloads with another scale layout, codebook or compute dtype: double quantization off
+    (fp32 absmax per block, deep dive 7.1 and 9.5), the fp4 codebook (deep dive 6.5, 8.1) or fp16 compute
+    (deep dive 8.3; the same draws rounded to fp16).  The whole quantize + fwd + bwd step of the 7 linears,
+    the forward GEMM alone, quantize bandwidth and the decode GEMV (64 rotated weight copies)."""
     res = {}
     alpha = workloads.CONFIGS[4]["alpha"]
-    Wn = [qlora.NF4Weight.empty(d["N"], d["K"], dev, double_quant=double_quant, quant_type=quant_type) for d in L]
+    dt = torch.bfloat16 if dtype is None else dtype
+    if dt != torch.bfloat16:
+        L = [dict(d, W=d["W"].to(dt), x=d["x"].to(dt), A=d["A"].to(dt), B=d["B"].to(dt), dy=d["dy"].to(dt),
+                  t=torch.empty_like(d["t"], dtype=dt), y=torch.empty_like(d["y"], dtype=dt),
+                  dx=torch.empty_like(d["dx"], dtype=dt)) for d in L]
+    Wn = [qlora.NF4Weight.empty(d["N"], d["K"], dev, double_quant=double_quant, quant_type=quant_type, dtype=dt)
+          for d in L]
     ws = torch.empty(max(qlora.bwd_workspace(M, d["N"], d["K"], r) for d in L), dtype=torch.uint8, device=dev)
     total_flops = sum(d["flops"]["fwd"] + d["flops"]["bwd"] for d in L)
     fwd_flops = sum(d["flops"]["fwd_gemm"] for d in L)
@@ -461,15 +469,15 @@ def extras_variant(torch, qlora, workloads, dev, to_dev, L, M, r, ev, double_qua
                        "TFLOP/s": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2)}
     res["quantize"] = {"GB/s": round(q_bytes / (q_ms * 1e-3) / 1e9, 1), "ms": round(q_ms, 4),
                        "bytes_per_weight": round(q_bytes / sum(d["N"] * d["K"] for d in L), 4)}
-    del Wn, ws
+    del Wn, ws, L
     c2 = workloads.CONFIGS[2]
     _, N2, K2 = c2["layers"][0]
-    W2 = to_dev(workloads.weight(2))
+    W2 = to_dev(workloads.weight(2)).to(dt)
     copies = [qlora.quantize(W2, double_quant=double_quant, quant_type=quant_type) for _ in range(64)]
-    B2 = to_dev(workloads.lora_B(2))
-    xd = to_dev(workloads.activations(2, M=1))
-    td = torch.zeros((1, c2["r"]), dtype=torch.bfloat16, device=dev)
-    yd = torch.empty((1, N2), dtype=torch.bfloat16, device=dev)
+    B2 = to_dev(workloads.lora_B(2)).to(dt)
+    xd = to_dev(workloads.activations(2, M=1)).to(dt)
+    td = torch.zeros((1, c2["r"]), dtype=dt, device=dev)
+    yd = torch.empty((1, N2), dtype=dt, device=dev)
     for w in copies[:4]:
         qlora.fused_gemm_fwd(w, xd, td, B2, y=yd)
     torch.cuda.synchronize()
