@@ -179,6 +179,19 @@ qlora_status qlora_fused_gemm_fwd(const qlora_nf4* w, const uint16_t* x, int64_t
                            (hipStream_t)stream);
 }
 
+qlora_status qlora_fused_gemm_bwd_dx(const qlora_nf4* w, const uint16_t* dy, int64_t M, const uint16_t* u,
+                                     const uint16_t* A, int r, uint16_t* dx, void* stream) {
+    qlora_status st = check_state(w);
+    if (st != QLORA_OK) return st;
+    const int64_t N = w->n, K = w->k;
+    if (bad_dims(M, N, K, r)) return QLORA_ERR_INVALID_ARG;
+    if (M == 0) return QLORA_OK;
+    if (!dy || !u || !A || !dx) return QLORA_ERR_INVALID_ARG;
+    if (!aligned16(dy) || !aligned16(u) || !aligned16(A) || !aligned16(dx)) return QLORA_ERR_MISALIGNED;
+    return launch_gemm_bwd_dx(dy, w->codes, w->q8, w->a2, cb_of(w), dt_of(w), u, A, dx, (int)M, (int)N, (int)K, r,
+                              (hipStream_t)stream);
+}
+
 qlora_status qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
                               int r, float alpha, uint16_t* y, uint16_t* t_out, void* ws, size_t ws_bytes,
                               void* stream) {

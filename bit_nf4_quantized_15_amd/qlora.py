@@ -59,6 +59,7 @@ def _load():
         "qlora_lora_down": (ctypes.c_int, [c_vp, c_i64, c_i64, c_vp, ctypes.c_int, ctypes.c_float, ctypes.c_int,
                                            c_vp, c_vp, c_sz, c_vp]),
         "qlora_fused_gemm_fwd": (ctypes.c_int, [P, c_vp, c_i64, c_vp, c_vp, ctypes.c_int, c_vp, c_vp]),
+        "qlora_fused_gemm_bwd_dx": (ctypes.c_int, [P, c_vp, c_i64, c_vp, c_vp, ctypes.c_int, c_vp, c_vp]),
         "qlora_pooled_fwd_workspace": (c_sz, [c_i64, c_i64, c_i64, ctypes.c_int, ctypes.c_int]),
         "qlora_pooled_fwd": (ctypes.c_int, [P, c_vp, c_i64, c_vp, c_vp, ctypes.c_int, ctypes.c_int, ctypes.c_float,
                                             c_vp, c_vp, c_vp, c_sz, c_vp]),
@@ -259,6 +260,20 @@ def fused_gemm_fwd(w, x, t, B, y=None):
     _check(lib.qlora_fused_gemm_fwd(ctypes.byref(st), _ptr(x), M, _ptr(t), _ptr(B), r, _ptr(y), _stream()),
            "qlora_fused_gemm_fwd")
     return y
+
+
+def fused_gemm_bwd_dx(w, dy, u, A, dx=None):
+    """dx = dy W_hat^T + u A^T (qlora_fused_gemm_bwd_dx), u = (alpha/r) dy B^T given: one kernel launch."""
+    M = dy.shape[0]
+    r = u.shape[1]
+    _dev(dy, w.dtype, "dy", (M, w.N))
+    _dev(u, w.dtype, "u", (M, r))
+    _dev(A, w.dtype, "A", (w.K, r))
+    dx = torch.empty((M, w.K), dtype=w.dtype, device=dy.device) if dx is None else _dev(dx, w.dtype, "dx", (M, w.K))
+    st = w.state()
+    _check(lib.qlora_fused_gemm_bwd_dx(ctypes.byref(st), _ptr(dy), M, _ptr(u), _ptr(A), r, _ptr(dx), _stream()),
+           "qlora_fused_gemm_bwd_dx")
+    return dx
 
 
 def linear_bwd(w, x, A, B, alpha, dy, t=None, need_dx=True, dx=None, dA=None, dB=None, ws=None):

@@ -198,6 +198,15 @@ qlora_status qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, int64_t M, 
                               const uint16_t* dy, uint16_t* dx, float* dA, float* dB, void* ws,
                               size_t ws_bytes, void* stream);
 
+/* The dx stage of qlora_linear_bwd alone, for a given u:
+ *   dx = dy W_hat^T + u A^T    [M, K]  bf16
+ * with u = s dy B^T [M, r] bf16 already scaled (s = alpha / r), A [K, r] bf16,
+ * dy [M, N] bf16.  One kernel launch (the fused dequant GEMM of the backward
+ * with the LoRA term folded in as r extra reduction steps), no workspace.
+ * Arguments and errors as qlora_linear_bwd; M = 0 is a no-op. */
+qlora_status qlora_fused_gemm_bwd_dx(const qlora_nf4* w, const uint16_t* dy, int64_t M, const uint16_t* u,
+                                     const uint16_t* A, int r, uint16_t* dx, void* stream);
+
 /* QA-LoRA pooled branch ("LoRA, QLoRA, QA-LoRA explained", sections 3-5): the
  * LoRA input is pool(x), the mean of each group of g consecutive input
  * columns, and A is [K/g, r]:

@@ -156,6 +156,13 @@ def test_linear_argument_errors(q):
     assert fwd(st, FAKE, 8, FAKE, FAKE, 8, 16.0, FAKE, None, None, ws_need, None) == WORKSPACE
     assert fwd(st, FAKE, 8, FAKE, FAKE, 8, 16.0, FAKE, None, FAKE, ws_need - 1, None) == WORKSPACE
     assert fwd(st, FAKE, 0, None, None, 8, 16.0, None, None, None, 0, None) == OK                 # M = 0: no-op
+    gdx = q.lib.qlora_fused_gemm_bwd_dx
+    # (w, dy, M, u, A, r, dx, stream)
+    assert gdx(st, FAKE, 8, FAKE, FAKE, 0, FAKE, None) == INVALID
+    assert gdx(st, None, 8, FAKE, FAKE, 8, FAKE, None) == INVALID
+    assert gdx(st, FAKE, 8, FAKE, FAKE, 8, None, None) == INVALID
+    assert gdx(st, FAKE, 8, FAKE + 2, FAKE, 8, FAKE, None) == MISALIGNED
+    assert gdx(st, None, 0, None, None, 8, None, None) == OK                          # M = 0: no-op
     bwd = q.lib.qlora_linear_bwd
     wsb = q.bwd_workspace(8, 64, 128, 8)
     # (w, x, M, A, B, r, alpha, t, dy, dx, dA, dB, ws, ws_bytes, stream)

@@ -95,6 +95,31 @@ def test_groups_straddling_a_block_pair(q, M, N, K, r):
     _check_full(q, W, x, A, B, dy, 2.0 * r, f"straddle {M}x{N}x{K} r{r}")
 
 
+@pytest.mark.parametrize("M,N,K,r", [(17, 130, 128, 8), (300, 520, 384, 64), (64, 72, 64 * 43, 16), (256, 256, 512, 100)])
+def test_fused_gemm_bwd_dx_alone(q, M, N, K, r):
+    """qlora_fused_gemm_bwd_dx for a given bf16 u: dx = dy W_hat^T + u A^T.  u is the oracle's
+    s dy B^T rounded to bf16, the reference uses that same u."""
+    import torch
+    seed = 20 * M + N + K + r
+    W = workloads.custom(seed, (N, K), 0.02)
+    A = workloads.custom(seed + 2, (K, r), float(1 / np.sqrt(r)))
+    B = workloads.custom(seed + 3, (r, N), 0.01)
+    dy = workloads.custom(seed + 4, (M, N), 1.0)
+    alpha = 2.0 * r
+    say(f"[bwd dx alone] M={M} N={N} K={K} r={r}")
+    dyf, Af, Bf = bf16.to_f64(dy), bf16.to_f64(A), bf16.to_f64(B)
+    u = bf16.from_f32_rne(((alpha / r) * (dyf @ Bf.T)).astype(np.float32))
+    w = q.quantize(dev_bf16(W))
+    dx = q.fused_gemm_bwd_dx(w, dev_bf16(dy), dev_bf16(u), dev_bf16(A))
+    torch.cuda.synchronize()
+    p, q8, a2 = nf4.quantize(W)
+    Wh = bf16.to_f64(nf4.dequantize(p, q8, a2, N, K))
+    ref = dyf @ Wh + bf16.to_f64(u) @ Af.T
+    e = lora.rel_err(host_f64(dx), ref)
+    say(f"    rel error dx {e:.3e}")
+    assert e <= TOL
+
+
 def test_recomputed_t_and_no_dx(q):
     M, N, K, r = 40, 192, 256, 16
     W = workloads.custom(1, (N, K), 0.02); x = workloads.custom(2, (M, K), 1.0)
