@@ -11,15 +11,17 @@ dequant GEMM with the LoRA up-projection), and the backward of all seven
 value = algorithmic fwd+bwd FLOP of the seven linears / step time, where a
 layer counts 2MKN (forward base) + 2MKN (dx) + 2Mr(K+N) (forward LoRA) +
 4Mr(K+N) (backward LoRA); quantization time is inside the step but adds no
-FLOP.  Extra fields: the dominant kernel against the bf16 MFMA roofline, the
-decode GEMV (4096x4096, M=1 and 16) against HBM bandwidth, quantize /
-dequantize bandwidth, a dense bf16 torch.matmul for context, and the CPU
-oracle timed on a bounded sample.
+FLOP.  Extra fields: the dominant kernel of the step (the fused backward dx
+GEMM, timed on its own on the same shapes right after the timed steps)
+against the bf16 MFMA roofline, the forward GEMM likewise, the decode GEMV
+(4096x4096, M=1 and 16) against HBM bandwidth, quantize / dequantize
+bandwidth, the scale-layout / codebook / dtype variants, a dense bf16
+torch.matmul for context, and the CPU oracle timed on a bounded sample.
 
 usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
        python bench.py --mode pmc     (a few untimed steps + a calibration copy, for rocprofv3 --pmc)
-       python bench.py --pmc-summary FETCH_CSV WRITE_CSV
-                                      (HBM bytes per launch of the forward GEMM from the two
+       python bench.py --pmc-summary FETCH_CSV WRITE_CSV [--pmc-kernel fwd|bwd_dx]
+                                      (HBM bytes per launch of one GEMM kernel from the two
                                        counter runs, scaled by the calibration copy)
 """
 import hashlib
@@ -46,13 +48,15 @@ def parse():
     p.add_argument("--no-extras", action="store_true", help="skip decode / quantize / dense context lines")
     p.add_argument("--mode", choices=["bench", "pmc"], default="bench")
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    p.add_argument("--pmc-kernel", choices=["fwd", "bwd_dx"], default="fwd")
     return p.parse_args()
 
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-FWD_KERNEL = "nf4_gemm_fwd_kernel"
+KERNELS = {"fwd": "nf4_gemm_fwd_kernel", "bwd_dx": "nf4_gemm_bwd_dx_kernel"}
 GEMM_SRC = os.path.join(HERE, "bit_nf4_quantized_15_amd", "csrc", "gemm.hip")
-TRAFFIC_FILE = os.path.join(HERE, "profiles", "nf4_gemm_fwd_kernel__7B_block_7_layers_M4096_r64__hbm_traffic.txt")
+TRAFFIC_FILES = {k: os.path.join(HERE, "profiles", f"{v}__7B_block_7_layers_M4096_r64__hbm_traffic.txt")
+                 for k, v in KERNELS.items()}
 CALIB_BYTES = 512 << 20
 
 
@@ -76,11 +80,24 @@ def fwd_algorithmic_bytes(layers, M, r):
     return tot / len(layers)
 
 
-def measured_traffic():
-    """HBM bytes per forward-GEMM launch from the committed counter runs, or None when
+def bwd_dx_algorithmic_bytes(layers, M, r):
+    """Per-launch HBM bytes the backward dx GEMM must move, averaged over the layer shapes:
+    dy, codes, q8, a2, u, A in and dx out."""
+    tot = 0
+    for _, N, K in layers:
+        tot += 2 * M * N + N * K // 2 + N * K // 64 + 4 * (-(-N * K // 16384)) + 2 * M * r + 2 * K * r + 2 * M * K
+    return tot / len(layers)
+
+
+def algorithmic_bytes(kind, layers, M, r):
+    return (fwd_algorithmic_bytes if kind == "fwd" else bwd_dx_algorithmic_bytes)(layers, M, r)
+
+
+def measured_traffic(kind):
+    """HBM bytes per launch of one GEMM kernel from the committed counter runs, or None when
     they are missing or were taken on a different version of the kernel source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILES[kind]) as f:
             kv = dict(line.split(": ", 1) for line in f.read().splitlines() if ": " in line and not line.startswith("#"))
         if kv.get("source_sha256", "").strip() != gemm_source_sha():
             return None
@@ -89,9 +106,10 @@ def measured_traffic():
         return None
 
 
-def pmc_summary(fetch_csv, write_csv):
-    """Per-launch FETCH_SIZE / WRITE_SIZE of the forward GEMM, each scaled by the factor
-    that makes the same counter read the calibration copy's known bytes."""
+def pmc_summary(fetch_csv, write_csv, kind):
+    """Per-launch FETCH_SIZE / WRITE_SIZE of one GEMM kernel (kind fwd or bwd_dx), each scaled by
+    the factor that makes the same counter read the calibration copy's known bytes."""
+    kname = KERNELS[kind]
     import csv
     import collections
 
@@ -101,11 +119,11 @@ def pmc_summary(fetch_csv, write_csv):
             if row["Counter_Name"] == counter:
                 vals[row["Dispatch_Id"]][row["Kernel_Name"]] = vals[row["Dispatch_Id"]].get(row["Kernel_Name"], 0.0) + \
                     float(row["Counter_Value"])
-        fwd = [v for d in vals.values() for k, v in d.items() if FWD_KERNEL in k]
+        ker = [v for d in vals.values() for k, v in d.items() if kname in k]
         cal = [v for d in vals.values() for k, v in d.items() if "elementwise" in k]
-        if not fwd or not cal:
-            raise SystemExit(f"{path}: no {FWD_KERNEL} or calibration dispatch for {counter}")
-        return sum(fwd) / len(fwd), len(fwd), max(cal)
+        if not ker or not cal:
+            raise SystemExit(f"{path}: no {kname} or calibration dispatch for {counter}")
+        return sum(ker) / len(ker), len(ker), max(cal)
 
     f_kib, n_f, f_cal = per_kernel(fetch_csv, "FETCH_SIZE")
     w_kib, n_w, w_cal = per_kernel(write_csv, "WRITE_SIZE")
@@ -113,9 +131,10 @@ def pmc_summary(fetch_csv, write_csv):
     fetch_b, write_b = f_kib * 1024 * f_scale, w_kib * 1024 * w_scale
     from bit_nf4_quantized_15_amd import workloads
     cfg = workloads.CONFIGS[4]
-    algo = fwd_algorithmic_bytes(cfg["layers"], cfg["M"], cfg["r"])
+    algo = algorithmic_bytes(kind, cfg["layers"], cfg["M"], cfg["r"])
     print(f"source_sha256: {gemm_source_sha()}")
-    print(f"fwd_dispatches: {n_f} (FETCH run), {n_w} (WRITE run)")
+    print(f"kernel: {kname}")
+    print(f"dispatches: {n_f} (FETCH run), {n_w} (WRITE run)")
     print(f"fetch_kib_per_launch_raw: {f_kib:.1f}")
     print(f"write_kib_per_launch_raw: {w_kib:.1f}")
     print(f"calibration_copy_bytes: {CALIB_BYTES} read + {CALIB_BYTES} written")
@@ -132,7 +151,7 @@ def pmc_summary(fetch_csv, write_csv):
 
 def layer_flops(M, N, K, r):
     return dict(fwd_gemm=2 * M * K * N + 2 * M * r * N, fwd=2 * M * K * N + 2 * M * r * (K + N),
-                bwd=2 * M * K * N + 4 * M * r * (K + N))
+                bwd_dx_gemm=2 * M * N * K + 2 * M * r * K, bwd=2 * M * K * N + 4 * M * r * (K + N))
 
 
 def graph_ms(calls, reps=5):
@@ -169,7 +188,7 @@ def gemv_bytes(M, N, K, r, double_quant=True):
 def main():
     args = parse()
     if args.pmc_summary:
-        pmc_summary(*args.pmc_summary)
+        pmc_summary(*args.pmc_summary, args.pmc_kernel)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -258,6 +277,25 @@ def main():
     ms_step = t_start.elapsed_time(t_stop) / args.steps
     value = total_flops / (ms_step * 1e-3) / 1e12
 
+    # The step's dominant kernel, the fused backward dx GEMM, on its own: qlora_linear_bwd launches it
+    # between other kernels, so it is timed through its stage entry point on the same shapes and inputs.
+    # As inside qlora_linear_bwd, each launch follows the kernel that computes u = (alpha/r) dy B^T from
+    # dy (untimed here), so dy is as warm in the caches as it is in the step.
+    for d in L:
+        d["Bt"] = d["B"].t().contiguous()
+        d["u"] = qlora.lora_down(d["dy"], d["Bt"], alpha)
+    for d in L:
+        qlora.fused_gemm_bwd_dx(d["w"], d["dy"], d["u"], d["A"], dx=d["dx"])
+    timing["bwd_dx"] = []
+    for _ in range(args.steps):
+        for d in L:
+            qlora.lora_down(d["dy"], d["Bt"], alpha, t=d["u"], ws=ws)
+            a = ev(); a.record()
+            qlora.fused_gemm_bwd_dx(d["w"], d["dy"], d["u"], d["A"], dx=d["dx"])
+            b = ev(); b.record()
+            timing["bwd_dx"].append((a, b, d["flops"]["bwd_dx_gemm"]))
+    torch.cuda.synchronize()
+
     def agg(lst):
         tot_ms = sum(a.elapsed_time(b) for a, b, _ in lst)
         tot_f = sum(f for _, _, f in lst)
@@ -265,6 +303,14 @@ def main():
 
     fwd_tfs, fwd_avg_ms = agg(timing["fwd_gemm"])
     bwd_tfs, bwd_avg_ms = agg(timing["bwd"])
+    bdx_tfs, bdx_avg_ms = agg(timing["bwd_dx"])
+
+    def roofline(kind, tfs, avg_ms, kernel_desc, flop_desc):
+        return {"kernel": kernel_desc, "bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": measured_traffic(kind),
+                "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                "algorithmic_bytes_per_launch": round(algorithmic_bytes(kind, cfg["layers"], M, r)),
+                "avg_launch_ms": round(avg_ms, 4), "per_launch_flop": flop_desc}
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -273,14 +319,14 @@ def main():
         "config": {"workload": cfg["workload"] + " (NF4 quantize + fwd + bwd of all 7 linears)",
                    "M": M, "r": r, "alpha": alpha, "layers": [[d["name"], d["N"], d["K"]] for d in L],
                    "blocksize": 64, "double_quant": "8-bit codes, fp32 per 256 blocks"},
-        "roofline": {"kernel": "nf4_gemm_fwd_kernel (fused dequant GEMM + LoRA up-projection)", "bound": "mfma",
-                     "achieved": round(fwd_tfs, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                     "frac": round(fwd_tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": measured_traffic(),
-                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                     "algorithmic_bytes_per_launch": round(fwd_algorithmic_bytes(cfg["layers"], M, r)),
-                     "avg_launch_ms": round(fwd_avg_ms, 4),
-                     "per_launch_flop": "2*M*K*N + 2*M*r*N over the 7 layer shapes, M=4096, r=64"},
-        "breakdown": {"bwd_call_tflops": round(bwd_tfs, 2), "bwd_call_avg_ms": round(bwd_avg_ms, 4),
+        "roofline": roofline("bwd_dx", bdx_tfs, bdx_avg_ms,
+                             "nf4_gemm_bwd_dx_kernel (fused dequant GEMM of dx + LoRA term u A^T; the step's "
+                             "largest share of GPU time)",
+                             "2*M*N*K + 2*M*r*K over the 7 layer shapes, M=4096, r=64"),
+        "breakdown": {"fwd_gemm_roofline": roofline("fwd", fwd_tfs, fwd_avg_ms,
+                                                     "nf4_gemm_fwd_kernel (fused dequant GEMM + LoRA up-projection)",
+                                                     "2*M*K*N + 2*M*r*N over the 7 layer shapes, M=4096, r=64"),
+                      "bwd_call_tflops": round(bwd_tfs, 2), "bwd_call_avg_ms": round(bwd_avg_ms, 4),
                       "wall_s_timed": round(wall, 3), "weights_per_step": n_weights,
                       "flop_per_step": total_flops},
     }
