@@ -266,16 +266,22 @@ def main():
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
+    # the headline: K steps with no events inside (an event recorded between two kernels leaves the GPU
+    # idle for several microseconds)
     t_start, t_stop = ev(), ev()
     wall0 = time.perf_counter()
     t_start.record()
     for _ in range(args.steps):
-        step(True)
+        step(False)
     t_stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_stop) / args.steps
     value = total_flops / (ms_step * 1e-3) / 1e12
+    # the same K steps again with events around each forward GEMM and each backward call, for the breakdown
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
 
     # The step's dominant kernel, the fused backward dx GEMM, on its own: qlora_linear_bwd launches it
     # between other kernels, so it is timed through its stage entry point on the same shapes and inputs.
