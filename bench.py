@@ -18,7 +18,7 @@ against the bf16 MFMA roofline, the forward GEMM likewise, the decode GEMV
 bandwidth, the scale-layout / codebook / dtype variants, a dense bf16
 torch.matmul for context, and the CPU oracle timed on a bounded sample.
 
-usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
+usage: python bench.py [--gpus 1] [--steps 10] [--warmup 10] [--no-cpu-baseline]
        python bench.py --mode pmc     (a few untimed steps + a calibration copy, for rocprofv3 --pmc)
        python bench.py --pmc-summary FETCH_CSV WRITE_CSV [--pmc-kernel fwd|bwd_dx]
                                       (HBM bytes per launch of one GEMM kernel from the two
@@ -43,7 +43,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="skip decode / quantize / dense context lines")
     p.add_argument("--mode", choices=["bench", "pmc"], default="bench")
