@@ -209,6 +209,26 @@ def dequant_blocks(packed, ahat, table=None, dtype="bf16"):
     return codec(dtype).from_f32_rne(w32)
 
 
+def dequant_blocks_f32(packed, ahat, table=None):
+    """fl32(a_hat * c_q) for whole blocks as float32 [nb, 64]: the dequantized weight before any rounding to a
+    16-bit compute dtype (section 5.2: w_hat = a * c_q, one IEEE float32 product; fp32 is one of the compute
+    dtypes of section 8.3)."""
+    c = nf4_table() if table is None else np.asarray(table, np.float32)
+    codes = unpack_nibbles(packed).reshape(-1, BLOCK)
+    ahat = np.asarray(ahat, dtype=np.float32)
+    return (ahat[:, None] * c[codes]).astype(np.float32)
+
+
+def dequantize_f32(packed, q8, A2, N, K, table=None):
+    """fp32 w_hat [N, K] = fl32(a_hat * c_q) with the double-quantized scales."""
+    return dequant_blocks_f32(packed, scale_dequant(q8, A2), table).reshape(N, K)
+
+
+def dequantize_nodq_f32(packed, absmax, N, K, table=None):
+    """fp32 w_hat [N, K] = fl32(a * c_q) with the stored fp32 block absmax."""
+    return dequant_blocks_f32(packed, np.asarray(absmax, np.float32), table).reshape(N, K)
+
+
 def dequantize_rows(packed, q8, A2, K, rows, table=None, dtype="bf16"):
     """w_hat of the selected rows of an [N, K] weight only (for sampled checks)."""
     rows = np.asarray(rows, dtype=np.int64)

@@ -341,3 +341,30 @@ def test_nodq_error_bound():
     half_gap = np.max(np.diff(nf4.nf4_table().astype(np.float64))) / 2
     bound = absmax.astype(np.float64)[:, None] * half_gap + np.abs(wh) * 2.0 ** -8
     assert np.all(np.abs(w - wh) <= bound + 1e-30)
+
+
+def test_fp32_dequant_is_the_rational_product_rounded_once():
+    """fp32 w_hat = round_f32(a_hat * c_q) element by element (Fraction products), for NF4 with double
+    quantization and for the stored-absmax layout; rounding it to bf16 gives the bf16 dequantization."""
+    from oracle import fp4
+    W = workloads.custom(79, (8, 192), 0.02)
+    packed, q8, A2 = nf4.quantize(W)
+    got = nf4.dequantize_f32(packed, q8, A2, 8, 192)
+    c = nf4.nf4_table()
+    ah = nf4.scale_dequant(q8, A2)
+    codes = nf4.unpack_nibbles(packed).reshape(-1, 64)
+    for b in range(codes.shape[0]):
+        for i in range(64):
+            p = Fraction(float(ah[b])) * Fraction(float(c[codes[b, i]]))
+            exp = brute.round_f32(p) if p != 0 else Fraction(0)
+            assert Fraction(float(got.reshape(-1, 64)[b, i])) == exp, (b, i)
+    assert np.array_equal(bf16.from_f32_rne(got), nf4.dequantize(packed, q8, A2, 8, 192))
+    pz, az = fp4.quantize_nodq(W)
+    g2 = nf4.dequantize_nodq_f32(pz, az, 8, 192, table=fp4.fp4_table())
+    t4 = fp4.fp4_table()
+    cz = nf4.unpack_nibbles(pz).reshape(-1, 64)
+    for b in range(cz.shape[0]):
+        for i in range(0, 64, 5):
+            p = Fraction(float(az[b])) * Fraction(float(t4[cz[b, i]]))
+            exp = brute.round_f32(p) if p != 0 else Fraction(0)
+            assert Fraction(float(g2.reshape(-1, 64)[b, i])) == exp
