@@ -123,6 +123,14 @@ qlora_status qlora_dequantize(const qlora_nf4* w, uint16_t* out, void* stream) {
                              (hipStream_t)stream);
 }
 
+qlora_status qlora_dequantize_f32(const qlora_nf4* w, float* out, void* stream) {
+    qlora_status st = check_state(w);
+    if (st != QLORA_OK) return st;
+    if (!out) return QLORA_ERR_INVALID_ARG;
+    if (!aligned16(out)) return QLORA_ERR_MISALIGNED;
+    return launch_dequantize_f32(w->codes, w->q8, w->a2, cb_of(w), w->n * w->k / kBlock, out, (hipStream_t)stream);
+}
+
 qlora_status qlora_merge(const qlora_nf4* w, const uint16_t* A, const uint16_t* B, int r, float alpha,
                          uint16_t* out, void* stream) {
     qlora_status st = check_state(w);

@@ -139,6 +139,8 @@ qlora_status launch_quantize(const uint16_t* W, int64_t nblocks, uint8_t* codes,
                              int dt, hipStream_t s);
 qlora_status launch_dequantize(const uint8_t* codes, const uint8_t* q8, const float* a2, int cb, int dt,
                                int64_t nblocks, uint16_t* out, hipStream_t s);
+qlora_status launch_dequantize_f32(const uint8_t* codes, const uint8_t* q8, const float* a2, int cb, int64_t nblocks,
+                                   float* out, hipStream_t s);
 qlora_status launch_merge(const uint8_t* codes, const uint8_t* q8, const float* a2, int cb, int dt, const uint16_t* A,
                           const uint16_t* B, int r, float s, uint16_t* out, int N, int K, hipStream_t st);
 qlora_status launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* q8, const float* a2, int cb,

@@ -170,12 +170,13 @@ __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint16_t* 
 // nf4_dequantize_kernel: 256 lanes x 8 weights = 32 blocks per workgroup.
 //   a_hat = fl32(fl32(a2/255) * q8) (without double quantization: the stored
 //   fp32 absmax a2[b]), w_hat = RNE_bf16(fl32(a_hat * c_code)).
-template <bool DQ, int CB, int DT>
+// F32: write the fp32 products fl32(a_hat * c_code) themselves (out is then float*).
+template <bool DQ, int CB, int DT, bool F32>
 __global__ __launch_bounds__(kThreads) void nf4_dequantize_kernel(const uint8_t* __restrict__ codes,
                                                                   const uint8_t* __restrict__ q8,
                                                                   const float* __restrict__ a2,
                                                                   int64_t nblocks,
-                                                                  uint16_t* __restrict__ out) {
+                                                                  void* __restrict__ out) {
     __shared__ float s_c[16];
     const int tid = threadIdx.x;
     if (tid < 16) s_c[tid] = level<CB>(tid);
@@ -186,14 +187,23 @@ __global__ __launch_bounds__(kThreads) void nf4_dequantize_kernel(const uint8_t*
     const float ahat = DQ ? __fmul_rn(__fdiv_rn(a2[b / kSuper], 255.0f), (float)q8[b]) : a2[b];
     const uint32_t pk = *reinterpret_cast<const uint32_t*>(codes + b * (kBlock / 2) + sub * 4);
     u32x4_t o;
+    float wf[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const uint32_t byte = (pk >> (8 * j)) & 0xFFu;
         const float w0 = __fmul_rn(ahat, s_c[byte >> 4]);
         const float w1 = __fmul_rn(ahat, s_c[byte & 0xFu]);
         o[j] = pack2<DT>(w0, w1);
+        wf[2 * j] = w0;
+        wf[2 * j + 1] = w1;
     }
-    *reinterpret_cast<u32x4_t*>(out + b * kBlock + sub * 8) = o;
+    if (F32) {
+        f32x4_t* dst = reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + b * kBlock + sub * 8);
+        dst[0] = f32x4_t{wf[0], wf[1], wf[2], wf[3]};
+        dst[1] = f32x4_t{wf[4], wf[5], wf[6], wf[7]};
+    } else {
+        *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(out) + b * kBlock + sub * 8) = o;
+    }
 }
 
 }  // namespace
@@ -219,11 +229,26 @@ qlora_status launch_dequantize(const uint8_t* codes, const uint8_t* q8, const fl
     with_cb_dt(cb, dt, [&](auto cbc, auto dtc) {
         constexpr int CB = decltype(cbc)::value, DT = decltype(dtc)::value;
         if (q8)
-            hipLaunchKernelGGL((nf4_dequantize_kernel<true, CB, DT>), dim3((unsigned)grid), dim3(kThreads), 0, s, codes,
-                               q8, a2, nblocks, out);
+            hipLaunchKernelGGL((nf4_dequantize_kernel<true, CB, DT, false>), dim3((unsigned)grid), dim3(kThreads), 0, s,
+                               codes, q8, a2, nblocks, static_cast<void*>(out));
         else
-            hipLaunchKernelGGL((nf4_dequantize_kernel<false, CB, DT>), dim3((unsigned)grid), dim3(kThreads), 0, s,
-                               codes, q8, a2, nblocks, out);
+            hipLaunchKernelGGL((nf4_dequantize_kernel<false, CB, DT, false>), dim3((unsigned)grid), dim3(kThreads), 0,
+                               s, codes, q8, a2, nblocks, static_cast<void*>(out));
+    });
+    return launch_status();
+}
+
+qlora_status launch_dequantize_f32(const uint8_t* codes, const uint8_t* q8, const float* a2, int cb, int64_t nblocks,
+                                   float* out, hipStream_t s) {
+    const int64_t grid = (nblocks + 31) / 32;
+    with_cb_dt(cb, kDtBf16, [&](auto cbc, auto) {
+        constexpr int CB = decltype(cbc)::value;
+        if (q8)
+            hipLaunchKernelGGL((nf4_dequantize_kernel<true, CB, kDtBf16, true>), dim3((unsigned)grid), dim3(kThreads),
+                               0, s, codes, q8, a2, nblocks, static_cast<void*>(out));
+        else
+            hipLaunchKernelGGL((nf4_dequantize_kernel<false, CB, kDtBf16, true>), dim3((unsigned)grid),
+                               dim3(kThreads), 0, s, codes, q8, a2, nblocks, static_cast<void*>(out));
     });
     return launch_status();
 }

@@ -51,6 +51,7 @@ def _load():
         "qlora_nf4_sizes_nodq": (ctypes.c_int, [c_i64, c_i64, ctypes.POINTER(c_sz), ctypes.POINTER(c_sz)]),
         "qlora_quantize": (ctypes.c_int, [c_vp, c_i64, c_i64, P, c_vp]),
         "qlora_dequantize": (ctypes.c_int, [P, c_vp, c_vp]),
+        "qlora_dequantize_f32": (ctypes.c_int, [P, c_vp, c_vp]),
         "qlora_merge": (ctypes.c_int, [P, c_vp, c_vp, ctypes.c_int, ctypes.c_float, c_vp, c_vp]),
         "qlora_fwd_workspace": (c_sz, [c_i64, c_i64, c_i64, ctypes.c_int]),
         "qlora_linear_fwd": (ctypes.c_int, [P, c_vp, c_i64, c_vp, c_vp, ctypes.c_int, ctypes.c_float,
@@ -175,12 +176,17 @@ def quantize(W, out=None, double_quant=True, quant_type="nf4"):
     return w
 
 
-def dequantize(w, out=None):
-    """bf16 [N, K] reconstruction (qlora_dequantize); tests and export only."""
-    o = torch.empty((w.N, w.K), dtype=w.dtype, device=w.codes.device) if out is None else out
-    _dev(o, w.dtype, "out", (w.N, w.K))
+def dequantize(w, out=None, fp32=False):
+    """[N, K] reconstruction in the weight's compute dtype (qlora_dequantize), or with fp32=True the fp32
+    products themselves (qlora_dequantize_f32); tests and export only."""
+    dt = torch.float32 if fp32 else w.dtype
+    o = torch.empty((w.N, w.K), dtype=dt, device=w.codes.device) if out is None else out
+    _dev(o, dt, "out", (w.N, w.K))
     st = w.state()
-    _check(lib.qlora_dequantize(ctypes.byref(st), _ptr(o), _stream()), "qlora_dequantize")
+    if fp32:
+        _check(lib.qlora_dequantize_f32(ctypes.byref(st), _ptr(o), _stream()), "qlora_dequantize_f32")
+    else:
+        _check(lib.qlora_dequantize(ctypes.byref(st), _ptr(o), _stream()), "qlora_dequantize")
     return o
 
 

@@ -135,6 +135,13 @@ qlora_status qlora_quantize(const uint16_t* W, int64_t N, int64_t K, const qlora
  * For tests and export only: the linear layer never materialises W. */
 qlora_status qlora_dequantize(const qlora_nf4* w, uint16_t* out, void* stream);
 
+/* Dequantize to fp32 out [N, K] (deep dive 5.2 with the fp32 compute dtype of
+ * section 8.3): out = fl32(a_hat * c_code), the product itself, with no 16-bit
+ * rounding (RNE_bf16 of it is what qlora_dequantize writes for a bf16 state).
+ * Either scale layout and codebook; w->dtype is not used.  out 16-byte aligned;
+ * NULL -> INVALID_ARG. */
+qlora_status qlora_dequantize_f32(const qlora_nf4* w, float* out, void* stream);
+
 /* LoRA merge for deployment ("LoRA, QLoRA, QA-LoRA explained", section 2:
  * W_eff = dequant(W4) + (alpha/r) A B; "bitsandbytes deep dive", section 12.10:
  * merge in higher precision, re-quantize afterwards if a 4-bit model is wanted,

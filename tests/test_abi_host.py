@@ -98,6 +98,9 @@ def test_quantize_argument_errors(q):
     assert f(FAKE, 64, 64, ctypes.byref(bad_dt), None) == INVALID
     assert q.lib.qlora_dequantize(ctypes.byref(bad_dt), FAKE, None) == INVALID
     assert q.lib.qlora_dequantize(ctypes.byref(st), None, None) == INVALID
+    assert q.lib.qlora_dequantize_f32(ctypes.byref(st), None, None) == INVALID
+    assert q.lib.qlora_dequantize_f32(ctypes.byref(st), FAKE + 4, None) == MISALIGNED
+    assert q.lib.qlora_dequantize_f32(ctypes.byref(bad_qt), FAKE, None) == INVALID
     assert q.lib.qlora_dequantize(ctypes.byref(st), FAKE + 4, None) == MISALIGNED
 
 

@@ -116,3 +116,27 @@ def test_c5_sampled_groups(q):
             assert np.array_equal(q8[g * 256:(g + 1) * 256], rq)
             assert a2[g] == ra[0]
         del w
+
+
+@pytest.mark.parametrize("cb,dq", [("nf4", True), ("nf4", False), ("fp4", True), ("fp4", False)])
+def test_dequantize_fp32_products(q, cb, dq):
+    """qlora_dequantize_f32: the fp32 products fl32(a_hat * c_q) bit for bit, on ragged groups."""
+    import torch
+    from oracle import fp4
+    N, K = 37, 640                                          # 370 blocks: one full group and a short one
+    W = workloads.custom(6100 + dq, (N, K), 0.02)
+    say(f"[dequantize fp32] {cb} double_quant={dq}")
+    w = q.quantize(dev_bf16(W), double_quant=dq, quant_type=cb)
+    got = q.dequantize(w, fp32=True)
+    torch.cuda.synchronize()
+    table = nf4.nf4_table() if cb == "nf4" else fp4.fp4_table()
+    mod = nf4 if cb == "nf4" else fp4
+    if dq:
+        p, q8, a2 = mod.quantize(W)
+        ref = nf4.dequantize_f32(p, q8, a2, N, K, table=table)
+    else:
+        p, a = mod.quantize_nodq(W)
+        ref = nf4.dequantize_nodq_f32(p, a, N, K, table=table)
+    g = got.cpu().numpy()
+    assert np.array_equal(g.view(np.uint32), ref.view(np.uint32)), \
+        f"differs at {np.flatnonzero(g.view(np.uint32) != ref.view(np.uint32))[:8]}"
