@@ -393,8 +393,10 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
         return *reinterpret_cast<const u32x4_t*>(cd + crl[u] * 64 + 16 * ((2 * j + h) ^ ((crl[u] >> 1) & 3)));
     };
 
-    // x panel rows [m0, M) as a buffer; lane's tile row 8*wave + lane/8, chunk
-    const i32x4_t xrs = buffer_rsrc(x + (int64_t)m0 * K, (uint32_t)((int64_t)(M - m0) * K * 2));
+    // x panel rows [m0, min(M, m0 + kTM)) as a buffer; lane's tile row 8*wave + lane/8, chunk
+    // the panel's own rows only (at most kTM; the launcher checks kTM * K * 2 < 2^32): a range over all rows
+    // to M could pass 4 GiB and wrap
+    const i32x4_t xrs = buffer_rsrc(x + (int64_t)m0 * K, (uint32_t)((int64_t)min(M - m0, kTM) * K * 2));
     const int xrow = 8 * wv + (lane >> 3);
     const int xchunk = (lane & 7) ^ (((xrow ^ (xrow >> 3)) & 3) ^ (xrow & 4));
     const uint32_t xvoff = (uint32_t)(((int64_t)xrow * K + 8 * xchunk) * 2);
@@ -753,9 +755,10 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][u][v] = 0.0f;
 
-    // dy panel rows [m0, M): direct loads when rows are 16-byte aligned
+    // dy panel rows [m0, min(M, m0 + kTM)): direct loads when rows are 16-byte aligned
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    const i32x4_t drs = buffer_rsrc(dy + (int64_t)m0 * N, (uint32_t)((int64_t)(M - m0) * N * 2));
+    // the panel's own rows only (at most kTM; DYVEC requires kTM * N * 2 < 2^32)
+    const i32x4_t drs = buffer_rsrc(dy + (int64_t)m0 * N, (uint32_t)((int64_t)min(M - m0, kTM) * N * 2));
     const int xrow = 8 * wv + (lane >> 3);
     const int xchunk = (lane & 7) ^ (((xrow ^ (xrow >> 3)) & 3) ^ (xrow & 4));
     const uint32_t dvoff = (uint32_t)(((int64_t)xrow * N + 8 * xchunk) * 2);

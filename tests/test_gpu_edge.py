@@ -7,6 +7,9 @@
   and the pooled branch.
 * An all-zero base weight: every block has absmax 0 and takes the zero code, so
   the layer reduces to its LoRA branch, y = s x A B and dx = s dy B^T A^T.
+* Activations of 4 GiB and more (M K 2 >= 2^32): the GEMMs read each 256-row
+  panel through a buffer whose byte range must not wrap (slow: 9 GB of device
+  memory).
 """
 import numpy as np
 import pytest
@@ -135,3 +138,43 @@ def test_all_zero_base_weight(q):
     torch.cuda.synchronize()
     ry, _ = lora.linear_fwd(bf16.to_f64(x[:1]), Wh, bf16.to_f64(A), bf16.to_f64(B), 32.0, r)
     assert lora.rel_err(host_f64(y1), ry) <= TOL
+
+
+@pytest.mark.slow
+def test_activation_panels_beyond_4_gib(q):
+    """x is [65536, 32768] bf16 = 2^32 bytes: a buffer range over all rows from a panel's first row would wrap
+    to 0 for the first panel.  Inputs come from torch's seeded device generator (not from the library);
+    sampled rows of y and dx, including the first panel's, are checked against the oracle."""
+    import torch
+    M, K, N, r, alpha = 65536, 32768, 256, 16, 32.0
+    dev = "cuda:0"
+    say(f"[edge] 4 GiB activations M={M} K={K} N={N}")
+    g = torch.Generator(device=dev).manual_seed(12345)
+    x = torch.randn((M, K), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    dy = torch.randn((M, N), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    W = workloads.custom(5500, (N, K), 0.02)
+    A = workloads.custom(5501, (K, r), 0.25)
+    B = workloads.custom(5502, (r, N), 0.01)
+    w = q.quantize(dev_bf16(W))
+    Ad, Bd = dev_bf16(A), dev_bf16(B)
+    y, t = q.linear_fwd(w, x, Ad, Bd, alpha)
+    del t
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 255, 256, 40000, M - 1])
+    xs = host_bits(x[torch.from_numpy(rows).to(dev)])
+    ys = host_f64(y[torch.from_numpy(rows).to(dev)])
+    del y
+    dx, _, _ = q.linear_bwd(w, x, Ad, Bd, alpha, dy)
+    torch.cuda.synchronize()
+    dys = host_bits(dy[torch.from_numpy(rows).to(dev)])
+    dxs = host_f64(dx[torch.from_numpy(rows).to(dev)])
+    del dx, x, dy
+    p, q8, a2 = nf4.quantize(W)
+    Wh = bf16.to_f64(nf4.dequantize(p, q8, a2, N, K))
+    Af, Bf = bf16.to_f64(A), bf16.to_f64(B)
+    ry, _ = lora.linear_fwd(bf16.to_f64(xs), Wh, Af, Bf, alpha, r)
+    rdx = bf16.to_f64(dys) @ Wh + (alpha / r) * (bf16.to_f64(dys) @ Bf.T) @ Af.T
+    for i in range(len(rows)):
+        ey = lora.rel_err(ys[i], ry[i])
+        ex = lora.rel_err(dxs[i], rdx[i])
+        assert ey <= TOL and ex <= TOL, f"row {rows[i]}: y rel err {ey:.3e}, dx rel err {ex:.3e}"
