@@ -12,8 +12,16 @@
 //      is exact in fp64, then rounded down to the bf16 grid), the group scale
 //      a2 = max a, and the 8-bit scale code;
 //   4. for a bf16 weight w and any real X, w > X  <=>  w > RD_bf16(X), so the
-//      code = #{j : w/a > m_j} (nearest level, ties to the lower index) is a
-//      4-step branchless binary search over T_j in fp32 compares;
+//      code = #{j : w/a > m_j} (nearest level, ties to the lower index) needs
+//      only exact compares against T_j.  A bucket index i = trunc(fma(w, 64/a,
+//      64)) places 64 (w/a + 1) in [i - e, i + 1 + e] with e < 2^-16; the
+//      midpoints 64 (m_j + 1) lie more than 5 buckets apart, so at most one of
+//      them, j = c, is in reach of bucket i, where c = #{j : 64 (m_j + 1) <
+//      i - 1/1024} comes from a 129-entry table.  Then code = c + [w > T_c]
+//      (T_15 = +inf), whichever side of its bucket w fell on: one fma, one
+//      table read, one threshold read and one compare per weight.  Blocks with
+//      0 < a < 2^-100 (64/a could overflow) take a branchless binary search
+//      over the same thresholds instead;
 //   5. nibbles are packed (element 2i high) and stored as one dword per lane.
 // Without double quantization (sections 7.1, 9.5) step 3 stores each block's
 // absmax as its fp32 scale instead of the 8-bit code and the group scale.
@@ -24,6 +32,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kPasses = kSuper / 32;  // 32 blocks per pass (4 waves x 8 blocks)
+constexpr int kThrStride = 17;        // per block: T_0..T_14, +inf, 64/a; an odd stride spreads blocks over banks
+constexpr int kBuckets = 129;         // trunc(64 (u + 1)) for u in [-1, 1]
+constexpr float kTinyScale = 0x1p-100f;
 
 __device__ __forceinline__ uint32_t absmax_bits8(u32x4_t v) {
     uint32_t m = 0;
@@ -61,8 +72,9 @@ __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint16_t* 
                                                                 uint8_t* __restrict__ q8,
                                                                 float* __restrict__ a2) {
     __shared__ float s_amax[kSuper];
-    __shared__ float s_thr[kSuper * 16];
+    __shared__ float s_thr[kSuper * kThrStride];
     __shared__ float s_wmax[kThreads / 64];
+    __shared__ uint8_t s_lut[kBuckets + 31];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -82,6 +94,18 @@ __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint16_t* 
         } else {
             v[p] = u32x4_t{0u, 0u, 0u, 0u};
         }
+    }
+
+    // bucket table: c(i) = number of midpoints m_j with 64 (m_j + 1) < i - 1/1024 (fp64, exact)
+    if (tid < kBuckets) {
+        int c = 0;
+#pragma unroll
+        for (int j = 0; j + 1 < kDistinctLevels<CB>; ++j) {
+            const double m = 0.5 * ((double)level<CB>(code_of_sorted<CB>(j)) +
+                                    (double)level<CB>(code_of_sorted<CB>(j + 1)));
+            c += (64.0 * m + 64.0 < (double)tid - 1.0 / 1024.0) ? 1 : 0;
+        }
+        s_lut[tid] = (uint8_t)c;
     }
 
     // 2. block absmax
@@ -119,11 +143,11 @@ __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint16_t* 
 #pragma unroll
             for (int j = 0; j < 15; ++j) T[j] = (j < kZeroCode) ? -1.0f : 1.0f;  // every w = 0 -> code 7
         }
-        f32x4_t* dst = reinterpret_cast<f32x4_t*>(&s_thr[tid * 16]);
-        dst[0] = f32x4_t{T[0], T[1], T[2], T[3]};
-        dst[1] = f32x4_t{T[4], T[5], T[6], T[7]};
-        dst[2] = f32x4_t{T[8], T[9], T[10], T[11]};
-        dst[3] = f32x4_t{T[12], T[13], T[14], 0.0f};
+        float* dst = &s_thr[tid * kThrStride];
+#pragma unroll
+        for (int j = 0; j < 15; ++j) dst[j] = T[j];
+        dst[15] = __builtin_huge_valf();                  // c = 15: every midpoint lies below the bucket
+        dst[16] = a >= kTinyScale ? __fdiv_rn(64.0f, a) : 0.0f;  // 0 (bucket 64) for a = 0 and tiny a
     }
     if (!DQ) {
         if (tid < nb_here) a2[b0 + tid] = a;  // the exact block absmax is the fp32 scale
@@ -153,14 +177,29 @@ __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint16_t* 
     for (int p = 0; p < kPasses; ++p) {
         const int bl = p * 32 + wave * 8 + (lane >> 3);
         if (bl < nb_here) {
-            const f32x4_t* src = reinterpret_cast<const f32x4_t*>(&s_thr[bl * 16]);
-            const f32x4_t t0 = src[0], t1 = src[1], t2 = src[2], t3 = src[3];
+            const float* tb = &s_thr[bl * kThrStride];
+            const float sc = tb[16];
             uint32_t packed = 0;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const uint32_t bits = (i & 1) ? (v[p][i >> 1] >> 16) : (v[p][i >> 1] & 0xFFFFu);
-                const uint32_t q = code_of_sorted<CB>(nf4_code(h16_to_f32<DT>(bits), t0, t1, t2, t3));
+                const float w = h16_to_f32<DT>(bits);
+                const int bucket = (int)__builtin_fmaf(w, sc, 64.0f);  // 0 .. 128 (trunc; -2^-16 -> 0)
+                const uint32_t c = s_lut[bucket];
+                const uint32_t q = code_of_sorted<CB>(c + (w > tb[c] ? 1u : 0u));
                 packed |= q << (4 * (i ^ 1));
+            }
+            const float ab = s_amax[bl];
+            if (ab > 0.0f && ab < kTinyScale) {               // rare: 64/a may not be finite
+                const f32x4_t t0 = {tb[0], tb[1], tb[2], tb[3]}, t1 = {tb[4], tb[5], tb[6], tb[7]};
+                const f32x4_t t2 = {tb[8], tb[9], tb[10], tb[11]}, t3 = {tb[12], tb[13], tb[14], 0.0f};
+                packed = 0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t bits = (i & 1) ? (v[p][i >> 1] >> 16) : (v[p][i >> 1] & 0xFFFFu);
+                    const uint32_t q = code_of_sorted<CB>(nf4_code(h16_to_f32<DT>(bits), t0, t1, t2, t3));
+                    packed |= q << (4 * (i ^ 1));
+                }
             }
             *reinterpret_cast<uint32_t*>(codes + (b0 + bl) * (kBlock / 2) + sub * 4) = packed;
         }
