@@ -98,6 +98,15 @@ def normal_f16(seed, shape, std):
     return v.astype(np.float16).view(np.uint16).reshape(shape)
 
 
+def normal_fp32(seed, shape, std):
+    """fp32 (uint32 bits) tensor of N(0, std^2) values: the same draws as normal_bf16, kept in binary32."""
+    n = int(np.prod(shape))
+    v = normal_f32(seed, n)
+    if std != 1.0:
+        v *= np.float32(std)
+    return np.ascontiguousarray(v).view(np.uint32).reshape(shape)
+
+
 def seed_of(cfg_id, layer, tensor_id):
     return CONFIGS[cfg_id]["base"] + 10 * layer + tensor_id
 

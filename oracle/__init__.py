@@ -25,6 +25,7 @@ Sources (web pages on QLoRA / NF4 / bitsandbytes):
 Modules:
   bf16   -- bf16 decode and round-to-nearest-even encode (own implementation)
   f16    -- fp16 decode and encode (numpy's IEEE binary16), the other 16-bit compute dtype
+  f32    -- fp32 bit patterns, the third compute dtype (no rounding of the dequantized weight)
   nf4    -- codebook, blocking, codes, packing, double quantization, dequant
   brute  -- exact rational (fractions.Fraction) brute-force versions
   lora   -- fp64 forward / backward of the QLoRA linear

@@ -9,6 +9,8 @@ round-to-nearest-even of an fp32 value.
 """
 import numpy as np
 
+BITS = np.uint16     # storage of one value
+
 
 def to_f32(u16):
     """Exact value of bf16 bit patterns as float32 (bits placed in the top half)."""

@@ -13,6 +13,8 @@ float32 -> float16 cast in the tests.
 """
 import numpy as np
 
+BITS = np.uint16     # storage of one value
+
 
 def to_f32(u16):
     """Exact value of fp16 bit patterns as float32."""

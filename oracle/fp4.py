@@ -113,7 +113,7 @@ def quantize(W_u16, dtype="bf16"):
     the NF4 quantization of the same weight (section 7: the constants are
     quantized after, and independently of, the codes).
     """
-    wb16 = nf4.blocks(np.asarray(W_u16, dtype=np.uint16))
+    wb16 = nf4.blocks(np.asarray(W_u16, dtype=nf4.codec(dtype).BITS))
     nb = wb16.shape[0]
     a = np.empty(nb, dtype=np.float64)
     codes = np.empty((nb, nf4.BLOCK), dtype=np.uint8)
@@ -132,7 +132,7 @@ def quantize(W_u16, dtype="bf16"):
 
 def quantize_nodq(W_u16, dtype="bf16"):
     """FP4 codes with one fp32 absmax per block (double quantization off) -> (packed codes, absmax)."""
-    wb16 = nf4.blocks(np.asarray(W_u16, dtype=np.uint16))
+    wb16 = nf4.blocks(np.asarray(W_u16, dtype=nf4.codec(dtype).BITS))
     nb = wb16.shape[0]
     a = np.empty(nb, dtype=np.float32)
     codes = np.empty((nb, nf4.BLOCK), dtype=np.uint8)

@@ -18,7 +18,7 @@ from statistics import NormalDist
 
 import numpy as np
 
-from . import bf16, f16
+from . import bf16, f16, f32
 
 BLOCK = 64          # first-level block (section 5.1: default block size 64)
 SUPER = 256         # first-level scales per fp32 second-level scale (section 7.2)
@@ -30,8 +30,9 @@ ZERO_CODE = 7       # index of the exact-zero codebook entry
 # a1: the NF4 codebook
 # ----------------------------------------------------------------------------
 def codec(dtype):
-    """The 16-bit float format of a tensor: "bf16" (the default compute dtype) or "f16" (deep dive 8.3)."""
-    return {"bf16": bf16, "f16": f16}[dtype]
+    """The float format of a tensor (deep dive 8.3): "bf16" (the default compute dtype), "f16", or "f32"
+    (binary32, where the dequantized weight keeps its fp32 product unrounded)."""
+    return {"bf16": bf16, "f16": f16, "f32": f32}[dtype]
 
 
 def nf4_delta():
@@ -250,12 +251,14 @@ def _ahat_of_blocks(q8, A2, bidx):
 # ----------------------------------------------------------------------------
 def quantize(W_u16, table=None, dtype="bf16"):
     """Quantize a bf16 (or, with dtype="f16", fp16) weight [N, K] (uint16 bits) -> (packed codes, q8, A2).
+    With dtype="f32" the weight is fp32 (uint32 bits); the steps are the same, since every threshold product
+    a * m_j (24-bit a, 25-bit m_j) is still exact in float64.
 
     The codes are taken against the true block absmax a (the page encodes the
     weights first and only then re-quantizes the constants, section 7).
     Returns packed uint8 [N*K/2], q8 uint8 [N*K/64], A2 float32 [ceil(N*K/16384)].
     """
-    wb16 = blocks(np.asarray(W_u16, dtype=np.uint16))
+    wb16 = blocks(np.asarray(W_u16, dtype=codec(dtype).BITS))
     nb = wb16.shape[0]
     a = np.empty(nb, dtype=np.float64)
     codes = np.empty((nb, BLOCK), dtype=np.uint8)
@@ -284,7 +287,7 @@ def quantize_nodq(W_u16, table=None, dtype="bf16"):
     against the true block absmax).  Returns packed uint8 [N*K/2] and absmax
     float32 [N*K/64] (exact: the absmax of bf16 values is a bf16 value).
     """
-    wb16 = blocks(np.asarray(W_u16, dtype=np.uint16))
+    wb16 = blocks(np.asarray(W_u16, dtype=codec(dtype).BITS))
     nb = wb16.shape[0]
     a = np.empty(nb, dtype=np.float32)
     codes = np.empty((nb, BLOCK), dtype=np.uint8)
