@@ -14,14 +14,19 @@ namespace {
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // q8 == NULL selects the state without double quantization (a2 = one fp32
-// absmax per block); codes and a2 are required either way.
-inline qlora_status check_state(const qlora_nf4* w) {
+// absmax per block); codes and a2 are required either way.  The 16-bit entry
+// points take bf16 and fp16 states, the _f32 ones fp32 states only; dtype_any
+// admits all three (qlora_dequantize_f32 does not read the dtype).
+enum DtypeClass { kDt16, kDt32, kDtAny };
+inline qlora_status check_state(const qlora_nf4* w, DtypeClass dc = kDt16) {
     if (!w || !w->codes || !w->a2) return QLORA_ERR_INVALID_ARG;
     if (w->n < 1 || w->k < 1) return QLORA_ERR_INVALID_ARG;
     if (w->k % kBlock) return QLORA_ERR_UNSUPPORTED_SHAPE;
     if (w->n > (int64_t(1) << 31) || w->k > (int64_t(1) << 31)) return QLORA_ERR_UNSUPPORTED_SHAPE;
     if (w->quant_type != QLORA_QUANT_NF4 && w->quant_type != QLORA_QUANT_FP4) return QLORA_ERR_INVALID_ARG;
-    if (w->dtype != QLORA_DTYPE_BF16 && w->dtype != QLORA_DTYPE_F16) return QLORA_ERR_INVALID_ARG;
+    const bool is16 = w->dtype == QLORA_DTYPE_BF16 || w->dtype == QLORA_DTYPE_F16;
+    const bool is32 = w->dtype == QLORA_DTYPE_F32;
+    if (!(dc == kDt16 ? is16 : dc == kDt32 ? is32 : (is16 || is32))) return QLORA_ERR_INVALID_ARG;
     if (!aligned16(w->codes) || (w->q8 && !aligned16(w->q8)) || !aligned16(w->a2)) return QLORA_ERR_MISALIGNED;
     return QLORA_OK;
 }
@@ -66,6 +71,35 @@ inline BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int r) {
 }
 
 inline uint8_t* at(void* ws, size_t off) { return static_cast<uint8_t*>(ws) + off; }
+
+// fp32 layer: bytes of the split partial sums of one contraction (0 when it does not split)
+inline size_t f32_part(int64_t rows, int64_t cols, int64_t red) {
+    const F32Plan p = plan_f32((int)rows, (int)cols, (int)std::max<int64_t>(red, 1));
+    return p.splits > 1 ? align256((size_t)p.splits * rows * cols * 4) : 0;
+}
+struct F32FwdWs {
+    size_t tbuf, part, total;
+};
+inline F32FwdWs f32_fwd_ws(int64_t M, int64_t N, int64_t K, int r) {
+    F32FwdWs w{};
+    w.tbuf = 0;
+    w.part = align256((size_t)M * r * 4);
+    w.total = w.part + std::max(f32_part(M, r, K), f32_part(M, N, K));
+    return w;
+}
+struct F32BwdWs {
+    size_t u, tbuf, part, total;
+};
+inline F32BwdWs f32_bwd_ws(int64_t M, int64_t N, int64_t K, int r) {
+    F32BwdWs w{};
+    w.u = 0;
+    w.tbuf = align256((size_t)M * r * 4);
+    w.part = 2 * w.tbuf;
+    const size_t p = std::max({f32_part(M, r, N), f32_part(M, r, K), f32_part(M, K, N), f32_part(K, r, M),
+                               f32_part(r, N, M)});
+    w.total = w.part + p;
+    return w;
+}
 
 }  // namespace
 
@@ -124,7 +158,7 @@ qlora_status qlora_dequantize(const qlora_nf4* w, uint16_t* out, void* stream) {
 }
 
 qlora_status qlora_dequantize_f32(const qlora_nf4* w, float* out, void* stream) {
-    qlora_status st = check_state(w);
+    qlora_status st = check_state(w, kDtAny);
     if (st != QLORA_OK) return st;
     if (!out) return QLORA_ERR_INVALID_ARG;
     if (!aligned16(out)) return QLORA_ERR_MISALIGNED;
@@ -263,6 +297,89 @@ qlora_status qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, int64_t M, 
         QLORA_OK)
         return st;
     return launch_tn(dy, t, reinterpret_cast<float*>(at(ws, L.pb)), dB, (int)M, (int)N, r, 1, N, dt_of(w), s);
+}
+
+// ---- fp32 compute dtype (deep dive 8.3): fp32 tensors, w_hat = fl32(a_hat * c_q)
+qlora_status qlora_quantize_f32(const float* W, int64_t N, int64_t K, const qlora_nf4* out, void* stream) {
+    if (!W) return QLORA_ERR_INVALID_ARG;
+    qlora_status st = check_state(out, kDt32);
+    if (st != QLORA_OK) return st;
+    if (out->n != N || out->k != K) return QLORA_ERR_INVALID_ARG;
+    if (!aligned16(W)) return QLORA_ERR_MISALIGNED;
+    return launch_quantize(W, N * K / kBlock, out->codes, out->q8, out->a2, cb_of(out), kDtF32, (hipStream_t)stream);
+}
+
+size_t qlora_fwd_workspace_f32(int64_t M, int64_t N, int64_t K, int r) {
+    if (bad_dims(M, N, K, r) || M == 0 || K % kBlock) return 0;
+    return f32_fwd_ws(M, N, K, r).total;
+}
+
+size_t qlora_bwd_workspace_f32(int64_t M, int64_t N, int64_t K, int r) {
+    if (bad_dims(M, N, K, r) || M == 0 || K % kBlock) return 0;
+    return f32_bwd_ws(M, N, K, r).total;
+}
+
+qlora_status qlora_linear_fwd_f32(const qlora_nf4* w, const float* x, int64_t M, const float* A, const float* B,
+                                  int r, float alpha, float* y, float* t_out, void* ws, size_t ws_bytes,
+                                  void* stream) {
+    qlora_status st = check_state(w, kDt32);
+    if (st != QLORA_OK) return st;
+    const int64_t N = w->n, K = w->k;
+    if (bad_dims(M, N, K, r) || !std::isfinite(alpha)) return QLORA_ERR_INVALID_ARG;
+    if (M == 0) return QLORA_OK;
+    if (!x || !A || !B || !y) return QLORA_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(y) || (t_out && !aligned16(t_out)))
+        return QLORA_ERR_MISALIGNED;
+    const F32FwdWs L = f32_fwd_ws(M, N, K, r);
+    if (!ws || ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
+    if (!aligned16(ws)) return QLORA_ERR_MISALIGNED;
+    hipStream_t s = (hipStream_t)stream;
+    float* part = reinterpret_cast<float*>(at(ws, L.part));
+    float* t = t_out ? t_out : reinterpret_cast<float*>(at(ws, L.tbuf));
+    const float scale = alpha / (float)r;
+    if ((st = launch_f32_lora(kF32LoraDown, x, A, (int)M, (int)K, r, scale, t, part, s)) != QLORA_OK) return st;
+    return launch_f32_fwd(x, w->codes, w->q8, w->a2, cb_of(w), t, B, y, (int)M, (int)N, (int)K, r, part, s);
+}
+
+qlora_status qlora_linear_bwd_f32(const qlora_nf4* w, const float* x, int64_t M, const float* A, const float* B,
+                                  int r, float alpha, const float* t, const float* dy, float* dx, float* dA,
+                                  float* dB, void* ws, size_t ws_bytes, void* stream) {
+    qlora_status st = check_state(w, kDt32);
+    if (st != QLORA_OK) return st;
+    const int64_t N = w->n, K = w->k;
+    if (bad_dims(M, N, K, r) || !std::isfinite(alpha)) return QLORA_ERR_INVALID_ARG;
+    if (!dA || !dB) return QLORA_ERR_INVALID_ARG;
+    if (!aligned16(dA) || !aligned16(dB)) return QLORA_ERR_MISALIGNED;
+    hipStream_t s = (hipStream_t)stream;
+    if (M == 0) {  // empty sums
+        if ((st = launch_fill(dA, K * r, 0.0f, s)) != QLORA_OK) return st;
+        return launch_fill(dB, (int64_t)r * N, 0.0f, s);
+    }
+    if (!x || !A || !B || !dy) return QLORA_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(dy) || (t && !aligned16(t)) ||
+        (dx && !aligned16(dx)))
+        return QLORA_ERR_MISALIGNED;
+    const F32BwdWs L = f32_bwd_ws(M, N, K, r);
+    if (!ws || ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
+    if (!aligned16(ws)) return QLORA_ERR_MISALIGNED;
+    const float scale = alpha / (float)r;
+    float* u = reinterpret_cast<float*>(at(ws, L.u));
+    float* part = reinterpret_cast<float*>(at(ws, L.part));
+    // u = s dy B^T
+    if ((st = launch_f32_lora(kF32LoraDownT, dy, B, (int)M, (int)N, r, scale, u, part, s)) != QLORA_OK) return st;
+    if (!t) {  // recompute t = s x A
+        float* tb = reinterpret_cast<float*>(at(ws, L.tbuf));
+        if ((st = launch_f32_lora(kF32LoraDown, x, A, (int)M, (int)K, r, scale, tb, part, s)) != QLORA_OK) return st;
+        t = tb;
+    }
+    if (dx) {
+        if ((st = launch_f32_bwd_dx(dy, w->codes, w->q8, w->a2, cb_of(w), u, A, dx, (int)M, (int)N, (int)K, r, part,
+                                    s)) != QLORA_OK)
+            return st;
+    }
+    // dA [K, r] = x^T u ; dB [r, N] = t^T dy
+    if ((st = launch_f32_lora(kF32Grad, x, u, (int)M, (int)K, r, 1.0f, dA, part, s)) != QLORA_OK) return st;
+    return launch_f32_lora(kF32GradT, t, dy, (int)M, (int)N, r, 1.0f, dB, part, s);
 }
 
 // ---- QA-LoRA pooled branch: A [K/g, r]; the plain path runs on A~ = expand(A) / g

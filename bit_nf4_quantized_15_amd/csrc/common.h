@@ -1,6 +1,7 @@
 // Internal helpers shared by the HIP kernels of libqlora (gfx950 only).
 #pragma once
 
+#include <algorithm>
 #include <type_traits>
 
 #include <hip/hip_runtime.h>
@@ -76,6 +77,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // "bitsandbytes deep dive" 8.3): bf16 (default) or IEEE fp16.
 constexpr int kDtBf16 = 0;
 constexpr int kDtF16 = 1;
+// IEEE fp32 (deep dive 8.3's third compute dtype): the fp32 kernel family
+// (gemm_f32.hip) and the quantizer only; with_cb_dt covers the 16-bit dtypes.
+constexpr int kDtF32 = 2;
 
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -134,8 +138,9 @@ inline qlora_status launch_status() {
 
 // Launchers (one per translation unit).
 // `cb` selects the codebook (kCbNf4, kCbFp4) of the codes the kernels read or
-// write, `dt` the compute dtype (kDtBf16, kDtF16) of every 16-bit tensor.
-qlora_status launch_quantize(const uint16_t* W, int64_t nblocks, uint8_t* codes, uint8_t* q8, float* a2, int cb,
+// write, `dt` the compute dtype (kDtBf16, kDtF16) of every 16-bit tensor
+// (launch_quantize also takes kDtF32: an fp32 source weight).
+qlora_status launch_quantize(const void* W, int64_t nblocks, uint8_t* codes, uint8_t* q8, float* a2, int cb,
                              int dt, hipStream_t s);
 qlora_status launch_dequantize(const uint8_t* codes, const uint8_t* q8, const float* a2, int cb, int dt,
                                int64_t nblocks, uint16_t* out, hipStream_t s);
@@ -164,5 +169,25 @@ qlora_status launch_tn(const uint16_t* X, const uint16_t* S, float* part, float*
 qlora_status launch_fill(float* out, int64_t count, float v, hipStream_t s);
 qlora_status launch_expand_pooled(const uint16_t* A, int K, int r, int g, int dt, uint16_t* out, hipStream_t s);
 qlora_status launch_pool_rows(const float* in, int K, int r, int g, float* out, hipStream_t s);
+
+// fp32 compute dtype (gemm_f32.hip).  A contraction whose tile grid is small
+// splits its reduction: `splits` partial sums of rows * cols fp32 each go to
+// the caller's `part` buffer (plan_f32 gives the count the launch will use).
+struct F32Plan {
+    int splits, kchunk;
+};
+F32Plan plan_f32(int rows, int cols, int red);
+constexpr int kF32LoraDown = 0;   // out [M, r] = scale * X [M, C] Y [C, r]
+constexpr int kF32LoraDownT = 1;  // out [M, r] = scale * X [M, C] Y^T, Y [r, C]
+constexpr int kF32Grad = 2;       // out [C, r] = scale * X^T Y, X [M, C], Y [M, r]
+constexpr int kF32GradT = 3;      // out [r, C] = scale * X^T Y, X [M, r], Y [M, C]
+qlora_status launch_f32_lora(int which, const float* X, const float* Y, int M, int C, int r, float scale, float* out,
+                             float* part, hipStream_t s);
+qlora_status launch_f32_fwd(const float* x, const uint8_t* codes, const uint8_t* q8, const float* a2, int cb,
+                            const float* t, const float* B, float* y, int M, int N, int K, int r, float* part,
+                            hipStream_t s);
+qlora_status launch_f32_bwd_dx(const float* dy, const uint8_t* codes, const uint8_t* q8, const float* a2, int cb,
+                               const float* u, const float* A, float* dx, int M, int N, int K, int r, float* part,
+                               hipStream_t s);
 
 }  // namespace qlora

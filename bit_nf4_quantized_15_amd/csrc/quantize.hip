@@ -25,6 +25,9 @@
 //   5. nibbles are packed (element 2i high) and stored as one dword per lane.
 // Without double quantization (sections 7.1, 9.5) step 3 stores each block's
 // absmax as its fp32 scale instead of the 8-bit code and the group scale.
+// An fp32 source weight (DT = kDtF32, deep dive 8.3) takes the same steps
+// with 32 B per lane per pass; for any fp32 w and real X, w > X <=>
+// w > RD_f32(X), so its thresholds are those of fp16 weights.
 #include "common.h"
 
 namespace qlora {
@@ -65,8 +68,15 @@ __device__ __forceinline__ uint32_t nf4_code(float w, f32x4_t t0, f32x4_t t1, f3
     return (b3 ? 8u : 0u) | (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
 }
 
+// value i (0..7) of a lane's 8 consecutive weights held as 16-bit pairs or 32-bit words
+template <int DT, int NW>
+__device__ __forceinline__ float elem(const u32x4_t (&v)[NW], int i) {
+    if constexpr (DT == kDtF32) return __uint_as_float(v[i >> 2][i & 3]);
+    else return h16_to_f32<DT>((i & 1) ? (v[0][i >> 1] >> 16) : (v[0][i >> 1] & 0xFFFFu));
+}
+
 template <bool DQ, int CB, int DT>
-__global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint16_t* __restrict__ W,
+__global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const void* __restrict__ Wv,
                                                                 int64_t nblocks,
                                                                 uint8_t* __restrict__ codes,
                                                                 uint8_t* __restrict__ q8,
@@ -83,16 +93,20 @@ __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint16_t* 
     const int nb_here = (int)min((int64_t)kSuper, nblocks - b0);
     const int sub = lane & 7;
 
-    // 1. all loads in flight at once
-    u32x4_t v[kPasses];
+    // 1. all loads in flight at once (8 weights per lane per pass: 16 B, or 32 B for fp32)
+    constexpr int NW = DT == kDtF32 ? 2 : 1;
+    const u32x4_t* W = static_cast<const u32x4_t*>(Wv);
+    u32x4_t v[kPasses][NW];
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
         const int bl = p * 32 + wave * 8 + (lane >> 3);
-        if (bl < nb_here) {
-            const u32x4_t* src = reinterpret_cast<const u32x4_t*>(W + (b0 + bl) * kBlock + sub * 8);
-            v[p] = __builtin_nontemporal_load(src);
-        } else {
-            v[p] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int h = 0; h < NW; ++h) {
+            if (bl < nb_here) {
+                v[p][h] = __builtin_nontemporal_load(W + ((b0 + bl) * kBlock + sub * 8) / (8 / NW) + h);
+            } else {
+                v[p][h] = u32x4_t{0u, 0u, 0u, 0u};
+            }
         }
     }
 
@@ -111,12 +125,21 @@ __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint16_t* 
     // 2. block absmax
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
-        uint32_t m = absmax_bits8(v[p]);
+        uint32_t m = 0;
+        if constexpr (DT == kDtF32) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m = max(m, v[p][i >> 2][i & 3] & 0x7FFFFFFFu);  // |w| orders as its bits
+        } else {
+            m = absmax_bits8(v[p][0]);
+        }
         m = max(m, (uint32_t)__shfl_xor((int)m, 1));
         m = max(m, (uint32_t)__shfl_xor((int)m, 2));
         m = max(m, (uint32_t)__shfl_xor((int)m, 4));
         const int bl = p * 32 + wave * 8 + (lane >> 3);
-        if (sub == 0) s_amax[bl] = h16_to_f32<DT>(m);   // 0 for blocks past the end
+        if (sub == 0) {                                  // 0 for blocks past the end
+            if constexpr (DT == kDtF32) s_amax[bl] = __uint_as_float(m);
+            else s_amax[bl] = h16_to_f32<DT>(m);
+        }
     }
     __syncthreads();
 
@@ -182,8 +205,7 @@ __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint16_t* 
             uint32_t packed = 0;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const uint32_t bits = (i & 1) ? (v[p][i >> 1] >> 16) : (v[p][i >> 1] & 0xFFFFu);
-                const float w = h16_to_f32<DT>(bits);
+                const float w = elem<DT, NW>(v[p], i);
                 const int bucket = (int)__builtin_fmaf(w, sc, 64.0f);  // 0 .. 128 (trunc; -2^-16 -> 0)
                 const uint32_t c = s_lut[bucket];
                 const uint32_t q = code_of_sorted<CB>(c + (w > tb[c] ? 1u : 0u));
@@ -196,8 +218,7 @@ __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint16_t* 
                 packed = 0;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const uint32_t bits = (i & 1) ? (v[p][i >> 1] >> 16) : (v[p][i >> 1] & 0xFFFFu);
-                    const uint32_t q = code_of_sorted<CB>(nf4_code(h16_to_f32<DT>(bits), t0, t1, t2, t3));
+                    const uint32_t q = code_of_sorted<CB>(nf4_code(elem<DT, NW>(v[p], i), t0, t1, t2, t3));
                     packed |= q << (4 * (i ^ 1));
                 }
             }
@@ -247,10 +268,10 @@ __global__ __launch_bounds__(kThreads) void nf4_dequantize_kernel(const uint8_t*
 
 }  // namespace
 
-qlora_status launch_quantize(const uint16_t* W, int64_t nblocks, uint8_t* codes, uint8_t* q8, float* a2, int cb,
+qlora_status launch_quantize(const void* W, int64_t nblocks, uint8_t* codes, uint8_t* q8, float* a2, int cb,
                              int dt, hipStream_t s) {
     const int64_t groups = (nblocks + kSuper - 1) / kSuper;
-    with_cb_dt(cb, dt, [&](auto cbc, auto dtc) {
+    auto go = [&](auto cbc, auto dtc) {
         constexpr int CB = decltype(cbc)::value, DT = decltype(dtc)::value;
         if (q8)
             hipLaunchKernelGGL((nf4_quantize_kernel<true, CB, DT>), dim3((unsigned)groups), dim3(kThreads), 0, s, W,
@@ -258,7 +279,13 @@ qlora_status launch_quantize(const uint16_t* W, int64_t nblocks, uint8_t* codes,
         else
             hipLaunchKernelGGL((nf4_quantize_kernel<false, CB, DT>), dim3((unsigned)groups), dim3(kThreads), 0, s, W,
                                nblocks, codes, q8, a2);
-    });
+    };
+    if (dt == kDtF32) {
+        if (cb == kCbFp4) go(IntC<kCbFp4>{}, IntC<kDtF32>{});
+        else go(IntC<kCbNf4>{}, IntC<kDtF32>{});
+    } else {
+        with_cb_dt(cb, dt, go);
+    }
     return launch_status();
 }
 

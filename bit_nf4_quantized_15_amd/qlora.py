@@ -29,12 +29,12 @@ class NF4State(ctypes.Structure):
 
 
 QUANT_TYPES = {"nf4": 0, "fp4": 1}                        # qlora_quant_type: the 4-bit codebook
-DTYPES = {torch.bfloat16: 0, torch.float16: 1}            # qlora_dtype: the 16-bit compute dtype
+DTYPES = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2}   # qlora_dtype: the compute dtype
 
 
 def _dtype_code(dtype):
     if dtype not in DTYPES:
-        raise TypeError(f"compute dtype must be torch.bfloat16 or torch.float16, got {dtype}")
+        raise TypeError(f"compute dtype must be torch.bfloat16, torch.float16 or torch.float32, got {dtype}")
     return DTYPES[dtype]
 
 
@@ -70,6 +70,13 @@ def _load():
         "qlora_bwd_workspace": (c_sz, [c_i64, c_i64, c_i64, ctypes.c_int]),
         "qlora_linear_bwd": (ctypes.c_int, [P, c_vp, c_i64, c_vp, c_vp, ctypes.c_int, ctypes.c_float,
                                             c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+        "qlora_quantize_f32": (ctypes.c_int, [c_vp, c_i64, c_i64, P, c_vp]),
+        "qlora_fwd_workspace_f32": (c_sz, [c_i64, c_i64, c_i64, ctypes.c_int]),
+        "qlora_linear_fwd_f32": (ctypes.c_int, [P, c_vp, c_i64, c_vp, c_vp, ctypes.c_int, ctypes.c_float,
+                                                c_vp, c_vp, c_vp, c_sz, c_vp]),
+        "qlora_bwd_workspace_f32": (c_sz, [c_i64, c_i64, c_i64, ctypes.c_int]),
+        "qlora_linear_bwd_f32": (ctypes.c_int, [P, c_vp, c_i64, c_vp, c_vp, ctypes.c_int, ctypes.c_float,
+                                                c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name, None)
@@ -130,8 +137,9 @@ def sizes_nodq(N, K):
 class NF4Weight:
     """Device-resident quantized weight: codes (uint8), q8 (uint8) and a2 (float32) tensors; without
     double quantization q8 is None and a2 holds one fp32 absmax per 64-block.  quant_type names the
-    4-bit codebook ("nf4" or "fp4"); dtype is the compute dtype of every 16-bit tensor used with it
-    (torch.bfloat16 or torch.float16)."""
+    4-bit codebook ("nf4" or "fp4"); dtype is the compute dtype of every float tensor used with it
+    (torch.bfloat16, torch.float16, or torch.float32: then the layer calls take the _f32 entry points and the
+    dequantized weight is the fp32 product itself)."""
 
     def __init__(self, codes, q8, a2, N, K, quant_type="nf4", dtype=torch.bfloat16):
         if quant_type not in QUANT_TYPES:
@@ -162,9 +170,10 @@ class NF4Weight:
 
 
 def quantize(W, out=None, double_quant=True, quant_type="nf4"):
-    """4-bit blockwise quantization of a bf16 or fp16 [N, K] device weight (qlora_quantize) with the NF4 or
-    the FP4 codebook, with or without double quantization of the block scales (both ignored when `out` is
-    given: its layout and quant_type decide).  W's dtype becomes the weight's compute dtype."""
+    """4-bit blockwise quantization of a bf16, fp16 or fp32 [N, K] device weight (qlora_quantize, or
+    qlora_quantize_f32 for fp32) with the NF4 or the FP4 codebook, with or without double quantization of
+    the block scales (both ignored when `out` is given: its layout and quant_type decide).  W's dtype
+    becomes the weight's compute dtype."""
     N, K = W.shape
     _dtype_code(W.dtype)
     _dev(W, W.dtype, "W")
@@ -172,13 +181,18 @@ def quantize(W, out=None, double_quant=True, quant_type="nf4"):
     if w.dtype != W.dtype:
         raise TypeError(f"out has compute dtype {w.dtype}, W is {W.dtype}")
     st = w.state()
-    _check(lib.qlora_quantize(_ptr(W), N, K, ctypes.byref(st), _stream()), "qlora_quantize")
+    if W.dtype == torch.float32:
+        _check(lib.qlora_quantize_f32(_ptr(W), N, K, ctypes.byref(st), _stream()), "qlora_quantize_f32")
+    else:
+        _check(lib.qlora_quantize(_ptr(W), N, K, ctypes.byref(st), _stream()), "qlora_quantize")
     return w
 
 
 def dequantize(w, out=None, fp32=False):
     """[N, K] reconstruction in the weight's compute dtype (qlora_dequantize), or with fp32=True the fp32
-    products themselves (qlora_dequantize_f32); tests and export only."""
+    products themselves (qlora_dequantize_f32, also the reconstruction of an fp32 weight); tests and export
+    only."""
+    fp32 = fp32 or w.dtype == torch.float32
     dt = torch.float32 if fp32 else w.dtype
     o = torch.empty((w.N, w.K), dtype=dt, device=w.codes.device) if out is None else out
     _dev(o, dt, "out", (w.N, w.K))
@@ -203,11 +217,15 @@ def merge(w, A, B, alpha, out=None):
     return o
 
 
-def fwd_workspace(M, N, K, r):
+def fwd_workspace(M, N, K, r, dtype=torch.bfloat16):
+    if dtype == torch.float32:
+        return int(lib.qlora_fwd_workspace_f32(M, N, K, r))
     return int(lib.qlora_fwd_workspace(M, N, K, r))
 
 
-def bwd_workspace(M, N, K, r):
+def bwd_workspace(M, N, K, r, dtype=torch.bfloat16):
+    if dtype == torch.float32:
+        return int(lib.qlora_bwd_workspace_f32(M, N, K, r))
     return int(lib.qlora_bwd_workspace(M, N, K, r))
 
 
@@ -232,10 +250,12 @@ def linear_fwd(w, x, A, B, alpha, y=None, t=None, want_t=True, ws=None):
         t = torch.empty((M, r), dtype=w.dtype, device=dev)
     if t is not None:
         _dev(t, w.dtype, "t", (M, r))
-    wsb, wsn = _ws(fwd_workspace(M, w.N, w.K, r), dev, ws)
+    wsb, wsn = _ws(fwd_workspace(M, w.N, w.K, r, w.dtype), dev, ws)
     st = w.state()
-    _check(lib.qlora_linear_fwd(ctypes.byref(st), _ptr(x), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(y),
-                                _ptr(t), _ptr(wsb), wsn, _stream()), "qlora_linear_fwd")
+    fn, name = ((lib.qlora_linear_fwd_f32, "qlora_linear_fwd_f32") if w.dtype == torch.float32
+                else (lib.qlora_linear_fwd, "qlora_linear_fwd"))
+    _check(fn(ctypes.byref(st), _ptr(x), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(y), _ptr(t), _ptr(wsb), wsn,
+              _stream()), name)
     return y, t
 
 
@@ -297,11 +317,12 @@ def linear_bwd(w, x, A, B, alpha, dy, t=None, need_dx=True, dx=None, dA=None, dB
         dx = torch.empty((M, w.K), dtype=w.dtype, device=dev) if dx is None else _dev(dx, w.dtype, "dx", (M, w.K))
     dA = torch.empty((w.K, r), dtype=torch.float32, device=dev) if dA is None else _dev(dA, torch.float32, "dA", (w.K, r))
     dB = torch.empty((r, w.N), dtype=torch.float32, device=dev) if dB is None else _dev(dB, torch.float32, "dB", (r, w.N))
-    wsb, wsn = _ws(bwd_workspace(M, w.N, w.K, r), dev, ws)
+    wsb, wsn = _ws(bwd_workspace(M, w.N, w.K, r, w.dtype), dev, ws)
     st = w.state()
-    _check(lib.qlora_linear_bwd(ctypes.byref(st), _ptr(x), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(t),
-                                _ptr(dy), _ptr(dx) if need_dx else None, _ptr(dA), _ptr(dB), _ptr(wsb), wsn,
-                                _stream()), "qlora_linear_bwd")
+    fn, name = ((lib.qlora_linear_bwd_f32, "qlora_linear_bwd_f32") if w.dtype == torch.float32
+                else (lib.qlora_linear_bwd, "qlora_linear_bwd"))
+    _check(fn(ctypes.byref(st), _ptr(x), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(t), _ptr(dy),
+              _ptr(dx) if need_dx else None, _ptr(dA), _ptr(dB), _ptr(wsb), wsn, _stream()), name)
     return (dx if need_dx else None), dA, dB
 
 

@@ -81,9 +81,13 @@ typedef enum qlora_quant_type { QLORA_QUANT_NF4 = 0, QLORA_QUANT_FP4 = 1 } qlora
  * default, zero-initialised) or IEEE binary16.  Dequantized weights are
  * RNE_16(fl32(a_hat * c_q)) in that format and the products run on the MFMA
  * instruction of that type with fp32 accumulation; dA and dB stay fp32.
- * Where the text below says bf16, read "the compute dtype".  fp32 compute is
- * not provided (the matrix cores' fp32 rate is 1/16 of the 16-bit rate). */
-typedef enum qlora_dtype { QLORA_DTYPE_BF16 = 0, QLORA_DTYPE_F16 = 1 } qlora_dtype;
+ * Where the text below says bf16, read "the compute dtype".
+ * QLORA_DTYPE_F32: every floating-point tensor of the layer is IEEE binary32
+ * and the dequantized weight is the fp32 product fl32(a_hat * c_q) itself,
+ * with no 16-bit rounding.  Such a state is used through the _f32 entry points
+ * below (float tensors), which take no other dtype; the 16-bit entry points
+ * reject it with INVALID_ARG.  qlora_dequantize_f32 takes every dtype. */
+typedef enum qlora_dtype { QLORA_DTYPE_BF16 = 0, QLORA_DTYPE_F16 = 1, QLORA_DTYPE_F32 = 2 } qlora_dtype;
 
 typedef struct qlora_nf4 {
     uint8_t* codes;     /* [N*K/2]            packed 4-bit codes                         */
@@ -95,7 +99,7 @@ typedef struct qlora_nf4 {
     int32_t quant_type; /* a qlora_quant_type; 0 (zero-initialised) is NF4. Any other   */
                         /* value -> QLORA_ERR_INVALID_ARG                                */
     int32_t dtype;      /* a qlora_dtype; 0 (zero-initialised) is bf16. Any other value  */
-                        /* -> QLORA_ERR_INVALID_ARG                                      */
+                        /* -> QLORA_ERR_INVALID_ARG; fp32 only through the _f32 calls    */
 } qlora_nf4;
 
 /* Library version (major*10000 + minor*100 + patch). */
@@ -213,6 +217,32 @@ qlora_status qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, int64_t M, 
  * Arguments and errors as qlora_linear_bwd; M = 0 is a no-op. */
 qlora_status qlora_fused_gemm_bwd_dx(const qlora_nf4* w, const uint16_t* dy, int64_t M, const uint16_t* u,
                                      const uint16_t* A, int r, uint16_t* dx, void* stream);
+
+/* fp32 compute dtype (deep dive 8.3 lists fp32 beside bf16 and fp16).  The
+ * state's dtype must be QLORA_DTYPE_F32 (else INVALID_ARG); every tensor is
+ * float, 16-byte aligned.  Definitions, arguments and errors are those of the
+ * 16-bit calls with bf16 read as fp32:
+ *   qlora_quantize_f32:   codes against the true absmax of fp32 W [N, K]; for
+ *                         fp32 weights w > X <=> w > RD_f32(X), so the exact
+ *                         thresholds are fp32 values.  Scales as qlora_quantize.
+ *   qlora_linear_fwd_f32: t = s x A, y = x W_hat + t B, with W_hat =
+ *                         fl32(a_hat * c_q); products on the fp32 matrix cores
+ *                         with fp32 accumulation.
+ *   qlora_linear_bwd_f32: u = s dy B^T, dx = dy W_hat^T + u A^T, dA = x^T u,
+ *                         dB = t^T dy, all fp32.
+ * Contractions with few output tiles split their reduction into fp32 partial
+ * sums in the workspace, added in a fixed order: results are deterministic.
+ * The decode GEMV, the merge, the pooled branch and the stage entry points are
+ * offered for the 16-bit dtypes only. */
+qlora_status qlora_quantize_f32(const float* W, int64_t N, int64_t K, const qlora_nf4* out, void* stream);
+size_t qlora_fwd_workspace_f32(int64_t M, int64_t N, int64_t K, int r);
+qlora_status qlora_linear_fwd_f32(const qlora_nf4* w, const float* x, int64_t M, const float* A, const float* B,
+                                  int r, float alpha, float* y, float* t_out, void* ws, size_t ws_bytes,
+                                  void* stream);
+size_t qlora_bwd_workspace_f32(int64_t M, int64_t N, int64_t K, int r);
+qlora_status qlora_linear_bwd_f32(const qlora_nf4* w, const float* x, int64_t M, const float* A, const float* B,
+                                  int r, float alpha, const float* t, const float* dy, float* dx, float* dA,
+                                  float* dB, void* ws, size_t ws_bytes, void* stream);
 
 /* QA-LoRA pooled branch ("LoRA, QLoRA, QA-LoRA explained", sections 3-5): the
  * LoRA input is pool(x), the mean of each group of g consecutive input

@@ -29,3 +29,14 @@ def dev_f16(u16):
     """uint16 fp16 bits (numpy) -> contiguous torch.float16 tensor on cuda:0."""
     a = np.ascontiguousarray(u16, dtype=np.uint16)
     return torch.from_numpy(a.view(np.int16)).view(torch.float16).to("cuda:0")
+
+
+def dev_f32(u32):
+    """uint32 fp32 bits (numpy) -> contiguous torch.float32 tensor on cuda:0."""
+    a = np.ascontiguousarray(u32, dtype=np.uint32)
+    return torch.from_numpy(a.view(np.float32)).to("cuda:0")
+
+
+def host_bits32(t):
+    """torch.float32 tensor -> uint32 numpy bits."""
+    return t.detach().cpu().numpy().view(np.uint32)

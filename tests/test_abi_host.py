@@ -92,11 +92,12 @@ def test_quantize_argument_errors(q):
     bad_qt.quant_type = 2
     assert f(FAKE, 64, 64, ctypes.byref(bad_qt), None) == INVALID
     assert q.lib.qlora_dequantize(ctypes.byref(bad_qt), FAKE, None) == INVALID
-    # dtype: 0 (bf16) and 1 (fp16) only
+    # dtype: 0 (bf16) and 1 (fp16) on the 16-bit calls; 2 (fp32) only through the _f32 calls; 3 is unknown
     bad_dt = _state(q)
-    bad_dt.dtype = 2
+    bad_dt.dtype = 3
     assert f(FAKE, 64, 64, ctypes.byref(bad_dt), None) == INVALID
     assert q.lib.qlora_dequantize(ctypes.byref(bad_dt), FAKE, None) == INVALID
+    assert q.lib.qlora_dequantize_f32(ctypes.byref(bad_dt), FAKE, None) == INVALID
     assert q.lib.qlora_dequantize(ctypes.byref(st), None, None) == INVALID
     assert q.lib.qlora_dequantize_f32(ctypes.byref(st), None, None) == INVALID
     assert q.lib.qlora_dequantize_f32(ctypes.byref(st), FAKE + 4, None) == MISALIGNED
@@ -175,6 +176,66 @@ def test_linear_argument_errors(q):
     assert bwd(st, FAKE, 8, FAKE, FAKE, 8, 16.0, None, FAKE, None, FAKE, FAKE, FAKE, wsb - 256, None) == WORKSPACE
     bad_k = ctypes.byref(_state(q, n=64, k=96))
     assert bwd(bad_k, FAKE, 8, FAKE, FAKE, 8, 16.0, None, FAKE, None, FAKE, FAKE, FAKE, wsb, None) == SHAPE
+
+
+def test_f32_argument_errors(q):
+    """fp32 states go through the _f32 calls only, and those take nothing else."""
+    s16 = ctypes.byref(_state(q, n=64, k=128))
+    st32 = _state(q, n=64, k=128)
+    st32.dtype = 2
+    s32 = ctypes.byref(st32)
+    lib = q.lib
+    # the 16-bit calls reject an fp32 state
+    assert lib.qlora_quantize(FAKE, 64, 128, s32, None) == INVALID
+    assert lib.qlora_dequantize(s32, FAKE, None) == INVALID
+    assert lib.qlora_merge(s32, FAKE, FAKE, 8, 16.0, FAKE, None) == INVALID
+    ws16 = q.fwd_workspace(8, 64, 128, 8)
+    assert lib.qlora_linear_fwd(s32, FAKE, 8, FAKE, FAKE, 8, 16.0, FAKE, None, FAKE, ws16, None) == INVALID
+    assert lib.qlora_fused_gemm_fwd(s32, FAKE, 8, FAKE, FAKE, 8, FAKE, None) == INVALID
+    assert lib.qlora_fused_gemm_bwd_dx(s32, FAKE, 8, FAKE, FAKE, 8, FAKE, None) == INVALID
+    # qlora_dequantize_f32 takes every dtype (argument errors still apply)
+    assert lib.qlora_dequantize_f32(s32, FAKE + 4, None) == MISALIGNED
+    # the _f32 calls reject a 16-bit state
+    ws_f = q.fwd_workspace(8, 64, 128, 8, torch_f32())
+    ws_b = q.bwd_workspace(8, 64, 128, 8, torch_f32())
+    assert ws_f > 0 and ws_b > 0
+    assert lib.qlora_quantize_f32(FAKE, 64, 128, s16, None) == INVALID
+    assert lib.qlora_linear_fwd_f32(s16, FAKE, 8, FAKE, FAKE, 8, 16.0, FAKE, None, FAKE, ws_f, None) == INVALID
+    assert lib.qlora_linear_bwd_f32(s16, FAKE, 8, FAKE, FAKE, 8, 16.0, None, FAKE, None, FAKE, FAKE, FAKE, ws_b,
+                                    None) == INVALID
+    # argument errors of the _f32 calls, checked before any launch
+    qf = lib.qlora_quantize_f32
+    assert qf(None, 64, 128, s32, None) == INVALID
+    assert qf(FAKE, 32, 128, s32, None) == INVALID                                # shape mismatch
+    assert qf(FAKE + 4, 64, 128, s32, None) == MISALIGNED
+    fwd = lib.qlora_linear_fwd_f32
+    # (w, x, M, A, B, r, alpha, y, t_out, ws, ws_bytes, stream)
+    assert fwd(s32, FAKE, 8, FAKE, FAKE, 0, 16.0, FAKE, None, FAKE, ws_f, None) == INVALID        # r = 0
+    assert fwd(s32, FAKE, 8, FAKE, FAKE, 129, 16.0, FAKE, None, FAKE, 1 << 30, None) == INVALID   # r > 128
+    assert fwd(s32, FAKE, 8, FAKE, FAKE, 8, float("inf"), FAKE, None, FAKE, ws_f, None) == INVALID
+    assert fwd(s32, None, 8, FAKE, FAKE, 8, 16.0, FAKE, None, FAKE, ws_f, None) == INVALID
+    assert fwd(s32, FAKE, 8, FAKE, FAKE, 8, 16.0, FAKE + 4, None, FAKE, ws_f, None) == MISALIGNED
+    assert fwd(s32, FAKE, 8, FAKE, FAKE, 8, 16.0, FAKE, None, None, ws_f, None) == WORKSPACE
+    assert fwd(s32, FAKE, 8, FAKE, FAKE, 8, 16.0, FAKE, None, FAKE, ws_f - 1, None) == WORKSPACE
+    assert fwd(s32, FAKE, 0, None, None, 8, 16.0, None, None, None, 0, None) == OK                # M = 0
+    bwd = lib.qlora_linear_bwd_f32
+    # (w, x, M, A, B, r, alpha, t, dy, dx, dA, dB, ws, ws_bytes, stream)
+    assert bwd(s32, FAKE, 8, FAKE, FAKE, 8, 16.0, None, FAKE, None, None, FAKE, FAKE, ws_b, None) == INVALID
+    assert bwd(s32, FAKE, 8, FAKE, FAKE, 8, 16.0, None, None, None, FAKE, FAKE, FAKE, ws_b, None) == INVALID
+    assert bwd(s32, FAKE, 8, FAKE, FAKE, 8, 16.0, None, FAKE, FAKE + 4, FAKE, FAKE, FAKE, ws_b, None) == MISALIGNED
+    assert bwd(s32, FAKE, 8, FAKE, FAKE, 8, 16.0, None, FAKE, None, FAKE, FAKE, FAKE, ws_b - 256, None) == WORKSPACE
+    bad_k = _state(q, n=64, k=96)
+    bad_k.dtype = 2
+    assert bwd(ctypes.byref(bad_k), FAKE, 8, FAKE, FAKE, 8, 16.0, None, FAKE, None, FAKE, FAKE, FAKE, ws_b,
+               None) == SHAPE
+    # workspace queries: 0 for invalid sizes and for M = 0
+    assert lib.qlora_fwd_workspace_f32(8, 64, 100, 8) == 0
+    assert lib.qlora_bwd_workspace_f32(0, 64, 128, 8) == 0
+
+
+def torch_f32():
+    import torch
+    return torch.float32
 
 
 def test_fp64_scale_step_equals_f32_division_for_all_bf16():
