@@ -35,6 +35,7 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA
+MFMA_F32_PEAK_TFS = 157.3      # MI355X dense fp32 MFMA
 FP32_VECTOR_PEAK_TFS = 157.3   # MI355X fp32 vector (non-matrix) peak
 METRIC = "fused NF4-dequant+LoRA linear TFLOP/s (M=4096) and decode GEMV HBM GB/s, 1 MI355X"
 
@@ -426,6 +427,7 @@ def extras(torch, qlora, workloads, dev, to_dev, L, M, r):
     res["fp4"] = extras_variant(torch, qlora, workloads, dev, to_dev, L, M, r, ev, quant_type="fp4")
     res["fp16_compute"] = extras_variant(torch, qlora, workloads, dev, to_dev, L, M, r, ev, dtype=torch.float16)
     res["qa_lora_pooled_g64"] = extras_pooled(torch, qlora, workloads, dev, to_dev, L, M, r, ev, 64)
+    res["fp32_compute"] = extras_fp32(torch, qlora, workloads, dev, L, M, r, ev)
 
     # LoRA merge for deployment (qlora_merge) of the 7 layers: N*K*r fp32 FMAs (VALU-bound) and
     # codes + scales + A + B in, the bf16 merged weight out
@@ -462,6 +464,56 @@ def extras(torch, qlora, workloads, dev, to_dev, L, M, r):
         tot_f += 2 * M * d["N"] * d["K"]
     res["context_dense_bf16_matmul_fwd_tflops"] = round(tot_f / (tot_ms * 1e-3) / 1e12, 1)
     return res
+
+
+def extras_fp32(torch, qlora, workloads, dev, L, M, r, ev):
+    """The fp32 compute dtype (deep dive 8.3) on the same 7 linears: every tensor fp32 (the bf16 draws
+    widened exactly), w_hat = fl32(a_hat * c_q), products on the fp32 matrix cores.  The whole quantize +
+    fwd + bwd step and the forward call, against the 157.3 TFLOP/s dense fp32 MFMA peak."""
+    alpha = workloads.CONFIGS[4]["alpha"]
+    f = torch.float32
+    Lf = [dict(N=d["N"], K=d["K"], flops=d["flops"], W=d["W"].to(f), x=d["x"].to(f), A=d["A"].to(f),
+               B=d["B"].to(f), dy=d["dy"].to(f), t=torch.empty((M, r), dtype=f, device=dev),
+               y=torch.empty((M, d["N"]), dtype=f, device=dev), dx=torch.empty((M, d["K"]), dtype=f, device=dev),
+               dA=d["dA"], dB=d["dB"]) for d in L]
+    Wn = [qlora.NF4Weight.empty(d["N"], d["K"], dev, dtype=f) for d in Lf]
+    ws = torch.empty(max(max(qlora.bwd_workspace(M, d["N"], d["K"], r, f), qlora.fwd_workspace(M, d["N"], d["K"], r, f))
+                         for d in Lf), dtype=torch.uint8, device=dev)
+    total_flops = sum(d["flops"]["fwd"] + d["flops"]["bwd"] for d in Lf)
+    fwd_flops = sum(d["flops"]["fwd"] for d in Lf)
+
+    def fwd():
+        for d, w in zip(Lf, Wn):
+            qlora.linear_fwd(w, d["x"], d["A"], d["B"], alpha, y=d["y"], t=d["t"], ws=ws)
+
+    def step():
+        for d, w in zip(Lf, Wn):
+            qlora.quantize(d["W"], out=w)
+        fwd()
+        for d, w in zip(Lf, Wn):
+            qlora.linear_bwd(w, d["x"], d["A"], d["B"], alpha, d["dy"], t=d["t"], dx=d["dx"], dA=d["dA"],
+                             dB=d["dB"], ws=ws)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    step_ms = timed(step, 3)
+    fwd_ms = timed(fwd, 3)
+    step_tfs = total_flops / (step_ms * 1e-3) / 1e12
+    fwd_tfs = fwd_flops / (fwd_ms * 1e-3) / 1e12
+    del Lf, Wn, ws
+    return {"step": {"ms": round(step_ms, 3), "TFLOP/s": round(step_tfs, 2),
+                     "frac_of_fp32_mfma_peak": round(step_tfs / MFMA_F32_PEAK_TFS, 4)},
+            "fwd_call": {"ms_7_layers": round(fwd_ms, 3), "TFLOP/s": round(fwd_tfs, 2),
+                         "frac_of_fp32_mfma_peak": round(fwd_tfs / MFMA_F32_PEAK_TFS, 4)}}
 
 
 def extras_variant(torch, qlora, workloads, dev, to_dev, L, M, r, ev, double_quant=True, quant_type="nf4",
