@@ -422,6 +422,7 @@ def extras(torch, qlora, workloads, dev, to_dev, L, M, r):
                           "GB/s_fwd_call": round(nb / (call_ms * 1e-3) / 1e9, 1)}
     res["decode_gemv_q_proj_4096x4096_r16"] = dec
     del copies
+    res["decode_gemv_fused_weights"] = extras_fused_decode(torch, qlora, workloads, dev, to_dev)
 
     res["double_quant_off"] = extras_variant(torch, qlora, workloads, dev, to_dev, L, M, r, ev, double_quant=False)
     res["fp4"] = extras_variant(torch, qlora, workloads, dev, to_dev, L, M, r, ev, quant_type="fp4")
@@ -464,6 +465,43 @@ def extras(torch, qlora, workloads, dev, to_dev, L, M, r):
         tot_f += 2 * M * d["N"] * d["K"]
     res["context_dense_bf16_matmul_fwd_tflops"] = round(tot_f / (tot_ms * 1e-3) / 1e12, 1)
     return res
+
+
+def extras_fused_decode(torch, qlora, workloads, dev, to_dev):
+    """Decode GEMV on fused weights.  q/k/v (and gate/up) read the same x, so their weights concatenated
+    along N are one NF4 weight (K = 4096: a row holds 64 blocks and a scale group 4 rows, so no group spans
+    two layers and the codes and scales equal those of the separate weights).  Each layer keeps its own
+    r = 16 LoRA pair: A concatenated along r, B block-diagonal (its zero blocks add exact zeros).  One GEMV
+    launch then streams 3x (2.7x) the bytes of q_proj alone.  Weight copies rotated past the 256 MB
+    Infinity Cache, launches replayed from a HIP graph, as for q_proj."""
+    out = {}
+    K, r1 = 4096, 16
+    for name, Ns, seed in (("qkv_3x4096x4096", [4096, 4096, 4096], 9100), ("gate_up_2x11008x4096", [11008, 11008], 9200)):
+        N, r = sum(Ns), r1 * len(Ns)
+        W = np.concatenate([workloads.custom(seed + i, (n, K), 0.02) for i, n in enumerate(Ns)], axis=0)
+        w0 = qlora.quantize(to_dev(W))
+        del W
+        ncopy = max(4, -(-600_000_000 // (N * K // 2)))
+        copies = [qlora.NF4Weight(w0.codes.clone(), w0.q8.clone(), w0.a2.clone(), N, K) for _ in range(ncopy)]
+        A = to_dev(np.concatenate([workloads.custom(seed + 10 + i, (K, r1), 0.25) for i in range(len(Ns))], axis=1))
+        Bbd = torch.zeros((r, N), dtype=torch.bfloat16, device=dev)
+        n0 = 0
+        for i, n in enumerate(Ns):
+            Bbd[r1 * i:r1 * (i + 1), n0:n0 + n] = to_dev(workloads.custom(seed + 20 + i, (r1, n), 0.01))
+            n0 += n
+        res = {}
+        for Md in (1, 16):
+            xd = to_dev(workloads.custom(seed + 30 + Md, (Md, K), 1.0))
+            td = qlora.lora_down(xd, A, 32.0)
+            yd = torch.empty((Md, N), dtype=torch.bfloat16, device=dev)
+            ms = graph_ms([lambda w=w: qlora.fused_gemm_fwd(w, xd, td, Bbd, y=yd) for w in copies])
+            nb = gemv_bytes(Md, N, K, r) - 2 * K * r
+            res[f"M={Md}"] = {"gemv_kernel_us": round(ms * 1e3, 2), "bytes_gemv_kernel": nb,
+                              "GB/s_gemv_kernel": round(nb / (ms * 1e-3) / 1e9, 1),
+                              "frac_of_hbm_peak_gemv_kernel": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        out[name] = res
+        del copies, w0
+    return out
 
 
 def extras_fp32(torch, qlora, workloads, dev, L, M, r, ev):

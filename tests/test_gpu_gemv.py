@@ -67,3 +67,42 @@ def test_gemv_fused_entry_matches_linear(q):
     y2 = q.fused_gemm_fwd(w, x, t, B)
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_fused_qkv_weight_equals_separate_layers(q, M):
+    """q/k/v concatenated along N as one weight (how the bench measures fused decode weights): with
+    K = 1024 a scale group is 16 rows, so the fused codes and scales are the separate ones concatenated,
+    bit for bit; each layer's LoRA pair sits in A concatenated along r and a block-diagonal B, with
+    alpha scaled by the layer count so that alpha / r is unchanged.  y of the fused launch matches the
+    oracle of the separate layers."""
+    import torch
+    Ns, K, r1, alpha = [256, 128, 128], 1024, 8, 16.0
+    Ws = [workloads.custom(8100 + i, (n, K), 0.02) for i, n in enumerate(Ns)]
+    As = [workloads.custom(8110 + i, (K, r1), 0.3) for i in range(3)]
+    Bs = [workloads.custom(8120 + i, (r1, n), 0.01) for i, n in enumerate(Ns)]
+    x = workloads.custom(8130 + M, (M, K), 1.0)
+    N, r = sum(Ns), 3 * r1
+    say(f"[gemv] fused q/k/v N={N} K={K} r={r} M={M}")
+    w = q.quantize(dev_bf16(np.concatenate(Ws, axis=0)))
+    sep = [q.quantize(dev_bf16(Wi)) for Wi in Ws]
+    Bbd = torch.zeros((r, N), dtype=torch.bfloat16, device="cuda:0")
+    n0 = 0
+    for i, n in enumerate(Ns):
+        Bbd[r1 * i:r1 * (i + 1), n0:n0 + n] = dev_bf16(Bs[i])
+        n0 += n
+    y, _ = q.linear_fwd(w, dev_bf16(x), dev_bf16(np.concatenate(As, axis=1)), Bbd, 3 * alpha)
+    torch.cuda.synchronize()
+    for name in ("codes", "q8", "a2"):
+        got = getattr(w, name).cpu().numpy()
+        want = np.concatenate([getattr(s, name).cpu().numpy() for s in sep])
+        assert np.array_equal(got, want), name
+    ref = []
+    for Wi, Ai, Bi in zip(Ws, As, Bs):
+        p, q8, a2 = nf4.quantize(Wi)
+        Wh = bf16.to_f64(nf4.dequantize(p, q8, a2, Wi.shape[0], K))
+        ref.append(lora.linear_fwd(bf16.to_f64(x), Wh, bf16.to_f64(Ai), bf16.to_f64(Bi), alpha, r1)[0])
+    ref = np.concatenate(ref, axis=1)
+    e = lora.rel_err(host_f64(y), ref)
+    say(f"    rel err {e:.3e}")
+    assert e <= TOL
