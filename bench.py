@@ -131,7 +131,7 @@ def pmc_summary(fetch_csv, write_csv, kind):
     f_scale, w_scale = CALIB_BYTES / (f_cal * 1024), CALIB_BYTES / (w_cal * 1024)
     fetch_b, write_b = f_kib * 1024 * f_scale, w_kib * 1024 * w_scale
     from bit_nf4_quantized_15_amd import workloads
-    cfg = workloads.CONFIGS[4]
+    cfg = workloads.CONFIGS[workloads.BLOCK_7B]
     algo = algorithmic_bytes(kind, cfg["layers"], cfg["M"], cfg["r"])
     print(f"source_sha256: {gemm_source_sha()}")
     print(f"kernel: {kname}")
@@ -193,7 +193,8 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path has no collectives; see the sharding note in DESIGN.md)", file=sys.stderr)
+              "(the path runs on one GPU and has no collectives: each GPU of a data-parallel job would run it on "
+              "its own share of the tokens)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -205,18 +206,18 @@ def main():
     def to_dev(u16):
         return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    # ---------------------------------------------------------------- workload (c4)
-    cfg_id = 4
-    cfg = workloads.CONFIGS[cfg_id]
+    # ---------------------------------------------------------------- workload: the 7B-like block
+    wl = workloads.BLOCK_7B
+    cfg = workloads.CONFIGS[wl]
     M, r, alpha = cfg["M"], cfg["r"], cfg["alpha"]
     L = []
     for li, (name, N, K) in enumerate(cfg["layers"]):
         d = dict(name=name, N=N, K=K)
-        d["W"] = to_dev(workloads.weight(cfg_id, li))
-        d["x"] = to_dev(workloads.activations(cfg_id, li))
-        d["A"] = to_dev(workloads.lora_A(cfg_id, li))
-        d["B"] = to_dev(workloads.lora_B(cfg_id, li))
-        d["dy"] = to_dev(workloads.grad_output(cfg_id, li))
+        d["W"] = to_dev(workloads.weight(wl, li))
+        d["x"] = to_dev(workloads.activations(wl, li))
+        d["A"] = to_dev(workloads.lora_A(wl, li))
+        d["B"] = to_dev(workloads.lora_B(wl, li))
+        d["dy"] = to_dev(workloads.grad_output(wl, li))
         d["w"] = qlora.NF4Weight.empty(N, K, dev)
         d["t"] = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
         d["y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -341,7 +342,7 @@ def main():
     if not args.no_extras:
         out["extras"] = extras(torch, qlora, workloads, dev, to_dev, L, M, r)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(workloads, cfg_id, total_flops, n_weights)
+        out["cpu_baseline"] = cpu_baseline(workloads, wl, total_flops, n_weights)
     print(json.dumps(out))
 
 
@@ -382,38 +383,38 @@ def extras(torch, qlora, workloads, dev, to_dev, L, M, r):
 
     # decode GEMV: 4096x4096 q_proj, r=16, M in {1, 16}; 64 distinct weight copies
     # (> 2x the 256 MB Infinity Cache) rotated so that HBM, not cache, is measured
-    c2 = workloads.CONFIGS[2]
-    _, N2, K2 = c2["layers"][0]
-    W2 = to_dev(workloads.weight(2))
+    qd = workloads.CONFIGS[workloads.Q_PROJ_DECODE]
+    _, N2, K2 = qd["layers"][0]
+    W2 = to_dev(workloads.weight(workloads.Q_PROJ_DECODE))
     copies = [qlora.quantize(W2) for _ in range(64)]
-    A2 = to_dev(workloads.lora_A(2)); B2 = to_dev(workloads.lora_B(2))
+    A2 = to_dev(workloads.lora_A(workloads.Q_PROJ_DECODE)); B2 = to_dev(workloads.lora_B(workloads.Q_PROJ_DECODE))
     dec = {}
     for Md in (1, 16):
-        xd = to_dev(workloads.activations(2, M=Md))
-        td = torch.empty((Md, c2["r"]), dtype=torch.bfloat16, device=dev)
+        xd = to_dev(workloads.activations(workloads.Q_PROJ_DECODE, M=Md))
+        td = torch.empty((Md, qd["r"]), dtype=torch.bfloat16, device=dev)
         yd = torch.empty((Md, N2), dtype=torch.bfloat16, device=dev)
-        wsd = torch.empty(max(qlora.fwd_workspace(Md, N2, K2, c2["r"]), 256), dtype=torch.uint8, device=dev)
+        wsd = torch.empty(max(qlora.fwd_workspace(Md, N2, K2, qd["r"]), 256), dtype=torch.uint8, device=dev)
         for w in copies[:4]:
-            qlora.linear_fwd(w, xd, A2, B2, c2["alpha"], y=yd, t=td, ws=wsd)
+            qlora.linear_fwd(w, xd, A2, B2, qd["alpha"], y=yd, t=td, ws=wsd)
         torch.cuda.synchronize()
         # back-to-back launches from a captured HIP graph: the GPU time per call
         # without Python's launch latency between calls
         gemv_ms = graph_ms([lambda w=w: qlora.fused_gemm_fwd(w, xd, td, B2, y=yd) for w in copies])
-        call_ms = graph_ms([lambda w=w: (qlora.lora_down(xd, A2, c2["alpha"], t=td, ws=wsd),
+        call_ms = graph_ms([lambda w=w: (qlora.lora_down(xd, A2, qd["alpha"], t=td, ws=wsd),
                                          qlora.fused_gemm_fwd(w, xd, td, B2, y=yd)) for w in copies])
         # eager calls one at a time, host launch latency included
         pairs = []
         for w in copies:
             a, b = ev(), ev()
             a.record()
-            qlora.lora_down(xd, A2, c2["alpha"], t=td, ws=wsd)
+            qlora.lora_down(xd, A2, qd["alpha"], t=td, ws=wsd)
             qlora.fused_gemm_fwd(w, xd, td, B2, y=yd)
             b.record()
             pairs.append((a, b))
         torch.cuda.synchronize()
         eager_ms = float(np.median([p.elapsed_time(q) for p, q in pairs]))
-        nb = gemv_bytes(Md, N2, K2, c2["r"])
-        nb_gemv = nb - 2 * K2 * c2["r"]  # A is read by the down-projection, not by the GEMV kernel
+        nb = gemv_bytes(Md, N2, K2, qd["r"])
+        nb_gemv = nb - 2 * K2 * qd["r"]  # A is read by the down-projection, not by the GEMV kernel
         dec[f"M={Md}"] = {"bytes_fwd_call": nb, "bytes_gemv_kernel": nb_gemv,
                           "gemv_kernel_us": round(gemv_ms * 1e3, 2), "fwd_call_us": round(call_ms * 1e3, 2),
                           "eager_fwd_call_us": round(eager_ms * 1e3, 2),
@@ -434,12 +435,12 @@ def extras(torch, qlora, workloads, dev, to_dev, L, M, r):
     # codes + scales + A + B in, the bf16 merged weight out
     mo = [torch.empty((d["N"], d["K"]), dtype=torch.bfloat16, device=dev) for d in L]
     for d, o in zip(L, mo):
-        qlora.merge(d["w"], d["A"], d["B"], workloads.CONFIGS[4]["alpha"], out=o)
+        qlora.merge(d["w"], d["A"], d["B"], workloads.CONFIGS[workloads.BLOCK_7B]["alpha"], out=o)
     a, b = ev(), ev()
     a.record()
     for _ in range(reps):
         for d, o in zip(L, mo):
-            qlora.merge(d["w"], d["A"], d["B"], workloads.CONFIGS[4]["alpha"], out=o)
+            qlora.merge(d["w"], d["A"], d["B"], workloads.CONFIGS[workloads.BLOCK_7B]["alpha"], out=o)
     b.record()
     torch.cuda.synchronize()
     m_ms = a.elapsed_time(b) / reps
@@ -508,7 +509,7 @@ def extras_fp32(torch, qlora, workloads, dev, L, M, r, ev):
     """The fp32 compute dtype (deep dive 8.3) on the same 7 linears: every tensor fp32 (the bf16 draws
     widened exactly), w_hat = fl32(a_hat * c_q), products on the fp32 matrix cores.  The whole quantize +
     fwd + bwd step and the forward call, against the 157.3 TFLOP/s dense fp32 MFMA peak."""
-    alpha = workloads.CONFIGS[4]["alpha"]
+    alpha = workloads.CONFIGS[workloads.BLOCK_7B]["alpha"]
     f = torch.float32
     Lf = [dict(N=d["N"], K=d["K"], flops=d["flops"], W=d["W"].to(f), x=d["x"].to(f), A=d["A"].to(f),
                B=d["B"].to(f), dy=d["dy"].to(f), t=torch.empty((M, r), dtype=f, device=dev),
@@ -561,7 +562,7 @@ def extras_variant(torch, qlora, workloads, dev, to_dev, L, M, r, ev, double_qua
     (deep dive 8.3; the same draws rounded to fp16).  The whole quantize + fwd + bwd step of the 7 linears,
     the forward GEMM alone, quantize bandwidth and the decode GEMV (64 rotated weight copies)."""
     res = {}
-    alpha = workloads.CONFIGS[4]["alpha"]
+    alpha = workloads.CONFIGS[workloads.BLOCK_7B]["alpha"]
     dt = torch.bfloat16 if dtype is None else dtype
     if dt != torch.bfloat16:
         L = [dict(d, W=d["W"].to(dt), x=d["x"].to(dt), A=d["A"].to(dt), B=d["B"].to(dt), dy=d["dy"].to(dt),
@@ -612,19 +613,19 @@ def extras_variant(torch, qlora, workloads, dev, to_dev, L, M, r, ev, double_qua
     res["quantize"] = {"GB/s": round(q_bytes / (q_ms * 1e-3) / 1e9, 1), "ms": round(q_ms, 4),
                        "bytes_per_weight": round(q_bytes / sum(d["N"] * d["K"] for d in L), 4)}
     del Wn, ws, L
-    c2 = workloads.CONFIGS[2]
-    _, N2, K2 = c2["layers"][0]
-    W2 = to_dev(workloads.weight(2)).to(dt)
+    qd = workloads.CONFIGS[workloads.Q_PROJ_DECODE]
+    _, N2, K2 = qd["layers"][0]
+    W2 = to_dev(workloads.weight(workloads.Q_PROJ_DECODE)).to(dt)
     copies = [qlora.quantize(W2, double_quant=double_quant, quant_type=quant_type) for _ in range(64)]
-    B2 = to_dev(workloads.lora_B(2)).to(dt)
-    xd = to_dev(workloads.activations(2, M=1)).to(dt)
-    td = torch.zeros((1, c2["r"]), dtype=dt, device=dev)
+    B2 = to_dev(workloads.lora_B(workloads.Q_PROJ_DECODE)).to(dt)
+    xd = to_dev(workloads.activations(workloads.Q_PROJ_DECODE, M=1)).to(dt)
+    td = torch.zeros((1, qd["r"]), dtype=dt, device=dev)
     yd = torch.empty((1, N2), dtype=dt, device=dev)
     for w in copies[:4]:
         qlora.fused_gemm_fwd(w, xd, td, B2, y=yd)
     torch.cuda.synchronize()
     gemv_ms = graph_ms([lambda w=w: qlora.fused_gemm_fwd(w, xd, td, B2, y=yd) for w in copies])
-    nb = gemv_bytes(1, N2, K2, c2["r"], double_quant=double_quant) - 2 * K2 * c2["r"]
+    nb = gemv_bytes(1, N2, K2, qd["r"], double_quant=double_quant) - 2 * K2 * qd["r"]
     res["decode_gemv_q_proj_M=1"] = {"gemv_kernel_us": round(gemv_ms * 1e3, 2), "bytes_gemv_kernel": nb,
                                      "GB/s_gemv_kernel": round(nb / (gemv_ms * 1e-3) / 1e9, 1)}
     return res
@@ -634,7 +635,7 @@ def extras_pooled(torch, qlora, workloads, dev, to_dev, L, M, r, ev, g):
     """The whole quantize + fwd + bwd step of the 7 linears with the QA-LoRA pooled branch
     ("LoRA, QLoRA, QA-LoRA explained", sections 3-5): A is [K/g, r] and the LoRA input is the mean
     of each group of g columns of x.  Reported beside the plain step it replaces."""
-    alpha = workloads.CONFIGS[4]["alpha"]
+    alpha = workloads.CONFIGS[workloads.BLOCK_7B]["alpha"]
     Ap = [to_dev(workloads.custom(900 + i, (d["K"] // g, r), float(1 / np.sqrt(r)))) for i, d in enumerate(L)]
     ws = torch.empty(max(max(qlora.lib.qlora_pooled_fwd_workspace(M, d["N"], d["K"], r, g),
                               qlora.lib.qlora_pooled_bwd_workspace(M, d["N"], d["K"], r, g)) for d in L),
@@ -664,7 +665,7 @@ def extras_pooled(torch, qlora, workloads, dev, to_dev, L, M, r, ev, g):
     return {"g": g, "step_ms": round(ms, 4), "TFLOP/s_plain_step_flops": round(total_flops / (ms * 1e-3) / 1e12, 2)}
 
 
-def cpu_baseline(workloads, cfg_id, total_flops, n_weights):
+def cpu_baseline(workloads, wl, total_flops, n_weights):
     """The oracle as it stands, on the host cores, on a bounded sample of the same step:
     quantize two of the seven weights (q_proj, gate_proj) and run fp64 forward+backward
     on 256 of the 4096 token rows for those two layers; the full-step time is
@@ -675,20 +676,20 @@ def cpu_baseline(workloads, cfg_id, total_flops, n_weights):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         blas_threads = os.cpu_count() or 1
-    cfg = workloads.CONFIGS[cfg_id]
+    cfg = workloads.CONFIGS[wl]
     M, r, alpha = cfg["M"], cfg["r"], cfg["alpha"]
     rows = 256
     q_w, q_s, f_f, f_s = 0, 0.0, 0, 0.0
     for li in (0, 4):
         name, N, K = cfg["layers"][li]
-        W = workloads.weight(cfg_id, li)
+        W = workloads.weight(wl, li)
         t0 = time.perf_counter()
         p, q8, a2 = nf4.quantize(W)
         q_s += time.perf_counter() - t0
         q_w += N * K
-        x = workloads.activations(cfg_id, li)[:rows]
-        dy = workloads.grad_output(cfg_id, li)[:rows]
-        A = workloads.lora_A(cfg_id, li); B = workloads.lora_B(cfg_id, li)
+        x = workloads.activations(wl, li)[:rows]
+        dy = workloads.grad_output(wl, li)[:rows]
+        A = workloads.lora_A(wl, li); B = workloads.lora_B(wl, li)
         t0 = time.perf_counter()
         Wh = bf16.to_f64(nf4.dequantize(p, q8, a2, N, K))
         xf, Af, Bf, dyf = (bf16.to_f64(v) for v in (x, A, B, dy))

@@ -55,9 +55,9 @@ def _check_full(q, W, x, A, B, dy, alpha, tag, pass_t=True):
 
 
 def test_c1_single_linear(q):
-    c = 1
+    c = workloads.LINEAR_256
     _check_full(q, workloads.weight(c), workloads.activations(c), workloads.lora_A(c), workloads.lora_B(c),
-                workloads.grad_output(c), workloads.CONFIGS[c]["alpha"], "c1")
+                workloads.grad_output(c), workloads.CONFIGS[c]["alpha"], c)
 
 
 @pytest.mark.parametrize("M,N,K,r", [
@@ -140,11 +140,11 @@ def test_lora_off_matches_dequant_product(q):
 
 
 def test_c2_decode(q):
-    c = 2
+    c = workloads.Q_PROJ_DECODE
     W = workloads.weight(c)
     for M in (1, 16):
         _check_full(q, W, workloads.activations(c, M=M), workloads.lora_A(c), workloads.lora_B(c),
-                    workloads.grad_output(c, M=M), workloads.CONFIGS[c]["alpha"], f"c2 M={M}")
+                    workloads.grad_output(c, M=M), workloads.CONFIGS[c]["alpha"], f"{c} M={M}")
 
 
 # ---------------------------------------------------------------- full-size, sampled
@@ -162,7 +162,7 @@ def _check_sampled(q, cfg, layer, seed=0):
     name, N, K = workloads.CONFIGS[cfg]["layers"][layer]
     C = workloads.CONFIGS[cfg]
     M, r, alpha = C["M"], C["r"], C["alpha"]
-    say(f"[linear] c{cfg} {name} M={M} N={N} K={K} r={r} (sampled)")
+    say(f"[linear] {cfg} {name} M={M} N={N} K={K} r={r} (sampled)")
     W = workloads.weight(cfg, layer)
     x = workloads.activations(cfg, layer); A = workloads.lora_A(cfg, layer)
     B = workloads.lora_B(cfg, layer); dy = workloads.grad_output(cfg, layer)
@@ -194,19 +194,19 @@ def _check_sampled(q, cfg, layer, seed=0):
                 dA=lora.rel_err(g_dA, dA_ref), dB=lora.rel_err(g_dB, dB_ref))
     say(f"    rel errors {errs}")
     for k, e in errs.items():
-        assert e <= TOL, f"c{cfg} {name}: {k} rel err {e:.3e}"
+        assert e <= TOL, f"{cfg} {name}: {k} rel err {e:.3e}"
 
 
 def test_c3_mlp_up_sampled(q):
-    _check_sampled(q, 3, 0)
+    _check_sampled(q, workloads.UP_PROJ_M2048, 0)
 
 
 @pytest.mark.parametrize("layer", [0, 4, 6])
 def test_c4_block_layers_sampled(q, layer):
-    _check_sampled(q, 4, layer)
+    _check_sampled(q, workloads.BLOCK_7B, layer)
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("layer", [0, 2])
 def test_c5_70b_mlp_sampled(q, layer):
-    _check_sampled(q, 5, layer)
+    _check_sampled(q, workloads.MLP_70B, layer)

@@ -66,9 +66,9 @@ def test_merge_q_proj_sampled_rows(q):
     import torch
     N = K = 4096
     r = 64
-    W = workloads.weight(4, 0)
-    A, B = workloads.lora_A(4, 0), workloads.lora_B(4, 0)
-    alpha = workloads.CONFIGS[4]["alpha"]
+    W = workloads.weight(workloads.BLOCK_7B, 0)
+    A, B = workloads.lora_A(workloads.BLOCK_7B, 0), workloads.lora_B(workloads.BLOCK_7B, 0)
+    alpha = workloads.CONFIGS[workloads.BLOCK_7B]["alpha"]
     say(f"[merge] q_proj {N}x{K} r={r} sampled rows")
     w = q.quantize(dev_bf16(W))
     out = q.merge(w, dev_bf16(A), dev_bf16(B), alpha)

@@ -27,7 +27,7 @@ def q():
 @pytest.mark.parametrize("N,K", [(256, 256), (4096, 4096), (3, 192), (257, 64), (64, 11008)])
 def test_quantize_dequantize_bit_exact(q, N, K):
     import torch
-    W = workloads.weight(2) if (N, K) == (4096, 4096) else workloads.custom(300 + N + K, (N, K), 0.02)
+    W = workloads.weight(workloads.Q_PROJ_DECODE) if (N, K) == (4096, 4096) else workloads.custom(300 + N + K, (N, K), 0.02)
     say(f"[nodq quantize] N={N} K={K}")
     w = q.quantize(dev_bf16(W), double_quant=False)
     assert w.q8 is None and w.a2.numel() == N * K // 64
@@ -65,7 +65,7 @@ def _check_linear(q, M, N, K, r, seed, alpha):
 
 
 @pytest.mark.parametrize("M,N,K,r", [
-    (256, 256, 256, 8),          # c1-sized
+    (256, 256, 256, 8),          # the 256 x 256 single-linear size
     (17, 130, 128, 8),           # one super-step of two blocks
     (300, 520, 384, 64),         # ragged M and N
     (64, 72, 11008 // 4, 32),    # 43 blocks per row: odd count, short last super-step

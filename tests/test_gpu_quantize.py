@@ -43,11 +43,11 @@ def _check_full(q, W, tag):
 
 
 def test_c1_linear_256(q):
-    _check_full(q, workloads.weight(1), "c1")
+    _check_full(q, workloads.weight(workloads.LINEAR_256), workloads.LINEAR_256)
 
 
 def test_c2_q_proj_with_outliers(q):
-    _check_full(q, workloads.weight(2), "c2")
+    _check_full(q, workloads.weight(workloads.Q_PROJ_DECODE), workloads.Q_PROJ_DECODE)
 
 
 @pytest.mark.parametrize("N,K", [(1, 64), (3, 192), (5, 640), (257, 64), (64, 11008), (7, 16384 + 64)])
@@ -88,12 +88,12 @@ def test_edge_blocks(q):
     _check_full(q, W, "edge blocks")
 
 
-@pytest.mark.parametrize("cfg", [3, 4])
+@pytest.mark.parametrize("cfg", [workloads.UP_PROJ_M2048, workloads.BLOCK_7B])
 def test_full_size_workloads(q, cfg):
     for li, (name, N, K) in enumerate(workloads.CONFIGS[cfg]["layers"]):
-        if cfg == 4 and li not in (0, 4, 6):                 # q, gate, down cover every shape
+        if cfg == workloads.BLOCK_7B and li not in (0, 4, 6):                 # q, gate, down cover every shape
             continue
-        _check_full(q, workloads.weight(cfg, li), f"c{cfg} {name}")
+        _check_full(q, workloads.weight(cfg, li), f"{cfg} {name}")
 
 
 @pytest.mark.slow
@@ -101,9 +101,9 @@ def test_c5_sampled_groups(q):
     """70B-like MLP weights (235M weights each): every group's a2, then sampled groups bit-exact."""
     import torch
     rng = np.random.default_rng(7)
-    for li, (name, N, K) in enumerate(workloads.CONFIGS[5]["layers"]):
-        say(f"[quantize] c5 {name} N={N} K={K} (sampled)")
-        W = workloads.weight(5, li)
+    for li, (name, N, K) in enumerate(workloads.CONFIGS[workloads.MLP_70B]["layers"]):
+        say(f"[quantize] {workloads.MLP_70B} {name} N={N} K={K} (sampled)")
+        W = workloads.weight(workloads.MLP_70B, li)
         w = q.quantize(dev_bf16(W))
         torch.cuda.synchronize()
         codes = w.codes.cpu().numpy(); q8 = w.q8.cpu().numpy(); a2 = w.a2.cpu().numpy()

@@ -140,7 +140,7 @@ def test_levels_times_power_of_two_scale_round_trip():
 def test_error_bound():
     """|u - c_q| <= (largest gap) / 2 = 1/6 for every element, and |w - w_hat| within that plus the
     scale and bf16 rounding terms."""
-    W = workloads.weight(2)[:128]                          # includes 10x outliers
+    W = workloads.weight(workloads.Q_PROJ_DECODE)[:128]                          # includes 10x outliers
     packed, q8, A2 = fp4.quantize(W)
     Wh = fp4.dequantize(packed, q8, A2, 128, 4096)
     w = bf16.to_f64(W).reshape(-1, 64)

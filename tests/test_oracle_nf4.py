@@ -222,7 +222,7 @@ def test_dequant_error_bound_and_idempotence():
     """|w - w_hat| <= a * max_half_gap + |a - a_hat| + bf16 rounding, and
     re-quantizing the dequantized weight reproduces the codes (each block keeps
     its +-1 code, and the bf16 rounding is far below the smallest half gap)."""
-    W = workloads.weight(2)[:256]                          # includes 10x outliers
+    W = workloads.weight(workloads.Q_PROJ_DECODE)[:256]                          # includes 10x outliers
     packed, q8, A2 = nf4.quantize(W)
     Wh = nf4.dequantize(packed, q8, A2, 256, 4096)
     w = bf16.to_f64(W).reshape(-1, 64)
@@ -333,7 +333,7 @@ def test_nodq_dequant_against_fraction_and_exact_extremes():
 def test_nodq_error_bound():
     """|w - w_hat| <= a * (largest half gap of the table) + bf16 rounding of w_hat: no scale error term,
     since the scale is stored exactly."""
-    W = workloads.weight(2)[:128]                          # includes 10x outliers
+    W = workloads.weight(workloads.Q_PROJ_DECODE)[:128]                          # includes 10x outliers
     packed, absmax = nf4.quantize_nodq(W)
     Wh = nf4.dequantize_nodq(packed, absmax, 128, 4096)
     w = bf16.to_f64(W).reshape(-1, 64)
