@@ -296,20 +296,27 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const uint16_t* __
             wait_vm_at_most(2 * (NG - 1 - j));  // group j's two code loads have landed
             const f32x4_t ah = *reinterpret_cast<const f32x4_t*>(alane + 4 * j);
             const uint8_t* const xg = xlane + 128 * (w * PBw + 4 * j);
+            // the group's four code words, then all 32 table reads, then the MFMAs: one
+            // wave per SIMD, so the two dependent LDS round trips are paid once per group
+            uint2 c[4];
 #pragma unroll
-            for (int h4 = 0; h4 < 4; ++h4) {
-                const uint2 c = *reinterpret_cast<const uint2*>(cgs[j] + clane + 16 * ((2 * h4 + (lg >> 1)) ^ cswz));
-                const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xg + 128 * h4));
-                const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xg + 128 * h4 + 16));
-                u32x4_t w0, w1;
+            for (int h4 = 0; h4 < 4; ++h4)
+                c[h4] = *reinterpret_cast<const uint2*>(cgs[j] + clane + 16 * ((2 * h4 + (lg >> 1)) ^ cswz));
+            u32x4_t w0[4], w1[4];
+#pragma unroll
+            for (int h4 = 0; h4 < 4; ++h4)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const uint32_t sel = 0x0C0C0000u | ((4u + jj) << 8);
-                    w0[jj] = *reinterpret_cast<const uint32_t*>(lut + __builtin_amdgcn_perm(c.x, lane4, sel));
-                    w1[jj] = *reinterpret_cast<const uint32_t*>(lut + __builtin_amdgcn_perm(c.y, lane4, sel));
+                    w0[h4][jj] = *reinterpret_cast<const uint32_t*>(lut + __builtin_amdgcn_perm(c[h4].x, lane4, sel));
+                    w1[h4][jj] = *reinterpret_cast<const uint32_t*>(lut + __builtin_amdgcn_perm(c[h4].y, lane4, sel));
                 }
-                f32x4_t part = mfma16<DT>(a0, __builtin_bit_cast(bf16x8_t, w0), f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
-                part = mfma16<DT>(a1, __builtin_bit_cast(bf16x8_t, w1), part);
+#pragma unroll
+            for (int h4 = 0; h4 < 4; ++h4) {
+                const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xg + 128 * h4));
+                const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xg + 128 * h4 + 16));
+                f32x4_t part = mfma16<DT>(a0, __builtin_bit_cast(bf16x8_t, w0[h4]), f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
+                part = mfma16<DT>(a1, __builtin_bit_cast(bf16x8_t, w1[h4]), part);
                 // blocks past the row end have a_hat = 0; their x and codes are
                 // staged values or zeros (finite), so they add exactly nothing
 #pragma unroll
