@@ -156,12 +156,21 @@ __device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, uint32_t bytes)
 // row 0 is the buffer base: columns [col0, col0 + 64) into `tile` (ftile
 // layout).  voff0 = this lane's byte offset of tile row 8*wave + lane/8, its
 // logical chunk, column 0.
+// An LDS pointer as the address_space(3) pointer the LDS builtins take.  The
+// address-space cast keeps the pointer's origin, so the compiler can tell a
+// direct load's destination from the tiles a step reads and waits only where
+// they may overlap; a round trip through an integer would hide the origin and
+// make every LDS read wait for every direct load in flight.
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(3))) T* as_lds(const void* p) {
+    return (__attribute__((address_space(3))) T*)(p);
+}
+
 __device__ __forceinline__ void load_tile_direct(i32x4_t rs, uint8_t* tile, uint32_t voff0, int wave, int col0,
                                                  int64_t ld) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        auto* dst = reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(
-            reinterpret_cast<uintptr_t>(tile + (32 * j + 8 * wave) * 128));
+        auto* dst = as_lds<uint32_t>(tile + (32 * j + 8 * wave) * 128);
         // the row offset goes in voffset: the buffer range check covers voffset
         // (not soffset), so rows past the end of the buffer read as zero
         raw_buffer_load_lds(rs, dst, 16, (int)(voff0 + (uint32_t)(32 * j * ld * 2)), (int)(col0 * 2), 0, 0);
@@ -737,12 +746,8 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
             a[i] = *reinterpret_cast<const bf16x8*>(A + offA[c] + 4096u * (4 * wm + i));
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                reinterpret_cast<__attribute__((address_space(3))) s16x4_t*>(
-                    reinterpret_cast<uintptr_t>(Bt + offB[u][0] + 8192u * c)));
-            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                reinterpret_cast<__attribute__((address_space(3))) s16x4_t*>(
-                    reinterpret_cast<uintptr_t>(Bt + offB[u][1] + 8192u * c)));
+            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds<s16x4_t>(Bt + offB[u][0] + 8192u * c));
+            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds<s16x4_t>(Bt + offB[u][1] + 8192u * c));
             b[u] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
     };
@@ -785,12 +790,11 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
     wait_direct_loads();
     __syncthreads();
 
-    for (int ns = 0; ns < NS; ++ns) {
-        const int buf = ns & 1;
-        const uint8_t* A = ldsA0 + buf * kTileBytes;
-        const uint8_t* Bt = ldsB0 + buf * kTileBytes;
-        uint8_t* An = ldsA0 + (buf ^ 1) * kTileBytes;
-        uint8_t* Bn = ldsB0 + (buf ^ 1) * kTileBytes;
+    // One step reads dy tile A and weight tile Bt and fills An (direct loads) and Bn.
+    // The four never overlap; restrict-qualified parameters tell the compiler so,
+    // which keeps it from waiting for the fill of An before the step's reads.
+    auto step = [&](int ns, const uint8_t* __restrict__ A, uint8_t* __restrict__ An, const uint8_t* __restrict__ Bt,
+                    uint8_t* __restrict__ Bn) {
         bf16x8 a[2][4], b[2][4];
         read_ops(A, Bt, 0, a[0], b[0]);
         load_dy(An, min(ns + 1, NS - 1));
@@ -820,6 +824,11 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
         nxt = nn;
         if (DYVEC) wait_direct_loads_behind<kStepLoads>();
         __syncthreads();
+    };
+    for (int ns = 0; ns < NS; ++ns) {
+        const int buf = ns & 1;
+        step(ns, ldsA0 + buf * kTileBytes, ldsA0 + (buf ^ 1) * kTileBytes, ldsB0 + buf * kTileBytes,
+             ldsB0 + (buf ^ 1) * kTileBytes);
     }
 
     // LoRA: r more reduction steps with A-operand u [M, r] (LDS) and B-operand

@@ -107,3 +107,41 @@ def test_gemv_group_waits_follow_the_code_loads(asm):
             elif o[0] == "A" and seen_d:
                 assert since_d == 0, f"{name}: {since_d} register loads between the code loads and a group wait"
     assert n_kernels == 72          # M classes x group counts x scale layout x codebook x dtype
+
+
+def test_backward_steps_wait_for_their_dy_tile_before_the_barrier(asm):
+    """The backward dx GEMM issues the next dy tile by direct loads at the start of a step and
+    reads it after the step's closing barrier; loads complete in order, so the tile has landed at
+    the barrier if some wait between its last direct load and the barrier allows no more loads in
+    flight than were issued after that load.  The step body is written so that the compiler need not
+    wait for the tile earlier (its LDS reads are of the other buffers); either way the check holds
+    for every step of every instantiation."""
+    n_kernels = 0
+    for name, body in _kernels(asm["gemm"], "nf4_gemm_bwd_dx_kernel"):
+        n_kernels += 1
+        if "ILb0E" in name[:60]:        # DYVEC off: dy is staged through registers, no direct loads
+            continue
+        steps, cur = [], []
+        for l in body:
+            cur.append(l)
+            if l == "s_barrier":
+                steps.append(cur)
+                cur = []
+        checked = 0
+        for st in steps:
+            ops = _ops(st)
+            d = [i for i, o in enumerate(ops) if o == "D"]
+            if len(d) < 8:
+                continue
+            after = ops[d[-1] + 1:]
+            waits = [i for i, o in enumerate(after) if isinstance(o, tuple)]
+            ok = False
+            for wi in waits:
+                issued = sum(1 for o in after[:wi] if o in ("D", "g"))
+                if after[wi][1] <= issued:
+                    ok = True
+                    break
+            assert ok, f"{name}: no wait covers the dy tile before the barrier"
+            checked += 1
+        assert checked >= 1, f"{name}: no main-loop step found"
+    assert n_kernels == 16
