@@ -22,7 +22,7 @@ inline qlora_status check_state(const qlora_nf4* w, DtypeClass dc = kDt16) {
     if (!w || !w->codes || !w->a2) return QLORA_ERR_INVALID_ARG;
     if (w->n < 1 || w->k < 1) return QLORA_ERR_INVALID_ARG;
     if (w->k % kBlock) return QLORA_ERR_UNSUPPORTED_SHAPE;
-    if (w->n > (int64_t(1) << 31) || w->k > (int64_t(1) << 31)) return QLORA_ERR_UNSUPPORTED_SHAPE;
+    if (w->n >= (int64_t(1) << 31) || w->k >= (int64_t(1) << 31)) return QLORA_ERR_UNSUPPORTED_SHAPE;
     if (w->quant_type != QLORA_QUANT_NF4 && w->quant_type != QLORA_QUANT_FP4) return QLORA_ERR_INVALID_ARG;
     const bool is16 = w->dtype == QLORA_DTYPE_BF16 || w->dtype == QLORA_DTYPE_F16;
     const bool is32 = w->dtype == QLORA_DTYPE_F32;
@@ -169,7 +169,7 @@ qlora_status qlora_merge(const qlora_nf4* w, const uint16_t* A, const uint16_t* 
                          uint16_t* out, void* stream) {
     qlora_status st = check_state(w);
     if (st != QLORA_OK) return st;
-    if (!A || !B || !out || r < 1 || r > 128 || !std::isfinite(alpha)) return QLORA_ERR_INVALID_ARG;
+    if (!A || !B || !out || bad_dims(0, w->n, w->k, r) || !std::isfinite(alpha)) return QLORA_ERR_INVALID_ARG;
     if (!aligned16(A) || !aligned16(B) || !aligned16(out)) return QLORA_ERR_MISALIGNED;
     const float s = alpha / (float)r;
     return launch_merge(w->codes, w->q8, w->a2, cb_of(w), dt_of(w), A, B, r, s, out, (int)w->n, (int)w->k,

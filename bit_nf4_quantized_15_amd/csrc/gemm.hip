@@ -920,7 +920,12 @@ qlora_status launch_gemm_bwd_dx(const uint16_t* dy, const uint8_t* codes, const 
                                 int cb, int dt, const uint16_t* u, const uint16_t* A, uint16_t* dx, int M, int N, int K,
                                 int r, hipStream_t s) {
     const int tm = (M + kTM - 1) / kTM, tk = (K + kTN - 1) / kTN;
-    const bool vec = (N % 8 == 0) && ((reinterpret_cast<uintptr_t>(dy) & 15u) == 0) &&
+    // Direct loads only when every step is 64 whole columns: a tile load puts the
+    // column offset in soffset, which the buffer range check does not cover, so a
+    // partial last step would read past row ends (the next row's head, or past the
+    // end of dy for the panel's last row).  Other widths take the register path,
+    // which zeroes every element past N.
+    const bool vec = (N % kTK == 0) && ((reinterpret_cast<uintptr_t>(dy) & 15u) == 0) &&
                      ((int64_t)kTM * N * 2 < (int64_t(1) << 32));
     // q8 == NULL: no double quantization, a2 holds one fp32 absmax per block
     with_cb_dt(cb, dt, [&](auto cbc, auto dtc) {

@@ -97,6 +97,16 @@ class QLoraError(RuntimeError):
         self.status = status
 
 
+def _empty(*shape, dtype, device):
+    """Every buffer this module hands to the library is allocated here (outputs, weight state and workspace).
+    Uninitialised, like torch.empty; the GPU tests replace `empty_hook` to fill new buffers with a poison
+    pattern, so that an element a kernel never writes cannot pass for a correct one."""
+    return empty_hook(*shape, dtype=dtype, device=device)
+
+
+empty_hook = torch.empty
+
+
 def _check(status, where):
     if status != 0:
         raise QLoraError(status, where)
@@ -156,12 +166,12 @@ class NF4Weight:
     def empty(cls, N, K, device="cuda", double_quant=True, quant_type="nf4", dtype=torch.bfloat16):
         if not double_quant:
             cb, ab = sizes_nodq(N, K)
-            return cls(torch.empty(cb, dtype=torch.uint8, device=device), None,
-                       torch.empty(ab // 4, dtype=torch.float32, device=device), N, K, quant_type, dtype)
+            return cls(_empty(cb, dtype=torch.uint8, device=device), None,
+                       _empty(ab // 4, dtype=torch.float32, device=device), N, K, quant_type, dtype)
         cb, qb, ab = sizes(N, K)
-        return cls(torch.empty(cb, dtype=torch.uint8, device=device),
-                   torch.empty(qb, dtype=torch.uint8, device=device),
-                   torch.empty(ab // 4, dtype=torch.float32, device=device), N, K, quant_type, dtype)
+        return cls(_empty(cb, dtype=torch.uint8, device=device),
+                   _empty(qb, dtype=torch.uint8, device=device),
+                   _empty(ab // 4, dtype=torch.float32, device=device), N, K, quant_type, dtype)
 
     def state(self):
         q8 = None if self.q8 is None else self.q8.data_ptr()
@@ -194,7 +204,7 @@ def dequantize(w, out=None, fp32=False):
     only."""
     fp32 = fp32 or w.dtype == torch.float32
     dt = torch.float32 if fp32 else w.dtype
-    o = torch.empty((w.N, w.K), dtype=dt, device=w.codes.device) if out is None else out
+    o = _empty((w.N, w.K), dtype=dt, device=w.codes.device) if out is None else out
     _dev(o, dt, "out", (w.N, w.K))
     st = w.state()
     if fp32:
@@ -210,7 +220,7 @@ def merge(w, A, B, alpha, out=None):
     K, r = A.shape
     _dev(A, w.dtype, "A", (w.K, r))
     _dev(B, w.dtype, "B", (r, w.N))
-    o = torch.empty((w.N, w.K), dtype=w.dtype, device=A.device) if out is None else out
+    o = _empty((w.N, w.K), dtype=w.dtype, device=A.device) if out is None else out
     _dev(o, w.dtype, "out", (w.N, w.K))
     st = w.state()
     _check(lib.qlora_merge(ctypes.byref(st), _ptr(A), _ptr(B), r, float(alpha), _ptr(o), _stream()), "qlora_merge")
@@ -234,7 +244,7 @@ def _ws(nbytes, device, ws):
         return None, 0
     if ws is not None and ws.numel() >= nbytes:
         return ws, ws.numel()
-    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+    return _empty(nbytes, dtype=torch.uint8, device=device), nbytes
 
 
 def linear_fwd(w, x, A, B, alpha, y=None, t=None, want_t=True, ws=None):
@@ -245,9 +255,9 @@ def linear_fwd(w, x, A, B, alpha, y=None, t=None, want_t=True, ws=None):
     _dev(A, w.dtype, "A", (w.K, r))
     _dev(B, w.dtype, "B", (r, w.N))
     dev = x.device
-    y = torch.empty((M, w.N), dtype=w.dtype, device=dev) if y is None else _dev(y, w.dtype, "y", (M, w.N))
+    y = _empty((M, w.N), dtype=w.dtype, device=dev) if y is None else _dev(y, w.dtype, "y", (M, w.N))
     if want_t and t is None:
-        t = torch.empty((M, r), dtype=w.dtype, device=dev)
+        t = _empty((M, r), dtype=w.dtype, device=dev)
     if t is not None:
         _dev(t, w.dtype, "t", (M, r))
     wsb, wsn = _ws(fwd_workspace(M, w.N, w.K, r, w.dtype), dev, ws)
@@ -267,7 +277,7 @@ def lora_down(x, A, alpha, t=None, ws=None):
     code = _dtype_code(dt)
     _dev(x, dt, "x")
     _dev(A, dt, "A", (K, r))
-    t = torch.empty((M, r), dtype=dt, device=x.device) if t is None else _dev(t, dt, "t", (M, r))
+    t = _empty((M, r), dtype=dt, device=x.device) if t is None else _dev(t, dt, "t", (M, r))
     wsb, wsn = _ws(int(lib.qlora_lora_down_workspace(M, K, r)), x.device, ws)
     _check(lib.qlora_lora_down(_ptr(x), M, K, _ptr(A), r, float(alpha), code, _ptr(t), _ptr(wsb), wsn, _stream()),
            "qlora_lora_down")
@@ -281,7 +291,7 @@ def fused_gemm_fwd(w, x, t, B, y=None):
     _dev(x, w.dtype, "x", (M, w.K))
     _dev(t, w.dtype, "t", (M, r))
     _dev(B, w.dtype, "B", (r, w.N))
-    y = torch.empty((M, w.N), dtype=w.dtype, device=x.device) if y is None else _dev(y, w.dtype, "y", (M, w.N))
+    y = _empty((M, w.N), dtype=w.dtype, device=x.device) if y is None else _dev(y, w.dtype, "y", (M, w.N))
     st = w.state()
     _check(lib.qlora_fused_gemm_fwd(ctypes.byref(st), _ptr(x), M, _ptr(t), _ptr(B), r, _ptr(y), _stream()),
            "qlora_fused_gemm_fwd")
@@ -295,7 +305,7 @@ def fused_gemm_bwd_dx(w, dy, u, A, dx=None):
     _dev(dy, w.dtype, "dy", (M, w.N))
     _dev(u, w.dtype, "u", (M, r))
     _dev(A, w.dtype, "A", (w.K, r))
-    dx = torch.empty((M, w.K), dtype=w.dtype, device=dy.device) if dx is None else _dev(dx, w.dtype, "dx", (M, w.K))
+    dx = _empty((M, w.K), dtype=w.dtype, device=dy.device) if dx is None else _dev(dx, w.dtype, "dx", (M, w.K))
     st = w.state()
     _check(lib.qlora_fused_gemm_bwd_dx(ctypes.byref(st), _ptr(dy), M, _ptr(u), _ptr(A), r, _ptr(dx), _stream()),
            "qlora_fused_gemm_bwd_dx")
@@ -314,9 +324,9 @@ def linear_bwd(w, x, A, B, alpha, dy, t=None, need_dx=True, dx=None, dA=None, dB
         _dev(t, w.dtype, "t", (M, r))
     dev = x.device
     if need_dx:
-        dx = torch.empty((M, w.K), dtype=w.dtype, device=dev) if dx is None else _dev(dx, w.dtype, "dx", (M, w.K))
-    dA = torch.empty((w.K, r), dtype=torch.float32, device=dev) if dA is None else _dev(dA, torch.float32, "dA", (w.K, r))
-    dB = torch.empty((r, w.N), dtype=torch.float32, device=dev) if dB is None else _dev(dB, torch.float32, "dB", (r, w.N))
+        dx = _empty((M, w.K), dtype=w.dtype, device=dev) if dx is None else _dev(dx, w.dtype, "dx", (M, w.K))
+    dA = _empty((w.K, r), dtype=torch.float32, device=dev) if dA is None else _dev(dA, torch.float32, "dA", (w.K, r))
+    dB = _empty((r, w.N), dtype=torch.float32, device=dev) if dB is None else _dev(dB, torch.float32, "dB", (r, w.N))
     wsb, wsn = _ws(bwd_workspace(M, w.N, w.K, r, w.dtype), dev, ws)
     st = w.state()
     fn, name = ((lib.qlora_linear_bwd_f32, "qlora_linear_bwd_f32") if w.dtype == torch.float32
@@ -333,8 +343,8 @@ def pooled_fwd(w, x, A, B, alpha, g, y=None, t=None, ws=None):
     _dev(x, w.dtype, "x", (M, w.K))
     _dev(A, w.dtype, "A", (w.K // g, r))
     _dev(B, w.dtype, "B", (r, w.N))
-    y = torch.empty((M, w.N), dtype=w.dtype, device=x.device) if y is None else _dev(y, w.dtype, "y", (M, w.N))
-    t = torch.empty((M, r), dtype=w.dtype, device=x.device) if t is None else _dev(t, w.dtype, "t", (M, r))
+    y = _empty((M, w.N), dtype=w.dtype, device=x.device) if y is None else _dev(y, w.dtype, "y", (M, w.N))
+    t = _empty((M, r), dtype=w.dtype, device=x.device) if t is None else _dev(t, w.dtype, "t", (M, r))
     wsb, wsn = _ws(int(lib.qlora_pooled_fwd_workspace(M, w.N, w.K, r, g)), x.device, ws)
     st = w.state()
     _check(lib.qlora_pooled_fwd(ctypes.byref(st), _ptr(x), M, _ptr(A), _ptr(B), r, g, float(alpha), _ptr(y), _ptr(t),
@@ -353,13 +363,13 @@ def pooled_bwd(w, x, A, B, alpha, g, dy, t=None, need_dx=True, dx=None, dA=None,
     if t is not None:
         _dev(t, w.dtype, "t", (M, r))
     if need_dx:
-        dx = torch.empty((M, w.K), dtype=w.dtype, device=x.device) if dx is None else \
+        dx = _empty((M, w.K), dtype=w.dtype, device=x.device) if dx is None else \
             _dev(dx, w.dtype, "dx", (M, w.K))
     else:
         dx = None
-    dA = torch.empty((w.K // g, r), dtype=torch.float32, device=x.device) if dA is None else \
+    dA = _empty((w.K // g, r), dtype=torch.float32, device=x.device) if dA is None else \
         _dev(dA, torch.float32, "dA", (w.K // g, r))
-    dB = torch.empty((r, w.N), dtype=torch.float32, device=x.device) if dB is None else \
+    dB = _empty((r, w.N), dtype=torch.float32, device=x.device) if dB is None else \
         _dev(dB, torch.float32, "dB", (r, w.N))
     wsb, wsn = _ws(int(lib.qlora_pooled_bwd_workspace(M, w.N, w.K, r, g)), x.device, ws)
     st = w.state()

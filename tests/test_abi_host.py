@@ -116,6 +116,11 @@ def test_merge_argument_errors(q):
     assert f(st, FAKE, FAKE, 8, 16.0, None, None) == INVALID
     assert f(st, FAKE, FAKE + 2, 8, 16.0, FAKE, None) == MISALIGNED
     assert f(ctypes.byref(_state(q, n=64, k=100)), FAKE, FAKE, 8, 16.0, FAKE, None) == SHAPE
+    # row and column counts must fit a signed 32-bit int: 2^31 itself is rejected, 2^31 - 1 is not
+    assert f(ctypes.byref(_state(q, n=1 << 31, k=128)), FAKE, FAKE, 8, 16.0, FAKE, None) == SHAPE
+    assert f(ctypes.byref(_state(q, n=64, k=1 << 31)), FAKE, FAKE, 8, 16.0, FAKE, None) == SHAPE
+    assert q.lib.qlora_dequantize(ctypes.byref(_state(q, n=1 << 31, k=64)), FAKE, None) == SHAPE
+    assert f(ctypes.byref(_state(q, n=(1 << 31) - 1, k=64)), FAKE, FAKE, 0, 16.0, FAKE, None) == INVALID
 
 
 def test_pooled_argument_errors(q):

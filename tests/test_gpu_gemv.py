@@ -106,3 +106,42 @@ def test_fused_qkv_weight_equals_separate_layers(q, M):
     e = lora.rel_err(host_f64(y), ref)
     say(f"    rel err {e:.3e}")
     assert e <= TOL
+
+
+def _shifted_activations(seed, M, K, kind):
+    """bf16 activations with a non-zero mean, as a layer sees them after a nonlinearity: N(0.5, 1), ReLU of
+    N(0, 1), SiLU of N(0, 1) (seeded normals transformed on the host, rounded to bf16)."""
+    z = bf16.to_f64(workloads.custom(seed, (M, K), 1.0))
+    if kind == "mean0.5":
+        v = z + 0.5
+    elif kind == "relu":
+        v = np.maximum(z, 0.0)
+    else:
+        v = z / (1.0 + np.exp(-z))
+    return bf16.from_f32_rne(v.astype(np.float32))
+
+
+@pytest.mark.parametrize("kind", ["mean0.5", "relu", "silu"])
+@pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (16, 4096, 4096), (1, 1024, 11008), (16, 512, 11008)])
+def test_gemv_nonzero_mean_activations(q, M, N, K, kind):
+    """With activations of non-zero mean, a weight that differs from the dequantized one by a fixed
+    per-level bias (rather than by independent roundings) adds up over K: the decode GEMV must multiply
+    by the dequantized weight RNE_16(fl32(a_hat c_q)) itself (deep dive 5.2), as the tiled forward does."""
+    import torch
+    r = 16
+    seed = 9000 + 3 * M + K
+    W = workloads.custom(seed, (N, K), 0.02)
+    x = _shifted_activations(seed + 1, M, K, kind)
+    A = workloads.custom(seed + 2, (K, r), float(1 / np.sqrt(r)))
+    B = workloads.custom(seed + 3, (r, N), 0.01)
+    alpha = 2.0 * r
+    say(f"[gemv] {kind} M={M} N={N} K={K}")
+    w = q.quantize(dev_bf16(W))
+    y, t = q.linear_fwd(w, dev_bf16(x), dev_bf16(A), dev_bf16(B), alpha)
+    torch.cuda.synchronize()
+    p, q8, a2 = nf4.quantize(W)
+    Wh = bf16.to_f64(nf4.dequantize(p, q8, a2, N, K))
+    y_ref, t_ref = lora.linear_fwd(bf16.to_f64(x), Wh, bf16.to_f64(A), bf16.to_f64(B), alpha, r)
+    ey, et = lora.rel_err(host_f64(y), y_ref), lora.rel_err(host_f64(t), t_ref)
+    say(f"    rel err y {ey:.3e}  t {et:.3e}")
+    assert ey <= TOL and et <= TOL

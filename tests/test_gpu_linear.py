@@ -4,7 +4,10 @@ Bar (normwise relative error, bf16 inputs, fp32 accumulation): y, t, dx, dA,
 dB <= 5e-3.  The oracle quantizes W itself (no GPU-produced codes are used as
 oracle input).  Small and ragged shapes are checked in full; the full-size
 workloads on sampled rows/columns of y and dx (computed one by one by the
-oracle) and in full for dA and dB.
+oracle) and in full for dA and dB; there the full y, t and dx are also checked to
+be finite everywhere, and the whole quantized state bit-exact.  Every output
+buffer starts out as NaN (tests/conftest.py), so an element that no kernel
+writes fails.
 """
 import numpy as np
 import pytest
@@ -120,6 +123,35 @@ def test_fused_gemm_bwd_dx_alone(q, M, N, K, r):
     assert e <= TOL
 
 
+@pytest.mark.parametrize("M,N,K,r", [(17, 72, 128, 8), (300, 200, 384, 16), (300, 192, 256, 16)])
+def test_bwd_dx_reads_nothing_past_dy(q, M, N, K, r):
+    """dy is the head of a larger buffer whose tail is NaN: the dx stage must read nothing past
+    dy's own M x N elements (partial column steps when N % 64 != 0, the last row panel when M % 256
+    != 0), or the NaN would reach dx through the zero weights of the padding."""
+    import torch
+    seed = 30 * M + N + K + r
+    W = workloads.custom(seed, (N, K), 0.02)
+    A = workloads.custom(seed + 2, (K, r), float(1 / np.sqrt(r)))
+    B = workloads.custom(seed + 3, (r, N), 0.01)
+    dy = workloads.custom(seed + 4, (M, N), 1.0)
+    alpha = 2.0 * r
+    say(f"[bwd dx, NaN past dy] M={M} N={N} K={K} r={r}")
+    dyf, Af, Bf = bf16.to_f64(dy), bf16.to_f64(A), bf16.to_f64(B)
+    u = bf16.from_f32_rne(((alpha / r) * (dyf @ Bf.T)).astype(np.float32))
+    big = torch.full((M * N + 4096,), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    big[: M * N].copy_(dev_bf16(dy).reshape(-1))
+    dyv = big[: M * N].view(M, N)
+    w = q.quantize(dev_bf16(W))
+    dx = q.fused_gemm_bwd_dx(w, dyv, dev_bf16(u), dev_bf16(A))
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(dx).all()), "NaN past the end of dy reached dx"
+    p, q8, a2 = nf4.quantize(W)
+    Wh = bf16.to_f64(nf4.dequantize(p, q8, a2, N, K))
+    e = lora.rel_err(host_f64(dx), dyf @ Wh + bf16.to_f64(u) @ Af.T)
+    say(f"    rel error dx {e:.3e}")
+    assert e <= TOL
+
+
 def test_recomputed_t_and_no_dx(q):
     M, N, K, r = 40, 192, 256, 16
     W = workloads.custom(1, (N, K), 0.02); x = workloads.custom(2, (M, K), 1.0)
@@ -181,8 +213,15 @@ def _check_sampled(q, cfg, layer, seed=0):
     g_t = host_f64(t[ri])
     g_dx = host_f64(dx[ri][:, torch.as_tensor(kcols, device=y.device)])
     g_dA = host_f64(dA); g_dB = host_f64(dB)
+    # every element of the full outputs was written (they start out as NaN) and is finite
+    for nm, v in (("y", y), ("t", t), ("dx", dx)):
+        assert bool(torch.isfinite(v).all()), f"{cfg} {name}: {nm} holds non-finite (or unwritten) elements"
+    g_codes, g_q8, g_a2 = w.codes.cpu().numpy(), w.q8.cpu().numpy(), w.a2.cpu().numpy()
     del w, y, t, dx, dA, dB, xd, dyd
     p, q8, a2 = nf4.quantize(W)
+    # the whole quantized state, bit for bit (deep dive 5.2, 7.2)
+    assert np.array_equal(g_codes, p) and np.array_equal(g_q8, q8), f"{cfg} {name}: codes / q8 differ"
+    assert np.array_equal(g_a2.view(np.uint32), a2.view(np.uint32)), f"{cfg} {name}: a2 differ"
     xf = bf16.to_f64(x[rows]); Af = bf16.to_f64(A); Bf = bf16.to_f64(B); dyf = bf16.to_f64(dy[rows])
     Wn = bf16.to_f64(nf4.dequantize_rows(p, q8, a2, K, ncols))          # W_hat rows for sampled outputs
     y_ref, t_ref = lora.linear_fwd(xf, Wn, Af, Bf[:, ncols], alpha, r)

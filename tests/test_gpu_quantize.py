@@ -1,9 +1,10 @@
 """Parity of qlora_quantize / qlora_dequantize (HIP) with the CPU oracle.
 
 Bar: packed codes, q8, a2 and the dequantized bf16 weight bit-exact.
-Small cases run the full oracle; the full-size weights of every workload are
-checked completely when the oracle finishes in seconds and on sampled scale
-groups otherwise (the oracle quantizes those groups on its own).
+Every case compares the whole weight: the small and ragged shapes, and the
+full-size weights of every workload, including the three 235M-weight layers of
+the 70B-like MLP (about 20 s of oracle time each).  Output buffers start out
+poisoned (tests/conftest.py), so a byte the kernel never writes cannot pass.
 """
 import numpy as np
 import pytest
@@ -91,31 +92,16 @@ def test_edge_blocks(q):
 @pytest.mark.parametrize("cfg", [workloads.UP_PROJ_M2048, workloads.BLOCK_7B])
 def test_full_size_workloads(q, cfg):
     for li, (name, N, K) in enumerate(workloads.CONFIGS[cfg]["layers"]):
-        if cfg == workloads.BLOCK_7B and li not in (0, 4, 6):                 # q, gate, down cover every shape
-            continue
         _check_full(q, workloads.weight(cfg, li), f"{cfg} {name}")
 
 
 @pytest.mark.slow
-def test_c5_sampled_groups(q):
-    """70B-like MLP weights (235M weights each): every group's a2, then sampled groups bit-exact."""
-    import torch
-    rng = np.random.default_rng(7)
-    for li, (name, N, K) in enumerate(workloads.CONFIGS[workloads.MLP_70B]["layers"]):
-        say(f"[quantize] {workloads.MLP_70B} {name} N={N} K={K} (sampled)")
-        W = workloads.weight(workloads.MLP_70B, li)
-        w = q.quantize(dev_bf16(W))
-        torch.cuda.synchronize()
-        codes = w.codes.cpu().numpy(); q8 = w.q8.cpu().numpy(); a2 = w.a2.cpu().numpy()
-        flat = W.reshape(-1)
-        ngroups = a2.size
-        for g in rng.choice(ngroups, 24, replace=False):
-            seg = flat[g * 16384:(g + 1) * 16384].reshape(1, -1)
-            rc, rq, ra = nf4.quantize(seg)
-            assert np.array_equal(codes[g * 8192:(g + 1) * 8192], rc), f"{name} group {g}"
-            assert np.array_equal(q8[g * 256:(g + 1) * 256], rq)
-            assert a2[g] == ra[0]
-        del w
+@pytest.mark.parametrize("layer", [0, 1, 2])
+def test_c5_full_layers(q, layer):
+    """70B-like MLP weights (235M weights each, deep dive 5.2 and 7.2): codes, q8, a2 and the dequantized
+    weight of the whole layer bit-exact against the oracle's full quantization of the same weight."""
+    name, N, K = workloads.CONFIGS[workloads.MLP_70B]["layers"][layer]
+    _check_full(q, workloads.weight(workloads.MLP_70B, layer), f"{workloads.MLP_70B} {name}")
 
 
 @pytest.mark.parametrize("cb,dq", [("nf4", True), ("nf4", False), ("fp4", True), ("fp4", False)])
