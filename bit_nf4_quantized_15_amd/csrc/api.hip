@@ -44,12 +44,14 @@ struct FwdWs {
     size_t part, tbuf, total;  // partial sums of t; t when the caller keeps none
 };
 inline FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int r) {
-    (void)N;
     FwdWs w{};
     const SplitPlan sp = plan_nt(M, K);
     w.part = 0;
     w.tbuf = w.part + align256((size_t)sp.splits * M * r * 4);
     w.total = w.tbuf + align256((size_t)M * r * 2);
+    // decode sizes run as one launch whose workspace starts at offset 0
+    if (gemv_supported((int)M, (int)N, (int)K, r))
+        w.total = std::max(w.total, gemv_linear_workspace((int)M, (int)N, (int)K, r));
     return w;
 }
 
@@ -250,6 +252,9 @@ qlora_status qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, 
     if (!aligned16(ws)) return QLORA_ERR_MISALIGNED;
     hipStream_t s = (hipStream_t)stream;
     const float scale = alpha / (float)r;
+    if (gemv_supported((int)M, (int)N, (int)K, r))  // decode sizes: t and y in one launch
+        return launch_gemv_linear(x, w->codes, w->q8, w->a2, cb_of(w), dt_of(w), A, B, scale, y, t_out, ws, (int)M,
+                                  (int)N, (int)K, r, s);
     float* part = reinterpret_cast<float*>(at(ws, L.part));
     uint16_t* t = t_out ? t_out : reinterpret_cast<uint16_t*>(at(ws, L.tbuf));
     if ((st = launch_nt(x, A, true, part, t, scale, (int)M, (int)K, r, dt_of(w), s)) != QLORA_OK) return st;

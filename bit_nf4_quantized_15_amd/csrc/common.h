@@ -151,12 +151,21 @@ qlora_status launch_merge(const uint8_t* codes, const uint8_t* q8, const float* 
 qlora_status launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* q8, const float* a2, int cb,
                              int dt, const uint16_t* t, const uint16_t* B, uint16_t* y, int M, int N, int K, int r,
                              hipStream_t s);
-// Decode-size forward (1 <= M <= kGemvMaxM): same result as launch_gemm_fwd.
+// Decode-size forward (1 <= M <= kGemvMaxM): the same dequantized weights as
+// launch_gemm_fwd (results differ only in the order of the fp32 sums).
 constexpr int kGemvMaxM = 16;
 bool gemv_supported(int M, int N, int K, int r);
 qlora_status launch_gemv_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* q8, const float* a2, int cb,
                              int dt, const uint16_t* t, const uint16_t* B, uint16_t* y, int M, int N, int K, int r,
                              hipStream_t s);
+// The whole decode-size layer call in one launch: t = bf16(scale x A) (also
+// stored to t_out when given) and y = x W_hat^T + t B.  ws holds the partial
+// products of x A and their publication tags (gemv_linear_workspace bytes,
+// 16-byte aligned; any initial contents).
+size_t gemv_linear_workspace(int M, int N, int K, int r);
+qlora_status launch_gemv_linear(const uint16_t* x, const uint8_t* codes, const uint8_t* q8, const float* a2, int cb,
+                                int dt, const uint16_t* A, const uint16_t* B, float scale, uint16_t* y,
+                                uint16_t* t_out, void* ws, int M, int N, int K, int r, hipStream_t s);
 qlora_status launch_gemm_bwd_dx(const uint16_t* dy, const uint8_t* codes, const uint8_t* q8, const float* a2,
                                 int cb, int dt, const uint16_t* u, const uint16_t* A, uint16_t* dx, int M, int N, int K, int r,
                                 hipStream_t s);

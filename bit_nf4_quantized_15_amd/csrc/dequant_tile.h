@@ -76,6 +76,36 @@ __device__ __forceinline__ u32x4_t deq8(const Nf4Tab& T, uint32_t d) {
                    perm_b32(hb, lb, 0x05010400u), perm_b32(hb, lb, 0x07030602u)};
 }
 
+// deq8 without the two selector interleaves: the 8 weights come out in the
+// order 1, 3, 5, 7, 0, 2, 4, 6 (odd weights from the low nibbles, then even
+// ones from the high nibbles).  A product that stages its other operand in the
+// same order within every 8 consecutive k (x_order8) saves 2 of the 27 VALU.
+// Its selectors mark the other half with bit 7 instead of bit 4 (any selector byte
+// >= 13 yields 0xFF): a high nibble's top bit is bit 7 already, which saves one
+// operation per 8 codes.
+__device__ __forceinline__ void lut4_b7(const Nf4Tab& T, uint32_t s1, uint32_t& lo, uint32_t& hi) {
+    const uint32_t s2 = s1 ^ 0x80808080u;
+    lo = perm_b32(T.lo[1], T.lo[0], s1) & perm_b32(T.lo[3], T.lo[2], s2);
+    hi = perm_b32(T.hi[1], T.hi[0], s1) & perm_b32(T.hi[3], T.hi[2], s2);
+}
+
+__device__ __forceinline__ u32x4_t deq8_oddeven(const Nf4Tab& T, uint32_t d) {
+    const uint32_t so = (d & 0x07070707u) | ((d << 4) & 0x80808080u);
+    const uint32_t se = ((d >> 4) & 0x07070707u) | (d & 0x80808080u);
+    uint32_t lo, ho, le, he;
+    lut4_b7(T, so, lo, ho);
+    lut4_b7(T, se, le, he);
+    return u32x4_t{perm_b32(ho, lo, 0x05010400u), perm_b32(ho, lo, 0x07030602u), perm_b32(he, le, 0x05010400u),
+                   perm_b32(he, le, 0x07030602u)};
+}
+
+// 8 consecutive 16-bit elements (4 dwords, element 2j in the low half of dword
+// j) reordered as 1, 3, 5, 7, 0, 2, 4, 6: the order of deq8_oddeven.
+__device__ __forceinline__ u32x4_t x_order8(u32x4_t v) {
+    return u32x4_t{perm_b32(v[1], v[0], 0x07060302u), perm_b32(v[3], v[2], 0x07060302u),
+                   perm_b32(v[1], v[0], 0x05040100u), perm_b32(v[3], v[2], 0x05040100u)};
+}
+
 // The fused forward's lane halves dequantize the same two columns: lanes 0-31
 // build the table of the first and lanes 32-63 that of the second, and
 // v_permlane32_swap hands each half the other's, so every lane ends with both.

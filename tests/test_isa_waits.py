@@ -9,9 +9,11 @@ loads were issued after it: the code tile and the scale loads the source
 places there.  A compiler that scheduled any other load into that window would
 turn the barrier into a race, so every step of every instantiation is checked.
 
-The decode GEMV waits for each group's direct code loads with explicit counts
-that assume no other load is issued after the phase's code loads; checked the
-same way.
+The decode kernels rely on the compiler's own waits; what is checked there is
+that no instantiation spills to scratch, that the streaming kernel's waits
+never drain its ring of code loads, that the cross-workgroup handshake
+of the layer call goes through device-coherent stores and loads, and that no
+kernel writes through the scalar data cache.
 """
 import os
 import re
@@ -93,20 +95,95 @@ def test_forward_steps_wait_for_exactly_their_x_tile(asm):
     assert n_kernels == 16          # scale layout x odd/even blocks x codebook x dtype
 
 
-def test_gemv_group_waits_follow_the_code_loads(asm):
-    n_kernels = 0
-    for name, body in _kernels(asm["gemv"], "nf4_gemv_kernel"):
-        n_kernels += 1
-        since_d = 0
-        seen_d = False
-        for o in _ops(body):
-            if o == "D":
-                seen_d, since_d = True, 0
-            elif o == "g":
-                since_d += 1
-            elif o[0] == "A" and seen_d:
-                assert since_d == 0, f"{name}: {since_d} register loads between the code loads and a group wait"
-    assert n_kernels == 72          # M classes x group counts x scale layout x codebook x dtype
+def _descriptor(asm, name):
+    m = re.search(r"\.amdhsa_kernel " + re.escape(name) + r"\n(.*?)\.end_amdhsa_kernel", asm, re.S)
+    assert m, name
+    return {k: int(v) for k, v in re.findall(r"\.(amdhsa_\w+) (\d+)", m.group(1))}
+
+
+def test_gemv_instantiations_keep_everything_in_registers(asm):
+    """Every decode-kernel instantiation runs without scratch memory: the phased kernel (batch-row
+    classes x scale layout x codebook x dtype x t given or computed in the launch) and the streaming
+    kernel (ring depth and tiles per pass x the same four).  The streaming kernel's static LDS is the
+    t operand, two slots of partial tiles and their counters (20 KB and at most 64 bytes); its x rows are dynamic
+    LDS."""
+    counts = {"nf4_gemv_kernel": 0, "nf4_gemv_stream_kernel": 0}
+    for kind in counts:
+        for name, _ in _kernels(asm["gemv"], kind + "I"):
+            counts[kind] += 1
+            d = _descriptor(asm["gemv"], name)
+            assert d["amdhsa_private_segment_fixed_size"] == 0, f"{name}: uses scratch"
+            if kind == "nf4_gemv_stream_kernel":
+                assert 20 * 1024 < d["amdhsa_group_segment_fixed_size"] <= 20 * 1024 + 64, f"{name}: static LDS"
+                # 8 compute waves and the helper wave: at most 3 waves on a SIMD
+                assert d["amdhsa_next_free_vgpr"] <= 168, f"{name}: {d['amdhsa_next_free_vgpr']} VGPRs"
+            else:
+                assert d["amdhsa_group_segment_fixed_size"] <= 76 * 1024, f"{name}: LDS above 76 KB"
+    assert counts == {"nf4_gemv_kernel": 80, "nf4_gemv_stream_kernel": 64}
+
+
+def test_gemv_main_loop_keeps_the_ring_in_flight(asm):
+    """The streaming kernel's block expansions (8 MFMAs each) never drain the ring of code loads: every
+    wait before or inside an expansion leaves at least one younger ring entry (4 loads with double
+    quantization, 3 without) in flight, and none is a vmcnt(0).  (The compiler's count is exact for the
+    first entry of a pass and more cautious for later ones, where the loop-carried state of its wait
+    analysis is merged; the bound checked here is the one that keeps loads overlapping the lookups.)"""
+    n = 0
+    for name, body in _kernels(asm["gemv"], "nf4_gemv_stream_kernelI"):
+        m = re.match(r".*nf4_gemv_stream_kernelILi(\d)ELi(\d)ELb(\d)", name)
+        D, dq = int(m.group(1)), m.group(3) == "1"
+        per = 4 if dq else 3
+        blocks, cur = [], []
+        for l in body:
+            if re.match(r"^\.LBB\S+:|^; %bb", l):
+                blocks.append(cur)
+                cur = []
+            else:
+                cur.append(l)
+        blocks.append(cur)
+        expand = [b for b in blocks if sum(l.startswith("v_mfma") for l in b) == 8]
+        assert len(expand) >= D, f"{name}: {len(expand)} expansion blocks"
+        for b in expand:
+            waits = [int(re.search(r"vmcnt\((\d+)\)", l).group(1)) for l in b
+                     if l.startswith("s_waitcnt") and "vmcnt" in l]
+            assert waits, f"{name}: an expansion without a wait for its ring entry"
+            assert min(waits) >= per, f"{name}: waits {waits} drain the ring"
+        n += 1
+    assert n == 64
+
+
+def test_gemv_publication_is_device_scope(asm):
+    """The layer call's decode kernels publish partial products of x A to other workgroups, which may run
+    on other XCDs with their own L2: the partials and the tag are written with device-coherent (sc1)
+    stores and read with device-coherent loads, and the poll loop sleeps between reads.  The kernels
+    that take t as an argument have no such traffic (their only waits are on other waves of the same
+    workgroup, in LDS)."""
+    n_ft = 0
+    for kind in ("nf4_gemv_kernelI", "nf4_gemv_stream_kernelI"):
+        for name, body in _kernels(asm["gemv"], kind):
+            text = "\n".join(body)
+            coherent_st = [l for l in body if l.startswith("global_store") and " sc1" in l]
+            coherent_ld = [l for l in body if l.startswith("global_load") and " sc1" in l]
+            if name.endswith("ELb1EEEvNS0_6GvArgsE"):
+                n_ft += 1
+                assert coherent_st, f"{name}: no device-coherent stores of the partials and the tag"
+                assert any(l.startswith("global_store_dwordx2") for l in coherent_st), f"{name}: no tag store"
+                assert any(l.startswith("global_load_dwordx2") for l in coherent_ld), f"{name}: no tag polls"
+                assert "s_sleep" in text, f"{name}: the poll loop does not sleep"
+            else:
+                assert not coherent_st and not coherent_ld, \
+                    f"{name}: a kernel with t given should not exchange data with other workgroups"
+    assert n_ft == 72
+
+
+def test_no_scalar_memory_writes(asm):
+    """No kernel writes through the scalar data cache (scalar stores, scalar atomics, scalar cache
+    write-back or discard): every global write is a vector store."""
+    for name in ("gemm", "gemv"):
+        for l in asm[name].split("\n"):
+            t = l.strip()
+            assert not t.startswith(("s_store", "s_buffer_store", "s_atomic", "s_buffer_atomic", "s_dcache_wb",
+                                     "s_dcache_discard")), f"{name}: {t}"
 
 
 def test_backward_steps_wait_for_their_dy_tile_before_the_barrier(asm):
