@@ -3,6 +3,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "common.h"
 #include "lora_plan.h"
@@ -73,6 +74,31 @@ inline BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int r) {
 }
 
 inline uint8_t* at(void* ws, size_t off) { return static_cast<uint8_t*>(ws) + off; }
+
+// Workspace of qlora_linear_fwd_noalloc: one fixed array per GPU, held until the process
+// ends.  In host code `scratch` names a host-side stand-in, so kernels get the device
+// address that hipGetSymbolAddress returns, taken once per device with that device
+// current.  Nothing in the workspace has to start at zero: the split partial sums are
+// written before they are read, and the decode kernel's publication tags identify
+// their launch.
+constexpr size_t kScratchBytes = QLORA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+qlora_status scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QLORA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return QLORA_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return QLORA_OK;
+}
 
 // fp32 layer: bytes of the split partial sums of one contraction (0 when it does not split)
 inline size_t f32_part(int64_t rows, int64_t cols, int64_t red) {
@@ -259,6 +285,20 @@ qlora_status qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, 
     uint16_t* t = t_out ? t_out : reinterpret_cast<uint16_t*>(at(ws, L.tbuf));
     if ((st = launch_nt(x, A, true, part, t, scale, (int)M, (int)K, r, dt_of(w), s)) != QLORA_OK) return st;
     return launch_gemm_fwd(x, w->codes, w->q8, w->a2, cb_of(w), dt_of(w), t, B, y, (int)M, (int)N, (int)K, r, s);
+}
+
+qlora_status qlora_linear_fwd_noalloc(const qlora_nf4* w, const uint16_t* x, int64_t M, const uint16_t* A,
+                                      const uint16_t* B, int r, float alpha, uint16_t* y, uint16_t* t_out,
+                                      void* stream) {
+    qlora_status st = check_state(w);
+    if (st != QLORA_OK) return st;
+    const int64_t N = w->n, K = w->k;
+    if (bad_dims(M, N, K, r) || !std::isfinite(alpha)) return QLORA_ERR_INVALID_ARG;
+    if (M == 0) return QLORA_OK;
+    if (fwd_ws(M, N, K, r).total > kScratchBytes) return QLORA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if ((st = scratch_address(&ws)) != QLORA_OK) return st;
+    return qlora_linear_fwd(w, x, M, A, B, r, alpha, y, t_out, ws, kScratchBytes, stream);
 }
 
 qlora_status qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,

@@ -56,6 +56,8 @@ def _load():
         "qlora_fwd_workspace": (c_sz, [c_i64, c_i64, c_i64, ctypes.c_int]),
         "qlora_linear_fwd": (ctypes.c_int, [P, c_vp, c_i64, c_vp, c_vp, ctypes.c_int, ctypes.c_float,
                                             c_vp, c_vp, c_vp, c_sz, c_vp]),
+        "qlora_linear_fwd_noalloc": (ctypes.c_int, [P, c_vp, c_i64, c_vp, c_vp, ctypes.c_int, ctypes.c_float,
+                                                    c_vp, c_vp, c_vp]),
         "qlora_lora_down_workspace": (c_sz, [c_i64, c_i64, ctypes.c_int]),
         "qlora_lora_down": (ctypes.c_int, [c_vp, c_i64, c_i64, c_vp, ctypes.c_int, ctypes.c_float, ctypes.c_int,
                                            c_vp, c_vp, c_sz, c_vp]),
@@ -266,6 +268,26 @@ def linear_fwd(w, x, A, B, alpha, y=None, t=None, want_t=True, ws=None):
                 else (lib.qlora_linear_fwd, "qlora_linear_fwd"))
     _check(fn(ctypes.byref(st), _ptr(x), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(y), _ptr(t), _ptr(wsb), wsn,
               _stream()), name)
+    return y, t
+
+
+def linear_fwd_noalloc(w, x, A, B, alpha, y=None, t=None, want_t=True):
+    """linear_fwd without a workspace argument (qlora_linear_fwd_noalloc): the library's fixed per-GPU
+    array serves as workspace, so the call itself allocates nothing.  Returns (y, t or None)."""
+    M, K = x.shape
+    r = A.shape[1]
+    _dev(x, w.dtype, "x", (M, w.K))
+    _dev(A, w.dtype, "A", (w.K, r))
+    _dev(B, w.dtype, "B", (r, w.N))
+    dev = x.device
+    y = _empty((M, w.N), dtype=w.dtype, device=dev) if y is None else _dev(y, w.dtype, "y", (M, w.N))
+    if want_t and t is None:
+        t = _empty((M, r), dtype=w.dtype, device=dev)
+    if t is not None:
+        _dev(t, w.dtype, "t", (M, r))
+    st = w.state()
+    _check(lib.qlora_linear_fwd_noalloc(ctypes.byref(st), _ptr(x), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(y),
+                                        _ptr(t), _stream()), "qlora_linear_fwd_noalloc")
     return y, t
 
 

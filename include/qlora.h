@@ -174,6 +174,20 @@ qlora_status qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, 
                               const uint16_t* B, int r, float alpha, uint16_t* y, uint16_t* t_out,
                               void* ws, size_t ws_bytes, void* stream);
 
+/* qlora_linear_fwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  It takes no workspace
+ * argument and allocates nothing; its workspace is a fixed array of
+ * QLORA_NOALLOC_SCRATCH_BYTES in the library's device memory, one per GPU, held until the
+ * process ends.  Same arguments (without ws), results and errors as qlora_linear_fwd,
+ * plus: sizes whose qlora_fwd_workspace() exceeds QLORA_NOALLOC_SCRATCH_BYTES ->
+ * QLORA_ERR_WORKSPACE; the device address of the array not available -> QLORA_ERR_HIP.
+ * Every call on one GPU uses the same array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and must be ordered by the caller. */
+#define QLORA_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+qlora_status qlora_linear_fwd_noalloc(const qlora_nf4* w, const uint16_t* x, int64_t M, const uint16_t* A,
+                                      const uint16_t* B, int r, float alpha, uint16_t* y, uint16_t* t_out,
+                                      void* stream);
+
 /* The two stages of qlora_linear_fwd, for callers that keep t across calls
  * or time the stages separately.  qlora_linear_fwd is exactly
  * qlora_lora_down followed by qlora_fused_gemm_fwd. */
