@@ -13,10 +13,13 @@ layer counts 2MKN (forward base) + 2MKN (dx) + 2Mr(K+N) (forward LoRA) +
 4Mr(K+N) (backward LoRA); quantization time is inside the step but adds no
 FLOP.  Extra fields: the dominant kernel of the step (the fused backward dx
 GEMM, timed on its own on the same shapes right after the timed steps)
-against the bf16 MFMA roofline, the forward GEMM likewise, the decode GEMV
-(4096x4096, M=1 and 16) against HBM bandwidth, quantize / dequantize
-bandwidth, the scale-layout / codebook / dtype variants, a dense bf16
-torch.matmul for context, and the CPU oracle timed on a bounded sample.
+against the bf16 MFMA roofline, the forward GEMM likewise, quantize /
+dequantize bandwidth, the decode forward on q_proj and fused q/k/v and gate/up
+weights against HBM bandwidth (the single-launch layer call, the GEMV kernel
+alone and a plain read of the same bytes), forward+backward of the up_proj (M=2048) and 70B-like MLP (M=8192)
+configs with the quantize rate of the latter's 704.6M weights, the
+scale-layout / codebook / dtype variants, a dense bf16 torch.matmul for
+context, and the CPU oracle timed on a bounded sample.
 
 usage: python bench.py [--gpus 1] [--steps 10] [--warmup 10] [--no-cpu-baseline]
        python bench.py --mode pmc     (a few untimed steps + a calibration copy, for rocprofv3 --pmc)
@@ -47,25 +50,37 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="skip decode / quantize / dense context lines")
-    p.add_argument("--mode", choices=["bench", "pmc"], default="bench")
+    p.add_argument("--mode", choices=["bench", "pmc", "pmc-decode"], default="bench")
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
-    p.add_argument("--pmc-kernel", choices=["fwd", "bwd_dx"], default="fwd")
+    p.add_argument("--pmc-kernel", choices=["fwd", "bwd_dx", "quantize", "gemv"], default="fwd")
+    p.add_argument("--decode-shape", choices=sorted(DECODE_SHAPES), default="gate_up")
+    p.add_argument("--decode-m", type=int, default=1)
+    p.add_argument("--pmc-counters", metavar="COUNTER_CSV",
+                   help="mean per dispatch of every counter in a rocprofv3 --pmc csv, by kernel")
     return p.parse_args()
 
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNELS = {"fwd": "nf4_gemm_fwd_kernel", "bwd_dx": "nf4_gemm_bwd_dx_kernel"}
-GEMM_SRC = os.path.join(HERE, "bit_nf4_quantized_15_amd", "csrc", "gemm.hip")
-TRAFFIC_FILES = {k: os.path.join(HERE, "profiles", f"{v}__7B_block_7_layers_M4096_r64__hbm_traffic.txt")
+KERNELS = {"fwd": "nf4_gemm_fwd_kernel", "bwd_dx": "nf4_gemm_bwd_dx_kernel", "quantize": "nf4_quantize_kernel",
+           "gemv": "nf4_gemv_stream_kernel"}
+_CSRC = os.path.join(HERE, "bit_nf4_quantized_15_amd", "csrc")
+SOURCES = {"fwd": "gemm.hip", "bwd_dx": "gemm.hip", "quantize": "quantize.hip", "gemv": "gemv.hip"}
+WORKLOAD_TAG = {"fwd": "7B_block_7_layers_M4096_r64", "bwd_dx": "7B_block_7_layers_M4096_r64",
+                "quantize": "7B_block_7_layers", "gemv": "gate_up_2x11008x4096_M1_r32"}
+TRAFFIC_FILES = {k: os.path.join(HERE, "profiles", f"{v}__{WORKLOAD_TAG[k]}__hbm_traffic.txt")
                  for k, v in KERNELS.items()}
 CALIB_BYTES = 512 << 20
+# the decode shape that the GEMV traffic summary uses: fused gate/up, M = 1
+PMC_DECODE = dict(N=22016, K=4096, r=32, M=1)
+# decode shapes of --mode pmc-decode (--decode-shape): [layer rows ...], K, r per layer
+DECODE_SHAPES = {"q_proj": ([4096], 4096, 16), "qkv": ([4096] * 3, 4096, 16), "gate_up": ([11008] * 2, 4096, 16)}
 
 
-def gemm_source_sha():
-    """sha256 of the GEMM source with comments and whitespace removed: a change of
+def gemm_source_sha(kind="fwd"):
+    """sha256 of a kernel's source with comments and whitespace removed: a change of
     the code (not of its comments) invalidates the recorded counter figures."""
     import re
-    with open(GEMM_SRC) as f:
+    with open(os.path.join(_CSRC, SOURCES[kind])) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
@@ -90,8 +105,21 @@ def bwd_dx_algorithmic_bytes(layers, M, r):
     return tot / len(layers)
 
 
+def quantize_algorithmic_bytes(layers):
+    """Per-launch HBM bytes of the quantize kernel, averaged over the layer shapes: the bf16 weight in,
+    codes, q8 and a2 out."""
+    return sum(N * K * 2 + N * K // 2 + N * K // 64 + 4 * (-(-N * K // 16384)) for _, N, K in layers) / len(layers)
+
+
 def algorithmic_bytes(kind, layers, M, r):
-    return (fwd_algorithmic_bytes if kind == "fwd" else bwd_dx_algorithmic_bytes)(layers, M, r)
+    if kind == "fwd":
+        return fwd_algorithmic_bytes(layers, M, r)
+    if kind == "bwd_dx":
+        return bwd_dx_algorithmic_bytes(layers, M, r)
+    if kind == "quantize":
+        return quantize_algorithmic_bytes(layers)
+    d = PMC_DECODE
+    return gemv_bytes(d["M"], d["N"], d["K"], d["r"]) - 2 * d["K"] * d["r"]
 
 
 def measured_traffic(kind):
@@ -100,7 +128,7 @@ def measured_traffic(kind):
     try:
         with open(TRAFFIC_FILES[kind]) as f:
             kv = dict(line.split(": ", 1) for line in f.read().splitlines() if ": " in line and not line.startswith("#"))
-        if kv.get("source_sha256", "").strip() != gemm_source_sha():
+        if kv.get("source_sha256", "").strip() != gemm_source_sha(kind):
             return None
         return float(kv["hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -108,7 +136,7 @@ def measured_traffic(kind):
 
 
 def pmc_summary(fetch_csv, write_csv, kind):
-    """Per-launch FETCH_SIZE / WRITE_SIZE of one GEMM kernel (kind fwd or bwd_dx), each scaled by
+    """Per-launch FETCH_SIZE / WRITE_SIZE of one kernel (fwd, bwd_dx, quantize or gemv), each scaled by
     the factor that makes the same counter read the calibration copy's known bytes."""
     kname = KERNELS[kind]
     import csv
@@ -120,7 +148,7 @@ def pmc_summary(fetch_csv, write_csv, kind):
             if row["Counter_Name"] == counter:
                 vals[row["Dispatch_Id"]][row["Kernel_Name"]] = vals[row["Dispatch_Id"]].get(row["Kernel_Name"], 0.0) + \
                     float(row["Counter_Value"])
-        ker = [v for d in vals.values() for k, v in d.items() if kname in k]
+        ker = [v for d in vals.values() for k, v in d.items() if kname in k and (kind != "gemv" or "false>" in k)]
         cal = [v for d in vals.values() for k, v in d.items() if "elementwise" in k]
         if not ker or not cal:
             raise SystemExit(f"{path}: no {kname} or calibration dispatch for {counter}")
@@ -133,7 +161,7 @@ def pmc_summary(fetch_csv, write_csv, kind):
     from bit_nf4_quantized_15_amd import workloads
     cfg = workloads.CONFIGS[workloads.BLOCK_7B]
     algo = algorithmic_bytes(kind, cfg["layers"], cfg["M"], cfg["r"])
-    print(f"source_sha256: {gemm_source_sha()}")
+    print(f"source_sha256: {gemm_source_sha(kind)}")
     print(f"kernel: {kname}")
     print(f"dispatches: {n_f} (FETCH run), {n_w} (WRITE run)")
     print(f"fetch_kib_per_launch_raw: {f_kib:.1f}")
@@ -148,6 +176,68 @@ def pmc_summary(fetch_csv, write_csv, kind):
     print(f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}")
     print(f"algorithmic_bytes_per_launch: {algo:.0f}")
     print(f"traffic_over_algorithmic: {(fetch_b + write_b) / algo:.3f}")
+
+
+def pmc_decode(torch, qlora, workloads, dev, to_dev, shape, M):
+    """Profiler runs of the decode forward on one shape (q_proj, fused q/k/v or fused gate/up, one LoRA
+    pair of r = 16 per layer) at M tokens: eight rotated weight copies, each through the layer call
+    (t and y in one launch) and through the GEMV kernel for a given t, then the calibration copy."""
+    rows, K, r1 = DECODE_SHAPES[shape]
+    N, r = sum(rows), r1 * len(rows)
+    W = np.concatenate([workloads.custom(9200 + i, (n, K), 0.02) for i, n in enumerate(rows)], axis=0)
+    w0 = qlora.quantize(to_dev(W))
+    copies = [qlora.NF4Weight(w0.codes.clone(), w0.q8.clone(), w0.a2.clone(), N, K) for _ in range(8)]
+    A = to_dev(workloads.custom(9210, (K, r), 0.25))
+    B = to_dev(workloads.custom(9220, (r, N), 0.01))
+    x = to_dev(workloads.custom(9231, (M, K), 1.0))
+    t = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(qlora.fwd_workspace(M, N, K, r), 256), dtype=torch.uint8, device=dev)
+    for w in copies:
+        qlora.linear_fwd(w, x, A, B, 2.0 * r, y=y, t=t, ws=ws)
+    for w in copies:
+        qlora.fused_gemm_fwd(w, x, t, B, y=y)
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.mul(src, 2.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "pmc-decode", "shape": shape, "N": N, "K": K, "r": r, "M": M,
+                      "calibration_copy_bytes": CALIB_BYTES}))
+
+
+def pmc_counters(csv_path):
+    """Mean per dispatch of every counter of a rocprofv3 --pmc csv (values of one dispatch summed over
+    the rows that carry them), for the path's kernels.  Derived where the counters are there:
+    mfma_flop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; mfma_busy_share = SQ_VALU_MFMA_BUSY_CYCLES (summed
+    over the 1024 SIMDs) / (GRBM_GUI_ACTIVE / 8 (one count per XCD, summed over the 8) x 1024);
+    lds_bank_conflict_share = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE."""
+    import csv
+    import collections
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    names = {}
+    for row in csv.DictReader(open(csv_path)):
+        per[row["Dispatch_Id"]][row["Counter_Name"]] += float(row["Counter_Value"])
+        names[row["Dispatch_Id"]] = row["Kernel_Name"]
+    groups = collections.defaultdict(list)
+    for did, vals in per.items():
+        kn = names[did]
+        for kind, kname in KERNELS.items():
+            if kname in kn:
+                variant = "t given" if kind == "gemv" and "false>" in kn else ("layer call" if kind == "gemv" else "")
+                groups[(kind, variant)].append(vals)
+    for (kind, variant), lst in sorted(groups.items()):
+        print(f"kernel: {KERNELS[kind]}{' (' + variant + ')' if variant else ''}")
+        print(f"dispatches: {len(lst)}")
+        counters = sorted({c for v in lst for c in v})
+        means = {c: sum(v.get(c, 0.0) for v in lst) / len(lst) for c in counters}
+        for c in counters:
+            print(f"  {c}: {means[c]:.1f}")
+        if means.get("SQ_INSTS_VALU_MFMA_MOPS_BF16"):
+            print(f"  mfma_flop: {means['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512:.4e}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in means and means.get("GRBM_GUI_ACTIVE"):
+            print(f"  mfma_busy_share: {means['SQ_VALU_MFMA_BUSY_CYCLES'] / (means['GRBM_GUI_ACTIVE'] / 8 * 1024):.4f}")
+        if "SQ_LDS_BANK_CONFLICT" in means and means.get("SQ_LDS_IDX_ACTIVE"):
+            print(f"  lds_bank_conflict_share: {means['SQ_LDS_BANK_CONFLICT'] / means['SQ_LDS_IDX_ACTIVE']:.4f}")
 
 
 def layer_flops(M, N, K, r):
@@ -191,6 +281,9 @@ def main():
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary, args.pmc_kernel)
         return
+    if args.pmc_counters:
+        pmc_counters(args.pmc_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path runs on one GPU and has no collectives: each GPU of a data-parallel job would run it on "
@@ -205,6 +298,10 @@ def main():
 
     def to_dev(u16):
         return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    if args.mode == "pmc-decode":
+        pmc_decode(torch, qlora, workloads, dev, to_dev, args.decode_shape, args.decode_m)
+        return
 
     # ---------------------------------------------------------------- workload: the 7B-like block
     wl = workloads.BLOCK_7B
@@ -381,50 +478,10 @@ def extras(torch, qlora, workloads, dev, to_dev, L, M, r):
     res["dequantize_q_proj"] = {"GB/s": round(dq_bytes / (dq_ms * 1e-3) / 1e9, 1), "ms": round(dq_ms, 4)}
     del out
 
-    # decode GEMV: 4096x4096 q_proj, r=16, M in {1, 16}; 64 distinct weight copies
-    # (> 2x the 256 MB Infinity Cache) rotated so that HBM, not cache, is measured
-    qd = workloads.CONFIGS[workloads.Q_PROJ_DECODE]
-    _, N2, K2 = qd["layers"][0]
-    W2 = to_dev(workloads.weight(workloads.Q_PROJ_DECODE))
-    copies = [qlora.quantize(W2) for _ in range(64)]
-    A2 = to_dev(workloads.lora_A(workloads.Q_PROJ_DECODE)); B2 = to_dev(workloads.lora_B(workloads.Q_PROJ_DECODE))
-    dec = {}
-    for Md in (1, 16):
-        xd = to_dev(workloads.activations(workloads.Q_PROJ_DECODE, M=Md))
-        td = torch.empty((Md, qd["r"]), dtype=torch.bfloat16, device=dev)
-        yd = torch.empty((Md, N2), dtype=torch.bfloat16, device=dev)
-        wsd = torch.empty(max(qlora.fwd_workspace(Md, N2, K2, qd["r"]), 256), dtype=torch.uint8, device=dev)
-        for w in copies[:4]:
-            qlora.linear_fwd(w, xd, A2, B2, qd["alpha"], y=yd, t=td, ws=wsd)
-        torch.cuda.synchronize()
-        # back-to-back launches from a captured HIP graph: the GPU time per call
-        # without Python's launch latency between calls
-        gemv_ms = graph_ms([lambda w=w: qlora.fused_gemm_fwd(w, xd, td, B2, y=yd) for w in copies])
-        call_ms = graph_ms([lambda w=w: (qlora.lora_down(xd, A2, qd["alpha"], t=td, ws=wsd),
-                                         qlora.fused_gemm_fwd(w, xd, td, B2, y=yd)) for w in copies])
-        # eager calls one at a time, host launch latency included
-        pairs = []
-        for w in copies:
-            a, b = ev(), ev()
-            a.record()
-            qlora.lora_down(xd, A2, qd["alpha"], t=td, ws=wsd)
-            qlora.fused_gemm_fwd(w, xd, td, B2, y=yd)
-            b.record()
-            pairs.append((a, b))
-        torch.cuda.synchronize()
-        eager_ms = float(np.median([p.elapsed_time(q) for p, q in pairs]))
-        nb = gemv_bytes(Md, N2, K2, qd["r"])
-        nb_gemv = nb - 2 * K2 * qd["r"]  # A is read by the down-projection, not by the GEMV kernel
-        dec[f"M={Md}"] = {"bytes_fwd_call": nb, "bytes_gemv_kernel": nb_gemv,
-                          "gemv_kernel_us": round(gemv_ms * 1e3, 2), "fwd_call_us": round(call_ms * 1e3, 2),
-                          "eager_fwd_call_us": round(eager_ms * 1e3, 2),
-                          "GB/s_gemv_kernel": round(nb_gemv / (gemv_ms * 1e-3) / 1e9, 1),
-                          "frac_of_hbm_peak_gemv_kernel": round(nb_gemv / (gemv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                          "GB/s_fwd_call": round(nb / (call_ms * 1e-3) / 1e9, 1)}
-    res["decode_gemv_q_proj_4096x4096_r16"] = dec
-    del copies
-    res["decode_gemv_fused_weights"] = extras_fused_decode(torch, qlora, workloads, dev, to_dev)
+    res["decode"] = extras_decode(torch, qlora, workloads, dev, to_dev)
 
+    res["up_proj_M2048_fwd_bwd"] = extras_train(torch, qlora, workloads, dev, to_dev, workloads.UP_PROJ_M2048, 10)
+    res["mlp_70b_M8192_fwd_bwd"] = extras_train(torch, qlora, workloads, dev, to_dev, workloads.MLP_70B, 3)
     res["double_quant_off"] = extras_variant(torch, qlora, workloads, dev, to_dev, L, M, r, ev, double_quant=False)
     res["fp4"] = extras_variant(torch, qlora, workloads, dev, to_dev, L, M, r, ev, quant_type="fp4")
     res["fp16_compute"] = extras_variant(torch, qlora, workloads, dev, to_dev, L, M, r, ev, dtype=torch.float16)
@@ -468,41 +525,152 @@ def extras(torch, qlora, workloads, dev, to_dev, L, M, r):
     return res
 
 
-def extras_fused_decode(torch, qlora, workloads, dev, to_dev):
-    """Decode GEMV on fused weights.  q/k/v (and gate/up) read the same x, so their weights concatenated
-    along N are one NF4 weight (K = 4096: a row holds 64 blocks and a scale group 4 rows, so no group spans
-    two layers and the codes and scales equal those of the separate weights).  Each layer keeps its own
-    r = 16 LoRA pair: A concatenated along r, B block-diagonal (its zero blocks add exact zeros).  One GEMV
-    launch then streams 3x (2.7x) the bytes of q_proj alone.  Weight copies rotated past the 256 MB
-    Infinity Cache, launches replayed from a HIP graph, as for q_proj."""
+def plain_read_us(torch, qlora, nbytes, dev):
+    """Same-size ceiling for a decode launch: the library's plain-read probe (qlora_read_probe, coalesced
+    16-byte loads and nothing else) over nbytes, the faster of its two launch shapes, over buffers
+    rotated past the 256 MB Infinity Cache, replayed from a HIP graph."""
+    n = max(4, -(-600_000_000 // nbytes))
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(n)]
+    sink = torch.zeros(1 << 20, dtype=torch.int32, device=dev)
+    best = None
+    for variant in (0, 1):
+        ms = graph_ms([lambda b=b: qlora.read_probe(b, sink, variant) for b in bufs])
+        best = ms if best is None else min(best, ms)
+    del bufs
+    return best * 1e3
+
+
+def extras_decode(torch, qlora, workloads, dev, to_dev):
+    """Decode forward (M = 1 and 16 tokens) on three weights: the 4096x4096 q_proj (r = 16, 0.1 % outliers)
+    and fused q/k/v (3x4096x4096) and gate/up (2x11008x4096) weights.  q/k/v (and gate/up) read the same x,
+    so their weights concatenated along N are one NF4 weight (K = 4096: a row holds 64 blocks and a scale
+    group 4 rows, so no group spans two layers and the codes and scales equal those of the separate
+    weights).  Each layer keeps its own r = 16 LoRA pair: A concatenated along r, B block-diagonal (its zero
+    blocks add exact zeros).  For each: the layer call qlora_linear_fwd (t = s x A and y in one launch), the
+    GEMV kernel alone for a given t (qlora_fused_gemm_fwd), and a plain read of the kernel's bytes as the
+    same-size ceiling.  Weight copies rotated past the 256 MB Infinity Cache, launches replayed from a HIP
+    graph (GPU time per call without host launch latency)."""
     out = {}
     K, r1 = 4096, 16
-    for name, Ns, seed in (("qkv_3x4096x4096", [4096, 4096, 4096], 9100), ("gate_up_2x11008x4096", [11008, 11008], 9200)):
+    qd = workloads.CONFIGS[workloads.Q_PROJ_DECODE]
+    shapes = (("q_proj_4096x4096_r16", [4096], None), ("qkv_3x4096x4096", [4096, 4096, 4096], 9100),
+              ("gate_up_2x11008x4096", [11008, 11008], 9200))
+    for name, Ns, seed in shapes:
         N, r = sum(Ns), r1 * len(Ns)
-        W = np.concatenate([workloads.custom(seed + i, (n, K), 0.02) for i, n in enumerate(Ns)], axis=0)
+        if seed is None:      # the q_proj decode config itself
+            W = workloads.weight(workloads.Q_PROJ_DECODE)
+            A = to_dev(workloads.lora_A(workloads.Q_PROJ_DECODE))
+            Bbd = to_dev(workloads.lora_B(workloads.Q_PROJ_DECODE))
+            alpha = qd["alpha"]
+        else:
+            W = np.concatenate([workloads.custom(seed + i, (n, K), 0.02) for i, n in enumerate(Ns)], axis=0)
+            A = to_dev(np.concatenate([workloads.custom(seed + 10 + i, (K, r1), 0.25) for i in range(len(Ns))],
+                                      axis=1))
+            Bbd = torch.zeros((r, N), dtype=torch.bfloat16, device=dev)
+            n0 = 0
+            for i, n in enumerate(Ns):
+                Bbd[r1 * i:r1 * (i + 1), n0:n0 + n] = to_dev(workloads.custom(seed + 20 + i, (r1, n), 0.01))
+                n0 += n
+            alpha = 2.0 * r
         w0 = qlora.quantize(to_dev(W))
         del W
         ncopy = max(4, -(-600_000_000 // (N * K // 2)))
         copies = [qlora.NF4Weight(w0.codes.clone(), w0.q8.clone(), w0.a2.clone(), N, K) for _ in range(ncopy)]
-        A = to_dev(np.concatenate([workloads.custom(seed + 10 + i, (K, r1), 0.25) for i in range(len(Ns))], axis=1))
-        Bbd = torch.zeros((r, N), dtype=torch.bfloat16, device=dev)
-        n0 = 0
-        for i, n in enumerate(Ns):
-            Bbd[r1 * i:r1 * (i + 1), n0:n0 + n] = to_dev(workloads.custom(seed + 20 + i, (r1, n), 0.01))
-            n0 += n
         res = {}
         for Md in (1, 16):
-            xd = to_dev(workloads.custom(seed + 30 + Md, (Md, K), 1.0))
-            td = qlora.lora_down(xd, A, 32.0)
+            xd = to_dev(workloads.activations(workloads.Q_PROJ_DECODE, M=Md)) if seed is None else \
+                to_dev(workloads.custom(seed + 30 + Md, (Md, K), 1.0))
+            td = torch.empty((Md, r), dtype=torch.bfloat16, device=dev)
             yd = torch.empty((Md, N), dtype=torch.bfloat16, device=dev)
-            ms = graph_ms([lambda w=w: qlora.fused_gemm_fwd(w, xd, td, Bbd, y=yd) for w in copies])
-            nb = gemv_bytes(Md, N, K, r) - 2 * K * r
-            res[f"M={Md}"] = {"gemv_kernel_us": round(ms * 1e3, 2), "bytes_gemv_kernel": nb,
-                              "GB/s_gemv_kernel": round(nb / (ms * 1e-3) / 1e9, 1),
-                              "frac_of_hbm_peak_gemv_kernel": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            ws = torch.empty(max(qlora.fwd_workspace(Md, N, K, r), 256), dtype=torch.uint8, device=dev)
+            for w in copies[:4]:
+                qlora.linear_fwd(w, xd, A, Bbd, alpha, y=yd, t=td, ws=ws)
+            torch.cuda.synchronize()
+            k_ms = graph_ms([lambda w=w: qlora.fused_gemm_fwd(w, xd, td, Bbd, y=yd) for w in copies])
+            c_ms = graph_ms([lambda w=w: qlora.linear_fwd(w, xd, A, Bbd, alpha, y=yd, t=td, ws=ws) for w in copies])
+            nb_call = gemv_bytes(Md, N, K, r)
+            nb_kernel = nb_call - 2 * K * r        # A is read by the call's producers, not by the GEMV tiles
+            ceil_us = plain_read_us(torch, qlora, nb_call, dev)
+            res[f"M={Md}"] = {
+                "fwd_call_us": round(c_ms * 1e3, 2), "gemv_kernel_us": round(k_ms * 1e3, 2),
+                "call_over_kernel": round(c_ms / k_ms, 3),
+                "bytes_fwd_call": nb_call, "bytes_gemv_kernel": nb_kernel,
+                "GB/s_fwd_call": round(nb_call / (c_ms * 1e-3) / 1e9, 1),
+                "frac_of_hbm_peak_fwd_call": round(nb_call / (c_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "GB/s_gemv_kernel": round(nb_kernel / (k_ms * 1e-3) / 1e9, 1),
+                "frac_of_hbm_peak_gemv_kernel": round(nb_kernel / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "plain_read_same_bytes_us": round(ceil_us, 2),
+                "GB/s_plain_read_same_bytes": round(nb_call / (ceil_us * 1e-6) / 1e9, 1),
+                "fwd_call_over_plain_read": round(c_ms * 1e3 / ceil_us, 3)}
         out[name] = res
         del copies, w0
     return out
+
+
+def extras_train(torch, qlora, workloads, dev, to_dev, wl, steps):
+    """Forward + backward of every layer of a training config (the up_proj config, M = 2048, and the
+    70B-like MLP, M = 8192): TFLOP/s over the same algorithmic FLOP as the headline (2MKN forward base,
+    2MKN dx, 6Mr(K+N) LoRA), weights already quantized; for the 70B MLP also the quantize rate of its
+    704.6M weights (bf16 in, codes + q8 + a2 out) against HBM peak."""
+    cfg = workloads.CONFIGS[wl]
+    M, r, alpha = cfg["M"], cfg["r"], cfg["alpha"]
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    L = []
+    for li, (name, N, K) in enumerate(cfg["layers"]):
+        d = dict(N=N, K=K)
+        d["W"] = to_dev(workloads.weight(wl, li))
+        d["x"] = to_dev(workloads.activations(wl, li))
+        d["A"] = to_dev(workloads.lora_A(wl, li))
+        d["B"] = to_dev(workloads.lora_B(wl, li))
+        d["dy"] = to_dev(workloads.grad_output(wl, li))
+        d["w"] = qlora.quantize(d["W"])
+        d["t"] = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
+        d["y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        d["dx"] = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        d["dA"] = torch.empty((K, r), dtype=torch.float32, device=dev)
+        d["dB"] = torch.empty((r, N), dtype=torch.float32, device=dev)
+        L.append(d)
+    ws = torch.empty(max(max(qlora.bwd_workspace(M, d["N"], d["K"], r), qlora.fwd_workspace(M, d["N"], d["K"], r))
+                         for d in L), dtype=torch.uint8, device=dev)
+    flops = sum(4 * M * d["N"] * d["K"] + 6 * M * r * (d["N"] + d["K"]) for d in L)
+
+    def step():
+        for d in L:
+            qlora.linear_fwd(d["w"], d["x"], d["A"], d["B"], alpha, y=d["y"], t=d["t"], ws=ws)
+        for d in L:
+            qlora.linear_bwd(d["w"], d["x"], d["A"], d["B"], alpha, d["dy"], t=d["t"], dx=d["dx"], dA=d["dA"],
+                             dB=d["dB"], ws=ws)
+
+    for _ in range(2):
+        step()
+    a, b = ev(), ev()
+    a.record()
+    for _ in range(steps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    res = {"layers": [[n, N, K] for n, N, K in cfg["layers"]], "M": M, "r": r, "steps": steps,
+           "fwd_bwd_ms": round(ms, 4), "fwd_bwd_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+           "frac_of_bf16_mfma_peak": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4)}
+    if wl == workloads.MLP_70B:
+        for d in L:
+            qlora.quantize(d["W"], out=d["w"])
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(steps):
+            for d in L:
+                qlora.quantize(d["W"], out=d["w"])
+        b.record()
+        torch.cuda.synchronize()
+        q_ms = a.elapsed_time(b) / steps
+        q_bytes = sum(d["N"] * d["K"] * 2 + sum(qlora.sizes(d["N"], d["K"])) for d in L)
+        res["quantize"] = {"weights": sum(d["N"] * d["K"] for d in L), "ms": round(q_ms, 4),
+                           "GB/s": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+                           "frac_of_hbm_peak": round(q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del L, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def extras_fp32(torch, qlora, workloads, dev, L, M, r, ev):
@@ -698,7 +866,21 @@ def cpu_baseline(workloads, wl, total_flops, n_weights):
         f_s += time.perf_counter() - t0
         f_f += 4 * rows * K * N + 6 * rows * r * (K + N)
     est_s = n_weights / (q_w / q_s) + total_flops / (f_f / f_s)
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
     return {"value": round(total_flops / est_s / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads),
+            "cpu_model": cpu_model, "nproc": os.cpu_count(), "usable_cpus": usable,
             "kind": "oracle",
             "sample": (f"numpy fp64 oracle: quantize q_proj+gate_proj ({q_w} weights, {q_s:.1f} s, 1 thread) and "
                        f"fwd+bwd on {rows}/{M} token rows of those layers ({f_f / 1e9:.1f} GFLOP, {f_s:.1f} s, "

@@ -55,6 +55,9 @@ constexpr int kALd = 144;                 // producer A slice rows: 128 + 16 bf1
                                           // transposed reads of 16 lanes)
 constexpr int kASliceBytes = 64 * kALd * 2;
 constexpr int kSpinLimit = 1 << 22;       // polls of one flag before a consumer gives up
+// cache policy of a buffer load (gfx950): sc1, the device-coherent level that device-scope
+// stores and atomics use
+constexpr int kCoherentLoad = 1 << 4;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
@@ -266,25 +269,38 @@ __device__ __forceinline__ void gv_helper_t(const GvArgs& a, uint16_t* tl, bool 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     fail = __builtin_amdgcn_ballot_w64(fail) != 0;
     const int M = a.M, r = a.r, MR = M * r, P = a.P;
-    for (int i0 = 0; i0 < 16 * kTLd; i0 += 64) {
-        const int i = i0 + lane, m = i >> 7, j = i & 127;
-        uint16_t v = 0;
-        if (m < M && j < r) {
-            const float* src = a.part + m * r + j;
-            float g[16];
 #pragma unroll
-            for (int p = 0; p < 16; ++p)         // 16 independent loads (producers past P re-read the last)
-                g[p] = __hip_atomic_load(src + (size_t)min(p, P - 1) * MR, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-            float s = 0.0f;
+    for (int i = 0; i < 16 * kTLd / 64; ++i) tl[64 * i + lane] = 0;   // t past M or r is zero in the operand
+    // The partials: plain loads that read device-coherent memory (the producers wrote them
+    // with device-scope stores), a round of 4 values x 16 producers per lane in flight at
+    // once (atomic loads would go out one at a time), added in producer order.
+    const rsrc_t prs = make_rsrc(a.part, (uint32_t)((size_t)P * MR * 4));
+    for (int v0 = 0; v0 < MR; v0 += 256) {
+        float g[4][16];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int v = v0 + 64 * k + lane;
 #pragma unroll
             for (int p = 0; p < 16; ++p)
-                if (p < P) s += g[p];
-            v = (uint16_t)(pack2<DT>(a.scale * s, 0.0f) & 0xFFFFu);
-            if (fail) v = 0x7FC0u;                // NaN in bf16 and in fp16 alike
-            if (first && a.t_out) a.t_out[m * r + j] = v;
+                g[k][p] = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(
+                               prs, opq(v < MR && p < P ? 4u * (uint32_t)(p * MR + v) : 0x80000000u), 0, kCoherentLoad));
         }
-        tl[i] = v;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int v = v0 + 64 * k + lane;
+            if (v < MR) {
+                float sum = 0.0f;
+#pragma unroll
+                for (int p = 0; p < 16; ++p)
+                    if (p < P) sum += g[k][p];
+                uint16_t out = (uint16_t)(pack2<DT>(a.scale * sum, 0.0f) & 0xFFFFu);
+                if (fail) out = 0x7FC0u;          // NaN in bf16 and in fp16 alike
+                const int m = v / r, j = v - m * r;
+                tl[m * kTLd + j] = out;
+                if (first && a.t_out) a.t_out[v] = out;
+            }
+        }
     }
 }
 
@@ -847,9 +863,15 @@ SvPlan sv_plan(int M, int N, int K, int r, int P, const void* B) {
         p.lds = std::max(xbytes, P > 0 ? (size_t)kASliceBytes : (size_t)0);
         if (p.lds + kSvStaticLds > (size_t)kLdsBytes) continue;
         const int tiles = (N + kGvRows * rg - 1) / (kGvRows * rg);
-        p.gw = std::min(tiles, kCUs - P);
+        // With producers (the layer call), tile workgroups beyond 256 - P wait for a
+        // producer's CU; that costs about a tile of start-up, so the grid keeps all 256
+        // only where leaving those CUs to the producers would add a whole tile per workgroup.
+        const int g_all = std::min(tiles, kCUs), g_rest = std::min(tiles, kCUs - P);
+        const int mk_all = (tiles + g_all - 1) / g_all, mk_rest = (tiles + g_rest - 1) / g_rest;
+        const bool all = P > 0 && mk_rest > mk_all;
+        p.gw = all ? g_all : g_rest;
         // the busiest workgroup's steps, plus about half a step of per-tile work
-        const double cost = (double)((tiles + p.gw - 1) / p.gw) * (nq0 + 0.5);
+        const double cost = (all ? mk_all + 0.5 : (double)mk_rest) * (nq0 + 0.5);
         p.ok = true;
         if (!best.ok || cost < best_cost) {
             best = p;

@@ -58,6 +58,7 @@ def _load():
                                             c_vp, c_vp, c_vp, c_sz, c_vp]),
         "qlora_linear_fwd_noalloc": (ctypes.c_int, [P, c_vp, c_i64, c_vp, c_vp, ctypes.c_int, ctypes.c_float,
                                                     c_vp, c_vp, c_vp]),
+        "qlora_read_probe": (ctypes.c_int, [c_vp, c_sz, c_vp, ctypes.c_int, c_vp]),
         "qlora_lora_down_workspace": (c_sz, [c_i64, c_i64, ctypes.c_int]),
         "qlora_lora_down": (ctypes.c_int, [c_vp, c_i64, c_i64, c_vp, ctypes.c_int, ctypes.c_float, ctypes.c_int,
                                            c_vp, c_vp, c_sz, c_vp]),
@@ -289,6 +290,12 @@ def linear_fwd_noalloc(w, x, A, B, alpha, y=None, t=None, want_t=True):
     _check(lib.qlora_linear_fwd_noalloc(ctypes.byref(st), _ptr(x), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(y),
                                         _ptr(t), _stream()), "qlora_linear_fwd_noalloc")
     return y, t
+
+
+def read_probe(buf, sink, variant=0):
+    """Plain read of a device buffer (qlora_read_probe): the same-size bandwidth ceiling of the bench."""
+    _check(lib.qlora_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), variant, _stream()),
+           "qlora_read_probe")
 
 
 def lora_down(x, A, alpha, t=None, ws=None):

@@ -174,6 +174,14 @@ qlora_status qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, 
                               const uint16_t* B, int r, float alpha, uint16_t* y, uint16_t* t_out,
                               void* ws, size_t ws_bytes, void* stream);
 
+/* Measurement aid, not a step of the layer: reads `bytes` of src through registers
+ * with coalesced 16-byte loads and nothing else (one store to sink that never
+ * happens keeps the loads alive); the bench reports the decode forward next to
+ * this same-size plain read.  variant 0: 256-thread workgroups, 4 loads per lane;
+ * 1: 512 threads, 8 loads.  src and sink 16-byte aligned, 0 < bytes < 2^31,
+ * otherwise INVALID_ARG / MISALIGNED. */
+qlora_status qlora_read_probe(const void* src, size_t bytes, uint32_t* sink, int variant, void* stream);
+
 /* qlora_linear_fwd for callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc.  It takes no workspace
  * argument and allocates nothing; its workspace is a fixed array of

@@ -87,24 +87,26 @@ def test_pmc_summary_scales_by_the_calibration_copy(tmp_path, capsys):
     assert out["dispatches"].startswith("2 ")
 
 
-def test_recorded_traffic_follows_the_gemm_source(tmp_path, monkeypatch):
+def test_recorded_traffic_follows_the_kernel_source(tmp_path, monkeypatch):
     rec = tmp_path / "traffic.txt"
     monkeypatch.setitem(bench.TRAFFIC_FILES, "bwd_dx", str(rec))
-    rec.write_text(f"# header\nsource_sha256: {bench.gemm_source_sha()}\nhbm_bytes_per_launch: 123456\n")
+    rec.write_text(f"# header\nsource_sha256: {bench.gemm_source_sha('bwd_dx')}\nhbm_bytes_per_launch: 123456\n")
     assert bench.measured_traffic("bwd_dx") == 123456.0
     rec.write_text("source_sha256: " + "0" * 64 + "\nhbm_bytes_per_launch: 123456\n")
     assert bench.measured_traffic("bwd_dx") is None                       # taken on other code
     rec.unlink()
     assert bench.measured_traffic("bwd_dx") is None                       # no record
+    # each kind hashes its own source: the GEMMs gemm.hip, quantize quantize.hip, the GEMV gemv.hip
+    assert bench.gemm_source_sha("fwd") == bench.gemm_source_sha("bwd_dx") != bench.gemm_source_sha("gemv")
     # comments do not change the hash; code does
-    src = open(bench.GEMM_SRC).read()
-    sha = bench.gemm_source_sha()
-    copy = tmp_path / "gemm.hip"
-    monkeypatch.setattr(bench, "GEMM_SRC", str(copy))
+    src = open(os.path.join(bench._CSRC, bench.SOURCES["bwd_dx"])).read()
+    sha = bench.gemm_source_sha("bwd_dx")
+    monkeypatch.setattr(bench, "_CSRC", str(tmp_path))
+    copy = tmp_path / bench.SOURCES["bwd_dx"]
     copy.write_text("// a new comment\n" + src.replace("\n", "\n  ", 3) + "\n/* trailing */\n")
-    assert bench.gemm_source_sha() == sha
+    assert bench.gemm_source_sha("bwd_dx") == sha
     copy.write_text(src + "\nint extra_symbol;\n")
-    assert bench.gemm_source_sha() != sha
+    assert bench.gemm_source_sha("bwd_dx") != sha
 
 
 def test_more_than_one_gpu_is_refused():
