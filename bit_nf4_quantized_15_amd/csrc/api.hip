@@ -42,13 +42,12 @@ inline bool bad_dims(int64_t M, int64_t N, int64_t K, int r) {
 
 // Workspace carve-up.  Every piece starts on a 256-byte boundary.
 struct FwdWs {
-    size_t part, tbuf, total;  // partial sums of t; t when the caller keeps none
+    size_t part, tbuf, total;  // split sums of t; t when the caller keeps none
 };
 inline FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int r) {
     FwdWs w{};
-    const SplitPlan sp = plan_nt(M, K);
     w.part = 0;
-    w.tbuf = w.part + align256((size_t)sp.splits * M * r * 4);
+    w.tbuf = w.part + align256(nt_ws_bytes(M, K, r));
     w.total = w.tbuf + align256((size_t)M * r * 2);
     // decode sizes run as one launch whose workspace starts at offset 0
     if (gemv_supported((int)M, (int)N, (int)K, r))
@@ -57,19 +56,17 @@ inline FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int r) {
 }
 
 struct BwdWs {
-    size_t u, part, tbuf, pa, pb, total;  // u; partials of u (and of t); t; partials of dA, dB
+    size_t u, part, tbuf, pa, pb, total;  // u; split sums of u (and of t); t; split sums of dA, dB
 };
 inline BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int r) {
     BwdWs w{};
-    const SplitPlan su = plan_nt(M, N), st = plan_nt(M, K);
-    const SplitPlan sa = plan_tn(M, K, r), sb = plan_tn(M, N, r);
     const size_t mr2 = align256((size_t)M * r * 2);
     w.u = 0;
     w.part = w.u + mr2;
-    w.tbuf = w.part + align256((size_t)std::max(su.splits, st.splits) * M * r * 4);
+    w.tbuf = w.part + align256(std::max(nt_ws_bytes(M, N, r), nt_ws_bytes(M, K, r)));
     w.pa = w.tbuf + mr2;
-    w.pb = w.pa + align256((size_t)sa.splits * K * r * 4);
-    w.total = w.pb + align256((size_t)sb.splits * r * N * 4);
+    w.pb = w.pa + align256(tn_ws_bytes(M, K, r));
+    w.total = w.pb + align256(tn_ws_bytes(M, N, r));
     return w;
 }
 
@@ -79,7 +76,7 @@ inline uint8_t* at(void* ws, size_t off) { return static_cast<uint8_t*>(ws) + of
 // ends.  In host code `scratch` names a host-side stand-in, so kernels get the device
 // address that hipGetSymbolAddress returns, taken once per device with that device
 // current.  Nothing in the workspace has to start at zero: the split partial sums are
-// written before they are read, and the decode kernel's publication tags identify
+// written before they are read, and the publication tags that guard them identify
 // their launch.
 constexpr size_t kScratchBytes = QLORA_NOALLOC_SCRATCH_BYTES;
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
@@ -216,8 +213,7 @@ size_t qlora_bwd_workspace(int64_t M, int64_t N, int64_t K, int r) {
 
 size_t qlora_lora_down_workspace(int64_t M, int64_t K, int r) {
     if (bad_dims(M, 1, K, r) || M == 0 || K % kBlock) return 0;
-    const SplitPlan sp = plan_nt(M, K);
-    return align256((size_t)sp.splits * M * r * 4);
+    return align256(nt_ws_bytes(M, K, r));
 }
 
 qlora_status qlora_lora_down(const uint16_t* x, int64_t M, int64_t K, const uint16_t* A, int r, float alpha,
@@ -231,9 +227,7 @@ qlora_status qlora_lora_down(const uint16_t* x, int64_t M, int64_t K, const uint
     const size_t need = qlora_lora_down_workspace(M, K, r);
     if (!ws || ws_bytes < need) return QLORA_ERR_WORKSPACE;
     if (!aligned16(ws)) return QLORA_ERR_MISALIGNED;
-    hipStream_t s = (hipStream_t)stream;
-    float* part = reinterpret_cast<float*>(ws);
-    return launch_nt(x, A, true, part, t_out, alpha / (float)r, (int)M, (int)K, r, dt_of(dtype), s);
+    return launch_nt(x, A, true, ws, t_out, alpha / (float)r, (int)M, (int)K, r, dt_of(dtype), (hipStream_t)stream);
 }
 
 qlora_status qlora_fused_gemm_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uint16_t* t,
@@ -281,7 +275,7 @@ qlora_status qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, 
     if (gemv_supported((int)M, (int)N, (int)K, r))  // decode sizes: t and y in one launch
         return launch_gemv_linear(x, w->codes, w->q8, w->a2, cb_of(w), dt_of(w), A, B, scale, y, t_out, ws, (int)M,
                                   (int)N, (int)K, r, s);
-    float* part = reinterpret_cast<float*>(at(ws, L.part));
+    void* part = at(ws, L.part);
     uint16_t* t = t_out ? t_out : reinterpret_cast<uint16_t*>(at(ws, L.tbuf));
     if ((st = launch_nt(x, A, true, part, t, scale, (int)M, (int)K, r, dt_of(w), s)) != QLORA_OK) return st;
     return launch_gemm_fwd(x, w->codes, w->q8, w->a2, cb_of(w), dt_of(w), t, B, y, (int)M, (int)N, (int)K, r, s);
@@ -324,7 +318,7 @@ qlora_status qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, int64_t M, 
     if (!aligned16(ws)) return QLORA_ERR_MISALIGNED;
     const float scale = alpha / (float)r;
     uint16_t* u = reinterpret_cast<uint16_t*>(at(ws, L.u));
-    float* part = reinterpret_cast<float*>(at(ws, L.part));
+    void* part = at(ws, L.part);
     // u = s dy B^T  (B [r, N] is the row-major transpose of B^T)
     if ((st = launch_nt(dy, B, false, part, u, scale, (int)M, (int)N, r, dt_of(w), s)) != QLORA_OK) return st;
     if (!t) {  // recompute t = s x A
@@ -338,10 +332,10 @@ qlora_status qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, int64_t M, 
             return st;
     }
     // dA [K, r] = x^T u ; dB [r, N] = t^T dy, stored transposed from the [N, r] reduction
-    if ((st = launch_tn(x, u, reinterpret_cast<float*>(at(ws, L.pa)), dA, (int)M, (int)K, r, r, 1, dt_of(w), s)) !=
+    if ((st = launch_tn(x, u, at(ws, L.pa), dA, (int)M, (int)K, r, r, 1, dt_of(w), s)) !=
         QLORA_OK)
         return st;
-    return launch_tn(dy, t, reinterpret_cast<float*>(at(ws, L.pb)), dB, (int)M, (int)N, r, 1, N, dt_of(w), s);
+    return launch_tn(dy, t, at(ws, L.pb), dB, (int)M, (int)N, r, 1, N, dt_of(w), s);
 }
 
 // ---- fp32 compute dtype (deep dive 8.3): fp32 tensors, w_hat = fl32(a_hat * c_q)

@@ -169,11 +169,12 @@ qlora_status launch_gemv_linear(const uint16_t* x, const uint8_t* codes, const u
 qlora_status launch_gemm_bwd_dx(const uint16_t* dy, const uint8_t* codes, const uint8_t* q8, const float* a2,
                                 int cb, int dt, const uint16_t* u, const uint16_t* A, uint16_t* dx, int M, int N, int K, int r,
                                 hipStream_t s);
-// out [M, r] = bf16(scale * X [M, C] Y), Y given as Yt [r, C] or, with y_natural, as [C, r]
-qlora_status launch_nt(const uint16_t* X, const uint16_t* Y, bool y_natural, float* part, uint16_t* out, float scale,
+// out [M, r] = bf16(scale * X [M, C] Y), Y given as Yt [r, C] or, with y_natural, as [C, r];
+// ws: nt_ws_bytes(M, C, r) bytes
+qlora_status launch_nt(const uint16_t* X, const uint16_t* Y, bool y_natural, void* ws, uint16_t* out, float scale,
                        int M, int C, int r, int dt, hipStream_t s);
-// out[d * ld_d + j * ld_j] = sum_m X [M, D][m, d] * S [M, r][m, j]
-qlora_status launch_tn(const uint16_t* X, const uint16_t* S, float* part, float* out, int M, int D, int r,
+// out[d * ld_d + j * ld_j] = sum_m X [M, D][m, d] * S [M, r][m, j]; ws: tn_ws_bytes(M, D, r) bytes
+qlora_status launch_tn(const uint16_t* X, const uint16_t* S, void* ws, float* out, int M, int D, int r,
                        int64_t ld_d, int64_t ld_j, int dt, hipStream_t s);
 qlora_status launch_fill(float* out, int64_t count, float v, hipStream_t s);
 qlora_status launch_expand_pooled(const uint16_t* A, int K, int r, int g, int dt, uint16_t* out, hipStream_t s);

@@ -38,12 +38,11 @@
 // hanging.
 #include "common.h"
 #include "dequant_tile.h"
+#include "split_sync.h"
 
 namespace qlora {
 
 // 64-bit index of the dispatch packet in its queue (monotonic per queue).
-__device__ uint64_t gv_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
-
 namespace {
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -54,10 +53,6 @@ constexpr int kTLd = 128;                 // t and B^T staging: [16][128] bf16, 
 constexpr int kALd = 144;                 // producer A slice rows: 128 + 16 bf16 (distinct banks for the
                                           // transposed reads of 16 lanes)
 constexpr int kASliceBytes = 64 * kALd * 2;
-constexpr int kSpinLimit = 1 << 22;       // polls of one flag before a consumer gives up
-// cache policy of a buffer load (gfx950): sc1, the device-coherent level that device-scope
-// stores and atomics use
-constexpr int kCoherentLoad = 1 << 4;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
@@ -79,21 +74,6 @@ __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                       c, 0, 0, 0);
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
                                                    c, 0, 0, 0);
-}
-
-// splitmix64 finalizer (Steele, Lea and Flood, "Fast splittable pseudorandom
-// number generators", 2014): a bijective 64-bit mix.
-__device__ __forceinline__ uint64_t mix64(uint64_t z) {
-    z += 0x9E3779B97F4A7C15ull;
-    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-    return z ^ (z >> 31);
-}
-
-// Tag of this launch: unique per (queue, packet), identical in every workgroup.
-__device__ __forceinline__ uint64_t launch_tag() {
-    const uint64_t q = (uint64_t)reinterpret_cast<uintptr_t>(__builtin_amdgcn_queue_ptr());
-    return mix64(gv_dispatch_id() ^ mix64(q));
 }
 
 // MFMA B operand from a row-major LDS slice S[row][col] (row stride ld bf16):
@@ -213,8 +193,8 @@ __device__ __forceinline__ void gv_produce(const GvArgs& a, uint8_t* lds, uint64
         }
     }
     // lane (j, g) holds rows m = 4 g + v of column j.  Device-scope atomic stores are
-    // coherent across the XCDs' L2 caches without a cache-wide write-back; once every
-    // wave's stores have completed, one store of the tag publishes them.
+    // coherent across the XCDs' L2 caches; once every wave's stores have completed, one
+    // store of the tag publishes them.
     float* const pp = a.part + (size_t)pid * M * r;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -226,9 +206,7 @@ __device__ __forceinline__ void gv_produce(const GvArgs& a, uint8_t* lds, uint64
                 __hip_atomic_store(pp + m * r + j, pacc[u][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // this wave's payload stores have completed
-    __syncthreads();
-    if (tid == 0) __hip_atomic_store(a.flags + pid, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    publish_tag(a.flags + pid, tag);
 }
 
 // Producer dispatch (workgroups 0 .. P-1 of the layer call).
@@ -284,7 +262,7 @@ __device__ __forceinline__ void gv_helper_t(const GvArgs& a, uint16_t* tl, bool 
             for (int p = 0; p < 16; ++p)
                 g[k][p] = __builtin_bit_cast(
                     float, __builtin_amdgcn_raw_buffer_load_b32(
-                               prs, opq(v < MR && p < P ? 4u * (uint32_t)(p * MR + v) : 0x80000000u), 0, kCoherentLoad));
+                               prs, opq(v < MR && p < P ? 4u * (uint32_t)(p * MR + v) : 0x80000000u), 0, kCoherent));
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {

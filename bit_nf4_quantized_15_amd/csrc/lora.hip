@@ -14,6 +14,7 @@
 // go to a workspace and are added in a fixed order (deterministic results).
 #include "common.h"
 #include "lora_plan.h"
+#include "split_sync.h"
 
 namespace qlora {
 namespace {
@@ -70,36 +71,6 @@ __device__ __forceinline__ bf16x8 bload8(rsrc_t rs, bool ok, uint32_t elem) {
 template <int TQ>
 constexpr int slice_ld() { return 32 * TQ + 16; }
 
-// Rows [row0, row0 + MAXROWS) of src (row stride r; rows at or past row_end and
-// columns at or past r read as zero) into dst[row * slice_ld + col], all loads of
-// a batch issued before its stores.  Every row is written, so steps padded past
-// the end of a split multiply zeros.
-template <int TQ, bool VEC, int MAXROWS>
-__device__ __forceinline__ void stage_slice(uint16_t* __restrict__ dst, const uint16_t* __restrict__ src, int r,
-                                            int row0, int row_end, int tid) {
-    constexpr int kCh = 4 * TQ;  // 16-byte chunks per slice row
-    constexpr int kLd = slice_ld<TQ>();
-    constexpr int kPer = MAXROWS * kCh / 256;
-    constexpr int kBatch = kPer < 16 ? kPer : 16;
-    const rsrc_t rs = buf_rsrc(src + (int64_t)row0 * r, (uint64_t)(row_end - row0) * r * 2);
-#pragma unroll
-    for (int e0 = 0; e0 < kPer; e0 += kBatch) {
-        bf16x8 v[kBatch];
-#pragma unroll
-        for (int e = 0; e < kBatch; ++e) {
-            const int idx = tid + 256 * (e0 + e), row = idx / kCh, ch = idx % kCh;
-            const bool ok = row0 + row < row_end;
-            v[e] = VEC ? bload8(rs, ok && 8 * ch < r, (uint32_t)(row * r + 8 * ch))
-                       : load8_row<false>(src, r, row0 + row, row_end, 8 * ch, r);
-        }
-#pragma unroll
-        for (int e = 0; e < kBatch; ++e) {
-            const int idx = tid + 256 * (e0 + e), row = idx / kCh, ch = idx % kCh;
-            *reinterpret_cast<bf16x8*>(dst + row * kLd + 8 * ch) = v[e];
-        }
-    }
-}
-
 // MFMA operand of 8 consecutive slice rows row .. row+7 of column col16 + l32 % 16
 // (col16 = the 16-column group of this half-wave), from two ds_read_b64_tr_b16:
 // lane j of a 16-lane group receives element j of the 4-element row pieces
@@ -114,33 +85,102 @@ __device__ __forceinline__ bf16x8 slice_col8(const uint16_t* __restrict__ slice,
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// part[split, m, j] = sum over c in the split's range of X[m, c] * Y[c, j]
+// ---- split sums
+// Every split of a contraction but the last publishes its fp32 partial tile
+// (device-coherent stores, then the launch's tag); the workgroup of the last
+// split, which the grid places after all others (row y = splits - 1), adds the
+// published tiles in split order, its own last, and writes the outputs.  A
+// partial tile is kept in the lanes' MFMA order (wave, 32-column group q, four
+// 16-byte pieces per lane), so every store and load is a 1 KB run per wave.
+template <int TQ>
+constexpr uint32_t part_tile_floats() { return 4u * TQ * 64u * 16u; }
+
+// Returns true in the workgroup that writes the outputs, with the totals in acc.
+template <int TQ>
+__device__ __forceinline__ bool split_sum(f32x16_t (&acc)[TQ], uint64_t* __restrict__ tags, float* __restrict__ part,
+                                          int tiles, int tile, int split, int splits) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr uint32_t kFloats = part_tile_floats<TQ>();
+    const uint64_t tag = launch_tag();
+    uint64_t* const flags = tags + (size_t)tile * splits;
+    auto off = [&](int q, int v4) { return (uint32_t)((((wave * TQ + q) * 4 + v4) * 64 + lane) * 16); };
+    if (split < splits - 1) {
+        const rsrc_t rs = buf_rsrc(part + ((size_t)split * tiles + tile) * kFloats, kFloats * 4);
+#pragma unroll
+        for (int q = 0; q < TQ; ++q)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+                const u32x4_t v = {__float_as_uint(acc[q][4 * v4]), __float_as_uint(acc[q][4 * v4 + 1]),
+                                   __float_as_uint(acc[q][4 * v4 + 2]), __float_as_uint(acc[q][4 * v4 + 3])};
+                __builtin_amdgcn_raw_buffer_store_b128(v, rs, off(q, v4), 0, kCoherent);
+            }
+        publish_tag(flags + split, tag);
+        return false;
+    }
+    const int P = splits - 1;
+    const bool fail = wait_tags(flags, P, tag);
+    // kRound splits' pieces in flight at once (64 VGPRs of loads per round at TQ = 2;
+    // a round of all 8 splits measured no faster and needs 330 VGPRs)
+    constexpr int kRound = TQ == 1 ? 8 : TQ == 2 ? 4 : 2;
+    f32x16_t tot[TQ];
+#pragma unroll
+    for (int q = 0; q < TQ; ++q)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) tot[q][v] = 0.0f;
+    for (int s0 = 0; s0 < P; s0 += kRound) {
+        u32x4_t g[kRound][TQ][4];
+#pragma unroll
+        for (int k = 0; k < kRound; ++k) {
+            const int s = min(s0 + k, P - 1);
+            const bool ok = s0 + k < P;
+            const rsrc_t rs = buf_rsrc(part + ((size_t)s * tiles + tile) * kFloats, kFloats * 4);
+#pragma unroll
+            for (int q = 0; q < TQ; ++q)
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4)
+                    g[k][q][v4] = __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? off(q, v4) : 0x80000000u, 0,
+                                                                        kCoherent);
+        }
+#pragma unroll
+        for (int k = 0; k < kRound; ++k)
+#pragma unroll
+            for (int q = 0; q < TQ; ++q)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    if (s0 + k < P) tot[q][v] += __uint_as_float(g[k][q][v >> 2][v & 3]);
+    }
+#pragma unroll
+    for (int q = 0; q < TQ; ++q)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[q][v] = fail ? __builtin_nanf("") : tot[q][v] + acc[q][v];
+    return true;
+}
+
+// out[m, j] = RNE_16( s * sum over c of X[m, c] * Y[c, j] )
 // Y comes either as its rows' transpose Yt [r, C] (YNAT false: u = dy B^T with
 // B [r, N]) or in its natural layout [C, r] (YNAT true: t = x A with A [K, r]).
 // Workgroup = 4 waves = 4 tiles of 32 rows of M; TQ 32-wide tiles of j; a
-// split covers `chunk` (a multiple of 64, at most kNtMaxChunk) columns of C.
-// The split's slice of Y is staged in LDS once (Yt rows padded so that 16
-// consecutive rows start 4 banks apart; natural rows as slice_ld, read with
-// transposed loads); after that single barrier every wave streams its X rows
-// through a 4-stage register ring (16 loads of 16 B per lane in flight) with
-// no further synchronisation.  Lane half h takes columns c + 32h .. c + 32h +
-// 31 of each 64-column step (the two halves of an MFMA's k slots may map to any
-// reduction indices, as long as both operands agree).
-constexpr int kNtMaxChunk = 512;  // columns of C per split
-constexpr int kNtRing = 4;
-static_assert(2 * kNtRing * 64 == kNtMaxChunk, "two ring passes cover a split");
-
-template <int TQ, bool YNAT>
-constexpr int nt_slice_elems() {
-    return YNAT ? kNtMaxChunk * slice_ld<TQ>() : 32 * TQ * (kNtMaxChunk + 8);
-}
-
+// split covers `chunk` (a multiple of 64, at most nt_max_chunk(r)) columns of C,
+// NST >= chunk / 64 steps of 64.  The split's slice of Y (from L2) is requested
+// first, then every X load of the split at once (steps past its end read
+// zeros), so the slice's LDS stores wait only for the slice while the X stream
+// is in flight; Yt rows are padded so that 16 consecutive rows start 4 banks
+// apart, natural rows are read with transposed loads.  Lane half h takes
+// columns c + 32h .. c + 32h + 31 of each 64-column step (the two halves of an
+// MFMA's k slots may map to any reduction indices, as long as both operands
+// agree).
 template <int TQ, bool VEC, bool YNAT, int NST, int DT>
-__global__ __launch_bounds__(256) void nt_partial_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Y,
-                                                         float* __restrict__ part, int M, int C, int r, int chunk) {
-    constexpr int kLdT = kNtMaxChunk + 8;  // Yt row (bf16)
-    constexpr int kLdN = slice_ld<TQ>();   // natural row (bf16)
-    __shared__ __attribute__((aligned(16))) uint16_t ys[nt_slice_elems<TQ, YNAT>()];
+__global__ __launch_bounds__(256) void nt_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Y,
+                                                 uint64_t* __restrict__ tags, float* __restrict__ part,
+                                                 uint16_t* __restrict__ out, float scale, int M, int C, int r,
+                                                 int chunk) {
+    static_assert(NST * 64 <= (TQ == 4 ? 256 : 512), "steps beyond nt_max_chunk");
+    constexpr int kCols = NST * 64;                   // columns of C per split (at most)
+    constexpr int kLdT = kCols + 8;                   // Yt row (bf16): 16 rows start 4 banks apart
+    constexpr int kLdN = slice_ld<TQ>();              // natural row (bf16)
+    constexpr int kCh = YNAT ? 4 * TQ : kCols / 8;    // 16-byte chunks per slice row
+    constexpr int kYPer = NST * TQ;                   // slice loads per thread
+    __shared__ __attribute__((aligned(16))) uint16_t ys[YNAT ? kCols * kLdN : 32 * TQ * kLdT];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
     const int tj = l32 & 15, tg = l32 >> 4;
     const int m0 = blockIdx.x * 128 + wave * 32;
@@ -148,48 +188,44 @@ __global__ __launch_bounds__(256) void nt_partial_kernel(const uint16_t* __restr
     const int c_begin = split * chunk;
     const int c_end = min(C, c_begin + chunk);
 
-    // X ring first (the long-latency HBM stream), then the Y slice (L2).  Steps
-    // past the split's end load zeros, so no load is conditional and the waits
-    // for the ring are exact counts.
+    bf16x8 yv[kYPer];
+    if (YNAT) {
+        const rsrc_t yrs = buf_rsrc(Y + (int64_t)c_begin * r, (uint64_t)(c_end - c_begin) * r * 2);
+#pragma unroll
+        for (int e = 0; e < kYPer; ++e) {
+            const int idx = tid + 256 * e, row = idx / kCh, ch = idx % kCh;
+            yv[e] = VEC ? bload8(yrs, c_begin + row < c_end && 8 * ch < r, (uint32_t)(row * r + 8 * ch))
+                        : load8_row<false>(Y, r, c_begin + row, c_end, 8 * ch, r);
+        }
+    } else {
+        const rsrc_t yrs = buf_rsrc(Y + c_begin, ((uint64_t)r * C - c_begin) * 2);
+#pragma unroll
+        for (int e = 0; e < kYPer; ++e) {
+            const int idx = tid + 256 * e, row = idx / kCh, ch = idx % kCh;
+            const int c = c_begin + 8 * ch;
+            yv[e] = VEC ? bload8(yrs, row < r && c < c_end, (uint32_t)(row * C + 8 * ch))
+                        : load8_row<false>(Y, C, row, r, c, c_end);
+        }
+    }
     const int bm0 = blockIdx.x * 128;
     const rsrc_t xrs = buf_rsrc(X + (int64_t)bm0 * C, (uint64_t)min(128, M - bm0) * C * 2);
     const int xrow = m0 + l32;
-    bf16x8 xa[kNtRing][4];
-    auto load_x = [&](int st, bf16x8 (&dst)[4]) {
+    bf16x8 xa[NST][4];
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
         const int c = c_begin + 64 * st + 32 * h;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (VEC)
-                dst[i] = bload8(xrs, xrow < M && c + 8 * i < c_end, (uint32_t)((xrow - bm0) * C + c + 8 * i));
+                xa[st][i] = bload8(xrs, xrow < M && c + 8 * i < c_end, (uint32_t)((xrow - bm0) * C + c + 8 * i));
             else
-                dst[i] = load8_row<false>(X, C, xrow, M, c + 8 * i, c_end);
+                xa[st][i] = load8_row<false>(X, C, xrow, M, c + 8 * i, c_end);
         }
-    };
+    }
 #pragma unroll
-    for (int st = 0; st < kNtRing; ++st) load_x(st, xa[st]);
-    if (YNAT) {
-        stage_slice<TQ, VEC, kNtMaxChunk>(ys, Y, r, c_begin, c_end, tid);
-    } else {
-        // Yt slice: 32*TQ rows x 64 chunks of 16 B (zeros past r or c_end)
-        constexpr int kPer = 32 * TQ * (kNtMaxChunk / 8) / 256;
-        constexpr int kBatch = kPer < 16 ? kPer : 16;
-        const rsrc_t yrs = buf_rsrc(Y + c_begin, ((uint64_t)r * C - c_begin) * 2);
-#pragma unroll
-        for (int e0 = 0; e0 < kPer; e0 += kBatch) {
-            bf16x8 yv[kBatch];
-#pragma unroll
-            for (int e = 0; e < kBatch; ++e) {
-                const int idx = tid + 256 * (e0 + e), row = idx >> 6, ch = idx & 63;
-                const int c = c_begin + 8 * ch;
-                yv[e] = VEC ? bload8(yrs, row < r && c < c_end, (uint32_t)(row * C + 8 * ch))
-                            : load8_row<false>(Y, C, row, r, c, c_end);
-            }
-#pragma unroll
-            for (int e = 0; e < kBatch; ++e) {
-                const int idx = tid + 256 * (e0 + e), row = idx >> 6, ch = idx & 63;
-                *reinterpret_cast<bf16x8*>(&ys[row * kLdT + 8 * ch]) = yv[e];
-            }
-        }
+    for (int e = 0; e < kYPer; ++e) {
+        const int idx = tid + 256 * e, row = idx / kCh, ch = idx % kCh;
+        *reinterpret_cast<bf16x8*>(&ys[row * (YNAT ? kLdN : kLdT) + 8 * ch]) = yv[e];
     }
     __syncthreads();
 
@@ -198,19 +234,8 @@ __global__ __launch_bounds__(256) void nt_partial_kernel(const uint16_t* __restr
     for (int q = 0; q < TQ; ++q)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[q][v] = 0.0f;
-    // NST (4 or 8, at least the split's step count) steps, all unrolled: a
-    // rolled loop copies the ring registers at its back edge, which waits for
-    // the loads in flight, and an early exit lets the compiler sink the refills
-    // behind it.
 #pragma unroll
-    for (int st = 0; st < NST; ++st) {
-        const int u = st % kNtRing;
-        bf16x8 ca[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ca[i] = xa[u][i];
-        if (st + kNtRing < NST) load_x(st + kNtRing, xa[u]);
-        // keep the refill ahead of this step's MFMAs
-        __builtin_amdgcn_sched_barrier(0);
+    for (int st = 0; st < NST; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -218,10 +243,9 @@ __global__ __launch_bounds__(256) void nt_partial_kernel(const uint16_t* __restr
                 const int c = 64 * st + 32 * h + 8 * i;  // slice column of the lane's k slots
                 const bf16x8 yb = YNAT ? slice_col8(ys, kLdN, c, 32 * q + 16 * tg, tj)
                                        : *reinterpret_cast<const bf16x8*>(&ys[(32 * q + l32) * kLdT + c]);
-                acc[q] = mfma32<DT>(ca[i], yb, acc[q]);
+                acc[q] = mfma32<DT>(xa[st][i], yb, acc[q]);
             }
-    }
-    float* out = part + (int64_t)split * M * r;
+    if (!split_sum<TQ>(acc, tags, part, (int)gridDim.x, (int)blockIdx.x, split, (int)gridDim.y)) return;
 #pragma unroll
     for (int q = 0; q < TQ; ++q) {
         const int j = 32 * q + l32;
@@ -229,95 +253,75 @@ __global__ __launch_bounds__(256) void nt_partial_kernel(const uint16_t* __restr
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int m = m0 + 8 * (v >> 2) + 4 * h + (v & 3);
-            if (m < M) out[(int64_t)m * r + j] = acc[q][v];
+            if (m < M) out[(int64_t)m * r + j] = (uint16_t)(pack2<DT>(scale * acc[q][v], 0.0f) & 0xFFFFu);
         }
     }
 }
 
-// Sum over splits of part[split * count + i] for the 64 outputs i of this
-// workgroup: thread (o, g) adds splits g, g + 4, ... with 4 independent loads
-// in flight, and the 4 groups' sums meet in LDS.  (A decode-size down-
-// projection has up to 64 splits of a handful of outputs: a serial loop per
-// output would wait for one load at a time.)
-__device__ __forceinline__ float sum_splits(const float* __restrict__ part, int splits, int64_t count, int64_t i,
-                                            bool ok) {
-    __shared__ float red[4][64];
-    const int o = threadIdx.x & 63, g = threadIdx.x >> 6;
-    float acc = 0.0f;
-    if (ok) {
-        int p = g;
-        for (; p + 12 < splits; p += 16) {
-            const float v0 = part[(int64_t)p * count + i], v1 = part[(int64_t)(p + 4) * count + i];
-            const float v2 = part[(int64_t)(p + 8) * count + i], v3 = part[(int64_t)(p + 12) * count + i];
-            acc += (v0 + v1) + (v2 + v3);
-        }
-        for (; p < splits; p += 4) acc += part[(int64_t)p * count + i];
-    }
-    red[g][o] = acc;
-    __syncthreads();
-    return (red[0][o] + red[1][o]) + (red[2][o] + red[3][o]);
-}
-
-// out[m, j] = RNE_16( s * sum_split part[split, m, j] ) in the compute dtype DT;
-// 256 threads per 64 outputs
-template <int DT>
-__global__ __launch_bounds__(256) void finalize_16_kernel(const float* __restrict__ part, int splits, int M, int r,
-                                                            float s, uint16_t* __restrict__ out) {
-    const int64_t count = (int64_t)M * r;
-    const int64_t i = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
-    const float v = sum_splits(part, splits, count, i, i < count);
-    if (threadIdx.x < 64 && i < count) out[i] = (uint16_t)(pack2<DT>(s * v, 0.0f) & 0xFFFFu);
-}
-
-// part[split, d, j] = sum over m in the split's range of X[m, d] * S[m, j]
-// (S [M, r] row-major: u or t).  Workgroup = 4 waves over 128 columns d of X
-// (32 each); a split covers `chunk` (a multiple of 64, at most tn_max_chunk(r))
-// rows m.  The split's slice of S is staged in LDS once and read with
-// transposed loads as the MFMA B operand (8 consecutive m of one column j).
-// The X rows stream through a 4-stage register ring into a double-buffered
-// [64 m x 128 d] LDS tile, read back down its columns for the A operand (8
-// consecutive m per lane), also with transposed loads.
+// out[d * ld_d + j * ld_j] = sum over m of X[m, d] * S[m, j]   (fp32; S [M, r]
+// row-major: u or t).  Workgroup = 4 waves over 128 columns d of X (32 each); a
+// split covers `chunk` (a multiple of 64, at most tn_max_chunk(r)) rows m, NST
+// >= chunk / 64 steps of 64.  The split's slice of S is requested first, then
+// every X load of the split at once; the slice is read with transposed loads as
+// the MFMA B operand (8 consecutive m of one column j).  X steps go through a
+// double-buffered [64 m x 128 d] LDS tile, read back down its columns for the A
+// operand (8 consecutive m per lane), also with transposed loads.
 constexpr int kTnRows = 64, kTnCols = 128, kTnLd = kTnCols + 32;  // 320-byte rows: conflict-free transposed reads
-constexpr int kTnRing = 4;
 
-template <int TQ, bool VEC, int DT>
-__global__ __launch_bounds__(256) void tn_partial_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ S,
-                                                         float* __restrict__ part, int M, int D, int r, int chunk) {
+template <int TQ, bool VEC, int NST, int DT>
+__global__ __launch_bounds__(256) void tn_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ S,
+                                                 uint64_t* __restrict__ tags, float* __restrict__ part,
+                                                 float* __restrict__ out, int M, int D, int r, int chunk,
+                                                 int64_t ld_d, int64_t ld_j) {
     constexpr int kTnMaxChunk = TQ <= 3 ? 512 : 256;  // = tn_max_chunk(r) for r in (32 (TQ-1), 32 TQ]
+    static_assert(NST * kTnRows <= kTnMaxChunk, "steps beyond the slice");
     constexpr int kSLd = slice_ld<TQ>();
+    constexpr int kCh = 4 * TQ;                       // 16-byte chunks per slice row
+    constexpr int kSPer = NST * kTnRows * kCh / 256;  // slice loads per thread
     __shared__ __attribute__((aligned(16))) uint16_t tile[2][kTnRows * kTnLd];
-    __shared__ __attribute__((aligned(16))) uint16_t ss[kTnMaxChunk * kSLd];
+    __shared__ __attribute__((aligned(16))) uint16_t ss[NST * kTnRows * kSLd];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
     const int tj = l32 & 15, tg = l32 >> 4;
     const int d0 = blockIdx.x * kTnCols;
     const int split = blockIdx.y;
     const int m_begin = split * chunk;
     const int m_end = min(M, m_begin + chunk);
-    const int steps = (m_end - m_begin + kTnRows - 1) / kTnRows;
-    // loader: row tid/4 of a 64-row step, columns 32*(tid%4) .. +31.  As in the
-    // down-projection, the step loop runs a multiple of the ring depth (at most
-    // kTnMaxChunk / 64 steps) and padded steps load zeros: no conditional loads.
+
+    bf16x8 sv[kSPer];
+    {
+        const rsrc_t srs = buf_rsrc(S + (int64_t)m_begin * r, (uint64_t)(m_end - m_begin) * r * 2);
+#pragma unroll
+        for (int e = 0; e < kSPer; ++e) {
+            const int idx = tid + 256 * e, row = idx / kCh, ch = idx % kCh;
+            sv[e] = VEC ? bload8(srs, m_begin + row < m_end && 8 * ch < r, (uint32_t)(row * r + 8 * ch))
+                        : load8_row<false>(S, r, m_begin + row, m_end, 8 * ch, r);
+        }
+    }
+    // loader: row tid/4 of a 64-row step, columns 32*(tid%4) .. +31
     const int lr = tid >> 2, lc = (tid & 3) * 32;
     const rsrc_t xrs = buf_rsrc(X + (int64_t)m_begin * D, (uint64_t)(m_end - m_begin) * D * 2);
-    bf16x8 xr[kTnRing][4];
-    auto load_x = [&](int st, bf16x8 (&dst)[4]) {
+    bf16x8 xr[NST][4];
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
         const int m = m_begin + kTnRows * st + lr;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int d = d0 + lc + 8 * i;
             if (VEC)
-                dst[i] = bload8(xrs, m < m_end && d < D, (uint32_t)((m - m_begin) * D + d));
+                xr[st][i] = bload8(xrs, m < m_end && d < D, (uint32_t)((m - m_begin) * D + d));
             else
-                dst[i] = load8_row<false>(X, D, m, m_end, d, D);
+                xr[st][i] = load8_row<false>(X, D, m, m_end, d, D);
         }
-    };
+    }
     auto store_x = [&](const bf16x8 (&src)[4], int buf) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) *reinterpret_cast<bf16x8*>(&tile[buf][lr * kTnLd + lc + 8 * i]) = src[i];
     };
 #pragma unroll
-    for (int st = 0; st < kTnRing; ++st) load_x(st, xr[st]);
-    stage_slice<TQ, VEC, kTnMaxChunk>(ss, S, r, m_begin, m_end, tid);
+    for (int e = 0; e < kSPer; ++e) {
+        const int idx = tid + 256 * e, row = idx / kCh, ch = idx % kCh;
+        *reinterpret_cast<bf16x8*>(&ss[row * kSLd + 8 * ch]) = sv[e];
+    }
     store_x(xr[0], 0);
     __syncthreads();
 
@@ -326,30 +330,25 @@ __global__ __launch_bounds__(256) void tn_partial_kernel(const uint16_t* __restr
     for (int q = 0; q < TQ; ++q)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[q][v] = 0.0f;
-    // A operand = X^T: 8 consecutive m of column d = 32*wave + l32 of the tile
-    for (int s0 = 0; s0 < steps; s0 += kTnRing) {
+    // A operand = X^T: 8 consecutive m of column d = 32*wave + l32 of the tile.  Step
+    // st + 1 goes into the buffer step st - 1 was read from (closed by the barrier).
 #pragma unroll
-        for (int u = 0; u < kTnRing; ++u) {
-            const int st = s0 + u;
-            const int buf = u & 1;
-            // next step's rows into the other buffer (read two steps ago), and
-            // this ring slot's next load (its data went to LDS a step ago)
-            store_x(xr[(u + 1) % kTnRing], buf ^ 1);
-            load_x(st + kTnRing, xr[u]);
+    for (int st = 0; st < NST; ++st) {
+        const int buf = st & 1;
+        if (st + 1 < NST) store_x(xr[st + 1], buf ^ 1);
 #pragma unroll
-            for (int mc = 0; mc < kTnRows / 16; ++mc) {
-                const int mr = mc * 16 + 8 * h;   // tile row of this lane's first k slot
-                const bf16x8 a = slice_col8(tile[buf], kTnLd, mr, 32 * wave + 16 * tg, tj);
+        for (int mc = 0; mc < kTnRows / 16; ++mc) {
+            const int mr = mc * 16 + 8 * h;   // tile row of this lane's first k slot
+            const bf16x8 a = slice_col8(tile[buf], kTnLd, mr, 32 * wave + 16 * tg, tj);
 #pragma unroll
-                for (int q = 0; q < TQ; ++q) {
-                    const bf16x8 b = slice_col8(ss, kSLd, kTnRows * st + mr, 32 * q + 16 * tg, tj);
-                    acc[q] = mfma32<DT>(a, b, acc[q]);
-                }
+            for (int q = 0; q < TQ; ++q) {
+                const bf16x8 b = slice_col8(ss, kSLd, kTnRows * st + mr, 32 * q + 16 * tg, tj);
+                acc[q] = mfma32<DT>(a, b, acc[q]);
             }
-            __syncthreads();
         }
+        if (st + 1 < NST) __syncthreads();
     }
-    float* out = part + (int64_t)split * D * r;
+    if (!split_sum<TQ>(acc, tags, part, (int)gridDim.x, (int)blockIdx.x, split, (int)gridDim.y)) return;
 #pragma unroll
     for (int q = 0; q < TQ; ++q) {
         const int j = 32 * q + l32;
@@ -357,20 +356,8 @@ __global__ __launch_bounds__(256) void tn_partial_kernel(const uint16_t* __restr
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int d = d0 + 32 * wave + 8 * (v >> 2) + 4 * h + (v & 3);
-            if (d < D) out[(int64_t)d * r + j] = acc[q][v];
+            if (d < D) out[(int64_t)d * ld_d + (int64_t)j * ld_j] = acc[q][v];
         }
-    }
-}
-
-// out[d * ld_d + j * ld_j] = sum_split part[split, d, j]   (fp32); 256 threads per 64 outputs
-__global__ __launch_bounds__(256) void reduce_f32_kernel(const float* __restrict__ part, int splits, int D, int r,
-                                                         int64_t ld_d, int64_t ld_j, float* __restrict__ out) {
-    const int64_t count = (int64_t)D * r;
-    const int64_t i = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
-    const float v = sum_splits(part, splits, count, i, i < count);
-    if (threadIdx.x < 64 && i < count) {
-        const int64_t d = i / r, j = i - d * r;
-        out[d * ld_d + j * ld_j] = v;
     }
 }
 
@@ -408,28 +395,34 @@ inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1)
 
 }  // namespace
 
-qlora_status launch_nt(const uint16_t* X, const uint16_t* Y, bool y_natural, float* part, uint16_t* out,
-                       float scale, int M, int C, int r, int dt, hipStream_t s) {
-    const SplitPlan sp = plan_nt(M, C);
-    const dim3 grid((unsigned)((M + 127) / 128), (unsigned)sp.splits);
+// Smallest supported step count (2, 4 or 8 steps of 64) that covers a split.
+inline int steps_template(int chunk) { return chunk <= 128 ? 2 : chunk <= 256 ? 4 : 8; }
+
+qlora_status launch_nt(const uint16_t* X, const uint16_t* Y, bool y_natural, void* ws, uint16_t* out, float scale,
+                       int M, int C, int r, int dt, hipStream_t s) {
+    const SplitPlan sp = plan_nt(M, C, r);
+    const int tiles = (M + 127) / 128;
+    const dim3 grid((unsigned)tiles, (unsigned)sp.splits);
+    uint64_t* tags = static_cast<uint64_t*>(ws);
+    float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + split_tags_bytes(tiles, sp));
     // vector path: 16-byte aligned rows, and one workgroup's rows (128 of X, r of
     // Yt) under 1 GiB of buffer offsets
     const bool vec = (C % 8 == 0) && (!y_natural || r % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15u) == 0) &&
                      ((reinterpret_cast<uintptr_t>(Y) & 15u) == 0) && (int64_t)C * 128 * 2 < (int64_t(1) << 30);
-    const int tq = (r + 31) / 32;
-    const bool short_split = sp.chunk <= 64 * kNtRing;
-#define QL_NT(TQ, V, NAT)                                                                                          \
-    if (short_split) hipLaunchKernelGGL((nt_partial_kernel<TQ, V, NAT, kNtRing, DT>), grid, dim3(256), 0, s, X, Y, part, \
-                                        M, C, r, sp.chunk);                                                        \
-    else hipLaunchKernelGGL((nt_partial_kernel<TQ, V, NAT, 2 * kNtRing, DT>), grid, dim3(256), 0, s, X, Y, part, M, C, \
-                            r, sp.chunk);
-#define QL_NT2(TQ)                                    \
-    if (y_natural) {                                  \
-        if (vec) { QL_NT(TQ, true, true) } else { QL_NT(TQ, false, true) } \
-    } else {                                          \
-        if (vec) { QL_NT(TQ, true, false) } else { QL_NT(TQ, false, false) } \
+    const int tq = (r + 31) / 32, nst = steps_template(sp.chunk);
+#define QL_NT(TQ, V, NAT, NST) \
+    hipLaunchKernelGGL((nt_kernel<TQ, V, NAT, NST, DT>), grid, dim3(256), 0, s, X, Y, tags, part, out, scale, M, C, r, \
+                       sp.chunk);
+#define QL_NT1(TQ, V, NAT)                                  \
+    if (nst == 2) { QL_NT(TQ, V, NAT, 2) }                  \
+    else if (nst == 4) { QL_NT(TQ, V, NAT, 4) }             \
+    else { QL_NT(TQ, V, NAT, (TQ == 4 ? 4 : 8)) }
+#define QL_NT2(TQ)                                                               \
+    if (y_natural) {                                                             \
+        if (vec) { QL_NT1(TQ, true, true) } else { QL_NT1(TQ, false, true) }    \
+    } else {                                                                     \
+        if (vec) { QL_NT1(TQ, true, false) } else { QL_NT1(TQ, false, false) }  \
     }
-    const int64_t count = (int64_t)M * r;
     with_dt(dt, [&](auto dtc) {
         constexpr int DT = decltype(dtc)::value;
         switch (tq) {
@@ -438,38 +431,45 @@ qlora_status launch_nt(const uint16_t* X, const uint16_t* Y, bool y_natural, flo
             case 3: QL_NT2(3) break;
             default: QL_NT2(4) break;
         }
-        hipLaunchKernelGGL(finalize_16_kernel<DT>, dim3(blocks_for(count, 64)), dim3(256), 0, s, part, sp.splits, M, r,
-                           scale, out);
     });
 #undef QL_NT2
+#undef QL_NT1
 #undef QL_NT
     return launch_status();
 }
 
-qlora_status launch_tn(const uint16_t* X, const uint16_t* S, float* part, float* out, int M, int D, int r,
-                       int64_t ld_d, int64_t ld_j, int dt, hipStream_t s) {
+qlora_status launch_tn(const uint16_t* X, const uint16_t* S, void* ws, float* out, int M, int D, int r, int64_t ld_d,
+                       int64_t ld_j, int dt, hipStream_t s) {
     const SplitPlan sp = plan_tn(M, D, r);
-    const dim3 grid((unsigned)((D + kTnCols - 1) / kTnCols), (unsigned)sp.splits);
+    const int tiles = (D + kTnCols - 1) / kTnCols;
+    const dim3 grid((unsigned)tiles, (unsigned)sp.splits);
+    uint64_t* tags = static_cast<uint64_t*>(ws);
+    float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + split_tags_bytes(tiles, sp));
     // vector path: 16-byte aligned rows, and one split's rows of X under 1 GiB
     const bool vec = (D % 8 == 0) && (r % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15u) == 0) &&
                      ((reinterpret_cast<uintptr_t>(S) & 15u) == 0) && (int64_t)D * 512 * 2 < (int64_t(1) << 30);
-    const int tq = (r + 31) / 32;
-#define QL_TN(TQ)                                                                                                   \
-    if (vec) hipLaunchKernelGGL((tn_partial_kernel<TQ, true, DT>), grid, dim3(256), 0, s, X, S, part, M, D, r, sp.chunk); \
-    else hipLaunchKernelGGL((tn_partial_kernel<TQ, false, DT>), grid, dim3(256), 0, s, X, S, part, M, D, r, sp.chunk);
+    const int tq = (r + 31) / 32, nst = steps_template(sp.chunk);
+#define QL_TN(TQ, V, NST) \
+    hipLaunchKernelGGL((tn_kernel<TQ, V, NST, DT>), grid, dim3(256), 0, s, X, S, tags, part, out, M, D, r, sp.chunk, \
+                       ld_d, ld_j);
+#define QL_TN1(TQ, V)                       \
+    if (nst == 2) { QL_TN(TQ, V, 2) }       \
+    else if (nst == 4) { QL_TN(TQ, V, 4) }  \
+    else { QL_TN(TQ, V, (TQ == 4 ? 4 : 8)) }
+#define QL_TN2(TQ) \
+    if (vec) { QL_TN1(TQ, true) } else { QL_TN1(TQ, false) }
     with_dt(dt, [&](auto dtc) {
         constexpr int DT = decltype(dtc)::value;
         switch (tq) {
-            case 1: QL_TN(1) break;
-            case 2: QL_TN(2) break;
-            case 3: QL_TN(3) break;
-            default: QL_TN(4) break;
+            case 1: QL_TN2(1) break;
+            case 2: QL_TN2(2) break;
+            case 3: QL_TN2(3) break;
+            default: QL_TN2(4) break;
         }
     });
+#undef QL_TN2
+#undef QL_TN1
 #undef QL_TN
-    const int64_t count = (int64_t)D * r;
-    hipLaunchKernelGGL(reduce_f32_kernel, dim3(blocks_for(count, 64)), dim3(256), 0, s, part, sp.splits, D, r, ld_d,
-                       ld_j, out);
     return launch_status();
 }
 

@@ -110,8 +110,8 @@ def test_noalloc_forward_argument_errors(q):
     its fixed array (4 MiB) -> WORKSPACE; M = 0 -> OK without a launch."""
     f = q.lib.qlora_linear_fwd_noalloc
     st = ctypes.byref(_state(q, n=64, k=64))
-    assert q.lib.qlora_fwd_workspace(8192, 64, 64, 128) > 4 << 20
-    assert f(st, FAKE, 8192, FAKE, FAKE, 128, 1.0, FAKE, None, None) == WORKSPACE
+    assert q.lib.qlora_fwd_workspace(32768, 64, 64, 128) > 4 << 20
+    assert f(st, FAKE, 32768, FAKE, FAKE, 128, 1.0, FAKE, None, None) == WORKSPACE
     assert f(st, FAKE, 0, FAKE, FAKE, 16, 1.0, FAKE, None, None) == OK
     assert f(st, FAKE, 16, FAKE, FAKE, 0, 1.0, FAKE, None, None) == INVALID
     assert f(st, FAKE, 16, FAKE, FAKE, 16, float("inf"), FAKE, None, None) == INVALID

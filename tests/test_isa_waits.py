@@ -13,7 +13,10 @@ The decode kernels rely on the compiler's own waits; what is checked there is
 that no instantiation spills to scratch, that the streaming kernel's waits
 never drain its ring of code loads, that the cross-workgroup handshake
 of the layer call goes through device-coherent stores and loads, and that no
-kernel writes through the scalar data cache.
+kernel writes through the scalar data cache.  Every kernel that hands partial
+results to another workgroup (the decode layer call, the split sums of the
+LoRA products) must have waited for its payload stores before the tag that
+publishes them.
 """
 import os
 import re
@@ -30,10 +33,10 @@ pytestmark = pytest.mark.skipif(not os.path.exists(build.HIPCC) and shutil.which
 
 @pytest.fixture(scope="module")
 def asm(tmp_path_factory):
-    """Device assembly of gemm.hip and gemv.hip, compiled side by side with the library's flags."""
+    """Device assembly of gemm.hip, gemv.hip and lora.hip, compiled side by side with the library's flags."""
     d = tmp_path_factory.mktemp("isa")
     procs = {}
-    for name in ("gemm", "gemv"):
+    for name in ("gemm", "gemv", "lora"):
         cmd = [build.HIPCC, *[f for f in build.CFLAGS if f != "-fPIC"], "--cuda-device-only", "-S",
                os.path.join(build.CSRC, f"{name}.hip"), "-o", str(d / f"{name}.s")]
         procs[name] = subprocess.Popen(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.PIPE)
@@ -176,10 +179,43 @@ def test_gemv_publication_is_device_scope(asm):
     assert n_ft == 72
 
 
+def test_publication_waits_for_the_payload(asm):
+    """A tag store (a device-coherent 8-byte store) follows a barrier that every wave reaches only after
+    its own device-coherent payload stores have completed: between the last payload store before that
+    barrier and the barrier there is an `s_waitcnt vmcnt(0)`.  Without it the tag could reach another
+    XCD before the data it announces."""
+    counts = {}
+    for src in ("gemv", "lora"):
+        n = 0
+        for name, body in _kernels(asm[src], ""):
+            for t in (i for i, l in enumerate(body) if l.startswith("global_store_dwordx2") and " sc1" in l):
+                b = max(i for i in range(t) if body[i] == "s_barrier")
+                p = max(i for i in range(b) if body[i].startswith(("buffer_store", "global_store")) and " sc1" in body[i])
+                assert any(body[i].startswith("s_waitcnt") and "vmcnt(0)" in body[i] for i in range(p, b)), \
+                    f"{name}: the tag may overtake the payload"
+                n += 1
+            # the payload is device-coherent already: no write-back of the whole L2 per workgroup
+            assert not any(l.startswith("buffer_wbl2") for l in body), f"{name}: L2 write-back"
+        counts[src] = n
+    assert counts["gemv"] >= 72 and counts["lora"] >= 64, counts
+
+
+def test_lora_kernels_keep_everything_in_registers(asm):
+    """The LoRA products hold all of a split's loads in registers at once; no instantiation spills."""
+    n = 0
+    for kind in ("nt_kernelI", "tn_kernelI"):
+        for name, _ in _kernels(asm["lora"], kind):
+            d = _descriptor(asm["lora"], name)
+            assert d["amdhsa_private_segment_fixed_size"] == 0, f"{name}: uses scratch"
+            assert d["amdhsa_group_segment_fixed_size"] <= 160 * 1024, name
+            n += 1
+    assert n == 88 + 44, n
+
+
 def test_no_scalar_memory_writes(asm):
     """No kernel writes through the scalar data cache (scalar stores, scalar atomics, scalar cache
     write-back or discard): every global write is a vector store."""
-    for name in ("gemm", "gemv"):
+    for name in ("gemm", "gemv", "lora"):
         for l in asm[name].split("\n"):
             t = l.strip()
             assert not t.startswith(("s_store", "s_buffer_store", "s_atomic", "s_buffer_atomic", "s_dcache_wb",

@@ -43,7 +43,7 @@ def test_noalloc_matches_linear_fwd_on_two_calls(q):
 
 def test_noalloc_rejects_sizes_beyond_the_array(q):
     import torch
-    M, N, K, r = 8192, 64, 64, 128
+    M, N, K, r = 32768, 64, 64, 128
     assert q.fwd_workspace(M, N, K, r) > 4 << 20
     w = q.quantize(dev_bf16(workloads.custom(9520, (N, K), 0.02)))
     x = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda:0")
