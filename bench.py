@@ -61,7 +61,7 @@ def parse():
 
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNELS = {"fwd": "nf4_gemm_fwd_kernel", "bwd_dx": "nf4_gemm_bwd_dx_kernel", "quantize": "nf4_quantize_kernel",
+KERNELS = {"fwd": "nf4_gemm_fwd_kernel", "bwd_dx": "nf4_gemm_bwd_dx_kernel", "quantize": "nf4_quantize_batch_kernel",
            "gemv": "nf4_gemv_stream_kernel"}
 _CSRC = os.path.join(HERE, "bit_nf4_quantized_15_amd", "csrc")
 SOURCES = {"fwd": "gemm.hip", "bwd_dx": "gemm.hip", "quantize": "quantize.hip", "gemv": "gemv.hip"}
@@ -106,9 +106,9 @@ def bwd_dx_algorithmic_bytes(layers, M, r):
 
 
 def quantize_algorithmic_bytes(layers):
-    """Per-launch HBM bytes of the quantize kernel, averaged over the layer shapes: the bf16 weight in,
-    codes, q8 and a2 out."""
-    return sum(N * K * 2 + N * K // 2 + N * K // 64 + 4 * (-(-N * K // 16384)) for _, N, K in layers) / len(layers)
+    """Per-launch HBM bytes of the quantize kernel, which takes every weight of the step in one launch:
+    the bf16 weights in, codes, q8 and a2 out."""
+    return sum(N * K * 2 + N * K // 2 + N * K // 64 + 4 * (-(-N * K // 16384)) for _, N, K in layers)
 
 
 def algorithmic_bytes(kind, layers, M, r):
@@ -333,8 +333,7 @@ def main():
     timing = dict(fwd_gemm=[], bwd=[])
 
     def step(record):
-        for d in L:
-            qlora.quantize(d["W"], out=d["w"])
+        qlora.quantize_batch([d["W"] for d in L], [d["w"] for d in L])
         for d in L:
             qlora.lora_down(d["x"], d["A"], alpha, t=d["t"], ws=ws)
             if record:
@@ -450,14 +449,12 @@ def extras(torch, qlora, workloads, dev, to_dev, L, M, r):
     # quantize / dequantize of the block's weights (bytes: bf16 in + codes/q8/a2 out)
     q_bytes = sum(d["N"] * d["K"] * 2 + sum(qlora.sizes(d["N"], d["K"])) for d in L)
     for _ in range(2):
-        for d in L:
-            qlora.quantize(d["W"], out=d["w"])
+        qlora.quantize_batch([d["W"] for d in L], [d["w"] for d in L])
     a, b = ev(), ev()
     a.record()
     reps = 5
     for _ in range(reps):
-        for d in L:
-            qlora.quantize(d["W"], out=d["w"])
+        qlora.quantize_batch([d["W"] for d in L], [d["w"] for d in L])
     b.record()
     torch.cuda.synchronize()
     q_ms = a.elapsed_time(b) / reps
@@ -654,13 +651,11 @@ def extras_train(torch, qlora, workloads, dev, to_dev, wl, steps):
            "fwd_bwd_ms": round(ms, 4), "fwd_bwd_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
            "frac_of_bf16_mfma_peak": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4)}
     if wl == workloads.MLP_70B:
-        for d in L:
-            qlora.quantize(d["W"], out=d["w"])
+        qlora.quantize_batch([d["W"] for d in L], [d["w"] for d in L])
         a, b = ev(), ev()
         a.record()
         for _ in range(steps):
-            for d in L:
-                qlora.quantize(d["W"], out=d["w"])
+            qlora.quantize_batch([d["W"] for d in L], [d["w"] for d in L])
         b.record()
         torch.cuda.synchronize()
         q_ms = a.elapsed_time(b) / steps
@@ -743,8 +738,7 @@ def extras_variant(torch, qlora, workloads, dev, to_dev, L, M, r, ev, double_qua
     fwd_flops = sum(d["flops"]["fwd_gemm"] for d in L)
 
     def quant():
-        for d, w in zip(L, Wn):
-            qlora.quantize(d["W"], out=w)
+        qlora.quantize_batch([d["W"] for d in L], Wn)
 
     def fwd():
         for d, w in zip(L, Wn):

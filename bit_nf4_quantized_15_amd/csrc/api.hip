@@ -173,6 +173,42 @@ qlora_status qlora_quantize(const uint16_t* W, int64_t N, int64_t K, const qlora
                            (hipStream_t)stream);
 }
 
+qlora_status qlora_quantize_batch(const uint16_t* const* W, const qlora_nf4* out, int count, void* stream) {
+    if (count < 0 || (count > 0 && (!W || !out))) return QLORA_ERR_INVALID_ARG;
+    for (int i = 0; i < count; ++i) {
+        if (!W[i]) return QLORA_ERR_INVALID_ARG;
+        const qlora_status st = check_state(&out[i]);
+        if (st != QLORA_OK) return st;
+        if (!aligned16(W[i])) return QLORA_ERR_MISALIGNED;
+    }
+    // one launch per run of consecutive weights that share codebook, dtype and double quantization
+    for (int i0 = 0; i0 < count;) {
+        const qlora_nf4& f = out[i0];
+        int n = 1;
+        while (i0 + n < count && n < kQuantBatchMax && out[i0 + n].quant_type == f.quant_type &&
+               out[i0 + n].dtype == f.dtype && (out[i0 + n].q8 == nullptr) == (f.q8 == nullptr))
+            ++n;
+        const void* w[kQuantBatchMax];
+        int64_t nb[kQuantBatchMax];
+        uint8_t* codes[kQuantBatchMax];
+        uint8_t* q8[kQuantBatchMax];
+        float* a2[kQuantBatchMax];
+        for (int j = 0; j < n; ++j) {
+            const qlora_nf4& o = out[i0 + j];
+            w[j] = W[i0 + j];
+            nb[j] = o.n * o.k / kBlock;
+            codes[j] = o.codes;
+            q8[j] = o.q8;
+            a2[j] = o.a2;
+        }
+        const qlora_status st =
+            launch_quantize_batch(w, nb, codes, q8, a2, n, cb_of(&f), dt_of(&f), (hipStream_t)stream);
+        if (st != QLORA_OK) return st;
+        i0 += n;
+    }
+    return QLORA_OK;
+}
+
 qlora_status qlora_dequantize(const qlora_nf4* w, uint16_t* out, void* stream) {
     qlora_status st = check_state(w);
     if (st != QLORA_OK) return st;

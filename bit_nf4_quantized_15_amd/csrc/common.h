@@ -142,6 +142,11 @@ inline qlora_status launch_status() {
 // (launch_quantize also takes kDtF32: an fp32 source weight).
 qlora_status launch_quantize(const void* W, int64_t nblocks, uint8_t* codes, uint8_t* q8, float* a2, int cb,
                              int dt, hipStream_t s);
+// up to kQuantBatchMax weights of one configuration (codebook, 16-bit dtype, with or
+// without double quantization: all q8 null or none) in one launch
+constexpr int kQuantBatchMax = 16;
+qlora_status launch_quantize_batch(const void* const* W, const int64_t* nblocks, uint8_t* const* codes,
+                                   uint8_t* const* q8, float* const* a2, int count, int cb, int dt, hipStream_t s);
 qlora_status launch_dequantize(const uint8_t* codes, const uint8_t* q8, const float* a2, int cb, int dt,
                                int64_t nblocks, uint16_t* out, hipStream_t s);
 qlora_status launch_dequantize_f32(const uint8_t* codes, const uint8_t* q8, const float* a2, int cb, int64_t nblocks,

@@ -75,12 +75,11 @@ __device__ __forceinline__ float elem(const u32x4_t (&v)[NW], int i) {
     else return h16_to_f32<DT>((i & 1) ? (v[0][i >> 1] >> 16) : (v[0][i >> 1] & 0xFFFFu));
 }
 
+// Group `group` (blocks 256 group .. 256 group + 255) of one weight, by one workgroup.
 template <bool DQ, int CB, int DT>
-__global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const void* __restrict__ Wv,
-                                                                int64_t nblocks,
-                                                                uint8_t* __restrict__ codes,
-                                                                uint8_t* __restrict__ q8,
-                                                                float* __restrict__ a2) {
+__device__ __forceinline__ void quantize_group(const void* __restrict__ Wv, int64_t nblocks,
+                                               uint8_t* __restrict__ codes, uint8_t* __restrict__ q8,
+                                               float* __restrict__ a2, int64_t group) {
     __shared__ float s_amax[kSuper];
     __shared__ float s_thr[kSuper * kThrStride];
     __shared__ float s_wmax[kThreads / 64];
@@ -89,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const void* __re
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t b0 = (int64_t)blockIdx.x * kSuper;
+    const int64_t b0 = group * kSuper;
     const int nb_here = (int)min((int64_t)kSuper, nblocks - b0);
     const int sub = lane & 7;
 
@@ -193,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const void* __re
         }
         q8[b0 + tid] = (uint8_t)k;
     }
-    if (DQ && tid == 0) a2[blockIdx.x] = A2;
+    if (DQ && tid == 0) a2[group] = A2;
 
     // 4-5. codes against the true absmax, packed and stored
 #pragma unroll
@@ -225,6 +224,35 @@ __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const void* __re
             *reinterpret_cast<uint32_t*>(codes + (b0 + bl) * (kBlock / 2) + sub * 4) = packed;
         }
     }
+}
+
+template <bool DQ, int CB, int DT>
+__global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const void* __restrict__ Wv, int64_t nblocks,
+                                                                uint8_t* __restrict__ codes,
+                                                                uint8_t* __restrict__ q8, float* __restrict__ a2) {
+    quantize_group<DQ, CB, DT>(Wv, nblocks, codes, q8, a2, blockIdx.x);
+}
+
+// Several weights of one configuration in one launch: workgroup g quantizes group
+// g - first[i] of weight i, first[i] <= g < first[i + 1].  One launch keeps the
+// chip streaming across the weights (the workgroups of one weight all start at
+// once and then compute at once), and saves a launch per weight.
+struct QuantBatch {
+    const void* W[kQuantBatchMax];
+    uint8_t* codes[kQuantBatchMax];
+    uint8_t* q8[kQuantBatchMax];
+    float* a2[kQuantBatchMax];
+    int64_t nblocks[kQuantBatchMax];
+    int64_t first[kQuantBatchMax + 1];
+    int count;
+};
+
+template <bool DQ, int CB, int DT>
+__global__ __launch_bounds__(kThreads) void nf4_quantize_batch_kernel(const QuantBatch b) {
+    const int64_t g = blockIdx.x;
+    int i = 0;
+    while (i + 1 < b.count && g >= b.first[i + 1]) ++i;   // uniform: the weight of this workgroup
+    quantize_group<DQ, CB, DT>(b.W[i], b.nblocks[i], b.codes[i], b.q8[i], b.a2[i], g - b.first[i]);
 }
 
 // nf4_dequantize_kernel: 256 lanes x 8 weights = 32 blocks per workgroup.
@@ -286,6 +314,36 @@ qlora_status launch_quantize(const void* W, int64_t nblocks, uint8_t* codes, uin
     } else {
         with_cb_dt(cb, dt, go);
     }
+    return launch_status();
+}
+
+qlora_status launch_quantize_batch(const void* const* W, const int64_t* nblocks, uint8_t* const* codes,
+                                   uint8_t* const* q8, float* const* a2, int count, int cb, int dt, hipStream_t s) {
+    if (count < 1 || count > kQuantBatchMax) return QLORA_ERR_INVALID_ARG;
+    QuantBatch b{};
+    b.count = count;
+    b.first[0] = 0;
+    for (int i = 0; i < count; ++i) {
+        b.W[i] = W[i];
+        b.codes[i] = codes[i];
+        b.q8[i] = q8[i];
+        b.a2[i] = a2[i];
+        b.nblocks[i] = nblocks[i];
+        b.first[i + 1] = b.first[i] + (nblocks[i] + kSuper - 1) / kSuper;
+    }
+    const int64_t groups = b.first[count];
+    if (groups >= (int64_t(1) << 31)) return QLORA_ERR_UNSUPPORTED_SHAPE;
+    const bool dq = q8[0] != nullptr;
+    auto go = [&](auto cbc, auto dtc) {
+        constexpr int CB = decltype(cbc)::value, DT = decltype(dtc)::value;
+        if (dq)
+            hipLaunchKernelGGL((nf4_quantize_batch_kernel<true, CB, DT>), dim3((unsigned)groups), dim3(kThreads), 0,
+                               s, b);
+        else
+            hipLaunchKernelGGL((nf4_quantize_batch_kernel<false, CB, DT>), dim3((unsigned)groups), dim3(kThreads), 0,
+                               s, b);
+    };
+    with_cb_dt(cb, dt, go);
     return launch_status();
 }
 

@@ -50,6 +50,7 @@ def _load():
                                            ctypes.POINTER(c_sz)]),
         "qlora_nf4_sizes_nodq": (ctypes.c_int, [c_i64, c_i64, ctypes.POINTER(c_sz), ctypes.POINTER(c_sz)]),
         "qlora_quantize": (ctypes.c_int, [c_vp, c_i64, c_i64, P, c_vp]),
+        "qlora_quantize_batch": (ctypes.c_int, [ctypes.POINTER(c_vp), P, ctypes.c_int, c_vp]),
         "qlora_dequantize": (ctypes.c_int, [P, c_vp, c_vp]),
         "qlora_dequantize_f32": (ctypes.c_int, [P, c_vp, c_vp]),
         "qlora_merge": (ctypes.c_int, [P, c_vp, c_vp, ctypes.c_int, ctypes.c_float, c_vp, c_vp]),
@@ -199,6 +200,22 @@ def quantize(W, out=None, double_quant=True, quant_type="nf4"):
     else:
         _check(lib.qlora_quantize(_ptr(W), N, K, ctypes.byref(st), _stream()), "qlora_quantize")
     return w
+
+
+def quantize_batch(Ws, outs):
+    """Quantize bf16/fp16 device weights Ws[i] into the existing NF4Weight outs[i] (qlora_quantize_batch:
+    the results of one qlora_quantize per weight, in one launch per run of up to 16 weights that share
+    their configuration)."""
+    if len(Ws) != len(outs):
+        raise ValueError("Ws and outs differ in length")
+    for W, w in zip(Ws, outs):
+        _dtype_code(W.dtype)
+        _dev(W, w.dtype, "W", (w.N, w.K))
+    n = len(Ws)
+    ptrs = (c_vp * max(n, 1))(*[_ptr(W) for W in Ws])
+    states = (NF4State * max(n, 1))(*[w.state() for w in outs])
+    _check(lib.qlora_quantize_batch(ptrs, states, n, _stream()), "qlora_quantize_batch")
+    return outs
 
 
 def dequantize(w, out=None, fp32=False):

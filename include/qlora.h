@@ -133,6 +133,17 @@ qlora_status qlora_nf4_sizes_nodq(int64_t N, int64_t K, size_t* codes_bytes, siz
 qlora_status qlora_quantize(const uint16_t* W, int64_t N, int64_t K, const qlora_nf4* out,
                             void* stream);
 
+/* Quantize `count` bf16/fp16 weights at once (deep dive 5.2 and 7.2, as
+ * qlora_quantize): W[i] [out[i].n, out[i].k] into out[i], for i < count.
+ * `out` is an array of count states (not pointers).  The results are those of
+ * count calls of qlora_quantize; consecutive weights that share quant_type,
+ * dtype and double quantization (all q8 set or all NULL) run as one launch of
+ * up to 16 weights, so the chip streams across the weights of a training step
+ * instead of ramping up and draining once per weight.  count == 0 is a no-op.
+ * Errors: count < 0, null arrays or entries, a state qlora_quantize rejects
+ * (checked for every entry before anything is launched), misaligned W[i]. */
+qlora_status qlora_quantize_batch(const uint16_t* const* W, const qlora_nf4* out, int count, void* stream);
+
 /* Dequantize to bf16 out [N, K] (deep dive 5.2: w_hat = a * c_q):
  *   a_hat = fl32( fl32(a2_S / 255) * q8_b ) (out->q8 == NULL: a_hat = a2_b),
  *   out = RNE_bf16( fl32(a_hat * c_code) ).

@@ -73,6 +73,21 @@ def _state(q, n=64, k=64, codes=FAKE, q8=FAKE, a2=FAKE):
     return q.NF4State(codes, q8, a2, n, k)
 
 
+def test_quantize_batch_argument_errors(q):
+    """qlora_quantize_batch checks every entry before it launches anything (no device is touched here)."""
+    f = q.lib.qlora_quantize_batch
+    W = lambda *p: (ctypes.c_void_p * len(p))(*p)
+    S = lambda *s: (q.NF4State * len(s))(*s)
+    assert f(None, None, 0, None) == OK                                        # nothing to do
+    assert f(W(FAKE), S(_state(q)), -1, None) == INVALID
+    assert f(None, S(_state(q)), 1, None) == INVALID
+    assert f(W(FAKE), None, 1, None) == INVALID
+    assert f(W(FAKE, None), S(_state(q), _state(q)), 2, None) == INVALID        # a null weight
+    assert f(W(FAKE, FAKE), S(_state(q), _state(q, k=100)), 2, None) == SHAPE
+    assert f(W(FAKE, FAKE + 2), S(_state(q), _state(q)), 2, None) == MISALIGNED
+    assert f(W(FAKE, FAKE), S(_state(q), _state(q, codes=0)), 2, None) == INVALID
+
+
 def test_quantize_argument_errors(q):
     st = _state(q)
     f = q.lib.qlora_quantize

@@ -126,3 +126,30 @@ def test_dequantize_fp32_products(q, cb, dq):
     g = got.cpu().numpy()
     assert np.array_equal(g.view(np.uint32), ref.view(np.uint32)), \
         f"differs at {np.flatnonzero(g.view(np.uint32) != ref.view(np.uint32))[:8]}"
+
+
+def test_batch_matches_per_weight_quantize_and_the_oracle(q):
+    """qlora_quantize_batch: 19 weights in one call (runs of one configuration, a run split at 16
+    weights, ragged groups, NF4 and FP4, with and without double quantization, bf16 and fp16) give
+    the states of one qlora_quantize per weight, byte for byte; the first two also equal the
+    oracle's."""
+    import torch
+    shapes = [(3, 192), (257, 64), (64, 1088), (5, 640)] * 4 + [(7, 16384 + 64), (1, 64), (96, 256)]
+    cfgs = [("nf4", True, torch.bfloat16)] * 17 + [("fp4", False, torch.bfloat16), ("nf4", True, torch.float16)]
+    Ws, ref, outs = [], [], []
+    for i, ((N, K), (cb, dq, dt)) in enumerate(zip(shapes, cfgs)):
+        W = dev_bf16(workloads.custom(900 + i, (N, K), 0.02)).to(dt)
+        Ws.append(W)
+        ref.append(q.quantize(W, double_quant=dq, quant_type=cb))
+        outs.append(q.NF4Weight.empty(N, K, W.device, dq, cb, dt))
+    say(f"[quantize batch] {len(Ws)} weights")
+    q.quantize_batch(Ws, outs)
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(ref, outs)):
+        assert torch.equal(a.codes, b.codes), f"weight {i}: codes differ"
+        assert torch.equal(a.a2.view(torch.int32), b.a2.view(torch.int32)), f"weight {i}: a2 differ"
+        assert (a.q8 is None) == (b.q8 is None) and (a.q8 is None or torch.equal(a.q8, b.q8)), f"weight {i}: q8"
+    for i in range(2):
+        rc, rq, ra = nf4.quantize(workloads.custom(900 + i, shapes[i], 0.02))
+        assert np.array_equal(outs[i].codes.cpu().numpy(), rc) and np.array_equal(outs[i].q8.cpu().numpy(), rq)
+        assert np.array_equal(outs[i].a2.cpu().numpy().view(np.uint32), ra.view(np.uint32))
