@@ -276,6 +276,11 @@ def gemv_bytes(M, N, K, r, double_quant=True):
     return N * K // 2 + scales + 2 * M * K + 2 * M * N + 2 * K * r + 2 * r * N
 
 
+def progress(msg):
+    """A phase of the run, on stderr (the JSON line alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -361,9 +366,11 @@ def main():
         print(json.dumps({"mode": "pmc", "calibration_copy_bytes": CALIB_BYTES}))
         return
 
+    progress(f"inputs ready; {args.warmup} warmup steps")
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
+    progress(f"{args.steps} timed steps")
     # the headline: K steps with no events inside (an event recorded between two kernels leaves the GPU
     # idle for several microseconds)
     t_start, t_stop = ev(), ev()
@@ -377,6 +384,7 @@ def main():
     ms_step = t_start.elapsed_time(t_stop) / args.steps
     value = total_flops / (ms_step * 1e-3) / 1e12
     # the same K steps again with events around each forward GEMM and each backward call, for the breakdown
+    progress(f"step {ms_step:.4f} ms ({value:.1f} TFLOP/s); breakdown pass")
     for _ in range(args.steps):
         step(True)
     torch.cuda.synchronize()
@@ -435,9 +443,11 @@ def main():
                       "flop_per_step": total_flops},
     }
 
+    progress(f"backward dx alone {bdx_tfs:.1f} TFLOP/s")
     if not args.no_extras:
         out["extras"] = extras(torch, qlora, workloads, dev, to_dev, L, M, r)
     if not args.no_cpu_baseline:
+        progress("cpu baseline (oracle on the host)")
         out["cpu_baseline"] = cpu_baseline(workloads, wl, total_flops, n_weights)
     print(json.dumps(out))
 
@@ -475,10 +485,13 @@ def extras(torch, qlora, workloads, dev, to_dev, L, M, r):
     res["dequantize_q_proj"] = {"GB/s": round(dq_bytes / (dq_ms * 1e-3) / 1e9, 1), "ms": round(dq_ms, 4)}
     del out
 
+    progress("extras: decode")
     res["decode"] = extras_decode(torch, qlora, workloads, dev, to_dev)
 
+    progress("extras: up_proj M=2048, 70B MLP M=8192")
     res["up_proj_M2048_fwd_bwd"] = extras_train(torch, qlora, workloads, dev, to_dev, workloads.UP_PROJ_M2048, 10)
     res["mlp_70b_M8192_fwd_bwd"] = extras_train(torch, qlora, workloads, dev, to_dev, workloads.MLP_70B, 3)
+    progress("extras: double quant off, fp4, fp16, pooled, fp32")
     res["double_quant_off"] = extras_variant(torch, qlora, workloads, dev, to_dev, L, M, r, ev, double_quant=False)
     res["fp4"] = extras_variant(torch, qlora, workloads, dev, to_dev, L, M, r, ev, quant_type="fp4")
     res["fp16_compute"] = extras_variant(torch, qlora, workloads, dev, to_dev, L, M, r, ev, dtype=torch.float16)
