@@ -208,8 +208,12 @@ qlora_status qlora_linear_fwd_noalloc(const qlora_nf4* w, const uint16_t* x, int
                                       void* stream);
 
 /* The two stages of qlora_linear_fwd, for callers that keep t across calls
- * or time the stages separately.  qlora_linear_fwd is exactly
- * qlora_lora_down followed by qlora_fused_gemm_fwd. */
+ * or time the stages separately.  Given the t that qlora_linear_fwd returns,
+ * qlora_fused_gemm_fwd reproduces its y bit for bit.  Above decode sizes
+ * qlora_linear_fwd is exactly qlora_lora_down followed by qlora_fused_gemm_fwd;
+ * at decode sizes (M <= 16, where one launch computes t and y) it adds the
+ * fp32 products of x A in another order than qlora_lora_down, so its t may
+ * differ from qlora_lora_down's in the last bit. */
 
 /* Workspace bytes qlora_lora_down needs (0 for M == 0). */
 size_t qlora_lora_down_workspace(int64_t M, int64_t K, int r);

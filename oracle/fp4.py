@@ -2,6 +2,11 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
+The level values are PARITY UNPINNED BY THE PAGES: the pages give none.  The
+tests pin them to the E2M1 element's format parameters from the OCP MX
+specification (tests/golden/e2m1_mx_element.json), not to a page; the
+encoder, the scales and the packing are pinned as NF4's are.
+
 "bitsandbytes deep dive" (aicoding.csdn.net), section 6.5 and section 8.1: the
 quant type picks the codebook, i.e. what value each 4-bit code 0..15 stands
 for; "fp4" is a floating-point-style layout of 16 codes, not a uniform integer

@@ -4,9 +4,12 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).  Parity status of each
 function is stated in its docstring; every function here is pinned by a
 ``-m "not gpu"`` test in ``tests/test_oracle_nf4.py`` against something other
 than itself (the pages' numbers, closed forms, brute force, library routines).
-The one part the pages cannot pin is the interior of the NF4 table: the page's
-formula was lost in extraction, so the interior values are pinned only to the
-construction below (reading R1) and to its quantile invariants.
+The one part the pages cannot pin is the interior of the NF4 table, which is
+therefore PARITY UNPINNED BY THE PAGES: the page's formula was lost in
+extraction, so the 14 interior values are pinned only to the construction
+below (reading R1) and to its quantile invariants; the endpoints +-1, the exact
+0 and every other function of this module are pinned by the pages or the
+mathematics.
 
 Notation follows "bitsandbytes deep dive" (aicoding.csdn.net), section 5.2:
 a block B = {w_i}, a = max_i |w_i|, u_i = w_i / a, q_i = argmin_j |u_i - c_j|,
