@@ -106,7 +106,7 @@ struct GvArgs {
     int M, N, K, r;
     int P;                  // producer workgroups (FT)
     int kp;                 // columns of K per producer: spp slices of 64 (FT)
-    int spp;                // slices loaded per group: 1 or 2 (FT)
+        int spp;                // slices loaded per group: 1, 2 or 4 (FT)
     int phases;             // phased kernel: x staging phases
     int gw;                 // streaming kernel: tile workgroups
     int rg;                 // streaming kernel: 16-row groups per tile (1 or 2)
@@ -216,10 +216,12 @@ __device__ __forceinline__ void gv_produce_any(const GvArgs& a, uint8_t* lds) {
     // A rows are 16-byte loads when r % 8 == 0, 2-byte loads otherwise
     if ((a.r & 7) == 0) {
         if (a.spp == 1) gv_produce<NW, DT, 1, true>(a, lds, tag);
-        else gv_produce<NW, DT, 2, true>(a, lds, tag);
+        else if (a.spp == 2) gv_produce<NW, DT, 2, true>(a, lds, tag);
+        else gv_produce<NW, DT, 4, true>(a, lds, tag);
     } else {
         if (a.spp == 1) gv_produce<NW, DT, 1, false>(a, lds, tag);
-        else gv_produce<NW, DT, 2, false>(a, lds, tag);
+        else if (a.spp == 2) gv_produce<NW, DT, 2, false>(a, lds, tag);
+        else gv_produce<NW, DT, 4, false>(a, lds, tag);
     }
 }
 
@@ -788,7 +790,8 @@ GvPlan gv_plan(int M, int K) {
 }
 
 // Producers of t: at most 16 (a consumer adds up at most 16 partials per value),
-// each over kp columns of K, loaded in groups of up to 2 slices of 64.
+// each over kp columns of K, loaded in groups of up to 4 slices of 64 (at K = 4096 a
+// producer's whole range is requested at once).
 struct GvProducers {
     int P, kp, spp;
 };
@@ -798,7 +801,7 @@ GvProducers gv_producers(int M, int K, int r) {
     const int kb = K / kBlock;
     const int per = (kb + 15) / 16;               // slices per producer
     const int P = (kb + per - 1) / per;
-    return GvProducers{P, per * kBlock, per >= 2 ? 2 : 1};
+        return GvProducers{P, per * kBlock, per >= 4 ? 4 : per >= 2 ? 2 : 1};
 }
 
 // Plan of the streaming kernel: tile height (16 or 32 rows), ring depth D, steps per
@@ -841,15 +844,16 @@ SvPlan sv_plan(int M, int N, int K, int r, int P, const void* B) {
         p.lds = std::max(xbytes, P > 0 ? (size_t)kASliceBytes : (size_t)0);
         if (p.lds + kSvStaticLds > (size_t)kLdsBytes) continue;
         const int tiles = (N + kGvRows * rg - 1) / (kGvRows * rg);
-        // With producers (the layer call), tile workgroups beyond 256 - P wait for a
-        // producer's CU; that costs about a tile of start-up, so the grid keeps all 256
-        // only where leaving those CUs to the producers would add a whole tile per workgroup.
-        const int g_all = std::min(tiles, kCUs), g_rest = std::min(tiles, kCUs - P);
-        const int mk_all = (tiles + g_all - 1) / g_all, mk_rest = (tiles + g_rest - 1) / g_rest;
-        const bool all = P > 0 && mk_rest > mk_all;
-        p.gw = all ? g_all : g_rest;
+                // With producers (the layer call), the tile workgroups leave P CUs to them: one CU
+        // holds one workgroup of this kernel, so a tile workgroup beyond 256 - P would wait
+        // for a producer to finish, and every tile needs t.  (Taking all 256 CUs where that
+        // saves a tile per workgroup measured slower on q_proj and fused q/k/v, and no
+        // faster elsewhere.)
+        const int gw = std::min(tiles, kCUs - P);
+        const int mk = (tiles + gw - 1) / gw;
+        p.gw = gw;
         // the busiest workgroup's steps, plus about half a step of per-tile work
-        const double cost = (all ? mk_all + 0.5 : (double)mk_rest) * (nq0 + 0.5);
+        const double cost = (double)mk * (nq0 + 0.5);
         p.ok = true;
         if (!best.ok || cost < best_cost) {
             best = p;
