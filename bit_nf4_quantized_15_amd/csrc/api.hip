@@ -368,10 +368,10 @@ qlora_status qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, int64_t M, 
             return st;
     }
     // dA [K, r] = x^T u ; dB [r, N] = t^T dy, stored transposed from the [N, r] reduction
-    if ((st = launch_tn(x, u, at(ws, L.pa), dA, (int)M, (int)K, r, r, 1, dt_of(w), s)) !=
-        QLORA_OK)
-        return st;
-    return launch_tn(dy, t, at(ws, L.pb), dB, (int)M, (int)N, r, 1, N, dt_of(w), s);
+    // (both in one launch: the second one's workgroups fill the CUs that the first one's
+    // finished splits leave while its last splits add up their tiles)
+    return launch_tn2(x, u, at(ws, L.pa), dA, (int)K, r, 1, dy, t, at(ws, L.pb), dB, (int)N, 1, N, (int)M, r,
+                      dt_of(w), s);
 }
 
 // ---- fp32 compute dtype (deep dive 8.3): fp32 tensors, w_hat = fl32(a_hat * c_q)

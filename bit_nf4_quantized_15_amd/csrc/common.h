@@ -181,6 +181,11 @@ qlora_status launch_nt(const uint16_t* X, const uint16_t* Y, bool y_natural, voi
 // out[d * ld_d + j * ld_j] = sum_m X [M, D][m, d] * S [M, r][m, j]; ws: tn_ws_bytes(M, D, r) bytes
 qlora_status launch_tn(const uint16_t* X, const uint16_t* S, void* ws, float* out, int M, int D, int r,
                        int64_t ld_d, int64_t ld_j, int dt, hipStream_t s);
+// two such contractions over the same M and r (dA and dB of a layer) in one launch;
+// ws0 and ws1: tn_ws_bytes(M, D0, r) and tn_ws_bytes(M, D1, r) bytes
+qlora_status launch_tn2(const uint16_t* X0, const uint16_t* S0, void* ws0, float* out0, int D0, int64_t ld_d0,
+                        int64_t ld_j0, const uint16_t* X1, const uint16_t* S1, void* ws1, float* out1, int D1,
+                        int64_t ld_d1, int64_t ld_j1, int M, int r, int dt, hipStream_t s);
 qlora_status launch_fill(float* out, int64_t count, float v, hipStream_t s);
 qlora_status launch_expand_pooled(const uint16_t* A, int K, int r, int g, int dt, uint16_t* out, hipStream_t s);
 qlora_status launch_pool_rows(const float* in, int K, int r, int g, float* out, hipStream_t s);

@@ -268,11 +268,23 @@ __global__ __launch_bounds__(256) void nt_kernel(const uint16_t* __restrict__ X,
 // operand (8 consecutive m per lane), also with transposed loads.
 constexpr int kTnRows = 64, kTnCols = 128, kTnLd = kTnCols + 32;  // 320-byte rows: conflict-free transposed reads
 
+// One contraction out[d * ld_d + j * ld_j] = sum_m X[m, d] S[m, j]: its operands, its
+// split workspace (tags, partial tiles) and its grid of tiles x splits.
+struct TnProb {
+    const uint16_t* X;
+    const uint16_t* S;
+    uint64_t* tags;
+    float* part;
+    float* out;
+    int M, D, r, chunk, tiles, splits;
+    int64_t ld_d, ld_j;
+};
+
 template <int TQ, bool VEC, int NST, int DT>
-__global__ __launch_bounds__(256) void tn_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ S,
-                                                 uint64_t* __restrict__ tags, float* __restrict__ part,
-                                                 float* __restrict__ out, int M, int D, int r, int chunk,
-                                                 int64_t ld_d, int64_t ld_j) {
+__device__ __forceinline__ void tn_body(const TnProb& pr, int ti, int split) {
+    const uint16_t* __restrict__ X = pr.X;
+    const uint16_t* __restrict__ S = pr.S;
+    const int M = pr.M, D = pr.D, r = pr.r, chunk = pr.chunk;
     constexpr int kTnMaxChunk = TQ <= 3 ? 512 : 256;  // = tn_max_chunk(r) for r in (32 (TQ-1), 32 TQ]
     static_assert(NST * kTnRows <= kTnMaxChunk, "steps beyond the slice");
     constexpr int kSLd = slice_ld<TQ>();
@@ -282,8 +294,7 @@ __global__ __launch_bounds__(256) void tn_kernel(const uint16_t* __restrict__ X,
     __shared__ __attribute__((aligned(16))) uint16_t ss[NST * kTnRows * kSLd];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
     const int tj = l32 & 15, tg = l32 >> 4;
-    const int d0 = blockIdx.x * kTnCols;
-    const int split = blockIdx.y;
+            const int d0 = ti * kTnCols;
     const int m_begin = split * chunk;
     const int m_end = min(M, m_begin + chunk);
 
@@ -348,7 +359,7 @@ __global__ __launch_bounds__(256) void tn_kernel(const uint16_t* __restrict__ X,
         }
         if (st + 1 < NST) __syncthreads();
     }
-    if (!split_sum<TQ>(acc, tags, part, (int)gridDim.x, (int)blockIdx.x, split, (int)gridDim.y)) return;
+            if (!split_sum<TQ>(acc, pr.tags, pr.part, pr.tiles, ti, split, pr.splits)) return;
 #pragma unroll
     for (int q = 0; q < TQ; ++q) {
         const int j = 32 * q + l32;
@@ -356,8 +367,29 @@ __global__ __launch_bounds__(256) void tn_kernel(const uint16_t* __restrict__ X,
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int d = d0 + 32 * wave + 8 * (v >> 2) + 4 * h + (v & 3);
-            if (d < D) out[(int64_t)d * ld_d + (int64_t)j * ld_j] = acc[q][v];
+            if (d < D) pr.out[(int64_t)d * pr.ld_d + (int64_t)j * pr.ld_j] = acc[q][v];
         }
+    }
+}
+
+template <int TQ, bool VEC, int NST, int DT>
+__global__ __launch_bounds__(256) void tn_kernel(const TnProb pr) {
+    tn_body<TQ, VEC, NST, DT>(pr, blockIdx.x, blockIdx.y);
+}
+
+// Two independent contractions in one grid (dA and dB of a layer): workgroups
+// [0, tiles0 x splits0) run the first and the rest the second, each numbered split
+// by split, so that the last split of every tile is dispatched after the tile's
+// other splits.  The second contraction's workgroups take the CUs that the first
+// one's finished splits leave while its last splits add up their tiles.
+template <int TQ, bool VEC, int NST, int DT>
+__global__ __launch_bounds__(256) void tn2_kernel(const TnProb p0, const TnProb p1) {
+    const int n0 = p0.tiles * p0.splits, b = blockIdx.x;
+    if (b < n0) {
+        tn_body<TQ, VEC, NST, DT>(p0, b % p0.tiles, b / p0.tiles);
+    } else {
+        const int c = b - n0;
+        tn_body<TQ, VEC, NST, DT>(p1, c % p1.tiles, c / p1.tiles);
     }
 }
 
@@ -438,20 +470,39 @@ qlora_status launch_nt(const uint16_t* X, const uint16_t* Y, bool y_natural, voi
     return launch_status();
 }
 
-qlora_status launch_tn(const uint16_t* X, const uint16_t* S, void* ws, float* out, int M, int D, int r, int64_t ld_d,
-                       int64_t ld_j, int dt, hipStream_t s) {
+namespace {
+
+// The contraction out[d * ld_d + j * ld_j] = sum_m X[M, D][m, d] S[M, r][m, j] with its
+// split plan and workspace; vec: the buffer-load path applies (16-byte aligned rows, and
+// one split's rows of X under 1 GiB).
+TnProb tn_prob(const uint16_t* X, const uint16_t* S, void* ws, float* out, int M, int D, int r, int64_t ld_d,
+               int64_t ld_j, bool& vec) {
     const SplitPlan sp = plan_tn(M, D, r);
-    const int tiles = (D + kTnCols - 1) / kTnCols;
-    const dim3 grid((unsigned)tiles, (unsigned)sp.splits);
-    uint64_t* tags = static_cast<uint64_t*>(ws);
-    float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + split_tags_bytes(tiles, sp));
-    // vector path: 16-byte aligned rows, and one split's rows of X under 1 GiB
-    const bool vec = (D % 8 == 0) && (r % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15u) == 0) &&
-                     ((reinterpret_cast<uintptr_t>(S) & 15u) == 0) && (int64_t)D * 512 * 2 < (int64_t(1) << 30);
-    const int tq = (r + 31) / 32, nst = steps_template(sp.chunk);
-#define QL_TN(TQ, V, NST) \
-    hipLaunchKernelGGL((tn_kernel<TQ, V, NST, DT>), grid, dim3(256), 0, s, X, S, tags, part, out, M, D, r, sp.chunk, \
-                       ld_d, ld_j);
+    TnProb p{};
+    p.X = X;
+    p.S = S;
+    p.tiles = (D + kTnCols - 1) / kTnCols;
+    p.splits = sp.splits;
+    p.chunk = sp.chunk;
+    p.tags = static_cast<uint64_t*>(ws);
+    p.part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + split_tags_bytes(p.tiles, sp));
+    p.out = out;
+    p.M = M;
+    p.D = D;
+    p.r = r;
+    p.ld_d = ld_d;
+    p.ld_j = ld_j;
+    vec = (D % 8 == 0) && (r % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15u) == 0) &&
+          ((reinterpret_cast<uintptr_t>(S) & 15u) == 0) && (int64_t)D * 512 * 2 < (int64_t(1) << 30);
+    return p;
+}
+
+// Calls go.template operator()<TQ, VEC, NST, DT>() for the instantiation that serves rank r,
+// the load path and the longest split.
+template <typename Go>
+void tn_dispatch(int r, bool vec, int chunk, int dt, Go&& go) {
+    const int tq = (r + 31) / 32, nst = steps_template(chunk);
+#define QL_TN(TQ, V, NST) go.template operator()<TQ, V, NST, DT>();
 #define QL_TN1(TQ, V)                       \
     if (nst == 2) { QL_TN(TQ, V, 2) }       \
     else if (nst == 4) { QL_TN(TQ, V, 4) }  \
@@ -470,6 +521,51 @@ qlora_status launch_tn(const uint16_t* X, const uint16_t* S, void* ws, float* ou
 #undef QL_TN2
 #undef QL_TN1
 #undef QL_TN
+}
+
+struct TnLaunch1 {
+    const TnProb& p;
+    dim3 grid;
+    hipStream_t s;
+    template <int TQ, bool V, int NST, int DT>
+    void operator()() const {
+        hipLaunchKernelGGL((tn_kernel<TQ, V, NST, DT>), grid, dim3(256), 0, s, p);
+    }
+};
+
+struct TnLaunch2 {
+    const TnProb& p0;
+    const TnProb& p1;
+    unsigned n;
+    hipStream_t s;
+    template <int TQ, bool V, int NST, int DT>
+    void operator()() const {
+        hipLaunchKernelGGL((tn2_kernel<TQ, V, NST, DT>), dim3(n), dim3(256), 0, s, p0, p1);
+    }
+};
+
+}  // namespace
+
+qlora_status launch_tn(const uint16_t* X, const uint16_t* S, void* ws, float* out, int M, int D, int r, int64_t ld_d,
+                       int64_t ld_j, int dt, hipStream_t s) {
+    bool vec = false;
+    const TnProb p = tn_prob(X, S, ws, out, M, D, r, ld_d, ld_j, vec);
+    const dim3 grid((unsigned)p.tiles, (unsigned)p.splits);
+        const TnLaunch1 go{p, grid, s};
+    tn_dispatch(r, vec, p.chunk, dt, go);
+    return launch_status();
+}
+
+qlora_status launch_tn2(const uint16_t* X0, const uint16_t* S0, void* ws0, float* out0, int D0, int64_t ld_d0,
+                        int64_t ld_j0, const uint16_t* X1, const uint16_t* S1, void* ws1, float* out1, int D1,
+                        int64_t ld_d1, int64_t ld_j1, int M, int r, int dt, hipStream_t s) {
+    bool vec0 = false, vec1 = false;
+    const TnProb p0 = tn_prob(X0, S0, ws0, out0, M, D0, r, ld_d0, ld_j0, vec0);
+    const TnProb p1 = tn_prob(X1, S1, ws1, out1, M, D1, r, ld_d1, ld_j1, vec1);
+    const int64_t n = (int64_t)p0.tiles * p0.splits + (int64_t)p1.tiles * p1.splits;
+    if (n >= (int64_t(1) << 31)) return QLORA_ERR_UNSUPPORTED_SHAPE;
+        const TnLaunch2 go{p0, p1, (unsigned)n, s};
+    tn_dispatch(r, vec0 && vec1, std::max(p0.chunk, p1.chunk), dt, go);
     return launch_status();
 }
 
