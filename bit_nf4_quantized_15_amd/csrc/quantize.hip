@@ -39,6 +39,22 @@ constexpr int kThrStride = 17;        // per block: T_0..T_14, +inf, 64/a; an od
 constexpr int kBuckets = 129;         // trunc(64 (u + 1)) for u in [-1, 1]
 constexpr float kTinyScale = 0x1p-100f;
 
+// RD_bf16(x) (DT = bf16) or RD_f32(x) (fp16 and fp32 weights) of an exact product x
+// whose magnitude is at least 2^-126: the double's significand cut to the target's 8
+// (24) bits toward zero converts to float exactly; a negative x that lost bits in the
+// cut steps one unit down (toward -inf), which may carry into the exponent.  Any
+// float weight w has w > X <=> w > RD_f32(X), and a bf16 weight also w > X <=>
+// w > RD_bf16(X).
+template <int DT>
+__device__ __forceinline__ float rd_to_grid(double x) {
+    constexpr int kDrop = DT == kDtBf16 ? 52 - 7 : 52 - 23;   // double significand bits below the target's
+    constexpr uint64_t kMask = (uint64_t(1) << kDrop) - 1;
+    const uint64_t d = (uint64_t)__double_as_longlong(x);
+    uint32_t u = __float_as_uint((float)__longlong_as_double((long long)(d & ~kMask)));
+    if ((d >> 63) && (d & kMask)) u += DT == kDtBf16 ? 0x00010000u : 1u;
+    return __uint_as_float(u);
+}
+
 __device__ __forceinline__ uint32_t absmax_bits8(u32x4_t v) {
     uint32_t m = 0;
 #pragma unroll
@@ -142,11 +158,24 @@ __device__ __forceinline__ void quantize_group(const void* __restrict__ Wv, int6
     }
     __syncthreads();
 
-    // 3. thresholds of block `tid`, group scale, scale code
+        // 3. thresholds of block `tid`, group scale, scale code
     const float a = s_amax[tid];
     {
         float T[15];
-        if (a > 0.0f) {
+        if (a >= kTinyScale) {
+            // |a m| > 2^-105: the rounding below stays in fp32's normal range
+            const double ad = (double)a;
+#pragma unroll
+            for (int j = 0; j < 15; ++j) {
+                if (j + 1 < kDistinctLevels<CB>) {
+                    const double m = 0.5 * ((double)level<CB>(code_of_sorted<CB>(j)) +
+                                            (double)level<CB>(code_of_sorted<CB>(j + 1)));  // exact
+                    T[j] = rd_to_grid<DT>(ad * m);
+                } else {
+                    T[j] = __builtin_huge_valf();
+                }
+            }
+        } else if (a > 0.0f) {
             const double ad = (double)a;
 #pragma unroll
             for (int j = 0; j < 15; ++j) {
@@ -199,17 +228,25 @@ __device__ __forceinline__ void quantize_group(const void* __restrict__ Wv, int6
     for (int p = 0; p < kPasses; ++p) {
         const int bl = p * 32 + wave * 8 + (lane >> 3);
         if (bl < nb_here) {
-            const float* tb = &s_thr[bl * kThrStride];
+                        const float* tb = &s_thr[bl * kThrStride];
             const float sc = tb[16];
-            uint32_t packed = 0;
+            // the block's threshold row as an LDS byte address, formed once: each weight's
+            // threshold is then one shift-and-add away (c * 4 + row)
+            const uint32_t trow = (uint32_t)reinterpret_cast<uintptr_t>(tb);
+                        uint32_t q[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float w = elem<DT, NW>(v[p], i);
                 const int bucket = (int)__builtin_fmaf(w, sc, 64.0f);  // 0 .. 128 (trunc; -2^-16 -> 0)
                 const uint32_t c = s_lut[bucket];
-                const uint32_t q = code_of_sorted<CB>(c + (w > tb[c] ? 1u : 0u));
-                packed |= q << (4 * (i ^ 1));
+                const float tc = *reinterpret_cast<const __attribute__((address_space(3))) float*>(
+                    (uintptr_t)((c << 2) + trow));
+                q[i] = code_of_sorted<CB>(c + (w > tc ? 1u : 0u));
             }
+            // byte j = element 2j in the high nibble, 2j + 1 in the low one
+            uint32_t packed = (q[0] << 4) | q[1];
+#pragma unroll
+            for (int j = 1; j < 4; ++j) packed |= ((q[2 * j] << 4) | q[2 * j + 1]) << (8 * j);
             const float ab = s_amax[bl];
             if (ab > 0.0f && ab < kTinyScale) {               // rare: 64/a may not be finite
                 const f32x4_t t0 = {tb[0], tb[1], tb[2], tb[3]}, t1 = {tb[4], tb[5], tb[6], tb[7]};
