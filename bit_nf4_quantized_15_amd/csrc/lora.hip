@@ -288,25 +288,31 @@ __device__ __forceinline__ void tn_body(const TnProb& pr, int ti, int split) {
     constexpr int kTnMaxChunk = TQ <= 3 ? 512 : 256;  // = tn_max_chunk(r) for r in (32 (TQ-1), 32 TQ]
     static_assert(NST * kTnRows <= kTnMaxChunk, "steps beyond the slice");
     constexpr int kSLd = slice_ld<TQ>();
-    constexpr int kCh = 4 * TQ;                       // 16-byte chunks per slice row
-    constexpr int kSPer = NST * kTnRows * kCh / 256;  // slice loads per thread
+        constexpr int kCh = 4 * TQ;                       // 16-byte chunks per slice row
+    // An 8-step split holds its slice of S in LDS in two phases of 256 rows (the second
+    // stored after step 3), so that at r <= 64 a workgroup takes 80 KB and two share a CU.
+    constexpr int kSH = NST > 4 ? 2 : 1;
+    constexpr int kSRows = NST * kTnRows / kSH;       // slice rows held in LDS
+    constexpr int kSPer = kSRows * kCh / 256;         // slice loads per thread and phase
     __shared__ __attribute__((aligned(16))) uint16_t tile[2][kTnRows * kTnLd];
-    __shared__ __attribute__((aligned(16))) uint16_t ss[NST * kTnRows * kSLd];
+    __shared__ __attribute__((aligned(16))) uint16_t ss[kSRows * kSLd];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
     const int tj = l32 & 15, tg = l32 >> 4;
-            const int d0 = ti * kTnCols;
+    const int d0 = ti * kTnCols;
     const int m_begin = split * chunk;
     const int m_end = min(M, m_begin + chunk);
 
-    bf16x8 sv[kSPer];
+        bf16x8 sv[kSH][kSPer];
     {
         const rsrc_t srs = buf_rsrc(S + (int64_t)m_begin * r, (uint64_t)(m_end - m_begin) * r * 2);
 #pragma unroll
-        for (int e = 0; e < kSPer; ++e) {
-            const int idx = tid + 256 * e, row = idx / kCh, ch = idx % kCh;
-            sv[e] = VEC ? bload8(srs, m_begin + row < m_end && 8 * ch < r, (uint32_t)(row * r + 8 * ch))
-                        : load8_row<false>(S, r, m_begin + row, m_end, 8 * ch, r);
-        }
+        for (int ph = 0; ph < kSH; ++ph)
+#pragma unroll
+            for (int e = 0; e < kSPer; ++e) {
+                const int idx = tid + 256 * e, row = kSRows * ph + idx / kCh, ch = idx % kCh;
+                sv[ph][e] = VEC ? bload8(srs, m_begin + row < m_end && 8 * ch < r, (uint32_t)(row * r + 8 * ch))
+                                : load8_row<false>(S, r, m_begin + row, m_end, 8 * ch, r);
+            }
     }
     // loader: row tid/4 of a 64-row step, columns 32*(tid%4) .. +31
     const int lr = tid >> 2, lc = (tid & 3) * 32;
@@ -328,11 +334,14 @@ __device__ __forceinline__ void tn_body(const TnProb& pr, int ti, int split) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) *reinterpret_cast<bf16x8*>(&tile[buf][lr * kTnLd + lc + 8 * i]) = src[i];
     };
+    auto store_s = [&](int ph) {
 #pragma unroll
-    for (int e = 0; e < kSPer; ++e) {
-        const int idx = tid + 256 * e, row = idx / kCh, ch = idx % kCh;
-        *reinterpret_cast<bf16x8*>(&ss[row * kSLd + 8 * ch]) = sv[e];
-    }
+        for (int e = 0; e < kSPer; ++e) {
+            const int idx = tid + 256 * e, row = idx / kCh, ch = idx % kCh;
+            *reinterpret_cast<bf16x8*>(&ss[row * kSLd + 8 * ch]) = sv[ph][e];
+        }
+    };
+    store_s(0);
     store_x(xr[0], 0);
     __syncthreads();
 
@@ -344,22 +353,28 @@ __device__ __forceinline__ void tn_body(const TnProb& pr, int ti, int split) {
     // A operand = X^T: 8 consecutive m of column d = 32*wave + l32 of the tile.  Step
     // st + 1 goes into the buffer step st - 1 was read from (closed by the barrier).
 #pragma unroll
-    for (int st = 0; st < NST; ++st) {
+        for (int st = 0; st < NST; ++st) {
         const int buf = st & 1;
+        constexpr int kHalf = NST / kSH;
+        if (kSH == 2 && st == kHalf) {     // every wave is past the first phase (the barrier above)
+            store_s(1);
+            __syncthreads();
+        }
         if (st + 1 < NST) store_x(xr[st + 1], buf ^ 1);
+        const int srow = kTnRows * (st % kHalf);   // this step's rows in the slice phase
 #pragma unroll
         for (int mc = 0; mc < kTnRows / 16; ++mc) {
             const int mr = mc * 16 + 8 * h;   // tile row of this lane's first k slot
             const bf16x8 a = slice_col8(tile[buf], kTnLd, mr, 32 * wave + 16 * tg, tj);
 #pragma unroll
             for (int q = 0; q < TQ; ++q) {
-                const bf16x8 b = slice_col8(ss, kSLd, kTnRows * st + mr, 32 * q + 16 * tg, tj);
+                const bf16x8 b = slice_col8(ss, kSLd, srow + mr, 32 * q + 16 * tg, tj);
                 acc[q] = mfma32<DT>(a, b, acc[q]);
             }
         }
         if (st + 1 < NST) __syncthreads();
     }
-            if (!split_sum<TQ>(acc, pr.tags, pr.part, pr.tiles, ti, split, pr.splits)) return;
+    if (!split_sum<TQ>(acc, pr.tags, pr.part, pr.tiles, ti, split, pr.splits)) return;
 #pragma unroll
     for (int q = 0; q < TQ; ++q) {
         const int j = 32 * q + l32;
@@ -372,8 +387,9 @@ __device__ __forceinline__ void tn_body(const TnProb& pr, int ti, int split) {
     }
 }
 
+// two workgroups per CU where r <= 64 on the buffer-load path (80 KB of LDS, at most 256 VGPRs)
 template <int TQ, bool VEC, int NST, int DT>
-__global__ __launch_bounds__(256) void tn_kernel(const TnProb pr) {
+__global__ __launch_bounds__(256, TQ <= 2 && VEC ? 2 : 1) void tn_kernel(const TnProb pr) {
     tn_body<TQ, VEC, NST, DT>(pr, blockIdx.x, blockIdx.y);
 }
 
@@ -383,7 +399,7 @@ __global__ __launch_bounds__(256) void tn_kernel(const TnProb pr) {
 // other splits.  The second contraction's workgroups take the CUs that the first
 // one's finished splits leave while its last splits add up their tiles.
 template <int TQ, bool VEC, int NST, int DT>
-__global__ __launch_bounds__(256) void tn2_kernel(const TnProb p0, const TnProb p1) {
+__global__ __launch_bounds__(256, TQ <= 2 && VEC ? 2 : 1) void tn2_kernel(const TnProb p0, const TnProb p1) {
     const int n0 = p0.tiles * p0.splits, b = blockIdx.x;
     if (b < n0) {
         tn_body<TQ, VEC, NST, DT>(p0, b % p0.tiles, b / p0.tiles);
