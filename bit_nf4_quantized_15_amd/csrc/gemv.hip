@@ -632,8 +632,14 @@ __global__ __launch_bounds__(kSW * 64 + (FT ? 64 : 0)) void nf4_gemv_stream_kern
             xv[e] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                                                     xrs, opq(c < nch ? 16u * (uint32_t)c : kOob), 0, 0));
     }
-    // x is staged before any ring request goes out: the ring requests of every CU at once
-    // would queue ahead of x in memory and hold up the whole workgroup
+    // x goes out first, then the ring and the first tile's B; staging x then waits for x
+    // alone (loads complete in order), so the ring's first code bytes travel from HBM
+    // while x is staged instead of after it
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < D; ++k) issue(k, TP > 1 ? k / NQS : 0, TP > 1 ? k % NQS : k);
+    load_b(0);
+    __builtin_amdgcn_sched_barrier(0);
     uint8_t* const xl = dyn;
 #pragma unroll
     for (int e = 0; e < XE; ++e) {
@@ -656,9 +662,6 @@ __global__ __launch_bounds__(kSW * 64 + (FT ? 64 : 0)) void nf4_gemv_stream_kern
         reduced[tid] = (tid >> 1) - kSvSlots;    // slot s is free for tile s
     }
     if (tid == 0) tickets = 0u;
-#pragma unroll
-    for (int k = 0; k < D; ++k) issue(k, TP > 1 ? k / NQS : 0, TP > 1 ? k % NQS : k);
-    load_b(0);
     __syncthreads();
 
     // ---- main loop: D steps per pass, each expanded, then its entry refilled D steps ahead
