@@ -208,12 +208,15 @@ qlora_status qlora_linear_fwd_noalloc(const qlora_nf4* w, const uint16_t* x, int
                                       void* stream);
 
 /* The two stages of qlora_linear_fwd, for callers that keep t across calls
- * or time the stages separately.  Given the t that qlora_linear_fwd returns,
- * qlora_fused_gemm_fwd reproduces its y bit for bit.  Above decode sizes
- * qlora_linear_fwd is exactly qlora_lora_down followed by qlora_fused_gemm_fwd;
- * at decode sizes (M <= 16, where one launch computes t and y) it adds the
- * fp32 products of x A in another order than qlora_lora_down, so its t may
- * differ from qlora_lora_down's in the last bit. */
+ * or time the stages separately.  Above decode sizes qlora_linear_fwd is
+ * exactly qlora_lora_down followed by qlora_fused_gemm_fwd, and given the t
+ * that qlora_linear_fwd returns, qlora_fused_gemm_fwd reproduces its y bit for
+ * bit.  At decode sizes (M <= 16, where one launch computes t and y) the layer
+ * call may split the weight's rows into taller tiles than the kernel with t
+ * given (it leaves CUs to the producers of t), which adds y's fp32 partial sums
+ * in another order: y may then differ in the last bit.  Its t adds the fp32
+ * products of x A in another order than qlora_lora_down, so t may also differ
+ * from qlora_lora_down's in the last bit. */
 
 /* Workspace bytes qlora_lora_down needs (0 for M == 0). */
 size_t qlora_lora_down_workspace(int64_t M, int64_t K, int r);

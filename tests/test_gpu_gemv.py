@@ -34,6 +34,8 @@ def q():
     (16, 100, 11008, 8),    # six x phases, the last one short
     (16, 16, 28672, 16),    # fourteen x phases
     (16, 4096, 4096, 16),   # two x phases at the decode shape
+    (1, 3880, 1024, 24),    # 243 tiles of 16 rows, more than the CUs the producers leave free
+    (7, 3880, 4096, 8),     # the same with a short last tile at M = 7
 ])
 def test_gemv_forward(q, M, N, K, r):
     import torch
@@ -55,10 +57,17 @@ def test_gemv_forward(q, M, N, K, r):
     assert ey <= TOL and et <= TOL
 
 
-def test_gemv_fused_entry_matches_linear(q):
-    """qlora_fused_gemm_fwd(x, t, B) == qlora_linear_fwd's y for the same t (one kernel, same bits)."""
+@pytest.mark.parametrize("M,N,K,r", [(4, 1000, 2048, 32), (40, 1000, 2048, 32), (1, 4096, 4096, 16),
+                                     (16, 4096, 4096, 16), (1, 12288, 4096, 48), (16, 12288, 4096, 48),
+                                     (1, 22016, 4096, 32), (16, 22016, 4096, 32)])
+def test_gemv_fused_entry_matches_linear(q, M, N, K, r):
+    """qlora_fused_gemm_fwd(x, t, B) against qlora_linear_fwd's y for the same t.  Above decode sizes the
+    two are one kernel and agree bit for bit.  At decode sizes the layer call may take taller tiles (it
+    leaves CUs to the producers of t), which only reorders y's fp32 partial sums: every element then
+    differs by at most one bf16 rounding plus the reordering's fp32 error (2^-16 of the largest |y|
+    here, which also covers elements near zero after cancellation)."""
     import torch
-    M, N, K, r = 4, 1000, 2048, 32
+    say(f"[gemv] fused entry vs layer call M={M} N={N} K={K} r={r}")
     W = workloads.custom(91, (N, K), 0.02)
     x, A, B = (dev_bf16(workloads.custom(92 + i, s, v)) for i, (s, v) in
                enumerate((((M, K), 1.0), ((K, r), 0.2), ((r, N), 0.01))))
@@ -66,7 +75,15 @@ def test_gemv_fused_entry_matches_linear(q):
     y1, t = q.linear_fwd(w, x, A, B, 64.0)
     y2 = q.fused_gemm_fwd(w, x, t, B)
     torch.cuda.synchronize()
-    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    if M > 16:
+        assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+        return
+    a, b = y1.float().cpu().numpy().astype(np.float64), y2.float().cpu().numpy().astype(np.float64)
+    ulp = np.spacing(np.maximum(np.abs(a), np.abs(b)).astype(np.float32)).astype(np.float64) * 2.0 ** 16
+    bound = ulp + 2.0 ** -16 * np.abs(a).max()
+    say(f"    elements that differ: {int((a != b).sum())} of {a.size}, largest difference "
+        f"{np.abs(a - b).max():.3e} (max |y| {np.abs(a).max():.3e})")
+    assert np.all(np.abs(a - b) <= bound), "y differs by more than a bf16 rounding of reordered fp32 sums"
 
 
 @pytest.mark.parametrize("M", [1, 16])
