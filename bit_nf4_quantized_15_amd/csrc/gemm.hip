@@ -7,8 +7,9 @@
 // the LoRA up-projection is the same product continued over r extra
 // reduction steps with operands [t | B] resp. [u | A^T]).
 //
-// Both kernels: 256 lanes (4 waves), output tile 256 x 256, reduction step 64
-// (one NF4 block).  The activation tile (256 rows x 64 of x, resp. of dy) is
+// Both kernels: output tile 256 x 256, reduction step 64 (one NF4 block); the
+// forward runs 256 lanes (4 waves, one per SIMD), the backward 512 (8 waves, two
+// per SIMD).  The activation tile (256 rows x 64 of x, resp. of dy) is
 // copied HBM -> LDS with direct buffer loads (16 B per lane, XOR-swizzled on
 // the global side), double buffered.
 //  * forward: wave w owns output columns [64w, 64w+64) over all 256 rows.
@@ -19,7 +20,7 @@
 //  * backward: the reduction runs over n, across rows of the stored codes, so
 //    the weight tile is dequantized cooperatively (lane = one row x one block)
 //    into LDS in its natural [n][k] layout and read transposed by the MFMA
-//    operand loads (ds_read_b64_tr_b16); waves form a 2 x 2 grid of 128 x 128
+//    operand loads (ds_read_b64_tr_b16); waves form a 2 x 4 grid of 128 x 64
 //    sub-tiles, and the dequantization VALU work is interleaved with the MFMAs.
 // Accumulation is fp32; outputs are rounded to bf16 (nearest even).
 #include "common.h"
@@ -636,15 +637,16 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_fwd_kernel(
 
 // ------------------------------------------------------------------ backward dx
 // dx[m, k] = sum_n dy[m, n] w_hat[n, k]: the reduction runs across rows of the
-// stored codes.  Each step covers 64 rows n: lane (n = tid % 64, block = tid / 64)
-// expands one 64-code block of row n with its own table into 8 x 16-byte
-// stores of a natural [n][k] weight tile in LDS; the MFMA B operand (8
+// stored codes.  Each step covers 64 rows n: lane (n = tid % 64, block =
+// (tid / 64) % 4, half = tid / 256) expands 32 codes of one block of row n with
+// the block's table into 4 x 16-byte stores of a natural [n][k] weight tile in
+// LDS; the MFMA B operand (8
 // consecutive n of one column k) is then read with ds_read_b64_tr_b16, which
 // hands lane j of a 16-lane group element j of the 4-element row pieces
 // addressed by 4 lanes (rows R..R+3 -> 4 consecutive n of column j).  The dy
-// tile arrives by direct HBM -> LDS loads.  Waves are 2 x 2 (128 x 128 each);
-// the next step's codes arrive two steps ahead and are expanded while this
-// step's MFMAs run.
+// tile arrives by direct HBM -> LDS loads.  Waves are 2 x 4 (128 x 64 each,
+// two per SIMD); the next step's codes arrive two steps ahead and are expanded
+// while this step's MFMAs run.
 
 // weight tile layout: 64 rows of 256 bf16 (512 B), 16-byte chunks XOR-swizzled
 // by a 4-bit function of the row (conflict-free 16-byte row stores and
@@ -654,8 +656,58 @@ __device__ __forceinline__ uint32_t wtile_off(int row, int col) {
     return (uint32_t)row * 512u + ((uint32_t)((col >> 3) ^ f) << 4) + ((uint32_t)(col & 7) << 1);
 }
 
+// Eight waves, two per SIMD: wave (wm, wk) = (wave / 4, wave % 4) owns rows
+// [128 wm, 128 wm + 128) x columns [64 wk, 64 wk + 64) of the tile (4 x 2 MFMA
+// tiles, 128 accumulators), so that one wave's LDS waits and barrier overlap the
+// other's MFMAs (with four waves of 128 x 128, one per SIMD, the same kernel ran
+// 3 % slower and its backward call 7 % slower).  Dequantization: thread (n, kb,
+// half) expands 32 codes of row n, block kb of the step (both halves build the
+// block's table).
+constexpr int kT8 = 512;
+__device__ __forceinline__ void load_tile_direct8(i32x4_t rs, uint8_t* tile, uint32_t voff0, int wave, int col0,
+                                                  int64_t ld) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        auto* dst = as_lds<uint32_t>(tile + (64 * j + 8 * wave) * 128);
+        raw_buffer_load_lds(rs, dst, 16, (int)(voff0 + (uint32_t)(64 * j * ld * 2)), (int)(col0 * 2), 0, 0);
+    }
+}
+
+// 256 x 64 bf16 tile of a row-major matrix through registers by 512 threads (rows
+// tid/8 + 64 p, 16-byte chunk tid % 8), zero outside [0, nrows) x [0, ncols).
+template <bool VEC>
+__device__ __forceinline__ void load_tile8(u32x4_t (&r)[4], const uint16_t* __restrict__ src, int64_t ld, int row0,
+                                           int nrows, int col0, int ncols, int tid) {
+    const int lr = tid >> 3, lc = tid & 7;
+    const int col = col0 + lc * 8;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int row = row0 + lr + 64 * p;
+        if (VEC) {
+            r[p] = (row < nrows && col < ncols) ? *reinterpret_cast<const u32x4_t*>(src + (int64_t)row * ld + col)
+                                                : u32x4_t{0u, 0u, 0u, 0u};
+        } else {
+            uint32_t w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c0 = col + 2 * i;
+                uint32_t lo = 0, hi = 0;
+                if (row < nrows && c0 < ncols) lo = src[(int64_t)row * ld + c0];
+                if (row < nrows && c0 + 1 < ncols) hi = src[(int64_t)row * ld + c0 + 1];
+                w[i] = lo | (hi << 16);
+            }
+            r[p] = u32x4_t{w[0], w[1], w[2], w[3]};
+        }
+    }
+}
+__device__ __forceinline__ void store_ftile8(uint8_t* lds, const u32x4_t (&r)[4], int tid) {
+    const int lr = tid >> 3, lc = tid & 7;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) *reinterpret_cast<u32x4_t*>(lds + ftile_off(lr + 64 * p, lc)) = r[p];
+}
+
 template <bool DYVEC, bool DQ, int CB, int DT>
-__global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
+__global__ __launch_bounds__(kT8, 1) void nf4_gemm_bwd_dx_kernel(
     const uint16_t* __restrict__ dy, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ q8,
     const float* __restrict__ a2, const uint16_t* __restrict__ u_, const uint16_t* __restrict__ Al,
     uint16_t* __restrict__ dx, int M, int N, int K, int r, int tiles_m, int tiles_k) {
@@ -665,32 +717,29 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, l32 = lane & 31;
-    const int wm = wave >> 1, wk = wave & 1;
+    const int wm = wave >> 2, wk = wave & 3;
     const int tile = xcd_tile(blockIdx.x, tiles_m * tiles_k);
     const int mt = tile / tiles_k, kt = tile - mt * tiles_k;
     const int m0 = mt * kTM, k0 = kt * kTN;
     const int KB = K / kTK;
     const int NS = (N + kTK - 1) / kTK;
 
-    // dequant role
-    const int dn = tid & 63, dkb = tid >> 6;
-    const int dkcol = k0 + dkb * kTK;                 // first column of this lane's block
+    // dequant role: row dn of the step, block dkb of the tile, half dh of the block's codes
+    const int dn = tid & 63, dkb = (tid >> 6) & 3, dh = tid >> 8;
+    const int dkcol = k0 + dkb * kTK;
     const bool dk_ok = dkcol < K;
     struct Step {
-        u32x4_t c0, c1;
+        u32x4_t c;
         uint32_t q;
         float g;
-        bool ok;  // false past row N or column K: the block's weights are zero
+        bool ok;
     };
-    // rows past N / blocks past K read a valid block and get scale code 0,
-    // i.e. all-zero weights (branch-free, so the loop stays one basic block)
     const int dkc = dk_ok ? dkcol : K - kTK;
     auto load_step = [&](int ns, Step& S) {
         const int n = ns * kTK + dn;
         const int nc = min(n, N - 1);
-        const uint8_t* p = codes + (int64_t)nc * (K / 2) + dkc / 2;
-        S.c0 = *reinterpret_cast<const u32x4_t*>(p);
-        S.c1 = *reinterpret_cast<const u32x4_t*>(p + 16);
+        const uint8_t* p = codes + (int64_t)nc * (K / 2) + dkc / 2 + 16 * dh;
+        S.c = *reinterpret_cast<const u32x4_t*>(p);
         const int64_t blk = (int64_t)nc * KB + dkc / kTK;
         S.ok = n < N && dk_ok;
         if (DQ) {
@@ -698,13 +747,10 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
             S.g = a2[blk >> 8];
         } else {
             S.q = 0u;
-            S.g = a2[blk];  // no double quantization: the block's fp32 absmax
+            S.g = a2[blk];
         }
     };
-    // loads per load_step: codes (2) and the scale data
-    constexpr int kStepLoads = DQ ? 4 : 3;
-    // scale of a loaded step; the load above stays unconditional because the
-    // validity select happens here, where the value is needed anyway
+    constexpr int kStepLoads = DQ ? 3 : 2;
     auto ahat_of = [&](const Step& S) {
         if (!DQ) {
             float g = S.g;
@@ -715,109 +761,100 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
         asm volatile("" : "+v"(q));
         return scale_step(S.g) * (float)(S.ok ? q : 0u);
     };
-    auto expand = [&](const Step& S, u32x4_t (&out)[8]) {
-        const Nf4Tab T = make_tab<CB, DT>(ahat_of(S));
+    auto store_w = [&](uint8_t* Bt, const u32x4_t (&w)[4]) {
 #pragma unroll
-        for (int d = 0; d < 8; ++d) out[d] = deq8(T, d < 4 ? S.c0[d] : S.c1[d - 4]);
-    };
-    auto store_w = [&](uint8_t* Bt, const u32x4_t (&w)[8]) {
-#pragma unroll
-        for (int d = 0; d < 8; ++d) *reinterpret_cast<u32x4_t*>(Bt + wtile_off(dn, dkb * kTK + 8 * d)) = w[d];
+        for (int d = 0; d < 4; ++d)
+            *reinterpret_cast<u32x4_t*>(Bt + wtile_off(dn, dkb * kTK + 32 * dh + 8 * d)) = w[d];
     };
 
-    // MFMA operand addresses
     uint32_t offA[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) offA[c] = ftile_off(l32, 2 * c + h);   // + 4096*(4wm + i)
-    // transposed reads: group lane j = l32 % 16 -> row 8h + 4*s2 + j/4 (+16c), column
-    // 128wk + 32u + 16*(l32/16) + 4*(j%4)
-    uint32_t offB[4][2];
+    uint32_t offB[2][2];
     {
         const int j = l32 & 15, g = l32 >> 4;
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
-                offB[u][s2] = wtile_off(8 * h + 4 * s2 + (j >> 2), 128 * wk + 32 * u + 16 * g + 4 * (j & 3));
+                offB[u][s2] = wtile_off(8 * h + 4 * s2 + (j >> 2), 64 * wk + 32 * u + 16 * g + 4 * (j & 3));
     }
-    auto read_ops = [&](const uint8_t* A, const uint8_t* Bt, int c, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
+    auto read_ops = [&](const uint8_t* A, const uint8_t* Bt, int c, bf16x8 (&a)[4], bf16x8 (&b)[2]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             a[i] = *reinterpret_cast<const bf16x8*>(A + offA[c] + 4096u * (4 * wm + i));
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 2; ++u) {
             const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds<s16x4_t>(Bt + offB[u][0] + 8192u * c));
             const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds<s16x4_t>(Bt + offB[u][1] + 8192u * c));
             b[u] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
     };
 
-    f32x16_t acc[4][4];
+    f32x16_t acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][u][v] = 0.0f;
 
-    // dy panel rows [m0, min(M, m0 + kTM)): direct loads when rows are 16-byte aligned
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    // the panel's own rows only (at most kTM; DYVEC requires kTM * N * 2 < 2^32)
     const i32x4_t drs = buffer_rsrc(dy + (int64_t)m0 * N, (uint32_t)((int64_t)min(M - m0, kTM) * N * 2));
     const int xrow = 8 * wv + (lane >> 3);
     const int xchunk = (lane & 7) ^ (((xrow ^ (xrow >> 3)) & 3) ^ (xrow & 4));
     const uint32_t dvoff = (uint32_t)(((int64_t)xrow * N + 8 * xchunk) * 2);
-    u32x4_t ar[8];
+    u32x4_t ar[4];
     auto load_dy = [&](uint8_t* A, int ns) {
         if (DYVEC) {
-            load_tile_direct(drs, A, dvoff, wv, ns * kTK, N);
+            load_tile_direct8(drs, A, dvoff, wv, ns * kTK, N);
         } else {
-            load_tile<false>(ar, dy, N, m0, M, ns * kTK, N, tid);
-            store_ftile(A, ar, tid);
+            load_tile8<false>(ar, dy, N, m0, M, ns * kTK, N, tid);
+            store_ftile8(A, ar, tid);
         }
     };
 
-    // prologue
     Step cur, nxt;
     load_dy(ldsA0, 0);
     load_step(0, cur);
     load_step(min(1, NS - 1), nxt);
     {
-        u32x4_t w[8];
-        expand(cur, w);
+        const Nf4Tab T = make_tab<CB, DT>(ahat_of(cur));
+        u32x4_t w[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) w[d] = deq8(T, cur.c[d]);
         store_w(ldsB0, w);
     }
     wait_direct_loads();
     __syncthreads();
 
-    // One step reads dy tile A and weight tile Bt and fills An (direct loads) and Bn.
-    // The four never overlap; restrict-qualified parameters tell the compiler so,
-    // which keeps it from waiting for the fill of An before the step's reads.
     auto step = [&](int ns, const uint8_t* __restrict__ A, uint8_t* __restrict__ An, const uint8_t* __restrict__ Bt,
                     uint8_t* __restrict__ Bn) {
-        bf16x8 a[2][4], b[2][4];
+        bf16x8 a[2][4], b[2][2];
         read_ops(A, Bt, 0, a[0], b[0]);
         load_dy(An, min(ns + 1, NS - 1));
-        __builtin_amdgcn_sched_barrier(kAllButVmem);  // keep the loads in this order
+        __builtin_amdgcn_sched_barrier(kAllButVmem);
         Step nn;
-        load_step(min(ns + 2, NS - 1), nn);  // kStepLoads loads: codes (2), scale data
-        u32x4_t w[8];
+        load_step(min(ns + 2, NS - 1), nn);
+        u32x4_t w[4];
         const Nf4Tab T = make_tab<CB, DT>(ahat_of(nxt));
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int p = c & 1;
             if (c < 3) read_ops(A, Bt, c + 1, a[p ^ 1], b[p ^ 1]);
-            w[2 * c] = deq8(T, c < 2 ? nxt.c0[2 * c] : nxt.c1[2 * c - 4]);
+            w[c] = deq8(T, nxt.c[c]);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int u = 0; u < 4; ++u) acc[i][u] = mfma32<DT>(a[p][i], b[p][u], acc[i][u]);
-            w[2 * c + 1] = deq8(T, c < 2 ? nxt.c0[2 * c + 1] : nxt.c1[2 * c - 3]);
+                for (int u = 0; u < 2; ++u) acc[i][u] = mfma32<DT>(a[p][i], b[p][u], acc[i][u]);
+            if (c < 3) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-            for (int i = 2; i < 4; ++i)
-#pragma unroll
-                for (int u = 0; u < 4; ++u) acc[i][u] = mfma32<DT>(a[p][i], b[p][u], acc[i][u]);
-            if (c < 3) QLORA_INTERLEAVE(12); else QLORA_INTERLEAVE(0);
+                for (int j_ = 0; j_ < 8; ++j_) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                }
+            }
         }
         store_w(Bn, w);
         cur = nxt;
@@ -831,23 +868,22 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
              ldsB0 + (buf ^ 1) * kTileBytes);
     }
 
-    // LoRA: r more reduction steps with A-operand u [M, r] (LDS) and B-operand
-    // A^T, i.e. rows of A [K, r] read directly (one 16-byte load when r % 8 == 0).
+    // LoRA: r more reduction steps with A-operand u [M, r] (LDS) and B-operand A^T
     const bool rvec = (r % 8) == 0;
     for (int j0 = 0; j0 < r; j0 += kTK) {
-        if (rvec) load_tile<true>(ar, u_, r, m0, M, j0, r, tid);
-        else load_tile<false>(ar, u_, r, m0, M, j0, r, tid);
-        store_ftile(ldsA0, ar, tid);
+        if (rvec) load_tile8<true>(ar, u_, r, m0, M, j0, r, tid);
+        else load_tile8<false>(ar, u_, r, m0, M, j0, r, tid);
+        store_ftile8(ldsA0, ar, tid);
         __syncthreads();
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            bf16x8 a[4], b[4];
+            bf16x8 a[4], b[2];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 a[i] = *reinterpret_cast<const bf16x8*>(ldsA0 + offA[c] + 4096u * (4 * wm + i));
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int col = k0 + 128 * wk + 32 * u + l32;
+            for (int u = 0; u < 2; ++u) {
+                const int col = k0 + 64 * wk + 32 * u + l32;
                 const int j = j0 + 16 * c + 8 * h;
                 if (rvec) {
                     b[u] = (col < K && j < r) ? *reinterpret_cast<const bf16x8*>(Al + (int64_t)col * r + j)
@@ -859,28 +895,26 @@ __global__ __launch_bounds__(kT, 1) void nf4_gemm_bwd_dx_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int u = 0; u < 4; ++u) acc[i][u] = mfma32<DT>(a[i], b[u], acc[i][u]);
+                for (int u = 0; u < 2; ++u) acc[i][u] = mfma32<DT>(a[i], b[u], acc[i][u]);
         }
         __syncthreads();
     }
 
-    // dx tile as bf16 through LDS (256 x 256 x 2 B: all four tile buffers):
-    // lane (column l32 of each 32 x 32 tile, rows 8*(v/4) + 4h + v%4) writes its
-    // values, then each thread stores 16-byte row chunks
+    // dx tile as bf16 through LDS (256 x 256 x 2 B: all four tile buffers)
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int row = 128 * wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-                *reinterpret_cast<uint16_t*>(lds + row * 512 + 2 * (128 * wk + 32 * u + l32)) =
+                *reinterpret_cast<uint16_t*>(lds + row * 512 + 2 * (64 * wk + 32 * u + l32)) =
                     (uint16_t)(pack2<DT>(acc[i][u][v], 0.0f) & 0xFFFFu);
             }
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-        const int idx = tid + kT * e, row = idx >> 5, ch = idx & 31;
+    for (int e = 0; e < 16; ++e) {
+        const int idx = tid + kT8 * e, row = idx >> 5, ch = idx & 31;
         const int m = m0 + row, k = k0 + 8 * ch;
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + row * 512 + 16 * ch);
         if (m < M && k < K) *reinterpret_cast<u32x4_t*>(dx + (int64_t)m * K + k) = v;
@@ -931,7 +965,7 @@ qlora_status launch_gemm_bwd_dx(const uint16_t* dy, const uint8_t* codes, const 
     with_cb_dt(cb, dt, [&](auto cbc, auto dtc) {
         constexpr int CB = decltype(cbc)::value, DT = decltype(dtc)::value;
 #define QL_BWD(V, DQ)                                                                                           \
-    hipLaunchKernelGGL((nf4_gemm_bwd_dx_kernel<V, DQ, CB, DT>), dim3(tm * tk), dim3(kT), 0, s, dy, codes, q8, a2, u, \
+    hipLaunchKernelGGL((nf4_gemm_bwd_dx_kernel<V, DQ, CB, DT>), dim3(tm * tk), dim3(kT8), 0, s, dy, codes, q8, a2, u, \
                        A, dx, M, N, K, r, tm, tk)
         if (q8) {
             if (vec) QL_BWD(true, true); else QL_BWD(false, true);

@@ -244,7 +244,7 @@ def test_backward_steps_wait_for_their_dy_tile_before_the_barrier(asm):
         for st in steps:
             ops = _ops(st)
             d = [i for i, o in enumerate(ops) if o == "D"]
-            if len(d) < 8:
+            if len(d) < 4:              # a step's dy tile: 4 direct loads per wave (8 waves x 32 rows)
                 continue
             after = ops[d[-1] + 1:]
             waits = [i for i, o in enumerate(after) if isinstance(o, tuple)]
