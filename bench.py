@@ -51,6 +51,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="skip decode / quantize / dense context lines")
     p.add_argument("--mode", choices=["bench", "pmc", "pmc-decode"], default="bench")
+    p.add_argument("--bwd", choices=["deferred", "per-layer"], default="deferred",
+                   help="backward schedule: u and dx per layer and every layer's dA, dB in one launch at the end "
+                        "(qlora_linear_bwd_dx + qlora_lora_grads_batch), or qlora_linear_bwd per layer")
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     p.add_argument("--pmc-kernel", choices=["fwd", "bwd_dx", "quantize", "gemv"], default="fwd")
     p.add_argument("--decode-shape", choices=sorted(DECODE_SHAPES), default="gate_up")
@@ -331,11 +334,17 @@ def main():
     ws_bytes = max(max(qlora.bwd_workspace(M, d["N"], d["K"], r), qlora.fwd_workspace(M, d["N"], d["K"], r),
                        int(qlora.lib.qlora_lora_down_workspace(M, d["K"], r))) for d in L)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    for d in L:
+        d["u"] = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
+    grads = [(d["x"], d["t"], d["u"], d["dy"]) for d in L]
+    grads_ws = torch.empty(max(1, int(qlora.lib.qlora_lora_grads_batch_workspace(
+        (qlora.LoraGrads * len(L))(*[qlora.LoraGrads(0, 0, 0, 0, 0, 0, M, d["N"], d["K"]) for d in L]), len(L), r))),
+        dtype=torch.uint8, device=dev)
     total_flops = sum(d["flops"]["fwd"] + d["flops"]["bwd"] for d in L)
     n_weights = sum(d["N"] * d["K"] for d in L)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
-    timing = dict(fwd_gemm=[], bwd=[])
+    timing = dict(fwd_gemm=[], bwd=[], bwd_dx_call=[], grads_batch=[])
 
     def step(record):
         qlora.quantize_batch([d["W"] for d in L], [d["w"] for d in L])
@@ -347,14 +356,30 @@ def main():
             if record:
                 b = ev(); b.record()
                 timing["fwd_gemm"].append((a, b, d["flops"]["fwd_gemm"]))
+        if args.bwd == "per-layer":
+            for d in L:
+                if record:
+                    a = ev(); a.record()
+                qlora.linear_bwd(d["w"], d["x"], d["A"], d["B"], alpha, d["dy"], t=d["t"], dx=d["dx"], dA=d["dA"],
+                                 dB=d["dB"], ws=ws)
+                if record:
+                    b = ev(); b.record()
+                    timing["bwd"].append((a, b, d["flops"]["bwd"]))
+            return
+        # dx (what the layer below waits for) per layer, then the LoRA weight gradients of all layers
         for d in L:
             if record:
                 a = ev(); a.record()
-            qlora.linear_bwd(d["w"], d["x"], d["A"], d["B"], alpha, d["dy"], t=d["t"], dx=d["dx"], dA=d["dA"],
-                             dB=d["dB"], ws=ws)
+            qlora.linear_bwd_dx(d["w"], d["A"], d["B"], alpha, d["dy"], u=d["u"], dx=d["dx"], ws=ws)
             if record:
                 b = ev(); b.record()
-                timing["bwd"].append((a, b, d["flops"]["bwd"]))
+                timing["bwd_dx_call"].append((a, b, d["flops"]["bwd"]))
+        if record:
+            a = ev(); a.record()
+        qlora.lora_grads_batch(grads, dA=[d["dA"] for d in L], dB=[d["dB"] for d in L], ws=grads_ws)
+        if record:
+            b = ev(); b.record()
+            timing["grads_batch"].append((a, b, 0))
 
     if args.mode == "pmc":
         for _ in range(2):
@@ -414,7 +439,19 @@ def main():
         return tot_f / (tot_ms * 1e-3) / 1e12, tot_ms / len(lst)
 
     fwd_tfs, fwd_avg_ms = agg(timing["fwd_gemm"])
-    bwd_tfs, bwd_avg_ms = agg(timing["bwd"])
+    if args.bwd == "per-layer":
+        bwd_tfs, bwd_avg_ms = agg(timing["bwd"])
+        bwd_sched = {"bwd_schedule": "qlora_linear_bwd per layer"}
+    else:
+        # a layer's backward: its u + dx call and a seventh of the gradient launch
+        dx_ms = sum(a.elapsed_time(b) for a, b, _ in timing["bwd_dx_call"])
+        gb_ms = sum(a.elapsed_time(b) for a, b, _ in timing["grads_batch"])
+        tot_f = sum(f for _, _, f in timing["bwd_dx_call"])
+        bwd_tfs = tot_f / ((dx_ms + gb_ms) * 1e-3) / 1e12
+        bwd_avg_ms = (dx_ms + gb_ms) / len(timing["bwd_dx_call"])
+        bwd_sched = {"bwd_schedule": "qlora_linear_bwd_dx per layer, then qlora_lora_grads_batch over the 7 layers",
+                     "bwd_dx_call_avg_ms": round(dx_ms / len(timing["bwd_dx_call"]), 4),
+                     "lora_grads_batch_ms": round(gb_ms / len(timing["grads_batch"]), 4)}
     bdx_tfs, bdx_avg_ms = agg(timing["bwd_dx"])
 
     def roofline(kind, tfs, avg_ms, kernel_desc, flop_desc):
@@ -438,7 +475,7 @@ def main():
         "breakdown": {"fwd_gemm_roofline": roofline("fwd", fwd_tfs, fwd_avg_ms,
                                                      "nf4_gemm_fwd_kernel (fused dequant GEMM + LoRA up-projection)",
                                                      "2*M*K*N + 2*M*r*N over the 7 layer shapes, M=4096, r=64"),
-                      "bwd_call_tflops": round(bwd_tfs, 2), "bwd_call_avg_ms": round(bwd_avg_ms, 4),
+                      "bwd_call_tflops": round(bwd_tfs, 2), "bwd_call_avg_ms": round(bwd_avg_ms, 4), **bwd_sched,
                       "wall_s_timed": round(wall, 3), "weights_per_step": n_weights,
                       "flop_per_step": total_flops},
     }
@@ -642,14 +679,18 @@ def extras_train(torch, qlora, workloads, dev, to_dev, wl, steps):
         L.append(d)
     ws = torch.empty(max(max(qlora.bwd_workspace(M, d["N"], d["K"], r), qlora.fwd_workspace(M, d["N"], d["K"], r))
                          for d in L), dtype=torch.uint8, device=dev)
+    for d in L:
+        d["u"] = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
     flops = sum(4 * M * d["N"] * d["K"] + 6 * M * r * (d["N"] + d["K"]) for d in L)
 
     def step():
+        # the headline's schedule: u and dx per layer, then the LoRA weight gradients of all layers
         for d in L:
             qlora.linear_fwd(d["w"], d["x"], d["A"], d["B"], alpha, y=d["y"], t=d["t"], ws=ws)
         for d in L:
-            qlora.linear_bwd(d["w"], d["x"], d["A"], d["B"], alpha, d["dy"], t=d["t"], dx=d["dx"], dA=d["dA"],
-                             dB=d["dB"], ws=ws)
+            qlora.linear_bwd_dx(d["w"], d["A"], d["B"], alpha, d["dy"], u=d["u"], dx=d["dx"], ws=ws)
+        qlora.lora_grads_batch([(d["x"], d["t"], d["u"], d["dy"]) for d in L], dA=[d["dA"] for d in L],
+                               dB=[d["dB"] for d in L])
 
     for _ in range(2):
         step()

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdint>
 #include <mutex>
+#include <vector>
 
 #include "common.h"
 #include "lora_plan.h"
@@ -290,6 +291,85 @@ qlora_status qlora_fused_gemm_bwd_dx(const qlora_nf4* w, const uint16_t* dy, int
     if (!aligned16(dy) || !aligned16(u) || !aligned16(A) || !aligned16(dx)) return QLORA_ERR_MISALIGNED;
     return launch_gemm_bwd_dx(dy, w->codes, w->q8, w->a2, cb_of(w), dt_of(w), u, A, dx, (int)M, (int)N, (int)K, r,
                               (hipStream_t)stream);
+}
+
+size_t qlora_linear_bwd_dx_workspace(int64_t M, int64_t N, int64_t K, int r) {
+    if (bad_dims(M, N, K, r) || M == 0) return 0;
+    return align256(nt_ws_bytes(M, N, r));
+}
+
+qlora_status qlora_linear_bwd_dx(const qlora_nf4* w, int64_t M, const uint16_t* A, const uint16_t* B, int r,
+                                 float alpha, const uint16_t* dy, uint16_t* u, uint16_t* dx, void* ws,
+                                 size_t ws_bytes, void* stream) {
+    qlora_status st = check_state(w);
+    if (st != QLORA_OK) return st;
+    const int64_t N = w->n, K = w->k;
+    if (bad_dims(M, N, K, r) || !std::isfinite(alpha)) return QLORA_ERR_INVALID_ARG;
+    if (M == 0) return QLORA_OK;
+    if (!A || !B || !dy || !u || !dx) return QLORA_ERR_INVALID_ARG;
+    if (!aligned16(A) || !aligned16(B) || !aligned16(dy) || !aligned16(u) || !aligned16(dx))
+        return QLORA_ERR_MISALIGNED;
+    if (!ws || ws_bytes < qlora_linear_bwd_dx_workspace(M, N, K, r)) return QLORA_ERR_WORKSPACE;
+    if (!aligned16(ws)) return QLORA_ERR_MISALIGNED;
+    hipStream_t s = (hipStream_t)stream;
+    // u = s dy B^T (B [r, N] is the row-major transpose of B^T), kept in the caller's buffer
+    if ((st = launch_nt(dy, B, false, ws, u, alpha / (float)r, (int)M, (int)N, r, dt_of(w), s)) != QLORA_OK)
+        return st;
+    return launch_gemm_bwd_dx(dy, w->codes, w->q8, w->a2, cb_of(w), dt_of(w), u, A, dx, (int)M, (int)N, (int)K, r,
+                              s);
+}
+
+// Workspace of one layer's two gradient contractions in qlora_lora_grads_batch.
+inline size_t grads_ws(const qlora_lora_grads& g, int r) {
+    if (g.M == 0) return 0;
+    return align256(tn_ws_bytes(g.M, g.K, r)) + align256(tn_ws_bytes(g.M, g.N, r));
+}
+
+size_t qlora_lora_grads_batch_workspace(const qlora_lora_grads* layers, int count, int r) {
+    if (!layers || count <= 0 || r < 1 || r > 128) return 0;
+    size_t total = 0;
+    for (int i = 0; i < count; ++i)
+        if (!bad_dims(layers[i].M, layers[i].N, layers[i].K, r)) total += grads_ws(layers[i], r);
+    return total;
+}
+
+qlora_status qlora_lora_grads_batch(const qlora_lora_grads* layers, int count, int r, int dtype, void* ws,
+                                    size_t ws_bytes, void* stream) {
+    if (count < 0 || r < 1 || r > 128) return QLORA_ERR_INVALID_ARG;
+    if (dtype != QLORA_DTYPE_BF16 && dtype != QLORA_DTYPE_F16) return QLORA_ERR_INVALID_ARG;
+    if (count == 0) return QLORA_OK;
+    if (!layers) return QLORA_ERR_INVALID_ARG;
+    // every entry is checked before anything is launched
+    for (int i = 0; i < count; ++i) {
+        const qlora_lora_grads& g = layers[i];
+        if (bad_dims(g.M, g.N, g.K, r) || !g.dA || !g.dB) return QLORA_ERR_INVALID_ARG;
+        if (!aligned16(g.dA) || !aligned16(g.dB)) return QLORA_ERR_MISALIGNED;
+        if (g.M == 0) continue;
+        if (!g.x || !g.t || !g.u || !g.dy) return QLORA_ERR_INVALID_ARG;
+        if (!aligned16(g.x) || !aligned16(g.t) || !aligned16(g.u) || !aligned16(g.dy)) return QLORA_ERR_MISALIGNED;
+    }
+    const size_t need = qlora_lora_grads_batch_workspace(layers, count, r);
+    if (need && (!ws || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
+    if (need && !aligned16(ws)) return QLORA_ERR_MISALIGNED;
+    hipStream_t s = (hipStream_t)stream;
+    std::vector<TnDesc> d;
+    d.reserve(2 * (size_t)count);
+    size_t off = 0;
+    qlora_status st = QLORA_OK;
+    for (int i = 0; i < count; ++i) {
+        const qlora_lora_grads& g = layers[i];
+        if (g.M == 0) {  // empty sums
+            if ((st = launch_fill(g.dA, g.K * r, 0.0f, s)) != QLORA_OK) return st;
+            if ((st = launch_fill(g.dB, (int64_t)r * g.N, 0.0f, s)) != QLORA_OK) return st;
+            continue;
+        }
+        // dA [K, r] = x^T u ; dB [r, N] = t^T dy, stored transposed from the [N, r] reduction
+        d.push_back(TnDesc{g.x, g.u, at(ws, off), g.dA, (int)g.M, (int)g.K, r, 1});
+        off += align256(tn_ws_bytes(g.M, g.K, r));
+        d.push_back(TnDesc{g.dy, g.t, at(ws, off), g.dB, (int)g.M, (int)g.N, 1, g.N});
+        off += align256(tn_ws_bytes(g.M, g.N, r));
+    }
+    return launch_tn_batch(d.data(), (int)d.size(), r, dt_of(dtype), s);
 }
 
 qlora_status qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,

@@ -186,6 +186,17 @@ qlora_status launch_tn(const uint16_t* X, const uint16_t* S, void* ws, float* ou
 qlora_status launch_tn2(const uint16_t* X0, const uint16_t* S0, void* ws0, float* out0, int D0, int64_t ld_d0,
                         int64_t ld_j0, const uint16_t* X1, const uint16_t* S1, void* ws1, float* out1, int D1,
                         int64_t ld_d1, int64_t ld_j1, int M, int r, int dt, hipStream_t s);
+// Any number of such contractions of one rank r, up to 16 per launch (each with its
+// own M, D, operands, output and tn_ws_bytes(M, D, r) bytes of workspace)
+struct TnDesc {
+    const uint16_t* X;
+    const uint16_t* S;
+    void* ws;
+    float* out;
+    int M, D;
+    int64_t ld_d, ld_j;
+};
+qlora_status launch_tn_batch(const TnDesc* d, int count, int r, int dt, hipStream_t s);
 qlora_status launch_fill(float* out, int64_t count, float v, hipStream_t s);
 qlora_status launch_expand_pooled(const uint16_t* A, int K, int r, int g, int dt, uint16_t* out, hipStream_t s);
 qlora_status launch_pool_rows(const float* in, int K, int r, int g, float* out, hipStream_t s);

@@ -409,6 +409,28 @@ __global__ __launch_bounds__(256, TQ <= 2 && VEC ? 2 : 1) void tn2_kernel(const 
     }
 }
 
+// Up to kTnBatch independent contractions of one rank in one grid (the weight
+// gradients dA, dB of several layers, deferred to the end of a backward pass):
+// problem i takes workgroups [first[i], first[i + 1]), numbered split by split as
+// in tn2_kernel, so every waiting workgroup waits only for workgroups with lower
+// ids.  One launch streams the x and dy of all the layers back to back, and each
+// contraction's split-sum tail overlaps the streaming of the ones after it.
+constexpr int kTnBatch = 16;
+struct TnBatch {
+    TnProb p[kTnBatch];
+    int first[kTnBatch + 1];
+    int n;
+};
+
+template <int TQ, bool VEC, int NST, int DT>
+__global__ __launch_bounds__(256, TQ <= 2 && VEC ? 2 : 1) void tnb_kernel(const TnBatch bt) {
+    const int b = blockIdx.x;
+    int i = 0;
+    while (i + 1 < bt.n && b >= bt.first[i + 1]) ++i;
+    const int c = b - bt.first[i];
+    tn_body<TQ, VEC, NST, DT>(bt.p[i], c % bt.p[i].tiles, c / bt.p[i].tiles);
+}
+
 // QA-LoRA pooled branch ("LoRA, QLoRA, QA-LoRA explained", sections 3-5):
 // pool(x) A = x A~ with A~[k, j] = A[k / g, j] / g, exact in bf16 for g a power
 // of two (a shift of the exponent) unless it underflows, so the plain kernels run on A~; the
@@ -583,6 +605,45 @@ qlora_status launch_tn2(const uint16_t* X0, const uint16_t* S0, void* ws0, float
         const TnLaunch2 go{p0, p1, (unsigned)n, s};
     tn_dispatch(r, vec0 && vec1, std::max(p0.chunk, p1.chunk), dt, go);
     return launch_status();
+}
+
+namespace {
+struct TnLaunchB {
+    const TnBatch& b;
+    unsigned n;
+    hipStream_t s;
+    template <int TQ, bool V, int NST, int DT>
+    void operator()() const {
+        hipLaunchKernelGGL((tnb_kernel<TQ, V, NST, DT>), dim3(n), dim3(256), 0, s, b);
+    }
+};
+}  // namespace
+
+qlora_status launch_tn_batch(const TnDesc* d, int count, int r, int dt, hipStream_t s) {
+    for (int i0 = 0; i0 < count; i0 += kTnBatch) {
+        const int n = std::min(kTnBatch, count - i0);
+        TnBatch b{};
+        b.n = n;
+        bool vec = true;
+        int chunk = 64;
+        int64_t total = 0;
+        for (int i = 0; i < n; ++i) {
+            const TnDesc& e = d[i0 + i];
+            bool v = false;
+            b.p[i] = tn_prob(e.X, e.S, e.ws, e.out, e.M, e.D, r, e.ld_d, e.ld_j, v);
+            vec = vec && v;
+            chunk = std::max(chunk, b.p[i].chunk);
+            b.first[i] = (int)total;
+            total += (int64_t)b.p[i].tiles * b.p[i].splits;
+            if (total >= (int64_t(1) << 31)) return QLORA_ERR_UNSUPPORTED_SHAPE;
+        }
+        b.first[n] = (int)total;
+        const TnLaunchB go{b, (unsigned)total, s};
+        tn_dispatch(r, vec, chunk, dt, go);
+        const qlora_status st = launch_status();
+        if (st != QLORA_OK) return st;
+    }
+    return QLORA_OK;
 }
 
 qlora_status launch_expand_pooled(const uint16_t* A, int K, int r, int g, int dt, uint16_t* out, hipStream_t s) {

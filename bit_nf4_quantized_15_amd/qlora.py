@@ -28,6 +28,12 @@ class NF4State(ctypes.Structure):
                 ("dtype", ctypes.c_int32)]
 
 
+class LoraGrads(ctypes.Structure):
+    """Mirror of struct qlora_lora_grads."""
+    _fields_ = [("x", c_vp), ("t", c_vp), ("u", c_vp), ("dy", c_vp), ("dA", c_vp), ("dB", c_vp), ("M", c_i64),
+                ("N", c_i64), ("K", c_i64)]
+
+
 QUANT_TYPES = {"nf4": 0, "fp4": 1}                        # qlora_quant_type: the 4-bit codebook
 DTYPES = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2}   # qlora_dtype: the compute dtype
 
@@ -74,6 +80,12 @@ def _load():
         "qlora_bwd_workspace": (c_sz, [c_i64, c_i64, c_i64, ctypes.c_int]),
         "qlora_linear_bwd": (ctypes.c_int, [P, c_vp, c_i64, c_vp, c_vp, ctypes.c_int, ctypes.c_float,
                                             c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+        "qlora_linear_bwd_dx_workspace": (c_sz, [c_i64, c_i64, c_i64, ctypes.c_int]),
+        "qlora_linear_bwd_dx": (ctypes.c_int, [P, c_i64, c_vp, c_vp, ctypes.c_int, ctypes.c_float, c_vp, c_vp, c_vp,
+                                               c_vp, c_sz, c_vp]),
+        "qlora_lora_grads_batch_workspace": (c_sz, [ctypes.POINTER(LoraGrads), ctypes.c_int, ctypes.c_int]),
+        "qlora_lora_grads_batch": (ctypes.c_int, [ctypes.POINTER(LoraGrads), ctypes.c_int, ctypes.c_int,
+                                                  ctypes.c_int, c_vp, c_sz, c_vp]),
         "qlora_quantize_f32": (ctypes.c_int, [c_vp, c_i64, c_i64, P, c_vp]),
         "qlora_fwd_workspace_f32": (c_sz, [c_i64, c_i64, c_i64, ctypes.c_int]),
         "qlora_linear_fwd_f32": (ctypes.c_int, [P, c_vp, c_i64, c_vp, c_vp, ctypes.c_int, ctypes.c_float,
@@ -380,6 +392,56 @@ def linear_bwd(w, x, A, B, alpha, dy, t=None, need_dx=True, dx=None, dA=None, dB
     _check(fn(ctypes.byref(st), _ptr(x), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(t), _ptr(dy),
               _ptr(dx) if need_dx else None, _ptr(dA), _ptr(dB), _ptr(wsb), wsn, _stream()), name)
     return (dx if need_dx else None), dA, dB
+
+
+def linear_bwd_dx(w, A, B, alpha, dy, u=None, dx=None, ws=None):
+    """(u, dx) of the layer for upstream dy (qlora_linear_bwd_dx): u = (alpha/r) dy B^T, kept for
+    lora_grads_batch, and dx = dy W_hat^T + u A^T."""
+    M = dy.shape[0]
+    r = A.shape[1]
+    _dev(A, w.dtype, "A", (w.K, r))
+    _dev(B, w.dtype, "B", (r, w.N))
+    _dev(dy, w.dtype, "dy", (M, w.N))
+    dev = dy.device
+    u = _empty((M, r), dtype=w.dtype, device=dev) if u is None else _dev(u, w.dtype, "u", (M, r))
+    dx = _empty((M, w.K), dtype=w.dtype, device=dev) if dx is None else _dev(dx, w.dtype, "dx", (M, w.K))
+    wsb, wsn = _ws(int(lib.qlora_linear_bwd_dx_workspace(M, w.N, w.K, r)), dev, ws)
+    st = w.state()
+    _check(lib.qlora_linear_bwd_dx(ctypes.byref(st), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(dy), _ptr(u),
+                                   _ptr(dx), _ptr(wsb), wsn, _stream()), "qlora_linear_bwd_dx")
+    return u, dx
+
+
+def lora_grads_batch(layers, dA=None, dB=None, ws=None):
+    """dA = x^T u and dB = t^T dy (fp32) of several layers in one launch per 8 layers
+    (qlora_lora_grads_batch).  layers: a list of (x, t, u, dy), all of one rank r and one dtype (bf16 or
+    fp16); dA, dB: optional lists of output tensors.  Returns the lists (dA, dB)."""
+    n = len(layers)
+    if n == 0:
+        return [], []
+    dt = layers[0][0].dtype
+    code = _dtype_code(dt)
+    r = layers[0][1].shape[1]
+    dA = [None] * n if dA is None else list(dA)
+    dB = [None] * n if dB is None else list(dB)
+    descs = (LoraGrads * n)()
+    for i, (x, t, u, dy) in enumerate(layers):
+        M, K = x.shape
+        N = dy.shape[1]
+        _dev(x, dt, "x")
+        _dev(t, dt, "t", (M, r))
+        _dev(u, dt, "u", (M, r))
+        _dev(dy, dt, "dy", (M, N))
+        dev = x.device
+        dA[i] = _empty((K, r), dtype=torch.float32, device=dev) if dA[i] is None else _dev(dA[i], torch.float32,
+                                                                                          "dA", (K, r))
+        dB[i] = _empty((r, N), dtype=torch.float32, device=dev) if dB[i] is None else _dev(dB[i], torch.float32,
+                                                                                          "dB", (r, N))
+        descs[i] = LoraGrads(x.data_ptr(), t.data_ptr(), u.data_ptr(), dy.data_ptr(), dA[i].data_ptr(),
+                             dB[i].data_ptr(), M, N, K)
+    wsb, wsn = _ws(int(lib.qlora_lora_grads_batch_workspace(descs, n, r)), layers[0][0].device, ws)
+    _check(lib.qlora_lora_grads_batch(descs, n, r, code, _ptr(wsb), wsn, _stream()), "qlora_lora_grads_batch")
+    return dA, dB
 
 
 def pooled_fwd(w, x, A, B, alpha, g, y=None, t=None, ws=None):

@@ -258,6 +258,45 @@ qlora_status qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, int64_t M, 
 qlora_status qlora_fused_gemm_bwd_dx(const qlora_nf4* w, const uint16_t* dy, int64_t M, const uint16_t* u,
                                      const uint16_t* A, int r, uint16_t* dx, void* stream);
 
+/* The backward split in two for callers that defer the LoRA weight gradients
+ * to the end of the backward pass (deep dive 12.4: with the base frozen, dA
+ * and dB are needed only by the optimizer step, while dx feeds the layer
+ * below).  qlora_linear_bwd_dx computes the part of qlora_linear_bwd that the
+ * layer below waits for:
+ *   u  = s * (dy B^T)           [M, r]   bf16, into the caller's u (kept for
+ *                                        qlora_lora_grads_batch)
+ *   dx = dy W_hat^T + u A^T     [M, K]   bf16
+ * and qlora_lora_grads_batch computes, for `count` layers in one launch of up
+ * to 8 layers,
+ *   dA = x^T u   [K, r] fp32,   dB = t^T dy   [r, N] fp32 (overwritten),
+ * with t the forward's t_out.  Both give bit for bit the u, dx, dA and dB of
+ * qlora_linear_bwd on the same inputs (the same kernels, split plans and
+ * summation orders).  One launch streams the x and dy of all the layers back to
+ * back instead of ramping up and draining once per layer.  Errors as
+ * qlora_linear_bwd; M == 0: linear_bwd_dx does nothing, grads_batch writes
+ * zeros.  qlora_lora_grads_batch: count < 0, r outside [1, 128], a dtype other
+ * than bf16 / fp16 (the format of x, t, u and dy) or a null array ->
+ * INVALID_ARG; every entry is checked before anything is launched; count == 0
+ * is a no-op.  Its workspace (the split sums of each contraction) is caller
+ * owned and needs no clearing. */
+typedef struct qlora_lora_grads {
+    const uint16_t* x;  /* [M, K] the layer's input                 */
+    const uint16_t* t;  /* [M, r] the forward's t = s x A           */
+    const uint16_t* u;  /* [M, r] u = s dy B^T (qlora_linear_bwd_dx) */
+    const uint16_t* dy; /* [M, N] the upstream gradient              */
+    float* dA;          /* [K, r] fp32 out                           */
+    float* dB;          /* [r, N] fp32 out                           */
+    int64_t M, N, K;
+} qlora_lora_grads;
+
+size_t qlora_linear_bwd_dx_workspace(int64_t M, int64_t N, int64_t K, int r);
+qlora_status qlora_linear_bwd_dx(const qlora_nf4* w, int64_t M, const uint16_t* A, const uint16_t* B, int r,
+                                 float alpha, const uint16_t* dy, uint16_t* u, uint16_t* dx, void* ws,
+                                 size_t ws_bytes, void* stream);
+size_t qlora_lora_grads_batch_workspace(const qlora_lora_grads* layers, int count, int r);
+qlora_status qlora_lora_grads_batch(const qlora_lora_grads* layers, int count, int r, int dtype, void* ws,
+                                    size_t ws_bytes, void* stream);
+
 /* fp32 compute dtype (deep dive 8.3 lists fp32 beside bf16 and fp16).  The
  * state's dtype must be QLORA_DTYPE_F32 (else INVALID_ARG); every tensor is
  * float, 16-byte aligned.  Definitions, arguments and errors are those of the

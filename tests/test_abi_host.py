@@ -210,6 +210,48 @@ def test_linear_argument_errors(q):
     assert bwd(bad_k, FAKE, 8, FAKE, FAKE, 8, 16.0, None, FAKE, None, FAKE, FAKE, FAKE, wsb, None) == SHAPE
 
 
+def test_deferred_backward_argument_errors(q):
+    """qlora_linear_bwd_dx and qlora_lora_grads_batch report every documented error before launching."""
+    st = ctypes.byref(_state(q, n=64, k=128))
+    f = q.lib.qlora_linear_bwd_dx
+    need = q.lib.qlora_linear_bwd_dx_workspace(8, 64, 128, 8)
+    assert need > 0 and q.lib.qlora_linear_bwd_dx_workspace(0, 64, 128, 8) == 0
+    # (w, M, A, B, r, alpha, dy, u, dx, ws, ws_bytes, stream)
+    assert f(st, 8, FAKE, FAKE, 0, 16.0, FAKE, FAKE, FAKE, FAKE, need, None) == INVALID          # r = 0
+    assert f(st, 8, FAKE, FAKE, 8, float("inf"), FAKE, FAKE, FAKE, FAKE, need, None) == INVALID
+    assert f(st, 8, FAKE, FAKE, 8, 16.0, FAKE, None, FAKE, FAKE, need, None) == INVALID           # u
+    assert f(st, 8, FAKE, FAKE, 8, 16.0, FAKE, FAKE, None, FAKE, need, None) == INVALID           # dx
+    assert f(st, 8, FAKE, FAKE, 8, 16.0, FAKE, FAKE + 2, FAKE, FAKE, need, None) == MISALIGNED
+    assert f(st, 8, FAKE, FAKE, 8, 16.0, FAKE, FAKE, FAKE, FAKE, need - 1, None) == WORKSPACE
+    assert f(st, 8, FAKE, FAKE, 8, 16.0, FAKE, FAKE, FAKE, None, need, None) == WORKSPACE
+    assert f(st, 0, None, None, 8, 16.0, None, None, None, None, 0, None) == OK                   # M = 0: no-op
+    bad_k = ctypes.byref(_state(q, n=64, k=96))
+    assert f(bad_k, 8, FAKE, FAKE, 8, 16.0, FAKE, FAKE, FAKE, FAKE, need, None) == SHAPE
+
+    g = q.lib.qlora_lora_grads_batch
+    L = (q.LoraGrads * 2)(q.LoraGrads(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 64, 128),
+                          q.LoraGrads(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 128, 64))
+    need = q.lib.qlora_lora_grads_batch_workspace(L, 2, 8)
+    assert need == (q.lib.qlora_lora_grads_batch_workspace(L, 1, 8)
+                    + q.lib.qlora_lora_grads_batch_workspace(ctypes.byref(L[1]), 1, 8))
+    # (layers, count, r, dtype, ws, ws_bytes, stream)
+    assert g(L, -1, 8, 0, FAKE, need, None) == INVALID
+    assert g(None, 2, 8, 0, FAKE, need, None) == INVALID
+    assert g(L, 2, 0, 0, FAKE, need, None) == INVALID                                # r = 0
+    assert g(L, 2, 129, 0, FAKE, need, None) == INVALID                              # r > 128
+    assert g(L, 2, 8, 2, FAKE, need, None) == INVALID                                # fp32 is not a 16-bit dtype
+    assert g(L, 2, 8, 0, FAKE, need - 1, None) == WORKSPACE
+    assert g(L, 2, 8, 0, None, need, None) == WORKSPACE
+    assert g(L, 2, 8, 0, FAKE + 8, need, None) == MISALIGNED
+    assert g(L, 0, 8, 0, None, 0, None) == OK                                        # count = 0: no-op
+    for field, bad, want in (("dy", None, INVALID), ("u", FAKE + 2, MISALIGNED), ("dA", None, INVALID),
+                             ("dB", FAKE + 4, MISALIGNED), ("M", -1, INVALID), ("N", 0, INVALID),
+                             ("K", 1 << 31, INVALID)):
+        M2 = (q.LoraGrads * 2)(L[0], L[1])
+        setattr(M2[1], field, bad)                    # the second entry is checked before the first launches
+        assert g(M2, 2, 8, 0, FAKE, need, None) == want, field
+
+
 def test_f32_argument_errors(q):
     """fp32 states go through the _f32 calls only, and those take nothing else."""
     s16 = ctypes.byref(_state(q, n=64, k=128))
