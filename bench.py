@@ -51,9 +51,12 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="skip decode / quantize / dense context lines")
     p.add_argument("--mode", choices=["bench", "pmc", "pmc-decode"], default="bench")
-    p.add_argument("--bwd", choices=["deferred", "per-layer"], default="deferred",
-                   help="backward schedule: u and dx per layer and every layer's dA, dB in one launch at the end "
-                        "(qlora_linear_bwd_dx + qlora_lora_grads_batch), or qlora_linear_bwd per layer")
+    p.add_argument("--schedule", choices=["grouped", "deferred", "per-layer"], default="grouped",
+                   help="grouped: the LoRA products t and u of the layers that share their input in one launch "
+                        "(qlora_lora_down_batch, qlora_lora_u_batch), the GEMMs per layer, every layer's dA, dB "
+                        "in one launch at the end (qlora_lora_grads_batch); deferred: t per layer, u and dx per "
+                        "layer (qlora_linear_bwd_dx), dA, dB at the end; per-layer: qlora_linear_fwd's stages and "
+                        "qlora_linear_bwd per layer")
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     p.add_argument("--pmc-kernel", choices=["fwd", "bwd_dx", "quantize", "gemv"], default="fwd")
     p.add_argument("--decode-shape", choices=sorted(DECODE_SHAPES), default="gate_up")
@@ -62,6 +65,9 @@ def parse():
                    help="mean per dispatch of every counter in a rocprofv3 --pmc csv, by kernel")
     return p.parse_args()
 
+
+# consecutive layers of a decoder block that read the same input
+SHARED_INPUT = {("q_proj", "k_proj"), ("k_proj", "v_proj"), ("gate_proj", "up_proj")}
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNELS = {"fwd": "nf4_gemm_fwd_kernel", "bwd_dx": "nf4_gemm_bwd_dx_kernel", "quantize": "nf4_quantize_batch_kernel",
@@ -346,17 +352,36 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)
     timing = dict(fwd_gemm=[], bwd=[], bwd_dx_call=[], grads_batch=[])
 
+    # layers whose inputs are ready together: q, k, v share x, gate and up share theirs (and get their dy
+    # together in the backward); o and down wait for the attention and the MLP activation
+    groups, cur = [], []
+    for i, d in enumerate(L):
+        if cur and (L[cur[-1]]["name"], d["name"]) not in SHARED_INPUT:
+            groups.append(cur)
+            cur = []
+        cur.append(i)
+    groups.append(cur)
+    lw = lambda C: int(qlora.lib.qlora_lora_down_workspace(M, C, r))
+    prod_ws = max(max(sum(lw(L[i]["K"]) for i in g), sum(lw(L[i]["N"]) for i in g)) for g in groups)
+    if prod_ws > ws.numel():
+        ws = torch.empty(prod_ws, dtype=torch.uint8, device=dev)
+
     def step(record):
         qlora.quantize_batch([d["W"] for d in L], [d["w"] for d in L])
-        for d in L:
-            qlora.lora_down(d["x"], d["A"], alpha, t=d["t"], ws=ws)
-            if record:
-                a = ev(); a.record()
-            qlora.fused_gemm_fwd(d["w"], d["x"], d["t"], d["B"], y=d["y"])
-            if record:
-                b = ev(); b.record()
-                timing["fwd_gemm"].append((a, b, d["flops"]["fwd_gemm"]))
-        if args.bwd == "per-layer":
+        for g in groups:
+            if args.schedule == "grouped":
+                qlora.lora_down_batch([(L[i]["x"], L[i]["A"]) for i in g], alpha, t=[L[i]["t"] for i in g], ws=ws)
+            for i in g:
+                d = L[i]
+                if args.schedule != "grouped":
+                    qlora.lora_down(d["x"], d["A"], alpha, t=d["t"], ws=ws)
+                if record:
+                    a = ev(); a.record()
+                qlora.fused_gemm_fwd(d["w"], d["x"], d["t"], d["B"], y=d["y"])
+                if record:
+                    b = ev(); b.record()
+                    timing["fwd_gemm"].append((a, b, d["flops"]["fwd_gemm"]))
+        if args.schedule == "per-layer":
             for d in L:
                 if record:
                     a = ev(); a.record()
@@ -366,14 +391,23 @@ def main():
                     b = ev(); b.record()
                     timing["bwd"].append((a, b, d["flops"]["bwd"]))
             return
-        # dx (what the layer below waits for) per layer, then the LoRA weight gradients of all layers
-        for d in L:
+        # u and dx (what the layer below waits for) per layer or per group, then the LoRA weight
+        # gradients of all layers in one launch
+        for g in groups:
             if record:
                 a = ev(); a.record()
-            qlora.linear_bwd_dx(d["w"], d["A"], d["B"], alpha, d["dy"], u=d["u"], dx=d["dx"], ws=ws)
+            if args.schedule == "grouped":
+                qlora.lora_u_batch([(L[i]["dy"], L[i]["B"]) for i in g], alpha, u=[L[i]["u"] for i in g], ws=ws)
+                for i in g:
+                    d = L[i]
+                    qlora.fused_gemm_bwd_dx(d["w"], d["dy"], d["u"], d["A"], dx=d["dx"])
+            else:
+                for i in g:
+                    d = L[i]
+                    qlora.linear_bwd_dx(d["w"], d["A"], d["B"], alpha, d["dy"], u=d["u"], dx=d["dx"], ws=ws)
             if record:
                 b = ev(); b.record()
-                timing["bwd_dx_call"].append((a, b, d["flops"]["bwd"]))
+                timing["bwd_dx_call"].append((a, b, sum(L[i]["flops"]["bwd"] for i in g)))
         if record:
             a = ev(); a.record()
         qlora.lora_grads_batch(grads, dA=[d["dA"] for d in L], dB=[d["dB"] for d in L], ws=grads_ws)
@@ -439,18 +473,23 @@ def main():
         return tot_f / (tot_ms * 1e-3) / 1e12, tot_ms / len(lst)
 
     fwd_tfs, fwd_avg_ms = agg(timing["fwd_gemm"])
-    if args.bwd == "per-layer":
+    if args.schedule == "per-layer":
         bwd_tfs, bwd_avg_ms = agg(timing["bwd"])
         bwd_sched = {"bwd_schedule": "qlora_linear_bwd per layer"}
     else:
-        # a layer's backward: its u + dx call and a seventh of the gradient launch
+        # a layer's backward: its u and dx and a seventh of the gradient launch
         dx_ms = sum(a.elapsed_time(b) for a, b, _ in timing["bwd_dx_call"])
         gb_ms = sum(a.elapsed_time(b) for a, b, _ in timing["grads_batch"])
         tot_f = sum(f for _, _, f in timing["bwd_dx_call"])
+        n_layer_calls = len(timing["grads_batch"]) * len(L)
         bwd_tfs = tot_f / ((dx_ms + gb_ms) * 1e-3) / 1e12
-        bwd_avg_ms = (dx_ms + gb_ms) / len(timing["bwd_dx_call"])
-        bwd_sched = {"bwd_schedule": "qlora_linear_bwd_dx per layer, then qlora_lora_grads_batch over the 7 layers",
-                     "bwd_dx_call_avg_ms": round(dx_ms / len(timing["bwd_dx_call"]), 4),
+        bwd_avg_ms = (dx_ms + gb_ms) / n_layer_calls
+        bwd_sched = {"bwd_schedule": (
+                         "per group of layers sharing their input: qlora_lora_u_batch, then qlora_fused_gemm_bwd_dx "
+                         "per layer; then qlora_lora_grads_batch over the 7 layers" if args.schedule == "grouped" else
+                         "qlora_linear_bwd_dx per layer, then qlora_lora_grads_batch over the 7 layers"),
+                     "layer_groups": [[L[i]["name"] for i in g] for g in groups],
+                     "u_dx_avg_ms_per_layer": round(dx_ms / n_layer_calls, 4),
                      "lora_grads_batch_ms": round(gb_ms / len(timing["grads_batch"]), 4)}
     bdx_tfs, bdx_avg_ms = agg(timing["bwd_dx"])
 

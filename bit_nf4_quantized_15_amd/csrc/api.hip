@@ -319,6 +319,57 @@ qlora_status qlora_linear_bwd_dx(const qlora_nf4* w, int64_t M, const uint16_t* 
                               s);
 }
 
+size_t qlora_lora_prod_batch_workspace(const qlora_lora_prod* items, int count, int r) {
+    if (!items || count <= 0 || r < 1 || r > 128) return 0;
+    size_t total = 0;
+    for (int i = 0; i < count; ++i) {
+        const qlora_lora_prod& e = items[i];
+        if (!bad_dims(e.M, 1, e.C, r) && e.M > 0) total += align256(nt_ws_bytes(e.M, e.C, r));
+    }
+    return total;
+}
+
+// t_i = s x_i A_i (y_natural) or u_i = s dy_i B_i^T for every item, in launches of up to 8.
+static qlora_status lora_prod_batch(const qlora_lora_prod* items, int count, int r, float alpha, int dtype,
+                                    bool y_natural, void* ws, size_t ws_bytes, void* stream) {
+    if (count < 0 || r < 1 || r > 128 || !std::isfinite(alpha)) return QLORA_ERR_INVALID_ARG;
+    if (dtype != QLORA_DTYPE_BF16 && dtype != QLORA_DTYPE_F16) return QLORA_ERR_INVALID_ARG;
+    if (count == 0) return QLORA_OK;
+    if (!items) return QLORA_ERR_INVALID_ARG;
+    for (int i = 0; i < count; ++i) {  // every entry is checked before anything is launched
+        const qlora_lora_prod& e = items[i];
+        if (bad_dims(e.M, 1, e.C, r)) return QLORA_ERR_INVALID_ARG;
+        if (y_natural && e.C % kBlock) return QLORA_ERR_UNSUPPORTED_SHAPE;
+        if (e.M == 0) continue;
+        if (!e.x || !e.w || !e.out) return QLORA_ERR_INVALID_ARG;
+        if (!aligned16(e.x) || !aligned16(e.w) || !aligned16(e.out)) return QLORA_ERR_MISALIGNED;
+    }
+    const size_t need = qlora_lora_prod_batch_workspace(items, count, r);
+    if (need && (!ws || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
+    if (need && !aligned16(ws)) return QLORA_ERR_MISALIGNED;
+    std::vector<NtDesc> d;
+    d.reserve((size_t)count);
+    size_t off = 0;
+    for (int i = 0; i < count; ++i) {
+        const qlora_lora_prod& e = items[i];
+        if (e.M == 0) continue;
+        d.push_back(NtDesc{e.x, e.w, at(ws, off), e.out, alpha / (float)r, (int)e.M, (int)e.C});
+        off += align256(nt_ws_bytes(e.M, e.C, r));
+    }
+    if (d.empty()) return QLORA_OK;
+    return launch_nt_batch(d.data(), (int)d.size(), y_natural, r, dt_of(dtype), (hipStream_t)stream);
+}
+
+qlora_status qlora_lora_down_batch(const qlora_lora_prod* items, int count, int r, float alpha, int dtype, void* ws,
+                                   size_t ws_bytes, void* stream) {
+    return lora_prod_batch(items, count, r, alpha, dtype, true, ws, ws_bytes, stream);
+}
+
+qlora_status qlora_lora_u_batch(const qlora_lora_prod* items, int count, int r, float alpha, int dtype, void* ws,
+                                size_t ws_bytes, void* stream) {
+    return lora_prod_batch(items, count, r, alpha, dtype, false, ws, ws_bytes, stream);
+}
+
 // Workspace of one layer's two gradient contractions in qlora_lora_grads_batch.
 inline size_t grads_ws(const qlora_lora_grads& g, int r) {
     if (g.M == 0) return 0;

@@ -178,6 +178,17 @@ qlora_status launch_gemm_bwd_dx(const uint16_t* dy, const uint8_t* codes, const 
 // ws: nt_ws_bytes(M, C, r) bytes
 qlora_status launch_nt(const uint16_t* X, const uint16_t* Y, bool y_natural, void* ws, uint16_t* out, float scale,
                        int M, int C, int r, int dt, hipStream_t s);
+// Any number of such products of one rank r and one layout of Y, up to 8 per launch (each
+// with its own M, C, X, Y, out, scale and nt_ws_bytes(M, C, r) bytes of workspace)
+struct NtDesc {
+    const uint16_t* X;
+    const uint16_t* Y;
+    void* ws;
+    uint16_t* out;
+    float scale;
+    int M, C;
+};
+qlora_status launch_nt_batch(const NtDesc* d, int count, bool y_natural, int r, int dt, hipStream_t s);
 // out[d * ld_d + j * ld_j] = sum_m X [M, D][m, d] * S [M, r][m, j]; ws: tn_ws_bytes(M, D, r) bytes
 qlora_status launch_tn(const uint16_t* X, const uint16_t* S, void* ws, float* out, int M, int D, int r,
                        int64_t ld_d, int64_t ld_j, int dt, hipStream_t s);

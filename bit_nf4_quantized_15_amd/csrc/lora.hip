@@ -170,10 +170,10 @@ __device__ __forceinline__ bool split_sum(f32x16_t (&acc)[TQ], uint64_t* __restr
 // MFMA's k slots may map to any reduction indices, as long as both operands
 // agree).
 template <int TQ, bool VEC, bool YNAT, int NST, int DT>
-__global__ __launch_bounds__(256) void nt_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Y,
-                                                 uint64_t* __restrict__ tags, float* __restrict__ part,
-                                                 uint16_t* __restrict__ out, float scale, int M, int C, int r,
-                                                 int chunk) {
+__device__ __forceinline__ void nt_body(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Y,
+                                        uint64_t* __restrict__ tags, float* __restrict__ part,
+                                        uint16_t* __restrict__ out, float scale, int M, int C, int r, int chunk,
+                                        int tile, int split, int tiles, int splits) {
     static_assert(NST * 64 <= (TQ == 4 ? 256 : 512), "steps beyond nt_max_chunk");
     constexpr int kCols = NST * 64;                   // columns of C per split (at most)
     constexpr int kLdT = kCols + 8;                   // Yt row (bf16): 16 rows start 4 banks apart
@@ -183,8 +183,7 @@ __global__ __launch_bounds__(256) void nt_kernel(const uint16_t* __restrict__ X,
     __shared__ __attribute__((aligned(16))) uint16_t ys[YNAT ? kCols * kLdN : 32 * TQ * kLdT];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
     const int tj = l32 & 15, tg = l32 >> 4;
-    const int m0 = blockIdx.x * 128 + wave * 32;
-    const int split = blockIdx.y;
+    const int m0 = tile * 128 + wave * 32;
     const int c_begin = split * chunk;
     const int c_end = min(C, c_begin + chunk);
 
@@ -207,7 +206,7 @@ __global__ __launch_bounds__(256) void nt_kernel(const uint16_t* __restrict__ X,
                         : load8_row<false>(Y, C, row, r, c, c_end);
         }
     }
-    const int bm0 = blockIdx.x * 128;
+    const int bm0 = tile * 128;
     const rsrc_t xrs = buf_rsrc(X + (int64_t)bm0 * C, (uint64_t)min(128, M - bm0) * C * 2);
     const int xrow = m0 + l32;
     bf16x8 xa[NST][4];
@@ -245,7 +244,7 @@ __global__ __launch_bounds__(256) void nt_kernel(const uint16_t* __restrict__ X,
                                        : *reinterpret_cast<const bf16x8*>(&ys[(32 * q + l32) * kLdT + c]);
                 acc[q] = mfma32<DT>(xa[st][i], yb, acc[q]);
             }
-    if (!split_sum<TQ>(acc, tags, part, (int)gridDim.x, (int)blockIdx.x, split, (int)gridDim.y)) return;
+    if (!split_sum<TQ>(acc, tags, part, tiles, tile, split, splits)) return;
 #pragma unroll
     for (int q = 0; q < TQ; ++q) {
         const int j = 32 * q + l32;
@@ -256,6 +255,47 @@ __global__ __launch_bounds__(256) void nt_kernel(const uint16_t* __restrict__ X,
             if (m < M) out[(int64_t)m * r + j] = (uint16_t)(pack2<DT>(scale * acc[q][v], 0.0f) & 0xFFFFu);
         }
     }
+}
+
+template <int TQ, bool VEC, bool YNAT, int NST, int DT>
+__global__ __launch_bounds__(256) void nt_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Y,
+                                                 uint64_t* __restrict__ tags, float* __restrict__ part,
+                                                 uint16_t* __restrict__ out, float scale, int M, int C, int r,
+                                                 int chunk) {
+    nt_body<TQ, VEC, YNAT, NST, DT>(X, Y, tags, part, out, scale, M, C, r, chunk, (int)blockIdx.x, (int)blockIdx.y,
+                                    (int)gridDim.x, (int)gridDim.y);
+}
+
+// Up to kNtBatch such products of one rank and one operand layout in one grid (t of
+// the layers that share their input, or u of the layers whose dy arrive together):
+// problem i takes workgroups [first[i], first[i + 1]), numbered split by split, so
+// that every waiting workgroup waits only for workgroups with lower ids, and each
+// product's split-sum tail overlaps the streaming of the ones after it.
+constexpr int kNtBatch = 8;
+struct NtProb {
+    const uint16_t* X;
+    const uint16_t* Y;
+    uint64_t* tags;
+    float* part;
+    uint16_t* out;
+    float scale;
+    int M, C, chunk, tiles, splits;
+};
+struct NtBatch {
+    NtProb p[kNtBatch];
+    int first[kNtBatch + 1];
+    int n, r;
+};
+
+template <int TQ, bool VEC, bool YNAT, int NST, int DT>
+__global__ __launch_bounds__(256) void ntb_kernel(const NtBatch bt) {
+    const int b = blockIdx.x;
+    int i = 0;
+    while (i + 1 < bt.n && b >= bt.first[i + 1]) ++i;
+    const NtProb& p = bt.p[i];
+    const int c = b - bt.first[i];
+    nt_body<TQ, VEC, YNAT, NST, DT>(p.X, p.Y, p.tags, p.part, p.out, p.scale, p.M, p.C, bt.r, p.chunk, c % p.tiles,
+                                    c / p.tiles, p.tiles, p.splits);
 }
 
 // out[d * ld_d + j * ld_j] = sum over m of X[m, d] * S[m, j]   (fp32; S [M, r]
@@ -605,6 +645,71 @@ qlora_status launch_tn2(const uint16_t* X0, const uint16_t* S0, void* ws0, float
         const TnLaunch2 go{p0, p1, (unsigned)n, s};
     tn_dispatch(r, vec0 && vec1, std::max(p0.chunk, p1.chunk), dt, go);
     return launch_status();
+}
+
+qlora_status launch_nt_batch(const NtDesc* d, int count, bool y_natural, int r, int dt, hipStream_t s) {
+    const int tq = (r + 31) / 32;
+    for (int i0 = 0; i0 < count; i0 += kNtBatch) {
+        const int n = std::min(kNtBatch, count - i0);
+        NtBatch b{};
+        b.n = n;
+        b.r = r;
+        bool vec = !y_natural || r % 8 == 0;
+        int chunk = 64;
+        int64_t total = 0;
+        for (int i = 0; i < n; ++i) {
+            const NtDesc& e = d[i0 + i];
+            const SplitPlan sp = plan_nt(e.M, e.C, r);
+            NtProb& p = b.p[i];
+            p.X = e.X;
+            p.Y = e.Y;
+            p.tiles = (e.M + 127) / 128;
+            p.splits = sp.splits;
+            p.chunk = sp.chunk;
+            p.tags = static_cast<uint64_t*>(e.ws);
+            p.part = reinterpret_cast<float*>(static_cast<uint8_t*>(e.ws) + split_tags_bytes(p.tiles, sp));
+            p.out = e.out;
+            p.scale = e.scale;
+            p.M = e.M;
+            p.C = e.C;
+            // the conditions of launch_nt's vector path, for every product of the launch
+            vec = vec && (e.C % 8 == 0) && ((reinterpret_cast<uintptr_t>(e.X) & 15u) == 0) &&
+                  ((reinterpret_cast<uintptr_t>(e.Y) & 15u) == 0) && (int64_t)e.C * 128 * 2 < (int64_t(1) << 30);
+            chunk = std::max(chunk, sp.chunk);
+            b.first[i] = (int)total;
+            total += (int64_t)p.tiles * p.splits;
+            if (total >= (int64_t(1) << 31)) return QLORA_ERR_UNSUPPORTED_SHAPE;
+        }
+        b.first[n] = (int)total;
+        const int nst = steps_template(chunk);
+#define QL_NTB(TQ, V, NAT, NST) \
+    hipLaunchKernelGGL((ntb_kernel<TQ, V, NAT, NST, DT>), dim3((unsigned)total), dim3(256), 0, s, b);
+#define QL_NTB1(TQ, V, NAT)                                  \
+    if (nst == 2) { QL_NTB(TQ, V, NAT, 2) }                  \
+    else if (nst == 4) { QL_NTB(TQ, V, NAT, 4) }             \
+    else { QL_NTB(TQ, V, NAT, (TQ == 4 ? 4 : 8)) }
+#define QL_NTB2(TQ)                                                                \
+    if (y_natural) {                                                               \
+        if (vec) { QL_NTB1(TQ, true, true) } else { QL_NTB1(TQ, false, true) }    \
+    } else {                                                                       \
+        if (vec) { QL_NTB1(TQ, true, false) } else { QL_NTB1(TQ, false, false) }  \
+    }
+        with_dt(dt, [&](auto dtc) {
+            constexpr int DT = decltype(dtc)::value;
+            switch (tq) {
+                case 1: QL_NTB2(1) break;
+                case 2: QL_NTB2(2) break;
+                case 3: QL_NTB2(3) break;
+                default: QL_NTB2(4) break;
+            }
+        });
+#undef QL_NTB2
+#undef QL_NTB1
+#undef QL_NTB
+        const qlora_status st = launch_status();
+        if (st != QLORA_OK) return st;
+    }
+    return QLORA_OK;
 }
 
 namespace {

@@ -34,6 +34,11 @@ class LoraGrads(ctypes.Structure):
                 ("N", c_i64), ("K", c_i64)]
 
 
+class LoraProd(ctypes.Structure):
+    """Mirror of struct qlora_lora_prod."""
+    _fields_ = [("x", c_vp), ("w", c_vp), ("out", c_vp), ("M", c_i64), ("C", c_i64)]
+
+
 QUANT_TYPES = {"nf4": 0, "fp4": 1}                        # qlora_quant_type: the 4-bit codebook
 DTYPES = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2}   # qlora_dtype: the compute dtype
 
@@ -86,6 +91,11 @@ def _load():
         "qlora_lora_grads_batch_workspace": (c_sz, [ctypes.POINTER(LoraGrads), ctypes.c_int, ctypes.c_int]),
         "qlora_lora_grads_batch": (ctypes.c_int, [ctypes.POINTER(LoraGrads), ctypes.c_int, ctypes.c_int,
                                                   ctypes.c_int, c_vp, c_sz, c_vp]),
+        "qlora_lora_prod_batch_workspace": (c_sz, [ctypes.POINTER(LoraProd), ctypes.c_int, ctypes.c_int]),
+        "qlora_lora_down_batch": (ctypes.c_int, [ctypes.POINTER(LoraProd), ctypes.c_int, ctypes.c_int,
+                                                 ctypes.c_float, ctypes.c_int, c_vp, c_sz, c_vp]),
+        "qlora_lora_u_batch": (ctypes.c_int, [ctypes.POINTER(LoraProd), ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                              ctypes.c_int, c_vp, c_sz, c_vp]),
         "qlora_quantize_f32": (ctypes.c_int, [c_vp, c_i64, c_i64, P, c_vp]),
         "qlora_fwd_workspace_f32": (c_sz, [c_i64, c_i64, c_i64, ctypes.c_int]),
         "qlora_linear_fwd_f32": (ctypes.c_int, [P, c_vp, c_i64, c_vp, c_vp, ctypes.c_int, ctypes.c_float,
@@ -442,6 +452,38 @@ def lora_grads_batch(layers, dA=None, dB=None, ws=None):
     wsb, wsn = _ws(int(lib.qlora_lora_grads_batch_workspace(descs, n, r)), layers[0][0].device, ws)
     _check(lib.qlora_lora_grads_batch(descs, n, r, code, _ptr(wsb), wsn, _stream()), "qlora_lora_grads_batch")
     return dA, dB
+
+
+def _lora_prod_batch(fn, name, items, alpha, natural, outs, ws):
+    n = len(items)
+    if n == 0:
+        return []
+    dt = items[0][0].dtype
+    code = _dtype_code(dt)
+    r = items[0][1].shape[1] if natural else items[0][1].shape[0]
+    outs = [None] * n if outs is None else list(outs)
+    descs = (LoraProd * n)()
+    for i, (X, Y) in enumerate(items):
+        M, C = X.shape
+        _dev(X, dt, "x" if natural else "dy")
+        _dev(Y, dt, "A" if natural else "B", (C, r) if natural else (r, C))
+        outs[i] = _empty((M, r), dtype=dt, device=X.device) if outs[i] is None else _dev(outs[i], dt, "out", (M, r))
+        descs[i] = LoraProd(X.data_ptr(), Y.data_ptr(), outs[i].data_ptr(), M, C)
+    wsb, wsn = _ws(int(lib.qlora_lora_prod_batch_workspace(descs, n, r)), items[0][0].device, ws)
+    _check(fn(descs, n, r, float(alpha), code, _ptr(wsb), wsn, _stream()), name)
+    return outs
+
+
+def lora_down_batch(items, alpha, t=None, ws=None):
+    """t_i = (alpha/r) x_i A_i for items [(x_i, A_i)] in one launch per 8 (qlora_lora_down_batch); each t_i is
+    that of lora_down.  t: optional list of outputs.  Returns the list of t_i."""
+    return _lora_prod_batch(lib.qlora_lora_down_batch, "qlora_lora_down_batch", items, alpha, True, t, ws)
+
+
+def lora_u_batch(items, alpha, u=None, ws=None):
+    """u_i = (alpha/r) dy_i B_i^T for items [(dy_i, B_i)], B_i [r, N_i], in one launch per 8
+    (qlora_lora_u_batch); each u_i is that of linear_bwd_dx.  u: optional list of outputs."""
+    return _lora_prod_batch(lib.qlora_lora_u_batch, "qlora_lora_u_batch", items, alpha, False, u, ws)
 
 
 def pooled_fwd(w, x, A, B, alpha, g, y=None, t=None, ws=None):

@@ -297,6 +297,34 @@ size_t qlora_lora_grads_batch_workspace(const qlora_lora_grads* layers, int coun
 qlora_status qlora_lora_grads_batch(const qlora_lora_grads* layers, int count, int r, int dtype, void* ws,
                                     size_t ws_bytes, void* stream);
 
+/* The LoRA products of several layers in one launch of up to 8 (deep dive
+ * 12.2: the rank-r side path s x A B and its chain rule), for the layers whose
+ * inputs are ready together: in a decoder block q, k and v share x, and gate
+ * and up share theirs (and, in the backward, receive their dy together).
+ *   qlora_lora_down_batch: out_i = s x_i A_i      [M_i, r] (A_i [C_i, r], the
+ *                          t of qlora_lora_down; C_i % 64 == 0 else
+ *                          UNSUPPORTED_SHAPE)
+ *   qlora_lora_u_batch:    out_i = s dy_i B_i^T   [M_i, r] (B_i [r, C_i], the u
+ *                          of qlora_linear_bwd_dx)
+ * with s = alpha / r, bf16 or fp16 (dtype) in and out.  Each output is bit for
+ * bit that of the single-layer call (the same kernel body, split plan and
+ * summation order).  count == 0 and M_i == 0 do nothing.  Errors: count < 0, r
+ * outside [1, 128], non-finite alpha, another dtype, a null array or entry ->
+ * INVALID_ARG (every entry checked before anything is launched); misaligned
+ * tensors; the workspace (caller owned, no clearing needed) missing or short. */
+typedef struct qlora_lora_prod {
+    const uint16_t* x;  /* [M, C]: x (down) or dy (u)          */
+    const uint16_t* w;  /* A [C, r] (down) or B [r, C] (u)     */
+    uint16_t* out;      /* [M, r]                               */
+    int64_t M, C;
+} qlora_lora_prod;
+
+size_t qlora_lora_prod_batch_workspace(const qlora_lora_prod* items, int count, int r);
+qlora_status qlora_lora_down_batch(const qlora_lora_prod* items, int count, int r, float alpha, int dtype, void* ws,
+                                   size_t ws_bytes, void* stream);
+qlora_status qlora_lora_u_batch(const qlora_lora_prod* items, int count, int r, float alpha, int dtype, void* ws,
+                                size_t ws_bytes, void* stream);
+
 /* fp32 compute dtype (deep dive 8.3 lists fp32 beside bf16 and fp16).  The
  * state's dtype must be QLORA_DTYPE_F32 (else INVALID_ARG); every tensor is
  * float, 16-byte aligned.  Definitions, arguments and errors are those of the

@@ -252,6 +252,32 @@ def test_deferred_backward_argument_errors(q):
         assert g(M2, 2, 8, 0, FAKE, need, None) == want, field
 
 
+def test_lora_product_batch_argument_errors(q):
+    """qlora_lora_down_batch and qlora_lora_u_batch check every entry before launching anything."""
+    P = q.LoraProd
+    items = (P * 2)(P(FAKE, FAKE, FAKE, 8, 128), P(FAKE, FAKE, FAKE, 300, 192))
+    need = q.lib.qlora_lora_prod_batch_workspace(items, 2, 16)
+    assert need == q.lib.qlora_lora_down_workspace(8, 128, 16) + q.lib.qlora_lora_down_workspace(300, 192, 16)
+    for f in (q.lib.qlora_lora_down_batch, q.lib.qlora_lora_u_batch):
+        # (items, count, r, alpha, dtype, ws, ws_bytes, stream)
+        assert f(items, -1, 16, 32.0, 0, FAKE, need, None) == INVALID
+        assert f(None, 2, 16, 32.0, 0, FAKE, need, None) == INVALID
+        assert f(items, 2, 0, 32.0, 0, FAKE, need, None) == INVALID
+        assert f(items, 2, 16, float("nan"), 0, FAKE, need, None) == INVALID
+        assert f(items, 2, 16, 32.0, 2, FAKE, need, None) == INVALID                  # fp32
+        assert f(items, 2, 16, 32.0, 0, FAKE, need - 1, None) == WORKSPACE
+        assert f(items, 2, 16, 32.0, 0, FAKE + 8, need, None) == MISALIGNED
+        assert f(items, 0, 16, 32.0, 0, None, 0, None) == OK
+        for field, bad, want in (("x", None, INVALID), ("w", FAKE + 2, MISALIGNED), ("out", None, INVALID),
+                                 ("M", -3, INVALID), ("C", 0, INVALID)):
+            it2 = (P * 2)(items[0], items[1])
+            setattr(it2[1], field, bad)
+            assert f(it2, 2, 16, 32.0, 0, FAKE, need, None) == want, field
+    odd = (P * 1)(P(FAKE, FAKE, FAKE, 8, 100))          # C % 64 != 0: t needs whole blocks, u does not
+    need1 = q.lib.qlora_lora_prod_batch_workspace(odd, 1, 16)
+    assert q.lib.qlora_lora_down_batch(odd, 1, 16, 32.0, 0, FAKE, need1, None) == SHAPE
+
+
 def test_f32_argument_errors(q):
     """fp32 states go through the _f32 calls only, and those take nothing else."""
     s16 = ctypes.byref(_state(q, n=64, k=128))

@@ -203,13 +203,13 @@ def test_publication_waits_for_the_payload(asm):
 def test_lora_kernels_keep_everything_in_registers(asm):
     """The LoRA products hold all of a split's loads in registers at once; no instantiation spills."""
     n = 0
-    for kind in ("nt_kernelI", "tn_kernelI", "tn2_kernelI", "tnb_kernelI"):
+    for kind in ("nt_kernelI", "ntb_kernelI", "tn_kernelI", "tn2_kernelI", "tnb_kernelI"):
         for name, _ in _kernels(asm["lora"], kind):
             d = _descriptor(asm["lora"], name)
             assert d["amdhsa_private_segment_fixed_size"] == 0, f"{name}: uses scratch"
             assert d["amdhsa_group_segment_fixed_size"] <= 160 * 1024, name
             n += 1
-    assert n == 88 + 44 + 44 + 44, n
+    assert n == 88 + 88 + 44 + 44 + 44, n
 
 
 def test_no_scalar_memory_writes(asm):
