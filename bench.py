@@ -722,12 +722,29 @@ def extras_train(torch, qlora, workloads, dev, to_dev, wl, steps):
         d["u"] = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
     flops = sum(4 * M * d["N"] * d["K"] + 6 * M * r * (d["N"] + d["K"]) for d in L)
 
+    groups, cur = [], []
+    for i, (name, _, _) in enumerate(cfg["layers"]):
+        if cur and (cfg["layers"][cur[-1]][0], name) not in SHARED_INPUT:
+            groups.append(cur)
+            cur = []
+        cur.append(i)
+    groups.append(cur)
+    lw = lambda C: int(qlora.lib.qlora_lora_down_workspace(M, C, r))
+    prod_ws = max(max(sum(lw(L[i]["K"]) for i in g), sum(lw(L[i]["N"]) for i in g)) for g in groups)
+    if prod_ws > ws.numel():
+        ws = torch.empty(prod_ws, dtype=torch.uint8, device=dev)
+
     def step():
-        # the headline's schedule: u and dx per layer, then the LoRA weight gradients of all layers
-        for d in L:
-            qlora.linear_fwd(d["w"], d["x"], d["A"], d["B"], alpha, y=d["y"], t=d["t"], ws=ws)
-        for d in L:
-            qlora.linear_bwd_dx(d["w"], d["A"], d["B"], alpha, d["dy"], u=d["u"], dx=d["dx"], ws=ws)
+        # the headline's grouped schedule: t and u per group of layers that share their input, the GEMMs
+        # per layer, then the LoRA weight gradients of all layers in one launch
+        for g in groups:
+            qlora.lora_down_batch([(L[i]["x"], L[i]["A"]) for i in g], alpha, t=[L[i]["t"] for i in g], ws=ws)
+            for i in g:
+                qlora.fused_gemm_fwd(L[i]["w"], L[i]["x"], L[i]["t"], L[i]["B"], y=L[i]["y"])
+        for g in groups:
+            qlora.lora_u_batch([(L[i]["dy"], L[i]["B"]) for i in g], alpha, u=[L[i]["u"] for i in g], ws=ws)
+            for i in g:
+                qlora.fused_gemm_bwd_dx(L[i]["w"], L[i]["dy"], L[i]["u"], L[i]["A"], dx=L[i]["dx"])
         qlora.lora_grads_batch([(d["x"], d["t"], d["u"], d["dy"]) for d in L], dA=[d["dA"] for d in L],
                                dB=[d["dB"] for d in L])
 
