@@ -58,7 +58,7 @@ def parse():
                         "layer (qlora_linear_bwd_dx), dA, dB at the end; per-layer: qlora_linear_fwd's stages and "
                         "qlora_linear_bwd per layer")
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
-    p.add_argument("--pmc-kernel", choices=["fwd", "bwd_dx", "quantize", "gemv"], default="fwd")
+    p.add_argument("--pmc-kernel", choices=["fwd", "bwd_dx", "quantize", "gemv", "grads"], default="fwd")
     p.add_argument("--decode-shape", choices=sorted(DECODE_SHAPES), default="gate_up")
     p.add_argument("--decode-m", type=int, default=1)
     p.add_argument("--pmc-counters", metavar="COUNTER_CSV",
@@ -71,11 +71,12 @@ SHARED_INPUT = {("q_proj", "k_proj"), ("k_proj", "v_proj"), ("gate_proj", "up_pr
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNELS = {"fwd": "nf4_gemm_fwd_kernel", "bwd_dx": "nf4_gemm_bwd_dx_kernel", "quantize": "nf4_quantize_batch_kernel",
-           "gemv": "nf4_gemv_stream_kernel"}
+           "gemv": "nf4_gemv_stream_kernel", "grads": "tnb_kernel"}
 _CSRC = os.path.join(HERE, "bit_nf4_quantized_15_amd", "csrc")
-SOURCES = {"fwd": "gemm.hip", "bwd_dx": "gemm.hip", "quantize": "quantize.hip", "gemv": "gemv.hip"}
+SOURCES = {"fwd": "gemm.hip", "bwd_dx": "gemm.hip", "quantize": "quantize.hip", "gemv": "gemv.hip", "grads": "lora.hip"}
 WORKLOAD_TAG = {"fwd": "7B_block_7_layers_M4096_r64", "bwd_dx": "7B_block_7_layers_M4096_r64",
-                "quantize": "7B_block_7_layers", "gemv": "gate_up_2x11008x4096_M1_r32"}
+                "quantize": "7B_block_7_layers", "gemv": "gate_up_2x11008x4096_M1_r32",
+                "grads": "7B_block_7_layers_M4096_r64"}
 TRAFFIC_FILES = {k: os.path.join(HERE, "profiles", f"{v}__{WORKLOAD_TAG[k]}__hbm_traffic.txt")
                  for k, v in KERNELS.items()}
 CALIB_BYTES = 512 << 20
@@ -120,7 +121,15 @@ def quantize_algorithmic_bytes(layers):
     return sum(N * K * 2 + N * K // 2 + N * K // 64 + 4 * (-(-N * K // 16384)) for _, N, K in layers)
 
 
+def grads_algorithmic_bytes(layers, M, r):
+    """HBM bytes of the one gradient launch of a step (every layer's dA and dB): x, dy, u and t in,
+    dA and dB (fp32) out."""
+    return sum(2 * M * K + 2 * M * N + 2 * 2 * M * r + 4 * K * r + 4 * r * N for _, N, K in layers)
+
+
 def algorithmic_bytes(kind, layers, M, r):
+    if kind == "grads":
+        return grads_algorithmic_bytes(layers, M, r)
     if kind == "fwd":
         return fwd_algorithmic_bytes(layers, M, r)
     if kind == "bwd_dx":

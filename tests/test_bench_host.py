@@ -47,6 +47,9 @@ def test_gemm_algorithmic_bytes_are_the_tensor_sizes():
     assert bench.algorithmic_bytes("fwd", BLOCK["layers"], M, r) == pytest.approx(sum(fwd) / 7, rel=1e-12)
     assert bench.algorithmic_bytes("bwd_dx", BLOCK["layers"], M, r) == pytest.approx(sum(bwd) / 7, rel=1e-12)
     assert round(sum(bwd) / 7) == 107465033
+    grads = sum(M * K * 2 + M * N * 2 + M * r * 2 * 2 + K * r * 4 + r * N * 4      # x, dy, u, t in; dA, dB out
+                for _, N, K in BLOCK["layers"])
+    assert bench.algorithmic_bytes("grads", BLOCK["layers"], M, r) == grads
 
 
 def test_decode_gemv_bytes_of_q_proj():
